@@ -1,0 +1,257 @@
+/*
+ * cconv_oracle.c -- CPU oracle for the depthwise causal short convolution fused with SiLU.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the benchmark's
+ * CPU-baseline leg may load this library. The product path (the HIP library) never links,
+ * loads or calls it, and the two share no code.
+ *
+ * Plain, slow, obviously correct loops written from the definitions, one output element at a
+ * time. The same source is compiled twice: ORACLE_REAL=double (the reference values the GPU
+ * is compared against) and ORACLE_REAL=float (the fp32 oracle). Every input value is exactly
+ * representable in fp32 (bf16 activations and state, bf16 or fp32 taps, fp32 bias), so inputs
+ * are passed as float arrays and widened to `real` on use. No FMA contraction (built with
+ * -ffp-contract=off), no fast-math.
+ *
+ * Definitions (sources are the three pages on this op):
+ *  - Tap order. [kernel-fun 0.2.0.dev1 wheel, strip.py, `_tap`]: the weight that multiplies
+ *    x[t-k] is w[:, W-1-k]. Equivalently z[t] = bias + sum_j w[d, j] * X[t-(W-1)+j].
+ *  - Zero history. [strip.py, `_ld_ring` and the backward's note on rows past T]: rows left
+ *    of the sequence start read as zero; rows at or past T contribute nothing.
+ *  - SiLU and its derivative. [strip.py, `_silu`, `_dsilu`]: y = z*sigma(z);
+ *    g = dy * s * (1 + z*(1 - s)) with s = sigma(z). sigma(z) = 1/(1+exp(-z)) is written
+ *    from its definition, not from the page's tanh approximation.
+ *  - Backward. [strip.py, `_bwd4` docstring]: dx[u] = sum_k w'[k] g[u+k] with
+ *    w'[k] = w[:, W-1-k]; dw is the sum over batch and time of g[t] * x[t-k] into column
+ *    W-1-k ([strip.py, partial-store comment]); dw and dbias are plain sums over every (b, t)
+ *    (the host `cconv_bwd` in strip.py sums the partials deterministically, with no atomics).
+ *  - Bias. Present in fla's parameter list ([kernel-fun wheel, _common/compat.py, FLA_KWARGS
+ *    row for causal_conv1d]) and in the decode API ([cudnn-frontend PR #797 "Add experimental
+ *    causal conv1d decode update", PR description, API]); read as added to z before SiLU, so
+ *    dbias = sum g.
+ *  - Decode. [PR #797 description, API and semantics]: advance a per-slot state of the last
+ *    W-1 inputs by one token; conv_state_indices picks the slot, -1 marks a padding row that
+ *    mutates nothing; invalid indices fail closed. Readings: state is stored oldest first
+ *    (for the token t being added, state[s, d, j] holds X[t-(W-1)+j]), so w[:, j] pairs
+ *    with state[:, j] and w[:, W-1] with the new token; a padding row's output is 0;
+ *    NULL indices mean slot n for row n; any index outside [-1, S) or a repeated non-negative
+ *    index makes the whole call invalid and nothing is written.
+ *
+ * Parity pins for every function here live in tests/test_oracle_pins.py (finite
+ * differences, a library convolution with autograd, an impulse, closed forms, decode ==
+ * forward, W padding). Parity unpinned: nothing beyond the last-ulp behaviour of exp().
+ */
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef ORACLE_REAL
+#define ORACLE_REAL double
+#endif
+typedef ORACLE_REAL real;
+
+#define ORACLE_IS_FLOAT (sizeof(real) == sizeof(float))
+
+static real r_exp(real v) { return ORACLE_IS_FLOAT ? (real)expf((float)v) : (real)exp((double)v); }
+
+/* sigma(z) = 1 / (1 + e^-z), written from the definition. */
+static real sigmoid(real z) { return (real)1 / ((real)1 + r_exp(-z)); }
+
+/* X[b, t, d]: the input with zeros outside 0 <= t < T. */
+static real xval(const float* x, int64_t T, int64_t D, int64_t b, int64_t t, int64_t d) {
+    if (t < 0 || t >= T) return 0;
+    return (real)x[(b * T + t) * D + d];
+}
+
+/* z[b, t, d] = bias[d] + sum_{j=0}^{W-1} w[d, j] * X[b, t-(W-1)+j, d]  (oldest tap first). */
+static real z_at(const float* x, int64_t T, int64_t D, const float* w, int W, const float* bias,
+                 int64_t b, int64_t t, int64_t d) {
+    real z = bias ? (real)bias[d] : (real)0;
+    for (int j = 0; j < W; ++j) z = z + (real)w[d * W + j] * xval(x, T, D, b, t - (W - 1) + j, d);
+    return z;
+}
+
+/* g[b, t, d] = dy * d silu/dz = dy * s * (1 + z*(1-s)), s = sigma(z); zero outside 0 <= t < T. */
+static real g_at(const float* x, const float* dy, int64_t T, int64_t D, const float* w, int W,
+                 const float* bias, int64_t b, int64_t t, int64_t d) {
+    if (t < 0 || t >= T) return 0;
+    real z = z_at(x, T, D, w, W, bias, b, t, d);
+    real s = sigmoid(z);
+    return (real)dy[(b * T + t) * D + d] * s * ((real)1 + z * ((real)1 - s));
+}
+
+/* dx[b, u, d] = sum_{j=0}^{W-1} w[d, j] * g[b, u+(W-1)-j, d]. */
+static real dx_at(const float* x, const float* dy, int64_t T, int64_t D, const float* w, int W,
+                  const float* bias, int64_t b, int64_t u, int64_t d) {
+    real acc = 0;
+    for (int j = 0; j < W; ++j)
+        acc = acc + (real)w[d * W + j] * g_at(x, dy, T, D, w, W, bias, b, u + (W - 1) - j, d);
+    return acc;
+}
+
+/* dw[d, j] = sum_b sum_t g[b, t, d] * X[b, t-(W-1)+j, d]. */
+static real dw_at(const float* x, const float* dy, int64_t B, int64_t T, int64_t D, const float* w,
+                  int W, const float* bias, int64_t d, int j) {
+    real acc = 0;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < T; ++t)
+            acc = acc + g_at(x, dy, T, D, w, W, bias, b, t, d) * xval(x, T, D, b, t - (W - 1) + j, d);
+    return acc;
+}
+
+/* dbias[d] = sum_b sum_t g[b, t, d]. */
+static real dbias_at(const float* x, const float* dy, int64_t B, int64_t T, int64_t D,
+                     const float* w, int W, const float* bias, int64_t d) {
+    real acc = 0;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < T; ++t) acc = acc + g_at(x, dy, T, D, w, W, bias, b, t, d);
+    return acc;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Exported entry points. Arrays are contiguous: x, dy, z, y, dx are [B, T, D]; w is [D, W];  */
+/* bias and dbias are [D] (bias may be NULL); dw is [D, W]. Outputs are unrounded `real`.     */
+/* OpenMP only spreads independent output elements over threads; every element is computed  */
+/* by one thread in the fixed order above, so results do not depend on the thread count.    */
+/* ---------------------------------------------------------------------------------------- */
+
+int oracle_real_bytes(void) { return (int)sizeof(real); }
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Forward: z (optional) and y = z * sigma(z) for every element. */
+void oracle_fwd(const float* x, int64_t B, int64_t T, int64_t D, const float* w, int W,
+                const float* bias, real* z_out, real* y_out) {
+    int64_t rows = B * T;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / T, t = r % T;
+        for (int64_t d = 0; d < D; ++d) {
+            real z = z_at(x, T, D, w, W, bias, b, t, d);
+            if (z_out) z_out[r * D + d] = z;
+            y_out[r * D + d] = z * sigmoid(z);
+        }
+    }
+}
+
+/* Backward: dx for every element, dw [D, W] and dbias [D] (dbias may be NULL). */
+void oracle_bwd(const float* x, const float* dy, int64_t B, int64_t T, int64_t D, const float* w,
+                int W, const float* bias, real* dx_out, real* dw_out, real* dbias_out) {
+    int64_t rows = B * T;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / T, u = r % T;
+        for (int64_t d = 0; d < D; ++d) dx_out[r * D + d] = dx_at(x, dy, T, D, w, W, bias, b, u, d);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t d = 0; d < D; ++d) {
+        for (int j = 0; j < W; ++j) dw_out[d * W + j] = dw_at(x, dy, B, T, D, w, W, bias, d, j);
+        if (dbias_out) dbias_out[d] = dbias_at(x, dy, B, T, D, w, W, bias, d);
+    }
+}
+
+/* Sampled forward: y at n listed (b, t, d) points of a full-size problem. */
+void oracle_fwd_points(const float* x, int64_t B, int64_t T, int64_t D, const float* w, int W,
+                       const float* bias, int64_t n, const int64_t* pb, const int64_t* pt,
+                       const int64_t* pd, real* y_out) {
+    (void)B;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        real z = z_at(x, T, D, w, W, bias, pb[i], pt[i], pd[i]);
+        y_out[i] = z * sigmoid(z);
+    }
+}
+
+/* Sampled backward: dx at n listed (b, u, d) points. */
+void oracle_dx_points(const float* x, const float* dy, int64_t B, int64_t T, int64_t D,
+                      const float* w, int W, const float* bias, int64_t n, const int64_t* pb,
+                      const int64_t* pu, const int64_t* pd, real* dx_out) {
+    (void)B;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) dx_out[i] = dx_at(x, dy, T, D, w, W, bias, pb[i], pu[i], pd[i]);
+}
+
+/* Sampled weight gradient: dw[d, :] and dbias[d] for n listed channels (full sums). */
+void oracle_dw_channels(const float* x, const float* dy, int64_t B, int64_t T, int64_t D,
+                        const float* w, int W, const float* bias, int64_t n, const int64_t* pd,
+                        real* dw_out /* [n, W] */, real* dbias_out /* [n] */) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        for (int j = 0; j < W; ++j) dw_out[i * W + j] = dw_at(x, dy, B, T, D, w, W, bias, pd[i], j);
+        dbias_out[i] = dbias_at(x, dy, B, T, D, w, W, bias, pd[i]);
+    }
+}
+
+/*
+ * Decode update [PR #797 description, API and semantics]. x: [N, D]; state: [S, D, W-1]
+ * (in/out, oldest first); idx: [N] or NULL (row n uses slot n, which needs N <= S);
+ * y_out: [N, D]. Returns 0 on success, 1 when the indices are invalid (then nothing is
+ * written: neither state nor y). For W == 1 the state holds nothing and is not touched.
+ */
+int oracle_update(const float* x, int64_t N, int64_t D, float* state, int64_t S,
+                  const int32_t* idx, const float* w, int W, const float* bias, real* y_out) {
+    const int64_t L = W - 1;
+    /* Validity first, so that an invalid call writes nothing. */
+    if (!idx && N > S) return 1;
+    if (idx) {
+        for (int64_t n = 0; n < N; ++n)
+            if (idx[n] < -1 || idx[n] >= S) return 1;
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t m = 0; m < n; ++m)
+                if (idx[n] >= 0 && idx[n] == idx[m]) return 1;
+    }
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t s = idx ? (int64_t)idx[n] : n;
+        if (s < 0) {
+            for (int64_t d = 0; d < D; ++d) y_out[n * D + d] = 0;
+            continue;
+        }
+        for (int64_t d = 0; d < D; ++d) {
+            float* st = state + (s * D + d) * L;
+            real z = bias ? (real)bias[d] : (real)0;
+            for (int64_t j = 0; j < L; ++j) z = z + (real)w[d * W + j] * (real)st[j];
+            z = z + (real)w[d * W + (W - 1)] * (real)x[n * D + d];
+            y_out[n * D + d] = z * sigmoid(z);
+            /* shift: drop the oldest, append the new token (plain value copies) */
+            for (int64_t j = 0; j + 1 < L; ++j) st[j] = st[j + 1];
+            if (L > 0) st[L - 1] = x[n * D + d];
+        }
+    }
+    return 0;
+}
+
+/*
+ * Round to bf16, nearest-even [strip.py, `_st`: downcast with rtne]. Written from the
+ * definition: the value is scaled so that bf16's 8 significant bits are the integer part,
+ * rounded half-to-even (nearbyint under the default rounding mode), and scaled back.
+ * Subnormal bf16 values share fp32's minimum exponent (-126), so their quantum is 2^-133.
+ */
+static uint16_t bf16_rtne(double v) {
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0) return sign;
+    int e = ilogb(a);
+    if (e < -126) e = -126;
+    double q = ldexp(1.0, e - 7);
+    double r = nearbyint(a / q) * q;
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+    float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(sign | (uint16_t)(bits >> 16));
+}
+
+void oracle_round_bf16(const real* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_rtne((double)in[i]);
+}

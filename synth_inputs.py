@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs for the depthwise causal short convolution + SiLU.
+
+This module draws random tensors and nothing else: it holds none of the operation's
+arithmetic, so both the CPU oracle (under ``oracle/``) and the HIP path may take their
+inputs from it without sharing any of the computation.
+
+Recipe (the same for every workload):
+  * a CPU ``torch.Generator`` seeded per workload;
+  * tensors drawn in a fixed order (training: x, w, bias, dy; decode: x, state, slot
+    permutation, w, bias);
+  * every draw is fp32 ``N(0, var)`` scaled by ``sqrt(var)`` and, where the tensor is bf16,
+    rounded to bf16 by torch's round-to-nearest-even cast. The bf16 bits that result are
+    what both sides receive.
+
+The variances follow the workloads the kernel-fun wheel page describes for this op
+(``cconv/__init__.py`` docstring: B=16, T=8192, D=2048, W=4 production call; D a multiple
+of n_heads*128): x and dy ~ N(0, 1), taps ~ N(0, 1/W) so that Var z is about 1, bias ~
+N(0, 0.1). The decode workload follows the cudnn-frontend PR #797 "Add experimental causal
+conv1d decode update" description (state ``[S, D, W-1]``, ``state_indices`` drawn without
+repeats).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class TrainShape:
+    """A fwd+bwd workload: x, dy are bf16 [B, T, D]; w is [D, W]; bias fp32 [D] or absent."""
+
+    name: str
+    B: int
+    T: int
+    D: int
+    W: int
+    bias: bool
+    seed: int
+
+
+@dataclass(frozen=True)
+class DecodeShape:
+    """A one-token decode workload: x bf16 [N, D], state bf16 [S, D, W-1], indices [N]."""
+
+    name: str
+    N: int
+    S: int
+    D: int
+    W: int
+    bias: bool
+    seed: int
+
+
+# The five workloads this implementation is checked and measured on.
+TINY = TrainShape("B1_T256_D512_W4_bias", 1, 256, 512, 4, True, 0)
+MEDIUM = TrainShape("B8_T1024_D4096_W4_nobias", 8, 1024, 4096, 4, False, 1)
+HEADLINE = TrainShape("B8_T8192_D4096_W4_bias", 8, 8192, 4096, 4, True, 2)
+RAGGED = TrainShape("B3_T1000_D2000_W2_bias", 3, 1000, 2000, 2, True, 3)
+DECODE = DecodeShape("decode_N256_S512_D4096_W4_bias", 256, 512, 4096, 4, True, 4)
+
+TRAIN_SHAPES = (TINY, MEDIUM, HEADLINE, RAGGED)
+
+
+def _normal(g: torch.Generator, shape, var: float) -> torch.Tensor:
+    return torch.randn(*shape, generator=g, dtype=torch.float32) * math.sqrt(var)
+
+
+def train_inputs(
+    B: int,
+    T: int,
+    D: int,
+    W: int,
+    *,
+    bias: bool,
+    seed: int,
+    w_dtype: torch.dtype = torch.bfloat16,
+    x_var: float = 1.0,
+) -> dict:
+    """Host tensors for one fwd+bwd call: x, w, bias (or None), dy.
+
+    x, dy: bf16 [B, T, D] contiguous. w: [D, W] in ``w_dtype`` (bf16 or fp32), variance 1/W.
+    bias: fp32 [D], variance 0.1, or None.
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = _normal(g, (B, T, D), x_var).to(torch.bfloat16)
+    w = _normal(g, (D, W), 1.0 / W).to(w_dtype)
+    b = _normal(g, (D,), 0.1) if bias else None
+    dy = _normal(g, (B, T, D), 1.0).to(torch.bfloat16)
+    return {"x": x, "w": w, "bias": b, "dy": dy}
+
+
+def train_inputs_for(shape: TrainShape, **kw) -> dict:
+    return train_inputs(shape.B, shape.T, shape.D, shape.W, bias=shape.bias, seed=shape.seed, **kw)
+
+
+def decode_inputs(
+    N: int,
+    S: int,
+    D: int,
+    W: int,
+    *,
+    bias: bool,
+    seed: int,
+    w_dtype: torch.dtype = torch.bfloat16,
+    identity: bool = False,
+) -> dict:
+    """Host tensors for one decode update: x, state, state_indices, w, bias.
+
+    x: bf16 [N, D]; state: bf16 [S, D, W-1]; state_indices: int32 [N], the first N entries of
+    a random permutation of range(S) (distinct, all valid), or None when ``identity``.
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = _normal(g, (N, D), 1.0).to(torch.bfloat16)
+    state = _normal(g, (S, D, W - 1), 1.0).to(torch.bfloat16)
+    perm = torch.randperm(S, generator=g)[:N].to(torch.int32)
+    w = _normal(g, (D, W), 1.0 / W).to(w_dtype)
+    b = _normal(g, (D,), 0.1) if bias else None
+    return {"x": x, "state": state, "state_indices": None if identity else perm, "w": w, "bias": b}
+
+
+def decode_inputs_for(shape: DecodeShape, **kw) -> dict:
+    return decode_inputs(shape.N, shape.S, shape.D, shape.W, bias=shape.bias, seed=shape.seed, **kw)

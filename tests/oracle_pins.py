@@ -1,0 +1,407 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each check takes an ``oracle.Oracle`` and raises AssertionError when it disagrees. The test
+suite runs every check on the real oracle (tests/test_oracle_pins.py) and on copies of the
+oracle with a planted mistake (tests/test_oracle_mutants.py), where at least one check must
+fail. Nothing here retypes the oracle's formulas: the pins are a library convolution with
+autograd (float64 torch), finite differences, hand-worked fixtures, impulses, closed forms,
+exact invariants and torch's own bf16 cast.
+"""
+
+from __future__ import annotations
+
+import math
+from pathlib import Path
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+# ----------------------------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------------------------
+
+
+def _bf16_values(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
+    """Random values that are exactly bf16 (so that fp32 holds them and small shifts are exact)."""
+    a = torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32))
+    return a.to(torch.bfloat16).float().numpy()
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _dsilu(z):
+    s = _sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def _problem(seed, B, T, D, W, bias=True, wscale=None):
+    rng = np.random.default_rng(seed)
+    x = _bf16_values(rng, (B, T, D))
+    w = _bf16_values(rng, (D, W), wscale if wscale is not None else 1.0 / math.sqrt(W))
+    b = _bf16_values(rng, (D,), 0.3) if bias else None
+    dy = _bf16_values(rng, (B, T, D))
+    return x, w, b, dy
+
+
+def _torch_reference(x, w, b, dy):
+    """float64 torch: grouped conv1d (cross-correlation) with W-1 left zeros, SiLU, autograd."""
+    B, T, D = x.shape
+    W = w.shape[1]
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+    bt = torch.tensor(b, dtype=torch.float64, requires_grad=True) if b is not None else None
+    z = F.conv1d(xt.transpose(1, 2), wt[:, None, :], bt, padding=W - 1, groups=D)[..., :T]
+    y = F.silu(z).transpose(1, 2)
+    loss = (y * torch.tensor(dy, dtype=torch.float64)).sum()
+    loss.backward()
+    return (
+        y.detach().numpy(),
+        xt.grad.numpy(),
+        wt.grad.numpy(),
+        None if bt is None else bt.grad.numpy(),
+    )
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.abs(a - b)
+    bound = atol + rtol * np.abs(b)
+    worst = np.max(err - bound) if err.size else 0.0
+    assert worst <= 0.0, f"{what}: max err {np.max(err) if err.size else 0:.3e} exceeds rtol={rtol}, atol={atol}"
+
+
+def _read_fixture(name):
+    rows = []
+    for line in (GOLDEN / name).read_text().splitlines():
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        rows.append((key, [float(v) for v in vals]))
+    return rows
+
+
+# ----------------------------------------------------------------------------------------------
+# checks
+# ----------------------------------------------------------------------------------------------
+
+
+def check_rounding_matches_torch(orc):
+    """RTNE to bf16 equals torch's fp32 -> bf16 cast on random values, exact ties, specials."""
+    rng = np.random.default_rng(11)
+    n = 200_000
+    rand = (rng.standard_normal(n) * np.exp2(rng.integers(-40, 40, n))).astype(np.float32)
+    pat = rng.integers(0, 0x7F80, 50_000).astype(np.uint32)
+    ties = ((pat << 16) | 0x8000).view(np.float32)
+    near = np.concatenate([((pat << 16) | 0x7FFF).view(np.float32), ((pat << 16) | 0x8001).view(np.float32)])
+    specials = np.array(
+        [0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45, 1.1754942e-38, 3.4028235e38, -3.4028235e38, 1.0, -1.0],
+        dtype=np.float32,
+    )
+    a = np.concatenate([rand, ties, -ties, near, specials])
+    want = torch.from_numpy(a.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for prec in ("f64", "f32"):
+        got = orc.round_bf16(a.astype(np.float64) if prec == "f64" else a, precision=prec)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"{prec} rounding differs from torch at {a[bad[:5]]}: {got[bad[:5]]} vs {want[bad[:5]]}"
+    nan = orc.round_bf16(np.array([np.nan]), precision="f64")
+    assert (nan[0] & 0x7F80) == 0x7F80 and (nan[0] & 0x007F) != 0, "NaN must stay NaN"
+
+
+def check_rounding_from_double_is_direct(orc):
+    """A double just above a bf16 tie rounds up: rounding must not pass through fp32 first."""
+    lo = 1.0  # bf16 neighbours 1.0 and 1.0078125; tie at 1.00390625
+    v = np.array([1.00390625 + 2.0**-40, 1.00390625 - 2.0**-40, 1.00390625, 1.01171875])
+    got = orc.round_bf16(v, precision="f64")
+    want = np.array([0x3F81, 0x3F80, 0x3F80, 0x3F82], dtype=np.uint16)  # last: tie 1.0117 -> even 1.015625
+    assert lo == 1.0 and np.array_equal(got, want), f"{got} vs {want}"
+
+
+def check_worked_example(orc):
+    """Hand-worked W=3 example (tests/golden/worked_example_w3.txt): z exact, y, dx, dw, dbias."""
+    rows = _read_fixture("worked_example_w3.txt")
+    kv = {}
+    cases = []
+    for key, vals in rows:
+        if key == "case":
+            cases.append({"t": int(vals[0])})
+        elif cases:
+            cases[-1][key] = vals
+        else:
+            kv[key] = vals
+    W = int(kv["W"][0])
+    x = np.array(kv["x"], np.float32).reshape(1, -1, 1)
+    T = x.shape[1]
+    w = np.array(kv["w"], np.float32).reshape(1, W)
+    b = np.array(kv["bias"], np.float32)
+    zwant = np.array(kv["z"])
+    z, y = orc.fwd(x, w, b)
+    assert np.array_equal(z[0, :, 0], zwant), f"z {z[0, :, 0]} vs {zwant}"
+    _close(y[0, :, 0], zwant * _sigmoid(zwant), 1e-14, what="worked y")
+    for c in cases:
+        dy = np.zeros_like(x)
+        dy[0, c["t"], 0] = 1.0
+        g = _dsilu(zwant[c["t"]])
+        dx, dw, db = orc.bwd(x, dy, w, b)
+        _close(dx[0, :, 0], np.array(c["dx_over_g"]) * g, 1e-14, 1e-300, what=f"worked dx t={c['t']}")
+        _close(dw[0], np.array(c["dw_over_g"]) * g, 1e-14, 1e-300, what=f"worked dw t={c['t']}")
+        _close(db, [g], 1e-14, what=f"worked dbias t={c['t']}")
+    assert T == 5
+
+
+def check_impulse(orc):
+    """x = 1 at one (b, t0, d), bias 0: z[t0+k] = w[d, W-1-k] for k < W, exactly, else 0."""
+    for W in (1, 2, 3, 4):
+        rng = np.random.default_rng(20 + W)
+        B, T, D = 2, 12, 3
+        w = _bf16_values(rng, (D, W))
+        x = np.zeros((B, T, D), np.float32)
+        b0, t0, d0 = 1, 5, 2
+        x[b0, t0, d0] = 1.0
+        z, _ = orc.fwd(x, w, None)
+        want = np.zeros((B, T, D))
+        for k in range(W):
+            want[b0, t0 + k, d0] = w[d0, W - 1 - k]
+        assert np.array_equal(z, want), f"impulse W={W}"
+
+
+def check_w1_closed_form(orc):
+    """W = 1 is pointwise: y = silu(w[d,0] * x + bias[d])."""
+    x, w, b, _ = _problem(3, 2, 17, 6, 1)
+    z, y = orc.fwd(x, w, b)
+    zz = b.astype(np.float64) + w[:, 0].astype(np.float64) * x.astype(np.float64)
+    assert np.array_equal(z, zz), "W=1 z"
+    _close(y, zz * _sigmoid(zz), 1e-14, 1e-300, what="W=1 y")
+
+
+def check_constant_input(orc):
+    """x = c everywhere: z[t] = bias + c * (sum of the taps that see rows >= 0)."""
+    for W in (2, 3, 4):
+        rng = np.random.default_rng(30 + W)
+        B, T, D = 1, 9, 4
+        c = 0.75
+        x = np.full((B, T, D), c, np.float32)
+        w = _bf16_values(rng, (D, W))
+        b = _bf16_values(rng, (D,), 0.3)
+        z, _ = orc.fwd(x, w, b)
+        for t in range(T):
+            first = max(0, W - 1 - t)  # taps j with t-(W-1)+j >= 0
+            want = b.astype(np.float64) + c * w[:, first:].astype(np.float64).sum(axis=1)
+            _close(z[0, t], want, 1e-14, 1e-15, what=f"constant W={W} t={t}")
+
+
+def check_torch_conv1d(orc):
+    """float64 torch conv1d(groups=D, left pad W-1) + SiLU + autograd: y, dx, dw, dbias."""
+    for W in (1, 2, 3, 4):
+        for bias in (True, False):
+            x, w, b, dy = _problem(40 + W, 2, 37, 5, W, bias)
+            y_t, dx_t, dw_t, db_t = _torch_reference(x, w, b, dy)
+            _, y = orc.fwd(x, w, b)
+            dx, dw, db = orc.bwd(x, dy, w, b)
+            _close(y, y_t, 1e-12, 1e-14, what=f"torch y W={W}")
+            _close(dx, dx_t, 1e-12, 1e-13, what=f"torch dx W={W}")
+            _close(dw, dw_t, 1e-12, 1e-12, what=f"torch dw W={W}")
+            if bias:
+                _close(db, db_t, 1e-12, 1e-12, what=f"torch dbias W={W}")
+            else:
+                # with no bias the returned dbias is still sum(g): compare against torch's
+                # gradient of a zero bias
+                _, _, _, db0 = _torch_reference(x, w, np.zeros(x.shape[2], np.float32), dy)
+                _close(db, db0, 1e-12, 1e-12, what=f"torch dbias (no bias) W={W}")
+
+
+def check_finite_differences(orc):
+    """Central differences of L = sum(dy * y) in fp64, Richardson-extrapolated (h = 2^-10 and
+    2^-11: exact shifts of bf16 values), against the analytic dx, dw, dbias."""
+    h = 2.0**-10
+
+    def fd(loss, arr, i):
+        def central(hh):
+            p, m = arr.copy(), arr.copy()
+            p[i] += hh
+            m[i] -= hh
+            return (loss(p) - loss(m)) / (2 * hh)
+
+        return (4 * central(h / 2) - central(h)) / 3
+
+    for W in (1, 2, 3, 4):
+        for bias in (True, False):
+            x, w, b, dy = _problem(50 + W, 2, 7, 3, W, bias)
+            dx, dw, db = orc.bwd(x, dy, w, b)
+
+            def loss(xx, ww, bb):
+                _, y = orc.fwd(xx, ww, bb)
+                return float(np.sum(dy.astype(np.float64) * y))
+
+            fdx = np.array([fd(lambda a: loss(a, w, b), x, i) for i in np.ndindex(x.shape)]).reshape(x.shape)
+            _close(dx, fdx, 1e-6, 1e-8, what=f"FD dx W={W}")
+            fdw = np.array([fd(lambda a: loss(x, a, b), w, i) for i in np.ndindex(w.shape)]).reshape(w.shape)
+            _close(dw, fdw, 1e-6, 1e-8, what=f"FD dw W={W}")
+            if bias:
+                fdb = np.array([fd(lambda a: loss(x, w, a), b, (i,)) for i in range(b.shape[0])])
+                _close(db, fdb, 1e-6, 1e-8, what=f"FD dbias W={W}")
+
+
+def check_w_padding(orc):
+    """W = 2 equals W = 4 with zero taps on the oldest side, exactly (y, dx; dw[:, 2:])."""
+    x, w2, b, dy = _problem(60, 2, 19, 5, 2, True)
+    w4 = np.zeros((5, 4), np.float32)
+    w4[:, 2:] = w2
+    _, y2 = orc.fwd(x, w2, b)
+    _, y4 = orc.fwd(x, w4, b)
+    assert np.array_equal(y2, y4), "padded y"
+    dx2, dw2, db2 = orc.bwd(x, dy, w2, b)
+    dx4, dw4, db4 = orc.bwd(x, dy, w4, b)
+    assert np.array_equal(dx2, dx4), "padded dx"
+    assert np.array_equal(dw2, dw4[:, 2:]), "padded dw"
+    assert np.array_equal(db2, db4), "padded dbias"
+
+
+def check_dbias_is_dw_of_unit_input(orc):
+    """With W = 1 and x = 1 everywhere, dw[:, 0] = sum g * 1 = dbias, exactly."""
+    rng = np.random.default_rng(70)
+    B, T, D = 2, 11, 4
+    x = np.ones((B, T, D), np.float32)
+    w = _bf16_values(rng, (D, 1))
+    b = _bf16_values(rng, (D,), 0.3)
+    dy = _bf16_values(rng, (B, T, D))
+    _, dw, db = orc.bwd(x, dy, w, b)
+    assert np.array_equal(dw[:, 0], db), "dbias vs dw with unit input"
+
+
+def check_channel_and_batch_independence(orc):
+    """Permuting channels permutes every output exactly; each batch row stands alone."""
+    x, w, b, dy = _problem(80, 3, 13, 6, 4, True)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    _, y = orc.fwd(x, w, b)
+    dx, dw, db = orc.bwd(x, dy, w, b)
+    _, yp = orc.fwd(x[:, :, perm], w[perm], b[perm])
+    dxp, dwp, dbp = orc.bwd(x[:, :, perm], dy[:, :, perm], w[perm], b[perm])
+    assert np.array_equal(yp, y[:, :, perm]) and np.array_equal(dxp, dx[:, :, perm])
+    assert np.array_equal(dwp, dw[perm]) and np.array_equal(dbp, db[perm])
+    dw_sum = np.zeros_like(dw)
+    for bi in range(3):
+        _, y1 = orc.fwd(x[bi : bi + 1], w, b)
+        dx1, dw1, _ = orc.bwd(x[bi : bi + 1], dy[bi : bi + 1], w, b)
+        assert np.array_equal(y1[0], y[bi]) and np.array_equal(dx1[0], dx[bi]), f"batch row {bi}"
+        dw_sum += dw1
+    _close(dw, dw_sum, 1e-12, 1e-12, what="dw = sum over batch rows")
+
+
+def check_decode_equals_forward(orc):
+    """Token-by-token decode from a zero state reproduces the forward bitwise; the final state
+    holds the last W-1 inputs (zero-filled when T < W-1); untouched slots stay as they were."""
+    for W in (1, 2, 3, 4):
+        for T in (7, 2):
+            x, w, b, _ = _problem(90 + W + T, 3, T, 5, W, True)
+            _, yf = orc.fwd(x, w, b)
+            S = 5
+            idx = np.array([3, 0, 4], np.int32)
+            rng = np.random.default_rng(7)
+            state = np.zeros((S, 5, W - 1), np.float32)
+            other = _bf16_values(rng, (5, W - 1))
+            state[1] = other  # a slot no row touches
+            for t in range(T):
+                ok, y, state = orc.update(x[:, t, :], state, idx, w, b)
+                assert ok, "valid indices rejected"
+                assert np.array_equal(y, yf[:, t, :]), f"decode != forward at W={W} t={t}"
+            for r, s in enumerate(idx):
+                hist = np.zeros((W - 1, 5), np.float32)
+                for j in range(W - 1):
+                    tt = T - (W - 1) + j
+                    if tt >= 0:
+                        hist[j] = x[r, tt]
+                assert np.array_equal(state[s], hist.T), f"final state W={W} T={T} row {r}"
+            assert np.array_equal(state[1], other) and not np.any(state[2]), "untouched slots changed"
+
+
+def check_decode_worked_example(orc):
+    """Hand-worked decode (tests/golden/worked_example_decode_w4.txt)."""
+    kv = dict(_read_fixture("worked_example_decode_w4.txt"))
+    W = int(kv["W"][0])
+    state = np.array(kv["state"], np.float32).reshape(1, 1, W - 1)
+    x = np.array(kv["x"], np.float32).reshape(1, 1)
+    w = np.array(kv["w"], np.float32).reshape(1, W)
+    ok, y, st = orc.update(x, state, None, w, None)
+    z = kv["z"][0]
+    assert ok
+    _close(y[0, 0], z * _sigmoid(z), 1e-14, what="decode worked y")
+    assert np.array_equal(st[0, 0], np.array(kv["new_state"], np.float32)), f"state {st[0, 0]}"
+
+
+def check_decode_index_validation(orc):
+    """Indices outside [-1, S) or repeated make the call fail and change nothing; -1 rows give
+    zero output and touch no slot; NULL indices are the identity and need N <= S."""
+    N, S, D, W = 4, 6, 3, 4
+    rng = np.random.default_rng(100)
+    x = _bf16_values(rng, (N, D))
+    w = _bf16_values(rng, (D, W))
+    b = _bf16_values(rng, (D,), 0.3)
+    state = _bf16_values(rng, (S, D, W - 1))
+    for bad in ([0, 1, -2, 3], [0, 1, 6, 3], [0, 5, 2, 5], [7, 0, 1, 2], [-1, -3, 0, 1]):
+        ok, y, st = orc.update(x, state, np.array(bad, np.int32), w, b)
+        assert not ok and y is None and np.array_equal(st, state), f"invalid {bad} accepted"
+    ok, y, st = orc.update(x, state, np.array([2, -1, 5, -1], np.int32), w, b)
+    assert ok
+    assert not np.any(y[1]) and not np.any(y[3]), "padding rows must output 0"
+    for s in (0, 1, 3, 4):
+        assert np.array_equal(st[s], state[s]), f"slot {s} touched"
+    assert not np.array_equal(st[2], state[2]) and not np.array_equal(st[5], state[5])
+    ok, y, st = orc.update(x, state, None, w, b)
+    assert ok and np.array_equal(st[4:], state[4:]) and not np.array_equal(st[0], state[0])
+    ok, _, _ = orc.update(_bf16_values(rng, (S + 1, D)), state, None, w, b)
+    assert not ok, "identity mapping with N > S accepted"
+
+
+def check_points_match_full(orc):
+    """The sampled entry points agree exactly with the full ones."""
+    x, w, b, dy = _problem(110, 2, 23, 7, 3, True)
+    _, y = orc.fwd(x, w, b)
+    dx, dw, db = orc.bwd(x, dy, w, b)
+    pb, pt, pd = np.meshgrid(np.arange(2), np.arange(23), np.arange(7), indexing="ij")
+    pb, pt, pd = pb.ravel(), pt.ravel(), pd.ravel()
+    assert np.array_equal(orc.fwd_points(x, w, b, pb, pt, pd), y[pb, pt, pd])
+    assert np.array_equal(orc.dx_points(x, dy, w, b, pb, pt, pd), dx[pb, pt, pd])
+    dwc, dbc = orc.dw_channels(x, dy, w, b, np.arange(7)[::-1])
+    assert np.array_equal(dwc, dw[::-1]) and np.array_equal(dbc, db[::-1])
+
+
+def check_f32_close_to_f64(orc):
+    """The fp32 build agrees with the fp64 build far inside the parity tolerances."""
+    x, w, b, dy = _problem(120, 2, 64, 16, 4, True)
+    _, y64 = orc.fwd(x, w, b, precision="f64")
+    _, y32 = orc.fwd(x, w, b, precision="f32")
+    dx64, dw64, db64 = orc.bwd(x, dy, w, b, precision="f64")
+    dx32, dw32, db32 = orc.bwd(x, dy, w, b, precision="f32")
+    _close(y32, y64, 1e-5, 1e-6, what="f32 y")
+    _close(dx32, dx64, 1e-5, 1e-6, what="f32 dx")
+    _close(dw32, dw64, 1e-5, 1e-5, what="f32 dw")
+    _close(db32, db64, 1e-5, 1e-5, what="f32 dbias")
+
+
+ALL_CHECKS = [
+    check_rounding_matches_torch,
+    check_rounding_from_double_is_direct,
+    check_worked_example,
+    check_impulse,
+    check_w1_closed_form,
+    check_constant_input,
+    check_torch_conv1d,
+    check_finite_differences,
+    check_w_padding,
+    check_dbias_is_dw_of_unit_input,
+    check_channel_and_batch_independence,
+    check_decode_equals_forward,
+    check_decode_worked_example,
+    check_decode_index_validation,
+    check_points_match_full,
+    check_f32_close_to_f64,
+]

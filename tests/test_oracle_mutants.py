@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check a pin catches each.
+
+Every mutant is an edit of the oracle's C source: a dropped term, a flipped sign, a wrong or
+transposed index, a wrong padding rule, a missing validity check, a wrong rounding rule. For
+each, at least one of the pins in oracle_pins.py must fail.
+"""
+
+import os
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+import oracle
+
+# (name, old text, new text): the first occurrence of `old` is replaced.
+MUTANTS = [
+    ("tap_order_reversed", "xval(x, T, D, b, t - (W - 1) + j, d);\n    return z;", "xval(x, T, D, b, t - j, d);\n    return z;"),
+    ("bias_dropped", "real z = bias ? (real)bias[d] : (real)0;\n    for (int j = 0; j < W; ++j)", "real z = 0;\n    for (int j = 0; j < W; ++j)"),
+    ("sigmoid_sign", "r_exp(-z)", "r_exp(z)"),
+    ("dsilu_sign", "s * ((real)1 + z * ((real)1 - s))", "s * ((real)1 - z * ((real)1 - s))"),
+    ("dsilu_dy_dropped", "return (real)dy[(b * T + t) * D + d] * s *", "return s *"),
+    ("dx_index", "g_at(x, dy, T, D, w, W, bias, b, u + (W - 1) - j, d)", "g_at(x, dy, T, D, w, W, bias, b, u + j, d)"),
+    ("dx_tap_transposed", "acc = acc + (real)w[d * W + j] * g_at", "acc = acc + (real)w[d * W + (W - 1 - j)] * g_at"),
+    ("dw_index", "* xval(x, T, D, b, t - (W - 1) + j, d);\n    return acc;", "* xval(x, T, D, b, t - j, d);\n    return acc;"),
+    ("dbias_skips_head", "for (int64_t t = 0; t < T; ++t) acc = acc + g_at", "for (int64_t t = W - 1; t < T; ++t) acc = acc + g_at"),
+    ("replicate_left_pad", "if (t < 0 || t >= T) return 0;\n    return (real)x", "if (t >= T) return 0;\n    if (t < 0) t = 0;\n    return (real)x"),
+    ("g_not_zero_past_T", "if (t < 0 || t >= T) return 0;\n    real z", "if (t < 0) return 0;\n    if (t >= T) t = T - 1;\n    real z"),
+    ("decode_taps_reversed", "(real)w[d * W + j] * (real)st[j]", "(real)w[d * W + (L - 1 - j)] * (real)st[j]"),
+    ("decode_new_token_tap", "(real)w[d * W + (W - 1)] * (real)x[n * D + d]", "(real)w[d * W + 0] * (real)x[n * D + d]"),
+    ("decode_shift_direction", "for (int64_t j = 0; j + 1 < L; ++j) st[j] = st[j + 1];\n            if (L > 0) st[L - 1] = x[n * D + d];", "for (int64_t j = L - 1; j > 0; --j) st[j] = st[j - 1];\n            if (L > 0) st[0] = x[n * D + d];"),
+    ("decode_no_duplicate_check", "if (idx[n] >= 0 && idx[n] == idx[m]) return 1;", "(void)m;"),
+    ("decode_range_off_by_one", "idx[n] >= S) return 1;", "idx[n] > S) return 1;"),
+    ("decode_padding_output", "y_out[n * D + d] = 0;", "y_out[n * D + d] = (real)x[n * D + d];"),
+    ("round_half_away", "nearbyint(a / q)", "floor(a / q + 0.5)"),
+    ("round_truncate", "nearbyint(a / q)", "trunc(a / q)"),
+]
+
+
+_CHILD = r"""
+import sys
+from pathlib import Path
+import oracle
+from oracle_pins import ALL_CHECKS
+name, workdir = sys.argv[1], Path(sys.argv[2])
+src = Path(workdir / "mutant.c").read_text()
+mutant = oracle.build_variant(src, workdir)
+for check in ALL_CHECKS:
+    try:
+        check(mutant)
+    except AssertionError as e:
+        print("CAUGHT", check.__name__, str(e)[:120], flush=True)
+        sys.exit(0)
+print("MISSED", name, flush=True)
+sys.exit(1)
+"""
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new, tmp_path):
+    """Each mutant runs in a child process: a planted indexing mistake may write out of bounds
+    and must not take the test process down with it."""
+    src = oracle.source_text()
+    assert old in src, f"mutant {name}: pattern not found in the oracle source"
+    (tmp_path / "mutant.c").write_text(src.replace(old, new, 1))
+    here = Path(__file__).resolve().parent
+    env = dict(os.environ, PYTHONPATH=os.pathsep.join([str(here.parent), str(here)]), OMP_NUM_THREADS="2")
+    r = subprocess.run(
+        [sys.executable, "-c", _CHILD, name, str(tmp_path)], capture_output=True, text=True, env=env, timeout=600
+    )
+    assert "CAUGHT" in r.stdout, f"no pin caught the planted mistake {name}: rc={r.returncode} {r.stdout[-400:]} {r.stderr[-400:]}"
