@@ -1,0 +1,316 @@
+"""Python binding of libcconv.so: the depthwise causal short convolution + SiLU on MI355X.
+
+Argument marshalling only. Every function here checks that its torch tensors are device
+tensors of the dtype and layout the C ABI expects, allocates outputs with ``torch.empty``
+where the caller passed none, and calls the function of the same name in ``include/cconv.h``
+on the current torch stream. All arithmetic runs in the HIP kernels. There is no fallback:
+if the library is missing and cannot be built, or a call returns an error status, a
+``CconvError`` is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import threading
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "CconvError",
+    "Config",
+    "lib",
+    "cconv_fwd",
+    "cconv_bwd",
+    "cconv_bwd_workspace_bytes",
+    "cconv_update",
+    "cconv_default_config",
+    "cconv_status_string",
+    "cconv_version",
+    "STATUS",
+]
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libcconv.so"
+ROOFLINE_LIB_PATH = _PKG / "libcconv_roofline.so"
+
+STATUS = {
+    0: "CCONV_OK",
+    1: "CCONV_ERR_NULL_POINTER",
+    2: "CCONV_ERR_BAD_SHAPE",
+    3: "CCONV_ERR_BAD_STRIDE",
+    4: "CCONV_ERR_UNSUPPORTED_DTYPE",
+    5: "CCONV_ERR_MISALIGNED",
+    6: "CCONV_ERR_ALIASING",
+    7: "CCONV_ERR_WORKSPACE",
+    8: "CCONV_ERR_INDEX",
+    9: "CCONV_ERR_LAUNCH",
+    10: "CCONV_ERR_BAD_CONFIG",
+}
+BF16, F32 = 0, 1
+
+
+class Config(ctypes.Structure):
+    """cconv_config_t: vec, rows_per_group, waves_per_block, seg_rows."""
+
+    _fields_ = [
+        ("vec", ctypes.c_int),
+        ("rows_per_group", ctypes.c_int),
+        ("waves_per_block", ctypes.c_int),
+        ("seg_rows", ctypes.c_int64),
+    ]
+
+    def __repr__(self):
+        return (
+            f"Config(vec={self.vec}, rows_per_group={self.rows_per_group}, "
+            f"waves_per_block={self.waves_per_block}, seg_rows={self.seg_rows})"
+        )
+
+
+class CconvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({cconv_status_string(status)})")
+
+
+_lock = threading.Lock()
+_lib = None
+_roof = None
+
+
+def _declare(L):
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.cconv_fwd.argtypes = [p, i64, i64, p, i32, p, p, i64, i64, i64, i32, p]
+    L.cconv_fwd.restype = i32
+    L.cconv_fwd_config.argtypes = [p, i64, i64, p, i32, p, p, i64, i64, i64, i32, ctypes.POINTER(Config), p]
+    L.cconv_fwd_config.restype = i32
+    L.cconv_bwd_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    L.cconv_bwd_workspace_bytes.restype = sz
+    L.cconv_bwd_workspace_bytes_config.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Config)]
+    L.cconv_bwd_workspace_bytes_config.restype = sz
+    bwd = [p, i64, i64, p, i64, i64, p, i32, p, p, p, i32, p, p, sz, i64, i64, i64, i32]
+    L.cconv_bwd.argtypes = bwd + [p]
+    L.cconv_bwd.restype = i32
+    L.cconv_bwd_config.argtypes = bwd + [ctypes.POINTER(Config), p]
+    L.cconv_bwd_config.restype = i32
+    L.cconv_update.argtypes = [p, i64, p, i64, p, p, i32, p, p, i64, i64, i32, p, p]
+    L.cconv_update.restype = i32
+    L.cconv_default_config.argtypes = [i32, i64, i64, i64, i32, ctypes.POINTER(Config)]
+    L.cconv_default_config.restype = i32
+    L.cconv_status_string.argtypes = [i32]
+    L.cconv_status_string.restype = ctypes.c_char_p
+    L.cconv_version.argtypes = []
+    L.cconv_version.restype = ctypes.c_char_p
+    return L
+
+
+def _ensure_built(path: Path):
+    if not path.exists():
+        from . import _build
+
+        _build.build()
+    if not path.exists():
+        raise CconvError(9, f"{path.name} is not built and could not be built")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libcconv.so (built in-tree on first use if absent)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            _ensure_built(LIB_PATH)
+            _lib = _declare(ctypes.CDLL(str(LIB_PATH)))
+        return _lib
+
+
+def roofline_lib() -> ctypes.CDLL:
+    """The loaded libcconv_roofline.so (flat-copy kernels for the bandwidth roofline)."""
+    global _roof
+    with _lock:
+        if _roof is None:
+            _ensure_built(ROOFLINE_LIB_PATH)
+            L = ctypes.CDLL(str(ROOFLINE_LIB_PATH))
+            p = ctypes.c_void_p
+            L.cconv_roofline_copy.argtypes = [ctypes.c_int, p, p, p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, p]
+            L.cconv_roofline_copy.restype = ctypes.c_int
+            _roof = L
+        return _roof
+
+
+def cconv_status_string(status: int) -> str:
+    return lib().cconv_status_string(int(status)).decode()
+
+
+def cconv_version() -> str:
+    return lib().cconv_version().decode()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+
+
+def _wdt(t: torch.Tensor, name: str) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"{name} must be bf16 or fp32 (got {t.dtype})")
+
+
+def _act(t: torch.Tensor, name: str):
+    _dev(t, name)
+    if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be bf16 [B, T, D] with unit channel stride")
+    return t.stride(0), t.stride(1)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise CconvError(status, where)
+
+
+def cconv_default_config(which: str, B: int, T: int, D: int, W: int) -> Config:
+    cfg = Config()
+    _check(lib().cconv_default_config(0 if which == "fwd" else 1, B, T, D, W, ctypes.byref(cfg)), "cconv_default_config")
+    return cfg
+
+
+def cconv_fwd(x, w, bias=None, *, y=None, config: Optional[Config] = None, stream=None):
+    """y = silu(causal depthwise conv(x, w) + bias). x bf16 [B, T, D]; w [D, W]; bias fp32 [D]."""
+    sb, st = _act(x, "x")
+    B, T, D = x.shape
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    if y is None:
+        y = torch.empty((B, T, D), dtype=torch.bfloat16, device=x.device)
+    elif y.dtype != torch.bfloat16 or tuple(y.shape) != (B, T, D) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous bf16 [B, T, D] tensor")
+    L = lib()
+    args = (_ptr(x), sb, st, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(y), B, T, D, W)
+    if config is None:
+        _check(L.cconv_fwd(*args, _stream(stream)), "cconv_fwd")
+    else:
+        _check(L.cconv_fwd_config(*args, ctypes.byref(config), _stream(stream)), "cconv_fwd_config")
+    return y
+
+
+def cconv_bwd_workspace_bytes(B: int, T: int, D: int, W: int, config: Optional[Config] = None) -> int:
+    if config is None:
+        return int(lib().cconv_bwd_workspace_bytes(B, T, D, W))
+    return int(lib().cconv_bwd_workspace_bytes_config(B, T, D, W, ctypes.byref(config)))
+
+
+def cconv_bwd(
+    x,
+    dy,
+    w,
+    bias=None,
+    *,
+    dx=None,
+    dw=None,
+    dbias=None,
+    want_dbias: bool = True,
+    dw_dtype: Optional[torch.dtype] = None,
+    workspace=None,
+    config: Optional[Config] = None,
+    stream=None,
+):
+    """(dx, dw, dbias) of y = silu(conv(x, w) + bias) for upstream gradient dy.
+
+    dw is returned in ``dw_dtype`` (default: w's dtype); dbias is fp32 (None if not wanted).
+    """
+    sb, st = _act(x, "x")
+    dsb, dst = _act(dy, "dy")
+    B, T, D = x.shape
+    if tuple(dy.shape) != (B, T, D):
+        raise ValueError("dy must have x's shape")
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((B, T, D), dtype=torch.bfloat16, device=dev)
+    if dw is None:
+        dw = torch.empty((D, W), dtype=dw_dtype or w.dtype, device=dev)
+    if want_dbias and dbias is None:
+        dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    need = cconv_bwd_workspace_bytes(B, T, D, W, config)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    L = lib()
+    args = (
+        _ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(dx), _ptr(dw),
+        _wdt(dw, "dw"), _ptr(dbias), _ptr(workspace), ws_bytes, B, T, D, W,
+    )
+    if config is None:
+        _check(L.cconv_bwd(*args, _stream(stream)), "cconv_bwd")
+    else:
+        _check(L.cconv_bwd_config(*args, ctypes.byref(config), _stream(stream)), "cconv_bwd_config")
+    return dx, dw, dbias
+
+
+def cconv_update(x, state, state_indices, w, bias=None, *, y=None, status=None, stream=None):
+    """One decode step: returns (y, status). state is updated in place.
+
+    x bf16 [N, D] (row stride >= D); state bf16 [S, D, W-1]; state_indices int32 [N] or None;
+    status: an int32 device tensor of one element (allocated if None); it receives
+    CCONV_OK (0) or CCONV_ERR_INDEX (8) on the device.
+    """
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be bf16 [N, D] with unit channel stride")
+    N, D = x.shape
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    _dev(state, "state")
+    if state.dtype != torch.bfloat16 or state.dim() != 3 or state.shape[1:] != (D, W - 1) or not state.is_contiguous():
+        raise ValueError("state must be a contiguous bf16 [S, D, W-1] tensor")
+    S = state.shape[0]
+    if state_indices is not None:
+        _dev(state_indices, "state_indices")
+        if state_indices.dtype != torch.int32 or state_indices.shape != (N,) or not state_indices.is_contiguous():
+            raise ValueError("state_indices must be a contiguous int32 [N] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    if y is None:
+        y = torch.empty((N, D), dtype=torch.bfloat16, device=x.device)
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=x.device)
+    _check(
+        lib().cconv_update(
+            _ptr(x), x.stride(0) if N > 0 else D, _ptr(state), S, _ptr(state_indices), _ptr(w), _wdt(w, "w"),
+            _ptr(bias), _ptr(y), N, D, W, _ptr(status), _stream(stream),
+        ),
+        "cconv_update",
+    )
+    return y, status

@@ -1,0 +1,354 @@
+// cconv_api.hip -- the C ABI declared in include/cconv.h: host-side validation, launch
+// planning and dispatch. Nothing here allocates device memory, synchronises, or reads device
+// memory; every check that can fail happens before the first launch, so an error leaves all
+// outputs untouched.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/cconv.h"
+#include "cconv_internal.hpp"
+
+using cconv::Plan;
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 40;        // any one size or stride
+constexpr int64_t kMaxDecodeRows = int64_t(1) << 24;  // N
+constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices (LDS bit set)
+constexpr int64_t kTargetWaves = 4096;  // 16 waves per CU over 256 CUs: one full round
+constexpr int64_t kMinSeg = 64;         // shorter segments re-read too large a share of rows
+constexpr int64_t kUpdateTargetBlocks = 1024;
+
+struct Span {
+    uintptr_t lo, hi;
+};
+
+Span span(const void* p, __int128 bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Bytes spanned by a [B, T, D] tensor with strides (sb, st, 1).
+__int128 extent3(int64_t B, int64_t T, int64_t D, int64_t sb, int64_t st, int esize) {
+    if (B == 0 || T == 0 || D == 0) return 0;
+    return (static_cast<__int128>(B - 1) * sb + static_cast<__int128>(T - 1) * st + D) * esize;
+}
+
+int esize(cconv_dtype_t t) { return t == CCONV_F32 ? 4 : 2; }
+bool dtype_ok(cconv_dtype_t t) { return t == CCONV_BF16 || t == CCONV_F32; }
+
+bool config_ok(const cconv_config_t& c, bool bwd) {
+    if (bwd ? !cconv::bwd_variant_exists(c.vec, c.rows_per_group)
+            : !cconv::fwd_variant_exists(c.vec, c.rows_per_group))
+        return false;
+    if (c.waves_per_block != 1 && c.waves_per_block != 2 && c.waves_per_block != 4 && c.waves_per_block != 8)
+        return false;
+    if (c.seg_rows < 8 || c.seg_rows > kMaxDim || c.seg_rows % c.rows_per_group != 0) return false;
+    return true;
+}
+
+cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) {
+    (void)W;
+    cconv_config_t c;
+    c.vec = 8;
+    c.rows_per_group = bwd ? 4 : 8;
+    c.waves_per_block = 4;
+    const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
+    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / kTargetWaves;
+    ts = std::max(kMinSeg, ts - ts % 8);
+    const int64_t tcap = ((std::max<int64_t>(T, 1) + 7) / 8) * 8;
+    c.seg_rows = std::min(ts, std::max<int64_t>(8, tcap));
+    return c;
+}
+
+bool make_plan(const cconv_config_t& c, int64_t B, int64_t T, int64_t D, Plan* p) {
+    p->vec = c.vec;
+    p->group = c.rows_per_group;
+    p->waves = c.waves_per_block;
+    p->seg_rows = c.seg_rows;
+    p->strips = (D + 64 * c.vec - 1) / (64 * c.vec);
+    p->segs = (T + c.seg_rows - 1) / c.seg_rows;
+    p->seg_groups = (p->segs + c.waves_per_block - 1) / c.waves_per_block;
+    const __int128 blocks = static_cast<__int128>(p->strips) * p->seg_groups * B;
+    if (blocks > INT32_MAX) return false;
+    p->blocks = static_cast<int64_t>(blocks);
+    p->partials = B * p->seg_groups;
+    return true;
+}
+
+// Checks shared by the forward and backward: shape, dtype, strides, alignment of x-like
+// inputs and of the taps/bias.
+cconv_status_t check_train_common(const void* w, cconv_dtype_t w_dtype, const float* bias, int64_t B,
+                                  int64_t T, int64_t D, int W) {
+    if (B < 0 || T < 0 || D < 0 || B > kMaxDim || T > kMaxDim || D > kMaxDim) return CCONV_ERR_BAD_SHAPE;
+    if (W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
+    if (D % 8 != 0) return CCONV_ERR_BAD_SHAPE;
+    if (!dtype_ok(w_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
+    if (!aligned(w, 16) || (bias && !aligned(bias, 16))) return CCONV_ERR_MISALIGNED;
+    return CCONV_OK;
+}
+
+cconv_status_t check_act(const void* p, int64_t sb, int64_t st, int64_t D) {
+    if (sb < 0 || st < D || sb > kMaxDim || st > kMaxDim) return CCONV_ERR_BAD_STRIDE;
+    if (sb % 8 != 0 || st % 8 != 0) return CCONV_ERR_BAD_STRIDE;
+    if (!aligned(p, 16)) return CCONV_ERR_MISALIGNED;
+    return CCONV_OK;
+}
+
+size_t bwd_workspace(const Plan& p, int64_t D, int W) {
+    return static_cast<size_t>(p.partials) * static_cast<size_t>(W + 1) * static_cast<size_t>(D) * sizeof(float);
+}
+
+cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
+                        const float* bias, void* y, int64_t B, int64_t T, int64_t D, int W,
+                        const cconv_config_t* cfg, cconv_stream_t stream) {
+    // a pointer may be NULL only when its tensor is empty
+    const bool act_empty = (B == 0 || T == 0 || D == 0);
+    if ((!x && !act_empty) || (!w && D > 0) || (!y && !act_empty)) return CCONV_ERR_NULL_POINTER;
+    cconv_status_t st = check_train_common(w, w_dtype, bias, B, T, D, W);
+    if (st != CCONV_OK) return st;
+    if ((st = check_act(x, x_sb, x_st, D)) != CCONV_OK) return st;
+    if (!aligned(y, 16)) return CCONV_ERR_MISALIGNED;
+    const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W);
+    if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
+    const Span sy = span(y, extent3(B, T, D, T * D, D, 2));
+    if (overlap(sy, span(x, extent3(B, T, D, x_sb, x_st, 2))) ||
+        overlap(sy, span(w, static_cast<__int128>(D) * W * esize(w_dtype))) ||
+        (bias && overlap(sy, span(bias, static_cast<__int128>(D) * 4))))
+        return CCONV_ERR_ALIASING;
+    Plan p;
+    if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
+    if (B == 0 || T == 0 || D == 0) return CCONV_OK;
+    cconv::FwdArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.x_sb = x_sb;
+    a.x_st = x_st;
+    a.w = w;
+    a.w_f32 = (w_dtype == CCONV_F32);
+    a.bias = bias;
+    a.y = static_cast<uint16_t*>(y);
+    a.B = B;
+    a.T = T;
+    a.D = D;
+    a.seg_rows = p.seg_rows;
+    a.strips = p.strips;
+    a.seg_groups = p.seg_groups;
+    return cconv::launch_fwd(p, W, a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? CCONV_OK
+                                                                                           : CCONV_ERR_LAUNCH;
+}
+
+cconv_status_t bwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb, int64_t dy_st,
+                        const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
+                        cconv_dtype_t dw_dtype, float* dbias, void* workspace, size_t workspace_bytes, int64_t B,
+                        int64_t T, int64_t D, int W, const cconv_config_t* cfg, cconv_stream_t stream) {
+    const bool act_empty = (B == 0 || T == 0 || D == 0);
+    if (((!x || !dy || !dx) && !act_empty) || ((!w || !dw) && D > 0)) return CCONV_ERR_NULL_POINTER;
+    cconv_status_t st = check_train_common(w, w_dtype, bias, B, T, D, W);
+    if (st != CCONV_OK) return st;
+    if (!dtype_ok(dw_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
+    if ((st = check_act(x, x_sb, x_st, D)) != CCONV_OK) return st;
+    if ((st = check_act(dy, dy_sb, dy_st, D)) != CCONV_OK) return st;
+    if (!aligned(dx, 16) || !aligned(dw, 16) || (dbias && !aligned(dbias, 16))) return CCONV_ERR_MISALIGNED;
+    const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W);
+    if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
+    Plan p;
+    if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
+    const size_t need = (B == 0 || T == 0 || D == 0) ? 0 : bwd_workspace(p, D, W);
+    if (need > 0 && (!workspace || !aligned(workspace, 16))) return workspace ? CCONV_ERR_MISALIGNED : CCONV_ERR_NULL_POINTER;
+
+    const Span in_x = span(x, extent3(B, T, D, x_sb, x_st, 2));
+    const Span in_dy = span(dy, extent3(B, T, D, dy_sb, dy_st, 2));
+    const Span in_w = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
+    const Span in_b = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
+    const Span o_dx = span(dx, extent3(B, T, D, T * D, D, 2));
+    const Span o_dw = span(dw, static_cast<__int128>(D) * W * esize(dw_dtype));
+    const Span o_db = dbias ? span(dbias, static_cast<__int128>(D) * 4) : Span{0, 0};
+    const Span o_ws = span(workspace, need);
+    const Span outs[4] = {o_dx, o_dw, o_db, o_ws};
+    const Span ins[4] = {in_x, in_dy, in_w, in_b};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlap(outs[i], ins[j])) return CCONV_ERR_ALIASING;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return CCONV_ERR_ALIASING;
+    }
+    if (workspace_bytes < need) return CCONV_ERR_WORKSPACE;
+    if (D == 0) return CCONV_OK;
+
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool empty = (B == 0 || T == 0);
+    if (!empty) {
+        cconv::BwdArgs a;
+        a.x = static_cast<const uint16_t*>(x);
+        a.x_sb = x_sb;
+        a.x_st = x_st;
+        a.dy = static_cast<const uint16_t*>(dy);
+        a.dy_sb = dy_sb;
+        a.dy_st = dy_st;
+        a.w = w;
+        a.w_f32 = (w_dtype == CCONV_F32);
+        a.bias = bias;
+        a.dx = static_cast<uint16_t*>(dx);
+        a.partial = static_cast<float*>(workspace);
+        a.B = B;
+        a.T = T;
+        a.D = D;
+        a.seg_rows = p.seg_rows;
+        a.strips = p.strips;
+        a.seg_groups = p.seg_groups;
+        if (cconv::launch_bwd(p, W, a, s) != hipSuccess) return CCONV_ERR_LAUNCH;
+    }
+    cconv::ReduceArgs r;
+    r.partial = static_cast<const float*>(workspace);
+    r.P = empty ? 0 : p.partials;
+    r.D = D;
+    r.W = W;
+    r.dw = dw;
+    r.dw_f32 = (dw_dtype == CCONV_F32);
+    r.dbias = dbias;
+    return cconv::launch_reduce(r, s) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+cconv_status_t cconv_fwd(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
+                         const float* bias, void* y, int64_t B, int64_t T, int64_t D, int W,
+                         cconv_stream_t stream) {
+    return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream);
+}
+
+cconv_status_t cconv_fwd_config(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
+                                const float* bias, void* y, int64_t B, int64_t T, int64_t D, int W,
+                                const cconv_config_t* cfg, cconv_stream_t stream) {
+    if (!cfg) return CCONV_ERR_NULL_POINTER;
+    return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, cfg, stream);
+}
+
+size_t cconv_bwd_workspace_bytes_config(int64_t B, int64_t T, int64_t D, int W, const cconv_config_t* cfg) {
+    if (B <= 0 || T <= 0 || D <= 0 || W < 1 || W > 4 || B > kMaxDim || T > kMaxDim || D > kMaxDim) return 0;
+    const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W);
+    if (!config_ok(c, true)) return 0;
+    Plan p;
+    if (!make_plan(c, B, T, D, &p)) return 0;
+    return bwd_workspace(p, D, W);
+}
+
+size_t cconv_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W) {
+    return cconv_bwd_workspace_bytes_config(B, T, D, W, nullptr);
+}
+
+cconv_status_t cconv_bwd(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb, int64_t dy_st,
+                         const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
+                         cconv_dtype_t dw_dtype, float* dbias, void* workspace, size_t workspace_bytes, int64_t B,
+                         int64_t T, int64_t D, int W, cconv_stream_t stream) {
+    return bwd_impl(x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias, workspace,
+                    workspace_bytes, B, T, D, W, nullptr, stream);
+}
+
+cconv_status_t cconv_bwd_config(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
+                                int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx,
+                                void* dw, cconv_dtype_t dw_dtype, float* dbias, void* workspace,
+                                size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int W,
+                                const cconv_config_t* cfg, cconv_stream_t stream) {
+    if (!cfg) return CCONV_ERR_NULL_POINTER;
+    return bwd_impl(x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias, workspace,
+                    workspace_bytes, B, T, D, W, cfg, stream);
+}
+
+cconv_status_t cconv_default_config(int which, int64_t B, int64_t T, int64_t D, int W, cconv_config_t* out) {
+    if (!out) return CCONV_ERR_NULL_POINTER;
+    if (which != 0 && which != 1) return CCONV_ERR_BAD_CONFIG;
+    if (B < 0 || T < 0 || D < 0 || W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
+    *out = default_config(which == 1, B, T, D, W);
+    return CCONV_OK;
+}
+
+cconv_status_t cconv_update(const void* x, int64_t x_ld, void* state, int64_t S, const int32_t* state_indices,
+                            const void* w, cconv_dtype_t w_dtype, const float* bias, void* y, int64_t N, int64_t D,
+                            int W, int32_t* status, cconv_stream_t stream) {
+    if (N < 0 || S < 0 || D < 0 || W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
+    if (((!x || !y) && N > 0 && D > 0) || (!w && D > 0) || (!state && S > 0 && D > 0 && W > 1))
+        return CCONV_ERR_NULL_POINTER;
+    if (N < 0 || S < 0 || D < 0 || N > kMaxDecodeRows || S > kMaxDim || D > kMaxDim) return CCONV_ERR_BAD_SHAPE;
+    if (W < 1 || W > 4 || D % 8 != 0) return CCONV_ERR_BAD_SHAPE;
+    if (state_indices && S > kMaxIndexedSlots) return CCONV_ERR_BAD_SHAPE;
+    if (!state_indices && N > S) return CCONV_ERR_BAD_SHAPE;
+    if (!dtype_ok(w_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
+    if (x_ld < D || x_ld > kMaxDim || x_ld % 8 != 0) return CCONV_ERR_BAD_STRIDE;
+    if (!aligned(x, 16) || !aligned(state, 16) || !aligned(w, 16) || !aligned(y, 16) ||
+        (bias && !aligned(bias, 16)) || (state_indices && !aligned(state_indices, 4)) ||
+        (status && !aligned(status, 4)))
+        return CCONV_ERR_MISALIGNED;
+    const int L = W - 1;
+    const Span in_x = span(x, N == 0 || D == 0 ? 0 : (static_cast<__int128>(N - 1) * x_ld + D) * 2);
+    const Span in_w = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
+    const Span in_b = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
+    const Span in_i = state_indices ? span(state_indices, static_cast<__int128>(N) * 4) : Span{0, 0};
+    const Span o_st = span(state, static_cast<__int128>(S) * D * L * 2);
+    const Span o_y = span(y, static_cast<__int128>(N) * D * 2);
+    const Span o_s = status ? span(status, 4) : Span{0, 0};
+    const Span outs[3] = {o_st, o_y, o_s};
+    const Span ins[4] = {in_x, in_w, in_b, in_i};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlap(outs[i], ins[j])) return CCONV_ERR_ALIASING;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return CCONV_ERR_ALIASING;
+    }
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (N == 0 || D == 0) {
+        if (status) return cconv::launch_status(status, CCONV_OK, s) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
+        return CCONV_OK;
+    }
+    const int64_t dv = D / 8;  // 8-channel vectors per row
+    const int threads = static_cast<int>(std::min<int64_t>(256, ((dv + 63) / 64) * 64));
+    const int64_t grid_x = (dv + threads - 1) / threads;
+    const int64_t rpb = std::max<int64_t>(1, (N * grid_x + kUpdateTargetBlocks - 1) / kUpdateTargetBlocks);
+    const int64_t grid_y = (N + rpb - 1) / rpb;
+    if (grid_x > INT32_MAX || grid_y > 65535) return CCONV_ERR_BAD_SHAPE;
+    const size_t lds = state_indices ? static_cast<size_t>((S + 31) / 32) * 4 : 0;
+    cconv::UpdateArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.x_ld = x_ld;
+    a.state = static_cast<uint16_t*>(state);
+    a.S = S;
+    a.idx = state_indices;
+    a.w = w;
+    a.w_f32 = (w_dtype == CCONV_F32);
+    a.bias = bias;
+    a.y = static_cast<uint16_t*>(y);
+    a.N = N;
+    a.D = D;
+    a.rows_per_block = rpb;
+    a.status = status;
+    return cconv::launch_update(W, a, threads, grid_x, grid_y, lds, s) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
+}
+
+const char* cconv_status_string(cconv_status_t status) {
+    switch (status) {
+        case CCONV_OK: return "ok";
+        case CCONV_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case CCONV_ERR_BAD_SHAPE: return "unsupported shape (negative size, W outside [1,4], D not a multiple of 8, or above a limit)";
+        case CCONV_ERR_BAD_STRIDE: return "unsupported stride (negative, row stride below D, or not a multiple of 8)";
+        case CCONV_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype (weights and dw must be bf16 or fp32)";
+        case CCONV_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, indices and status 4)";
+        case CCONV_ERR_ALIASING: return "an output overlaps an input or another output";
+        case CCONV_ERR_WORKSPACE: return "workspace smaller than cconv_bwd_workspace_bytes()";
+        case CCONV_ERR_INDEX: return "state_indices out of [-1, S) or repeated";
+        case CCONV_ERR_LAUNCH: return "kernel launch failed";
+        case CCONV_ERR_BAD_CONFIG: return "invalid launch configuration";
+    }
+    return "unknown status";
+}
+
+const char* cconv_version(void) { return "cconv 0.1.0 for gfx950, built with " __VERSION__; }
+
+}  // extern "C"

@@ -1,0 +1,273 @@
+// cconv_bwd.hip -- backward of the depthwise causal short convolution + SiLU on gfx950.
+//
+// Same decomposition as the forward (lane = VEC channels, wave = channel strip x time
+// segment x batch row). Each row recomputes z from the x ring (the forward is never re-run),
+// forms g = dy * s * (1 + z(1-s)), s = sigmoid(z) [strip.py: `_dsilu`], accumulates the tap
+// gradients dw_k += g[t] * x[t-k] and dbias += g[t] in fp32, and keeps the W-1 previous
+// rows of g in a second ring: dx[u] = sum_k w[:, W-1-k] * g[u+k] is complete W-1 rows after u
+// [strip.py: `_bwd4` docstring]. A segment does not own dx for its first W-1 rows' lag
+// window: the previous segment finishes those from a right halo of W-1 rows whose g it
+// recomputes without accumulating dw [strip.py: `cconv_bwd_strip` halo].
+//
+// dw/dbias partials: the waves of a block (consecutive segments of one strip and batch row)
+// are summed through LDS in wave order, and the block writes one fp32 partial row
+// [W+1][D] (columns 0..W-1 dw, column W dbias). A second kernel sums the partials over
+// blocks in a fixed order and casts dw to its dtype [strip.py: host `cconv_bwd`, the
+// deterministic reduction with no atomics]. Both orders are fixed, so dw/dbias are bitwise
+// reproducible.
+#include "cconv_device.hpp"
+#include "cconv_internal.hpp"
+
+namespace cconv {
+
+// One backward row t. `acc_on`: the row belongs to this segment (accumulate dw/dbias);
+// `emit`: dx of row t-(W-1) is this segment's and gets stored.
+template <int VEC, int W>
+__device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float (&b)[VEC],
+                                        const Row<VEC>& rx, const Row<VEC>& rdy,
+                                        float (&xr)[W > 1 ? W - 1 : 1][VEC],
+                                        float (&gr)[W > 1 ? W - 1 : 1][VEC], float (&acc)[W][VEC],
+                                        float (&db)[VEC], bool acc_on, bool emit,
+                                        uint16_t* __restrict__ dxp) {
+    float xt[VEC], dyt[VEC], g[VEC];
+    widen(rx, xt);
+    widen(rdy, dyt);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        const float z = conv_z<VEC, W>(tap, b, xt, xr, v);
+        const float s = sigmoid(z);
+        const float q = __builtin_fmaf(z, 1.0f - s, 1.0f);
+        g[v] = (dyt[v] * s) * q;
+    }
+    if (acc_on) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            acc[0][v] = __builtin_fmaf(g[v], xt[v], acc[0][v]);
+#pragma unroll
+            for (int k = 1; k < W; ++k) acc[k][v] = __builtin_fmaf(g[v], xr[k - 1][v], acc[k][v]);
+            db[v] += g[v];
+        }
+    }
+    if (emit) {
+        // dx[u], u = t-(W-1): sum over k ascending of tap[k] * g[u+k]; g[u+k] is g (k = W-1)
+        // or the ring entry gr[W-2-k] = g[t-(W-1-k)].
+        float dx[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            float s = tap[0][v] * (W == 1 ? g[v] : gr[W > 1 ? W - 2 : 0][v]);
+#pragma unroll
+            for (int k = 1; k < W; ++k) s = __builtin_fmaf(tap[k][v], k == W - 1 ? g[v] : gr[W - 2 - k][v], s);
+            dx[v] = s;
+        }
+        store_row<VEC>(dxp, narrow<VEC>(dx));
+    }
+#pragma unroll
+    for (int k = W - 2; k > 0; --k)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            xr[k][v] = xr[k - 1][v];
+            gr[k][v] = gr[k - 1][v];
+        }
+    if constexpr (W > 1) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            xr[0][v] = xt[v];
+            gr[0][v] = g[v];
+        }
+    }
+}
+
+template <int VEC, int G, int W>
+__global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
+    constexpr int R = W > 1 ? W - 1 : 1;
+    extern __shared__ float red[];  // [waves][VEC][64], one column at a time
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t strip = tile % a.strips;
+    const int64_t rest = tile / a.strips;
+    const int64_t sg = rest % a.seg_groups;
+    const int64_t b = rest / a.seg_groups;
+    const int waves = blockDim.x / kWave;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int64_t t0 = (sg * waves + wave) * a.seg_rows;
+    const int64_t t1 = min(t0 + a.seg_rows, a.T);
+    const int64_t d = (strip * kWave + lane) * VEC;
+    const bool active = d < a.D;
+
+    float acc[W][VEC], db[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        db[v] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < W; ++k) acc[k][v] = 0.0f;
+    }
+
+    if (active && t0 < a.T) {
+        const uint16_t* __restrict__ xp = a.x + b * a.x_sb + d;
+        const uint16_t* __restrict__ dyp = a.dy + b * a.dy_sb + d;
+        uint16_t* __restrict__ dxp = a.dx + b * a.T * a.D + d;
+        const int64_t xs = a.x_st, dys = a.dy_st, dxs = a.D;
+
+        float tap[W][VEC];
+        load_taps<VEC, W>(a.w, a.w_f32, d, tap);
+        float bs[VEC];
+        load_bias<VEC>(a.bias, d, bs);
+
+        float xr[R][VEC], gr[R][VEC];
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int64_t t = t0 - 1 - k;
+            if (W > 1 && t >= 0) {
+                widen(load_row<VEC>(xp + t * xs), xr[k]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) xr[k][v] = 0.0f;
+            }
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) gr[k][v] = 0.0f;  // rows before t0 are not ours
+        }
+
+        int64_t t = t0;
+        for (; t + G <= t1; t += G) {
+            Row<VEC> rx[G], rdy[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) rx[g] = load_row<VEC>(xp + (t + g) * xs);
+#pragma unroll
+            for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC>(dyp + (t + g) * dys);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int64_t u = t + g - (W - 1);
+                bwd_row<VEC, W>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, true, u >= t0, dxp + u * dxs);
+            }
+        }
+        for (; t < t1; ++t) {
+            const int64_t u = t - (W - 1);
+            bwd_row<VEC, W>(tap, bs, load_row<VEC>(xp + t * xs), load_row<VEC>(dyp + t * dys), xr, gr, acc,
+                            db, true, u >= t0, dxp + u * dxs);
+        }
+        // right halo: rows t1 .. t1+W-2 finish dx of this segment's last W-1 rows; rows at or
+        // past T have g = 0 (their x and dy read as zero).
+#pragma unroll
+        for (int h = 0; h < W - 1; ++h) {
+            const int64_t th = t1 + h;
+            const int64_t u = th - (W - 1);
+            const bool in = th < a.T;
+            const Row<VEC> hx = in ? load_row<VEC>(xp + th * xs) : zero_row<VEC>();
+            const Row<VEC> hdy = in ? load_row<VEC>(dyp + th * dys) : zero_row<VEC>();
+            bwd_row<VEC, W>(tap, bs, hx, hdy, xr, gr, acc, db, false, u >= t0, dxp + u * dxs);
+        }
+    }
+
+    // Sum the block's waves in wave order, one column at a time; wave 0 stores the partial.
+    const int64_t p = b * a.seg_groups + sg;
+    float* __restrict__ out = a.partial + p * (W + 1) * a.D + d;
+#pragma unroll
+    for (int j = 0; j <= W; ++j) {
+        // column j < W is dw[:, j], the gradient of tap k = W-1-j; column W is dbias
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+            red[(wave * VEC + v) * kWave + lane] = (j < W) ? acc[W - 1 - j][v] : db[v];
+        __syncthreads();
+        if (wave == 0 && active) {
+            float s[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                s[v] = red[v * kWave + lane];
+                for (int w2 = 1; w2 < waves; ++w2) s[v] += red[(w2 * VEC + v) * kWave + lane];
+            }
+            float* o = out + j * a.D;
+            if constexpr (VEC == 8) {
+                reinterpret_cast<float4*>(o)[0] = make_float4(s[0], s[1], s[2], s[3]);
+                reinterpret_cast<float4*>(o)[1] = make_float4(s[4], s[5], s[6], s[7]);
+            } else {
+                reinterpret_cast<float4*>(o)[0] = make_float4(s[0], s[1], s[2], s[3]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// dw[d, j] = sum_p partial[p, j, d] (j < W), dbias[d] = sum_p partial[p, W, d]. A block
+// handles 64 consecutive (j, d) entries; its 4 waves each sum a contiguous quarter of the
+// partials in ascending order, then the four sums are added in wave order. P == 0 writes
+// zeros (an empty batch or sequence).
+__global__ __launch_bounds__(256) void cconv_dw_reduce_kernel(const ReduceArgs a) {
+    __shared__ float part[4][kWave];
+    const int lane = threadIdx.x % kWave, q = threadIdx.x / kWave;
+    const int64_t E = static_cast<int64_t>(a.W + 1) * a.D;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+    float s = 0.0f;
+    if (e < E) {
+        const int64_t chunk = (a.P + 3) / 4;
+        const int64_t p0 = q * chunk, p1 = min(a.P, p0 + chunk);
+        const float* __restrict__ src = a.partial + e;
+        int64_t p = p0;
+        for (; p + 4 <= p1; p += 4) {
+            const float v0 = src[(p + 0) * E], v1 = src[(p + 1) * E], v2 = src[(p + 2) * E], v3 = src[(p + 3) * E];
+            s += v0;
+            s += v1;
+            s += v2;
+            s += v3;
+        }
+        for (; p < p1; ++p) s += src[p * E];
+    }
+    part[q][lane] = s;
+    __syncthreads();
+    if (q == 0 && e < E) {
+        const float tot = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+        const int64_t j = e / a.D, d = e % a.D;
+        if (j < a.W) {
+            if (a.dw_f32) {
+                static_cast<float*>(a.dw)[d * a.W + j] = tot;
+            } else {
+                static_cast<uint16_t*>(a.dw)[d * a.W + j] = static_cast<uint16_t>(pack_bf16x2(tot, 0.0f) & 0xffffu);
+            }
+        } else if (a.dbias) {
+            a.dbias[d] = tot;
+        }
+    }
+}
+
+namespace {
+
+template <int VEC, int G>
+hipError_t launch_bwd_w(int W, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
+    switch (W) {
+        case 1: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, 1>), grid, block, lds, s, a); break;
+        case 2: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, 2>), grid, block, lds, s, a); break;
+        case 3: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, 3>), grid, block, lds, s, a); break;
+        case 4: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, 4>), grid, block, lds, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_variant_exists(int vec, int group) {
+    return (vec == 4 || vec == 8) && (group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
+    const size_t lds = static_cast<size_t>(p.waves) * p.vec * kWave * sizeof(float);
+    if (p.vec == 8) {
+        if (p.group == 2) return launch_bwd_w<8, 2>(W, grid, block, lds, a, s);
+        if (p.group == 4) return launch_bwd_w<8, 4>(W, grid, block, lds, a, s);
+        if (p.group == 8) return launch_bwd_w<8, 8>(W, grid, block, lds, a, s);
+    } else if (p.vec == 4) {
+        if (p.group == 2) return launch_bwd_w<4, 2>(W, grid, block, lds, a, s);
+        if (p.group == 4) return launch_bwd_w<4, 4>(W, grid, block, lds, a, s);
+        if (p.group == 8) return launch_bwd_w<4, 8>(W, grid, block, lds, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+    const int64_t E = static_cast<int64_t>(a.W + 1) * a.D;
+    const int64_t blocks = (E + kWave - 1) / kWave;
+    hipLaunchKernelGGL(cconv_dw_reduce_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace cconv

@@ -1,0 +1,153 @@
+// cconv_device.hpp -- gfx950 device helpers for the causal depthwise short convolution.
+//
+// Data movement is in whole rows of a lane's VEC contiguous channels: one 16-byte (VEC = 8)
+// or 8-byte (VEC = 4) global load or store per row, so a wave64 moves 1 KB (or 512 B) of a
+// bf16 row per instruction, fully coalesced. bf16 values stay packed two to a dword until
+// they are used; widening is a shift or a mask, narrowing is gfx950's packed
+// round-to-nearest-even convert (v_cvt_pk_bf16_f32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cconv {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// VEC bf16 values of one row, packed two per dword (element 2i in the low half of u[i]).
+template <int VEC>
+struct Row {
+    uint32_t u[VEC / 2];
+};
+
+template <int VEC>
+__device__ __forceinline__ Row<VEC> load_row(const uint16_t* __restrict__ p) {
+    static_assert(VEC == 4 || VEC == 8, "VEC is 4 or 8");
+    Row<VEC> r;
+    if constexpr (VEC == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        r.u[0] = v.x;
+        r.u[1] = v.y;
+        r.u[2] = v.z;
+        r.u[3] = v.w;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        r.u[0] = v.x;
+        r.u[1] = v.y;
+    }
+    return r;
+}
+
+template <int VEC>
+__device__ __forceinline__ Row<VEC> zero_row() {
+    Row<VEC> r;
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) r.u[i] = 0u;
+    return r;
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_row(uint16_t* __restrict__ p, const Row<VEC>& r) {
+    if constexpr (VEC == 8) {
+        *reinterpret_cast<uint4*>(p) = make_uint4(r.u[0], r.u[1], r.u[2], r.u[3]);
+    } else {
+        *reinterpret_cast<uint2*>(p) = make_uint2(r.u[0], r.u[1]);
+    }
+}
+
+// bf16 -> fp32 is exact: the bf16 pattern is the high half of the fp32 pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+template <int VEC>
+__device__ __forceinline__ void widen(const Row<VEC>& r, float (&f)[VEC]) {
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+        f[2 * i] = bf16_lo(r.u[i]);
+        f[2 * i + 1] = bf16_hi(r.u[i]);
+    }
+}
+
+// Two fp32 -> two bf16 (round to nearest even), packed: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    const bf16x2 b = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+template <int VEC>
+__device__ __forceinline__ Row<VEC> narrow(const float (&f)[VEC]) {
+    Row<VEC> r;
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) r.u[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return r;
+}
+
+// sigma(z) = 1 / (1 + e^-z) = 1 / (1 + 2^(-z log2 e)): one v_exp_f32 and one v_rcp_f32 (each
+// accurate to about 1 ulp). Saturates correctly: e^-z -> inf gives 0, e^-z -> 0 gives 1.
+__device__ __forceinline__ float sigmoid(float z) {
+    const float e = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Taps of VEC consecutive channels d .. d+VEC-1 in the tap-major order the ring uses:
+// tap[k][v] multiplies x[t-k] of channel d+v, i.e. tap[k][v] = w[d+v, W-1-k]; taps k >= W
+// are zero. w is [D, W] row-major, bf16 (w_f32 == 0) or fp32.
+template <int VEC, int W>
+__device__ __forceinline__ void load_taps(const void* __restrict__ w, int w_f32, int64_t d,
+                                          float (&tap)[W][VEC]) {
+    if (w_f32) {
+        const float* wf = static_cast<const float*>(w) + d * W;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+#pragma unroll
+            for (int k = 0; k < W; ++k) tap[k][v] = wf[v * W + (W - 1 - k)];
+    } else {
+        const uint16_t* wb = static_cast<const uint16_t*>(w) + d * W;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+                tap[k][v] = __uint_as_float(static_cast<uint32_t>(wb[v * W + (W - 1 - k)]) << 16);
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_bias(const float* __restrict__ bias, int64_t d,
+                                          float (&b)[VEC]) {
+    if (bias) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) b[v] = bias[d + v];
+    } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) b[v] = 0.0f;
+    }
+}
+
+// z = bias + sum_k tap[k] * x[t-k], accumulated newest tap first (x[t], then x[t-1], ...).
+// Every kernel uses this one order, so y, dx and the decode output do not depend on the
+// launch shape, and zero taps appended on the oldest side leave z unchanged.
+template <int VEC, int W>
+__device__ __forceinline__ float conv_z(const float (&tap)[W][VEC], const float (&b)[VEC],
+                                        const float (&xt)[VEC], const float (&ring)[W > 1 ? W - 1 : 1][VEC],
+                                        int v) {
+    float z = __builtin_fmaf(tap[0][v], xt[v], b[v]);
+#pragma unroll
+    for (int k = 1; k < W; ++k) z = __builtin_fmaf(tap[k][v], ring[k - 1][v], z);
+    return z;
+}
+
+// Workgroup -> logical tile, so that the contiguous logical range [x*q, (x+1)*q) runs on one
+// XCD. Workgroups are handed to the 8 XCDs round-robin by id; neighbouring tiles (adjacent
+// time segments of one channel strip) then share an L2 for the rows they both read.
+__device__ __forceinline__ int64_t xcd_tile(int64_t pid, int64_t n) {
+    constexpr int64_t kXcd = 8;
+    const int64_t xcd = pid % kXcd, k = pid / kXcd;
+    const int64_t q = n / kXcd, r = n % kXcd;
+    return xcd * q + (xcd < r ? xcd : r) + k;
+}
+
+}  // namespace cconv

@@ -1,0 +1,124 @@
+// cconv_fwd.hip -- forward of the depthwise causal short convolution + SiLU on gfx950.
+//
+// Work decomposition (after the channel-strip, time-sequential scheme of the kernel-fun
+// wheel's strip.py module docstring, re-cut for wave64): a lane owns VEC consecutive
+// channels; a wave owns a strip of 64*VEC channels for one time segment of one batch row and
+// walks the segment's rows in order. The W-1 previous rows of x stay in VGPRs as a ring, so
+// each element costs one coalesced load, one sigmoid and one store. Rows are loaded G at a
+// time (all G loads issued before the group's arithmetic) to keep bytes in flight.
+//
+// y[b,t,d] = silu(bias[d] + sum_k w[d, W-1-k] * x[b, t-k, d]), x = 0 before t = 0
+// [strip.py: `_tap`, `_ld_ring`, `_silu`, `_fwd4`].
+#include "cconv_device.hpp"
+#include "cconv_internal.hpp"
+
+namespace cconv {
+
+template <int VEC, int W>
+__device__ __forceinline__ Row<VEC> fwd_row(const float (&tap)[W][VEC], const float (&b)[VEC],
+                                            const Row<VEC>& raw,
+                                            float (&ring)[W > 1 ? W - 1 : 1][VEC]) {
+    float xt[VEC];
+    widen(raw, xt);
+    float y[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        const float z = conv_z<VEC, W>(tap, b, xt, ring, v);
+        y[v] = z * sigmoid(z);
+    }
+    // rotate: ring[k] holds x[t-1-k]
+#pragma unroll
+    for (int k = W - 2; k > 0; --k)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) ring[k][v] = ring[k - 1][v];
+    if constexpr (W > 1) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) ring[0][v] = xt[v];
+    }
+    return narrow<VEC>(y);
+}
+
+template <int VEC, int G, int W>
+__global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
+    constexpr int R = W > 1 ? W - 1 : 1;
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t strip = tile % a.strips;
+    const int64_t rest = tile / a.strips;
+    const int64_t sg = rest % a.seg_groups;
+    const int64_t b = rest / a.seg_groups;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int64_t t0 = (sg * (blockDim.x / kWave) + wave) * a.seg_rows;
+    if (t0 >= a.T) return;  // a trailing wave of the last segment group
+    const int64_t t1 = min(t0 + a.seg_rows, a.T);
+    const int64_t d = (strip * kWave + lane) * VEC;
+    if (d >= a.D) return;  // lanes past the last channel (D is a multiple of VEC)
+
+    const uint16_t* __restrict__ xp = a.x + b * a.x_sb + d;
+    uint16_t* __restrict__ yp = a.y + b * a.T * a.D + d;
+    const int64_t xs = a.x_st, ys = a.D;
+
+    float tap[W][VEC];
+    load_taps<VEC, W>(a.w, a.w_f32, d, tap);
+    float bs[VEC];
+    load_bias<VEC>(a.bias, d, bs);
+
+    // ring prologue: x[t0-1-k], zero before the sequence start
+    float ring[R][VEC];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int64_t t = t0 - 1 - k;
+        if (W > 1 && t >= 0) {
+            widen(load_row<VEC>(xp + t * xs), ring[k]);
+        } else {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) ring[k][v] = 0.0f;
+        }
+    }
+
+    int64_t t = t0;
+    for (; t + G <= t1; t += G) {
+        Row<VEC> raw[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) raw[g] = load_row<VEC>(xp + (t + g) * xs);
+#pragma unroll
+        for (int g = 0; g < G; ++g) store_row<VEC>(yp + (t + g) * ys, fwd_row<VEC, W>(tap, bs, raw[g], ring));
+    }
+    for (; t < t1; ++t) store_row<VEC>(yp + t * ys, fwd_row<VEC, W>(tap, bs, load_row<VEC>(xp + t * xs), ring));
+}
+
+namespace {
+
+template <int VEC, int G>
+hipError_t launch_fwd_w(int W, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
+    switch (W) {
+        case 1: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, 1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, 2>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, 3>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, 4>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_variant_exists(int vec, int group) {
+    return (vec == 4 || vec == 8) && (group == 4 || group == 8 || group == 16);
+}
+
+hipError_t launch_fwd(const Plan& p, int W, const FwdArgs& a, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
+    if (p.vec == 8) {
+        if (p.group == 4) return launch_fwd_w<8, 4>(W, grid, block, a, s);
+        if (p.group == 8) return launch_fwd_w<8, 8>(W, grid, block, a, s);
+        if (p.group == 16) return launch_fwd_w<8, 16>(W, grid, block, a, s);
+    } else if (p.vec == 4) {
+        if (p.group == 4) return launch_fwd_w<4, 4>(W, grid, block, a, s);
+        if (p.group == 8) return launch_fwd_w<4, 8>(W, grid, block, a, s);
+        if (p.group == 16) return launch_fwd_w<4, 16>(W, grid, block, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace cconv

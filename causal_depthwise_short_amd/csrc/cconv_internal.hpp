@@ -1,0 +1,88 @@
+// cconv_internal.hpp -- launch plans and kernel launchers shared by the C ABI (cconv_api.hip)
+// and the kernels (cconv_fwd.hip, cconv_bwd.hip, cconv_update.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cconv {
+
+// How a forward or backward call is cut into work.
+//   A lane owns `vec` consecutive channels; a wave owns a strip of 64*vec channels and one
+//   time segment of `seg_rows` rows of one batch row; a block holds `waves` waves that take
+//   consecutive segments of the same strip and batch row. `group` rows are loaded together.
+struct Plan {
+    int vec;
+    int group;
+    int waves;
+    int64_t seg_rows;
+    // derived
+    int64_t strips;      // ceil(D / (64*vec))
+    int64_t segs;        // ceil(T / seg_rows)
+    int64_t seg_groups;  // ceil(segs / waves)
+    int64_t blocks;      // strips * seg_groups * B
+    int64_t partials;    // backward: B * seg_groups fp32 partial rows of [W+1, D]
+};
+
+struct FwdArgs {
+    const uint16_t* x;
+    int64_t x_sb, x_st;
+    const void* w;
+    int w_f32;
+    const float* bias;
+    uint16_t* y;
+    int64_t B, T, D;
+    int64_t seg_rows, strips, seg_groups;
+};
+
+struct BwdArgs {
+    const uint16_t* x;
+    int64_t x_sb, x_st;
+    const uint16_t* dy;
+    int64_t dy_sb, dy_st;
+    const void* w;
+    int w_f32;
+    const float* bias;
+    uint16_t* dx;
+    float* partial;  // [partials, W+1, D]
+    int64_t B, T, D;
+    int64_t seg_rows, strips, seg_groups;
+};
+
+struct ReduceArgs {
+    const float* partial;  // [P, W+1, D]
+    int64_t P, D;
+    int W;
+    void* dw;  // [D, W]
+    int dw_f32;
+    float* dbias;  // [D] or null
+};
+
+struct UpdateArgs {
+    const uint16_t* x;
+    int64_t x_ld;
+    uint16_t* state;  // [S, D, W-1]
+    int64_t S;
+    const int32_t* idx;  // [N] or null
+    const void* w;
+    int w_f32;
+    const float* bias;
+    uint16_t* y;  // [N, D]
+    int64_t N, D;
+    int64_t rows_per_block;  // rows of N each block walks
+    int32_t* status;
+};
+
+// Launchers: enqueue on `stream`, return hipGetLastError() after the launch.
+hipError_t launch_fwd(const Plan& p, int W, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+hipError_t launch_update(int W, const UpdateArgs& a, int block_threads, int64_t grid_x,
+                         int64_t grid_y, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_status(int32_t* status, int32_t value, hipStream_t stream);
+
+// Which (vec, group) pairs are compiled.
+bool fwd_variant_exists(int vec, int group);
+bool bwd_variant_exists(int vec, int group);
+
+}  // namespace cconv

@@ -1,0 +1,141 @@
+// cconv_update.hip -- one-token decode update of the causal depthwise short convolution +
+// SiLU on gfx950 [cudnn-frontend PR #797 "Add experimental causal conv1d decode update",
+// PR description: API and semantics].
+//
+// A thread owns 8 consecutive channels of a run of rows: per row it gathers the slot
+// s = state_indices[n] (or n), reads x[n, d..d+7] (16 B) and state[s, d..d+7, 0..W-2]
+// (8*(W-1) contiguous bf16, 16*(W-1) B), forms z = bias + sum_j w[d, j] state_j + w[d, W-1] x
+// in the forward's tap order, writes y = silu(z) and the shifted state (bit copies: the
+// oldest value drops out and x becomes the newest).
+//
+// Fail-closed validation without a device trap: every block reads all N indices and checks
+// them against an S-bit set in LDS (range [-1, S) and no repeated non-negative slot), so all
+// blocks reach the same verdict. If any index is invalid no block writes state; block 0
+// reports the verdict in *status. The page's kernel scans all earlier rows per row (quadratic
+// in N) and traps; here a block pays O(N + S/32) and the grid is sized so that the number of
+// blocks stays near a constant, keeping the total linear in N.
+#include "../../include/cconv.h"
+#include "cconv_device.hpp"
+#include "cconv_internal.hpp"
+
+namespace cconv {
+
+template <int W>
+__global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
+    constexpr int VEC = 8;
+    constexpr int L = W - 1;  // state length
+    extern __shared__ uint32_t seen[];
+
+    bool bad = false;
+    if (a.idx) {
+        const int64_t words = (a.S + 31) / 32;
+        for (int64_t i = threadIdx.x; i < words; i += blockDim.x) seen[i] = 0u;
+        __syncthreads();
+        for (int64_t i = threadIdx.x; i < a.N; i += blockDim.x) {
+            const int32_t v = a.idx[i];
+            if (v < -1 || static_cast<int64_t>(v) >= a.S) {
+                bad = true;
+            } else if (v >= 0) {
+                const uint32_t bit = 1u << (v & 31);
+                const uint32_t old = atomicOr(&seen[v >> 5], bit);
+                if (old & bit) bad = true;
+            }
+        }
+        bad = __syncthreads_or(bad);
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && a.status)
+        a.status[0] = bad ? CCONV_ERR_INDEX : CCONV_OK;
+    if (bad) return;
+
+    const int64_t d = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * VEC;
+    if (d >= a.D) return;
+
+    float tap[W][VEC];
+    load_taps<VEC, W>(a.w, a.w_f32, d, tap);
+    float bs[VEC];
+    load_bias<VEC>(a.bias, d, bs);
+
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * a.rows_per_block;
+    const int64_t n1 = min(n0 + a.rows_per_block, a.N);
+    for (int64_t n = n0; n < n1; ++n) {
+        const int64_t s = a.idx ? static_cast<int64_t>(a.idx[n]) : n;
+        uint16_t* __restrict__ yp = a.y + n * a.D + d;
+        if (s < 0) {  // padding row: no state access, output 0
+            store_row<VEC>(yp, zero_row<VEC>());
+            continue;
+        }
+        const Row<VEC> rx = load_row<VEC>(a.x + n * a.x_ld + d);
+        float xt[VEC];
+        widen(rx, xt);
+        // state of channel d+v, entry j, at 16-bit position v*L + j
+        uint16_t h[VEC * (L > 0 ? L : 1)];
+        uint16_t* __restrict__ sp = a.state + (s * a.D + d) * L;
+        if constexpr (L > 0) {
+#pragma unroll
+            for (int q = 0; q < L; ++q) {
+                const uint4 v4 = reinterpret_cast<const uint4*>(sp)[q];
+                const uint32_t u[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    h[q * 8 + 2 * i] = static_cast<uint16_t>(u[i] & 0xffffu);
+                    h[q * 8 + 2 * i + 1] = static_cast<uint16_t>(u[i] >> 16);
+                }
+            }
+        }
+        // ring view in the forward's order: ring[k-1] = x[t-k] = state[.., L-k]
+        float ring[L > 0 ? L : 1][VEC];
+#pragma unroll
+        for (int k = 1; k <= L; ++k)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) ring[k - 1][v] = __uint_as_float(static_cast<uint32_t>(h[v * L + (L - k)]) << 16);
+        float y[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const float z = conv_z<VEC, W>(tap, bs, xt, ring, v);
+            y[v] = z * sigmoid(z);
+        }
+        store_row<VEC>(yp, narrow<VEC>(y));
+        if constexpr (L > 0) {
+            uint16_t nh[VEC * L];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+#pragma unroll
+                for (int j = 0; j + 1 < L; ++j) nh[v * L + j] = h[v * L + j + 1];
+                const uint32_t xw = rx.u[v / 2];
+                nh[v * L + L - 1] = static_cast<uint16_t>((v & 1) ? (xw >> 16) : (xw & 0xffffu));
+            }
+#pragma unroll
+            for (int q = 0; q < L; ++q) {
+                uint32_t u[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    u[i] = static_cast<uint32_t>(nh[q * 8 + 2 * i]) | (static_cast<uint32_t>(nh[q * 8 + 2 * i + 1]) << 16);
+                reinterpret_cast<uint4*>(sp)[q] = make_uint4(u[0], u[1], u[2], u[3]);
+            }
+        }
+    }
+}
+
+__global__ void cconv_status_kernel(int32_t* status, int32_t value) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) status[0] = value;
+}
+
+hipError_t launch_update(int W, const UpdateArgs& a, int block_threads, int64_t grid_x, int64_t grid_y,
+                         size_t lds, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(grid_x), static_cast<uint32_t>(grid_y)), block(block_threads);
+    switch (W) {
+        case 1: hipLaunchKernelGGL(cconv_update_kernel<1>, grid, block, lds, s, a); break;
+        case 2: hipLaunchKernelGGL(cconv_update_kernel<2>, grid, block, lds, s, a); break;
+        case 3: hipLaunchKernelGGL(cconv_update_kernel<3>, grid, block, lds, s, a); break;
+        case 4: hipLaunchKernelGGL(cconv_update_kernel<4>, grid, block, lds, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_status(int32_t* status, int32_t value, hipStream_t s) {
+    hipLaunchKernelGGL(cconv_status_kernel, dim3(1), dim3(64), 0, s, status, value);
+    return hipGetLastError();
+}
+
+}  // namespace cconv

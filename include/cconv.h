@@ -1,0 +1,179 @@
+/*
+ * cconv.h -- C ABI of libcconv.so: the depthwise causal short convolution (width W <= 4,
+ * one set of taps per channel, optional bias) fused with SiLU, on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation. For activations x[B, T, D] (channel dimension contiguous) and taps w[D, W]:
+ *
+ *     z[b, t, d] = bias[d] + sum_{j=0}^{W-1} w[d, j] * x[b, t-(W-1)+j, d]    (x = 0 for t < 0)
+ *     y[b, t, d] = z * sigmoid(z)
+ *
+ * i.e. the tap that multiplies x[t-k] is w[:, W-1-k] [kernel-fun 0.2.0.dev1 wheel, page 2,
+ * strip.py: `_tap`], the history before the sequence start is zero [strip.py: `_ld_ring`],
+ * and SiLU is fused [kernel-fun wheel, cconv/__init__.py docstring; strip.py: `_silu`]. The
+ * backward returns dx, dw and dbias through SiLU's derivative without re-running the
+ * forward [strip.py: module docstring and `_bwd4`; `_dsilu`]. The decode update advances a
+ * per-sequence state of the last W-1 inputs by one token [cudnn-frontend PR #797 "Add
+ * experimental causal conv1d decode update", PR description: API and semantics].
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer is caller-owned device memory. It may be NULL where stated, and any
+ *    pointer may be NULL when the tensor it points to is empty (torch hands out NULL data
+ *    pointers for empty tensors). The library
+ *    allocates nothing, keeps no pointer beyond the call and owns no output (outputs are
+ *    never cached; compare the kernel-fun wheel's _common/cache.py docstring on outputs).
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the null stream):
+ *    no host synchronisation, no device-to-host read. Calls are reentrant and may be
+ *    captured into a HIP graph from the first call.
+ *  - bf16 tensors are passed as raw 16-bit patterns; fp32 as IEEE binary32. Outputs in
+ *    bf16 are rounded to nearest-even [strip.py: `_st`].
+ *  - Alignment: every tensor pointer must be 16-byte aligned, except state_indices and
+ *    status (4 bytes) [PR #797 review thread: alignment contract]. D must be a multiple of 8
+ *    and every row stride a multiple of 8 elements, so that each lane moves 16-byte vectors.
+ *  - Errors fail closed. A problem visible on the host returns its code before anything is
+ *    enqueued, leaving every output untouched: NULL required pointer, negative size, W
+ *    outside [1, 4] (the pages' kernels are written for at most 4 taps, strip.py module
+ *    docstring), bad stride, unsupported dtype, misalignment, an output overlapping another
+ *    operand, a workspace that is too small. A failed launch returns CCONV_ERR_LAUNCH.
+ *  - An empty problem (B*T*D == 0, N*D == 0) is CCONV_OK; the backward still writes its
+ *    zero dw/dbias when D > 0, and the decode update still writes *status when given.
+ */
+#ifndef CCONV_H
+#define CCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+/* A hipStream_t. NULL means the null stream. */
+typedef struct ihipStream_t* cconv_stream_t;
+
+typedef enum { CCONV_BF16 = 0, CCONV_F32 = 1 } cconv_dtype_t;
+
+typedef enum {
+    CCONV_OK = 0,
+    CCONV_ERR_NULL_POINTER = 1,
+    CCONV_ERR_BAD_SHAPE = 2,
+    CCONV_ERR_BAD_STRIDE = 3,
+    CCONV_ERR_UNSUPPORTED_DTYPE = 4,
+    CCONV_ERR_MISALIGNED = 5,
+    CCONV_ERR_ALIASING = 6,
+    CCONV_ERR_WORKSPACE = 7,
+    CCONV_ERR_INDEX = 8,
+    CCONV_ERR_LAUNCH = 9,
+    CCONV_ERR_BAD_CONFIG = 10
+} cconv_status_t;
+
+/*
+ * Forward [strip.py: `cconv_fwd`, `cconv_fwd_strip`; bias as in fla's parameter list,
+ * kernel-fun wheel _common/compat.py FLA_KWARGS].
+ *   x     bf16 [B, T, D]: element (b, t, d) at x[b*x_sb + t*x_st + d]; x_st >= D.
+ *   w     [D, W] contiguous, dtype w_dtype (CCONV_BF16 or CCONV_F32).
+ *   bias  fp32 [D], or NULL for none.
+ *   y     bf16 [B, T, D] contiguous (written; must not overlap x, w or bias).
+ *   B, T, D >= 0; 1 <= W <= 4.
+ */
+cconv_status_t cconv_fwd(const void* x, int64_t x_sb, int64_t x_st, const void* w,
+                         cconv_dtype_t w_dtype, const float* bias, void* y, int64_t B,
+                         int64_t T, int64_t D, int W, cconv_stream_t stream);
+
+/* Bytes of device workspace cconv_bwd needs for this problem (fp32 dw/dbias partials). */
+size_t cconv_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W);
+
+/*
+ * Backward [strip.py: `cconv_bwd`, `cconv_bwd_strip`, `_bwd4`, `_dsilu`]. With
+ * g = dy * s * (1 + z*(1-s)), s = sigmoid(z) recomputed from x:
+ *   dx[b, u, d] = sum_j w[d, j] * g[b, u+(W-1)-j, d]            (g = 0 at or past T)
+ *   dw[d, j]    = sum_{b,t} g[b, t, d] * x[b, t-(W-1)+j, d]      (x = 0 before t = 0)
+ *   dbias[d]    = sum_{b,t} g[b, t, d]
+ *   x, dy    bf16 [B, T, D] with strides (x_sb, x_st, 1) and (dy_sb, dy_st, 1).
+ *   w, bias  as in cconv_fwd (bias only enters z; NULL = no bias).
+ *   dx       bf16 [B, T, D] contiguous, written.
+ *   dw       [D, W] in dw_dtype (CCONV_BF16 or CCONV_F32), overwritten (not accumulated).
+ *   dbias    fp32 [D], overwritten, or NULL when not wanted.
+ *   workspace, workspace_bytes: caller-provided device scratch of at least
+ *            cconv_bwd_workspace_bytes(B, T, D, W) bytes (may be NULL when that is 0).
+ * dw and dbias are summed in a fixed order with no atomics, so they are bitwise
+ * reproducible run to run [strip.py: host `cconv_bwd`, comment on the reduction].
+ */
+cconv_status_t cconv_bwd(const void* x, int64_t x_sb, int64_t x_st, const void* dy,
+                         int64_t dy_sb, int64_t dy_st, const void* w, cconv_dtype_t w_dtype,
+                         const float* bias, void* dx, void* dw, cconv_dtype_t dw_dtype,
+                         float* dbias, void* workspace, size_t workspace_bytes, int64_t B,
+                         int64_t T, int64_t D, int W, cconv_stream_t stream);
+
+/*
+ * One-token decode update [PR #797 description: `CausalConv1dUpdate` API and semantics].
+ *   x       bf16 [N, D], row n at x + n*x_ld, x_ld >= D (a slice of a wider projection).
+ *   state   bf16 [S, D, W-1] contiguous, in/out, oldest first: state[s, d, j] holds the
+ *           input that came W-1-j tokens before the one being added. Updated in place by
+ *           bit copies: the oldest value drops out and x[n, d] becomes the newest.
+ *   state_indices  int32 [N]: the slot of row n; -1 marks a padding row that reads and
+ *           writes no state and whose y row is 0. NULL means slot n for row n (needs N <= S).
+ *   w, bias as in cconv_fwd; y bf16 [N, D] contiguous, written.
+ *   z = bias + sum_{j<W-1} w[d, j] * state[s, d, j] + w[d, W-1] * x[n, d];  y = silu(z).
+ *   status  device int32 or NULL: receives CCONV_OK or CCONV_ERR_INDEX.
+ * Index validation happens on the device, inside the one kernel: an index outside [-1, S),
+ * or a non-negative index that appears twice, makes the whole call invalid. Then no state
+ * row is written (bitwise unchanged), y is unspecified, and *status = CCONV_ERR_INDEX.
+ * No device trap is raised, so the process stays usable. Limits: N <= 2^24; with indices,
+ * S <= 2^19 (the duplicate check keeps an S-bit set in LDS).
+ */
+cconv_status_t cconv_update(const void* x, int64_t x_ld, void* state, int64_t S,
+                            const int32_t* state_indices, const void* w, cconv_dtype_t w_dtype,
+                            const float* bias, void* y, int64_t N, int64_t D, int W,
+                            int32_t* status, cconv_stream_t stream);
+
+/* A short English description of a status code (static storage). */
+const char* cconv_status_string(cconv_status_t status);
+
+/* Library version and build string (static storage). */
+const char* cconv_version(void);
+
+/*
+ * Launch configuration, for sweeps and for tests of invariance to the launch shape. The
+ * entry points above pick one from a static table; these take it explicitly. y and dx do
+ * not depend on the configuration (bitwise); dw and dbias depend on it only through the
+ * order of their fixed-order sum.
+ *   vec              channels per lane: 4 or 8 (8 or 16 bytes per row per lane)
+ *   rows_per_group   rows whose loads are issued together: fwd 4, 8 or 16; bwd 2, 4 or 8
+ *   waves_per_block  1, 2, 4 or 8 waves; the waves of a block take consecutive time
+ *                    segments of the same channel strip and batch row
+ *   seg_rows         rows per wave segment: a multiple of rows_per_group, >= 8
+ */
+typedef struct {
+    int vec;
+    int rows_per_group;
+    int waves_per_block;
+    int64_t seg_rows;
+} cconv_config_t;
+
+/* The configuration cconv_fwd (which = 0) or cconv_bwd (which = 1) uses for this shape. */
+cconv_status_t cconv_default_config(int which, int64_t B, int64_t T, int64_t D, int W,
+                                    cconv_config_t* out);
+
+cconv_status_t cconv_fwd_config(const void* x, int64_t x_sb, int64_t x_st, const void* w,
+                                cconv_dtype_t w_dtype, const float* bias, void* y, int64_t B,
+                                int64_t T, int64_t D, int W, const cconv_config_t* cfg,
+                                cconv_stream_t stream);
+
+/* Workspace for cconv_bwd_config with this configuration; 0 for an invalid one. */
+size_t cconv_bwd_workspace_bytes_config(int64_t B, int64_t T, int64_t D, int W,
+                                        const cconv_config_t* cfg);
+
+cconv_status_t cconv_bwd_config(const void* x, int64_t x_sb, int64_t x_st, const void* dy,
+                                int64_t dy_sb, int64_t dy_st, const void* w,
+                                cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
+                                cconv_dtype_t dw_dtype, float* dbias, void* workspace,
+                                size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int W,
+                                const cconv_config_t* cfg, cconv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCONV_H */

@@ -1,0 +1,188 @@
+"""Host-side contract of libcconv.so (CPU only: no kernel is ever launched here).
+
+The library must load and export every function include/*.h declares, and every problem the
+host can see must come back as its status code before any HIP call is made. Device pointers
+are fake integers: validation never dereferences them, and no case here passes validation
+with a non-empty problem.
+"""
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import causal_depthwise_short_amd as cc
+
+ROOT = Path(__file__).resolve().parent.parent
+OK, NULLP, SHAPE, STRIDE, DTYPE, MISAL, ALIAS, WS, INDEX, LAUNCH, CONFIG = range(11)
+BF16, F32 = 0, 1
+
+# fake, 16-byte aligned, widely separated device addresses
+X, DY, WT, BIAS, Y, DX, DW, DB, WSP, ST, IDX, STATUS = (0x10_0000_0000 + i * 0x1_0000_0000 for i in range(12))
+
+
+def _declared(header: Path):
+    text = re.sub(r"/\*.*?\*/", "", header.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(cconv_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    for header, path in ((ROOT / "include" / "cconv.h", cc.LIB_PATH), (ROOT / "include" / "cconv_roofline.h", cc.ROOFLINE_LIB_PATH)):
+        names = _declared(header)
+        assert names, header
+        lib = ctypes.CDLL(str(path))
+        missing = [n for n in names if not hasattr(lib, n)]
+        assert not missing, f"{path.name} lacks {missing}"
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in cc.cconv_version()
+    for code in range(11):
+        s = cc.cconv_status_string(code)
+        assert s and s != "unknown status"
+    assert cc.cconv_status_string(99) == "unknown status"
+
+
+def fwd(x=X, x_sb=None, x_st=None, w=WT, w_dt=BF16, bias=BIAS, y=Y, B=2, T=64, D=512, W=4):
+    x_st = D if x_st is None else x_st
+    x_sb = T * x_st if x_sb is None else x_sb
+    return cc.lib().cconv_fwd(x, x_sb, x_st, w, w_dt, bias, y, B, T, D, W, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(x=None), NULLP),
+        (dict(w=None), NULLP),
+        (dict(y=None), NULLP),
+        (dict(B=-1), SHAPE),
+        (dict(T=-5), SHAPE),
+        (dict(W=0), SHAPE),
+        (dict(W=5), SHAPE),
+        (dict(D=500), SHAPE),
+        (dict(x_st=504, D=512), STRIDE),
+        (dict(x_st=516), STRIDE),
+        (dict(x_sb=-8), STRIDE),
+        (dict(w_dt=7), DTYPE),
+        (dict(x=X + 2), MISAL),
+        (dict(y=Y + 8), MISAL),
+        (dict(w=WT + 4), MISAL),
+        (dict(bias=BIAS + 4), MISAL),
+        (dict(y=X), ALIAS),
+        (dict(y=X + 64 * 512), ALIAS),
+        (dict(y=WT - 16), ALIAS),
+        (dict(bias=Y + 1024), ALIAS),
+    ],
+)
+def test_fwd_host_errors(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_fwd_empty_is_ok_without_launch():
+    assert fwd(B=0) == OK
+    assert fwd(T=0) == OK
+    assert fwd(D=0) == OK
+
+
+def bwd(x=X, dy=DY, w=WT, w_dt=BF16, bias=BIAS, dx=DX, dw=DW, dw_dt=BF16, db=DB, ws=WSP, ws_bytes=1 << 40,
+        B=2, T=64, D=512, W=4, x_st=None, dy_st=None):
+    x_st = D if x_st is None else x_st
+    dy_st = D if dy_st is None else dy_st
+    return cc.lib().cconv_bwd(x, T * x_st, x_st, dy, T * dy_st, dy_st, w, w_dt, bias, dx, dw, dw_dt, db, ws, ws_bytes,
+                              B, T, D, W, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(x=None), NULLP),
+        (dict(dy=None), NULLP),
+        (dict(dx=None), NULLP),
+        (dict(dw=None), NULLP),
+        (dict(ws=None), NULLP),
+        (dict(W=7), SHAPE),
+        (dict(D=12), SHAPE),
+        (dict(dy_st=100), STRIDE),
+        (dict(dw_dt=3), DTYPE),
+        (dict(w_dt=2), DTYPE),
+        (dict(dx=DX + 2), MISAL),
+        (dict(dw=DW + 8), MISAL),
+        (dict(db=DB + 4), MISAL),
+        (dict(ws=WSP + 8), MISAL),
+        (dict(dx=DY), ALIAS),
+        (dict(dw=DX + 16), ALIAS),
+        (dict(db=DW), ALIAS),
+        (dict(ws=X), ALIAS),
+        (dict(ws_bytes=16), WS),
+    ],
+)
+def test_bwd_host_errors(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_workspace_matches_plan():
+    for B, T, D, W in [(1, 256, 512, 4), (8, 8192, 4096, 4), (3, 1000, 2000, 2), (2, 5, 8, 1)]:
+        cfg = cc.cconv_default_config("bwd", B, T, D, W)
+        assert cfg.seg_rows % cfg.rows_per_group == 0 and cfg.seg_rows >= 8
+        segs = -(-T // cfg.seg_rows)
+        groups = -(-segs // cfg.waves_per_block)
+        assert cc.cconv_bwd_workspace_bytes(B, T, D, W) == B * groups * (W + 1) * D * 4
+        # and the config entry point agrees
+        assert cc.cconv_bwd_workspace_bytes(B, T, D, W, cfg) == B * groups * (W + 1) * D * 4
+    assert cc.cconv_bwd_workspace_bytes(0, 10, 8, 4) == 0
+    bad = cc.Config(vec=8, rows_per_group=3, waves_per_block=4, seg_rows=64)
+    assert cc.cconv_bwd_workspace_bytes(2, 64, 512, 4, bad) == 0
+
+
+@pytest.mark.parametrize(
+    "cfg",
+    [
+        dict(vec=6, rows_per_group=8, waves_per_block=4, seg_rows=64),
+        dict(vec=8, rows_per_group=5, waves_per_block=4, seg_rows=64),
+        dict(vec=8, rows_per_group=8, waves_per_block=3, seg_rows=64),
+        dict(vec=8, rows_per_group=8, waves_per_block=4, seg_rows=60),
+        dict(vec=8, rows_per_group=8, waves_per_block=4, seg_rows=0),
+    ],
+)
+def test_bad_config_rejected(cfg):
+    c = cc.Config(**cfg)
+    st = cc.lib().cconv_fwd_config(X, 64 * 512, 512, WT, BF16, BIAS, Y, 2, 64, 512, 4, ctypes.byref(c), None)
+    assert st == CONFIG
+
+
+def upd(x=X, x_ld=None, state=ST, S=512, idx=IDX, w=WT, w_dt=BF16, bias=BIAS, y=Y, N=256, D=4096, W=4, status=STATUS):
+    x_ld = D if x_ld is None else x_ld
+    return cc.lib().cconv_update(x, x_ld, state, S, idx, w, w_dt, bias, y, N, D, W, status, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(x=None), NULLP),
+        (dict(state=None), NULLP),
+        (dict(y=None), NULLP),
+        (dict(W=5), SHAPE),
+        (dict(D=4100), SHAPE),
+        (dict(N=-1), SHAPE),
+        (dict(N=(1 << 24) + 1), SHAPE),
+        (dict(S=(1 << 19) + 1), SHAPE),
+        (dict(idx=None, N=600, S=512), SHAPE),
+        (dict(x_ld=4000), STRIDE),
+        (dict(x_ld=4100), STRIDE),
+        (dict(w_dt=9), DTYPE),
+        (dict(state=ST + 2), MISAL),
+        (dict(idx=IDX + 2), MISAL),
+        (dict(status=STATUS + 1), MISAL),
+        (dict(y=X), ALIAS),
+        (dict(state=WT), ALIAS),
+        (dict(status=ST + 64), ALIAS),
+        (dict(status=Y + 4), ALIAS),
+    ],
+)
+def test_update_host_errors(kw, code):
+    assert upd(**kw) == code
+
+
+def test_update_empty_without_status_is_ok():
+    assert upd(N=0, status=None) == OK

@@ -1,0 +1,259 @@
+"""GPU parity of the forward and backward against the CPU oracle, through the C ABI.
+
+Sizes the oracle finishes in seconds are compared element by element (every y, dx, dw,
+dbias); the 8x8192x4096 workload, in the launch configuration the benchmark times, is
+compared on sampled outputs the oracle computes one by one (random points plus the sequence
+start, segment boundaries, the sequence end and strip edges) and on sampled channels of dw
+and dbias (full sums over batch and time). Tolerances are in parity.py.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import causal_depthwise_short_amd as cc
+import oracle
+import synth_inputs as si
+from parity import TOL_BWD, TOL_FWD, as_f64, assert_close, bits, canaries_intact, guarded
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _gpu(inp):
+    return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+
+
+def run_train(inp, *, config_fwd=None, config_bwd=None, dw_dtype=None, want_dbias=True):
+    g = _gpu(inp)
+    y = cc.cconv_fwd(g["x"], g["w"], g["bias"], config=config_fwd)
+    dx, dw, db = cc.cconv_bwd(g["x"], g["dy"], g["w"], g["bias"], config=config_bwd, dw_dtype=dw_dtype,
+                              want_dbias=want_dbias)
+    torch.cuda.synchronize()
+    return y.cpu(), dx.cpu(), dw.cpu(), (None if db is None else db.cpu())
+
+
+def check_against_oracle(inp, outs, what):
+    y, dx, dw, db = outs
+    _, yr = oracle.fwd(inp["x"], inp["w"], inp["bias"])
+    dxr, dwr, dbr = oracle.bwd(inp["x"], inp["dy"], inp["w"], inp["bias"])
+    ey = assert_close(y, yr, TOL_FWD, f"{what} y")
+    edx = assert_close(dx, dxr, TOL_BWD, f"{what} dx")
+    edw = assert_close(dw, dwr, TOL_BWD, f"{what} dw")
+    edb = assert_close(db, dbr, TOL_BWD, f"{what} dbias") if db is not None else 0.0
+    print(f"{what}: err y {ey:.2e} dx {edx:.2e} dw {edw:.2e} dbias {edb:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("shape", [si.TINY, si.RAGGED, si.MEDIUM], ids=lambda s: s.name)
+def test_parity_full(shape):
+    inp = si.train_inputs_for(shape)
+    check_against_oracle(inp, run_train(inp), shape.name)
+
+
+@pytest.fixture(scope="module")
+def headline():
+    s = si.HEADLINE
+    inp = si.train_inputs_for(s)
+    outs = run_train(inp)
+    xf = inp["x"].float().numpy()
+    dyf = inp["dy"].float().numpy()
+    return s, inp, outs, xf, dyf
+
+
+def _sample_points(s, cfg, rng, n_random=6000):
+    B, T, D = s.B, s.T, s.D
+    pts = [np.stack([rng.integers(0, B, n_random), rng.integers(0, T, n_random), rng.integers(0, D, n_random)], 1)]
+    # sequence start, end, segment boundaries and strip edges
+    ts = {0, 1, 2, 3, 4, T - 1, T - 2, T - 3, T - 4}
+    for k in range(1, min(64, (T + cfg.seg_rows - 1) // cfg.seg_rows)):
+        for off in (-4, -3, -2, -1, 0, 1, 2, 3):
+            t = k * cfg.seg_rows + off
+            if 0 <= t < T:
+                ts.add(t)
+    strip = 64 * cfg.vec
+    ds = sorted({0, 1, 7, 8, strip - 1, strip, D - 1, D - 8} | set(int(v) for v in rng.integers(0, D, 6)))
+    ds = [d for d in ds if 0 <= d < D]
+    for b in range(B):
+        for t in sorted(ts):
+            pts.append(np.array([[b, t, d] for d in ds]))
+    p = np.concatenate(pts, 0)
+    return p[:, 0], p[:, 1], p[:, 2]
+
+
+def test_headline_sampled_parity(headline):
+    s, inp, (y, dx, dw, db), xf, dyf = headline
+    rng = np.random.default_rng(1234)
+    cfg_f = cc.cconv_default_config("fwd", s.B, s.T, s.D, s.W)
+    pb, pt, pd = _sample_points(s, cfg_f, rng)
+    yr = oracle.fwd_points(xf, inp["w"], inp["bias"], pb, pt, pd)
+    e1 = assert_close(y[pb, pt, pd], yr, TOL_FWD, "headline y (sampled)")
+    cfg_b = cc.cconv_default_config("bwd", s.B, s.T, s.D, s.W)
+    pb, pt, pd = _sample_points(s, cfg_b, rng)
+    dxr = oracle.dx_points(xf, dyf, inp["w"], inp["bias"], pb, pt, pd)
+    e2 = assert_close(dx[pb, pt, pd], dxr, TOL_BWD, "headline dx (sampled)")
+    ch = np.unique(np.concatenate([rng.integers(0, s.D, 40), [0, 1, 511, 512, s.D - 1]]))
+    dwr, dbr = oracle.dw_channels(xf, dyf, inp["w"], inp["bias"], ch)
+    e3 = assert_close(dw[ch], dwr, TOL_BWD, "headline dw (sampled channels)")
+    e4 = assert_close(db[ch], dbr, TOL_BWD, "headline dbias (sampled channels)")
+    print(f"headline sampled: err y {e1:.2e} dx {e2:.2e} dw {e3:.2e} dbias {e4:.2e} ({pb.size} points, {ch.size} channels)")
+
+
+def test_headline_outputs_finite_and_deterministic(headline):
+    s, inp, (y, dx, dw, db), _, _ = headline
+    assert torch.isfinite(y.float()).all() and torch.isfinite(dx.float()).all()
+    _, dx2, dw2, db2 = run_train(inp)
+    assert torch.equal(bits(dx2), bits(dx)), "dx differs run to run"
+    assert torch.equal(bits(dw2), bits(dw)) and torch.equal(bits(db2), bits(db)), "dw/dbias not bitwise reproducible"
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 9])
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+def test_short_sequences(T, W):
+    inp = si.train_inputs(2, T, 64, W, bias=True, seed=100 + T * 4 + W)
+    check_against_oracle(inp, run_train(inp), f"T={T} W={W}")
+
+
+@pytest.mark.parametrize("D", [8, 16, 24, 520, 1032, 2056])
+def test_channel_tails(D):
+    inp = si.train_inputs(2, 77, D, 4, bias=True, seed=200 + D)
+    check_against_oracle(inp, run_train(inp), f"D={D}")
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("w_dtype", [torch.bfloat16, torch.float32], ids=["wbf16", "wf32"])
+def test_widths_bias_dtypes(W, bias, w_dtype):
+    inp = si.train_inputs(2, 301, 264, W, bias=bias, seed=300 + W, w_dtype=w_dtype)
+    for dw_dtype in (torch.bfloat16, torch.float32):
+        outs = run_train(inp, dw_dtype=dw_dtype)
+        assert outs[2].dtype == dw_dtype
+        check_against_oracle(inp, outs, f"W={W} bias={bias} w={w_dtype} dw={dw_dtype}")
+
+
+def test_empty_problems():
+    for B, T in [(0, 16), (3, 0)]:
+        inp = si.train_inputs(B, T, 64, 4, bias=True, seed=1)
+        g = _gpu(inp)
+        y = cc.cconv_fwd(g["x"], g["w"], g["bias"])
+        dw = torch.full((64, 4), 7.0, dtype=torch.float32, device=DEV)
+        db = torch.full((64,), 7.0, dtype=torch.float32, device=DEV)
+        dx, dw, db = cc.cconv_bwd(g["x"], g["dy"], g["w"], g["bias"], dw=dw, dbias=db)
+        torch.cuda.synchronize()
+        assert y.numel() == 0 and dx.numel() == 0
+        assert not dw.any() and not db.any(), "empty batch/sequence must give zero dw/dbias"
+
+
+def test_strided_inputs_match_contiguous():
+    B, T, D, W = 2, 257, 512, 4
+    inp = si.train_inputs(B, T, D, W, bias=True, seed=7)
+    g = _gpu(inp)
+    wide_x = torch.zeros(B, T, 3 * D, dtype=torch.bfloat16, device=DEV)
+    wide_x[:, :, D : 2 * D] = g["x"]
+    wide_dy = torch.zeros(B, T + 5, 2 * D, dtype=torch.bfloat16, device=DEV)
+    wide_dy[:, :T, :D] = g["dy"]
+    xs = wide_x[:, :, D : 2 * D]
+    dys = wide_dy[:, :T, :D]
+    assert xs.stride() == (T * 3 * D, 3 * D, 1) and dys.stride() == ((T + 5) * 2 * D, 2 * D, 1)
+    y = cc.cconv_fwd(xs, g["w"], g["bias"])
+    dx, dw, db = cc.cconv_bwd(xs, dys, g["w"], g["bias"])
+    y0 = cc.cconv_fwd(g["x"], g["w"], g["bias"])
+    dx0, dw0, db0 = cc.cconv_bwd(g["x"], g["dy"], g["w"], g["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(bits(y), bits(y0)) and torch.equal(bits(dx), bits(dx0))
+    assert torch.equal(bits(dw), bits(dw0)) and torch.equal(bits(db), bits(db0))
+
+
+CONFIGS_FWD = [
+    dict(vec=8, rows_per_group=8, waves_per_block=4, seg_rows=64),
+    dict(vec=8, rows_per_group=4, waves_per_block=1, seg_rows=8),
+    dict(vec=8, rows_per_group=16, waves_per_block=8, seg_rows=96),
+    dict(vec=4, rows_per_group=8, waves_per_block=2, seg_rows=40),
+    dict(vec=4, rows_per_group=4, waves_per_block=4, seg_rows=1000),
+]
+CONFIGS_BWD = [
+    dict(vec=8, rows_per_group=4, waves_per_block=4, seg_rows=64),
+    dict(vec=8, rows_per_group=2, waves_per_block=1, seg_rows=8),
+    dict(vec=8, rows_per_group=8, waves_per_block=8, seg_rows=96),
+    dict(vec=4, rows_per_group=4, waves_per_block=2, seg_rows=40),
+    dict(vec=4, rows_per_group=8, waves_per_block=4, seg_rows=1000),
+]
+
+
+def test_launch_config_invariance():
+    """y and dx are bitwise independent of the launch shape; dw/dbias stay within tolerance."""
+    inp = si.train_inputs(3, 1000, 2000, 4, bias=True, seed=9)
+    base = run_train(inp)
+    dwr = oracle.bwd(inp["x"], inp["dy"], inp["w"], inp["bias"])
+    for cf, cb in zip(CONFIGS_FWD, CONFIGS_BWD):
+        y, dx, dw, db = run_train(inp, config_fwd=cc.Config(**cf), config_bwd=cc.Config(**cb))
+        assert torch.equal(bits(y), bits(base[0])), f"y depends on launch config {cf}"
+        assert torch.equal(bits(dx), bits(base[1])), f"dx depends on launch config {cb}"
+        assert_close(dw, dwr[1], TOL_BWD, f"dw under {cb}")
+        assert_close(db, dwr[2], TOL_BWD, f"dbias under {cb}")
+        _, _, dw2, db2 = run_train(inp, config_bwd=cc.Config(**cb))
+        assert torch.equal(bits(dw2), bits(dw)) and torch.equal(bits(db2), bits(db)), f"dw not reproducible {cb}"
+
+
+def test_w2_equals_zero_padded_w4():
+    """W=2 equals W=4 with zero taps on the oldest side (the pages' w2 check)."""
+    inp2 = si.train_inputs(2, 500, 512, 2, bias=True, seed=11)
+    inp4 = dict(inp2)
+    w4 = torch.zeros(512, 4, dtype=torch.bfloat16)
+    w4[:, 2:] = inp2["w"]
+    inp4["w"] = w4
+    y2, dx2, dw2, db2 = run_train(inp2)
+    y4, dx4, dw4, db4 = run_train(inp4)
+    assert torch.equal(y2.float(), y4.float()) and torch.equal(dx2.float(), dx4.float())
+    assert torch.equal(bits(dw2), bits(dw4[:, 2:].contiguous())) and torch.equal(bits(db2), bits(db4))
+    assert not dw4[:, :2].isnan().any()
+
+
+def test_guard_bands_and_inputs_untouched():
+    B, T, D, W = 3, 1000, 2000, 2
+    inp = si.train_inputs(B, T, D, W, bias=True, seed=13)
+    g = _gpu(inp)
+    keep = {k: bits(v) for k, v in g.items() if v is not None}
+    y, ybuf, ylo, yhi = guarded((B, T, D), torch.bfloat16, DEV)
+    dx, dxbuf, dxlo, dxhi = guarded((B, T, D), torch.bfloat16, DEV)
+    dw, dwbuf, dwlo, dwhi = guarded((D, W), torch.bfloat16, DEV)
+    db, dbbuf, dblo, dbhi = guarded((D,), torch.float32, DEV)
+    cc.cconv_fwd(g["x"], g["w"], g["bias"], y=y)
+    cc.cconv_bwd(g["x"], g["dy"], g["w"], g["bias"], dx=dx, dw=dw, dbias=db)
+    torch.cuda.synchronize()
+    for name, (buf, lo, hi) in {"y": (ybuf, ylo, yhi), "dx": (dxbuf, dxlo, dxhi), "dw": (dwbuf, dwlo, dwhi),
+                                "dbias": (dbbuf, dblo, dbhi)}.items():
+        assert canaries_intact(buf, lo, hi), f"{name} written outside its extent"
+    for k, v in g.items():
+        if v is not None:
+            assert torch.equal(bits(v), keep[k]), f"input {k} modified"
+    check_against_oracle(inp, (y.cpu(), dx.cpu(), dw.cpu(), db.cpu()), "guarded")
+
+
+def test_graph_capture_replay_bitwise():
+    """fwd + bwd captured into a HIP graph on their first call replay bit-identically."""
+    B, T, D, W = 2, 600, 1024, 4
+    inp = si.train_inputs(B, T, D, W, bias=True, seed=17)
+    g = _gpu(inp)
+    eager = run_train(inp)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    y = torch.empty(B, T, D, dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty_like(y)
+    dw = torch.empty(D, W, dtype=torch.bfloat16, device=DEV)
+    db = torch.empty(D, dtype=torch.float32, device=DEV)
+    ws = torch.empty(cc.cconv_bwd_workspace_bytes(B, T, D, W) // 4, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        cc.cconv_fwd(g["x"], g["w"], g["bias"], y=y)
+        cc.cconv_bwd(g["x"], g["dy"], g["w"], g["bias"], dx=dx, dw=dw, dbias=db, workspace=ws)
+    for rep in range(3):
+        for t in (y, dx, dw, db):
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (y.cpu(), dx.cpu(), dw.cpu(), db.cpu())
+        for a, b_, name in zip(got, eager, ("y", "dx", "dw", "dbias")):
+            assert torch.equal(bits(a), bits(b_)), f"graph replay {rep}: {name} differs from eager"
+        _ = run_train(inp)  # eager work between replays
