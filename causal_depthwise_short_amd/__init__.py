@@ -24,6 +24,8 @@ __all__ = [
     "cconv_fwd",
     "cconv_bwd",
     "cconv_bwd_workspace_bytes",
+    "cconv_bwd_main",
+    "cconv_bwd_finish",
     "cconv_update",
     "cconv_default_config",
     "cconv_status_string",
@@ -52,20 +54,24 @@ BF16, F32 = 0, 1
 
 
 class Config(ctypes.Structure):
-    """cconv_config_t: vec, rows_per_group, waves_per_block, seg_rows."""
+    """cconv_config_t: vec, rows_per_group, waves_per_block, options, seg_rows."""
 
     _fields_ = [
         ("vec", ctypes.c_int),
         ("rows_per_group", ctypes.c_int),
         ("waves_per_block", ctypes.c_int),
+        ("options", ctypes.c_int),
         ("seg_rows", ctypes.c_int64),
     ]
 
     def __repr__(self):
         return (
             f"Config(vec={self.vec}, rows_per_group={self.rows_per_group}, "
-            f"waves_per_block={self.waves_per_block}, seg_rows={self.seg_rows})"
+            f"waves_per_block={self.waves_per_block}, options={self.options}, seg_rows={self.seg_rows})"
         )
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 class CconvError(RuntimeError):
@@ -94,6 +100,10 @@ def _declare(L):
     L.cconv_bwd.restype = i32
     L.cconv_bwd_config.argtypes = bwd + [ctypes.POINTER(Config), p]
     L.cconv_bwd_config.restype = i32
+    L.cconv_bwd_main.argtypes = [p, i64, i64, p, i64, i64, p, i32, p, p, p, sz, i64, i64, i64, i32, p]
+    L.cconv_bwd_main.restype = i32
+    L.cconv_bwd_finish.argtypes = [p, sz, p, i32, p, i64, i64, i64, i32, p]
+    L.cconv_bwd_finish.restype = i32
     L.cconv_update.argtypes = [p, i64, p, i64, p, p, i32, p, p, i64, i64, i32, p, p]
     L.cconv_update.restype = i32
     L.cconv_default_config.argtypes = [i32, i64, i64, i64, i32, ctypes.POINTER(Config)]
@@ -273,6 +283,35 @@ def cconv_bwd(
     else:
         _check(L.cconv_bwd_config(*args, ctypes.byref(config), _stream(stream)), "cconv_bwd_config")
     return dx, dw, dbias
+
+
+def cconv_bwd_main(x, dy, w, bias, dx, workspace, *, stream=None):
+    """First backward stage: dx and the fp32 dw/dbias partials (into `workspace`)."""
+    sb, st = _act(x, "x")
+    dsb, dst = _act(dy, "dy")
+    B, T, D = x.shape
+    W = w.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(
+        lib().cconv_bwd_main(
+            _ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(dx), _ptr(workspace),
+            ws_bytes, B, T, D, W, _stream(stream),
+        ),
+        "cconv_bwd_main",
+    )
+    return dx
+
+
+def cconv_bwd_finish(workspace, dw, dbias, B: int, T: int, D: int, W: int, *, stream=None):
+    """Second backward stage: dw (in dw's dtype) and dbias from the partials."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(
+        lib().cconv_bwd_finish(
+            _ptr(workspace), ws_bytes, _ptr(dw), _wdt(dw, "dw"), _ptr(dbias), B, T, D, W, _stream(stream)
+        ),
+        "cconv_bwd_finish",
+    )
+    return dw, dbias
 
 
 def cconv_update(x, state, state_indices, w, bias=None, *, y=None, status=None, stream=None):

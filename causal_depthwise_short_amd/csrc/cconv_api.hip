@@ -17,7 +17,9 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 40;        // any one size or stride
 constexpr int64_t kMaxDecodeRows = int64_t(1) << 24;  // N
 constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices (LDS bit set)
-constexpr int64_t kTargetWaves = 4096;  // 16 waves per CU over 256 CUs: one full round
+constexpr int64_t kFwdWaves = 1024;     // forward grid: one wave per SIMD (256 CUs x 4)
+constexpr int64_t kBwdWaves = 2048;     // backward grid: two waves per SIMD
+constexpr int kNtLoadStore = 3;         // non-temporal loads and stores (streamed once)
 constexpr int64_t kMinSeg = 64;         // shorter segments re-read too large a share of rows
 constexpr int64_t kUpdateTargetBlocks = 1024;
 
@@ -25,7 +27,9 @@ struct Span {
     uintptr_t lo, hi;
 };
 
+// The byte range of an operand; an absent (NULL) operand occupies nothing.
 Span span(const void* p, __int128 bytes) {
+    if (!p) return {0, 0};
     const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
     return {lo, lo + static_cast<uintptr_t>(bytes)};
 }
@@ -50,17 +54,25 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
     if (c.waves_per_block != 1 && c.waves_per_block != 2 && c.waves_per_block != 4 && c.waves_per_block != 8)
         return false;
     if (c.seg_rows < 8 || c.seg_rows > kMaxDim || c.seg_rows % c.rows_per_group != 0) return false;
+    if (c.options < 0 || c.options > 7) return false;
     return true;
 }
 
+// The static launch table. One wave per (channel strip, time segment, batch row); segments
+// are sized so the grid holds about kFwdWaves / kBwdWaves waves, i.e. one (forward) or two
+// (backward, register-limited to two waves per SIMD) waves per SIMD of the 256 CUs, each
+// streaming a long run of rows; never below kMinSeg rows (the re-read W-1 rows per segment
+// stay under 5%). The backward packs 8 waves (8 consecutive segments) per block so their dw
+// partials are summed in LDS before one partial per block is written.
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) {
     (void)W;
     cconv_config_t c;
     c.vec = 8;
     c.rows_per_group = bwd ? 4 : 8;
-    c.waves_per_block = 4;
+    c.waves_per_block = bwd ? 8 : 1;
+    c.options = kNtLoadStore;
     const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
-    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / kTargetWaves;
+    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / (bwd ? kBwdWaves : kFwdWaves);
     ts = std::max(kMinSeg, ts - ts % 8);
     const int64_t tcap = ((std::max<int64_t>(T, 1) + 7) / 8) * 8;
     c.seg_rows = std::min(ts, std::max<int64_t>(8, tcap));
@@ -72,6 +84,7 @@ bool make_plan(const cconv_config_t& c, int64_t B, int64_t T, int64_t D, Plan* p
     p->group = c.rows_per_group;
     p->waves = c.waves_per_block;
     p->seg_rows = c.seg_rows;
+    p->options = c.options;
     p->strips = (D + 64 * c.vec - 1) / (64 * c.vec);
     p->segs = (T + c.seg_rows - 1) / c.seg_rows;
     p->seg_groups = (p->segs + c.waves_per_block - 1) / c.waves_per_block;
@@ -143,12 +156,31 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
                                                                                            : CCONV_ERR_LAUNCH;
 }
 
-cconv_status_t bwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb, int64_t dy_st,
-                        const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
+// Stages of the backward: kMain computes dx and the fp32 partials in the workspace, kFinish
+// reduces the partials into dw and dbias. cconv_bwd runs both.
+constexpr int kMain = 1, kFinish = 2;
+
+cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
+                        int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
                         cconv_dtype_t dw_dtype, float* dbias, void* workspace, size_t workspace_bytes, int64_t B,
                         int64_t T, int64_t D, int W, const cconv_config_t* cfg, cconv_stream_t stream) {
     const bool act_empty = (B == 0 || T == 0 || D == 0);
-    if (((!x || !dy || !dx) && !act_empty) || ((!w || !dw) && D > 0)) return CCONV_ERR_NULL_POINTER;
+    const bool main = (stages & kMain) != 0, finish = (stages & kFinish) != 0;
+    if (main && (((!x || !dy || !dx) && !act_empty) || (!w && D > 0))) return CCONV_ERR_NULL_POINTER;
+    if (finish && !dw && D > 0) return CCONV_ERR_NULL_POINTER;
+    if (!main) {  // the finishing stage reads only the workspace: treat the inputs as absent
+        x = dy = w = nullptr;
+        dx = nullptr;
+        bias = nullptr;
+        x_sb = dy_sb = 0;
+        x_st = dy_st = D;
+        w_dtype = CCONV_BF16;
+    }
+    if (!finish) {
+        dw = nullptr;
+        dbias = nullptr;
+        dw_dtype = CCONV_BF16;
+    }
     cconv_status_t st = check_train_common(w, w_dtype, bias, B, T, D, W);
     if (st != CCONV_OK) return st;
     if (!dtype_ok(dw_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
@@ -183,7 +215,7 @@ cconv_status_t bwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* d
 
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool empty = (B == 0 || T == 0);
-    if (!empty) {
+    if (main && !empty) {
         cconv::BwdArgs a;
         a.x = static_cast<const uint16_t*>(x);
         a.x_sb = x_sb;
@@ -204,6 +236,7 @@ cconv_status_t bwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* d
         a.seg_groups = p.seg_groups;
         if (cconv::launch_bwd(p, W, a, s) != hipSuccess) return CCONV_ERR_LAUNCH;
     }
+    if (!finish) return CCONV_OK;
     cconv::ReduceArgs r;
     r.partial = static_cast<const float*>(workspace);
     r.P = empty ? 0 : p.partials;
@@ -249,8 +282,22 @@ cconv_status_t cconv_bwd(const void* x, int64_t x_sb, int64_t x_st, const void* 
                          const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
                          cconv_dtype_t dw_dtype, float* dbias, void* workspace, size_t workspace_bytes, int64_t B,
                          int64_t T, int64_t D, int W, cconv_stream_t stream) {
-    return bwd_impl(x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias, workspace,
-                    workspace_bytes, B, T, D, W, nullptr, stream);
+    return bwd_impl(kMain | kFinish, x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias,
+                    workspace, workspace_bytes, B, T, D, W, nullptr, stream);
+}
+
+cconv_status_t cconv_bwd_main(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
+                              int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx,
+                              void* workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int W,
+                              cconv_stream_t stream) {
+    return bwd_impl(kMain, x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, nullptr, CCONV_BF16, nullptr,
+                    workspace, workspace_bytes, B, T, D, W, nullptr, stream);
+}
+
+cconv_status_t cconv_bwd_finish(const void* workspace, size_t workspace_bytes, void* dw, cconv_dtype_t dw_dtype,
+                                float* dbias, int64_t B, int64_t T, int64_t D, int W, cconv_stream_t stream) {
+    return bwd_impl(kFinish, nullptr, 0, D, nullptr, 0, D, nullptr, CCONV_BF16, nullptr, nullptr, dw, dw_dtype,
+                    dbias, const_cast<void*>(workspace), workspace_bytes, B, T, D, W, nullptr, stream);
 }
 
 cconv_status_t cconv_bwd_config(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
@@ -259,8 +306,8 @@ cconv_status_t cconv_bwd_config(const void* x, int64_t x_sb, int64_t x_st, const
                                 size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int W,
                                 const cconv_config_t* cfg, cconv_stream_t stream) {
     if (!cfg) return CCONV_ERR_NULL_POINTER;
-    return bwd_impl(x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias, workspace,
-                    workspace_bytes, B, T, D, W, cfg, stream);
+    return bwd_impl(kMain | kFinish, x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias,
+                    workspace, workspace_bytes, B, T, D, W, cfg, stream);
 }
 
 cconv_status_t cconv_default_config(int which, int64_t B, int64_t T, int64_t D, int W, cconv_config_t* out) {

@@ -22,7 +22,7 @@ namespace cconv {
 
 // One backward row t. `acc_on`: the row belongs to this segment (accumulate dw/dbias);
 // `emit`: dx of row t-(W-1) is this segment's and gets stored.
-template <int VEC, int W>
+template <int VEC, int W, bool NTS>
 __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float (&b)[VEC],
                                         const Row<VEC>& rx, const Row<VEC>& rdy,
                                         float (&xr)[W > 1 ? W - 1 : 1][VEC],
@@ -59,7 +59,7 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
             for (int k = 1; k < W; ++k) s = __builtin_fmaf(tap[k][v], k == W - 1 ? g[v] : gr[W - 2 - k][v], s);
             dx[v] = s;
         }
-        store_row<VEC>(dxp, narrow<VEC>(dx));
+        store_row<VEC, NTS>(dxp, narrow<VEC>(dx));
     }
 #pragma unroll
     for (int k = W - 2; k > 0; --k)
@@ -77,9 +77,10 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
     }
 }
 
-template <int VEC, int G, int W>
+template <int VEC, int G, int W, int F>
 __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
     constexpr int R = W > 1 ? W - 1 : 1;
+    constexpr bool NTL = (F & kNtLoad) != 0, NTS = (F & kNtStore) != 0, PF = (F & kPrefetch) != 0;
     extern __shared__ float red[];  // [waves][VEC][64], one column at a time
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t strip = tile % a.strips;
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
     const int64_t sg = rest % a.seg_groups;
     const int64_t b = rest / a.seg_groups;
     const int waves = blockDim.x / kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
     const int64_t t0 = (sg * waves + wave) * a.seg_rows;
     const int64_t t1 = min(t0 + a.seg_rows, a.T);
@@ -128,22 +129,51 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
         }
 
         int64_t t = t0;
-        for (; t + G <= t1; t += G) {
-            Row<VEC> rx[G], rdy[G];
+        if constexpr (PF) {
+            // Software pipeline: the next group's x and dy loads are in flight while this
+            // group is computed. The look-ahead row is clamped into the segment.
+            if (t + G <= t1) {
+                Row<VEC> cx[G], cdy[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) rx[g] = load_row<VEC>(xp + (t + g) * xs);
+                for (int g = 0; g < G; ++g) cx[g] = load_row<VEC, NTL>(xp + (t + g) * xs);
 #pragma unroll
-            for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC>(dyp + (t + g) * dys);
+                for (int g = 0; g < G; ++g) cdy[g] = load_row<VEC, NTL>(dyp + (t + g) * dys);
+                for (; t + G <= t1; t += G) {
+                    Row<VEC> nx[G], ndy[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int64_t u = t + g - (W - 1);
-                bwd_row<VEC, W>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, true, u >= t0, dxp + u * dxs);
+                    for (int g = 0; g < G; ++g) nx[g] = load_row<VEC, NTL>(xp + min(t + G + g, t1 - 1) * xs);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) ndy[g] = load_row<VEC, NTL>(dyp + min(t + G + g, t1 - 1) * dys);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const int64_t u = t + g - (W - 1);
+                        bwd_row<VEC, W, NTS>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, true, u >= t0, dxp + u * dxs);
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        cx[g] = nx[g];
+                        cdy[g] = ndy[g];
+                    }
+                }
+            }
+        } else {
+            for (; t + G <= t1; t += G) {
+                Row<VEC> rx[G], rdy[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NTL>(xp + (t + g) * xs);
+#pragma unroll
+                for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC, NTL>(dyp + (t + g) * dys);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int64_t u = t + g - (W - 1);
+                    bwd_row<VEC, W, NTS>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, true, u >= t0, dxp + u * dxs);
+                }
             }
         }
         for (; t < t1; ++t) {
             const int64_t u = t - (W - 1);
-            bwd_row<VEC, W>(tap, bs, load_row<VEC>(xp + t * xs), load_row<VEC>(dyp + t * dys), xr, gr, acc,
-                            db, true, u >= t0, dxp + u * dxs);
+            bwd_row<VEC, W, NTS>(tap, bs, load_row<VEC, NTL>(xp + t * xs), load_row<VEC, NTL>(dyp + t * dys), xr,
+                                 gr, acc, db, true, u >= t0, dxp + u * dxs);
         }
         // right halo: rows t1 .. t1+W-2 finish dx of this segment's last W-1 rows; rows at or
         // past T have g = 0 (their x and dy read as zero).
@@ -152,9 +182,12 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
             const int64_t th = t1 + h;
             const int64_t u = th - (W - 1);
             const bool in = th < a.T;
-            const Row<VEC> hx = in ? load_row<VEC>(xp + th * xs) : zero_row<VEC>();
-            const Row<VEC> hdy = in ? load_row<VEC>(dyp + th * dys) : zero_row<VEC>();
-            bwd_row<VEC, W>(tap, bs, hx, hdy, xr, gr, acc, db, false, u >= t0, dxp + u * dxs);
+            Row<VEC> hx = zero_row<VEC>(), hdy = zero_row<VEC>();
+            if (in) {
+                hx = load_row<VEC>(xp + th * xs);
+                hdy = load_row<VEC>(dyp + th * dys);
+            }
+            bwd_row<VEC, W, NTS>(tap, bs, hx, hdy, xr, gr, acc, db, false, u >= t0, dxp + u * dxs);
         }
     }
 
@@ -189,9 +222,11 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
 
 // dw[d, j] = sum_p partial[p, j, d] (j < W), dbias[d] = sum_p partial[p, W, d]. A block
 // handles 64 consecutive (j, d) entries; its 4 waves each sum a contiguous quarter of the
-// partials in ascending order, then the four sums are added in wave order. P == 0 writes
-// zeros (an empty batch or sequence).
+// partials in ascending order, then the four sums are added in wave order. Loads are issued
+// in batches of kBatch before they are summed, so a quarter of up to kBatch partials costs one
+// memory latency. P == 0 writes zeros (an empty batch or sequence).
 __global__ __launch_bounds__(256) void cconv_dw_reduce_kernel(const ReduceArgs a) {
+    constexpr int kBatch = 16;
     __shared__ float part[4][kWave];
     const int lane = threadIdx.x % kWave, q = threadIdx.x / kWave;
     const int64_t E = static_cast<int64_t>(a.W + 1) * a.D;
@@ -201,15 +236,14 @@ __global__ __launch_bounds__(256) void cconv_dw_reduce_kernel(const ReduceArgs a
         const int64_t chunk = (a.P + 3) / 4;
         const int64_t p0 = q * chunk, p1 = min(a.P, p0 + chunk);
         const float* __restrict__ src = a.partial + e;
-        int64_t p = p0;
-        for (; p + 4 <= p1; p += 4) {
-            const float v0 = src[(p + 0) * E], v1 = src[(p + 1) * E], v2 = src[(p + 2) * E], v3 = src[(p + 3) * E];
-            s += v0;
-            s += v1;
-            s += v2;
-            s += v3;
+        for (int64_t p = p0; p < p1; p += kBatch) {
+            float v[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) v[i] = (p + i < p1) ? src[(p + i) * E] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                if (p + i < p1) s += v[i];
         }
-        for (; p < p1; ++p) s += src[p * E];
     }
     part[q][lane] = s;
     __syncthreads();
@@ -230,35 +264,50 @@ __global__ __launch_bounds__(256) void cconv_dw_reduce_kernel(const ReduceArgs a
 
 namespace {
 
-template <int VEC, int G>
-hipError_t launch_bwd_w(int W, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
-    switch (W) {
-        case 1: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, 1>), grid, block, lds, s, a); break;
-        case 2: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, 2>), grid, block, lds, s, a); break;
-        case 3: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, 3>), grid, block, lds, s, a); break;
-        case 4: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, 4>), grid, block, lds, s, a); break;
+template <int VEC, int G, int W>
+hipError_t launch_bwd_f(int F, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
+    switch (F) {
+#define CCONV_BWD_CASE(f) \
+    case f: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, W, f>), grid, block, lds, s, a); break;
+        CCONV_BWD_CASE(0)
+        CCONV_BWD_CASE(1)
+        CCONV_BWD_CASE(2)
+        CCONV_BWD_CASE(3)
+        CCONV_BWD_CASE(4)
+        CCONV_BWD_CASE(5)
+        CCONV_BWD_CASE(6)
+        CCONV_BWD_CASE(7)
+#undef CCONV_BWD_CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <int VEC, int G>
+hipError_t launch_bwd_w(int W, int F, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
+    switch (W) {
+        case 1: return launch_bwd_f<VEC, G, 1>(F, grid, block, lds, a, s);
+        case 2: return launch_bwd_f<VEC, G, 2>(F, grid, block, lds, a, s);
+        case 3: return launch_bwd_f<VEC, G, 3>(F, grid, block, lds, a, s);
+        case 4: return launch_bwd_f<VEC, G, 4>(F, grid, block, lds, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
-bool bwd_variant_exists(int vec, int group) {
-    return (vec == 4 || vec == 8) && (group == 2 || group == 4 || group == 8);
-}
+bool bwd_variant_exists(int vec, int group) { return (vec == 4 || vec == 8) && (group == 4 || group == 8); }
 
 hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
     const size_t lds = static_cast<size_t>(p.waves) * p.vec * kWave * sizeof(float);
+    const int F = p.options;
     if (p.vec == 8) {
-        if (p.group == 2) return launch_bwd_w<8, 2>(W, grid, block, lds, a, s);
-        if (p.group == 4) return launch_bwd_w<8, 4>(W, grid, block, lds, a, s);
-        if (p.group == 8) return launch_bwd_w<8, 8>(W, grid, block, lds, a, s);
+        if (p.group == 4) return launch_bwd_w<8, 4>(W, F, grid, block, lds, a, s);
+        if (p.group == 8) return launch_bwd_w<8, 8>(W, F, grid, block, lds, a, s);
     } else if (p.vec == 4) {
-        if (p.group == 2) return launch_bwd_w<4, 2>(W, grid, block, lds, a, s);
-        if (p.group == 4) return launch_bwd_w<4, 4>(W, grid, block, lds, a, s);
-        if (p.group == 8) return launch_bwd_w<4, 8>(W, grid, block, lds, a, s);
+        if (p.group == 4) return launch_bwd_w<4, 4>(W, F, grid, block, lds, a, s);
+        if (p.group == 8) return launch_bwd_w<4, 8>(W, F, grid, block, lds, a, s);
     }
     return hipErrorInvalidValue;
 }

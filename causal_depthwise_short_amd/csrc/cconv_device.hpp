@@ -23,18 +23,32 @@ struct Row {
     uint32_t u[VEC / 2];
 };
 
-template <int VEC>
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// NT selects non-temporal loads/stores (streamed data that is not re-read soon).
+template <int VEC, bool NT = false>
 __device__ __forceinline__ Row<VEC> load_row(const uint16_t* __restrict__ p) {
     static_assert(VEC == 4 || VEC == 8, "VEC is 4 or 8");
     Row<VEC> r;
     if constexpr (VEC == 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        u32x4 v;
+        if constexpr (NT) {
+            v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        } else {
+            v = *reinterpret_cast<const u32x4*>(p);
+        }
         r.u[0] = v.x;
         r.u[1] = v.y;
         r.u[2] = v.z;
         r.u[3] = v.w;
     } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        u32x2 v;
+        if constexpr (NT) {
+            v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        } else {
+            v = *reinterpret_cast<const u32x2*>(p);
+        }
         r.u[0] = v.x;
         r.u[1] = v.y;
     }
@@ -49,14 +63,32 @@ __device__ __forceinline__ Row<VEC> zero_row() {
     return r;
 }
 
-template <int VEC>
+template <int VEC, bool NT = false>
 __device__ __forceinline__ void store_row(uint16_t* __restrict__ p, const Row<VEC>& r) {
     if constexpr (VEC == 8) {
-        *reinterpret_cast<uint4*>(p) = make_uint4(r.u[0], r.u[1], r.u[2], r.u[3]);
+        const u32x4 v = {r.u[0], r.u[1], r.u[2], r.u[3]};
+        if constexpr (NT) {
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+        } else {
+            *reinterpret_cast<u32x4*>(p) = v;
+        }
     } else {
-        *reinterpret_cast<uint2*>(p) = make_uint2(r.u[0], r.u[1]);
+        const u32x2 v = {r.u[0], r.u[1]};
+        if constexpr (NT) {
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+        } else {
+            *reinterpret_cast<u32x2*>(p) = v;
+        }
     }
 }
+
+// Option bits of the row kernels (a template parameter).
+constexpr int kNtLoad = 1;    // non-temporal loads of x (and dy)
+constexpr int kNtStore = 2;   // non-temporal stores of y (dx)
+constexpr int kPrefetch = 4;  // next group's loads issued before the current group's math
+
+// The wave's index in its block, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 
 // bf16 -> fp32 is exact: the bf16 pattern is the high half of the fp32 pattern.
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }

@@ -38,15 +38,16 @@ __device__ __forceinline__ Row<VEC> fwd_row(const float (&tap)[W][VEC], const fl
     return narrow<VEC>(y);
 }
 
-template <int VEC, int G, int W>
+template <int VEC, int G, int W, int F>
 __global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
     constexpr int R = W > 1 ? W - 1 : 1;
+    constexpr bool NTL = (F & kNtLoad) != 0, NTS = (F & kNtStore) != 0, PF = (F & kPrefetch) != 0;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t strip = tile % a.strips;
     const int64_t rest = tile / a.strips;
     const int64_t sg = rest % a.seg_groups;
     const int64_t b = rest / a.seg_groups;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
     const int64_t t0 = (sg * (blockDim.x / kWave) + wave) * a.seg_rows;
     if (t0 >= a.T) return;  // a trailing wave of the last segment group
@@ -77,46 +78,84 @@ __global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
     }
 
     int64_t t = t0;
-    for (; t + G <= t1; t += G) {
-        Row<VEC> raw[G];
+    if constexpr (PF) {
+        // Software pipeline: while a group is computed, the next group's loads are in flight.
+        // The look-ahead row index is clamped into the segment, so the last iteration re-reads
+        // valid rows instead of running past them.
+        if (t + G <= t1) {
+            Row<VEC> cur[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) raw[g] = load_row<VEC>(xp + (t + g) * xs);
+            for (int g = 0; g < G; ++g) cur[g] = load_row<VEC, NTL>(xp + (t + g) * xs);
+            for (; t + G <= t1; t += G) {
+                Row<VEC> nxt[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) store_row<VEC>(yp + (t + g) * ys, fwd_row<VEC, W>(tap, bs, raw[g], ring));
+                for (int g = 0; g < G; ++g) nxt[g] = load_row<VEC, NTL>(xp + min(t + G + g, t1 - 1) * xs);
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    store_row<VEC, NTS>(yp + (t + g) * ys, fwd_row<VEC, W>(tap, bs, cur[g], ring));
+#pragma unroll
+                for (int g = 0; g < G; ++g) cur[g] = nxt[g];
+            }
+        }
+    } else {
+        for (; t + G <= t1; t += G) {
+            Row<VEC> raw[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) raw[g] = load_row<VEC, NTL>(xp + (t + g) * xs);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                store_row<VEC, NTS>(yp + (t + g) * ys, fwd_row<VEC, W>(tap, bs, raw[g], ring));
+        }
     }
-    for (; t < t1; ++t) store_row<VEC>(yp + t * ys, fwd_row<VEC, W>(tap, bs, load_row<VEC>(xp + t * xs), ring));
+    for (; t < t1; ++t)
+        store_row<VEC, NTS>(yp + t * ys, fwd_row<VEC, W>(tap, bs, load_row<VEC, NTL>(xp + t * xs), ring));
 }
 
 namespace {
 
-template <int VEC, int G>
-hipError_t launch_fwd_w(int W, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
-    switch (W) {
-        case 1: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, 1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, 2>), grid, block, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, 3>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, 4>), grid, block, 0, s, a); break;
+template <int VEC, int G, int W>
+hipError_t launch_fwd_f(int F, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
+    switch (F) {
+#define CCONV_FWD_CASE(f) \
+    case f: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, W, f>), grid, block, 0, s, a); break;
+        CCONV_FWD_CASE(0)
+        CCONV_FWD_CASE(1)
+        CCONV_FWD_CASE(2)
+        CCONV_FWD_CASE(3)
+        CCONV_FWD_CASE(4)
+        CCONV_FWD_CASE(5)
+        CCONV_FWD_CASE(6)
+        CCONV_FWD_CASE(7)
+#undef CCONV_FWD_CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <int VEC, int G>
+hipError_t launch_fwd_w(int W, int F, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
+    switch (W) {
+        case 1: return launch_fwd_f<VEC, G, 1>(F, grid, block, a, s);
+        case 2: return launch_fwd_f<VEC, G, 2>(F, grid, block, a, s);
+        case 3: return launch_fwd_f<VEC, G, 3>(F, grid, block, a, s);
+        case 4: return launch_fwd_f<VEC, G, 4>(F, grid, block, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
-bool fwd_variant_exists(int vec, int group) {
-    return (vec == 4 || vec == 8) && (group == 4 || group == 8 || group == 16);
-}
+bool fwd_variant_exists(int vec, int group) { return (vec == 4 || vec == 8) && (group == 4 || group == 8); }
 
 hipError_t launch_fwd(const Plan& p, int W, const FwdArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
+    const int F = p.options;
     if (p.vec == 8) {
-        if (p.group == 4) return launch_fwd_w<8, 4>(W, grid, block, a, s);
-        if (p.group == 8) return launch_fwd_w<8, 8>(W, grid, block, a, s);
-        if (p.group == 16) return launch_fwd_w<8, 16>(W, grid, block, a, s);
+        if (p.group == 4) return launch_fwd_w<8, 4>(W, F, grid, block, a, s);
+        if (p.group == 8) return launch_fwd_w<8, 8>(W, F, grid, block, a, s);
     } else if (p.vec == 4) {
-        if (p.group == 4) return launch_fwd_w<4, 4>(W, grid, block, a, s);
-        if (p.group == 8) return launch_fwd_w<4, 8>(W, grid, block, a, s);
-        if (p.group == 16) return launch_fwd_w<4, 16>(W, grid, block, a, s);
+        if (p.group == 4) return launch_fwd_w<4, 4>(W, F, grid, block, a, s);
+        if (p.group == 8) return launch_fwd_w<4, 8>(W, F, grid, block, a, s);
     }
     return hipErrorInvalidValue;
 }

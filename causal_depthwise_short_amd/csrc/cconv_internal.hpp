@@ -16,6 +16,7 @@ struct Plan {
     int group;
     int waves;
     int64_t seg_rows;
+    int options;  // kNtLoad | kNtStore | kPrefetch
     // derived
     int64_t strips;      // ceil(D / (64*vec))
     int64_t segs;        // ceil(T / seg_rows)

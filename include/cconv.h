@@ -107,6 +107,22 @@ cconv_status_t cconv_bwd(const void* x, int64_t x_sb, int64_t x_st, const void* 
                          int64_t T, int64_t D, int W, cconv_stream_t stream);
 
 /*
+ * The backward's two stages, for callers that want the fp32 partials themselves (a
+ * data-parallel caller can sum them across ranks before the final cast) or that time the
+ * stages apart. cconv_bwd_main writes dx and fills the workspace with fp32 dw/dbias partial
+ * sums; cconv_bwd_finish sums the partials in a fixed order into dw (dw_dtype) and dbias
+ * (fp32, or NULL). Both take the same B, T, D, W as the cconv_bwd call they split, and
+ * cconv_bwd == cconv_bwd_main followed by cconv_bwd_finish, bit for bit.
+ */
+cconv_status_t cconv_bwd_main(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
+                              int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx,
+                              void* workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int W,
+                              cconv_stream_t stream);
+
+cconv_status_t cconv_bwd_finish(const void* workspace, size_t workspace_bytes, void* dw, cconv_dtype_t dw_dtype,
+                                float* dbias, int64_t B, int64_t T, int64_t D, int W, cconv_stream_t stream);
+
+/*
  * One-token decode update [PR #797 description: `CausalConv1dUpdate` API and semantics].
  *   x       bf16 [N, D], row n at x + n*x_ld, x_ld >= D (a slice of a wider projection).
  *   state   bf16 [S, D, W-1] contiguous, in/out, oldest first: state[s, d, j] holds the
@@ -140,15 +156,19 @@ const char* cconv_version(void);
  * not depend on the configuration (bitwise); dw and dbias depend on it only through the
  * order of their fixed-order sum.
  *   vec              channels per lane: 4 or 8 (8 or 16 bytes per row per lane)
- *   rows_per_group   rows whose loads are issued together: fwd 4, 8 or 16; bwd 2, 4 or 8
+ *   rows_per_group   rows whose loads are issued together: 4 or 8
  *   waves_per_block  1, 2, 4 or 8 waves; the waves of a block take consecutive time
  *                    segments of the same channel strip and batch row
  *   seg_rows         rows per wave segment: a multiple of rows_per_group, >= 8
+ *   options          bit 0: non-temporal loads of x (and dy); bit 1: non-temporal stores of
+ *                    y (dx); bit 2: issue the next row group's loads before the current
+ *                    group's arithmetic (software prefetch). Results do not depend on them.
  */
 typedef struct {
     int vec;
     int rows_per_group;
     int waves_per_block;
+    int options;
     int64_t seg_rows;
 } cconv_config_t;
 

@@ -186,3 +186,17 @@ def test_update_host_errors(kw, code):
 
 def test_update_empty_without_status_is_ok():
     assert upd(N=0, status=None) == OK
+
+
+def test_bwd_stages_host_errors():
+    L = cc.lib()
+    D, T, B, W = 512, 64, 2, 4
+    main = lambda **k: L.cconv_bwd_main(k.get("x", X), T * D, D, k.get("dy", DY), T * D, D, k.get("w", WT), BF16,
+                                        BIAS, k.get("dx", DX), k.get("ws", WSP), k.get("ws_bytes", 1 << 40), B, T, D, W,
+                                        None)
+    fin = lambda **k: L.cconv_bwd_finish(k.get("ws", WSP), k.get("ws_bytes", 1 << 40), k.get("dw", DW),
+                                         k.get("dw_dt", BF16), k.get("db", DB), B, T, D, W, None)
+    assert main(x=None) == NULLP and main(dx=None) == NULLP and main(ws=None) == NULLP
+    assert main(dx=X) == ALIAS and main(ws=DY) == ALIAS and main(ws_bytes=8) == WS
+    assert fin(dw=None) == NULLP and fin(ws=None) == NULLP and fin(dw_dt=5) == DTYPE
+    assert fin(dw=WSP) == ALIAS and fin(db=DW) == ALIAS and fin(ws_bytes=8) == WS and fin(db=DB + 4) == MISAL

@@ -22,9 +22,12 @@ DEV = "cuda"
 CCONV_OK, CCONV_ERR_INDEX = 0, 8
 
 
-def run_update(inp, *, x=None, idx="inp"):
+_FROM_INPUTS = object()
+
+
+def run_update(inp, *, x=None, idx=_FROM_INPUTS):
     g = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
-    if idx != "inp":
+    if idx is not _FROM_INPUTS:
         g["state_indices"] = None if idx is None else torch.as_tensor(idx, dtype=torch.int32, device=DEV)
     xs = g["x"] if x is None else x
     y, status = cc.cconv_update(xs, g["state"], g["state_indices"], g["w"], g["bias"])

@@ -168,13 +168,13 @@ def test_strided_inputs_match_contiguous():
 CONFIGS_FWD = [
     dict(vec=8, rows_per_group=8, waves_per_block=4, seg_rows=64),
     dict(vec=8, rows_per_group=4, waves_per_block=1, seg_rows=8),
-    dict(vec=8, rows_per_group=16, waves_per_block=8, seg_rows=96),
+    dict(vec=8, rows_per_group=8, waves_per_block=8, options=4, seg_rows=96),
     dict(vec=4, rows_per_group=8, waves_per_block=2, seg_rows=40),
     dict(vec=4, rows_per_group=4, waves_per_block=4, seg_rows=1000),
 ]
 CONFIGS_BWD = [
     dict(vec=8, rows_per_group=4, waves_per_block=4, seg_rows=64),
-    dict(vec=8, rows_per_group=2, waves_per_block=1, seg_rows=8),
+    dict(vec=8, rows_per_group=4, waves_per_block=1, options=5, seg_rows=8),
     dict(vec=8, rows_per_group=8, waves_per_block=8, seg_rows=96),
     dict(vec=4, rows_per_group=4, waves_per_block=2, seg_rows=40),
     dict(vec=4, rows_per_group=8, waves_per_block=4, seg_rows=1000),
@@ -257,3 +257,28 @@ def test_graph_capture_replay_bitwise():
         for a, b_, name in zip(got, eager, ("y", "dx", "dw", "dbias")):
             assert torch.equal(bits(a), bits(b_)), f"graph replay {rep}: {name} differs from eager"
         _ = run_train(inp)  # eager work between replays
+
+
+def test_two_stage_backward_equals_fused():
+    B, T, D, W = 3, 1000, 2000, 2
+    inp = si.train_inputs(B, T, D, W, bias=True, seed=19)
+    g = _gpu(inp)
+    dx0, dw0, db0 = cc.cconv_bwd(g["x"], g["dy"], g["w"], g["bias"])
+    ws = torch.empty(cc.cconv_bwd_workspace_bytes(B, T, D, W) // 4, dtype=torch.float32, device=DEV)
+    dx = torch.empty_like(dx0)
+    dw = torch.empty_like(dw0)
+    db = torch.empty_like(db0)
+    cc.cconv_bwd_main(g["x"], g["dy"], g["w"], g["bias"], dx, ws)
+    cc.cconv_bwd_finish(ws, dw, db, B, T, D, W)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(dx), bits(dx0)) and torch.equal(bits(dw), bits(dw0)) and torch.equal(bits(db), bits(db0))
+
+
+def test_launch_options_do_not_change_results():
+    inp = si.train_inputs(2, 700, 1024, 4, bias=True, seed=23)
+    base = run_train(inp)
+    for h in range(1, 8):
+        cf = cc.Config(vec=8, rows_per_group=8, waves_per_block=2, options=h, seg_rows=128)
+        cb = cc.Config(vec=4, rows_per_group=8, waves_per_block=4, options=h, seg_rows=128)
+        y, dx, _, _ = run_train(inp, config_fwd=cf, config_bwd=cb)
+        assert torch.equal(bits(y), bits(base[0])) and torch.equal(bits(dx), bits(base[1])), f"options {h}"
