@@ -54,21 +54,23 @@ BF16, F32 = 0, 1
 
 
 class Config(ctypes.Structure):
-    """cconv_config_t: vec, rows_per_group, waves_per_block, options, seg_rows."""
+    """cconv_config_t: vec, rows_per_group, waves_per_block, strips_per_block, options, seg_rows."""
 
     _fields_ = [
         ("vec", ctypes.c_int),
         ("rows_per_group", ctypes.c_int),
         ("waves_per_block", ctypes.c_int),
+        ("strips_per_block", ctypes.c_int),
         ("options", ctypes.c_int),
         ("seg_rows", ctypes.c_int64),
     ]
 
+    def __init__(self, *args, **kw):
+        kw.setdefault("strips_per_block", 1)
+        super().__init__(*args, **kw)
+
     def __repr__(self):
-        return (
-            f"Config(vec={self.vec}, rows_per_group={self.rows_per_group}, "
-            f"waves_per_block={self.waves_per_block}, options={self.options}, seg_rows={self.seg_rows})"
-        )
+        return "Config(" + ", ".join(f"{k}={v}" for k, v in self.as_dict().items()) + ")"
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -16,10 +16,10 @@ namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 40;        // any one size or stride
 constexpr int64_t kMaxDecodeRows = int64_t(1) << 24;  // N
+constexpr int64_t kMaxChannels = int64_t(1) << 30;    // D: lane channel offsets are 32-bit
 constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices (LDS bit set)
-constexpr int64_t kFwdWaves = 1024;     // forward grid: one wave per SIMD (256 CUs x 4)
-constexpr int64_t kBwdWaves = 2048;     // backward grid: two waves per SIMD
-constexpr int kNtLoadStore = 3;         // non-temporal loads and stores (streamed once)
+constexpr int64_t kTargetWaves = 1024;  // one wave per SIMD (256 CUs x 4 SIMDs)
+constexpr int kNtLoadStorePrefetch = 7;  // non-temporal loads and stores, software prefetch
 constexpr int64_t kMinSeg = 64;         // shorter segments re-read too large a share of rows
 constexpr int64_t kUpdateTargetBlocks = 1024;
 
@@ -53,26 +53,30 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
         return false;
     if (c.waves_per_block != 1 && c.waves_per_block != 2 && c.waves_per_block != 4 && c.waves_per_block != 8)
         return false;
+    if (c.strips_per_block < 1 || c.waves_per_block % c.strips_per_block != 0) return false;
     if (c.seg_rows < 8 || c.seg_rows > kMaxDim || c.seg_rows % c.rows_per_group != 0) return false;
     if (c.options < 0 || c.options > 7) return false;
     return true;
 }
 
-// The static launch table. One wave per (channel strip, time segment, batch row); segments
-// are sized so the grid holds about kFwdWaves / kBwdWaves waves, i.e. one (forward) or two
-// (backward, register-limited to two waves per SIMD) waves per SIMD of the 256 CUs, each
-// streaming a long run of rows; never below kMinSeg rows (the re-read W-1 rows per segment
-// stay under 5%). The backward packs 8 waves (8 consecutive segments) per block so their dw
-// partials are summed in LDS before one partial per block is written.
+// The static launch table (from sweeps on MI355X at 8x8192x4096, W=4). Each wave owns one
+// (channel strip, time segment, batch row) and streams its rows with the next row group's
+// loads in flight while the current group is computed, non-temporal loads and stores. The
+// segment length is chosen so the grid holds about kTargetWaves waves, one per SIMD of the
+// 256 CUs: fewer, longer-running waves beat more, shorter ones for both kernels. Segments
+// never drop below kMinSeg rows (the W-1 rows each segment re-reads stay a small share).
+// The forward loads 8 rows per group; the backward 4 (x and dy: 8 loads per group, and its
+// larger per-lane state leaves fewer registers for rows in flight).
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) {
     (void)W;
     cconv_config_t c;
     c.vec = 8;
     c.rows_per_group = bwd ? 4 : 8;
-    c.waves_per_block = bwd ? 8 : 1;
-    c.options = kNtLoadStore;
+    c.waves_per_block = 1;
+    c.strips_per_block = 1;
+    c.options = kNtLoadStorePrefetch;
     const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
-    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / (bwd ? kBwdWaves : kFwdWaves);
+    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / kTargetWaves;
     ts = std::max(kMinSeg, ts - ts % 8);
     const int64_t tcap = ((std::max<int64_t>(T, 1) + 7) / 8) * 8;
     c.seg_rows = std::min(ts, std::max<int64_t>(8, tcap));
@@ -83,12 +87,15 @@ bool make_plan(const cconv_config_t& c, int64_t B, int64_t T, int64_t D, Plan* p
     p->vec = c.vec;
     p->group = c.rows_per_group;
     p->waves = c.waves_per_block;
+    p->ws = c.strips_per_block;
     p->seg_rows = c.seg_rows;
     p->options = c.options;
     p->strips = (D + 64 * c.vec - 1) / (64 * c.vec);
+    p->strip_groups = (p->strips + p->ws - 1) / p->ws;
     p->segs = (T + c.seg_rows - 1) / c.seg_rows;
-    p->seg_groups = (p->segs + c.waves_per_block - 1) / c.waves_per_block;
-    const __int128 blocks = static_cast<__int128>(p->strips) * p->seg_groups * B;
+    const int64_t wt = c.waves_per_block / c.strips_per_block;
+    p->seg_groups = (p->segs + wt - 1) / wt;
+    const __int128 blocks = static_cast<__int128>(p->strip_groups) * p->seg_groups * B;
     if (blocks > INT32_MAX) return false;
     p->blocks = static_cast<int64_t>(blocks);
     p->partials = B * p->seg_groups;
@@ -101,7 +108,7 @@ cconv_status_t check_train_common(const void* w, cconv_dtype_t w_dtype, const fl
                                   int64_t T, int64_t D, int W) {
     if (B < 0 || T < 0 || D < 0 || B > kMaxDim || T > kMaxDim || D > kMaxDim) return CCONV_ERR_BAD_SHAPE;
     if (W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
-    if (D % 8 != 0) return CCONV_ERR_BAD_SHAPE;
+    if (D % 8 != 0 || D > kMaxChannels) return CCONV_ERR_BAD_SHAPE;
     if (!dtype_ok(w_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
     if (!aligned(w, 16) || (bias && !aligned(bias, 16))) return CCONV_ERR_MISALIGNED;
     return CCONV_OK;
@@ -150,8 +157,9 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     a.T = T;
     a.D = D;
     a.seg_rows = p.seg_rows;
-    a.strips = p.strips;
+    a.strip_groups = p.strip_groups;
     a.seg_groups = p.seg_groups;
+    a.ws = p.ws;
     return cconv::launch_fwd(p, W, a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? CCONV_OK
                                                                                            : CCONV_ERR_LAUNCH;
 }
@@ -232,8 +240,9 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
         a.T = T;
         a.D = D;
         a.seg_rows = p.seg_rows;
-        a.strips = p.strips;
+        a.strip_groups = p.strip_groups;
         a.seg_groups = p.seg_groups;
+        a.ws = p.ws;
         if (cconv::launch_bwd(p, W, a, s) != hipSuccess) return CCONV_ERR_LAUNCH;
     }
     if (!finish) return CCONV_OK;

@@ -28,7 +28,7 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
                                         float (&xr)[W > 1 ? W - 1 : 1][VEC],
                                         float (&gr)[W > 1 ? W - 1 : 1][VEC], float (&acc)[W][VEC],
                                         float (&db)[VEC], bool acc_on, bool emit,
-                                        uint16_t* __restrict__ dxp) {
+                                        uint16_t* __restrict__ dxrow, uint32_t lo) {
     float xt[VEC], dyt[VEC], g[VEC];
     widen(rx, xt);
     widen(rdy, dyt);
@@ -59,7 +59,7 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
             for (int k = 1; k < W; ++k) s = __builtin_fmaf(tap[k][v], k == W - 1 ? g[v] : gr[W - 2 - k][v], s);
             dx[v] = s;
         }
-        store_row<VEC, NTS>(dxp, narrow<VEC>(dx));
+        store_row<VEC, NTS>(at(dxrow, lo), narrow<VEC>(dx));
     }
 #pragma unroll
     for (int k = W - 2; k > 0; --k)
@@ -82,18 +82,12 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
     constexpr int R = W > 1 ? W - 1 : 1;
     constexpr bool NTL = (F & kNtLoad) != 0, NTS = (F & kNtStore) != 0, PF = (F & kPrefetch) != 0;
     extern __shared__ float red[];  // [waves][VEC][64], one column at a time
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t strip = tile % a.strips;
-    const int64_t rest = tile / a.strips;
-    const int64_t sg = rest % a.seg_groups;
-    const int64_t b = rest / a.seg_groups;
-    const int waves = blockDim.x / kWave;
+    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T);
+    const int64_t t0 = wt.t0, t1 = wt.t1;
     const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
-    const int64_t t0 = (sg * waves + wave) * a.seg_rows;
-    const int64_t t1 = min(t0 + a.seg_rows, a.T);
-    const int64_t d = (strip * kWave + lane) * VEC;
-    const bool active = d < a.D;
+    const bool active = wt.d < a.D;
+    const uint32_t lo = static_cast<uint32_t>(wt.d) * 2u;  // byte offset of the lane's channels
 
     float acc[W][VEC], db[VEC];
 #pragma unroll
@@ -104,22 +98,23 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
     }
 
     if (active && t0 < a.T) {
-        const uint16_t* __restrict__ xp = a.x + b * a.x_sb + d;
-        const uint16_t* __restrict__ dyp = a.dy + b * a.dy_sb + d;
-        uint16_t* __restrict__ dxp = a.dx + b * a.T * a.D + d;
+        // wave-uniform row bases plus the lane's 32-bit channel offset
+        const uint16_t* __restrict__ xb = a.x + wt.b * a.x_sb;
+        const uint16_t* __restrict__ dyb = a.dy + wt.b * a.dy_sb;
+        uint16_t* __restrict__ dxb = a.dx + wt.b * a.T * a.D;
         const int64_t xs = a.x_st, dys = a.dy_st, dxs = a.D;
 
         float tap[W][VEC];
-        load_taps<VEC, W>(a.w, a.w_f32, d, tap);
+        load_taps<VEC, W>(a.w, a.w_f32, wt.d, tap);
         float bs[VEC];
-        load_bias<VEC>(a.bias, d, bs);
+        load_bias<VEC>(a.bias, wt.d, bs);
 
         float xr[R][VEC], gr[R][VEC];
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             const int64_t t = t0 - 1 - k;
             if (W > 1 && t >= 0) {
-                widen(load_row<VEC>(xp + t * xs), xr[k]);
+                widen(load_row<VEC>(at(xb + t * xs, lo)), xr[k]);
             } else {
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) xr[k][v] = 0.0f;
@@ -135,19 +130,20 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
             if (t + G <= t1) {
                 Row<VEC> cx[G], cdy[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) cx[g] = load_row<VEC, NTL>(xp + (t + g) * xs);
+                for (int g = 0; g < G; ++g) cx[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
 #pragma unroll
-                for (int g = 0; g < G; ++g) cdy[g] = load_row<VEC, NTL>(dyp + (t + g) * dys);
+                for (int g = 0; g < G; ++g) cdy[g] = load_row<VEC, NTL>(at(dyb + (t + g) * dys, lo));
                 for (; t + G <= t1; t += G) {
                     Row<VEC> nx[G], ndy[G];
 #pragma unroll
-                    for (int g = 0; g < G; ++g) nx[g] = load_row<VEC, NTL>(xp + min(t + G + g, t1 - 1) * xs);
+                    for (int g = 0; g < G; ++g) nx[g] = load_row<VEC, NTL>(at(xb + min(t + G + g, t1 - 1) * xs, lo));
 #pragma unroll
-                    for (int g = 0; g < G; ++g) ndy[g] = load_row<VEC, NTL>(dyp + min(t + G + g, t1 - 1) * dys);
+                    for (int g = 0; g < G; ++g)
+                        ndy[g] = load_row<VEC, NTL>(at(dyb + min(t + G + g, t1 - 1) * dys, lo));
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
                         const int64_t u = t + g - (W - 1);
-                        bwd_row<VEC, W, NTS>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, true, u >= t0, dxp + u * dxs);
+                        bwd_row<VEC, W, NTS>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, true, u >= t0, dxb + u * dxs, lo);
                     }
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
@@ -160,20 +156,20 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
             for (; t + G <= t1; t += G) {
                 Row<VEC> rx[G], rdy[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NTL>(xp + (t + g) * xs);
+                for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
 #pragma unroll
-                for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC, NTL>(dyp + (t + g) * dys);
+                for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC, NTL>(at(dyb + (t + g) * dys, lo));
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const int64_t u = t + g - (W - 1);
-                    bwd_row<VEC, W, NTS>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, true, u >= t0, dxp + u * dxs);
+                    bwd_row<VEC, W, NTS>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, true, u >= t0, dxb + u * dxs, lo);
                 }
             }
         }
         for (; t < t1; ++t) {
             const int64_t u = t - (W - 1);
-            bwd_row<VEC, W, NTS>(tap, bs, load_row<VEC, NTL>(xp + t * xs), load_row<VEC, NTL>(dyp + t * dys), xr,
-                                 gr, acc, db, true, u >= t0, dxp + u * dxs);
+            bwd_row<VEC, W, NTS>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)), load_row<VEC, NTL>(at(dyb + t * dys, lo)),
+                                 xr, gr, acc, db, true, u >= t0, dxb + u * dxs, lo);
         }
         // right halo: rows t1 .. t1+W-2 finish dx of this segment's last W-1 rows; rows at or
         // past T have g = 0 (their x and dy read as zero).
@@ -181,19 +177,19 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
         for (int h = 0; h < W - 1; ++h) {
             const int64_t th = t1 + h;
             const int64_t u = th - (W - 1);
-            const bool in = th < a.T;
             Row<VEC> hx = zero_row<VEC>(), hdy = zero_row<VEC>();
-            if (in) {
-                hx = load_row<VEC>(xp + th * xs);
-                hdy = load_row<VEC>(dyp + th * dys);
+            if (th < a.T) {
+                hx = load_row<VEC>(at(xb + th * xs, lo));
+                hdy = load_row<VEC>(at(dyb + th * dys, lo));
             }
-            bwd_row<VEC, W, NTS>(tap, bs, hx, hdy, xr, gr, acc, db, false, u >= t0, dxp + u * dxs);
+            bwd_row<VEC, W, NTS>(tap, bs, hx, hdy, xr, gr, acc, db, false, u >= t0, dxb + u * dxs, lo);
         }
     }
 
-    // Sum the block's waves in wave order, one column at a time; wave 0 stores the partial.
-    const int64_t p = b * a.seg_groups + sg;
-    float* __restrict__ out = a.partial + p * (W + 1) * a.D + d;
+    // The waves that share a strip (same ws_i, consecutive segments) are summed through LDS in
+    // segment order, one column at a time; the first of them stores the block's partial.
+    const int64_t p = wt.b * a.seg_groups + wt.sg;
+    float* __restrict__ out = a.partial + p * (W + 1) * a.D;
 #pragma unroll
     for (int j = 0; j <= W; ++j) {
         // column j < W is dw[:, j], the gradient of tap k = W-1-j; column W is dbias
@@ -201,14 +197,14 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
         for (int v = 0; v < VEC; ++v)
             red[(wave * VEC + v) * kWave + lane] = (j < W) ? acc[W - 1 - j][v] : db[v];
         __syncthreads();
-        if (wave == 0 && active) {
+        if (wt.wt_i == 0 && active) {
             float s[VEC];
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
-                s[v] = red[v * kWave + lane];
-                for (int w2 = 1; w2 < waves; ++w2) s[v] += red[(w2 * VEC + v) * kWave + lane];
+                s[v] = red[(wt.ws_i * VEC + v) * kWave + lane];
+                for (int i = 1; i < wt.wt; ++i) s[v] += red[((i * a.ws + wt.ws_i) * VEC + v) * kWave + lane];
             }
-            float* o = out + j * a.D;
+            float* o = at(out + j * a.D, lo * 2u);  // fp32 partials: twice the bf16 byte offset
             if constexpr (VEC == 8) {
                 reinterpret_cast<float4*>(o)[0] = make_float4(s[0], s[1], s[2], s[3]);
                 reinterpret_cast<float4*>(o)[1] = make_float4(s[4], s[5], s[6], s[7]);

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace cconv {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -89,6 +91,15 @@ constexpr int kPrefetch = 4;  // next group's loads issued before the current gr
 
 // The wave's index in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
+// A row element at a wave-uniform base plus a lane's byte offset. Keeping the offset a 32-bit
+// byte count lets the compiler use the scalar-base addressing form (global_load v, v_off,
+// s[base]), so a new row costs scalar arithmetic only.
+template <typename P>
+__device__ __forceinline__ P* at(P* base, uint32_t off_bytes) {
+    using C = typename std::conditional<std::is_const<P>::value, const char, char>::type;
+    return reinterpret_cast<P*>(reinterpret_cast<C*>(base) + off_bytes);
+}
 
 // bf16 -> fp32 is exact: the bf16 pattern is the high half of the fp32 pattern.
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -180,6 +191,33 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t pid, int64_t n) {
     const int64_t xcd = pid % kXcd, k = pid / kXcd;
     const int64_t q = n / kXcd, r = n % kXcd;
     return xcd * q + (xcd < r ? xcd : r) + k;
+}
+
+// Where a wave works. The block id (XCD-remapped) selects a (strip group, segment group,
+// batch row); the wave's index selects its strip within the group (ws_i) and its segment
+// within the group (wt_i). All fields are wave-uniform except `d`, the lane's first channel.
+struct WaveTile {
+    int64_t b, sg, t0, t1, d;
+    int ws_i, wt_i, wt;
+};
+
+template <int VEC>
+__device__ __forceinline__ WaveTile wave_tile(int64_t strip_groups, int64_t seg_groups, int ws, int64_t seg_rows,
+                                              int64_t T) {
+    WaveTile w;
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t sgrp = tile % strip_groups;
+    const int64_t rest = tile / strip_groups;
+    w.sg = rest % seg_groups;
+    w.b = rest / seg_groups;
+    const int wave = wave_id();
+    w.wt = (blockDim.x / kWave) / ws;
+    w.ws_i = wave % ws;
+    w.wt_i = wave / ws;
+    w.t0 = (w.sg * w.wt + w.wt_i) * seg_rows;
+    w.t1 = min(w.t0 + seg_rows, T);
+    w.d = ((sgrp * ws + w.ws_i) * kWave + static_cast<int64_t>(threadIdx.x % kWave)) * VEC;
+    return w;
 }
 
 }  // namespace cconv

@@ -42,27 +42,22 @@ template <int VEC, int G, int W, int F>
 __global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
     constexpr int R = W > 1 ? W - 1 : 1;
     constexpr bool NTL = (F & kNtLoad) != 0, NTS = (F & kNtStore) != 0, PF = (F & kPrefetch) != 0;
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t strip = tile % a.strips;
-    const int64_t rest = tile / a.strips;
-    const int64_t sg = rest % a.seg_groups;
-    const int64_t b = rest / a.seg_groups;
-    const int wave = wave_id();
-    const int lane = threadIdx.x % kWave;
-    const int64_t t0 = (sg * (blockDim.x / kWave) + wave) * a.seg_rows;
-    if (t0 >= a.T) return;  // a trailing wave of the last segment group
-    const int64_t t1 = min(t0 + a.seg_rows, a.T);
-    const int64_t d = (strip * kWave + lane) * VEC;
-    if (d >= a.D) return;  // lanes past the last channel (D is a multiple of VEC)
+    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T);
+    const int64_t t0 = wt.t0, t1 = wt.t1;
+    if (t0 >= a.T) return;    // a trailing wave of the last segment group
+    if (wt.d >= a.D) return;  // lanes past the last channel (D is a multiple of VEC)
 
-    const uint16_t* __restrict__ xp = a.x + b * a.x_sb + d;
-    uint16_t* __restrict__ yp = a.y + b * a.T * a.D + d;
+    // Row bases are wave-uniform (scalar registers); a lane adds its 32-bit channel offset,
+    // so a row load is one global_load with a scalar base and no per-row VALU address math.
+    const uint32_t lo = static_cast<uint32_t>(wt.d) * 2u;  // byte offset of the lane's channels
+    const uint16_t* __restrict__ xb = a.x + wt.b * a.x_sb;
+    uint16_t* __restrict__ yb = a.y + wt.b * a.T * a.D;
     const int64_t xs = a.x_st, ys = a.D;
 
     float tap[W][VEC];
-    load_taps<VEC, W>(a.w, a.w_f32, d, tap);
+    load_taps<VEC, W>(a.w, a.w_f32, wt.d, tap);
     float bs[VEC];
-    load_bias<VEC>(a.bias, d, bs);
+    load_bias<VEC>(a.bias, wt.d, bs);
 
     // ring prologue: x[t0-1-k], zero before the sequence start
     float ring[R][VEC];
@@ -70,7 +65,7 @@ __global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
     for (int k = 0; k < R; ++k) {
         const int64_t t = t0 - 1 - k;
         if (W > 1 && t >= 0) {
-            widen(load_row<VEC>(xp + t * xs), ring[k]);
+            widen(load_row<VEC>(at(xb + t * xs, lo)), ring[k]);
         } else {
 #pragma unroll
             for (int v = 0; v < VEC; ++v) ring[k][v] = 0.0f;
@@ -85,14 +80,14 @@ __global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
         if (t + G <= t1) {
             Row<VEC> cur[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) cur[g] = load_row<VEC, NTL>(xp + (t + g) * xs);
+            for (int g = 0; g < G; ++g) cur[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
             for (; t + G <= t1; t += G) {
                 Row<VEC> nxt[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) nxt[g] = load_row<VEC, NTL>(xp + min(t + G + g, t1 - 1) * xs);
+                for (int g = 0; g < G; ++g) nxt[g] = load_row<VEC, NTL>(at(xb + min(t + G + g, t1 - 1) * xs, lo));
 #pragma unroll
                 for (int g = 0; g < G; ++g)
-                    store_row<VEC, NTS>(yp + (t + g) * ys, fwd_row<VEC, W>(tap, bs, cur[g], ring));
+                    store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), fwd_row<VEC, W>(tap, bs, cur[g], ring));
 #pragma unroll
                 for (int g = 0; g < G; ++g) cur[g] = nxt[g];
             }
@@ -101,14 +96,14 @@ __global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
         for (; t + G <= t1; t += G) {
             Row<VEC> raw[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) raw[g] = load_row<VEC, NTL>(xp + (t + g) * xs);
+            for (int g = 0; g < G; ++g) raw[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
 #pragma unroll
             for (int g = 0; g < G; ++g)
-                store_row<VEC, NTS>(yp + (t + g) * ys, fwd_row<VEC, W>(tap, bs, raw[g], ring));
+                store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), fwd_row<VEC, W>(tap, bs, raw[g], ring));
         }
     }
     for (; t < t1; ++t)
-        store_row<VEC, NTS>(yp + t * ys, fwd_row<VEC, W>(tap, bs, load_row<VEC, NTL>(xp + t * xs), ring));
+        store_row<VEC, NTS>(at(yb + t * ys, lo), fwd_row<VEC, W>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)), ring));
 }
 
 namespace {

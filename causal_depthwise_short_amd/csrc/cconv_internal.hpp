@@ -9,20 +9,23 @@ namespace cconv {
 
 // How a forward or backward call is cut into work.
 //   A lane owns `vec` consecutive channels; a wave owns a strip of 64*vec channels and one
-//   time segment of `seg_rows` rows of one batch row; a block holds `waves` waves that take
-//   consecutive segments of the same strip and batch row. `group` rows are loaded together.
+//   time segment of `seg_rows` rows of one batch row. A block holds `waves` waves arranged as
+//   `ws` adjacent strips x `waves/ws` consecutive segments of one batch row. `group` rows are
+//   loaded together.
 struct Plan {
     int vec;
     int group;
     int waves;
+    int ws;  // strips per block
     int64_t seg_rows;
     int options;  // kNtLoad | kNtStore | kPrefetch
     // derived
-    int64_t strips;      // ceil(D / (64*vec))
-    int64_t segs;        // ceil(T / seg_rows)
-    int64_t seg_groups;  // ceil(segs / waves)
-    int64_t blocks;      // strips * seg_groups * B
-    int64_t partials;    // backward: B * seg_groups fp32 partial rows of [W+1, D]
+    int64_t strips;        // ceil(D / (64*vec))
+    int64_t strip_groups;  // ceil(strips / ws)
+    int64_t segs;          // ceil(T / seg_rows)
+    int64_t seg_groups;    // ceil(segs / (waves/ws))
+    int64_t blocks;        // strip_groups * seg_groups * B
+    int64_t partials;      // backward: B * seg_groups fp32 partial rows of [W+1, D]
 };
 
 struct FwdArgs {
@@ -33,7 +36,8 @@ struct FwdArgs {
     const float* bias;
     uint16_t* y;
     int64_t B, T, D;
-    int64_t seg_rows, strips, seg_groups;
+    int64_t seg_rows, strip_groups, seg_groups;
+    int ws;
 };
 
 struct BwdArgs {
@@ -47,7 +51,8 @@ struct BwdArgs {
     uint16_t* dx;
     float* partial;  // [partials, W+1, D]
     int64_t B, T, D;
-    int64_t seg_rows, strips, seg_groups;
+    int64_t seg_rows, strip_groups, seg_groups;
+    int ws;
 };
 
 struct ReduceArgs {

@@ -75,7 +75,7 @@ typedef enum {
  *   w     [D, W] contiguous, dtype w_dtype (CCONV_BF16 or CCONV_F32).
  *   bias  fp32 [D], or NULL for none.
  *   y     bf16 [B, T, D] contiguous (written; must not overlap x, w or bias).
- *   B, T, D >= 0; 1 <= W <= 4.
+ *   B, T >= 0; 0 <= D <= 2^30; 1 <= W <= 4.
  */
 cconv_status_t cconv_fwd(const void* x, int64_t x_sb, int64_t x_st, const void* w,
                          cconv_dtype_t w_dtype, const float* bias, void* y, int64_t B,
@@ -157,8 +157,11 @@ const char* cconv_version(void);
  * order of their fixed-order sum.
  *   vec              channels per lane: 4 or 8 (8 or 16 bytes per row per lane)
  *   rows_per_group   rows whose loads are issued together: 4 or 8
- *   waves_per_block  1, 2, 4 or 8 waves; the waves of a block take consecutive time
- *                    segments of the same channel strip and batch row
+ *   waves_per_block  1, 2, 4 or 8 waves per block
+ *   strips_per_block a divisor of waves_per_block: the block's waves cover this many
+ *                    adjacent channel strips (64*vec channels each) times
+ *                    waves_per_block/strips_per_block consecutive time segments of one batch
+ *                    row; the backward sums the dw partials of a strip's segments in LDS
  *   seg_rows         rows per wave segment: a multiple of rows_per_group, >= 8
  *   options          bit 0: non-temporal loads of x (and dy); bit 1: non-temporal stores of
  *                    y (dx); bit 2: issue the next row group's loads before the current
@@ -168,6 +171,7 @@ typedef struct {
     int vec;
     int rows_per_group;
     int waves_per_block;
+    int strips_per_block;
     int options;
     int64_t seg_rows;
 } cconv_config_t;

@@ -171,6 +171,8 @@ CONFIGS_FWD = [
     dict(vec=8, rows_per_group=8, waves_per_block=8, options=4, seg_rows=96),
     dict(vec=4, rows_per_group=8, waves_per_block=2, seg_rows=40),
     dict(vec=4, rows_per_group=4, waves_per_block=4, seg_rows=1000),
+    dict(vec=8, rows_per_group=8, waves_per_block=8, strips_per_block=8, options=7, seg_rows=128),
+    dict(vec=4, rows_per_group=4, waves_per_block=4, strips_per_block=2, options=3, seg_rows=200),
 ]
 CONFIGS_BWD = [
     dict(vec=8, rows_per_group=4, waves_per_block=4, seg_rows=64),
@@ -178,6 +180,8 @@ CONFIGS_BWD = [
     dict(vec=8, rows_per_group=8, waves_per_block=8, seg_rows=96),
     dict(vec=4, rows_per_group=4, waves_per_block=2, seg_rows=40),
     dict(vec=4, rows_per_group=8, waves_per_block=4, seg_rows=1000),
+    dict(vec=8, rows_per_group=4, waves_per_block=8, strips_per_block=2, options=7, seg_rows=64),
+    dict(vec=4, rows_per_group=8, waves_per_block=8, strips_per_block=8, options=3, seg_rows=128),
 ]
 
 
