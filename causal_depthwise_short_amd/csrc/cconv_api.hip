@@ -19,7 +19,8 @@ constexpr int64_t kMaxDecodeRows = int64_t(1) << 24;  // N
 constexpr int64_t kMaxChannels = int64_t(1) << 30;    // D: lane channel offsets are 32-bit
 constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices (LDS bit set)
 constexpr int64_t kTargetWaves = 1024;  // one wave per SIMD (256 CUs x 4 SIMDs)
-constexpr int kNtLoadStorePrefetch = 7;  // non-temporal loads and stores, software prefetch
+constexpr int kNtLoadStore = 3;          // non-temporal loads and stores
+constexpr int kNtLoadStorePrefetch = 7;  // ... and software prefetch of the next row group
 constexpr int64_t kMinSeg = 64;         // shorter segments re-read too large a share of rows
 constexpr int64_t kUpdateTargetBlocks = 1024;
 
@@ -65,21 +66,25 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 // segment length is chosen so the grid holds about kTargetWaves waves, one per SIMD of the
 // 256 CUs: fewer, longer-running waves beat more, shorter ones for both kernels. Segments
 // never drop below kMinSeg rows (the W-1 rows each segment re-reads stay a small share).
-// The forward loads 8 rows per group; the backward 4 (x and dy: 8 loads per group, and its
-// larger per-lane state leaves fewer registers for rows in flight).
+// The forward runs 4 channels per lane and loads 16 rows per group (no prefetch needed at that
+// depth); the backward runs 8 channels per lane, 4 rows per group (x and dy: 8 loads) with the
+// next group prefetched — its larger per-lane state leaves fewer registers for rows in flight.
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) {
     (void)W;
     cconv_config_t c;
-    c.vec = 8;
-    c.rows_per_group = bwd ? 4 : 8;
+    c.vec = bwd ? 8 : 4;
+    c.rows_per_group = bwd ? 4 : 16;
     c.waves_per_block = 1;
     c.strips_per_block = 1;
-    c.options = kNtLoadStorePrefetch;
+    c.options = bwd ? kNtLoadStorePrefetch : kNtLoadStore;
+    // segment length: a multiple of the row group (and of 8), at least kMinSeg rows, at most
+    // T rounded up
+    const int64_t align = std::max<int64_t>(8, c.rows_per_group);
     const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
     int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / kTargetWaves;
-    ts = std::max(kMinSeg, ts - ts % 8);
-    const int64_t tcap = ((std::max<int64_t>(T, 1) + 7) / 8) * 8;
-    c.seg_rows = std::min(ts, std::max<int64_t>(8, tcap));
+    ts = std::max(kMinSeg, ts - ts % align);
+    const int64_t tcap = ((std::max<int64_t>(T, 1) + align - 1) / align) * align;
+    c.seg_rows = std::min(ts, tcap);
     return c;
 }
 

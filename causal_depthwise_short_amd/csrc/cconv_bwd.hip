@@ -34,10 +34,11 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
     widen(rdy, dyt);
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
+        // g = dy * s * (1 + z(1-s)) as a + a*m with a = dy*s and m = z - z*s: three VALU ops
         const float z = conv_z<VEC, W>(tap, b, xt, xr, v);
         const float s = sigmoid(z);
-        const float q = __builtin_fmaf(z, 1.0f - s, 1.0f);
-        g[v] = (dyt[v] * s) * q;
+        const float a = dyt[v] * s;
+        g[v] = __builtin_fmaf(a, __builtin_fmaf(-z, s, z), a);
     }
     if (acc_on) {
 #pragma unroll
@@ -292,7 +293,9 @@ hipError_t launch_bwd_w(int W, int F, dim3 grid, dim3 block, size_t lds, const B
 
 }  // namespace
 
-bool bwd_variant_exists(int vec, int group) { return (vec == 4 || vec == 8) && (group == 4 || group == 8); }
+bool bwd_variant_exists(int vec, int group) {
+    return (vec == 8 && (group == 4 || group == 8)) || (vec == 4 && (group == 4 || group == 8 || group == 16));
+}
 
 hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
@@ -304,6 +307,7 @@ hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t s) {
     } else if (p.vec == 4) {
         if (p.group == 4) return launch_bwd_w<4, 4>(W, F, grid, block, lds, a, s);
         if (p.group == 8) return launch_bwd_w<4, 8>(W, F, grid, block, lds, a, s);
+        if (p.group == 16) return launch_bwd_w<4, 16>(W, F, grid, block, lds, a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -140,7 +140,9 @@ hipError_t launch_fwd_w(int W, int F, dim3 grid, dim3 block, const FwdArgs& a, h
 
 }  // namespace
 
-bool fwd_variant_exists(int vec, int group) { return (vec == 4 || vec == 8) && (group == 4 || group == 8); }
+bool fwd_variant_exists(int vec, int group) {
+    return (vec == 8 && (group == 4 || group == 8)) || (vec == 4 && (group == 4 || group == 8 || group == 16));
+}
 
 hipError_t launch_fwd(const Plan& p, int W, const FwdArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
@@ -151,6 +153,7 @@ hipError_t launch_fwd(const Plan& p, int W, const FwdArgs& a, hipStream_t s) {
     } else if (p.vec == 4) {
         if (p.group == 4) return launch_fwd_w<4, 4>(W, F, grid, block, a, s);
         if (p.group == 8) return launch_fwd_w<4, 8>(W, F, grid, block, a, s);
+        if (p.group == 16) return launch_fwd_w<4, 16>(W, F, grid, block, a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -156,7 +156,7 @@ const char* cconv_version(void);
  * not depend on the configuration (bitwise); dw and dbias depend on it only through the
  * order of their fixed-order sum.
  *   vec              channels per lane: 4 or 8 (8 or 16 bytes per row per lane)
- *   rows_per_group   rows whose loads are issued together: 4 or 8
+ *   rows_per_group   rows whose loads are issued together: 4 or 8 (and 16 with vec 4)
  *   waves_per_block  1, 2, 4 or 8 waves per block
  *   strips_per_block a divisor of waves_per_block: the block's waves cover this many
  *                    adjacent channel strips (64*vec channels each) times

@@ -200,3 +200,21 @@ def test_bwd_stages_host_errors():
     assert main(dx=X) == ALIAS and main(ws=DY) == ALIAS and main(ws_bytes=8) == WS
     assert fin(dw=None) == NULLP and fin(ws=None) == NULLP and fin(dw_dt=5) == DTYPE
     assert fin(dw=WSP) == ALIAS and fin(db=DW) == ALIAS and fin(ws_bytes=8) == WS and fin(db=DB + 4) == MISAL
+
+
+@pytest.mark.parametrize("which", ["fwd", "bwd"])
+def test_default_configs_are_valid(which):
+    """Every default plan over a grid of shapes is one the library accepts."""
+    for B in (1, 3, 8):
+        for T in (1, 2, 7, 8, 15, 16, 17, 100, 1000, 8192, 100003):
+            for D in (8, 520, 4096):
+                for W in (1, 4):
+                    c = cc.cconv_default_config(which, B, T, D, W)
+                    assert c.seg_rows % c.rows_per_group == 0 and c.seg_rows >= 8, (which, B, T, D, W, c)
+                    assert c.waves_per_block % c.strips_per_block == 0
+                    assert cc.cconv_bwd_workspace_bytes(B, T, D, W, c if which == "bwd" else None) > 0
+                    if which == "fwd":
+                        # y aliases x on purpose: the aliasing check comes after the config check,
+                        # so ALIAS (not BAD_CONFIG) means the plan was accepted, with nothing launched
+                        st = cc.lib().cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, B, T, D, W, ctypes.byref(c), None)
+                        assert st == ALIAS, (B, T, D, W, c, st)
