@@ -8,6 +8,7 @@
 #include <cstdint>
 
 #include "../../include/cconv.h"
+#include "cconv_device.hpp"
 #include "cconv_internal.hpp"
 
 using cconv::Plan;
@@ -19,8 +20,9 @@ constexpr int64_t kMaxDecodeRows = int64_t(1) << 24;  // N
 constexpr int64_t kMaxChannels = int64_t(1) << 30;    // D: lane channel offsets are 32-bit
 constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices (LDS bit set)
 constexpr int64_t kTargetWaves = 1024;  // one wave per SIMD (256 CUs x 4 SIMDs)
-constexpr int kNtLoadStore = 3;          // non-temporal loads and stores
-constexpr int kNtLoadStorePrefetch = 7;  // ... and software prefetch of the next row group
+// forward: non-temporal loads and stores, solo kernel; backward: the same plus prefetch
+constexpr int kFwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
+constexpr int kBwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kPrefetch | cconv::kSolo;
 constexpr int64_t kMinSeg = 64;         // shorter segments re-read too large a share of rows
 constexpr int64_t kUpdateTargetBlocks = 1024;
 
@@ -56,27 +58,27 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
         return false;
     if (c.strips_per_block < 1 || c.waves_per_block % c.strips_per_block != 0) return false;
     if (c.seg_rows < 8 || c.seg_rows > kMaxDim || c.seg_rows % c.rows_per_group != 0) return false;
-    if (c.options < 0 || c.options > 7) return false;
+    if (c.options < 0 || c.options > 15) return false;
+    if ((c.options & cconv::kSolo) && c.waves_per_block != 1) return false;  // solo kernels run one-wave blocks
     return true;
 }
 
 // The static launch table (from sweeps on MI355X at 8x8192x4096, W=4). Each wave owns one
-// (channel strip, time segment, batch row) and streams its rows with the next row group's
-// loads in flight while the current group is computed, non-temporal loads and stores. The
-// segment length is chosen so the grid holds about kTargetWaves waves, one per SIMD of the
-// 256 CUs: fewer, longer-running waves beat more, shorter ones for both kernels. Segments
-// never drop below kMinSeg rows (the W-1 rows each segment re-reads stay a small share).
-// The forward runs 4 channels per lane and loads 16 rows per group (no prefetch needed at that
-// depth); the backward runs 8 channels per lane, 4 rows per group (x and dy: 8 loads) with the
-// next group prefetched — its larger per-lane state leaves fewer registers for rows in flight.
+// (channel strip, time segment, batch row) and streams its rows; segments are sized so the
+// grid holds about kTargetWaves waves, one per SIMD of the 256 CUs: fewer, longer-running
+// waves beat more, shorter ones for both kernels, and a wave alone on its SIMD may use the
+// whole register file (the "solo" kernels), which is what lets deep row groups stay in flight
+// without scratch spills. Segments never drop below kMinSeg rows (the W-1 rows each segment
+// re-reads stay a small share). Forward: 4 channels per lane, 16-row groups. Backward: 8
+// channels per lane, 8-row groups of x and dy with the next group prefetched.
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) {
     (void)W;
     cconv_config_t c;
     c.vec = bwd ? 8 : 4;
-    c.rows_per_group = bwd ? 4 : 16;
+    c.rows_per_group = bwd ? 8 : 16;
     c.waves_per_block = 1;
     c.strips_per_block = 1;
-    c.options = bwd ? kNtLoadStorePrefetch : kNtLoadStore;
+    c.options = bwd ? kBwdOptions : kFwdOptions;
     // segment length: a multiple of the row group (and of 8), at least kMinSeg rows, at most
     // T rounded up
     const int64_t align = std::max<int64_t>(8, c.rows_per_group);

@@ -79,7 +79,7 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
 }
 
 template <int VEC, int G, int W, int F>
-__global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
+__device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     constexpr int R = W > 1 ? W - 1 : 1;
     constexpr bool NTL = (F & kNtLoad) != 0, NTS = (F & kNtStore) != 0, PF = (F & kPrefetch) != 0;
     extern __shared__ float red[];  // [waves][VEC][64], one column at a time
@@ -217,6 +217,20 @@ __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
     }
 }
 
+// The kernels: a general one (blocks of up to 8 waves, at most 256 VGPRs per wave so two
+// waves fit a SIMD), and a "solo" one for one-wave blocks run one wave per SIMD, which may use
+// the whole register file (256 VGPRs + 256 AGPRs): deeper row groups then fit without scratch
+// spills (the compiler parks values in AGPRs).
+template <int VEC, int G, int W, int F>
+__global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
+    bwd_body<VEC, G, W, F>(a);
+}
+
+template <int VEC, int G, int W, int F>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void cconv_bwd_kernel_solo(const BwdArgs a) {
+    bwd_body<VEC, G, W, F>(a);
+}
+
 // dw[d, j] = sum_p partial[p, j, d] (j < W), dbias[d] = sum_p partial[p, W, d]. A block
 // handles 64 consecutive (j, d) entries; its 4 waves each sum a contiguous quarter of the
 // partials in ascending order, then the four sums are added in wave order. Loads are issued
@@ -264,8 +278,9 @@ namespace {
 template <int VEC, int G, int W>
 hipError_t launch_bwd_f(int F, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
     switch (F) {
-#define CCONV_BWD_CASE(f) \
-    case f: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, W, f>), grid, block, lds, s, a); break;
+#define CCONV_BWD_CASE(f)                                                                                \
+    case f: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, W, f>), grid, block, lds, s, a); break;         \
+    case f + kSolo: hipLaunchKernelGGL((cconv_bwd_kernel_solo<VEC, G, W, f>), grid, block, lds, s, a); break;
         CCONV_BWD_CASE(0)
         CCONV_BWD_CASE(1)
         CCONV_BWD_CASE(2)

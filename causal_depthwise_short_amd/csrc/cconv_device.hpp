@@ -88,6 +88,7 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ p, const Row<VE
 constexpr int kNtLoad = 1;    // non-temporal loads of x (and dy)
 constexpr int kNtStore = 2;   // non-temporal stores of y (dx)
 constexpr int kPrefetch = 4;  // next group's loads issued before the current group's math
+constexpr int kSolo = 8;      // one-wave blocks, one wave per SIMD, whole register file (launch-time)
 
 // The wave's index in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }

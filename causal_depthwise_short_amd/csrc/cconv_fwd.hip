@@ -39,7 +39,7 @@ __device__ __forceinline__ Row<VEC> fwd_row(const float (&tap)[W][VEC], const fl
 }
 
 template <int VEC, int G, int W, int F>
-__global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
+__device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     constexpr int R = W > 1 ? W - 1 : 1;
     constexpr bool NTL = (F & kNtLoad) != 0, NTS = (F & kNtStore) != 0, PF = (F & kPrefetch) != 0;
     const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T);
@@ -106,13 +106,26 @@ __global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
         store_row<VEC, NTS>(at(yb + t * ys, lo), fwd_row<VEC, W>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)), ring));
 }
 
+// A general kernel (blocks of up to 8 waves) and a "solo" one for one-wave blocks run one wave
+// per SIMD, which may use the whole register file (256 VGPRs + 256 AGPRs).
+template <int VEC, int G, int W, int F>
+__global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
+    fwd_body<VEC, G, W, F>(a);
+}
+
+template <int VEC, int G, int W, int F>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void cconv_fwd_kernel_solo(const FwdArgs a) {
+    fwd_body<VEC, G, W, F>(a);
+}
+
 namespace {
 
 template <int VEC, int G, int W>
 hipError_t launch_fwd_f(int F, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
     switch (F) {
-#define CCONV_FWD_CASE(f) \
-    case f: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, W, f>), grid, block, 0, s, a); break;
+#define CCONV_FWD_CASE(f)                                                                  \
+    case f: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, W, f>), grid, block, 0, s, a); break; \
+    case f + kSolo: hipLaunchKernelGGL((cconv_fwd_kernel_solo<VEC, G, W, f>), grid, block, 0, s, a); break;
         CCONV_FWD_CASE(0)
         CCONV_FWD_CASE(1)
         CCONV_FWD_CASE(2)

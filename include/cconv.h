@@ -165,7 +165,9 @@ const char* cconv_version(void);
  *   seg_rows         rows per wave segment: a multiple of rows_per_group, >= 8
  *   options          bit 0: non-temporal loads of x (and dy); bit 1: non-temporal stores of
  *                    y (dx); bit 2: issue the next row group's loads before the current
- *                    group's arithmetic (software prefetch). Results do not depend on them.
+ *                    group's arithmetic (software prefetch); bit 3: "solo" kernels for
+ *                    one-wave blocks (waves_per_block must be 1) that run one wave per SIMD
+ *                    and may use the whole register file. Results do not depend on them.
  */
 typedef struct {
     int vec;

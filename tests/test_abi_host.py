@@ -143,6 +143,8 @@ def test_bwd_workspace_matches_plan():
         dict(vec=8, rows_per_group=8, waves_per_block=3, seg_rows=64),
         dict(vec=8, rows_per_group=8, waves_per_block=4, seg_rows=60),
         dict(vec=8, rows_per_group=8, waves_per_block=4, seg_rows=0),
+        dict(vec=8, rows_per_group=8, waves_per_block=2, options=8, seg_rows=64),
+        dict(vec=8, rows_per_group=8, waves_per_block=1, options=16, seg_rows=64),
     ],
 )
 def test_bad_config_rejected(cfg):

@@ -173,6 +173,7 @@ CONFIGS_FWD = [
     dict(vec=4, rows_per_group=4, waves_per_block=4, seg_rows=1000),
     dict(vec=8, rows_per_group=8, waves_per_block=8, strips_per_block=8, options=7, seg_rows=128),
     dict(vec=4, rows_per_group=4, waves_per_block=4, strips_per_block=2, options=3, seg_rows=200),
+    dict(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=128),
 ]
 CONFIGS_BWD = [
     dict(vec=8, rows_per_group=4, waves_per_block=4, seg_rows=64),
@@ -182,6 +183,7 @@ CONFIGS_BWD = [
     dict(vec=4, rows_per_group=8, waves_per_block=4, seg_rows=1000),
     dict(vec=8, rows_per_group=4, waves_per_block=8, strips_per_block=2, options=7, seg_rows=64),
     dict(vec=4, rows_per_group=8, waves_per_block=8, strips_per_block=8, options=3, seg_rows=128),
+    dict(vec=8, rows_per_group=8, waves_per_block=1, options=15, seg_rows=96),
 ]
 
 
@@ -281,8 +283,9 @@ def test_two_stage_backward_equals_fused():
 def test_launch_options_do_not_change_results():
     inp = si.train_inputs(2, 700, 1024, 4, bias=True, seed=23)
     base = run_train(inp)
-    for h in range(1, 8):
-        cf = cc.Config(vec=8, rows_per_group=8, waves_per_block=2, options=h, seg_rows=128)
-        cb = cc.Config(vec=4, rows_per_group=8, waves_per_block=4, options=h, seg_rows=128)
+    for h in range(1, 16):
+        wpb = 1 if h & 8 else 2
+        cf = cc.Config(vec=8, rows_per_group=8, waves_per_block=wpb, options=h, seg_rows=128)
+        cb = cc.Config(vec=4, rows_per_group=8, waves_per_block=wpb, options=h, seg_rows=128)
         y, dx, _, _ = run_train(inp, config_fwd=cf, config_bwd=cb)
         assert torch.equal(bits(y), bits(base[0])) and torch.equal(bits(dx), bits(base[1])), f"options {h}"
