@@ -54,6 +54,8 @@ def _load(path: Path, prec: str):
     lib.oracle_fwd_points.argtypes = [f, i64, i64, i64, f, ctypes.c_int, f, i64, f, f, f, f]
     lib.oracle_dx_points.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, i64, f, f, f, f]
     lib.oracle_dw_channels.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, i64, f, f, f]
+    lib.oracle_fwd_state.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, f, f]
+    lib.oracle_bwd_state.argtypes = [f, f, f, i64, i64, i64, f, ctypes.c_int, f, f, f, f, f]
     lib.oracle_update.argtypes = [f, i64, i64, f, i64, f, f, ctypes.c_int, f, f]
     lib.oracle_update.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [f, f, i64]
@@ -179,6 +181,33 @@ class Oracle:
         )
         return dw, db
 
+    def fwd_state(self, x, h0, w, bias=None, *, precision: str = "f64"):
+        """y and the final state for x [B, T, D] after the history h0 [B, D, W-1] (None =
+        zeros). Returns (y unrounded, hT float32 [B, D, W-1])."""
+        xf, hf, wf, bf = _f32(x), _f32(h0), _f32(w), _f32(bias)
+        B, T, D = xf.shape
+        W = wf.shape[1]
+        assert wf.shape == (D, W) and (hf is None or hf.shape == (B, D, W - 1))
+        y = np.empty((B, T, D), _NP[precision])
+        hT = np.empty((B, D, W - 1), np.float32)
+        self.lib(precision).oracle_fwd_state(_p(xf), _p(hf), B, T, D, _p(wf), W, _p(bf), _p(y), _p(hT))
+        return y, hT
+
+    def bwd_state(self, x, h0, dy, w, bias=None, *, precision: str = "f64"):
+        """(dx, dw, dbias, dh0) for the forward with history h0 (None = zeros)."""
+        xf, hf, dyf, wf, bf = _f32(x), _f32(h0), _f32(dy), _f32(w), _f32(bias)
+        B, T, D = xf.shape
+        W = wf.shape[1]
+        assert dyf.shape == xf.shape and wf.shape == (D, W) and (hf is None or hf.shape == (B, D, W - 1))
+        dx = np.empty((B, T, D), _NP[precision])
+        dw = np.empty((D, W), _NP[precision])
+        db = np.empty((D,), _NP[precision])
+        dh0 = np.empty((B, D, W - 1), _NP[precision])
+        self.lib(precision).oracle_bwd_state(
+            _p(xf), _p(hf), _p(dyf), B, T, D, _p(wf), W, _p(bf), _p(dx), _p(dw), _p(db), _p(dh0)
+        )
+        return dx, dw, db, dh0
+
     def update(self, x, state, state_indices, w, bias=None, *, precision: str = "f64"):
         """One decode step. Returns (ok, y [N, D], new_state float32 [S, D, W-1]).
 
@@ -237,4 +266,6 @@ fwd_points = _default.fwd_points
 dx_points = _default.dx_points
 dw_channels = _default.dw_channels
 update = _default.update
+fwd_state = _default.fwd_state
+bwd_state = _default.bwd_state
 round_bf16 = _default.round_bf16

@@ -28,6 +28,10 @@
  *    row for causal_conv1d]) and in the decode API ([cudnn-frontend PR #797 "Add experimental
  *    causal conv1d decode update", PR description, API]); read as added to z before SiLU, so
  *    dbias = sum g.
+ *  - History. [kernel-fun wheel, _common/compat.py: fla's initial_state and
+ *    output_final_state]: an optional h0 [B, D, W-1], oldest first (the decode state layout),
+ *    replaces the zero history before t = 0; the final state is the last W-1 values of the
+ *    extended sequence; the history's gradient is dx at the W-1 virtual rows before t = 0.
  *  - Decode. [PR #797 description, API and semantics]: advance a per-slot state of the last
  *    W-1 inputs by one token; conv_state_indices picks the slot, -1 marks a padding row that
  *    mutates nothing; invalid indices fail closed. Readings: state is stored oldest first
@@ -60,54 +64,58 @@ static real r_exp(real v) { return ORACLE_IS_FLOAT ? (real)expf((float)v) : (rea
 /* sigma(z) = 1 / (1 + e^-z), written from the definition. */
 static real sigmoid(real z) { return (real)1 / ((real)1 + r_exp(-z)); }
 
-/* X[b, t, d]: the input with zeros outside 0 <= t < T. */
-static real xval(const float* x, int64_t T, int64_t D, int64_t b, int64_t t, int64_t d) {
-    if (t < 0 || t >= T) return 0;
-    return (real)x[(b * T + t) * D + d];
+/* X[b, t, d]: the input for 0 <= t < T; before t = 0 the history h0[b, d, t + W - 1] (oldest
+ * first) when h0 is given, else zero; zero at or past T. */
+static real xval(const float* x, const float* h0, int64_t T, int64_t D, int W, int64_t b, int64_t t, int64_t d) {
+    if (t >= T) return 0;
+    if (t >= 0) return (real)x[(b * T + t) * D + d];
+    if (h0 && t >= -(int64_t)(W - 1)) return (real)h0[(b * D + d) * (W - 1) + (t + W - 1)];
+    return 0;
 }
 
 /* z[b, t, d] = bias[d] + sum_{j=0}^{W-1} w[d, j] * X[b, t-(W-1)+j, d]  (oldest tap first). */
-static real z_at(const float* x, int64_t T, int64_t D, const float* w, int W, const float* bias,
+static real z_at(const float* x, const float* h0, int64_t T, int64_t D, const float* w, int W, const float* bias,
                  int64_t b, int64_t t, int64_t d) {
     real z = bias ? (real)bias[d] : (real)0;
-    for (int j = 0; j < W; ++j) z = z + (real)w[d * W + j] * xval(x, T, D, b, t - (W - 1) + j, d);
+    for (int j = 0; j < W; ++j) z = z + (real)w[d * W + j] * xval(x, h0, T, D, W, b, t - (W - 1) + j, d);
     return z;
 }
 
 /* g[b, t, d] = dy * d silu/dz = dy * s * (1 + z*(1-s)), s = sigma(z); zero outside 0 <= t < T. */
-static real g_at(const float* x, const float* dy, int64_t T, int64_t D, const float* w, int W,
+static real g_at(const float* x, const float* h0, const float* dy, int64_t T, int64_t D, const float* w, int W,
                  const float* bias, int64_t b, int64_t t, int64_t d) {
     if (t < 0 || t >= T) return 0;
-    real z = z_at(x, T, D, w, W, bias, b, t, d);
+    real z = z_at(x, h0, T, D, w, W, bias, b, t, d);
     real s = sigmoid(z);
     return (real)dy[(b * T + t) * D + d] * s * ((real)1 + z * ((real)1 - s));
 }
 
-/* dx[b, u, d] = sum_{j=0}^{W-1} w[d, j] * g[b, u+(W-1)-j, d]. */
-static real dx_at(const float* x, const float* dy, int64_t T, int64_t D, const float* w, int W,
+/* dx[b, u, d] = sum_{j=0}^{W-1} w[d, j] * g[b, u+(W-1)-j, d]; for -(W-1) <= u < 0 this is the
+ * gradient of the history value at u (the initial state's gradient). */
+static real dx_at(const float* x, const float* h0, const float* dy, int64_t T, int64_t D, const float* w, int W,
                   const float* bias, int64_t b, int64_t u, int64_t d) {
     real acc = 0;
     for (int j = 0; j < W; ++j)
-        acc = acc + (real)w[d * W + j] * g_at(x, dy, T, D, w, W, bias, b, u + (W - 1) - j, d);
+        acc = acc + (real)w[d * W + j] * g_at(x, h0, dy, T, D, w, W, bias, b, u + (W - 1) - j, d);
     return acc;
 }
 
 /* dw[d, j] = sum_b sum_t g[b, t, d] * X[b, t-(W-1)+j, d]. */
-static real dw_at(const float* x, const float* dy, int64_t B, int64_t T, int64_t D, const float* w,
-                  int W, const float* bias, int64_t d, int j) {
+static real dw_at(const float* x, const float* h0, const float* dy, int64_t B, int64_t T, int64_t D,
+                  const float* w, int W, const float* bias, int64_t d, int j) {
     real acc = 0;
     for (int64_t b = 0; b < B; ++b)
         for (int64_t t = 0; t < T; ++t)
-            acc = acc + g_at(x, dy, T, D, w, W, bias, b, t, d) * xval(x, T, D, b, t - (W - 1) + j, d);
+            acc = acc + g_at(x, h0, dy, T, D, w, W, bias, b, t, d) * xval(x, h0, T, D, W, b, t - (W - 1) + j, d);
     return acc;
 }
 
 /* dbias[d] = sum_b sum_t g[b, t, d]. */
-static real dbias_at(const float* x, const float* dy, int64_t B, int64_t T, int64_t D,
+static real dbias_at(const float* x, const float* h0, const float* dy, int64_t B, int64_t T, int64_t D,
                      const float* w, int W, const float* bias, int64_t d) {
     real acc = 0;
     for (int64_t b = 0; b < B; ++b)
-        for (int64_t t = 0; t < T; ++t) acc = acc + g_at(x, dy, T, D, w, W, bias, b, t, d);
+        for (int64_t t = 0; t < T; ++t) acc = acc + g_at(x, h0, dy, T, D, w, W, bias, b, t, d);
     return acc;
 }
 
@@ -136,7 +144,7 @@ void oracle_fwd(const float* x, int64_t B, int64_t T, int64_t D, const float* w,
     for (int64_t r = 0; r < rows; ++r) {
         int64_t b = r / T, t = r % T;
         for (int64_t d = 0; d < D; ++d) {
-            real z = z_at(x, T, D, w, W, bias, b, t, d);
+            real z = z_at(x, NULL, T, D, w, W, bias, b, t, d);
             if (z_out) z_out[r * D + d] = z;
             y_out[r * D + d] = z * sigmoid(z);
         }
@@ -150,12 +158,12 @@ void oracle_bwd(const float* x, const float* dy, int64_t B, int64_t T, int64_t D
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         int64_t b = r / T, u = r % T;
-        for (int64_t d = 0; d < D; ++d) dx_out[r * D + d] = dx_at(x, dy, T, D, w, W, bias, b, u, d);
+        for (int64_t d = 0; d < D; ++d) dx_out[r * D + d] = dx_at(x, NULL, dy, T, D, w, W, bias, b, u, d);
     }
 #pragma omp parallel for schedule(static)
     for (int64_t d = 0; d < D; ++d) {
-        for (int j = 0; j < W; ++j) dw_out[d * W + j] = dw_at(x, dy, B, T, D, w, W, bias, d, j);
-        if (dbias_out) dbias_out[d] = dbias_at(x, dy, B, T, D, w, W, bias, d);
+        for (int j = 0; j < W; ++j) dw_out[d * W + j] = dw_at(x, NULL, dy, B, T, D, w, W, bias, d, j);
+        if (dbias_out) dbias_out[d] = dbias_at(x, NULL, dy, B, T, D, w, W, bias, d);
     }
 }
 
@@ -166,7 +174,7 @@ void oracle_fwd_points(const float* x, int64_t B, int64_t T, int64_t D, const fl
     (void)B;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
-        real z = z_at(x, T, D, w, W, bias, pb[i], pt[i], pd[i]);
+        real z = z_at(x, NULL, T, D, w, W, bias, pb[i], pt[i], pd[i]);
         y_out[i] = z * sigmoid(z);
     }
 }
@@ -177,7 +185,7 @@ void oracle_dx_points(const float* x, const float* dy, int64_t B, int64_t T, int
                       const int64_t* pu, const int64_t* pd, real* dx_out) {
     (void)B;
 #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; ++i) dx_out[i] = dx_at(x, dy, T, D, w, W, bias, pb[i], pu[i], pd[i]);
+    for (int64_t i = 0; i < n; ++i) dx_out[i] = dx_at(x, NULL, dy, T, D, w, W, bias, pb[i], pu[i], pd[i]);
 }
 
 /* Sampled weight gradient: dw[d, :] and dbias[d] for n listed channels (full sums). */
@@ -186,9 +194,56 @@ void oracle_dw_channels(const float* x, const float* dy, int64_t B, int64_t T, i
                         real* dw_out /* [n, W] */, real* dbias_out /* [n] */) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
-        for (int j = 0; j < W; ++j) dw_out[i * W + j] = dw_at(x, dy, B, T, D, w, W, bias, pd[i], j);
-        dbias_out[i] = dbias_at(x, dy, B, T, D, w, W, bias, pd[i]);
+        for (int j = 0; j < W; ++j) dw_out[i * W + j] = dw_at(x, NULL, dy, B, T, D, w, W, bias, pd[i], j);
+        dbias_out[i] = dbias_at(x, NULL, dy, B, T, D, w, W, bias, pd[i]);
     }
+}
+
+/*
+ * Forward with a history [kernel-fun wheel, _common/compat.py: fla's initial_state and
+ * output_final_state parameters]: h0 [B, D, W-1] (oldest first, NULL = zeros) is the input
+ * before t = 0; hT [B, D, W-1] (may be NULL) receives the last W-1 values of the extended
+ * sequence (history then x), i.e. the state a decode update continues from.
+ */
+void oracle_fwd_state(const float* x, const float* h0, int64_t B, int64_t T, int64_t D, const float* w, int W,
+                      const float* bias, real* y_out, float* hT_out) {
+    int64_t rows = B * T;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / T, t = r % T;
+        for (int64_t d = 0; d < D; ++d) {
+            real z = z_at(x, h0, T, D, w, W, bias, b, t, d);
+            y_out[r * D + d] = z * sigmoid(z);
+        }
+    }
+    if (hT_out)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t d = 0; d < D; ++d)
+                for (int j = 0; j < W - 1; ++j)
+                    hT_out[(b * D + d) * (W - 1) + j] = (float)xval(x, h0, T, D, W, b, T - (W - 1) + j, d);
+}
+
+/* Backward with a history: dx, dw, dbias as oracle_bwd with X extended by h0, and dh0 [B, D,
+ * W-1] (may be NULL): the gradient of each history value, dx at u = -(W-1) .. -1. */
+void oracle_bwd_state(const float* x, const float* h0, const float* dy, int64_t B, int64_t T, int64_t D,
+                      const float* w, int W, const float* bias, real* dx_out, real* dw_out, real* dbias_out,
+                      real* dh0_out) {
+    int64_t rows = B * T;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / T, u = r % T;
+        for (int64_t d = 0; d < D; ++d) dx_out[r * D + d] = dx_at(x, h0, dy, T, D, w, W, bias, b, u, d);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t d = 0; d < D; ++d) {
+        for (int j = 0; j < W; ++j) dw_out[d * W + j] = dw_at(x, h0, dy, B, T, D, w, W, bias, d, j);
+        if (dbias_out) dbias_out[d] = dbias_at(x, h0, dy, B, T, D, w, W, bias, d);
+    }
+    if (dh0_out)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t d = 0; d < D; ++d)
+                for (int j = 0; j < W - 1; ++j)
+                    dh0_out[(b * D + d) * (W - 1) + j] = dx_at(x, h0, dy, T, D, w, W, bias, b, -(int64_t)(W - 1) + j, d);
 }
 
 /*

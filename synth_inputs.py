@@ -123,3 +123,17 @@ def decode_inputs(
 
 def decode_inputs_for(shape: DecodeShape, **kw) -> dict:
     return decode_inputs(shape.N, shape.S, shape.D, shape.W, bias=shape.bias, seed=shape.seed, **kw)
+
+
+def train_inputs_device(
+    B: int, T: int, D: int, W: int, *, bias: bool, seed: int, device: str = "cuda"
+) -> dict:
+    """The same recipe as train_inputs, drawn by a seeded generator on the device (for sizes
+    whose host copies would be impractical). Values differ from train_inputs' for the same
+    seed; both sides still see identical bits, since host windows are copied from these."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    x = (torch.randn(B, T, D, generator=g, device=device, dtype=torch.float32)).to(torch.bfloat16)
+    w = (torch.randn(D, W, generator=g, device=device, dtype=torch.float32) * math.sqrt(1.0 / W)).to(torch.bfloat16)
+    b = torch.randn(D, generator=g, device=device, dtype=torch.float32) * math.sqrt(0.1) if bias else None
+    dy = torch.randn(B, T, D, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return {"x": x, "w": w, "bias": b, "dy": dy}

@@ -387,6 +387,94 @@ def check_f32_close_to_f64(orc):
     _close(db32, db64, 1e-5, 1e-5, what="f32 dbias")
 
 
+def _problem_h0(seed, B, T, D, W, bias=True):
+    x, w, b, dy = _problem(seed, B, T, D, W, bias)
+    rng = np.random.default_rng(seed + 1000)
+    h0 = _bf16_values(rng, (B, D, W - 1))
+    return x, h0, w, b, dy
+
+
+def check_history_torch(orc):
+    """float64 torch conv1d (no padding) over the history followed by x, SiLU, autograd: y, the
+    final state (the last W-1 inputs), dx, dw, dbias and the history's gradient."""
+    for W in (1, 2, 3, 4):
+        for T in (1, 2, 13):
+            x, h0, w, b, dy = _problem_h0(140 + W + T, 2, T, 5, W)
+            B, _, D = x.shape
+            xe = torch.cat([torch.tensor(h0, dtype=torch.float64).permute(0, 2, 1), torch.tensor(x, dtype=torch.float64)], 1)
+            xe.requires_grad_(True)
+            wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+            bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+            z = F.conv1d(xe.transpose(1, 2), wt[:, None, :], bt, padding=0, groups=D)
+            y_t = F.silu(z).transpose(1, 2)
+            (y_t * torch.tensor(dy, dtype=torch.float64)).sum().backward()
+            y, hT = orc.fwd_state(x, h0, w, b)
+            _close(y, y_t.detach().numpy(), 1e-12, 1e-14, what=f"history y W={W} T={T}")
+            want_hT = xe.detach()[:, T:, :].permute(0, 2, 1).numpy()  # the last W-1 rows of [h0; x]
+            assert np.array_equal(hT.astype(np.float64), want_hT), f"final state W={W} T={T}"
+            dx, dw, db, dh0 = orc.bwd_state(x, h0, dy, w, b)
+            ge = xe.grad.numpy()
+            _close(dx, ge[:, W - 1 :, :], 1e-12, 1e-13, what=f"history dx W={W} T={T}")
+            _close(dh0, ge[:, : W - 1, :].transpose(0, 2, 1), 1e-12, 1e-13, what=f"history dh0 W={W} T={T}")
+            _close(dw, wt.grad.numpy(), 1e-12, 1e-12, what=f"history dw W={W} T={T}")
+            _close(db, bt.grad.numpy(), 1e-12, 1e-12, what=f"history dbias W={W} T={T}")
+
+
+def check_history_chunking(orc):
+    """Processing a sequence in two chunks, the second starting from the first's final state,
+    equals processing it whole: y and the final state exactly; dx exactly on the second chunk
+    and, on the first, after adding the second chunk's history gradient; dw as a sum."""
+    for W in (2, 3, 4):
+        x, h0, w, b, dy = _problem_h0(160 + W, 2, 17, 4, W)
+        T1 = 9
+        y, hT = orc.fwd_state(x, h0, w, b)
+        y1, h1 = orc.fwd_state(x[:, :T1], h0, w, b)
+        y2, h2 = orc.fwd_state(x[:, T1:], h1, w, b)
+        assert np.array_equal(y, np.concatenate([y1, y2], 1)) and np.array_equal(hT, h2), f"chunked forward W={W}"
+        dx, dw, db, dh0 = orc.bwd_state(x, h0, dy, w, b)
+        dx1, dw1, db1, dh01 = orc.bwd_state(x[:, :T1], h0, dy[:, :T1], w, b)
+        dx2, dw2, db2, dh02 = orc.bwd_state(x[:, T1:], h1, dy[:, T1:], w, b)
+        assert np.array_equal(dx[:, T1:], dx2), f"chunked dx (second chunk) W={W}"
+        joined = dx1.copy()
+        joined[:, T1 - (W - 1) :, :] += dh02.transpose(0, 2, 1)
+        _close(dx[:, :T1], joined, 1e-12, 1e-13, what=f"chunked dx (first chunk) W={W}")
+        assert np.array_equal(dh0, dh01), f"chunked history gradient W={W}"
+        _close(dw, dw1 + dw2, 1e-12, 1e-12, what=f"chunked dw W={W}")
+        _close(db, db1 + db2, 1e-12, 1e-12, what=f"chunked dbias W={W}")
+
+
+def check_history_zero_is_plain(orc):
+    """A zero history is the plain op, exactly; the history gradient is dx at the W-1 rows
+    before t = 0 (equal to the plain op's gradient of a zero-padded input)."""
+    x, _, w, b, dy = _problem_h0(180, 2, 11, 5, 4)
+    z0 = np.zeros((2, 5, 3), np.float32)
+    _, y = orc.fwd(x, w, b)
+    ys, _ = orc.fwd_state(x, z0, w, b)
+    ysn, _ = orc.fwd_state(x, None, w, b)
+    assert np.array_equal(y, ys) and np.array_equal(y, ysn)
+    dx, dw, db = orc.bwd(x, dy, w, b)
+    dxs, dws, dbs, dh0 = orc.bwd_state(x, z0, dy, w, b)
+    assert np.array_equal(dx, dxs) and np.array_equal(dw, dws) and np.array_equal(db, dbs)
+    xp = np.concatenate([np.zeros((2, 3, 5), np.float32), x], 1)
+    dyp = np.concatenate([np.zeros((2, 3, 5), np.float32), dy], 1)
+    dxp, _, _ = orc.bwd(xp, dyp, w, b)
+    assert np.array_equal(dh0, dxp[:, :3].transpose(0, 2, 1)), "history gradient vs zero-padded input"
+
+
+def check_prefill_then_decode(orc):
+    """A prefill from a history, then token-by-token decode from its final state, reproduces
+    the forward of the whole extended sequence bitwise (in the oracle)."""
+    for W in (2, 4):
+        x, h0, w, b, _ = _problem_h0(190 + W, 3, 12, 6, W)
+        T1 = 7
+        y, hT = orc.fwd_state(x, h0, w, b)
+        _, state = orc.fwd_state(x[:, :T1], h0, w, b)
+        for t in range(T1, 12):
+            ok, yt, state = orc.update(x[:, t], state, None, w, b)
+            assert ok and np.array_equal(yt, y[:, t]), f"decode after prefill W={W} t={t}"
+        assert np.array_equal(state, hT), f"final state after decode W={W}"
+
+
 ALL_CHECKS = [
     check_rounding_matches_torch,
     check_rounding_from_double_is_direct,
@@ -404,4 +492,8 @@ ALL_CHECKS = [
     check_decode_index_validation,
     check_points_match_full,
     check_f32_close_to_f64,
+    check_history_torch,
+    check_history_chunking,
+    check_history_zero_is_plain,
+    check_prefill_then_decode,
 ]

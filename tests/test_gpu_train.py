@@ -289,3 +289,43 @@ def test_launch_options_do_not_change_results():
         cb = cc.Config(vec=4, rows_per_group=8, waves_per_block=wpb, options=h, seg_rows=128)
         y, dx, _, _ = run_train(inp, config_fwd=cf, config_bwd=cb)
         assert torch.equal(bits(y), bits(base[0])) and torch.equal(bits(dx), bits(base[1])), f"options {h}"
+
+
+def test_offsets_beyond_2_31_elements():
+    """B*T*D > 2^31 (4.3 GB per tensor, ragged last segment): every offset is 64-bit. Checked
+    against the oracle on windows of the full tensors around sampled points and on full
+    per-channel sums for sampled channels."""
+    B, T, D, W = 2, 262151, 4096, 4
+    assert B * T * D > 2**31
+    g = si.train_inputs_device(B, T, D, W, bias=True, seed=31)
+    y = cc.cconv_fwd(g["x"], g["w"], g["bias"])
+    dx, dw, db = cc.cconv_bwd(g["x"], g["dy"], g["w"], g["bias"], dw_dtype=torch.float32)
+    torch.cuda.synchronize()
+    w_h, b_h = g["w"].cpu(), g["bias"].cpu()
+    rng = np.random.default_rng(5)
+    pts = [(b_, t, d) for b_, t, d in zip(rng.integers(0, B, 40), rng.integers(0, T, 40), rng.integers(0, D, 40))]
+    pts += [(1, T - 1, D - 1), (1, T - 4, 4095), (0, 0, 0), (1, 3, 777)]
+    for b_, t, d in pts:
+        b_, t, d = int(b_), int(t), int(d)
+        lo, hi = max(0, t - (W - 1)), min(T, t + W)
+        xw = g["x"][b_ : b_ + 1, max(0, lo - (W - 1)) : hi].cpu()
+        dyw = g["dy"][b_ : b_ + 1, max(0, lo - (W - 1)) : hi].cpu()
+        off = t - max(0, lo - (W - 1))
+        # windows start at the sequence start or at least W-1 rows before every row they
+        # answer for, and end at the sequence end or W-1 rows after it
+        _, yr = oracle.fwd(xw, w_h, b_h)
+        assert abs(float(y[b_, t, d]) - yr[0, off, d]) <= TOL_FWD * max(1.0, abs(yr[0, off, d])), (b_, t, d)
+        if hi == T or hi - t >= W:
+            dxr, _, _ = oracle.bwd(xw, dyw, w_h, b_h)
+            assert abs(float(dx[b_, t, d]) - dxr[0, off, d]) <= TOL_BWD * max(1.0, abs(dxr[0, off, d])), (b_, t, d)
+    for d in (0, 1, 2047, 4095):
+        xc = g["x"][:, :, d : d + 1].cpu()
+        dyc = g["dy"][:, :, d : d + 1].cpu()
+        dwr, dbr = oracle.dw_channels(xc, dyc, w_h[d : d + 1], b_h[d : d + 1], [0])
+        assert_close(dw[d : d + 1].cpu(), dwr, TOL_BWD, f"dw channel {d}")
+        assert_close(db[d : d + 1].cpu(), dbr, TOL_BWD, f"dbias channel {d}")
+
+
+def test_very_wide_channels():
+    inp = si.train_inputs(1, 33, 131072, 3, bias=True, seed=37)
+    check_against_oracle(inp, run_train(inp), "D=131072")

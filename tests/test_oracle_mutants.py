@@ -16,16 +16,16 @@ import oracle
 
 # (name, old text, new text): the first occurrence of `old` is replaced.
 MUTANTS = [
-    ("tap_order_reversed", "xval(x, T, D, b, t - (W - 1) + j, d);\n    return z;", "xval(x, T, D, b, t - j, d);\n    return z;"),
+    ("tap_order_reversed", "xval(x, h0, T, D, W, b, t - (W - 1) + j, d);\n    return z;", "xval(x, h0, T, D, W, b, t - j, d);\n    return z;"),
     ("bias_dropped", "real z = bias ? (real)bias[d] : (real)0;\n    for (int j = 0; j < W; ++j)", "real z = 0;\n    for (int j = 0; j < W; ++j)"),
     ("sigmoid_sign", "r_exp(-z)", "r_exp(z)"),
     ("dsilu_sign", "s * ((real)1 + z * ((real)1 - s))", "s * ((real)1 - z * ((real)1 - s))"),
     ("dsilu_dy_dropped", "return (real)dy[(b * T + t) * D + d] * s *", "return s *"),
-    ("dx_index", "g_at(x, dy, T, D, w, W, bias, b, u + (W - 1) - j, d)", "g_at(x, dy, T, D, w, W, bias, b, u + j, d)"),
+    ("dx_index", "g_at(x, h0, dy, T, D, w, W, bias, b, u + (W - 1) - j, d)", "g_at(x, h0, dy, T, D, w, W, bias, b, u + j, d)"),
     ("dx_tap_transposed", "acc = acc + (real)w[d * W + j] * g_at", "acc = acc + (real)w[d * W + (W - 1 - j)] * g_at"),
-    ("dw_index", "* xval(x, T, D, b, t - (W - 1) + j, d);\n    return acc;", "* xval(x, T, D, b, t - j, d);\n    return acc;"),
+    ("dw_index", "* xval(x, h0, T, D, W, b, t - (W - 1) + j, d);\n    return acc;", "* xval(x, h0, T, D, W, b, t - j, d);\n    return acc;"),
     ("dbias_skips_head", "for (int64_t t = 0; t < T; ++t) acc = acc + g_at", "for (int64_t t = W - 1; t < T; ++t) acc = acc + g_at"),
-    ("replicate_left_pad", "if (t < 0 || t >= T) return 0;\n    return (real)x", "if (t >= T) return 0;\n    if (t < 0) t = 0;\n    return (real)x"),
+    ("replicate_left_pad", "    return 0;\n}\n\n/* z[b, t, d]", "    return (real)x[(b * T + 0) * D + d];\n}\n\n/* z[b, t, d]"),
     ("g_not_zero_past_T", "if (t < 0 || t >= T) return 0;\n    real z", "if (t < 0) return 0;\n    if (t >= T) t = T - 1;\n    real z"),
     ("decode_taps_reversed", "(real)w[d * W + j] * (real)st[j]", "(real)w[d * W + (L - 1 - j)] * (real)st[j]"),
     ("decode_new_token_tap", "(real)w[d * W + (W - 1)] * (real)x[n * D + d]", "(real)w[d * W + 0] * (real)x[n * D + d]"),
@@ -33,6 +33,10 @@ MUTANTS = [
     ("decode_no_duplicate_check", "if (idx[n] >= 0 && idx[n] == idx[m]) return 1;", "(void)m;"),
     ("decode_range_off_by_one", "idx[n] >= S) return 1;", "idx[n] > S) return 1;"),
     ("decode_padding_output", "y_out[n * D + d] = 0;", "y_out[n * D + d] = (real)x[n * D + d];"),
+    ("history_reversed", "h0[(b * D + d) * (W - 1) + (t + W - 1)]", "h0[(b * D + d) * (W - 1) + (-1 - t)]"),
+    ("history_ignored", "if (h0 && t >= -(int64_t)(W - 1))", "if (0)"),
+    ("final_state_off_by_one", "xval(x, h0, T, D, W, b, T - (W - 1) + j, d)", "xval(x, h0, T, D, W, b, T - W + j, d)"),
+    ("history_grad_shifted", "b, -(int64_t)(W - 1) + j, d)", "b, -(int64_t)(W - 1) + j + 1, d)"),
     ("round_half_away", "nearbyint(a / q)", "floor(a / q + 0.5)"),
     ("round_truncate", "nearbyint(a / q)", "trunc(a / q)"),
 ]
