@@ -23,6 +23,8 @@ __all__ = [
     "lib",
     "cconv_fwd",
     "cconv_bwd",
+    "cconv_fwd_state",
+    "cconv_bwd_state",
     "cconv_bwd_workspace_bytes",
     "cconv_bwd_main",
     "cconv_bwd_finish",
@@ -102,6 +104,11 @@ def _declare(L):
     L.cconv_bwd.restype = i32
     L.cconv_bwd_config.argtypes = bwd + [ctypes.POINTER(Config), p]
     L.cconv_bwd_config.restype = i32
+    L.cconv_fwd_state.argtypes = [p, i64, i64, p, i32, p, p, p, p, i64, i64, i64, i32, p]
+    L.cconv_fwd_state.restype = i32
+    L.cconv_bwd_state.argtypes = [p, i64, i64, p, i64, i64, p, i32, p, p, p, p, i32, p, p, p, sz, i64, i64, i64,
+                                  i32, p]
+    L.cconv_bwd_state.restype = i32
     L.cconv_bwd_main.argtypes = [p, i64, i64, p, i64, i64, p, i32, p, p, p, sz, i64, i64, i64, i32, p]
     L.cconv_bwd_main.restype = i32
     L.cconv_bwd_finish.argtypes = [p, sz, p, i32, p, i64, i64, i64, i32, p]
@@ -285,6 +292,97 @@ def cconv_bwd(
     else:
         _check(L.cconv_bwd_config(*args, ctypes.byref(config), _stream(stream)), "cconv_bwd_config")
     return dx, dw, dbias
+
+
+def _state(t: Optional[torch.Tensor], name: str, B: int, D: int, W: int):
+    if t is None:
+        return
+    _dev(t, name)
+    if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, D, W - 1) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bf16 [B, D, W-1] tensor")
+
+
+def cconv_fwd_state(x, w, bias=None, init_state=None, *, final_state=None, want_final_state=True, y=None,
+                    stream=None):
+    """Forward with a history before t = 0; returns (y, final_state).
+
+    init_state, final_state: bf16 [B, D, W-1], oldest value first (the decode state layout).
+    init_state None means zeros. final_state (allocated when None and wanted) receives the last
+    W-1 values of history-then-x; passing init_state itself advances it in place.
+    """
+    sb, st = _act(x, "x")
+    B, T, D = x.shape
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    _state(init_state, "init_state", B, D, W)
+    if want_final_state and final_state is None:
+        final_state = torch.empty((B, D, W - 1), dtype=torch.bfloat16, device=x.device)
+    _state(final_state, "final_state", B, D, W)
+    if y is None:
+        y = torch.empty((B, T, D), dtype=torch.bfloat16, device=x.device)
+    elif y.dtype != torch.bfloat16 or tuple(y.shape) != (B, T, D) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous bf16 [B, T, D] tensor")
+    _check(
+        lib().cconv_fwd_state(
+            _ptr(x), sb, st, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(init_state), _ptr(final_state), _ptr(y),
+            B, T, D, W, _stream(stream),
+        ),
+        "cconv_fwd_state",
+    )
+    return y, final_state
+
+
+def cconv_bwd_state(x, dy, w, bias=None, init_state=None, *, dx=None, dw=None, dbias=None, d_init_state=None,
+                    want_dbias: bool = True, want_d_init_state: bool = True, dw_dtype=None, workspace=None,
+                    stream=None):
+    """Backward with a history before t = 0; returns (dx, dw, dbias, d_init_state).
+
+    dw includes the products with the history; d_init_state (bf16 [B, D, W-1]) is the gradient
+    of each history value.
+    """
+    sb, st = _act(x, "x")
+    dsb, dst = _act(dy, "dy")
+    B, T, D = x.shape
+    if tuple(dy.shape) != (B, T, D):
+        raise ValueError("dy must have x's shape")
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    _state(init_state, "init_state", B, D, W)
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((B, T, D), dtype=torch.bfloat16, device=dev)
+    if dw is None:
+        dw = torch.empty((D, W), dtype=dw_dtype or w.dtype, device=dev)
+    if want_dbias and dbias is None:
+        dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    if want_d_init_state and d_init_state is None:
+        d_init_state = torch.empty((B, D, W - 1), dtype=torch.bfloat16, device=dev)
+    _state(d_init_state, "d_init_state", B, D, W)
+    need = cconv_bwd_workspace_bytes(B, T, D, W)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(
+        lib().cconv_bwd_state(
+            _ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(init_state), _ptr(dx),
+            _ptr(dw), _wdt(dw, "dw"), _ptr(dbias), _ptr(d_init_state), _ptr(workspace), ws_bytes, B, T, D, W,
+            _stream(stream),
+        ),
+        "cconv_bwd_state",
+    )
+    return dx, dw, dbias, d_init_state
 
 
 def cconv_bwd_main(x, dy, w, bias, dx, workspace, *, stream=None):

@@ -134,7 +134,8 @@ size_t bwd_workspace(const Plan& p, int64_t D, int W) {
 
 cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
                         const float* bias, void* y, int64_t B, int64_t T, int64_t D, int W,
-                        const cconv_config_t* cfg, cconv_stream_t stream) {
+                        const cconv_config_t* cfg, cconv_stream_t stream, const void* h0 = nullptr,
+                        void* hT = nullptr) {
     // a pointer may be NULL only when its tensor is empty
     const bool act_empty = (B == 0 || T == 0 || D == 0);
     if ((!x && !act_empty) || (!w && D > 0) || (!y && !act_empty)) return CCONV_ERR_NULL_POINTER;
@@ -145,12 +146,22 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
     const Span sy = span(y, extent3(B, T, D, T * D, D, 2));
-    if (overlap(sy, span(x, extent3(B, T, D, x_sb, x_st, 2))) ||
-        overlap(sy, span(w, static_cast<__int128>(D) * W * esize(w_dtype))) ||
-        (bias && overlap(sy, span(bias, static_cast<__int128>(D) * 4))))
+    const Span sx = span(x, extent3(B, T, D, x_sb, x_st, 2));
+    const Span sw = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
+    const Span sb = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
+    if (overlap(sy, sx) || overlap(sy, sw) || overlap(sy, sb)) return CCONV_ERR_ALIASING;
+    // history in, final state out: [B, D, W-1] bf16; the final state may be the history's own
+    // buffer (advancing a cache in place) but must not overlap anything else
+    if (W == 1) h0 = hT = nullptr;
+    if (!aligned(h0, 16) || !aligned(hT, 16)) return CCONV_ERR_MISALIGNED;
+    const __int128 state_bytes = static_cast<__int128>(B) * D * (W - 1) * 2;
+    const Span sh0 = span(h0, state_bytes), shT = span(hT, state_bytes);
+    if (overlap(sh0, sy) || overlap(shT, sy) || overlap(shT, sx) || overlap(shT, sw) || overlap(shT, sb) ||
+        (hT != h0 && overlap(shT, sh0)))
         return CCONV_ERR_ALIASING;
     Plan p;
     if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
+    if (hT && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;  // a final state needs at least one token
     if (B == 0 || T == 0 || D == 0) return CCONV_OK;
     cconv::FwdArgs a;
     a.x = static_cast<const uint16_t*>(x);
@@ -160,6 +171,8 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     a.w_f32 = (w_dtype == CCONV_F32);
     a.bias = bias;
     a.y = static_cast<uint16_t*>(y);
+    a.h0 = static_cast<const uint16_t*>(h0);
+    a.hT = static_cast<uint16_t*>(hT);
     a.B = B;
     a.T = T;
     a.D = D;
@@ -178,7 +191,8 @@ constexpr int kMain = 1, kFinish = 2;
 cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
                         int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
                         cconv_dtype_t dw_dtype, float* dbias, void* workspace, size_t workspace_bytes, int64_t B,
-                        int64_t T, int64_t D, int W, const cconv_config_t* cfg, cconv_stream_t stream) {
+                        int64_t T, int64_t D, int W, const cconv_config_t* cfg, cconv_stream_t stream,
+                        const void* h0 = nullptr, void* dh0 = nullptr) {
     const bool act_empty = (B == 0 || T == 0 || D == 0);
     const bool main = (stages & kMain) != 0, finish = (stages & kFinish) != 0;
     if (main && (((!x || !dy || !dx) && !act_empty) || (!w && D > 0))) return CCONV_ERR_NULL_POINTER;
@@ -217,15 +231,21 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     const Span o_dw = span(dw, static_cast<__int128>(D) * W * esize(dw_dtype));
     const Span o_db = dbias ? span(dbias, static_cast<__int128>(D) * 4) : Span{0, 0};
     const Span o_ws = span(workspace, need);
-    const Span outs[4] = {o_dx, o_dw, o_db, o_ws};
-    const Span ins[4] = {in_x, in_dy, in_w, in_b};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 4; ++j)
+    if (W == 1 || !main) h0 = dh0 = nullptr;
+    if (!aligned(h0, 16) || !aligned(dh0, 16)) return CCONV_ERR_MISALIGNED;
+    const __int128 state_bytes = static_cast<__int128>(B) * D * (W - 1) * 2;
+    const Span in_h = span(h0, state_bytes);
+    const Span o_dh = span(dh0, state_bytes);
+    const Span outs[5] = {o_dx, o_dw, o_db, o_ws, o_dh};
+    const Span ins[5] = {in_x, in_dy, in_w, in_b, in_h};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 5; ++j)
             if (overlap(outs[i], ins[j])) return CCONV_ERR_ALIASING;
-        for (int j = i + 1; j < 4; ++j)
+        for (int j = i + 1; j < 5; ++j)
             if (overlap(outs[i], outs[j])) return CCONV_ERR_ALIASING;
     }
     if (workspace_bytes < need) return CCONV_ERR_WORKSPACE;
+    if (dh0 && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;  // a history gradient needs at least one token
     if (D == 0) return CCONV_OK;
 
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -243,6 +263,8 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
         a.bias = bias;
         a.dx = static_cast<uint16_t*>(dx);
         a.partial = static_cast<float*>(workspace);
+        a.h0 = static_cast<const uint16_t*>(h0);
+        a.dh0 = static_cast<uint16_t*>(dh0);
         a.B = B;
         a.T = T;
         a.D = D;
@@ -272,6 +294,21 @@ cconv_status_t cconv_fwd(const void* x, int64_t x_sb, int64_t x_st, const void* 
                          const float* bias, void* y, int64_t B, int64_t T, int64_t D, int W,
                          cconv_stream_t stream) {
     return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream);
+}
+
+cconv_status_t cconv_fwd_state(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
+                               const float* bias, const void* init_state, void* final_state, void* y, int64_t B,
+                               int64_t T, int64_t D, int W, cconv_stream_t stream) {
+    return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream, init_state, final_state);
+}
+
+cconv_status_t cconv_bwd_state(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
+                               int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias,
+                               const void* init_state, void* dx, void* dw, cconv_dtype_t dw_dtype, float* dbias,
+                               void* d_init_state, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                               int64_t D, int W, cconv_stream_t stream) {
+    return bwd_impl(kMain | kFinish, x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias,
+                    workspace, workspace_bytes, B, T, D, W, nullptr, stream, init_state, d_init_state);
 }
 
 cconv_status_t cconv_fwd_config(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,

@@ -28,7 +28,8 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
                                         float (&xr)[W > 1 ? W - 1 : 1][VEC],
                                         float (&gr)[W > 1 ? W - 1 : 1][VEC], float (&acc)[W][VEC],
                                         float (&db)[VEC], bool acc_on, bool emit,
-                                        uint16_t* __restrict__ dxrow, uint32_t lo) {
+                                        uint16_t* __restrict__ dxrow, uint32_t lo, uint16_t* hist_grad = nullptr,
+                                        int64_t hb = 0, int64_t D = 0, int64_t d = 0, int hj = 0) {
     float xt[VEC], dyt[VEC], g[VEC];
     widen(rx, xt);
     widen(rdy, dyt);
@@ -60,7 +61,12 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
             for (int k = 1; k < W; ++k) s = __builtin_fmaf(tap[k][v], k == W - 1 ? g[v] : gr[W - 2 - k][v], s);
             dx[v] = s;
         }
-        store_row<VEC, NTS>(at(dxrow, lo), narrow<VEC>(dx));
+        if (hist_grad) {  // a row before t = 0: the history's gradient, slot hj of [B, D, W-1]
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) store_state_bf16(hist_grad, hb, D, d + v, W - 1, hj, dx[v]);
+        } else {
+            store_row<VEC, NTS>(at(dxrow, lo), narrow<VEC>(dx));
+        }
     }
 #pragma unroll
     for (int k = W - 2; k > 0; --k)
@@ -110,6 +116,10 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         float bs[VEC];
         load_bias<VEC>(a.bias, wt.d, bs);
 
+        // ring prologue as in the forward; before t = 0, the history (or zeros)
+        const bool first = (t0 == 0);
+        float hist[R][VEC];
+        if (first) load_history<VEC, W>(a.h0, wt.b, a.D, wt.d, hist);
         float xr[R][VEC], gr[R][VEC];
 #pragma unroll
         for (int k = 0; k < R; ++k) {
@@ -118,11 +128,14 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
                 widen(load_row<VEC>(at(xb + t * xs, lo)), xr[k]);
             } else {
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) xr[k][v] = 0.0f;
+                for (int v = 0; v < VEC; ++v) xr[k][v] = (W > 1 && first) ? hist[R - 1 - k][v] : 0.0f;
             }
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) gr[k][v] = 0.0f;  // rows before t0 are not ours
+            for (int v = 0; v < VEC; ++v) gr[k][v] = 0.0f;  // rows before t0 are not ours (history rows have g = 0)
         }
+        // With a history gradient requested, the first segment also emits "dx" for the W-1
+        // rows before t = 0, into dh0; elsewhere rows before t0 belong to the previous segment.
+        uint16_t* const hg = (first && a.dh0) ? a.dh0 : nullptr;
 
         int64_t t = t0;
         if constexpr (PF) {
@@ -144,7 +157,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
                         const int64_t u = t + g - (W - 1);
-                        bwd_row<VEC, W, NTS>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, true, u >= t0, dxb + u * dxs, lo);
+                        bwd_row<VEC, W, NTS>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, true, u >= t0 || (hg && u >= -R),
+                                             dxb + u * dxs, lo, u < 0 ? hg : nullptr, wt.b, a.D, wt.d,
+                                             static_cast<int>(u + R));
                     }
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
@@ -163,14 +178,17 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const int64_t u = t + g - (W - 1);
-                    bwd_row<VEC, W, NTS>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, true, u >= t0, dxb + u * dxs, lo);
+                    bwd_row<VEC, W, NTS>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, true, u >= t0 || (hg && u >= -R),
+                                         dxb + u * dxs, lo, u < 0 ? hg : nullptr, wt.b, a.D, wt.d,
+                                         static_cast<int>(u + R));
                 }
             }
         }
         for (; t < t1; ++t) {
             const int64_t u = t - (W - 1);
             bwd_row<VEC, W, NTS>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)), load_row<VEC, NTL>(at(dyb + t * dys, lo)),
-                                 xr, gr, acc, db, true, u >= t0, dxb + u * dxs, lo);
+                                 xr, gr, acc, db, true, u >= t0 || (hg && u >= -R), dxb + u * dxs, lo,
+                                 u < 0 ? hg : nullptr, wt.b, a.D, wt.d, static_cast<int>(u + R));
         }
         // right halo: rows t1 .. t1+W-2 finish dx of this segment's last W-1 rows; rows at or
         // past T have g = 0 (their x and dy read as zero).
@@ -183,7 +201,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
                 hx = load_row<VEC>(at(xb + th * xs, lo));
                 hdy = load_row<VEC>(at(dyb + th * dys, lo));
             }
-            bwd_row<VEC, W, NTS>(tap, bs, hx, hdy, xr, gr, acc, db, false, u >= t0, dxb + u * dxs, lo);
+            bwd_row<VEC, W, NTS>(tap, bs, hx, hdy, xr, gr, acc, db, false, u >= t0 || (hg && u >= -R), dxb + u * dxs,
+                                 lo, u < 0 ? hg : nullptr, wt.b, a.D, wt.d, static_cast<int>(u + R));
         }
     }
 

@@ -194,6 +194,25 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t pid, int64_t n) {
     return xcd * q + (xcd < r ? xcd : r) + k;
 }
 
+// The history before t = 0 of VEC consecutive channels d.. of batch row b: hist[j][v] =
+// h0[b, d+v, j] (j = 0 is the oldest), from the [B, D, W-1] layout; zeros without h0.
+template <int VEC, int W>
+__device__ __forceinline__ void load_history(const uint16_t* h0, int64_t b, int64_t D, int64_t d,
+                                             float (&hist)[W > 1 ? W - 1 : 1][VEC]) {
+    constexpr int L = W - 1;
+#pragma unroll
+    for (int j = 0; j < (L > 0 ? L : 1); ++j)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+            hist[j][v] = (h0 && L > 0) ? __uint_as_float(static_cast<uint32_t>(h0[(b * D + d + v) * L + j]) << 16) : 0.0f;
+}
+
+// One bf16 value of channel d+v, slot j, of a [B, D, W-1] state.
+__device__ __forceinline__ void store_state_bf16(uint16_t* st, int64_t b, int64_t D, int64_t d, int L, int j,
+                                                 float val) {
+    st[(b * D + d) * L + j] = static_cast<uint16_t>(pack_bf16x2(val, 0.0f) & 0xffffu);
+}
+
 // Where a wave works. The block id (XCD-remapped) selects a (strip group, segment group,
 // batch row); the wave's index selects its strip within the group (ws_i) and its segment
 // within the group (wt_i). All fields are wave-uniform except `d`, the lane's first channel.

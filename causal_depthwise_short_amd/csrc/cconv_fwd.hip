@@ -59,7 +59,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     float bs[VEC];
     load_bias<VEC>(a.bias, wt.d, bs);
 
-    // ring prologue: x[t0-1-k], zero before the sequence start
+    // ring prologue: x[t0-1-k]; before the sequence start, the history (or zeros). Only the
+    // first segment's wave reaches t < 0, and only it reads the history and writes the final
+    // state, so the two may share one buffer.
+    float hist[R][VEC];
+    const bool first = (t0 == 0);
+    if (first) load_history<VEC, W>(a.h0, wt.b, a.D, wt.d, hist);
     float ring[R][VEC];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
@@ -68,7 +73,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
             widen(load_row<VEC>(at(xb + t * xs, lo)), ring[k]);
         } else {
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) ring[k][v] = 0.0f;
+            for (int v = 0; v < VEC; ++v) ring[k][v] = (W > 1 && first) ? hist[R - 1 - k][v] : 0.0f;
         }
     }
 
@@ -104,6 +109,27 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     }
     for (; t < t1; ++t)
         store_row<VEC, NTS>(at(yb + t * ys, lo), fwd_row<VEC, W>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)), ring));
+
+    // final state: the last W-1 values of the extended sequence (history, then x)
+    if constexpr (W > 1) {
+        if (first && a.hT) {
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int64_t tt = a.T - R + j;
+                float v8[VEC];
+                if (tt >= 0) {
+                    widen(load_row<VEC>(at(xb + tt * xs, lo)), v8);
+                } else {  // T < W-1: part of the history survives (re-read: slot T+j > j is not written yet)
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v)
+                        v8[v] = a.h0 ? __uint_as_float(static_cast<uint32_t>(a.h0[(wt.b * a.D + wt.d + v) * R + (tt + R)]) << 16)
+                                     : 0.0f;
+                }
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) store_state_bf16(a.hT, wt.b, a.D, wt.d + v, R, j, v8[v]);
+            }
+        }
+    }
 }
 
 // A general kernel (blocks of up to 8 waves) and a "solo" one for one-wave blocks run one wave

@@ -35,6 +35,8 @@ struct FwdArgs {
     int w_f32;
     const float* bias;
     uint16_t* y;
+    const uint16_t* h0;  // [B, D, W-1] history before t = 0, or null (zeros)
+    uint16_t* hT;        // [B, D, W-1] final state out, or null; may equal h0
     int64_t B, T, D;
     int64_t seg_rows, strip_groups, seg_groups;
     int ws;
@@ -49,7 +51,9 @@ struct BwdArgs {
     int w_f32;
     const float* bias;
     uint16_t* dx;
-    float* partial;  // [partials, W+1, D]
+    float* partial;      // [partials, W+1, D]
+    const uint16_t* h0;  // [B, D, W-1] history before t = 0, or null (zeros)
+    uint16_t* dh0;       // [B, D, W-1] gradient of the history out, or null
     int64_t B, T, D;
     int64_t seg_rows, strip_groups, seg_groups;
     int ws;

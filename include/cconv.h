@@ -107,6 +107,31 @@ cconv_status_t cconv_bwd(const void* x, int64_t x_sb, int64_t x_st, const void* 
                          int64_t T, int64_t D, int W, cconv_stream_t stream);
 
 /*
+ * Forward and backward with a history before t = 0: the prefill <-> decode state handoff
+ * (fla's initial_state and output_final_state parameters, in the kernel-fun wheel's
+ * _common/compat.py FLA_KWARGS table; the decode PR's description names a direct
+ * full-sequence-to-decode state handoff as the next step). States use the decode layout:
+ * bf16 [B, D, W-1] contiguous, oldest first, 16-byte aligned; for W == 1 they hold nothing
+ * and are ignored.
+ *   init_state   history of each sequence before t = 0 (NULL = zeros, i.e. cconv_fwd/bwd).
+ *   final_state  out: the last W-1 values of the extended sequence (history, then x) -- the
+ *                state a cconv_update continues from. May be init_state's own buffer (an
+ *                in-place advance); must not overlap anything else. Needs T >= 1.
+ *   d_init_state out (backward): the gradient of each history value (dx at the W-1 rows before
+ *                t = 0), bf16; NULL when not wanted. Needs T >= 1.
+ * The backward's dw includes the history's products; dx is unchanged in meaning.
+ */
+cconv_status_t cconv_fwd_state(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
+                               const float* bias, const void* init_state, void* final_state, void* y, int64_t B,
+                               int64_t T, int64_t D, int W, cconv_stream_t stream);
+
+cconv_status_t cconv_bwd_state(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
+                               int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias,
+                               const void* init_state, void* dx, void* dw, cconv_dtype_t dw_dtype, float* dbias,
+                               void* d_init_state, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                               int64_t D, int W, cconv_stream_t stream);
+
+/*
  * The backward's two stages, for callers that want the fp32 partials themselves (a
  * data-parallel caller can sum them across ranks before the final cast) or that time the
  * stages apart. cconv_bwd_main writes dx and fills the workspace with fp32 dw/dbias partial

@@ -7,7 +7,7 @@ inputs from it without sharing any of the computation.
 Recipe (the same for every workload):
   * a CPU ``torch.Generator`` seeded per workload;
   * tensors drawn in a fixed order (training: x, w, bias, dy; decode: x, state, slot
-    permutation, w, bias);
+    permutation, w, bias); a training history (state before t = 0) from a second generator;
   * every draw is fp32 ``N(0, var)`` scaled by ``sqrt(var)`` and, where the tensor is bf16,
     rounded to bf16 by torch's round-to-nearest-even cast. The bf16 bits that result are
     what both sides receive.
@@ -94,6 +94,14 @@ def train_inputs(
 
 def train_inputs_for(shape: TrainShape, **kw) -> dict:
     return train_inputs(shape.B, shape.T, shape.D, shape.W, bias=shape.bias, seed=shape.seed, **kw)
+
+
+def history_input(B: int, D: int, W: int, *, seed: int) -> torch.Tensor:
+    """A history before t = 0 for each sequence: bf16 [B, D, W-1] ~ N(0, 1), oldest first (the
+    decode state layout). Drawn from its own generator (seed + 1000) so that the training draws
+    of the same seed are unchanged."""
+    g = torch.Generator(device="cpu").manual_seed(seed + 1000)
+    return _normal(g, (B, D, W - 1), 1.0).to(torch.bfloat16)
 
 
 def decode_inputs(

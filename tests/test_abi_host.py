@@ -220,3 +220,66 @@ def test_default_configs_are_valid(which):
                         # so ALIAS (not BAD_CONFIG) means the plan was accepted, with nothing launched
                         st = cc.lib().cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, B, T, D, W, ctypes.byref(c), None)
                         assert st == ALIAS, (B, T, D, W, c, st)
+
+
+H0, HT, DH = (0x30_0000_0000 + i * 0x1_0000_0000 for i in range(3))
+
+
+def fwd_state(x=X, w=WT, bias=BIAS, h0=H0, hT=HT, y=Y, B=2, T=64, D=512, W=4):
+    return cc.lib().cconv_fwd_state(x, T * D, D, w, BF16, bias, h0, hT, y, B, T, D, W, None)
+
+
+def bwd_state(x=X, dy=DY, h0=H0, dx=DX, dw=DW, db=DB, dh=DH, ws=WSP, ws_bytes=1 << 40, B=2, T=64, D=512, W=4):
+    return cc.lib().cconv_bwd_state(x, T * D, D, dy, T * D, D, WT, BF16, BIAS, h0, dx, dw, BF16, db, dh, ws, ws_bytes,
+                                    B, T, D, W, None)
+
+
+STATE_BYTES = 2 * 512 * 3 * 2  # B * D * (W-1) bf16
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(x=None), NULLP),
+        (dict(h0=H0 + 2), MISAL),
+        (dict(hT=HT + 8), MISAL),
+        (dict(hT=X + 16), ALIAS),
+        (dict(hT=WT), ALIAS),
+        (dict(hT=BIAS), ALIAS),
+        (dict(hT=Y + 32), ALIAS),
+        (dict(h0=Y), ALIAS),
+        (dict(hT=H0 + 16), ALIAS),  # overlaps the history without being the same buffer
+        (dict(hT=H0 - STATE_BYTES + 16), ALIAS),
+        (dict(T=0), SHAPE),  # a final state needs at least one token
+        (dict(T=0, hT=H0), SHAPE),  # in place passes the aliasing check (fails later on T)
+        (dict(W=5), SHAPE),
+    ],
+)
+def test_fwd_state_host_errors(kw, code):
+    assert fwd_state(**kw) == code
+
+
+def test_fwd_state_empty_and_unused():
+    assert fwd_state(B=0) == OK and fwd_state(D=0) == OK
+    assert fwd_state(T=0, hT=None) == OK  # nothing to produce
+    # W = 1 holds no state: the state pointers are ignored, even misaligned ones
+    assert fwd_state(W=1, h0=H0 + 2, hT=HT + 2, T=0) == OK
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(dh=DH + 2), MISAL),
+        (dict(h0=H0 + 8), MISAL),
+        (dict(dh=X), ALIAS),
+        (dict(dh=H0 + 16), ALIAS),
+        (dict(dh=DX + 64), ALIAS),
+        (dict(dh=WSP), ALIAS),
+        (dict(dx=H0), ALIAS),
+        (dict(ws=H0), ALIAS),
+        (dict(T=0), SHAPE),
+        (dict(dh=None, ws_bytes=8), WS),
+    ],
+)
+def test_bwd_state_host_errors(kw, code):
+    assert bwd_state(**kw) == code
