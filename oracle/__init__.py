@@ -56,6 +56,8 @@ def _load(path: Path, prec: str):
     lib.oracle_dw_channels.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, i64, f, f, f]
     lib.oracle_fwd_state.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, f, f]
     lib.oracle_bwd_state.argtypes = [f, f, f, i64, i64, i64, f, ctypes.c_int, f, f, f, f, f]
+    lib.oracle_fwd_pool.argtypes = [f, i64, i64, i64, f, ctypes.c_int, f, f, i64, f, f, f]
+    lib.oracle_fwd_pool.restype = ctypes.c_int
     lib.oracle_update.argtypes = [f, i64, i64, f, i64, f, f, ctypes.c_int, f, f]
     lib.oracle_update.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [f, f, i64]
@@ -208,6 +210,33 @@ class Oracle:
         )
         return dx, dw, db, dh0
 
+    def fwd_pool(self, x, state, state_indices, has_initial_state, w, bias=None, *, precision: str = "f64"):
+        """Prefill x [B, T, D] into the decode pool state [S, D, W-1] (slot state_indices[b],
+        -1 = none; history read only where has_initial_state[b], None = nowhere).
+
+        Returns (ok, y unrounded or None, new_state float32). The input state is not modified.
+        """
+        xf, wf, bf = _f32(x), _f32(w), _f32(bias)
+        st = _f32(state).copy()
+        B, T, D = xf.shape
+        W = wf.shape[1]
+        S = st.shape[0]
+        assert st.shape == (S, D, W - 1)
+        idx = np.ascontiguousarray(np.asarray(state_indices, dtype=np.int32))
+        assert idx.shape == (B,)
+        hi = None
+        if has_initial_state is not None:
+            hi = np.ascontiguousarray(np.asarray(has_initial_state, dtype=np.uint8))
+            assert hi.shape == (B,)
+        y = np.empty((B, T, D), _NP[precision])
+        rc = self.lib(precision).oracle_fwd_pool(
+            _p(xf), B, T, D, _p(wf), W, _p(bf), _p(st), S, _p(idx), _p(hi), _p(y)
+        )
+        if rc != 0:
+            assert rc == 1, rc
+            return False, None, st
+        return True, y, st
+
     def update(self, x, state, state_indices, w, bias=None, *, precision: str = "f64"):
         """One decode step. Returns (ok, y [N, D], new_state float32 [S, D, W-1]).
 
@@ -266,6 +295,7 @@ fwd_points = _default.fwd_points
 dx_points = _default.dx_points
 dw_channels = _default.dw_channels
 update = _default.update
+fwd_pool = _default.fwd_pool
 fwd_state = _default.fwd_state
 bwd_state = _default.bwd_state
 round_bf16 = _default.round_bf16

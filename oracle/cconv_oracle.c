@@ -32,6 +32,9 @@
  *    output_final_state]: an optional h0 [B, D, W-1], oldest first (the decode state layout),
  *    replaces the zero history before t = 0; the final state is the last W-1 values of the
  *    extended sequence; the history's gradient is dx at the W-1 virtual rows before t = 0.
+ *  - Prefill into the decode pool. [PR #797 discussion: the follow-up's direct
+ *    full-sequence-to-decode state handoff]: the history and final state of sequence b live
+ *    in slot state_indices[b] of the decode state pool, under the decode slot rule.
  *  - Decode. [PR #797 description, API and semantics]: advance a per-slot state of the last
  *    W-1 inputs by one token; conv_state_indices picks the slot, -1 marks a padding row that
  *    mutates nothing; invalid indices fail closed. Readings: state is stored oldest first
@@ -47,6 +50,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -252,18 +256,48 @@ void oracle_bwd_state(const float* x, const float* h0, const float* dy, int64_t 
  * y_out: [N, D]. Returns 0 on success, 1 when the indices are invalid (then nothing is
  * written: neither state nor y). For W == 1 the state holds nothing and is not touched.
  */
+/* The decode API's slot rule: every index in [-1, S) and no non-negative slot named twice. */
+static int slots_valid(const int32_t* idx, int64_t N, int64_t S) {
+    for (int64_t n = 0; n < N; ++n)
+        if (idx[n] < -1 || idx[n] >= S) return 0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < n; ++m)
+            if (idx[n] >= 0 && idx[n] == idx[m]) return 0;
+    return 1;
+}
+
+/* Prefill straight into a decode state pool [S, D, W-1]: sequence b reads its history from
+ * slot idx[b] when has_init[b] is set (zeros otherwise, and always for idx[b] = -1), and its
+ * final state replaces that slot (idx[b] = -1: nothing written). The slot rule is the decode
+ * one; a call that breaks it writes nothing (neither y nor state) and returns 1. */
+int oracle_fwd_pool(const float* x, int64_t B, int64_t T, int64_t D, const float* w, int W, const float* bias,
+                    float* state, int64_t S, const int32_t* idx, const uint8_t* has_init, real* y_out) {
+    const int64_t L = W - 1;
+    if (!slots_valid(idx, B, S)) return 1;
+    float* h0 = (float*)calloc((size_t)(B * D * (L > 0 ? L : 1)), sizeof(float));
+    float* hT = (float*)calloc((size_t)(B * D * (L > 0 ? L : 1)), sizeof(float));
+    if (!h0 || !hT) {
+        free(h0);
+        free(hT);
+        return 2;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        if (idx[b] >= 0 && has_init && has_init[b])
+            memcpy(h0 + b * D * L, state + (int64_t)idx[b] * D * L, (size_t)(D * L) * sizeof(float));
+    oracle_fwd_state(x, h0, B, T, D, w, W, bias, y_out, hT);
+    for (int64_t b = 0; b < B; ++b)
+        if (idx[b] >= 0) memcpy(state + (int64_t)idx[b] * D * L, hT + b * D * L, (size_t)(D * L) * sizeof(float));
+    free(h0);
+    free(hT);
+    return 0;
+}
+
 int oracle_update(const float* x, int64_t N, int64_t D, float* state, int64_t S,
                   const int32_t* idx, const float* w, int W, const float* bias, real* y_out) {
     const int64_t L = W - 1;
     /* Validity first, so that an invalid call writes nothing. */
     if (!idx && N > S) return 1;
-    if (idx) {
-        for (int64_t n = 0; n < N; ++n)
-            if (idx[n] < -1 || idx[n] >= S) return 1;
-        for (int64_t n = 0; n < N; ++n)
-            for (int64_t m = 0; m < n; ++m)
-                if (idx[n] >= 0 && idx[n] == idx[m]) return 1;
-    }
+    if (idx && !slots_valid(idx, N, S)) return 1;
     for (int64_t n = 0; n < N; ++n) {
         int64_t s = idx ? (int64_t)idx[n] : n;
         if (s < 0) {

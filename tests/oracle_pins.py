@@ -475,6 +475,76 @@ def check_prefill_then_decode(orc):
         assert np.array_equal(state, hT), f"final state after decode W={W}"
 
 
+def check_pool_matches_gathered_history(orc):
+    """Prefill into a decode pool is the forward with history gathered from the slots (zeros
+    for -1 or has_initial_state = 0), with each final state scattered back to its slot; slots
+    no sequence names are untouched."""
+    for W in (2, 3, 4):
+        B, T, D, S = 4, 9, 5, 7
+        x, w, b, _ = _problem(300 + W, B, T, D, W)
+        rng = np.random.default_rng(310 + W)
+        state = _bf16_values(rng, (S, D, W - 1))
+        idx = np.array([5, -1, 0, 3], np.int32)
+        for has in (np.array([1, 1, 0, 1], np.uint8), None):
+            ok, y, st = orc.fwd_pool(x, state, idx, has, w, b)
+            assert ok
+            h0 = np.zeros((B, D, W - 1), np.float32)
+            for i in range(B):
+                if idx[i] >= 0 and has is not None and has[i]:
+                    h0[i] = state[idx[i]]
+            yr, hT = orc.fwd_state(x, h0, w, b)
+            assert np.array_equal(y, yr), f"pool y W={W}"
+            for i in range(B):
+                if idx[i] >= 0:
+                    assert np.array_equal(st[idx[i]], hT[i]), f"slot {idx[i]} W={W}"
+            for sl in (1, 2, 4, 6):
+                assert np.array_equal(st[sl], state[sl]), f"slot {sl} touched W={W}"
+            # by hand: a sequence's final state is its last W-1 inputs (T >= W-1 here)
+            assert np.array_equal(st[5], x[0, T - (W - 1):].T), f"slot 5 by hand W={W}"
+
+
+def check_pool_prefill_then_decode(orc):
+    """Chunked prefill through the pool (second chunk with has_initial_state) and then decode
+    from the pool reproduce the plain forward of the whole sequence bitwise (in the oracle)."""
+    for W in (2, 4):
+        B, T, D, S = 3, 14, 6, 5
+        x, w, b, _ = _problem(320 + W, B, T, D, W)
+        rng = np.random.default_rng(330 + W)
+        state = _bf16_values(rng, (S, D, W - 1))  # stale contents: must be ignored at first
+        idx = np.array([4, 0, 2], np.int32)
+        _, y = orc.fwd(x, w, b)
+        ok, y1, st = orc.fwd_pool(x[:, :5], state, idx, np.zeros(B, np.uint8), w, b)
+        assert ok and np.array_equal(y1, y[:, :5]), f"first chunk W={W}"
+        ok, y2, st = orc.fwd_pool(x[:, 5:11], st, idx, np.ones(B, np.uint8), w, b)
+        assert ok and np.array_equal(y2, y[:, 5:11]), f"second chunk W={W}"
+        xs = np.zeros((S, D), np.float32)
+        for t in range(11, T):
+            xs = x[:, t]
+            ok, yt, st = orc.update(xs, st, idx, w, b)
+            assert ok and np.array_equal(yt, y[:, t]), f"decode t={t} W={W}"
+        assert np.array_equal(st[1], state[1]) and np.array_equal(st[3], state[3])
+
+
+def check_pool_index_validation(orc):
+    """The pool follows the decode slot rule: the same verdict as the decode update for the
+    same index arrays, and a rejected call changes nothing."""
+    B, T, D, S, W = 4, 3, 2, 6, 3
+    x, w, b, _ = _problem(340, B, T, D, W)
+    rng = np.random.default_rng(341)
+    state = _bf16_values(rng, (S, D, W - 1))
+    xd = _bf16_values(rng, (B, D))
+    cases = ([0, 1, -2, 3], [0, 1, 6, 3], [0, 5, 2, 5], [7, 0, 1, 2], [-1, -3, 0, 1],
+             [-1, -1, 5, 0], [5, 4, 3, 2], [0, 1, 2, -1])
+    expect = (False, False, False, False, False, True, True, True)
+    for case, want in zip(cases, expect):
+        idx = np.array(case, np.int32)
+        ok, y, st = orc.fwd_pool(x, state, idx, np.ones(B, np.uint8), w, b)
+        okd, _, _ = orc.update(xd, state, idx, w, b)
+        assert ok == want == okd, f"{case}: pool {ok}, decode {okd}, expected {want}"
+        if not ok:
+            assert y is None and np.array_equal(st, state), f"rejected {case} changed the state"
+
+
 ALL_CHECKS = [
     check_rounding_matches_torch,
     check_rounding_from_double_is_direct,
@@ -496,4 +566,7 @@ ALL_CHECKS = [
     check_history_chunking,
     check_history_zero_is_plain,
     check_prefill_then_decode,
+    check_pool_matches_gathered_history,
+    check_pool_prefill_then_decode,
+    check_pool_index_validation,
 ]

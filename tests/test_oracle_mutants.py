@@ -30,8 +30,11 @@ MUTANTS = [
     ("decode_taps_reversed", "(real)w[d * W + j] * (real)st[j]", "(real)w[d * W + (L - 1 - j)] * (real)st[j]"),
     ("decode_new_token_tap", "(real)w[d * W + (W - 1)] * (real)x[n * D + d]", "(real)w[d * W + 0] * (real)x[n * D + d]"),
     ("decode_shift_direction", "for (int64_t j = 0; j + 1 < L; ++j) st[j] = st[j + 1];\n            if (L > 0) st[L - 1] = x[n * D + d];", "for (int64_t j = L - 1; j > 0; --j) st[j] = st[j - 1];\n            if (L > 0) st[0] = x[n * D + d];"),
-    ("decode_no_duplicate_check", "if (idx[n] >= 0 && idx[n] == idx[m]) return 1;", "(void)m;"),
-    ("decode_range_off_by_one", "idx[n] >= S) return 1;", "idx[n] > S) return 1;"),
+    ("slot_no_duplicate_check", "if (idx[n] >= 0 && idx[n] == idx[m]) return 0;", "(void)m;"),
+    ("slot_range_off_by_one", "idx[n] >= S) return 0;", "idx[n] > S) return 0;"),
+    ("pool_ignores_has_init", "if (idx[b] >= 0 && has_init && has_init[b])", "if (idx[b] >= 0)"),
+    ("pool_final_state_dropped", "if (idx[b] >= 0) memcpy(state + (int64_t)idx[b] * D * L", "if (0) memcpy(state + (int64_t)idx[b] * D * L"),
+    ("pool_slot_by_batch_row", "memcpy(state + (int64_t)idx[b] * D * L, hT", "memcpy(state + b * D * L, hT"),
     ("decode_padding_output", "y_out[n * D + d] = 0;", "y_out[n * D + d] = (real)x[n * D + d];"),
     ("history_reversed", "h0[(b * D + d) * (W - 1) + (t + W - 1)]", "h0[(b * D + d) * (W - 1) + (-1 - t)]"),
     ("history_ignored", "if (h0 && t >= -(int64_t)(W - 1))", "if (0)"),
