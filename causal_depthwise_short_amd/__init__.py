@@ -25,6 +25,7 @@ __all__ = [
     "cconv_bwd",
     "cconv_fwd_state",
     "cconv_bwd_state",
+    "cconv_fwd_pool",
     "cconv_bwd_workspace_bytes",
     "cconv_bwd_main",
     "cconv_bwd_finish",
@@ -106,6 +107,8 @@ def _declare(L):
     L.cconv_bwd_config.restype = i32
     L.cconv_fwd_state.argtypes = [p, i64, i64, p, i32, p, p, p, p, i64, i64, i64, i32, p]
     L.cconv_fwd_state.restype = i32
+    L.cconv_fwd_pool.argtypes = [p, i64, i64, p, i32, p, p, i64, p, p, p, p, i64, i64, i64, i32, p]
+    L.cconv_fwd_pool.restype = i32
     L.cconv_bwd_state.argtypes = [p, i64, i64, p, i64, i64, p, i32, p, p, p, p, i32, p, p, p, sz, i64, i64, i64,
                                   i32, p]
     L.cconv_bwd_state.restype = i32
@@ -336,6 +339,53 @@ def cconv_fwd_state(x, w, bias=None, init_state=None, *, final_state=None, want_
         "cconv_fwd_state",
     )
     return y, final_state
+
+
+def cconv_fwd_pool(x, w, bias, state, state_indices, has_initial_state=None, *, y=None, status=None, stream=None):
+    """Prefill x [B, T, D] into the decode pool ``state`` [S, D, W-1] (updated in place);
+    returns (y, status).
+
+    state_indices: int32 [B] (slot of sequence b, -1 = padding); has_initial_state: bool or
+    uint8 [B] or None (start every sequence from zeros). status (allocated if None) receives
+    0 on the device, or 8 (CCONV_ERR_INDEX) when the indices break the decode slot rule, in
+    which case neither y nor state was written.
+    """
+    sb, st = _act(x, "x")
+    B, T, D = x.shape
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    _dev(state, "state")
+    if state.dtype != torch.bfloat16 or state.dim() != 3 or state.shape[1:] != (D, W - 1) or not state.is_contiguous():
+        raise ValueError("state must be a contiguous bf16 [S, D, W-1] tensor")
+    S = state.shape[0]
+    _dev(state_indices, "state_indices")
+    if state_indices.dtype != torch.int32 or state_indices.shape != (B,) or not state_indices.is_contiguous():
+        raise ValueError("state_indices must be a contiguous int32 [B] tensor")
+    if has_initial_state is not None:
+        _dev(has_initial_state, "has_initial_state")
+        if has_initial_state.dtype not in (torch.bool, torch.uint8) or has_initial_state.shape != (B,) \
+                or not has_initial_state.is_contiguous():
+            raise ValueError("has_initial_state must be a contiguous bool or uint8 [B] tensor")
+    if y is None:
+        y = torch.empty((B, T, D), dtype=torch.bfloat16, device=x.device)
+    elif y.dtype != torch.bfloat16 or tuple(y.shape) != (B, T, D) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous bf16 [B, T, D] tensor")
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=x.device)
+    _check(
+        lib().cconv_fwd_pool(
+            _ptr(x), sb, st, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(state), S, _ptr(state_indices),
+            _ptr(has_initial_state), _ptr(status), _ptr(y), B, T, D, W, _stream(stream),
+        ),
+        "cconv_fwd_pool",
+    )
+    return y, status
 
 
 def cconv_bwd_state(x, dy, w, bias=None, init_state=None, *, dx=None, dw=None, dbias=None, d_init_state=None,

@@ -132,10 +132,18 @@ size_t bwd_workspace(const Plan& p, int64_t D, int W) {
     return static_cast<size_t>(p.partials) * static_cast<size_t>(W + 1) * static_cast<size_t>(D) * sizeof(float);
 }
 
+// The decode pool a forward reads histories from and writes final states to (cconv_fwd_pool).
+struct Pool {
+    int64_t S;
+    const int32_t* sidx;
+    const uint8_t* has_init;
+    int32_t* status;
+};
+
 cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
                         const float* bias, void* y, int64_t B, int64_t T, int64_t D, int W,
                         const cconv_config_t* cfg, cconv_stream_t stream, const void* h0 = nullptr,
-                        void* hT = nullptr) {
+                        void* hT = nullptr, const Pool* pool = nullptr) {
     // a pointer may be NULL only when its tensor is empty
     const bool act_empty = (B == 0 || T == 0 || D == 0);
     if ((!x && !act_empty) || (!w && D > 0) || (!y && !act_empty)) return CCONV_ERR_NULL_POINTER;
@@ -154,14 +162,27 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     // buffer (advancing a cache in place) but must not overlap anything else
     if (W == 1) h0 = hT = nullptr;
     if (!aligned(h0, 16) || !aligned(hT, 16)) return CCONV_ERR_MISALIGNED;
-    const __int128 state_bytes = static_cast<__int128>(B) * D * (W - 1) * 2;
+    const __int128 state_bytes = static_cast<__int128>(pool ? pool->S : B) * D * (W - 1) * 2;
     const Span sh0 = span(h0, state_bytes), shT = span(hT, state_bytes);
     if (overlap(sh0, sy) || overlap(shT, sy) || overlap(shT, sx) || overlap(shT, sw) || overlap(shT, sb) ||
         (hT != h0 && overlap(shT, sh0)))
         return CCONV_ERR_ALIASING;
+    if (pool) {  // the slot indices and flags are inputs, the status word an output
+        const Span si = span(pool->sidx, static_cast<__int128>(B) * 4);
+        const Span sf = span(pool->has_init, B);
+        const Span ss = span(pool->status, 4);
+        const Span all[8] = {sx, sw, sb, sy, shT, sh0, si, sf};
+        for (const Span& o : all)
+            if (overlap(ss, o)) return CCONV_ERR_ALIASING;
+        if (overlap(sy, si) || overlap(sy, sf) || overlap(shT, si) || overlap(shT, sf)) return CCONV_ERR_ALIASING;
+    }
     Plan p;
     if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
     if (hT && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;  // a final state needs at least one token
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    // pool mode: the slot check always runs, so the status word is written by every call
+    if (pool && cconv::launch_slots(pool->sidx, B, pool->S, pool->status, hs) != hipSuccess)
+        return CCONV_ERR_LAUNCH;
     if (B == 0 || T == 0 || D == 0) return CCONV_OK;
     cconv::FwdArgs a;
     a.x = static_cast<const uint16_t*>(x);
@@ -173,6 +194,9 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     a.y = static_cast<uint16_t*>(y);
     a.h0 = static_cast<const uint16_t*>(h0);
     a.hT = static_cast<uint16_t*>(hT);
+    a.sidx = pool ? pool->sidx : nullptr;
+    a.has_init = pool ? pool->has_init : nullptr;
+    a.status = pool ? pool->status : nullptr;
     a.B = B;
     a.T = T;
     a.D = D;
@@ -180,8 +204,7 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     a.strip_groups = p.strip_groups;
     a.seg_groups = p.seg_groups;
     a.ws = p.ws;
-    return cconv::launch_fwd(p, W, a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? CCONV_OK
-                                                                                           : CCONV_ERR_LAUNCH;
+    return cconv::launch_fwd(p, W, a, hs) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
 }
 
 // Stages of the backward: kMain computes dx and the fp32 partials in the workspace, kFinish
@@ -300,6 +323,19 @@ cconv_status_t cconv_fwd_state(const void* x, int64_t x_sb, int64_t x_st, const 
                                const float* bias, const void* init_state, void* final_state, void* y, int64_t B,
                                int64_t T, int64_t D, int W, cconv_stream_t stream) {
     return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream, init_state, final_state);
+}
+
+cconv_status_t cconv_fwd_pool(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
+                              const float* bias, void* state, int64_t S, const int32_t* state_indices,
+                              const uint8_t* has_initial_state, int32_t* status, void* y, int64_t B, int64_t T,
+                              int64_t D, int W, cconv_stream_t stream) {
+    if (!status || (!state_indices && B > 0)) return CCONV_ERR_NULL_POINTER;
+    if (W >= 2 && W <= 4 && !state && S > 0 && D > 0) return CCONV_ERR_NULL_POINTER;
+    if (S < 0 || S > kMaxIndexedSlots || B > kMaxDecodeRows) return CCONV_ERR_BAD_SHAPE;
+    if (!aligned(status, 4) || !aligned(state_indices, 4)) return CCONV_ERR_MISALIGNED;
+    const Pool pool{S, state_indices, has_initial_state, status};
+    return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream, has_initial_state ? state : nullptr,
+                    state, &pool);
 }
 
 cconv_status_t cconv_bwd_state(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,

@@ -213,6 +213,27 @@ __device__ __forceinline__ void store_state_bf16(uint16_t* st, int64_t b, int64_
     st[(b * D + d) * L + j] = static_cast<uint16_t>(pack_bf16x2(val, 0.0f) & 0xffffu);
 }
 
+// The decode slot rule, checked by one block: true (in every thread of the block) when some
+// idx[n] lies outside [-1, S) or a non-negative slot appears twice. `seen` is an LDS bit set of
+// (S + 31) / 32 words. O(N + S/32) per block, no device trap.
+__device__ __forceinline__ bool block_slots_bad(const int32_t* idx, int64_t N, int64_t S, uint32_t* seen) {
+    const int64_t words = (S + 31) / 32;
+    for (int64_t i = threadIdx.x; i < words; i += blockDim.x) seen[i] = 0u;
+    __syncthreads();
+    bool bad = false;
+    for (int64_t i = threadIdx.x; i < N; i += blockDim.x) {
+        const int32_t v = idx[i];
+        if (v < -1 || static_cast<int64_t>(v) >= S) {
+            bad = true;
+        } else if (v >= 0) {
+            const uint32_t bit = 1u << (v & 31);
+            const uint32_t old = atomicOr(&seen[v >> 5], bit);
+            if (old & bit) bad = true;
+        }
+    }
+    return __syncthreads_or(bad);
+}
+
 // Where a wave works. The block id (XCD-remapped) selects a (strip group, segment group,
 // batch row); the wave's index selects its strip within the group (ws_i) and its segment
 // within the group (wt_i). All fields are wave-uniform except `d`, the lane's first channel.

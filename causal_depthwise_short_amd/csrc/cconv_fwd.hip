@@ -46,6 +46,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     const int64_t t0 = wt.t0, t1 = wt.t1;
     if (t0 >= a.T) return;    // a trailing wave of the last segment group
     if (wt.d >= a.D) return;  // lanes past the last channel (D is a multiple of VEC)
+    if (a.status && *a.status != 0) return;  // pool mode: the slot check failed, write nothing
 
     // Row bases are wave-uniform (scalar registers); a lane adds its 32-bit channel offset,
     // so a row load is one global_load with a scalar base and no per-row VALU address math.
@@ -64,7 +65,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     // state, so the two may share one buffer.
     float hist[R][VEC];
     const bool first = (t0 == 0);
-    if (first) load_history<VEC, W>(a.h0, wt.b, a.D, wt.d, hist);
+    // the sequence's state row: its batch row, or in pool mode its slot (-1: none)
+    int64_t hrow = wt.b;
+    const uint16_t* h0 = a.h0;
+    if (a.sidx && first) {
+        hrow = a.sidx[wt.b];
+        if (hrow < 0 || !(a.has_init && a.has_init[wt.b])) h0 = nullptr;
+    }
+    if (first) load_history<VEC, W>(h0, hrow, a.D, wt.d, hist);
     float ring[R][VEC];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
@@ -112,7 +120,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 
     // final state: the last W-1 values of the extended sequence (history, then x)
     if constexpr (W > 1) {
-        if (first && a.hT) {
+        if (first && a.hT && hrow >= 0) {
 #pragma unroll
             for (int j = 0; j < R; ++j) {
                 const int64_t tt = a.T - R + j;
@@ -122,11 +130,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
                 } else {  // T < W-1: part of the history survives (re-read: slot T+j > j is not written yet)
 #pragma unroll
                     for (int v = 0; v < VEC; ++v)
-                        v8[v] = a.h0 ? __uint_as_float(static_cast<uint32_t>(a.h0[(wt.b * a.D + wt.d + v) * R + (tt + R)]) << 16)
-                                     : 0.0f;
+                        v8[v] = h0 ? __uint_as_float(static_cast<uint32_t>(h0[(hrow * a.D + wt.d + v) * R + (tt + R)]) << 16)
+                                   : 0.0f;
                 }
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) store_state_bf16(a.hT, wt.b, a.D, wt.d + v, R, j, v8[v]);
+                for (int v = 0; v < VEC; ++v) store_state_bf16(a.hT, hrow, a.D, wt.d + v, R, j, v8[v]);
             }
         }
     }

@@ -37,6 +37,13 @@ struct FwdArgs {
     uint16_t* y;
     const uint16_t* h0;  // [B, D, W-1] history before t = 0, or null (zeros)
     uint16_t* hT;        // [B, D, W-1] final state out, or null; may equal h0
+    // Pool mode (sidx non-null): h0 and hT are a decode pool [S, D, W-1] and sequence b uses
+    // slot sidx[b] (-1: zero history, no final state); its history is read only where
+    // has_init[b] is set (null: nowhere). Every wave first reads *status, the verdict of the
+    // slot check, and writes nothing unless it is CCONV_OK.
+    const int32_t* sidx;
+    const uint8_t* has_init;
+    const int32_t* status;
     int64_t B, T, D;
     int64_t seg_rows, strip_groups, seg_groups;
     int ws;
@@ -90,6 +97,7 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_update(int W, const UpdateArgs& a, int block_threads, int64_t grid_x,
                          int64_t grid_y, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_status(int32_t* status, int32_t value, hipStream_t stream);
+hipError_t launch_slots(const int32_t* idx, int64_t N, int64_t S, int32_t* status, hipStream_t stream);
 
 // Which (vec, group) pairs are compiled.
 bool fwd_variant_exists(int vec, int group);

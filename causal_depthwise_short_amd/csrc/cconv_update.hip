@@ -26,23 +26,7 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
     constexpr int L = W - 1;  // state length
     extern __shared__ uint32_t seen[];
 
-    bool bad = false;
-    if (a.idx) {
-        const int64_t words = (a.S + 31) / 32;
-        for (int64_t i = threadIdx.x; i < words; i += blockDim.x) seen[i] = 0u;
-        __syncthreads();
-        for (int64_t i = threadIdx.x; i < a.N; i += blockDim.x) {
-            const int32_t v = a.idx[i];
-            if (v < -1 || static_cast<int64_t>(v) >= a.S) {
-                bad = true;
-            } else if (v >= 0) {
-                const uint32_t bit = 1u << (v & 31);
-                const uint32_t old = atomicOr(&seen[v >> 5], bit);
-                if (old & bit) bad = true;
-            }
-        }
-        bad = __syncthreads_or(bad);
-    }
+    const bool bad = a.idx ? block_slots_bad(a.idx, a.N, a.S, seen) : false;
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && a.status)
         a.status[0] = bad ? CCONV_ERR_INDEX : CCONV_OK;
     if (bad) return;
@@ -116,6 +100,15 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
     }
 }
 
+// The slot check alone, for the prefill into a pool: one block writes the verdict, which the
+// forward's waves read before they write anything.
+__global__ __launch_bounds__(1024) void cconv_slots_kernel(const int32_t* idx, int64_t N, int64_t S,
+                                                           int32_t* status) {
+    extern __shared__ uint32_t seen[];
+    const bool bad = block_slots_bad(idx, N, S, seen);
+    if (threadIdx.x == 0) status[0] = bad ? CCONV_ERR_INDEX : CCONV_OK;
+}
+
 __global__ void cconv_status_kernel(int32_t* status, int32_t value) {
     if (threadIdx.x == 0 && blockIdx.x == 0) status[0] = value;
 }
@@ -130,6 +123,12 @@ hipError_t launch_update(int W, const UpdateArgs& a, int block_threads, int64_t 
         case 4: hipLaunchKernelGGL(cconv_update_kernel<4>, grid, block, lds, s, a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_slots(const int32_t* idx, int64_t N, int64_t S, int32_t* status, hipStream_t s) {
+    const size_t lds = static_cast<size_t>((S + 31) / 32) * 4;
+    hipLaunchKernelGGL(cconv_slots_kernel, dim3(1), dim3(1024), lds, s, idx, N, S, status);
     return hipGetLastError();
 }
 

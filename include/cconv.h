@@ -132,6 +132,30 @@ cconv_status_t cconv_bwd_state(const void* x, int64_t x_sb, int64_t x_st, const 
                                int64_t D, int W, cconv_stream_t stream);
 
 /*
+ * Prefill straight into the decode state pool: the forward of B sequences whose histories
+ * and final states live in slots of the pool cconv_update advances (the follow-up scope in
+ * the decode PR's discussion: a direct full-sequence-to-decode state handoff).
+ *   state              bf16 [S, D, W-1] pool, the cconv_update layout (16-byte aligned); read
+ *                      and written in place. May be NULL when it holds no element.
+ *   state_indices      int32 [B] on the device: sequence b uses slot state_indices[b]; -1 marks
+ *                      a padding sequence (zero history, y computed, no slot written). The
+ *                      decode slot rule applies: every index in [-1, S), no slot named twice.
+ *   has_initial_state  uint8 [B] on the device or NULL (= all zero): sequence b starts from the
+ *                      history in its slot when nonzero, from zeros otherwise.
+ *   status             int32 on the device, required: receives CCONV_OK, or CCONV_ERR_INDEX
+ *                      when the slot rule fails -- then nothing else is written (neither y nor
+ *                      any slot). Written by every call that returns CCONV_OK.
+ * After the call, slot state_indices[b] holds the last W-1 values of history-then-x of
+ * sequence b (as cconv_fwd_state's final state). x, w, bias, y as in cconv_fwd. Limits:
+ * S <= 2^19, B <= 2^24; T >= 1 when B > 0 and W > 1. W == 1: no state; the slot rule is still
+ * checked.
+ */
+cconv_status_t cconv_fwd_pool(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
+                              const float* bias, void* state, int64_t S, const int32_t* state_indices,
+                              const uint8_t* has_initial_state, int32_t* status, void* y, int64_t B, int64_t T,
+                              int64_t D, int W, cconv_stream_t stream);
+
+/*
  * The backward's two stages, for callers that want the fp32 partials themselves (a
  * data-parallel caller can sum them across ranks before the final cast) or that time the
  * stages apart. cconv_bwd_main writes dx and fills the workspace with fp32 dw/dbias partial

@@ -283,3 +283,46 @@ def test_fwd_state_empty_and_unused():
 )
 def test_bwd_state_host_errors(kw, code):
     assert bwd_state(**kw) == code
+
+
+POOL, PIDX, PFLAG, PST = (0x40_0000_0000 + i * 0x1_0000_0000 for i in range(4))
+
+
+def fwd_pool(x=X, state=POOL, S=64, idx=PIDX, flags=PFLAG, status=PST, y=Y, B=2, T=64, D=512, W=4):
+    return cc.lib().cconv_fwd_pool(x, T * D, D, WT, BF16, BIAS, state, S, idx, flags, status, y, B, T, D, W, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(status=None), NULLP),
+        (dict(idx=None), NULLP),
+        (dict(state=None), NULLP),
+        (dict(S=-1), SHAPE),
+        (dict(S=(1 << 19) + 1), SHAPE),
+        (dict(B=(1 << 24) + 1, T=1), SHAPE),
+        (dict(T=0), SHAPE),
+        (dict(status=PST + 2), MISAL),
+        (dict(idx=PIDX + 2), MISAL),
+        (dict(state=POOL + 8), MISAL),
+        (dict(state=X), ALIAS),
+        (dict(state=Y + 64), ALIAS),
+        (dict(status=X + 16), ALIAS),
+        (dict(status=POOL + 64), ALIAS),
+        (dict(status=PIDX), ALIAS),
+        (dict(status=PFLAG + 1 - 1), ALIAS),
+        (dict(idx=Y), ALIAS),
+        (dict(flags=POOL + 32), ALIAS),
+        (dict(y=PIDX - 64), ALIAS),
+    ],
+)
+def test_fwd_pool_host_errors(kw, code):
+    assert fwd_pool(**kw) == code
+
+
+def test_fwd_pool_null_state_allowed_when_empty():
+    """The pool may be NULL when it holds nothing (S = 0 or W = 1): validation goes on past the
+    NULL check (here to the misaligned y, so nothing is launched)."""
+    assert fwd_pool(state=None) == NULLP
+    assert fwd_pool(state=None, S=0, y=Y + 8) == MISAL
+    assert fwd_pool(state=None, W=1, y=Y + 8) == MISAL
