@@ -56,6 +56,10 @@ def _load(path: Path, prec: str):
     lib.oracle_dw_channels.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, i64, f, f, f]
     lib.oracle_fwd_state.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, f, f]
     lib.oracle_bwd_state.argtypes = [f, f, f, i64, i64, i64, f, ctypes.c_int, f, f, f, f, f]
+    lib.oracle_fwd_varlen.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, f, f, f]
+    lib.oracle_fwd_varlen.restype = ctypes.c_int
+    lib.oracle_bwd_varlen.argtypes = [f, f, f, i64, i64, i64, f, ctypes.c_int, f, f, f, f, f, f]
+    lib.oracle_bwd_varlen.restype = ctypes.c_int
     lib.oracle_fwd_pool.argtypes = [f, i64, i64, i64, f, ctypes.c_int, f, f, i64, f, f, f]
     lib.oracle_fwd_pool.restype = ctypes.c_int
     lib.oracle_update.argtypes = [f, i64, i64, f, i64, f, f, ctypes.c_int, f, f]
@@ -210,6 +214,44 @@ class Oracle:
         )
         return dx, dw, db, dh0
 
+    def fwd_varlen(self, x, cu_seqlens, w, bias=None, h0=None, *, precision: str = "f64"):
+        """Packed batch: x [total, D], cu_seqlens [n+1]; h0 [n, D, W-1] or None. Returns
+        (ok, y unrounded [total, D] or None, hT float32 [n, D, W-1] or None)."""
+        xf, wf, bf, hf = _f32(x), _f32(w), _f32(bias), _f32(h0)
+        total, D = xf.shape
+        W = wf.shape[1]
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        n = cu.shape[0] - 1
+        assert n >= 0 and (hf is None or hf.shape == (n, D, W - 1))
+        y = np.empty((total, D), _NP[precision])
+        hT = np.empty((n, D, W - 1), np.float32)
+        rc = self.lib(precision).oracle_fwd_varlen(_p(xf), _p(cu), n, total, D, _p(wf), W, _p(bf), _p(hf), _p(y), _p(hT))
+        if rc != 0:
+            assert rc == 1, rc
+            return False, None, None
+        return True, y, hT
+
+    def bwd_varlen(self, x, dy, cu_seqlens, w, bias=None, h0=None, *, precision: str = "f64"):
+        """Backward of the packed batch. Returns (ok, dx, dw, dbias, dh0) (None values when the
+        offsets are rejected)."""
+        xf, dyf, wf, bf, hf = _f32(x), _f32(dy), _f32(w), _f32(bias), _f32(h0)
+        total, D = xf.shape
+        W = wf.shape[1]
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        n = cu.shape[0] - 1
+        assert dyf.shape == xf.shape and (hf is None or hf.shape == (n, D, W - 1))
+        dx = np.empty((total, D), _NP[precision])
+        dw = np.empty((D, W), _NP[precision])
+        db = np.empty((D,), _NP[precision])
+        dh0 = np.empty((n, D, W - 1), _NP[precision])
+        rc = self.lib(precision).oracle_bwd_varlen(
+            _p(xf), _p(dyf), _p(cu), n, total, D, _p(wf), W, _p(bf), _p(hf), _p(dx), _p(dw), _p(db), _p(dh0)
+        )
+        if rc != 0:
+            assert rc == 1, rc
+            return False, None, None, None, None
+        return True, dx, dw, db, dh0
+
     def fwd_pool(self, x, state, state_indices, has_initial_state, w, bias=None, *, precision: str = "f64"):
         """Prefill x [B, T, D] into the decode pool state [S, D, W-1] (slot state_indices[b],
         -1 = none; history read only where has_initial_state[b], None = nowhere).
@@ -296,6 +338,8 @@ dx_points = _default.dx_points
 dw_channels = _default.dw_channels
 update = _default.update
 fwd_pool = _default.fwd_pool
+fwd_varlen = _default.fwd_varlen
+bwd_varlen = _default.bwd_varlen
 fwd_state = _default.fwd_state
 bwd_state = _default.bwd_state
 round_bf16 = _default.round_bf16

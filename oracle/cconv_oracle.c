@@ -32,6 +32,10 @@
  *    output_final_state]: an optional h0 [B, D, W-1], oldest first (the decode state layout),
  *    replaces the zero history before t = 0; the final state is the last W-1 values of the
  *    extended sequence; the history's gradient is dx at the W-1 virtual rows before t = 0.
+ *  - Packed batches. [kernel-fun wheel, _common/compat.py: fla's cu_seqlens]: sequences of
+ *    different lengths packed along time; offsets cu[0] = 0 <= cu[1] <= ... <= cu[n] = total
+ *    mark sequence i as rows cu[i] .. cu[i+1]-1; every sequence has its own zero (or given)
+ *    history and nothing crosses a boundary.
  *  - Prefill into the decode pool. [PR #797 discussion: the follow-up's direct
  *    full-sequence-to-decode state handoff]: the history and final state of sequence b live
  *    in slot state_indices[b] of the decode state pool, under the decode slot rule.
@@ -256,6 +260,61 @@ void oracle_bwd_state(const float* x, const float* h0, const float* dy, int64_t 
  * y_out: [N, D]. Returns 0 on success, 1 when the indices are invalid (then nothing is
  * written: neither state nor y). For W == 1 the state holds nothing and is not touched.
  */
+/* The packed-batch rule: offsets start at 0, never decrease and end at the row count. */
+static int offsets_valid(const int32_t* cu, int64_t n, int64_t total) {
+    if (cu[0] != 0 || (int64_t)cu[n] != total) return 0;
+    for (int64_t i = 0; i < n; ++i)
+        if (cu[i] > cu[i + 1]) return 0;
+    return 1;
+}
+
+/* A packed batch: sequence i is rows cu[i] .. cu[i+1]-1 of x [total, D], with its own history
+ * h0[i] (h0 NULL: zeros) and final state hT[i] (NULL: not wanted), both [n, D, W-1]. Each
+ * sequence is the forward of a [1, len, D] batch on its own; nothing crosses a boundary. An
+ * empty sequence's final state is its history. Offsets that break the rule: returns 1 and
+ * writes nothing. */
+int oracle_fwd_varlen(const float* x, const int32_t* cu, int64_t n, int64_t total, int64_t D, const float* w,
+                      int W, const float* bias, const float* h0, real* y_out, float* hT_out) {
+    const int64_t L = W - 1;
+    if (!offsets_valid(cu, n, total)) return 1;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t a = cu[i], len = (int64_t)cu[i + 1] - cu[i];
+        oracle_fwd_state(x + a * D, h0 ? h0 + i * D * L : NULL, 1, len, D, w, W, bias, y_out + a * D,
+                         hT_out ? hT_out + i * D * L : NULL);
+    }
+    return 0;
+}
+
+/* Backward of the packed batch: dx and the history gradient per sequence, dw and dbias summed
+ * over the sequences in order. Same offset rule and return value as the forward. */
+int oracle_bwd_varlen(const float* x, const float* dy, const int32_t* cu, int64_t n, int64_t total, int64_t D,
+                      const float* w, int W, const float* bias, const float* h0, real* dx_out, real* dw_out,
+                      real* dbias_out, real* dh0_out) {
+    const int64_t L = W - 1;
+    if (!offsets_valid(cu, n, total)) return 1;
+    real* dwi = (real*)calloc((size_t)(D * W), sizeof(real));
+    real* dbi = (real*)calloc((size_t)(D > 0 ? D : 1), sizeof(real));
+    if (!dwi || !dbi) {
+        free(dwi);
+        free(dbi);
+        return 2;
+    }
+    for (int64_t e = 0; e < D * W; ++e) dw_out[e] = 0;
+    if (dbias_out)
+        for (int64_t d = 0; d < D; ++d) dbias_out[d] = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t a = cu[i], len = (int64_t)cu[i + 1] - cu[i];
+        oracle_bwd_state(x + a * D, h0 ? h0 + i * D * L : NULL, dy + a * D, 1, len, D, w, W, bias, dx_out + a * D,
+                         dwi, dbi, dh0_out ? dh0_out + i * D * L : NULL);
+        for (int64_t e = 0; e < D * W; ++e) dw_out[e] = dw_out[e] + dwi[e];
+        if (dbias_out)
+            for (int64_t d = 0; d < D; ++d) dbias_out[d] = dbias_out[d] + dbi[d];
+    }
+    free(dwi);
+    free(dbi);
+    return 0;
+}
+
 /* The decode API's slot rule: every index in [-1, S) and no non-negative slot named twice. */
 static int slots_valid(const int32_t* idx, int64_t N, int64_t S) {
     for (int64_t n = 0; n < N; ++n)

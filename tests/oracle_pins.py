@@ -545,6 +545,101 @@ def check_pool_index_validation(orc):
             assert y is None and np.array_equal(st, state), f"rejected {case} changed the state"
 
 
+def _varlen_problem(seed, lens, D, W, bias=True):
+    rng = np.random.default_rng(seed)
+    total = int(sum(lens))
+    x = _bf16_values(rng, (total, D))
+    dy = _bf16_values(rng, (total, D))
+    w = _bf16_values(rng, (D, W), 1.0 / math.sqrt(W))
+    b = _bf16_values(rng, (D,), 0.3) if bias else None
+    h0 = _bf16_values(rng, (len(lens), D, W - 1))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return x, dy, w, b, h0, cu
+
+
+def check_varlen_torch(orc):
+    """Each packed sequence against float64 torch conv1d over [its history; its rows], SiLU and
+    autograd: y, final state, dx, history gradient; dw and dbias summed over the sequences.
+    Lengths include 0, 1, 2 and lengths around W."""
+    for W in (1, 2, 4):
+        lens = [5, 0, 1, 2, 3, 9, 4, 0]
+        x, dy, w, b, h0, cu = _varlen_problem(400 + W, lens, 6, W)
+        D = x.shape[1]
+        ok, y, hT = orc.fwd_varlen(x, cu, w, b, h0)
+        ok2, dx, dw, db, dh0 = orc.bwd_varlen(x, dy, cu, w, b, h0)
+        assert ok and ok2
+        wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+        bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+        for i, L in enumerate(lens):
+            a = int(cu[i])
+            if L == 0:  # nothing to convolve: the state passes through, no gradient reaches it
+                assert np.array_equal(hT[i], h0[i]) and not np.any(dh0[i]), f"empty seq {i} W={W}"
+                continue
+            xe = torch.cat([torch.tensor(h0[i], dtype=torch.float64).T, torch.tensor(x[a:a + L], dtype=torch.float64)], 0)
+            xe.requires_grad_(True)
+            z = F.conv1d(xe.T[None], wt[:, None, :], bt, padding=0, groups=D)[0].T
+            yi = F.silu(z)
+            (yi * torch.tensor(dy[a:a + L], dtype=torch.float64)).sum().backward()
+            _close(y[a:a + L], yi.detach().numpy(), 1e-12, 1e-14, what=f"varlen y W={W} seq {i}")
+            assert np.array_equal(hT[i].astype(np.float64), xe.detach()[L:].T.numpy()), f"varlen hT W={W} seq {i}"
+            g = xe.grad.numpy()
+            _close(dx[a:a + L], g[W - 1:], 1e-12, 1e-13, what=f"varlen dx W={W} seq {i}")
+            _close(dh0[i], g[:W - 1].T, 1e-12, 1e-13, what=f"varlen dh0 W={W} seq {i}")
+        _close(dw, wt.grad.numpy(), 1e-12, 1e-12, what=f"varlen dw W={W}")
+        _close(db, bt.grad.numpy(), 1e-12, 1e-12, what=f"varlen dbias W={W}")
+
+
+def check_varlen_equal_lengths_is_batch(orc):
+    """Packing B sequences of equal length T is the [B, T, D] batch: y, dx and the states bit for
+    bit, dw and dbias up to the order of the sums."""
+    B, T, D, W = 3, 7, 5, 4
+    x, dy, w, b, h0, cu = _varlen_problem(420, [T] * B, D, W)
+    ok, y, hT = orc.fwd_varlen(x, cu, w, b, h0)
+    _, dx, dw, db, dh0 = orc.bwd_varlen(x, dy, cu, w, b, h0)
+    yb, hTb = orc.fwd_state(x.reshape(B, T, D), h0, w, b)
+    dxb, dwb, dbb, dh0b = orc.bwd_state(x.reshape(B, T, D), h0, dy.reshape(B, T, D), w, b)
+    assert ok and np.array_equal(y, yb.reshape(B * T, D)) and np.array_equal(hT, hTb)
+    assert np.array_equal(dx, dxb.reshape(B * T, D)) and np.array_equal(dh0, dh0b)
+    _close(dw, dwb, 1e-13, 1e-14, what="varlen vs batch dw")
+    _close(db, dbb, 1e-13, 1e-14, what="varlen vs batch dbias")
+
+
+def check_varlen_offsets_validation(orc):
+    """Offsets must start at 0, never decrease and end at the row count; otherwise nothing is
+    computed."""
+    x, dy, w, b, h0, _ = _varlen_problem(430, [4, 4], 3, 3)
+    for bad in ([1, 4, 8], [0, 5, 4, 8], [0, 4, 7], [0, 4, 9], [0, 9, 8]):
+        n = len(bad) - 1
+        hh = np.zeros((n, 3, 2), np.float32)
+        ok, y, hT = orc.fwd_varlen(x, np.array(bad, np.int32), w, b, hh)
+        ok2 = orc.bwd_varlen(x, dy, np.array(bad, np.int32), w, b, hh)[0]
+        assert not ok and not ok2 and y is None, f"offsets {bad} accepted"
+    for good in ([0, 8], [0, 0, 8], [0, 8, 8], [0, 3, 3, 8]):
+        n = len(good) - 1
+        assert orc.fwd_varlen(x, np.array(good, np.int32), w, b, np.zeros((n, 3, 2), np.float32))[0], good
+
+
+def check_varlen_sequences_independent(orc):
+    """A sequence's outputs do not depend on its neighbours' rows or histories; an empty
+    sequence's final state is its history and its history gradient is zero."""
+    lens = [6, 0, 5, 3]
+    x, dy, w, b, h0, cu = _varlen_problem(440, lens, 4, 4)
+    _, y, hT = orc.fwd_varlen(x, cu, w, b, h0)
+    _, dx, _, _, dh0 = orc.bwd_varlen(x, dy, cu, w, b, h0)
+    assert np.array_equal(hT[1], h0[1]) and not np.any(dh0[1]), "empty sequence"
+    x2, dy2, h02 = x.copy(), dy.copy(), h0.copy()
+    x2[:6] += 1.0
+    x2[11:] -= 0.5
+    dy2[:6] *= -1
+    h02[0] += 2.0
+    h02[3] -= 1.0
+    _, y2, hT2 = orc.fwd_varlen(x2, cu, w, b, h02)
+    _, dx2, _, _, dh02 = orc.bwd_varlen(x2, dy2, cu, w, b, h02)
+    assert np.array_equal(y2[6:11], y[6:11]) and np.array_equal(dx2[6:11], dx[6:11]), "sequence 2 moved"
+    assert np.array_equal(hT2[2], hT[2]) and np.array_equal(dh02[2], dh0[2])
+    assert not np.array_equal(y2[:6], y[:6]) and not np.array_equal(y2[11:], y[11:])
+
+
 ALL_CHECKS = [
     check_rounding_matches_torch,
     check_rounding_from_double_is_direct,
@@ -569,4 +664,8 @@ ALL_CHECKS = [
     check_pool_matches_gathered_history,
     check_pool_prefill_then_decode,
     check_pool_index_validation,
+    check_varlen_torch,
+    check_varlen_equal_lengths_is_batch,
+    check_varlen_offsets_validation,
+    check_varlen_sequences_independent,
 ]

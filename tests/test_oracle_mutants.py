@@ -40,6 +40,10 @@ MUTANTS = [
     ("history_ignored", "if (h0 && t >= -(int64_t)(W - 1))", "if (0)"),
     ("final_state_off_by_one", "xval(x, h0, T, D, W, b, T - (W - 1) + j, d)", "xval(x, h0, T, D, W, b, T - W + j, d)"),
     ("history_grad_shifted", "b, -(int64_t)(W - 1) + j, d)", "b, -(int64_t)(W - 1) + j + 1, d)"),
+    ("varlen_end_unchecked", "if (cu[0] != 0 || (int64_t)cu[n] != total) return 0;", "if (cu[0] != 0) return 0;"),
+    ("varlen_history_of_next", "oracle_fwd_state(x + a * D, h0 ? h0 + i * D * L : NULL", "oracle_fwd_state(x + a * D, h0 ? h0 + ((i + 1) % n) * D * L : NULL"),
+    ("varlen_rows_shifted", "oracle_fwd_state(x + a * D,", "oracle_fwd_state(x + (a > 0 ? a - 1 : 0) * D,"),
+    ("varlen_dw_last_only", "dw_out[e] = dw_out[e] + dwi[e];", "dw_out[e] = dwi[e];"),
     ("round_half_away", "nearbyint(a / q)", "floor(a / q + 0.5)"),
     ("round_truncate", "nearbyint(a / q)", "trunc(a / q)"),
 ]
