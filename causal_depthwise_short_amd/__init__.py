@@ -26,6 +26,8 @@ __all__ = [
     "cconv_fwd_state",
     "cconv_bwd_state",
     "cconv_fwd_pool",
+    "cconv_fwd_varlen",
+    "cconv_bwd_varlen",
     "cconv_bwd_workspace_bytes",
     "cconv_bwd_main",
     "cconv_bwd_finish",
@@ -109,6 +111,16 @@ def _declare(L):
     L.cconv_fwd_state.restype = i32
     L.cconv_fwd_pool.argtypes = [p, i64, i64, p, i32, p, p, i64, p, p, p, p, i64, i64, i64, i32, p]
     L.cconv_fwd_pool.restype = i32
+    L.cconv_fwd_varlen.argtypes = [p, i64, p, i64, i64, p, i32, p, p, p, p, p, i64, i32, p]
+    L.cconv_fwd_varlen.restype = i32
+    L.cconv_fwd_varlen_config.argtypes = [p, i64, p, i64, i64, p, i32, p, p, p, p, p, i64, i32,
+                                          ctypes.POINTER(Config), p]
+    L.cconv_fwd_varlen_config.restype = i32
+    bv = [p, i64, p, i64, p, i64, i64, p, i32, p, p, p, p, i32, p, p, p, sz, p, i64, i32]
+    L.cconv_bwd_varlen.argtypes = bv + [p]
+    L.cconv_bwd_varlen.restype = i32
+    L.cconv_bwd_varlen_config.argtypes = bv + [ctypes.POINTER(Config), p]
+    L.cconv_bwd_varlen_config.restype = i32
     L.cconv_bwd_state.argtypes = [p, i64, i64, p, i64, i64, p, i32, p, p, p, p, i32, p, p, p, sz, i64, i64, i64,
                                   i32, p]
     L.cconv_bwd_state.restype = i32
@@ -433,6 +445,102 @@ def cconv_bwd_state(x, dy, w, bias=None, init_state=None, *, dx=None, dw=None, d
         "cconv_bwd_state",
     )
     return dx, dw, dbias, d_init_state
+
+
+def _packed(t, name: str):
+    _dev(t, name)
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be bf16 [total, D] with unit channel stride")
+    return t.stride(0)
+
+
+def _offsets(cu_seqlens, W: int, D: int, init_state, dev):
+    _dev(cu_seqlens, "cu_seqlens")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 [nseq + 1] tensor")
+    n = cu_seqlens.numel() - 1
+    _state(init_state, "init_state", n, D, W)
+    return n
+
+
+def cconv_fwd_varlen(x, cu_seqlens, w, bias=None, init_state=None, *, final_state=None, want_final_state=False,
+                     y=None, status=None, config: Optional[Config] = None, stream=None):
+    """Packed batch forward: x bf16 [total, D]; cu_seqlens int32 [nseq+1] (device). Returns
+    (y, final_state or None, status): status receives 0, or 8 when the offsets are not a valid
+    partition of the rows (then nothing else was written)."""
+    xst = _packed(x, "x")
+    total, D = x.shape
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    n = _offsets(cu_seqlens, W, D, init_state, x.device)
+    if want_final_state and final_state is None:
+        final_state = torch.empty((n, D, W - 1), dtype=torch.bfloat16, device=x.device)
+    _state(final_state, "final_state", n, D, W)
+    if y is None:
+        y = torch.empty((total, D), dtype=torch.bfloat16, device=x.device)
+    elif y.dtype != torch.bfloat16 or tuple(y.shape) != (total, D) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous bf16 [total, D] tensor")
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=x.device)
+    args = (_ptr(x), xst, _ptr(cu_seqlens), n, total, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(init_state),
+            _ptr(final_state), _ptr(status), _ptr(y), D, W)
+    L = lib()
+    if config is None:
+        _check(L.cconv_fwd_varlen(*args, _stream(stream)), "cconv_fwd_varlen")
+    else:
+        _check(L.cconv_fwd_varlen_config(*args, ctypes.byref(config), _stream(stream)), "cconv_fwd_varlen_config")
+    return y, final_state, status
+
+
+def cconv_bwd_varlen(x, dy, cu_seqlens, w, bias=None, init_state=None, *, dx=None, dw=None, dbias=None,
+                     d_init_state=None, want_dbias: bool = True, want_d_init_state: bool = False, dw_dtype=None,
+                     workspace=None, status=None, config: Optional[Config] = None, stream=None):
+    """Packed batch backward. Returns (dx, dw, dbias, d_init_state, status)."""
+    xst = _packed(x, "x")
+    dyst = _packed(dy, "dy")
+    total, D = x.shape
+    if tuple(dy.shape) != (total, D):
+        raise ValueError("dy must have x's shape")
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    n = _offsets(cu_seqlens, W, D, init_state, x.device)
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    if dw is None:
+        dw = torch.empty((D, W), dtype=dw_dtype or w.dtype, device=dev)
+    if want_dbias and dbias is None:
+        dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    if want_d_init_state and d_init_state is None:
+        d_init_state = torch.empty((n, D, W - 1), dtype=torch.bfloat16, device=dev)
+    _state(d_init_state, "d_init_state", n, D, W)
+    need = cconv_bwd_workspace_bytes(1, total, D, W, config)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    args = (_ptr(x), xst, _ptr(dy), dyst, _ptr(cu_seqlens), n, total, _ptr(w), _wdt(w, "w"), _ptr(bias),
+            _ptr(init_state), _ptr(dx), _ptr(dw), _wdt(dw, "dw"), _ptr(dbias), _ptr(d_init_state), _ptr(workspace),
+            ws_bytes, _ptr(status), D, W)
+    L = lib()
+    if config is None:
+        _check(L.cconv_bwd_varlen(*args, _stream(stream)), "cconv_bwd_varlen")
+    else:
+        _check(L.cconv_bwd_varlen_config(*args, ctypes.byref(config), _stream(stream)), "cconv_bwd_varlen_config")
+    return dx, dw, dbias, d_init_state, status
 
 
 def cconv_bwd_main(x, dy, w, bias, dx, workspace, *, stream=None):

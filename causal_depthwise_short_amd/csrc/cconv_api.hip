@@ -19,6 +19,7 @@ constexpr int64_t kMaxDim = int64_t(1) << 40;        // any one size or stride
 constexpr int64_t kMaxDecodeRows = int64_t(1) << 24;  // N
 constexpr int64_t kMaxChannels = int64_t(1) << 30;    // D: lane channel offsets are 32-bit
 constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices (LDS bit set)
+constexpr int64_t kMaxSequences = int64_t(1) << 24;     // packed sequences per call
 constexpr int64_t kTargetWaves = 1024;  // one wave per SIMD (256 CUs x 4 SIMDs)
 // forward: non-temporal loads and stores, solo kernel; backward: the same plus prefetch
 constexpr int kFwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
@@ -132,18 +133,82 @@ size_t bwd_workspace(const Plan& p, int64_t D, int W) {
     return static_cast<size_t>(p.partials) * static_cast<size_t>(W + 1) * static_cast<size_t>(D) * sizeof(float);
 }
 
-// The decode pool a forward reads histories from and writes final states to (cconv_fwd_pool).
-struct Pool {
-    int64_t S;
-    const int32_t* sidx;
-    const uint8_t* has_init;
-    int32_t* status;
+// What a call adds to the plain forward or backward: a history and its output (the final
+// state, or the history's gradient), and the mode those live in.
+//   kPerSeq  one state row per batch row, [B, D, W-1] (the forward may advance it in place);
+//   kPool    rows of a decode pool [S, D, W-1], addressed by slot indices, under the slot rule;
+//   kPacked  one row per packed sequence, [nseq, D, W-1], sequences given by device offsets.
+// Pool and packed calls report through a device status word, written by every call that
+// returns CCONV_OK; the streaming kernels write nothing unless it reads CCONV_OK.
+enum Mode { kPerSeq, kPool, kPacked };
+struct Extra {
+    Mode mode = kPerSeq;
+    const void* h0 = nullptr;
+    void* out = nullptr;
+    int64_t rows = 0;                   // state rows for kPool (S) and kPacked (nseq)
+    const int32_t* sidx = nullptr;      // kPool
+    const uint8_t* has_init = nullptr;  // kPool
+    const int32_t* cu = nullptr;        // kPacked
+    int32_t* status = nullptr;          // kPool, kPacked
 };
+
+// Checks of the states and of the pool/packed metadata against the call's other operands.
+// `ins` and `outs` are the call's own tensors; returns CCONV_OK or the error.
+cconv_status_t check_extra(const Extra& ex, int64_t B, int64_t D, int W, bool fwd, const Span* ins, int n_in,
+                           const Span* outs, int n_out, Span* sh0_out) {
+    const void* h0 = ex.h0;
+    const void* out = ex.out;
+    if (!aligned(h0, 16) || !aligned(out, 16)) return CCONV_ERR_MISALIGNED;
+    const int64_t rows = ex.mode == kPerSeq ? B : ex.rows;
+    const __int128 state_bytes = static_cast<__int128>(rows) * D * (W - 1) * 2;
+    const Span sh0 = span(h0, state_bytes), so = span(out, state_bytes);
+    *sh0_out = sh0;
+    // the output state against every operand; in place only for a forward's per-sequence
+    // states or pool (the packed final state is written while other waves still read h0)
+    for (int i = 0; i < n_in; ++i)
+        if (overlap(so, ins[i])) return CCONV_ERR_ALIASING;
+    for (int i = 0; i < n_out; ++i)
+        if (overlap(so, outs[i]) || overlap(sh0, outs[i])) return CCONV_ERR_ALIASING;
+    const bool in_place_ok = fwd && ex.mode != kPacked && out == h0;
+    if (!in_place_ok && overlap(so, sh0)) return CCONV_ERR_ALIASING;
+    if (ex.mode == kPerSeq) return CCONV_OK;
+    if (!ex.status) return CCONV_ERR_NULL_POINTER;
+    if (!aligned(ex.status, 4) || !aligned(ex.sidx, 4) || !aligned(ex.cu, 4)) return CCONV_ERR_MISALIGNED;
+    const Span meta[3] = {span(ex.sidx, static_cast<__int128>(B) * 4), span(ex.has_init, B),
+                          span(ex.cu, ex.mode == kPacked ? static_cast<__int128>(ex.rows + 1) * 4 : 0)};
+    const Span ss = span(ex.status, 4);
+    for (int i = 0; i < n_in; ++i)
+        if (overlap(ss, ins[i])) return CCONV_ERR_ALIASING;
+    for (int i = 0; i < n_out; ++i)
+        if (overlap(ss, outs[i])) return CCONV_ERR_ALIASING;
+    if (overlap(ss, sh0) || overlap(ss, so)) return CCONV_ERR_ALIASING;
+    for (const Span& m : meta) {
+        if (overlap(ss, m) || overlap(so, m)) return CCONV_ERR_ALIASING;
+        for (int i = 0; i < n_out; ++i)
+            if (overlap(m, outs[i])) return CCONV_ERR_ALIASING;
+    }
+    return CCONV_OK;
+}
+
+// The first launches of a pool or packed call: the check that writes the status word, and for
+// packed batches the states of empty sequences.
+cconv_status_t launch_checks(const Extra& ex, int64_t B, int64_t T, int64_t D, int W, bool fwd, hipStream_t s) {
+    if (ex.mode == kPool && cconv::launch_slots(ex.sidx, B, ex.rows, ex.status, s) != hipSuccess)
+        return CCONV_ERR_LAUNCH;
+    if (ex.mode == kPacked) {
+        if (cconv::launch_offsets(ex.cu, ex.rows, T, ex.status, s) != hipSuccess) return CCONV_ERR_LAUNCH;
+        const uint16_t* h0 = static_cast<const uint16_t*>(ex.h0);
+        uint16_t* o = static_cast<uint16_t*>(ex.out);
+        if (cconv::launch_empty_seqs(ex.cu, ex.rows, h0, fwd ? o : nullptr, fwd ? nullptr : o, D, W - 1, ex.status,
+                                     s) != hipSuccess)
+            return CCONV_ERR_LAUNCH;
+    }
+    return CCONV_OK;
+}
 
 cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
                         const float* bias, void* y, int64_t B, int64_t T, int64_t D, int W,
-                        const cconv_config_t* cfg, cconv_stream_t stream, const void* h0 = nullptr,
-                        void* hT = nullptr, const Pool* pool = nullptr) {
+                        const cconv_config_t* cfg, cconv_stream_t stream, Extra ex = Extra{}) {
     // a pointer may be NULL only when its tensor is empty
     const bool act_empty = (B == 0 || T == 0 || D == 0);
     if ((!x && !act_empty) || (!w && D > 0) || (!y && !act_empty)) return CCONV_ERR_NULL_POINTER;
@@ -153,36 +218,23 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     if (!aligned(y, 16)) return CCONV_ERR_MISALIGNED;
     const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
+    if (ex.mode == kPacked && (c.options & ~cconv::kSolo) != cconv::kVarlenFwdOptions) return CCONV_ERR_BAD_CONFIG;
     const Span sy = span(y, extent3(B, T, D, T * D, D, 2));
     const Span sx = span(x, extent3(B, T, D, x_sb, x_st, 2));
     const Span sw = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
     const Span sb = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
     if (overlap(sy, sx) || overlap(sy, sw) || overlap(sy, sb)) return CCONV_ERR_ALIASING;
-    // history in, final state out: [B, D, W-1] bf16; the final state may be the history's own
-    // buffer (advancing a cache in place) but must not overlap anything else
-    if (W == 1) h0 = hT = nullptr;
-    if (!aligned(h0, 16) || !aligned(hT, 16)) return CCONV_ERR_MISALIGNED;
-    const __int128 state_bytes = static_cast<__int128>(pool ? pool->S : B) * D * (W - 1) * 2;
-    const Span sh0 = span(h0, state_bytes), shT = span(hT, state_bytes);
-    if (overlap(sh0, sy) || overlap(shT, sy) || overlap(shT, sx) || overlap(shT, sw) || overlap(shT, sb) ||
-        (hT != h0 && overlap(shT, sh0)))
-        return CCONV_ERR_ALIASING;
-    if (pool) {  // the slot indices and flags are inputs, the status word an output
-        const Span si = span(pool->sidx, static_cast<__int128>(B) * 4);
-        const Span sf = span(pool->has_init, B);
-        const Span ss = span(pool->status, 4);
-        const Span all[8] = {sx, sw, sb, sy, shT, sh0, si, sf};
-        for (const Span& o : all)
-            if (overlap(ss, o)) return CCONV_ERR_ALIASING;
-        if (overlap(sy, si) || overlap(sy, sf) || overlap(shT, si) || overlap(shT, sf)) return CCONV_ERR_ALIASING;
-    }
+    // history in, final state out (W == 1 has none)
+    if (W == 1) ex.h0 = ex.out = nullptr;
+    const Span ins[3] = {sx, sw, sb};
+    Span sh0;
+    if ((st = check_extra(ex, B, D, W, true, ins, 3, &sy, 1, &sh0)) != CCONV_OK) return st;
     Plan p;
     if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
-    if (hT && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;  // a final state needs at least one token
+    // a per-sequence or pool final state needs at least one token
+    if (ex.out && ex.mode != kPacked && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    // pool mode: the slot check always runs, so the status word is written by every call
-    if (pool && cconv::launch_slots(pool->sidx, B, pool->S, pool->status, hs) != hipSuccess)
-        return CCONV_ERR_LAUNCH;
+    if ((st = launch_checks(ex, B, T, D, W, true, hs)) != CCONV_OK) return st;
     if (B == 0 || T == 0 || D == 0) return CCONV_OK;
     cconv::FwdArgs a;
     a.x = static_cast<const uint16_t*>(x);
@@ -192,11 +244,13 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     a.w_f32 = (w_dtype == CCONV_F32);
     a.bias = bias;
     a.y = static_cast<uint16_t*>(y);
-    a.h0 = static_cast<const uint16_t*>(h0);
-    a.hT = static_cast<uint16_t*>(hT);
-    a.sidx = pool ? pool->sidx : nullptr;
-    a.has_init = pool ? pool->has_init : nullptr;
-    a.status = pool ? pool->status : nullptr;
+    a.h0 = static_cast<const uint16_t*>(ex.h0);
+    a.hT = static_cast<uint16_t*>(ex.out);
+    a.sidx = ex.sidx;
+    a.has_init = ex.has_init;
+    a.status = ex.status;
+    a.cu = ex.cu;
+    a.nseq = ex.mode == kPacked ? ex.rows : 0;
     a.B = B;
     a.T = T;
     a.D = D;
@@ -215,7 +269,7 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
                         int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
                         cconv_dtype_t dw_dtype, float* dbias, void* workspace, size_t workspace_bytes, int64_t B,
                         int64_t T, int64_t D, int W, const cconv_config_t* cfg, cconv_stream_t stream,
-                        const void* h0 = nullptr, void* dh0 = nullptr) {
+                        Extra ex = Extra{}) {
     const bool act_empty = (B == 0 || T == 0 || D == 0);
     const bool main = (stages & kMain) != 0, finish = (stages & kFinish) != 0;
     if (main && (((!x || !dy || !dx) && !act_empty) || (!w && D > 0))) return CCONV_ERR_NULL_POINTER;
@@ -241,6 +295,7 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     if (!aligned(dx, 16) || !aligned(dw, 16) || (dbias && !aligned(dbias, 16))) return CCONV_ERR_MISALIGNED;
     const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W);
     if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
+    if (ex.mode == kPacked && (c.options & ~cconv::kSolo) != cconv::kVarlenBwdOptions) return CCONV_ERR_BAD_CONFIG;
     Plan p;
     if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
     const size_t need = (B == 0 || T == 0 || D == 0) ? 0 : bwd_workspace(p, D, W);
@@ -254,24 +309,24 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     const Span o_dw = span(dw, static_cast<__int128>(D) * W * esize(dw_dtype));
     const Span o_db = dbias ? span(dbias, static_cast<__int128>(D) * 4) : Span{0, 0};
     const Span o_ws = span(workspace, need);
-    if (W == 1 || !main) h0 = dh0 = nullptr;
-    if (!aligned(h0, 16) || !aligned(dh0, 16)) return CCONV_ERR_MISALIGNED;
-    const __int128 state_bytes = static_cast<__int128>(B) * D * (W - 1) * 2;
-    const Span in_h = span(h0, state_bytes);
-    const Span o_dh = span(dh0, state_bytes);
-    const Span outs[5] = {o_dx, o_dw, o_db, o_ws, o_dh};
-    const Span ins[5] = {in_x, in_dy, in_w, in_b, in_h};
-    for (int i = 0; i < 5; ++i) {
-        for (int j = 0; j < 5; ++j)
+    if (W == 1 || !main) ex.h0 = ex.out = nullptr;
+    const Span outs[4] = {o_dx, o_dw, o_db, o_ws};
+    const Span ins[4] = {in_x, in_dy, in_w, in_b};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 4; ++j)
             if (overlap(outs[i], ins[j])) return CCONV_ERR_ALIASING;
-        for (int j = i + 1; j < 5; ++j)
+        for (int j = i + 1; j < 4; ++j)
             if (overlap(outs[i], outs[j])) return CCONV_ERR_ALIASING;
     }
+    Span sh0;
+    if ((st = check_extra(ex, B, D, W, false, ins, 4, outs, 4, &sh0)) != CCONV_OK) return st;
     if (workspace_bytes < need) return CCONV_ERR_WORKSPACE;
-    if (dh0 && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;  // a history gradient needs at least one token
+    // a per-sequence history gradient needs at least one token
+    if (ex.out && ex.mode != kPacked && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if ((st = launch_checks(ex, B, T, D, W, false, s)) != CCONV_OK) return st;
     if (D == 0) return CCONV_OK;
 
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool empty = (B == 0 || T == 0);
     if (main && !empty) {
         cconv::BwdArgs a;
@@ -286,8 +341,11 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
         a.bias = bias;
         a.dx = static_cast<uint16_t*>(dx);
         a.partial = static_cast<float*>(workspace);
-        a.h0 = static_cast<const uint16_t*>(h0);
-        a.dh0 = static_cast<uint16_t*>(dh0);
+        a.h0 = static_cast<const uint16_t*>(ex.h0);
+        a.dh0 = static_cast<uint16_t*>(ex.out);
+        a.cu = ex.cu;
+        a.nseq = ex.mode == kPacked ? ex.rows : 0;
+        a.status = ex.status;
         a.B = B;
         a.T = T;
         a.D = D;
@@ -306,7 +364,45 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     r.dw = dw;
     r.dw_f32 = (dw_dtype == CCONV_F32);
     r.dbias = dbias;
+    r.status = ex.status;
     return cconv::launch_reduce(r, s) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
+}
+
+// The packed entry points: B = 1 and T = total rows, with the offsets, states and status word
+// in the packed-mode descriptor.
+cconv_status_t packed_extra(const int32_t* cu_seqlens, int64_t nseq, int64_t total, const void* h0, void* out,
+                            int32_t* status, Extra* ex) {
+    if (!status || !cu_seqlens) return CCONV_ERR_NULL_POINTER;
+    if (nseq < 0 || nseq > kMaxSequences || total < 0 || total > INT32_MAX) return CCONV_ERR_BAD_SHAPE;
+    ex->mode = kPacked;
+    ex->h0 = h0;
+    ex->out = out;
+    ex->rows = nseq;
+    ex->cu = cu_seqlens;
+    ex->status = status;
+    return CCONV_OK;
+}
+
+cconv_status_t fwd_varlen_impl(const void* x, int64_t x_st, const int32_t* cu_seqlens, int64_t nseq, int64_t total,
+                               const void* w, cconv_dtype_t w_dtype, const float* bias, const void* init_state,
+                               void* final_state, int32_t* status, void* y, int64_t D, int W,
+                               const cconv_config_t* cfg, cconv_stream_t stream) {
+    Extra ex;
+    const cconv_status_t st = packed_extra(cu_seqlens, nseq, total, init_state, final_state, status, &ex);
+    if (st != CCONV_OK) return st;
+    return fwd_impl(x, 0, x_st, w, w_dtype, bias, y, 1, total, D, W, cfg, stream, ex);
+}
+
+cconv_status_t bwd_varlen_impl(const void* x, int64_t x_st, const void* dy, int64_t dy_st, const int32_t* cu_seqlens,
+                               int64_t nseq, int64_t total, const void* w, cconv_dtype_t w_dtype, const float* bias,
+                               const void* init_state, void* dx, void* dw, cconv_dtype_t dw_dtype, float* dbias,
+                               void* d_init_state, void* workspace, size_t workspace_bytes, int32_t* status,
+                               int64_t D, int W, const cconv_config_t* cfg, cconv_stream_t stream) {
+    Extra ex;
+    const cconv_status_t st = packed_extra(cu_seqlens, nseq, total, init_state, d_init_state, status, &ex);
+    if (st != CCONV_OK) return st;
+    return bwd_impl(kMain | kFinish, x, 0, x_st, dy, 0, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias, workspace,
+                    workspace_bytes, 1, total, D, W, cfg, stream, ex);
 }
 
 }  // namespace
@@ -322,7 +418,10 @@ cconv_status_t cconv_fwd(const void* x, int64_t x_sb, int64_t x_st, const void* 
 cconv_status_t cconv_fwd_state(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
                                const float* bias, const void* init_state, void* final_state, void* y, int64_t B,
                                int64_t T, int64_t D, int W, cconv_stream_t stream) {
-    return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream, init_state, final_state);
+    Extra ex;
+    ex.h0 = init_state;
+    ex.out = final_state;
+    return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream, ex);
 }
 
 cconv_status_t cconv_fwd_pool(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
@@ -332,10 +431,15 @@ cconv_status_t cconv_fwd_pool(const void* x, int64_t x_sb, int64_t x_st, const v
     if (!status || (!state_indices && B > 0)) return CCONV_ERR_NULL_POINTER;
     if (W >= 2 && W <= 4 && !state && S > 0 && D > 0) return CCONV_ERR_NULL_POINTER;
     if (S < 0 || S > kMaxIndexedSlots || B > kMaxDecodeRows) return CCONV_ERR_BAD_SHAPE;
-    if (!aligned(status, 4) || !aligned(state_indices, 4)) return CCONV_ERR_MISALIGNED;
-    const Pool pool{S, state_indices, has_initial_state, status};
-    return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream, has_initial_state ? state : nullptr,
-                    state, &pool);
+    Extra ex;
+    ex.mode = kPool;
+    ex.h0 = has_initial_state ? state : nullptr;
+    ex.out = state;
+    ex.rows = S;
+    ex.sidx = state_indices;
+    ex.has_init = has_initial_state;
+    ex.status = status;
+    return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream, ex);
 }
 
 cconv_status_t cconv_bwd_state(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
@@ -343,8 +447,48 @@ cconv_status_t cconv_bwd_state(const void* x, int64_t x_sb, int64_t x_st, const 
                                const void* init_state, void* dx, void* dw, cconv_dtype_t dw_dtype, float* dbias,
                                void* d_init_state, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
                                int64_t D, int W, cconv_stream_t stream) {
+    Extra ex;
+    ex.h0 = init_state;
+    ex.out = d_init_state;
     return bwd_impl(kMain | kFinish, x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias,
-                    workspace, workspace_bytes, B, T, D, W, nullptr, stream, init_state, d_init_state);
+                    workspace, workspace_bytes, B, T, D, W, nullptr, stream, ex);
+}
+
+cconv_status_t cconv_fwd_varlen(const void* x, int64_t x_st, const int32_t* cu_seqlens, int64_t nseq, int64_t total,
+                                const void* w, cconv_dtype_t w_dtype, const float* bias, const void* init_state,
+                                void* final_state, int32_t* status, void* y, int64_t D, int W,
+                                cconv_stream_t stream) {
+    return fwd_varlen_impl(x, x_st, cu_seqlens, nseq, total, w, w_dtype, bias, init_state, final_state, status, y, D,
+                           W, nullptr, stream);
+}
+
+cconv_status_t cconv_fwd_varlen_config(const void* x, int64_t x_st, const int32_t* cu_seqlens, int64_t nseq,
+                                       int64_t total, const void* w, cconv_dtype_t w_dtype, const float* bias,
+                                       const void* init_state, void* final_state, int32_t* status, void* y,
+                                       int64_t D, int W, const cconv_config_t* config, cconv_stream_t stream) {
+    if (!config) return CCONV_ERR_NULL_POINTER;
+    return fwd_varlen_impl(x, x_st, cu_seqlens, nseq, total, w, w_dtype, bias, init_state, final_state, status, y, D,
+                           W, config, stream);
+}
+
+cconv_status_t cconv_bwd_varlen(const void* x, int64_t x_st, const void* dy, int64_t dy_st, const int32_t* cu_seqlens,
+                                int64_t nseq, int64_t total, const void* w, cconv_dtype_t w_dtype, const float* bias,
+                                const void* init_state, void* dx, void* dw, cconv_dtype_t dw_dtype, float* dbias,
+                                void* d_init_state, void* workspace, size_t workspace_bytes, int32_t* status,
+                                int64_t D, int W, cconv_stream_t stream) {
+    return bwd_varlen_impl(x, x_st, dy, dy_st, cu_seqlens, nseq, total, w, w_dtype, bias, init_state, dx, dw, dw_dtype,
+                           dbias, d_init_state, workspace, workspace_bytes, status, D, W, nullptr, stream);
+}
+
+cconv_status_t cconv_bwd_varlen_config(const void* x, int64_t x_st, const void* dy, int64_t dy_st,
+                                       const int32_t* cu_seqlens, int64_t nseq, int64_t total, const void* w,
+                                       cconv_dtype_t w_dtype, const float* bias, const void* init_state, void* dx,
+                                       void* dw, cconv_dtype_t dw_dtype, float* dbias, void* d_init_state,
+                                       void* workspace, size_t workspace_bytes, int32_t* status, int64_t D, int W,
+                                       const cconv_config_t* config, cconv_stream_t stream) {
+    if (!config) return CCONV_ERR_NULL_POINTER;
+    return bwd_varlen_impl(x, x_st, dy, dy_st, cu_seqlens, nseq, total, w, w_dtype, bias, init_state, dx, dw, dw_dtype,
+                           dbias, d_init_state, workspace, workspace_bytes, status, D, W, config, stream);
 }
 
 cconv_status_t cconv_fwd_config(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
@@ -478,7 +622,7 @@ const char* cconv_status_string(cconv_status_t status) {
         case CCONV_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, indices and status 4)";
         case CCONV_ERR_ALIASING: return "an output overlaps an input or another output";
         case CCONV_ERR_WORKSPACE: return "workspace smaller than cconv_bwd_workspace_bytes()";
-        case CCONV_ERR_INDEX: return "state_indices out of [-1, S) or repeated";
+        case CCONV_ERR_INDEX: return "state_indices out of [-1, S) or repeated, or cu_seqlens not a valid partition";
         case CCONV_ERR_LAUNCH: return "kernel launch failed";
         case CCONV_ERR_BAD_CONFIG: return "invalid launch configuration";
     }

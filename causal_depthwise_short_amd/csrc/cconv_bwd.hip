@@ -84,7 +84,125 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
     }
 }
 
-template <int VEC, int G, int W, int F>
+// Where a run's dx rows go. Row u's dx is emitted when row u+W-1 is processed. Rows u >= own
+// are this wave's; with hg set (the wave holds the sequence's first row), the W-1 rows before
+// `start` give the history gradient of state row s instead.
+struct DxSink {
+    uint16_t* dxb;
+    int64_t dxs;
+    uint32_t lo;
+    int64_t own, start;
+    uint16_t* hg;
+    int64_t s, D, d;
+};
+
+// One row t of a run. GEN: the general emission rule (the first W-1 rows of a run, the tail
+// and the halo); otherwise row t-(W-1) is known to be this wave's own dx row.
+template <int VEC, int W, bool NTS, bool GEN>
+__device__ __forceinline__ void bwd_step(const float (&tap)[W][VEC], const float (&bs)[VEC], const Row<VEC>& rx,
+                                         const Row<VEC>& rdy, float (&xr)[W > 1 ? W - 1 : 1][VEC],
+                                         float (&gr)[W > 1 ? W - 1 : 1][VEC], float (&acc)[W][VEC], float (&db)[VEC],
+                                         const DxSink& k, int64_t t, bool acc_on) {
+    const int64_t u = t - (W - 1);
+    if constexpr (GEN) {
+        const bool emit = u >= k.own || (k.hg && u >= k.start - (W - 1));
+        bwd_row<VEC, W, NTS>(tap, bs, rx, rdy, xr, gr, acc, db, acc_on, emit, k.dxb + u * k.dxs, k.lo,
+                             u < k.start ? k.hg : nullptr, k.s, k.D, k.d, static_cast<int>(u - k.start + (W - 1)));
+    } else {
+        bwd_row<VEC, W, NTS>(tap, bs, rx, rdy, xr, gr, acc, db, acc_on, true, k.dxb + u * k.dxs, k.lo);
+    }
+}
+
+// Rows [t, e) of one sequence, t being the first row whose dx this wave owns in it (k.own).
+// Only the first G >= W-1 rows can emit a row before k.own, so the first group takes the
+// general rule and the steady loop none. With PF the next group's x and dy loads are in
+// flight while a group is computed (look-ahead clamped into [t, e)).
+template <int VEC, int G, int W, bool NTL, bool NTS, bool PF>
+__device__ __forceinline__ void bwd_run(const float (&tap)[W][VEC], const float (&bs)[VEC],
+                                        float (&xr)[W > 1 ? W - 1 : 1][VEC], float (&gr)[W > 1 ? W - 1 : 1][VEC],
+                                        float (&acc)[W][VEC], float (&db)[VEC], const uint16_t* __restrict__ xb,
+                                        int64_t xs, const uint16_t* __restrict__ dyb, int64_t dys, const DxSink& k,
+                                        int64_t t, const int64_t e) {
+    static_assert(G >= W - 1, "the first group must cover the rows that need the general rule");
+    const uint32_t lo = k.lo;
+    if constexpr (PF) {
+        if (t + G <= e) {
+            Row<VEC> cx[G], cdy[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) cx[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
+#pragma unroll
+            for (int g = 0; g < G; ++g) cdy[g] = load_row<VEC, NTL>(at(dyb + (t + g) * dys, lo));
+            bool head = true;
+            for (; t + G <= e; t += G) {
+                Row<VEC> nx[G], ndy[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) nx[g] = load_row<VEC, NTL>(at(xb + min(t + G + g, e - 1) * xs, lo));
+#pragma unroll
+                for (int g = 0; g < G; ++g) ndy[g] = load_row<VEC, NTL>(at(dyb + min(t + G + g, e - 1) * dys, lo));
+                if (head) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        bwd_step<VEC, W, NTS, true>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, k, t + g, true);
+                    head = false;
+                } else {
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        bwd_step<VEC, W, NTS, false>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, k, t + g, true);
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    cx[g] = nx[g];
+                    cdy[g] = ndy[g];
+                }
+            }
+        }
+    } else {
+        bool head = true;
+        for (; t + G <= e; t += G) {
+            Row<VEC> rx[G], rdy[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
+#pragma unroll
+            for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC, NTL>(at(dyb + (t + g) * dys, lo));
+            if (head) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    bwd_step<VEC, W, NTS, true>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, k, t + g, true);
+                head = false;
+            } else {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    bwd_step<VEC, W, NTS, false>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, k, t + g, true);
+            }
+        }
+    }
+    for (; t < e; ++t)
+        bwd_step<VEC, W, NTS, true>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)),
+                                    load_row<VEC, NTL>(at(dyb + t * dys, lo)), xr, gr, acc, db, k, t, true);
+}
+
+// The halo after a run ending at row e: rows e .. e+W-2 finish dx of the run's last W-1 rows.
+// Rows before the sequence end are read (the next segment's first rows: g only, no dw); rows
+// at or past it have g = 0 for this sequence.
+template <int VEC, int W, bool NTS>
+__device__ __forceinline__ void bwd_halo(const float (&tap)[W][VEC], const float (&bs)[VEC],
+                                         float (&xr)[W > 1 ? W - 1 : 1][VEC], float (&gr)[W > 1 ? W - 1 : 1][VEC],
+                                         float (&acc)[W][VEC], float (&db)[VEC], const uint16_t* __restrict__ xb,
+                                         int64_t xs, const uint16_t* __restrict__ dyb, int64_t dys, const DxSink& k,
+                                         int64_t e, int64_t end) {
+#pragma unroll
+    for (int h = 0; h < W - 1; ++h) {
+        const int64_t th = e + h;
+        Row<VEC> hx = zero_row<VEC>(), hdy = zero_row<VEC>();
+        if (th < end) {
+            hx = load_row<VEC>(at(xb + th * xs, k.lo));
+            hdy = load_row<VEC>(at(dyb + th * dys, k.lo));
+        }
+        bwd_step<VEC, W, NTS, true>(tap, bs, hx, hdy, xr, gr, acc, db, k, th, false);
+    }
+}
+
+template <int VEC, int G, int W, int F, bool VL>
 __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     constexpr int R = W > 1 ? W - 1 : 1;
     constexpr bool NTL = (F & kNtLoad) != 0, NTS = (F & kNtStore) != 0, PF = (F & kPrefetch) != 0;
@@ -94,6 +212,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
     const bool active = wt.d < a.D;
+    const bool valid = !(a.status && *a.status != 0);  // the offset check passed (or there is none)
     const uint32_t lo = static_cast<uint32_t>(wt.d) * 2u;  // byte offset of the lane's channels
 
     float acc[W][VEC], db[VEC];
@@ -104,105 +223,60 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         for (int k = 0; k < W; ++k) acc[k][v] = 0.0f;
     }
 
-    if (active && t0 < a.T) {
+    if (active && valid && t0 < a.T) {
         // wave-uniform row bases plus the lane's 32-bit channel offset
         const uint16_t* __restrict__ xb = a.x + wt.b * a.x_sb;
         const uint16_t* __restrict__ dyb = a.dy + wt.b * a.dy_sb;
-        uint16_t* __restrict__ dxb = a.dx + wt.b * a.T * a.D;
-        const int64_t xs = a.x_st, dys = a.dy_st, dxs = a.D;
+        const int64_t xs = a.x_st, dys = a.dy_st;
 
         float tap[W][VEC];
         load_taps<VEC, W>(a.w, a.w_f32, wt.d, tap);
         float bs[VEC];
         load_bias<VEC>(a.bias, wt.d, bs);
 
-        // ring prologue as in the forward; before t = 0, the history (or zeros)
-        const bool first = (t0 == 0);
-        float hist[R][VEC];
-        if (first) load_history<VEC, W>(a.h0, wt.b, a.D, wt.d, hist);
-        float xr[R][VEC], gr[R][VEC];
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const int64_t t = t0 - 1 - k;
-            if (W > 1 && t >= 0) {
-                widen(load_row<VEC>(at(xb + t * xs, lo)), xr[k]);
-            } else {
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) xr[k][v] = (W > 1 && first) ? hist[R - 1 - k][v] : 0.0f;
-            }
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) gr[k][v] = 0.0f;  // rows before t0 are not ours (history rows have g = 0)
+        // the sequence holding row t0: its rows [start, end) and its state row
+        int64_t s = wt.b, start = 0, end = a.T;
+        if constexpr (VL) {
+            s = seq_of(a.cu, a.nseq, t0);
+            start = a.cu[s];
+            end = a.cu[s + 1];
         }
-        // With a history gradient requested, the first segment also emits "dx" for the W-1
-        // rows before t = 0, into dh0; elsewhere rows before t0 belong to the previous segment.
-        uint16_t* const hg = (first && a.dh0) ? a.dh0 : nullptr;
+        // ring prologue as in the forward; the g ring starts at zero (rows before t0 are not
+        // this wave's, and history rows have no g)
+        float xr[R][VEC], gr[R][VEC];
+        ring_at<VEC, W>(xr, t0, start, xb, xs, lo, a.h0, s, a.D, wt.d);
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) gr[k][v] = 0.0f;
+        DxSink k{a.dx + wt.b * a.T * a.D, a.D, lo, t0, start, (t0 == start) ? a.dh0 : nullptr, s, a.D, wt.d};
 
         int64_t t = t0;
-        if constexpr (PF) {
-            // Software pipeline: the next group's x and dy loads are in flight while this
-            // group is computed. The look-ahead row is clamped into the segment.
-            if (t + G <= t1) {
-                Row<VEC> cx[G], cdy[G];
+        for (;;) {
+            const int64_t e = VL ? min(t1, end) : t1;
+            bwd_run<VEC, G, W, NTL, NTS, PF>(tap, bs, xr, gr, acc, db, xb, xs, dyb, dys, k, t, e);
+            bwd_halo<VEC, W, NTS>(tap, bs, xr, gr, acc, db, xb, xs, dyb, dys, k, e, end);
+            if constexpr (!VL) {
+                break;
+            } else {
+                if (e >= t1) break;
+                // the next non-empty sequence starts at row e: this wave holds its first row
+                do {
+                    ++s;
+                } while (a.cu[s + 1] <= e);
+                start = e;
+                end = a.cu[s + 1];
+                ring_at<VEC, W>(xr, e, start, xb, xs, lo, a.h0, s, a.D, wt.d);
 #pragma unroll
-                for (int g = 0; g < G; ++g) cx[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
+                for (int kk = 0; kk < R; ++kk)
 #pragma unroll
-                for (int g = 0; g < G; ++g) cdy[g] = load_row<VEC, NTL>(at(dyb + (t + g) * dys, lo));
-                for (; t + G <= t1; t += G) {
-                    Row<VEC> nx[G], ndy[G];
-#pragma unroll
-                    for (int g = 0; g < G; ++g) nx[g] = load_row<VEC, NTL>(at(xb + min(t + G + g, t1 - 1) * xs, lo));
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        ndy[g] = load_row<VEC, NTL>(at(dyb + min(t + G + g, t1 - 1) * dys, lo));
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const int64_t u = t + g - (W - 1);
-                        bwd_row<VEC, W, NTS>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, true, u >= t0 || (hg && u >= -R),
-                                             dxb + u * dxs, lo, u < 0 ? hg : nullptr, wt.b, a.D, wt.d,
-                                             static_cast<int>(u + R));
-                    }
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        cx[g] = nx[g];
-                        cdy[g] = ndy[g];
-                    }
-                }
+                    for (int v = 0; v < VEC; ++v) gr[kk][v] = 0.0f;
+                k.own = e;
+                k.start = e;
+                k.hg = a.dh0;
+                k.s = s;
+                t = e;
             }
-        } else {
-            for (; t + G <= t1; t += G) {
-                Row<VEC> rx[G], rdy[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
-#pragma unroll
-                for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC, NTL>(at(dyb + (t + g) * dys, lo));
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const int64_t u = t + g - (W - 1);
-                    bwd_row<VEC, W, NTS>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, true, u >= t0 || (hg && u >= -R),
-                                         dxb + u * dxs, lo, u < 0 ? hg : nullptr, wt.b, a.D, wt.d,
-                                         static_cast<int>(u + R));
-                }
-            }
-        }
-        for (; t < t1; ++t) {
-            const int64_t u = t - (W - 1);
-            bwd_row<VEC, W, NTS>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)), load_row<VEC, NTL>(at(dyb + t * dys, lo)),
-                                 xr, gr, acc, db, true, u >= t0 || (hg && u >= -R), dxb + u * dxs, lo,
-                                 u < 0 ? hg : nullptr, wt.b, a.D, wt.d, static_cast<int>(u + R));
-        }
-        // right halo: rows t1 .. t1+W-2 finish dx of this segment's last W-1 rows; rows at or
-        // past T have g = 0 (their x and dy read as zero).
-#pragma unroll
-        for (int h = 0; h < W - 1; ++h) {
-            const int64_t th = t1 + h;
-            const int64_t u = th - (W - 1);
-            Row<VEC> hx = zero_row<VEC>(), hdy = zero_row<VEC>();
-            if (th < a.T) {
-                hx = load_row<VEC>(at(xb + th * xs, lo));
-                hdy = load_row<VEC>(at(dyb + th * dys, lo));
-            }
-            bwd_row<VEC, W, NTS>(tap, bs, hx, hdy, xr, gr, acc, db, false, u >= t0 || (hg && u >= -R), dxb + u * dxs,
-                                 lo, u < 0 ? hg : nullptr, wt.b, a.D, wt.d, static_cast<int>(u + R));
         }
     }
 
@@ -217,7 +291,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         for (int v = 0; v < VEC; ++v)
             red[(wave * VEC + v) * kWave + lane] = (j < W) ? acc[W - 1 - j][v] : db[v];
         __syncthreads();
-        if (wt.wt_i == 0 && active) {
+        if (wt.wt_i == 0 && active && valid) {
             float s[VEC];
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
@@ -240,14 +314,14 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 // waves fit a SIMD), and a "solo" one for one-wave blocks run one wave per SIMD, which may use
 // the whole register file (256 VGPRs + 256 AGPRs): deeper row groups then fit without scratch
 // spills (the compiler parks values in AGPRs).
-template <int VEC, int G, int W, int F>
+template <int VEC, int G, int W, int F, bool VL>
 __global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
-    bwd_body<VEC, G, W, F>(a);
+    bwd_body<VEC, G, W, F, VL>(a);
 }
 
-template <int VEC, int G, int W, int F>
+template <int VEC, int G, int W, int F, bool VL>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void cconv_bwd_kernel_solo(const BwdArgs a) {
-    bwd_body<VEC, G, W, F>(a);
+    bwd_body<VEC, G, W, F, VL>(a);
 }
 
 // dw[d, j] = sum_p partial[p, j, d] (j < W), dbias[d] = sum_p partial[p, W, d]. A block
@@ -258,6 +332,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 __global__ __launch_bounds__(256) void cconv_dw_reduce_kernel(const ReduceArgs a) {
     constexpr int kBatch = 16;
     __shared__ float part[4][kWave];
+    if (a.status && *a.status != 0) return;  // the offset check failed: write nothing
     const int lane = threadIdx.x % kWave, q = threadIdx.x / kWave;
     const int64_t E = static_cast<int64_t>(a.W + 1) * a.D;
     const int64_t e = static_cast<int64_t>(blockIdx.x) * kWave + lane;
@@ -295,32 +370,40 @@ __global__ __launch_bounds__(256) void cconv_dw_reduce_kernel(const ReduceArgs a
 namespace {
 
 template <int VEC, int G, int W>
-hipError_t launch_bwd_f(int F, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_f(int F, bool vl, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
+#define CCONV_BWD_CASE(f, vl)                                                                              \
+    case f: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, W, f, vl>), grid, block, lds, s, a); break;        \
+    case f + kSolo: hipLaunchKernelGGL((cconv_bwd_kernel_solo<VEC, G, W, f, vl>), grid, block, lds, s, a); break;
+    if (vl) {  // packed batches: the streaming options only
+        switch (F) {
+            CCONV_BWD_CASE(kVarlenBwdOptions, true)
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (F) {
-#define CCONV_BWD_CASE(f)                                                                                \
-    case f: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, W, f>), grid, block, lds, s, a); break;         \
-    case f + kSolo: hipLaunchKernelGGL((cconv_bwd_kernel_solo<VEC, G, W, f>), grid, block, lds, s, a); break;
-        CCONV_BWD_CASE(0)
-        CCONV_BWD_CASE(1)
-        CCONV_BWD_CASE(2)
-        CCONV_BWD_CASE(3)
-        CCONV_BWD_CASE(4)
-        CCONV_BWD_CASE(5)
-        CCONV_BWD_CASE(6)
-        CCONV_BWD_CASE(7)
-#undef CCONV_BWD_CASE
+        CCONV_BWD_CASE(0, false)
+        CCONV_BWD_CASE(1, false)
+        CCONV_BWD_CASE(2, false)
+        CCONV_BWD_CASE(3, false)
+        CCONV_BWD_CASE(4, false)
+        CCONV_BWD_CASE(5, false)
+        CCONV_BWD_CASE(6, false)
+        CCONV_BWD_CASE(7, false)
         default: return hipErrorInvalidValue;
     }
+#undef CCONV_BWD_CASE
     return hipGetLastError();
 }
 
 template <int VEC, int G>
 hipError_t launch_bwd_w(int W, int F, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
+    const bool vl = a.cu != nullptr;
     switch (W) {
-        case 1: return launch_bwd_f<VEC, G, 1>(F, grid, block, lds, a, s);
-        case 2: return launch_bwd_f<VEC, G, 2>(F, grid, block, lds, a, s);
-        case 3: return launch_bwd_f<VEC, G, 3>(F, grid, block, lds, a, s);
-        case 4: return launch_bwd_f<VEC, G, 4>(F, grid, block, lds, a, s);
+        case 1: return launch_bwd_f<VEC, G, 1>(F, vl, grid, block, lds, a, s);
+        case 2: return launch_bwd_f<VEC, G, 2>(F, vl, grid, block, lds, a, s);
+        case 3: return launch_bwd_f<VEC, G, 3>(F, vl, grid, block, lds, a, s);
+        case 4: return launch_bwd_f<VEC, G, 4>(F, vl, grid, block, lds, a, s);
         default: return hipErrorInvalidValue;
     }
 }

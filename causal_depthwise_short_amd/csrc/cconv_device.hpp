@@ -89,6 +89,9 @@ constexpr int kNtLoad = 1;    // non-temporal loads of x (and dy)
 constexpr int kNtStore = 2;   // non-temporal stores of y (dx)
 constexpr int kPrefetch = 4;  // next group's loads issued before the current group's math
 constexpr int kSolo = 8;      // one-wave blocks, one wave per SIMD, whole register file (launch-time)
+// Packed batches are compiled for the streaming options only (with or without kSolo).
+constexpr int kVarlenFwdOptions = kNtLoad | kNtStore;
+constexpr int kVarlenBwdOptions = kNtLoad | kNtStore | kPrefetch;
 
 // The wave's index in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
@@ -194,17 +197,44 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t pid, int64_t n) {
     return xcd * q + (xcd < r ? xcd : r) + k;
 }
 
-// The history before t = 0 of VEC consecutive channels d.. of batch row b: hist[j][v] =
-// h0[b, d+v, j] (j = 0 is the oldest), from the [B, D, W-1] layout; zeros without h0.
+// The W-1 inputs before row t of a sequence whose first row is `start`, newest first:
+// ring[k] = X[t-1-k] for VEC consecutive channels d... Rows at or after `start` are read from
+// x; earlier ones come from the sequence's history, state row `hrow` of h0 ([rows, D, W-1],
+// slot row - start + W - 1, oldest first), or are zero without a history or before it.
 template <int VEC, int W>
-__device__ __forceinline__ void load_history(const uint16_t* h0, int64_t b, int64_t D, int64_t d,
-                                             float (&hist)[W > 1 ? W - 1 : 1][VEC]) {
-    constexpr int L = W - 1;
+__device__ __forceinline__ void ring_at(float (&ring)[W > 1 ? W - 1 : 1][VEC], int64_t t, int64_t start,
+                                        const uint16_t* __restrict__ xb, int64_t xs, uint32_t lo,
+                                        const uint16_t* h0, int64_t hrow, int64_t D, int64_t d) {
+    constexpr int R = W > 1 ? W - 1 : 1;
 #pragma unroll
-    for (int j = 0; j < (L > 0 ? L : 1); ++j)
+    for (int k = 0; k < R; ++k) {
+        const int64_t row = t - 1 - k;
+        if (W > 1 && row >= start) {
+            widen(load_row<VEC>(at(xb + row * xs, lo)), ring[k]);
+        } else {
+            const int64_t slot = row - start + R;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v)
-            hist[j][v] = (h0 && L > 0) ? __uint_as_float(static_cast<uint32_t>(h0[(b * D + d + v) * L + j]) << 16) : 0.0f;
+            for (int v = 0; v < VEC; ++v)
+                ring[k][v] = (W > 1 && h0 && slot >= 0)
+                                 ? __uint_as_float(static_cast<uint32_t>(h0[(hrow * D + d + v) * R + slot]) << 16)
+                                 : 0.0f;
+        }
+    }
+}
+
+// The sequence of a packed batch that holds row t: the largest s < n with cu[s] <= t, so empty
+// sequences are passed over (the offsets were checked first: cu[0] = 0 <= t < cu[n]).
+// Wave-uniform: a binary search on scalar loads.
+__device__ __forceinline__ int64_t seq_of(const int32_t* cu, int64_t n, int64_t t) {
+    int64_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
 }
 
 // One bf16 value of channel d+v, slot j, of a [B, D, W-1] state.

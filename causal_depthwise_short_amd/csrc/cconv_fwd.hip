@@ -38,7 +38,49 @@ __device__ __forceinline__ Row<VEC> fwd_row(const float (&tap)[W][VEC], const fl
     return narrow<VEC>(y);
 }
 
-template <int VEC, int G, int W, int F>
+// Rows [t, e) of one sequence: per row one coalesced load, the convolution over the ring,
+// SiLU, one store. Rows are loaded G at a time; with PF the next group's loads are in flight
+// while the current group is computed (the look-ahead row is clamped into [t, e), so the last
+// iteration re-reads valid rows instead of running past them).
+template <int VEC, int G, int W, bool NTL, bool NTS, bool PF>
+__device__ __forceinline__ void fwd_run(const float (&tap)[W][VEC], const float (&bs)[VEC],
+                                        float (&ring)[W > 1 ? W - 1 : 1][VEC], const uint16_t* __restrict__ xb,
+                                        int64_t xs, uint16_t* __restrict__ yb, int64_t ys, uint32_t lo, int64_t t,
+                                        const int64_t e) {
+    if constexpr (PF) {
+        if (t + G <= e) {
+            Row<VEC> cur[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) cur[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
+            for (; t + G <= e; t += G) {
+                Row<VEC> nxt[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) nxt[g] = load_row<VEC, NTL>(at(xb + min(t + G + g, e - 1) * xs, lo));
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), fwd_row<VEC, W>(tap, bs, cur[g], ring));
+#pragma unroll
+                for (int g = 0; g < G; ++g) cur[g] = nxt[g];
+            }
+        }
+    } else {
+        for (; t + G <= e; t += G) {
+            Row<VEC> raw[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) raw[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), fwd_row<VEC, W>(tap, bs, raw[g], ring));
+        }
+    }
+    for (; t < e; ++t)
+        store_row<VEC, NTS>(at(yb + t * ys, lo), fwd_row<VEC, W>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)), ring));
+}
+
+// One wave: a strip of 64*VEC channels over the rows [t0, t1) of its segment. A batch row is
+// one sequence. In a packed batch (VL) the segment may cross sequence boundaries: it is cut
+// into runs, and at each sequence start the ring restarts from that sequence's history.
+template <int VEC, int G, int W, int F, bool VL>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     constexpr int R = W > 1 ? W - 1 : 1;
     constexpr bool NTL = (F & kNtLoad) != 0, NTS = (F & kNtStore) != 0, PF = (F & kPrefetch) != 0;
@@ -46,7 +88,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     const int64_t t0 = wt.t0, t1 = wt.t1;
     if (t0 >= a.T) return;    // a trailing wave of the last segment group
     if (wt.d >= a.D) return;  // lanes past the last channel (D is a multiple of VEC)
-    if (a.status && *a.status != 0) return;  // pool mode: the slot check failed, write nothing
+    if (a.status && *a.status != 0) return;  // the slot or offset check failed: write nothing
 
     // Row bases are wave-uniform (scalar registers); a lane adds its 32-bit channel offset,
     // so a row load is one global_load with a scalar base and no per-row VALU address math.
@@ -60,66 +102,55 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     float bs[VEC];
     load_bias<VEC>(a.bias, wt.d, bs);
 
-    // ring prologue: x[t0-1-k]; before the sequence start, the history (or zeros). Only the
-    // first segment's wave reaches t < 0, and only it reads the history and writes the final
-    // state, so the two may share one buffer.
-    float hist[R][VEC];
-    const bool first = (t0 == 0);
-    // the sequence's state row: its batch row, or in pool mode its slot (-1: none)
-    int64_t hrow = wt.b;
+    // the sequence holding row t0: its rows [start, end) and its state row
+    int64_t s = wt.b, start = 0, end = a.T;
+    if constexpr (VL) {
+        s = seq_of(a.cu, a.nseq, t0);
+        start = a.cu[s];
+        end = a.cu[s + 1];
+    }
+    // Fixed-length batches: only the first segment's wave reaches rows before t = 0, and only
+    // it reads the history and writes the final state, so the two may share one buffer. In
+    // pool mode the state row is the sequence's slot (-1: none), its history used only where
+    // flagged.
+    const bool first = (t0 == start);
+    int64_t hrow = s;
     const uint16_t* h0 = a.h0;
-    if (a.sidx && first) {
+    if (!VL && a.sidx && first) {
         hrow = a.sidx[wt.b];
         if (hrow < 0 || !(a.has_init && a.has_init[wt.b])) h0 = nullptr;
     }
-    if (first) load_history<VEC, W>(h0, hrow, a.D, wt.d, hist);
     float ring[R][VEC];
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const int64_t t = t0 - 1 - k;
-        if (W > 1 && t >= 0) {
-            widen(load_row<VEC>(at(xb + t * xs, lo)), ring[k]);
-        } else {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) ring[k][v] = (W > 1 && first) ? hist[R - 1 - k][v] : 0.0f;
-        }
-    }
+    ring_at<VEC, W>(ring, t0, start, xb, xs, lo, h0, hrow, a.D, wt.d);
 
     int64_t t = t0;
-    if constexpr (PF) {
-        // Software pipeline: while a group is computed, the next group's loads are in flight.
-        // The look-ahead row index is clamped into the segment, so the last iteration re-reads
-        // valid rows instead of running past them.
-        if (t + G <= t1) {
-            Row<VEC> cur[G];
+    for (;;) {
+        const int64_t e = VL ? min(t1, end) : t1;
+        fwd_run<VEC, G, W, NTL, NTS, PF>(tap, bs, ring, xb, xs, yb, ys, lo, t, e);
+        if constexpr (!VL) {
+            break;
+        } else {
+            // the sequence ends in this wave: its final state is the ring
+            if (W > 1 && e == end && a.hT) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) cur[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
-            for (; t + G <= t1; t += G) {
-                Row<VEC> nxt[G];
+                for (int j = 0; j < R; ++j)
 #pragma unroll
-                for (int g = 0; g < G; ++g) nxt[g] = load_row<VEC, NTL>(at(xb + min(t + G + g, t1 - 1) * xs, lo));
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), fwd_row<VEC, W>(tap, bs, cur[g], ring));
-#pragma unroll
-                for (int g = 0; g < G; ++g) cur[g] = nxt[g];
+                    for (int v = 0; v < VEC; ++v) store_state_bf16(a.hT, s, a.D, wt.d + v, R, j, ring[R - 1 - j][v]);
             }
-        }
-    } else {
-        for (; t + G <= t1; t += G) {
-            Row<VEC> raw[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) raw[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-                store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), fwd_row<VEC, W>(tap, bs, raw[g], ring));
+            if (e >= t1) break;
+            // the next non-empty sequence starts at row e
+            do {
+                ++s;
+            } while (a.cu[s + 1] <= e);
+            start = e;
+            end = a.cu[s + 1];
+            ring_at<VEC, W>(ring, e, start, xb, xs, lo, a.h0, s, a.D, wt.d);
+            t = e;
         }
     }
-    for (; t < t1; ++t)
-        store_row<VEC, NTS>(at(yb + t * ys, lo), fwd_row<VEC, W>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)), ring));
 
-    // final state: the last W-1 values of the extended sequence (history, then x)
-    if constexpr (W > 1) {
+    // fixed-length final state: the last W-1 values of the extended sequence (history, then x)
+    if constexpr (W > 1 && !VL) {
         if (first && a.hT && hrow >= 0) {
 #pragma unroll
             for (int j = 0; j < R; ++j) {
@@ -142,45 +173,53 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 
 // A general kernel (blocks of up to 8 waves) and a "solo" one for one-wave blocks run one wave
 // per SIMD, which may use the whole register file (256 VGPRs + 256 AGPRs).
-template <int VEC, int G, int W, int F>
+template <int VEC, int G, int W, int F, bool VL>
 __global__ __launch_bounds__(512) void cconv_fwd_kernel(const FwdArgs a) {
-    fwd_body<VEC, G, W, F>(a);
+    fwd_body<VEC, G, W, F, VL>(a);
 }
 
-template <int VEC, int G, int W, int F>
+template <int VEC, int G, int W, int F, bool VL>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void cconv_fwd_kernel_solo(const FwdArgs a) {
-    fwd_body<VEC, G, W, F>(a);
+    fwd_body<VEC, G, W, F, VL>(a);
 }
 
 namespace {
 
 template <int VEC, int G, int W>
-hipError_t launch_fwd_f(int F, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd_f(int F, bool vl, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
+#define CCONV_FWD_CASE(f, vl)                                                                        \
+    case f: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, W, f, vl>), grid, block, 0, s, a); break;     \
+    case f + kSolo: hipLaunchKernelGGL((cconv_fwd_kernel_solo<VEC, G, W, f, vl>), grid, block, 0, s, a); break;
+    if (vl) {  // packed batches: the streaming options only
+        switch (F) {
+            CCONV_FWD_CASE(kVarlenFwdOptions, true)
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (F) {
-#define CCONV_FWD_CASE(f)                                                                  \
-    case f: hipLaunchKernelGGL((cconv_fwd_kernel<VEC, G, W, f>), grid, block, 0, s, a); break; \
-    case f + kSolo: hipLaunchKernelGGL((cconv_fwd_kernel_solo<VEC, G, W, f>), grid, block, 0, s, a); break;
-        CCONV_FWD_CASE(0)
-        CCONV_FWD_CASE(1)
-        CCONV_FWD_CASE(2)
-        CCONV_FWD_CASE(3)
-        CCONV_FWD_CASE(4)
-        CCONV_FWD_CASE(5)
-        CCONV_FWD_CASE(6)
-        CCONV_FWD_CASE(7)
-#undef CCONV_FWD_CASE
+        CCONV_FWD_CASE(0, false)
+        CCONV_FWD_CASE(1, false)
+        CCONV_FWD_CASE(2, false)
+        CCONV_FWD_CASE(3, false)
+        CCONV_FWD_CASE(4, false)
+        CCONV_FWD_CASE(5, false)
+        CCONV_FWD_CASE(6, false)
+        CCONV_FWD_CASE(7, false)
         default: return hipErrorInvalidValue;
     }
+#undef CCONV_FWD_CASE
     return hipGetLastError();
 }
 
 template <int VEC, int G>
 hipError_t launch_fwd_w(int W, int F, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
+    const bool vl = a.cu != nullptr;
     switch (W) {
-        case 1: return launch_fwd_f<VEC, G, 1>(F, grid, block, a, s);
-        case 2: return launch_fwd_f<VEC, G, 2>(F, grid, block, a, s);
-        case 3: return launch_fwd_f<VEC, G, 3>(F, grid, block, a, s);
-        case 4: return launch_fwd_f<VEC, G, 4>(F, grid, block, a, s);
+        case 1: return launch_fwd_f<VEC, G, 1>(F, vl, grid, block, a, s);
+        case 2: return launch_fwd_f<VEC, G, 2>(F, vl, grid, block, a, s);
+        case 3: return launch_fwd_f<VEC, G, 3>(F, vl, grid, block, a, s);
+        case 4: return launch_fwd_f<VEC, G, 4>(F, vl, grid, block, a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -44,6 +44,11 @@ struct FwdArgs {
     const int32_t* sidx;
     const uint8_t* has_init;
     const int32_t* status;
+    // Packed mode (cu non-null): B = 1, T = total rows; sequence i is rows cu[i] .. cu[i+1]-1
+    // with its own history h0[i] and final state hT[i] (written by the wave holding its last
+    // row, so hT must not share h0's memory). *status holds the offset check's verdict.
+    const int32_t* cu;
+    int64_t nseq;
     int64_t B, T, D;
     int64_t seg_rows, strip_groups, seg_groups;
     int ws;
@@ -61,6 +66,12 @@ struct BwdArgs {
     float* partial;      // [partials, W+1, D]
     const uint16_t* h0;  // [B, D, W-1] history before t = 0, or null (zeros)
     uint16_t* dh0;       // [B, D, W-1] gradient of the history out, or null
+    // Packed mode as in FwdArgs: h0 and dh0 are [nseq, D, W-1]; sequence i's history gradient
+    // is written by the wave holding its first row. Waves skip everything unless *status
+    // (when given) is CCONV_OK, and then leave their partials unwritten.
+    const int32_t* cu;
+    int64_t nseq;
+    const int32_t* status;
     int64_t B, T, D;
     int64_t seg_rows, strip_groups, seg_groups;
     int ws;
@@ -73,6 +84,7 @@ struct ReduceArgs {
     void* dw;  // [D, W]
     int dw_f32;
     float* dbias;  // [D] or null
+    const int32_t* status;  // when given, nothing is written unless *status is CCONV_OK
 };
 
 struct UpdateArgs {
@@ -98,6 +110,11 @@ hipError_t launch_update(int W, const UpdateArgs& a, int block_threads, int64_t 
                          int64_t grid_y, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_status(int32_t* status, int32_t value, hipStream_t stream);
 hipError_t launch_slots(const int32_t* idx, int64_t N, int64_t S, int32_t* status, hipStream_t stream);
+// Packed batches: the offset check (one block writes *status), and the states of empty
+// sequences (final state = history or zeros, history gradient = 0), which no wave holds.
+hipError_t launch_offsets(const int32_t* cu, int64_t nseq, int64_t total, int32_t* status, hipStream_t stream);
+hipError_t launch_empty_seqs(const int32_t* cu, int64_t nseq, const uint16_t* h0, uint16_t* hT, uint16_t* dh0,
+                             int64_t D, int L, const int32_t* status, hipStream_t stream);
 
 // Which (vec, group) pairs are compiled.
 bool fwd_variant_exists(int vec, int group);

@@ -63,7 +63,7 @@ typedef enum {
     CCONV_ERR_MISALIGNED = 5,
     CCONV_ERR_ALIASING = 6,
     CCONV_ERR_WORKSPACE = 7,
-    CCONV_ERR_INDEX = 8,
+    CCONV_ERR_INDEX = 8, /* device-side: bad state_indices, or cu_seqlens that are not a partition */
     CCONV_ERR_LAUNCH = 9,
     CCONV_ERR_BAD_CONFIG = 10
 } cconv_status_t;
@@ -154,6 +154,55 @@ cconv_status_t cconv_fwd_pool(const void* x, int64_t x_sb, int64_t x_st, const v
                               const float* bias, void* state, int64_t S, const int32_t* state_indices,
                               const uint8_t* has_initial_state, int32_t* status, void* y, int64_t B, int64_t T,
                               int64_t D, int W, cconv_stream_t stream);
+
+/*
+ * Packed variable-length batches (fla's cu_seqlens parameter: kernel-fun wheel,
+ * _common/compat.py, FLA_KWARGS row for causal_conv1d). Sequences of different lengths are
+ * packed along time into one [total, D] tensor; sequence i is rows cu_seqlens[i] ..
+ * cu_seqlens[i+1]-1 and is convolved on its own: it starts from its own history (zeros
+ * without one) and nothing crosses a boundary.
+ *   x, dy         bf16 [total, D], channels contiguous, row stride x_st / dy_st (elements, a
+ *                 multiple of 8, >= D), 16-byte aligned. y, dx: bf16 [total, D] contiguous.
+ *   cu_seqlens    int32 [nseq+1] on the device. Checked on the device: cu[0] == 0, never
+ *                 decreasing, cu[nseq] == total; empty sequences are allowed.
+ *   init_state    bf16 [nseq, D, W-1] (decode layout) or NULL (zeros).
+ *   final_state   out, bf16 [nseq, D, W-1] or NULL: the last W-1 values of each sequence's
+ *                 history-then-rows (an empty sequence's is its history). Must not overlap
+ *                 init_state (no in-place advance for packed batches).
+ *   d_init_state  out (backward), bf16 [nseq, D, W-1] or NULL: each history's gradient.
+ *   status        int32 on the device, required: receives CCONV_OK, or CCONV_ERR_INDEX when
+ *                 the offsets break the rule -- then nothing else is written (y, dx, dw,
+ *                 dbias and the states keep their contents). Written by every call that
+ *                 returns CCONV_OK.
+ *   workspace     as for cconv_bwd with B = 1, T = total: cconv_bwd_workspace_bytes(1, total,
+ *                 D, W), or cconv_bwd_workspace_bytes_config(1, total, D, W, config).
+ * Limits: total <= 2^31 - 1, nseq <= 2^24. dw and dbias sum over all sequences. The _config
+ * variants take a launch configuration as for one batch row of total rows; only the streaming
+ * options (options & ~8 == 3 forward, 7 backward) are compiled for packed batches, others
+ * give CCONV_ERR_BAD_CONFIG.
+ */
+cconv_status_t cconv_fwd_varlen(const void* x, int64_t x_st, const int32_t* cu_seqlens, int64_t nseq, int64_t total,
+                                const void* w, cconv_dtype_t w_dtype, const float* bias, const void* init_state,
+                                void* final_state, int32_t* status, void* y, int64_t D, int W,
+                                cconv_stream_t stream);
+
+cconv_status_t cconv_fwd_varlen_config(const void* x, int64_t x_st, const int32_t* cu_seqlens, int64_t nseq,
+                                       int64_t total, const void* w, cconv_dtype_t w_dtype, const float* bias,
+                                       const void* init_state, void* final_state, int32_t* status, void* y,
+                                       int64_t D, int W, const cconv_config_t* config, cconv_stream_t stream);
+
+cconv_status_t cconv_bwd_varlen(const void* x, int64_t x_st, const void* dy, int64_t dy_st, const int32_t* cu_seqlens,
+                                int64_t nseq, int64_t total, const void* w, cconv_dtype_t w_dtype, const float* bias,
+                                const void* init_state, void* dx, void* dw, cconv_dtype_t dw_dtype, float* dbias,
+                                void* d_init_state, void* workspace, size_t workspace_bytes, int32_t* status,
+                                int64_t D, int W, cconv_stream_t stream);
+
+cconv_status_t cconv_bwd_varlen_config(const void* x, int64_t x_st, const void* dy, int64_t dy_st,
+                                       const int32_t* cu_seqlens, int64_t nseq, int64_t total, const void* w,
+                                       cconv_dtype_t w_dtype, const float* bias, const void* init_state, void* dx,
+                                       void* dw, cconv_dtype_t dw_dtype, float* dbias, void* d_init_state,
+                                       void* workspace, size_t workspace_bytes, int32_t* status, int64_t D, int W,
+                                       const cconv_config_t* config, cconv_stream_t stream);
 
 /*
  * The backward's two stages, for callers that want the fp32 partials themselves (a

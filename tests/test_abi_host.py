@@ -326,3 +326,77 @@ def test_fwd_pool_null_state_allowed_when_empty():
     assert fwd_pool(state=None) == NULLP
     assert fwd_pool(state=None, S=0, y=Y + 8) == MISAL
     assert fwd_pool(state=None, W=1, y=Y + 8) == MISAL
+
+
+CU = 0x50_0000_0000
+
+
+def fwd_varlen(x=X, x_st=512, cu=CU, nseq=4, total=1000, h0=H0, hT=HT, status=PST, y=Y, D=512, W=4, cfg=None):
+    L = cc.lib()
+    args = (x, x_st, cu, nseq, total, WT, BF16, BIAS, h0, hT, status, y, D, W)
+    if cfg is None:
+        return L.cconv_fwd_varlen(*args, None)
+    return L.cconv_fwd_varlen_config(*args, ctypes.byref(cfg), None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(status=None), NULLP),
+        (dict(cu=None), NULLP),
+        (dict(x=None), NULLP),
+        (dict(nseq=-1), SHAPE),
+        (dict(nseq=(1 << 24) + 1), SHAPE),
+        (dict(total=1 << 31), SHAPE),
+        (dict(total=-1), SHAPE),
+        (dict(D=100), SHAPE),
+        (dict(x_st=500), STRIDE),
+        (dict(cu=CU + 2), MISAL),
+        (dict(status=PST + 1), MISAL),
+        (dict(hT=HT + 8), MISAL),
+        (dict(hT=H0), ALIAS),  # packed batches do not advance a state in place
+        (dict(hT=H0 + 4 * 512 * 3 * 2 - 16), ALIAS),  # the last 16 bytes of the history
+        (dict(status=CU + 4), ALIAS),
+        (dict(status=X), ALIAS),
+        (dict(status=HT + 32), ALIAS),
+        (dict(y=CU - 64), ALIAS),
+        (dict(hT=CU), ALIAS),
+        (dict(cfg=cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=15, seg_rows=64)), CONFIG),
+        (dict(cfg=cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=8, seg_rows=64)), CONFIG),
+        (dict(cfg=cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64), y=Y + 8), MISAL),
+    ],
+)
+def test_fwd_varlen_host_errors(kw, code):
+    assert fwd_varlen(**kw) == code
+
+
+def bwd_varlen(x=X, dy=DY, cu=CU, nseq=4, total=1000, h0=H0, dx=DX, dw=DW, db=DB, dh=DH, ws=WSP, ws_bytes=1 << 40,
+               status=PST, D=512, W=4, cfg=None):
+    L = cc.lib()
+    args = (x, D, dy, D, cu, nseq, total, WT, BF16, BIAS, h0, dx, dw, BF16, db, dh, ws, ws_bytes, status, D, W)
+    if cfg is None:
+        return L.cconv_bwd_varlen(*args, None)
+    return L.cconv_bwd_varlen_config(*args, ctypes.byref(cfg), None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(status=None), NULLP),
+        (dict(cu=None), NULLP),
+        (dict(dx=None), NULLP),
+        (dict(total=1 << 31), SHAPE),
+        (dict(dh=H0), ALIAS),
+        (dict(dh=DX + 16), ALIAS),
+        (dict(dx=H0), ALIAS),
+        (dict(dh=CU), ALIAS),
+        (dict(status=DW), ALIAS),
+        (dict(ws=CU), ALIAS),
+        (dict(dh=DH + 2), MISAL),
+        (dict(ws_bytes=16), WS),
+        (dict(cfg=cc.Config(vec=8, rows_per_group=8, waves_per_block=1, options=11, seg_rows=64)), CONFIG),
+        (dict(cfg=cc.Config(vec=8, rows_per_group=8, waves_per_block=1, options=15, seg_rows=64), ws_bytes=16), WS),
+    ],
+)
+def test_bwd_varlen_host_errors(kw, code):
+    assert bwd_varlen(**kw) == code
