@@ -62,6 +62,8 @@ def _load(path: Path, prec: str):
     lib.oracle_bwd_varlen.restype = ctypes.c_int
     lib.oracle_fwd_pool.argtypes = [f, i64, i64, i64, f, ctypes.c_int, f, f, i64, f, f, f]
     lib.oracle_fwd_pool.restype = ctypes.c_int
+    lib.oracle_update_ex.argtypes = [f, i64, i64, f, i64, ctypes.c_int, f, f, f, ctypes.c_int, f, f]
+    lib.oracle_update_ex.restype = ctypes.c_int
     lib.oracle_update.argtypes = [f, i64, i64, f, i64, f, f, ctypes.c_int, f, f]
     lib.oracle_update.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [f, f, i64]
@@ -303,6 +305,25 @@ class Oracle:
             return False, None, st
         return True, y, st
 
+    def update_ex(self, x, state, state_indices, cache_seqlens, w, bias=None, *, precision: str = "f64"):
+        """Decode step with a state of L entries (state [S, D, L], L = W-1 or W) and, when
+        cache_seqlens is given, circular-buffer addressing. Returns (ok, y, new_state float32)."""
+        xf, wf, bf = _f32(x), _f32(w), _f32(bias)
+        st = _f32(state).copy()
+        N, D = xf.shape
+        W = wf.shape[1]
+        S, L = st.shape[0], st.shape[2]
+        assert st.shape == (S, D, L)
+        idx = None if state_indices is None else np.ascontiguousarray(np.asarray(state_indices, dtype=np.int32))
+        cs = None if cache_seqlens is None else np.ascontiguousarray(np.asarray(cache_seqlens, dtype=np.int32))
+        y = np.empty((N, D), _NP[precision])
+        rc = self.lib(precision).oracle_update_ex(
+            _p(xf), N, D, _p(st), S, L, _p(idx), _p(cs), _p(wf), W, _p(bf), _p(y)
+        )
+        if rc != 0:
+            return False, None, st
+        return True, y, st
+
     def round_bf16(self, a, *, precision: str = "f64") -> np.ndarray:
         """Round-to-nearest-even to bf16; returns the uint16 bit patterns."""
         arr = np.ascontiguousarray(np.asarray(a, dtype=_NP[precision]))
@@ -338,6 +359,7 @@ dx_points = _default.dx_points
 dw_channels = _default.dw_channels
 update = _default.update
 fwd_pool = _default.fwd_pool
+update_ex = _default.update_ex
 fwd_varlen = _default.fwd_varlen
 bwd_varlen = _default.bwd_varlen
 fwd_state = _default.fwd_state

@@ -39,6 +39,10 @@
  *  - Prefill into the decode pool. [PR #797 discussion: the follow-up's direct
  *    full-sequence-to-decode state handoff]: the history and final state of sequence b live
  *    in slot state_indices[b] of the decode state pool, under the decode slot rule.
+ *  - Decode variants. [PR #797 description, API]: conv_state [S, D, L] with L in {3, 4} for
+ *    W = 4, i.e. L = W-1 or W; optional cache_seqlens circular-buffer metadata (reserved there,
+ *    read here as: entry c mod L takes the new token, entry (c-k) mod L holds the token k
+ *    steps back).
  *  - Decode. [PR #797 description, API and semantics]: advance a per-slot state of the last
  *    W-1 inputs by one token; conv_state_indices picks the slot, -1 marks a padding row that
  *    mutates nothing; invalid indices fail closed. Readings: state is stored oldest first
@@ -383,6 +387,51 @@ int oracle_update(const float* x, int64_t N, int64_t D, float* state, int64_t S,
  * rounded half-to-even (nearbyint under the default rounding mode), and scaled back.
  * Subnormal bf16 values share fp32's minimum exponent (-126), so their quantum is 2^-133.
  */
+/* The decode variants: a state of L entries per channel (L = W-1 or W; with L = W the oldest
+ * entry is carried but not used), updated by a shift (drop the oldest, append the token), or,
+ * with cache_seqlens, as a circular buffer: for row n with c = cache_seqlens[n], the token k
+ * steps back sits in entry (c - k) mod L and the new token is written to entry c mod L, nothing
+ * else moves. Validity: the slot rule, every cache_seqlens entry >= 0, L >= 1 in circular mode;
+ * an invalid call writes nothing and returns 1. */
+int oracle_update_ex(const float* x, int64_t N, int64_t D, float* state, int64_t S, int L, const int32_t* idx,
+                     const int32_t* cache_seqlens, const float* w, int W, const float* bias, real* y_out) {
+    if (L != W - 1 && L != W) return 1;
+    if (cache_seqlens && L < 1) return 1;
+    if (!idx && N > S) return 1;
+    if (idx && !slots_valid(idx, N, S)) return 1;
+    if (cache_seqlens)
+        for (int64_t n = 0; n < N; ++n)
+            if (cache_seqlens[n] < 0) return 1;
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t s = idx ? (int64_t)idx[n] : n;
+        if (s < 0) {
+            for (int64_t d = 0; d < D; ++d) y_out[n * D + d] = 0;
+            continue;
+        }
+        const int64_t c = cache_seqlens ? (int64_t)cache_seqlens[n] : 0;
+        for (int64_t d = 0; d < D; ++d) {
+            float* st = state + (s * D + d) * L;
+            /* the inputs 1 .. W-1 steps back, in the state's order of entries */
+            real z = bias ? (real)bias[d] : (real)0;
+            for (int j = 0; j < W - 1; ++j) {
+                const int k = W - 1 - j; /* steps back; weight w[d, j] */
+                const int64_t e = cache_seqlens ? ((c - k) % L + L) % L : L - k;
+                z = z + (real)w[d * W + j] * (real)st[e];
+            }
+            z = z + (real)w[d * W + (W - 1)] * (real)x[n * D + d];
+            y_out[n * D + d] = z * sigmoid(z);
+            if (L == 0) continue;
+            if (cache_seqlens) {
+                st[c % L] = x[n * D + d];
+            } else {
+                for (int j = 0; j + 1 < L; ++j) st[j] = st[j + 1];
+                st[L - 1] = x[n * D + d];
+            }
+        }
+    }
+    return 0;
+}
+
 static uint16_t bf16_rtne(double v) {
     uint16_t sign = signbit(v) ? 0x8000u : 0u;
     if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);

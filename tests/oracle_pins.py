@@ -640,6 +640,103 @@ def check_varlen_sequences_independent(orc):
     assert not np.array_equal(y2[:6], y[:6]) and not np.array_equal(y2[11:], y[11:])
 
 
+def check_update_ex_by_hand(orc):
+    """Small decode steps worked by hand (values exact in float): which entries feed z and
+    which entry takes the token, for shift and circular states of both lengths."""
+    w = np.array([[0.5, 2.0]], np.float32)  # W = 2: w0 pairs with the previous token, w1 with x
+    x = np.array([[4.0]], np.float32)
+    st = np.array([[[1.0, 3.0]]], np.float32)  # L = 2 = W: entries [a, b]
+    # shift: previous token = last entry b = 3 -> z = 0.5*3 + 2*4 = 9.5; state -> [3, 4]
+    ok, y, ns = orc.update_ex(x, st, None, None, w)
+    assert ok and np.array_equal(ns[0, 0], [3.0, 4.0])
+    _close(y[0, 0], 9.5 * _sigmoid(9.5), 1e-14, what="shift L=W")
+    # circular, c = 3: previous token in entry (3-1) mod 2 = 0 -> a = 1 -> z = 0.5 + 8 = 8.5;
+    # the token goes to entry 3 mod 2 = 1 -> [1, 4]
+    ok, y, ns = orc.update_ex(x, st, None, np.array([3], np.int32), w)
+    assert ok and np.array_equal(ns[0, 0], [1.0, 4.0])
+    _close(y[0, 0], 8.5 * _sigmoid(8.5), 1e-14, what="circular L=W c=3")
+    # W = 4, L = 4, circular, c = 5: tokens 1, 2, 3 steps back in entries 0, 3, 2; entry 1 takes x
+    w4 = np.array([[0.25, 0.5, 1.0, 2.0]], np.float32)
+    st4 = np.array([[[10.0, 20.0, 30.0, 40.0]]], np.float32)
+    ok, y, ns = orc.update_ex(x, st4, None, np.array([5], np.int32), w4)
+    z = 0.25 * 30.0 + 0.5 * 40.0 + 1.0 * 10.0 + 2.0 * 4.0  # x[t-3]=e2, x[t-2]=e3, x[t-1]=e0
+    assert ok and np.array_equal(ns[0, 0], [10.0, 4.0, 30.0, 40.0])
+    _close(y[0, 0], z * _sigmoid(z), 1e-14, what="circular W=4 L=4 c=5")
+    # W = 4, L = 3, circular, c = 7: entries (7-1)%3=0, (7-2)%3=2, (7-3)%3=1; x -> entry 7%3=1
+    st3 = np.array([[[10.0, 20.0, 30.0]]], np.float32)
+    ok, y, ns = orc.update_ex(x, st3, None, np.array([7], np.int32), w4)
+    z = 0.25 * 20.0 + 0.5 * 30.0 + 1.0 * 10.0 + 2.0 * 4.0
+    assert ok and np.array_equal(ns[0, 0], [10.0, 4.0, 30.0])
+    _close(y[0, 0], z * _sigmoid(z), 1e-14, what="circular W=4 L=3 c=7")
+
+
+def check_update_ex_matches_update(orc):
+    """L = W-1 with a shift is the plain decode update, bit for bit (y and state), padding
+    rows and all."""
+    N, S, D, W = 5, 9, 6, 4
+    rng = np.random.default_rng(500)
+    x = _bf16_values(rng, (N, D))
+    w = _bf16_values(rng, (D, W))
+    b = _bf16_values(rng, (D,), 0.3)
+    state = _bf16_values(rng, (S, D, W - 1))
+    idx = np.array([3, -1, 0, 8, 5], np.int32)
+    ok, y, st = orc.update(x, state, idx, w, b)
+    ok2, y2, st2 = orc.update_ex(x, state, idx, None, w, b)
+    assert ok and ok2 and np.array_equal(y, y2) and np.array_equal(st, st2)
+
+
+def check_update_ex_decode_equals_forward(orc):
+    """Token by token, every variant (L = W-1 or W; shift, or circular from ring start c0)
+    reproduces the forward over the sequence from its history, bit for bit in the oracle."""
+    B, T, D = 3, 11, 5
+    for W in (2, 3, 4):
+        x, h0, w, b, _ = _problem_h0(510 + W, B, T, D, W)
+        y_ref, _ = orc.fwd_state(x, h0, w, b)
+        for L in (W - 1, W):
+            for c0 in (None, 0, 1, 5):
+                st = np.zeros((B, D, L), np.float32)
+                for k in range(1, W):  # the history, k steps back from the first token
+                    e = (L - k) if c0 is None else (c0 - k) % L
+                    st[:, :, e] = h0[:, :, W - 1 - k]
+                for t in range(T):
+                    cs = None if c0 is None else np.full(B, c0 + t, np.int32)
+                    ok, yt, st = orc.update_ex(x[:, t], st, None, cs, w, b)
+                    assert ok and np.array_equal(yt, y_ref[:, t]), f"W={W} L={L} c0={c0} t={t}"
+
+
+def check_update_ex_oldest_entry_unused(orc):
+    """With L = W the oldest entry is carried but never used; a shift drops it."""
+    N, D, W = 3, 4, 4
+    rng = np.random.default_rng(520)
+    x = _bf16_values(rng, (N, D))
+    w = _bf16_values(rng, (D, W))
+    st = _bf16_values(rng, (N, D, W))
+    _, y, ns = orc.update_ex(x, st, None, None, w)
+    st2 = st.copy()
+    st2[:, :, 0] += 5.0
+    _, y2, ns2 = orc.update_ex(x, st2, None, None, w)
+    assert np.array_equal(y, y2) and np.array_equal(ns, ns2)
+    assert np.array_equal(ns[:, :, :W - 1], st[:, :, 1:]) and np.array_equal(ns[:, :, W - 1], x)
+
+
+def check_update_ex_validation(orc):
+    """A negative cache_seqlens entry, a bad state length or a circular state without entries
+    fail the whole call, which then changes nothing."""
+    N, D, W = 3, 2, 4
+    rng = np.random.default_rng(530)
+    x = _bf16_values(rng, (N, D))
+    w = _bf16_values(rng, (D, W))
+    for L, cs in ((3, [0, -1, 2]), (4, [-5, 0, 0]), (2, None), (5, None)):
+        st = _bf16_values(rng, (N, D, L))
+        ok, y, ns = orc.update_ex(x, st, None, None if cs is None else np.array(cs, np.int32), w)
+        assert not ok and y is None and np.array_equal(ns, st), (L, cs)
+    w1 = _bf16_values(rng, (D, 1))
+    ok, _, _ = orc.update_ex(x, np.zeros((N, D, 0), np.float32), None, np.zeros(N, np.int32), w1)
+    assert not ok, "circular state without entries accepted"
+    ok, _, _ = orc.update_ex(x, np.zeros((N, D, 0), np.float32), None, None, w1)
+    assert ok
+
+
 ALL_CHECKS = [
     check_rounding_matches_torch,
     check_rounding_from_double_is_direct,
@@ -668,4 +765,9 @@ ALL_CHECKS = [
     check_varlen_equal_lengths_is_batch,
     check_varlen_offsets_validation,
     check_varlen_sequences_independent,
+    check_update_ex_by_hand,
+    check_update_ex_matches_update,
+    check_update_ex_decode_equals_forward,
+    check_update_ex_oldest_entry_unused,
+    check_update_ex_validation,
 ]

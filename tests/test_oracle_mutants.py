@@ -44,6 +44,10 @@ MUTANTS = [
     ("varlen_history_of_next", "oracle_fwd_state(x + a * D, h0 ? h0 + i * D * L : NULL", "oracle_fwd_state(x + a * D, h0 ? h0 + ((i + 1) % n) * D * L : NULL"),
     ("varlen_rows_shifted", "oracle_fwd_state(x + a * D,", "oracle_fwd_state(x + (a > 0 ? a - 1 : 0) * D,"),
     ("varlen_dw_last_only", "dw_out[e] = dw_out[e] + dwi[e];", "dw_out[e] = dwi[e];"),
+    ("ring_write_off_by_one", "st[c % L] = x[n * D + d];", "st[(c + 1) % L] = x[n * D + d];"),
+    ("ring_read_reversed", "((c - k) % L + L) % L", "((c + k) % L + L) % L"),
+    ("ex_shift_reads_oldest", "cache_seqlens ? ((c - k) % L + L) % L : L - k;", "cache_seqlens ? ((c - k) % L + L) % L : (L - k) % (W - 1);"),
+    ("ex_negative_seqlen_accepted", "if (cache_seqlens[n] < 0) return 1;", "(void)n;"),
     ("round_half_away", "nearbyint(a / q)", "floor(a / q + 0.5)"),
     ("round_truncate", "nearbyint(a / q)", "trunc(a / q)"),
 ]
