@@ -32,6 +32,7 @@ __all__ = [
     "cconv_bwd_main",
     "cconv_bwd_finish",
     "cconv_update",
+    "cconv_update_ex",
     "cconv_default_config",
     "cconv_status_string",
     "cconv_version",
@@ -128,6 +129,8 @@ def _declare(L):
     L.cconv_bwd_main.restype = i32
     L.cconv_bwd_finish.argtypes = [p, sz, p, i32, p, i64, i64, i64, i32, p]
     L.cconv_bwd_finish.restype = i32
+    L.cconv_update_ex.argtypes = [p, i64, p, i64, i32, p, p, p, i32, p, p, i64, i64, i32, p, p]
+    L.cconv_update_ex.restype = i32
     L.cconv_update.argtypes = [p, i64, p, i64, p, p, i32, p, p, i64, i64, i32, p, p]
     L.cconv_update.restype = i32
     L.cconv_default_config.argtypes = [i32, i64, i64, i64, i32, ctypes.POINTER(Config)]
@@ -609,5 +612,45 @@ def cconv_update(x, state, state_indices, w, bias=None, *, y=None, status=None, 
             _ptr(bias), _ptr(y), N, D, W, _ptr(status), _stream(stream),
         ),
         "cconv_update",
+    )
+    return y, status
+
+
+def cconv_update_ex(x, state, state_indices, w, bias=None, *, cache_seqlens=None, y=None, status=None, stream=None):
+    """A decode step with a state of L entries (state bf16 [S, D, L], L = W-1 or W; L is read
+    from the state's shape) and, with cache_seqlens (int32 [N]), circular-buffer addressing:
+    the token k steps back is entry (c - k) mod L, the new token goes to entry c mod L. Returns
+    (y, status); state is updated in place."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be bf16 [N, D] with unit channel stride")
+    N, D = x.shape
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    _dev(state, "state")
+    if state.dtype != torch.bfloat16 or state.dim() != 3 or state.shape[1] != D or not state.is_contiguous():
+        raise ValueError("state must be a contiguous bf16 [S, D, L] tensor")
+    S, L = state.shape[0], state.shape[2]
+    for t, name in ((state_indices, "state_indices"), (cache_seqlens, "cache_seqlens")):
+        if t is not None:
+            _dev(t, name)
+            if t.dtype != torch.int32 or t.shape != (N,) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 [N] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    if y is None:
+        y = torch.empty((N, D), dtype=torch.bfloat16, device=x.device)
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=x.device)
+    _check(
+        lib().cconv_update_ex(
+            _ptr(x), x.stride(0) if N > 0 else D, _ptr(state), S, L, _ptr(state_indices), _ptr(cache_seqlens),
+            _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(y), N, D, W, _ptr(status), _stream(stream),
+        ),
+        "cconv_update_ex",
     )
     return y, status

@@ -405,6 +405,73 @@ cconv_status_t bwd_varlen_impl(const void* x, int64_t x_st, const void* dy, int6
                     workspace_bytes, 1, total, D, W, cfg, stream, ex);
 }
 
+// The decode update: state of L entries (L = W-1 or W), shift or (with cache_seqlens)
+// circular addressing.
+cconv_status_t update_impl(const void* x, int64_t x_ld, void* state, int64_t S, int L, const int32_t* state_indices,
+                           const int32_t* cache_seqlens, const void* w, cconv_dtype_t w_dtype, const float* bias,
+                           void* y, int64_t N, int64_t D, int W, int32_t* status, cconv_stream_t stream) {
+    if (N < 0 || S < 0 || D < 0 || W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
+    if (L != W - 1 && L != W) return CCONV_ERR_BAD_SHAPE;
+    if (cache_seqlens && L < 1) return CCONV_ERR_BAD_SHAPE;  // a circular state needs entries
+    if (((!x || !y) && N > 0 && D > 0) || (!w && D > 0) || (!state && S > 0 && D > 0 && L > 0))
+        return CCONV_ERR_NULL_POINTER;
+    if (N < 0 || S < 0 || D < 0 || N > kMaxDecodeRows || S > kMaxDim || D > kMaxDim) return CCONV_ERR_BAD_SHAPE;
+    if (W < 1 || W > 4 || D % 8 != 0) return CCONV_ERR_BAD_SHAPE;
+    if (state_indices && S > kMaxIndexedSlots) return CCONV_ERR_BAD_SHAPE;
+    if (!state_indices && N > S) return CCONV_ERR_BAD_SHAPE;
+    if (!dtype_ok(w_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
+    if (x_ld < D || x_ld > kMaxDim || x_ld % 8 != 0) return CCONV_ERR_BAD_STRIDE;
+    if (!aligned(x, 16) || !aligned(state, 16) || !aligned(w, 16) || !aligned(y, 16) ||
+        (bias && !aligned(bias, 16)) || (state_indices && !aligned(state_indices, 4)) ||
+        (cache_seqlens && !aligned(cache_seqlens, 4)) || (status && !aligned(status, 4)))
+        return CCONV_ERR_MISALIGNED;
+    const Span in_x = span(x, N == 0 || D == 0 ? 0 : (static_cast<__int128>(N - 1) * x_ld + D) * 2);
+    const Span in_w = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
+    const Span in_b = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
+    const Span in_i = state_indices ? span(state_indices, static_cast<__int128>(N) * 4) : Span{0, 0};
+    const Span in_c = cache_seqlens ? span(cache_seqlens, static_cast<__int128>(N) * 4) : Span{0, 0};
+    const Span o_st = span(state, static_cast<__int128>(S) * D * L * 2);
+    const Span o_y = span(y, static_cast<__int128>(N) * D * 2);
+    const Span o_s = status ? span(status, 4) : Span{0, 0};
+    const Span outs[3] = {o_st, o_y, o_s};
+    const Span ins[5] = {in_x, in_w, in_b, in_i, in_c};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlap(outs[i], ins[j])) return CCONV_ERR_ALIASING;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return CCONV_ERR_ALIASING;
+    }
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (N == 0 || D == 0) {
+        if (status) return cconv::launch_status(status, CCONV_OK, s) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
+        return CCONV_OK;
+    }
+    const int64_t dv = D / 8;  // 8-channel vectors per row
+    const int threads = static_cast<int>(std::min<int64_t>(256, ((dv + 63) / 64) * 64));
+    const int64_t grid_x = (dv + threads - 1) / threads;
+    const int64_t rpb = std::max<int64_t>(1, (N * grid_x + kUpdateTargetBlocks - 1) / kUpdateTargetBlocks);
+    const int64_t grid_y = (N + rpb - 1) / rpb;
+    if (grid_x > INT32_MAX || grid_y > 65535) return CCONV_ERR_BAD_SHAPE;
+    const size_t lds = state_indices ? static_cast<size_t>((S + 31) / 32) * 4 : 0;
+    cconv::UpdateArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.x_ld = x_ld;
+    a.state = static_cast<uint16_t*>(state);
+    a.S = S;
+    a.idx = state_indices;
+    a.cs = cache_seqlens;
+    a.w = w;
+    a.w_f32 = (w_dtype == CCONV_F32);
+    a.bias = bias;
+    a.y = static_cast<uint16_t*>(y);
+    a.N = N;
+    a.D = D;
+    a.rows_per_block = rpb;
+    a.status = status;
+    return cconv::launch_update(W, L, a, threads, grid_x, grid_y, lds, s) == hipSuccess ? CCONV_OK
+                                                                                        : CCONV_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -554,62 +621,15 @@ cconv_status_t cconv_default_config(int which, int64_t B, int64_t T, int64_t D, 
 cconv_status_t cconv_update(const void* x, int64_t x_ld, void* state, int64_t S, const int32_t* state_indices,
                             const void* w, cconv_dtype_t w_dtype, const float* bias, void* y, int64_t N, int64_t D,
                             int W, int32_t* status, cconv_stream_t stream) {
-    if (N < 0 || S < 0 || D < 0 || W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
-    if (((!x || !y) && N > 0 && D > 0) || (!w && D > 0) || (!state && S > 0 && D > 0 && W > 1))
-        return CCONV_ERR_NULL_POINTER;
-    if (N < 0 || S < 0 || D < 0 || N > kMaxDecodeRows || S > kMaxDim || D > kMaxDim) return CCONV_ERR_BAD_SHAPE;
-    if (W < 1 || W > 4 || D % 8 != 0) return CCONV_ERR_BAD_SHAPE;
-    if (state_indices && S > kMaxIndexedSlots) return CCONV_ERR_BAD_SHAPE;
-    if (!state_indices && N > S) return CCONV_ERR_BAD_SHAPE;
-    if (!dtype_ok(w_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
-    if (x_ld < D || x_ld > kMaxDim || x_ld % 8 != 0) return CCONV_ERR_BAD_STRIDE;
-    if (!aligned(x, 16) || !aligned(state, 16) || !aligned(w, 16) || !aligned(y, 16) ||
-        (bias && !aligned(bias, 16)) || (state_indices && !aligned(state_indices, 4)) ||
-        (status && !aligned(status, 4)))
-        return CCONV_ERR_MISALIGNED;
-    const int L = W - 1;
-    const Span in_x = span(x, N == 0 || D == 0 ? 0 : (static_cast<__int128>(N - 1) * x_ld + D) * 2);
-    const Span in_w = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
-    const Span in_b = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
-    const Span in_i = state_indices ? span(state_indices, static_cast<__int128>(N) * 4) : Span{0, 0};
-    const Span o_st = span(state, static_cast<__int128>(S) * D * L * 2);
-    const Span o_y = span(y, static_cast<__int128>(N) * D * 2);
-    const Span o_s = status ? span(status, 4) : Span{0, 0};
-    const Span outs[3] = {o_st, o_y, o_s};
-    const Span ins[4] = {in_x, in_w, in_b, in_i};
-    for (int i = 0; i < 3; ++i) {
-        for (int j = 0; j < 4; ++j)
-            if (overlap(outs[i], ins[j])) return CCONV_ERR_ALIASING;
-        for (int j = i + 1; j < 3; ++j)
-            if (overlap(outs[i], outs[j])) return CCONV_ERR_ALIASING;
-    }
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (N == 0 || D == 0) {
-        if (status) return cconv::launch_status(status, CCONV_OK, s) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
-        return CCONV_OK;
-    }
-    const int64_t dv = D / 8;  // 8-channel vectors per row
-    const int threads = static_cast<int>(std::min<int64_t>(256, ((dv + 63) / 64) * 64));
-    const int64_t grid_x = (dv + threads - 1) / threads;
-    const int64_t rpb = std::max<int64_t>(1, (N * grid_x + kUpdateTargetBlocks - 1) / kUpdateTargetBlocks);
-    const int64_t grid_y = (N + rpb - 1) / rpb;
-    if (grid_x > INT32_MAX || grid_y > 65535) return CCONV_ERR_BAD_SHAPE;
-    const size_t lds = state_indices ? static_cast<size_t>((S + 31) / 32) * 4 : 0;
-    cconv::UpdateArgs a;
-    a.x = static_cast<const uint16_t*>(x);
-    a.x_ld = x_ld;
-    a.state = static_cast<uint16_t*>(state);
-    a.S = S;
-    a.idx = state_indices;
-    a.w = w;
-    a.w_f32 = (w_dtype == CCONV_F32);
-    a.bias = bias;
-    a.y = static_cast<uint16_t*>(y);
-    a.N = N;
-    a.D = D;
-    a.rows_per_block = rpb;
-    a.status = status;
-    return cconv::launch_update(W, a, threads, grid_x, grid_y, lds, s) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
+    return update_impl(x, x_ld, state, S, W - 1, state_indices, nullptr, w, w_dtype, bias, y, N, D, W, status, stream);
+}
+
+cconv_status_t cconv_update_ex(const void* x, int64_t x_ld, void* state, int64_t S, int L,
+                               const int32_t* state_indices, const int32_t* cache_seqlens, const void* w,
+                               cconv_dtype_t w_dtype, const float* bias, void* y, int64_t N, int64_t D, int W,
+                               int32_t* status, cconv_stream_t stream) {
+    return update_impl(x, x_ld, state, S, L, state_indices, cache_seqlens, w, w_dtype, bias, y, N, D, W, status,
+                       stream);
 }
 
 const char* cconv_status_string(cconv_status_t status) {

@@ -90,9 +90,10 @@ struct ReduceArgs {
 struct UpdateArgs {
     const uint16_t* x;
     int64_t x_ld;
-    uint16_t* state;  // [S, D, W-1]
+    uint16_t* state;  // [S, D, L], L = W-1 or W
     int64_t S;
     const int32_t* idx;  // [N] or null
+    const int32_t* cs;   // [N] cache_seqlens (circular state) or null (shift)
     const void* w;
     int w_f32;
     const float* bias;
@@ -106,7 +107,7 @@ struct UpdateArgs {
 hipError_t launch_fwd(const Plan& p, int W, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
-hipError_t launch_update(int W, const UpdateArgs& a, int block_threads, int64_t grid_x,
+hipError_t launch_update(int W, int L, const UpdateArgs& a, int block_threads, int64_t grid_x,
                          int64_t grid_y, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_status(int32_t* status, int32_t value, hipStream_t stream);
 hipError_t launch_slots(const int32_t* idx, int64_t N, int64_t S, int32_t* status, hipStream_t stream);

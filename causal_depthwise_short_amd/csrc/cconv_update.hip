@@ -20,13 +20,33 @@
 
 namespace cconv {
 
-template <int W>
+// The tokens 1 .. W-1 steps back, from the L state entries a thread loaded (h[v*L + e] is
+// entry e of channel d+v), in the forward's ring order: ring[k-1] = x[t-k]. Shift mode
+// (ROT < 0): entry L-k. Circular mode with rotation ROT = c mod L: entry (ROT - k) mod L.
+template <int W, int L, int ROT>
+__device__ __forceinline__ void ring_from_state(const uint16_t (&h)[8 * (L > 0 ? L : 1)],
+                                                float (&ring)[W > 1 ? W - 1 : 1][8]) {
+#pragma unroll
+    for (int k = 1; k < W; ++k) {
+        const int e = ROT < 0 ? L - k : ((ROT - k) % L + L) % L;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) ring[k - 1][v] = __uint_as_float(static_cast<uint32_t>(h[v * L + e]) << 16);
+    }
+}
+
+template <int W, int L, bool CIRC>
 __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
     constexpr int VEC = 8;
-    constexpr int L = W - 1;  // state length
+    constexpr int R = W > 1 ? W - 1 : 1;
     extern __shared__ uint32_t seen[];
 
-    const bool bad = a.idx ? block_slots_bad(a.idx, a.N, a.S, seen) : false;
+    bool bad = a.idx ? block_slots_bad(a.idx, a.N, a.S, seen) : false;
+    if (CIRC) {  // every cache_seqlens entry must be >= 0
+        bool neg = false;
+        for (int64_t i = threadIdx.x; i < a.N; i += blockDim.x)
+            if (a.cs[i] < 0) neg = true;
+        bad = __syncthreads_or(neg || bad);
+    }
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && a.status)
         a.status[0] = bad ? CCONV_ERR_INDEX : CCONV_OK;
     if (bad) return;
@@ -51,7 +71,8 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
         const Row<VEC> rx = load_row<VEC>(a.x + n * a.x_ld + d);
         float xt[VEC];
         widen(rx, xt);
-        // state of channel d+v, entry j, at 16-bit position v*L + j
+        // the thread's 8 channels x L entries: 16*L contiguous bytes, entry e of channel d+v at
+        // 16-bit position v*L + e
         uint16_t h[VEC * (L > 0 ? L : 1)];
         uint16_t* __restrict__ sp = a.state + (s * a.D + d) * L;
         if constexpr (L > 0) {
@@ -66,12 +87,21 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
                 }
             }
         }
-        // ring view in the forward's order: ring[k-1] = x[t-k] = state[.., L-k]
-        float ring[L > 0 ? L : 1][VEC];
-#pragma unroll
-        for (int k = 1; k <= L; ++k)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) ring[k - 1][v] = __uint_as_float(static_cast<uint32_t>(h[v * L + (L - k)]) << 16);
+        float ring[R][VEC];
+        int rot = 0;  // circular: the entry that takes the token (block-uniform: one row at a time)
+        if constexpr (W > 1) {
+            if constexpr (!CIRC) {
+                ring_from_state<W, L, -1>(h, ring);
+            } else {
+                rot = static_cast<int>(static_cast<int64_t>(a.cs[n]) % L);
+                if (rot == 0) ring_from_state<W, L, 0>(h, ring);
+                if constexpr (L > 1) if (rot == 1) ring_from_state<W, L, (L > 1 ? 1 : 0)>(h, ring);
+                if constexpr (L > 2) if (rot == 2) ring_from_state<W, L, (L > 2 ? 2 : 0)>(h, ring);
+                if constexpr (L > 3) if (rot == 3) ring_from_state<W, L, (L > 3 ? 3 : 0)>(h, ring);
+            }
+        } else if constexpr (CIRC) {
+            rot = static_cast<int>(static_cast<int64_t>(a.cs[n]) % L);
+        }
         float y[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
@@ -80,21 +110,29 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
         }
         store_row<VEC>(yp, narrow<VEC>(y));
         if constexpr (L > 0) {
-            uint16_t nh[VEC * L];
+            if constexpr (CIRC) {  // write only the token's entry (bit copies of x)
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) {
+                for (int v = 0; v < VEC; ++v) {
+                    const uint32_t xw = rx.u[v / 2];
+                    sp[v * L + rot] = static_cast<uint16_t>((v & 1) ? (xw >> 16) : (xw & 0xffffu));
+                }
+            } else {  // shift: drop the oldest entry, append the token
+                uint16_t nh[VEC * L];
 #pragma unroll
-                for (int j = 0; j + 1 < L; ++j) nh[v * L + j] = h[v * L + j + 1];
-                const uint32_t xw = rx.u[v / 2];
-                nh[v * L + L - 1] = static_cast<uint16_t>((v & 1) ? (xw >> 16) : (xw & 0xffffu));
-            }
+                for (int v = 0; v < VEC; ++v) {
 #pragma unroll
-            for (int q = 0; q < L; ++q) {
-                uint32_t u[4];
+                    for (int j = 0; j + 1 < L; ++j) nh[v * L + j] = h[v * L + j + 1];
+                    const uint32_t xw = rx.u[v / 2];
+                    nh[v * L + L - 1] = static_cast<uint16_t>((v & 1) ? (xw >> 16) : (xw & 0xffffu));
+                }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    u[i] = static_cast<uint32_t>(nh[q * 8 + 2 * i]) | (static_cast<uint32_t>(nh[q * 8 + 2 * i + 1]) << 16);
-                reinterpret_cast<uint4*>(sp)[q] = make_uint4(u[0], u[1], u[2], u[3]);
+                for (int q = 0; q < L; ++q) {
+                    uint32_t u[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        u[i] = static_cast<uint32_t>(nh[q * 8 + 2 * i]) | (static_cast<uint32_t>(nh[q * 8 + 2 * i + 1]) << 16);
+                    reinterpret_cast<uint4*>(sp)[q] = make_uint4(u[0], u[1], u[2], u[3]);
+                }
             }
         }
     }
@@ -113,17 +151,47 @@ __global__ void cconv_status_kernel(int32_t* status, int32_t value) {
     if (threadIdx.x == 0 && blockIdx.x == 0) status[0] = value;
 }
 
-hipError_t launch_update(int W, const UpdateArgs& a, int block_threads, int64_t grid_x, int64_t grid_y,
-                         size_t lds, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(grid_x), static_cast<uint32_t>(grid_y)), block(block_threads);
-    switch (W) {
-        case 1: hipLaunchKernelGGL(cconv_update_kernel<1>, grid, block, lds, s, a); break;
-        case 2: hipLaunchKernelGGL(cconv_update_kernel<2>, grid, block, lds, s, a); break;
-        case 3: hipLaunchKernelGGL(cconv_update_kernel<3>, grid, block, lds, s, a); break;
-        case 4: hipLaunchKernelGGL(cconv_update_kernel<4>, grid, block, lds, s, a); break;
-        default: return hipErrorInvalidValue;
+namespace {
+
+template <int W, int L, bool CIRC>
+void launch_update_k(dim3 grid, dim3 block, size_t lds, const UpdateArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((cconv_update_kernel<W, L, CIRC>), grid, block, lds, s, a);
+}
+
+template <int W>
+hipError_t launch_update_w(int L, bool circ, dim3 grid, dim3 block, size_t lds, const UpdateArgs& a, hipStream_t s) {
+    if (L == W - 1) {
+        if (!circ) {
+            launch_update_k<W, W - 1, false>(grid, block, lds, a, s);
+        } else if constexpr (W > 1) {
+            launch_update_k<W, W - 1, true>(grid, block, lds, a, s);
+        } else {
+            return hipErrorInvalidValue;  // a circular state needs at least one entry
+        }
+    } else if (L == W) {
+        if (circ)
+            launch_update_k<W, W, true>(grid, block, lds, a, s);
+        else
+            launch_update_k<W, W, false>(grid, block, lds, a, s);
+    } else {
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_update(int W, int L, const UpdateArgs& a, int block_threads, int64_t grid_x, int64_t grid_y,
+                         size_t lds, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(grid_x), static_cast<uint32_t>(grid_y)), block(block_threads);
+    const bool circ = a.cs != nullptr;
+    switch (W) {
+        case 1: return launch_update_w<1>(L, circ, grid, block, lds, a, s);
+        case 2: return launch_update_w<2>(L, circ, grid, block, lds, a, s);
+        case 3: return launch_update_w<3>(L, circ, grid, block, lds, a, s);
+        case 4: return launch_update_w<4>(L, circ, grid, block, lds, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_slots(const int32_t* idx, int64_t N, int64_t S, int32_t* status, hipStream_t s) {

@@ -186,23 +186,11 @@ cconv_status_t cconv_fwd_varlen(const void* x, int64_t x_st, const int32_t* cu_s
                                 void* final_state, int32_t* status, void* y, int64_t D, int W,
                                 cconv_stream_t stream);
 
-cconv_status_t cconv_fwd_varlen_config(const void* x, int64_t x_st, const int32_t* cu_seqlens, int64_t nseq,
-                                       int64_t total, const void* w, cconv_dtype_t w_dtype, const float* bias,
-                                       const void* init_state, void* final_state, int32_t* status, void* y,
-                                       int64_t D, int W, const cconv_config_t* config, cconv_stream_t stream);
-
 cconv_status_t cconv_bwd_varlen(const void* x, int64_t x_st, const void* dy, int64_t dy_st, const int32_t* cu_seqlens,
                                 int64_t nseq, int64_t total, const void* w, cconv_dtype_t w_dtype, const float* bias,
                                 const void* init_state, void* dx, void* dw, cconv_dtype_t dw_dtype, float* dbias,
                                 void* d_init_state, void* workspace, size_t workspace_bytes, int32_t* status,
                                 int64_t D, int W, cconv_stream_t stream);
-
-cconv_status_t cconv_bwd_varlen_config(const void* x, int64_t x_st, const void* dy, int64_t dy_st,
-                                       const int32_t* cu_seqlens, int64_t nseq, int64_t total, const void* w,
-                                       cconv_dtype_t w_dtype, const float* bias, const void* init_state, void* dx,
-                                       void* dw, cconv_dtype_t dw_dtype, float* dbias, void* d_init_state,
-                                       void* workspace, size_t workspace_bytes, int32_t* status, int64_t D, int W,
-                                       const cconv_config_t* config, cconv_stream_t stream);
 
 /*
  * The backward's two stages, for callers that want the fp32 partials themselves (a
@@ -241,6 +229,26 @@ cconv_status_t cconv_update(const void* x, int64_t x_ld, void* state, int64_t S,
                             const int32_t* state_indices, const void* w, cconv_dtype_t w_dtype,
                             const float* bias, void* y, int64_t N, int64_t D, int W,
                             int32_t* status, cconv_stream_t stream);
+
+/*
+ * Decode variants [the decode PR's API: conv_state [S, D, L] with L in {3, 4} for W = 4, and
+ * reserved cache_seqlens circular-buffer metadata].
+ *   L              entries per channel in the state: W-1 (as cconv_update) or W (the oldest
+ *                  entry is carried but not used: a shift drops it).
+ *   state          bf16 [S, D, L], 16-byte aligned, updated in place.
+ *   cache_seqlens  int32 [N] on the device, or NULL. NULL: shift mode (drop the oldest entry,
+ *                  append the token: L entries rewritten). Given: circular mode, nothing
+ *                  moves: for row n with c = cache_seqlens[n] >= 0 the token k steps back is
+ *                  entry (c - k) mod L and the new token is written to entry c mod L only (2
+ *                  bytes per channel). The caller advances cache_seqlens. A state written by a
+ *                  prefill (oldest first) is a circular state with c = 0 (mod L). Needs L >= 1.
+ * Everything else as cconv_update; a negative cache_seqlens entry fails the call like an
+ * invalid index (CCONV_ERR_INDEX in *status, nothing written).
+ */
+cconv_status_t cconv_update_ex(const void* x, int64_t x_ld, void* state, int64_t S, int L,
+                               const int32_t* state_indices, const int32_t* cache_seqlens, const void* w,
+                               cconv_dtype_t w_dtype, const float* bias, void* y, int64_t N, int64_t D, int W,
+                               int32_t* status, cconv_stream_t stream);
 
 /* A short English description of a status code (static storage). */
 const char* cconv_status_string(cconv_status_t status);
@@ -295,6 +303,19 @@ cconv_status_t cconv_bwd_config(const void* x, int64_t x_sb, int64_t x_st, const
                                 cconv_dtype_t dw_dtype, float* dbias, void* workspace,
                                 size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int W,
                                 const cconv_config_t* cfg, cconv_stream_t stream);
+
+/* Packed batches with an explicit launch configuration (see cconv_fwd_varlen). */
+cconv_status_t cconv_fwd_varlen_config(const void* x, int64_t x_st, const int32_t* cu_seqlens, int64_t nseq,
+                                       int64_t total, const void* w, cconv_dtype_t w_dtype, const float* bias,
+                                       const void* init_state, void* final_state, int32_t* status, void* y,
+                                       int64_t D, int W, const cconv_config_t* config, cconv_stream_t stream);
+
+cconv_status_t cconv_bwd_varlen_config(const void* x, int64_t x_st, const void* dy, int64_t dy_st,
+                                       const int32_t* cu_seqlens, int64_t nseq, int64_t total, const void* w,
+                                       cconv_dtype_t w_dtype, const float* bias, const void* init_state, void* dx,
+                                       void* dw, cconv_dtype_t dw_dtype, float* dbias, void* d_init_state,
+                                       void* workspace, size_t workspace_bytes, int32_t* status, int64_t D, int W,
+                                       const cconv_config_t* config, cconv_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -400,3 +400,35 @@ def bwd_varlen(x=X, dy=DY, cu=CU, nseq=4, total=1000, h0=H0, dx=DX, dw=DW, db=DB
 )
 def test_bwd_varlen_host_errors(kw, code):
     assert bwd_varlen(**kw) == code
+
+
+CSL = 0x60_0000_0000
+
+
+def upd_ex(x=X, state=ST, S=512, L=3, idx=IDX, cs=CSL, y=Y, N=256, D=4096, W=4, status=STATUS):
+    return cc.lib().cconv_update_ex(x, D, state, S, L, idx, cs, WT, BF16, BIAS, y, N, D, W, status, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(L=2), SHAPE),
+        (dict(L=5), SHAPE),
+        (dict(W=1, L=0), SHAPE),  # a circular state needs entries
+        (dict(state=None), NULLP),
+        (dict(cs=CSL + 2), MISAL),
+        (dict(state=ST + 16 * 0 + 8), MISAL),
+        (dict(cs=Y + 64), ALIAS),
+        (dict(cs=ST + 4096), ALIAS),
+        (dict(status=CSL), ALIAS),
+        (dict(y=CSL - 512), ALIAS),
+        (dict(L=4, state=Y - 512 * 4096 * 4 * 2 + 16), ALIAS),  # an L = 4 pool reaches further than L = 3
+    ],
+)
+def test_update_ex_host_errors(kw, code):
+    assert upd_ex(**kw) == code
+
+
+def test_update_ex_width_one_shift_needs_no_state():
+    # W = 1, L = 0, shift: no state at all; nothing to launch for N = 0
+    assert upd_ex(W=1, L=0, cs=None, state=None, N=0, status=None) == OK
