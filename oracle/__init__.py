@@ -56,6 +56,8 @@ def _load(path: Path, prec: str):
     lib.oracle_dw_channels.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, i64, f, f, f]
     lib.oracle_fwd_state.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, f, f]
     lib.oracle_bwd_state.argtypes = [f, f, f, i64, i64, i64, f, ctypes.c_int, f, f, f, f, f]
+    lib.oracle_fwd_epi.argtypes = [f, f, f, ctypes.c_int, i64, i64, i64, f, ctypes.c_int, f, f]
+    lib.oracle_bwd_epi.argtypes = [f, f, f, ctypes.c_int, i64, i64, i64, f, ctypes.c_int, f, f, f, f, f]
     lib.oracle_fwd_varlen.argtypes = [f, f, i64, i64, i64, f, ctypes.c_int, f, f, f, f]
     lib.oracle_fwd_varlen.restype = ctypes.c_int
     lib.oracle_bwd_varlen.argtypes = [f, f, f, i64, i64, i64, f, ctypes.c_int, f, f, f, f, f, f]
@@ -216,6 +218,30 @@ class Oracle:
         )
         return dx, dw, db, dh0
 
+    def fwd_epi(self, x, w, bias=None, *, h0=None, residual=None, act: bool = True, precision: str = "f64"):
+        """y = act(z) + residual (act: SiLU or none), unrounded; x [B, T, D], h0 [B, D, W-1] or None,
+        residual [B, T, D] or None."""
+        xf, hf, rf, wf, bf = _f32(x), _f32(h0), _f32(residual), _f32(w), _f32(bias)
+        B, T, D = xf.shape
+        W = wf.shape[1]
+        assert rf is None or rf.shape == xf.shape
+        y = np.empty((B, T, D), _NP[precision])
+        self.lib(precision).oracle_fwd_epi(_p(xf), _p(hf), _p(rf), int(act), B, T, D, _p(wf), W, _p(bf), _p(y))
+        return y
+
+    def bwd_epi(self, x, dy, w, bias=None, *, h0=None, act: bool = True, precision: str = "f64"):
+        """(dx, dw, dbias, dh0) of y = act(z) (+ residual, whose gradient is dy itself)."""
+        xf, hf, dyf, wf, bf = _f32(x), _f32(h0), _f32(dy), _f32(w), _f32(bias)
+        B, T, D = xf.shape
+        W = wf.shape[1]
+        dx = np.empty((B, T, D), _NP[precision])
+        dw = np.empty((D, W), _NP[precision])
+        db = np.empty((D,), _NP[precision])
+        dh0 = np.empty((B, D, W - 1), _NP[precision])
+        self.lib(precision).oracle_bwd_epi(_p(xf), _p(hf), _p(dyf), int(act), B, T, D, _p(wf), W, _p(bf), _p(dx),
+                                           _p(dw), _p(db), _p(dh0))
+        return dx, dw, db, dh0
+
     def fwd_varlen(self, x, cu_seqlens, w, bias=None, h0=None, *, precision: str = "f64"):
         """Packed batch: x [total, D], cu_seqlens [n+1]; h0 [n, D, W-1] or None. Returns
         (ok, y unrounded [total, D] or None, hT float32 [n, D, W-1] or None)."""
@@ -360,6 +386,8 @@ dw_channels = _default.dw_channels
 update = _default.update
 fwd_pool = _default.fwd_pool
 update_ex = _default.update_ex
+fwd_epi = _default.fwd_epi
+bwd_epi = _default.bwd_epi
 fwd_varlen = _default.fwd_varlen
 bwd_varlen = _default.bwd_varlen
 fwd_state = _default.fwd_state

@@ -32,6 +32,8 @@
  *    output_final_state]: an optional h0 [B, D, W-1], oldest first (the decode state layout),
  *    replaces the zero history before t = 0; the final state is the last W-1 values of the
  *    extended sequence; the history's gradient is dx at the W-1 virtual rows before t = 0.
+ *  - Epilogue. [kernel-fun wheel, _common/compat.py: fla's activation and residual]: without an
+ *    activation y = z (and g = dy); a residual is added to the output after the activation.
  *  - Packed batches. [kernel-fun wheel, _common/compat.py: fla's cu_seqlens]: sequences of
  *    different lengths packed along time; offsets cu[0] = 0 <= cu[1] <= ... <= cu[n] = total
  *    mark sequence i as rows cu[i] .. cu[i+1]-1; every sequence has its own zero (or given)
@@ -93,11 +95,13 @@ static real z_at(const float* x, const float* h0, int64_t T, int64_t D, const fl
     return z;
 }
 
-/* g[b, t, d] = dy * d silu/dz = dy * s * (1 + z*(1-s)), s = sigma(z); zero outside 0 <= t < T. */
+/* g[b, t, d] = dy * dy/dz: with SiLU (act = 1) dy * s * (1 + z*(1-s)), s = sigma(z); without an
+ * activation (act = 0, y = z) dy itself; zero outside 0 <= t < T. */
 static real g_at(const float* x, const float* h0, const float* dy, int64_t T, int64_t D, const float* w, int W,
-                 const float* bias, int64_t b, int64_t t, int64_t d) {
+                 const float* bias, int64_t b, int64_t t, int64_t d, int act) {
     if (t < 0 || t >= T) return 0;
     real z = z_at(x, h0, T, D, w, W, bias, b, t, d);
+    if (!act) return (real)dy[(b * T + t) * D + d];
     real s = sigmoid(z);
     return (real)dy[(b * T + t) * D + d] * s * ((real)1 + z * ((real)1 - s));
 }
@@ -105,29 +109,29 @@ static real g_at(const float* x, const float* h0, const float* dy, int64_t T, in
 /* dx[b, u, d] = sum_{j=0}^{W-1} w[d, j] * g[b, u+(W-1)-j, d]; for -(W-1) <= u < 0 this is the
  * gradient of the history value at u (the initial state's gradient). */
 static real dx_at(const float* x, const float* h0, const float* dy, int64_t T, int64_t D, const float* w, int W,
-                  const float* bias, int64_t b, int64_t u, int64_t d) {
+                  const float* bias, int64_t b, int64_t u, int64_t d, int act) {
     real acc = 0;
     for (int j = 0; j < W; ++j)
-        acc = acc + (real)w[d * W + j] * g_at(x, h0, dy, T, D, w, W, bias, b, u + (W - 1) - j, d);
+        acc = acc + (real)w[d * W + j] * g_at(x, h0, dy, T, D, w, W, bias, b, u + (W - 1) - j, d, act);
     return acc;
 }
 
 /* dw[d, j] = sum_b sum_t g[b, t, d] * X[b, t-(W-1)+j, d]. */
 static real dw_at(const float* x, const float* h0, const float* dy, int64_t B, int64_t T, int64_t D,
-                  const float* w, int W, const float* bias, int64_t d, int j) {
+                  const float* w, int W, const float* bias, int64_t d, int j, int act) {
     real acc = 0;
     for (int64_t b = 0; b < B; ++b)
         for (int64_t t = 0; t < T; ++t)
-            acc = acc + g_at(x, h0, dy, T, D, w, W, bias, b, t, d) * xval(x, h0, T, D, W, b, t - (W - 1) + j, d);
+            acc = acc + g_at(x, h0, dy, T, D, w, W, bias, b, t, d, act) * xval(x, h0, T, D, W, b, t - (W - 1) + j, d);
     return acc;
 }
 
 /* dbias[d] = sum_b sum_t g[b, t, d]. */
 static real dbias_at(const float* x, const float* h0, const float* dy, int64_t B, int64_t T, int64_t D,
-                     const float* w, int W, const float* bias, int64_t d) {
+                     const float* w, int W, const float* bias, int64_t d, int act) {
     real acc = 0;
     for (int64_t b = 0; b < B; ++b)
-        for (int64_t t = 0; t < T; ++t) acc = acc + g_at(x, h0, dy, T, D, w, W, bias, b, t, d);
+        for (int64_t t = 0; t < T; ++t) acc = acc + g_at(x, h0, dy, T, D, w, W, bias, b, t, d, act);
     return acc;
 }
 
@@ -170,12 +174,12 @@ void oracle_bwd(const float* x, const float* dy, int64_t B, int64_t T, int64_t D
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         int64_t b = r / T, u = r % T;
-        for (int64_t d = 0; d < D; ++d) dx_out[r * D + d] = dx_at(x, NULL, dy, T, D, w, W, bias, b, u, d);
+        for (int64_t d = 0; d < D; ++d) dx_out[r * D + d] = dx_at(x, NULL, dy, T, D, w, W, bias, b, u, d, 1);
     }
 #pragma omp parallel for schedule(static)
     for (int64_t d = 0; d < D; ++d) {
-        for (int j = 0; j < W; ++j) dw_out[d * W + j] = dw_at(x, NULL, dy, B, T, D, w, W, bias, d, j);
-        if (dbias_out) dbias_out[d] = dbias_at(x, NULL, dy, B, T, D, w, W, bias, d);
+        for (int j = 0; j < W; ++j) dw_out[d * W + j] = dw_at(x, NULL, dy, B, T, D, w, W, bias, d, j, 1);
+        if (dbias_out) dbias_out[d] = dbias_at(x, NULL, dy, B, T, D, w, W, bias, d, 1);
     }
 }
 
@@ -197,7 +201,7 @@ void oracle_dx_points(const float* x, const float* dy, int64_t B, int64_t T, int
                       const int64_t* pu, const int64_t* pd, real* dx_out) {
     (void)B;
 #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; ++i) dx_out[i] = dx_at(x, NULL, dy, T, D, w, W, bias, pb[i], pu[i], pd[i]);
+    for (int64_t i = 0; i < n; ++i) dx_out[i] = dx_at(x, NULL, dy, T, D, w, W, bias, pb[i], pu[i], pd[i], 1);
 }
 
 /* Sampled weight gradient: dw[d, :] and dbias[d] for n listed channels (full sums). */
@@ -206,8 +210,8 @@ void oracle_dw_channels(const float* x, const float* dy, int64_t B, int64_t T, i
                         real* dw_out /* [n, W] */, real* dbias_out /* [n] */) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
-        for (int j = 0; j < W; ++j) dw_out[i * W + j] = dw_at(x, NULL, dy, B, T, D, w, W, bias, pd[i], j);
-        dbias_out[i] = dbias_at(x, NULL, dy, B, T, D, w, W, bias, pd[i]);
+        for (int j = 0; j < W; ++j) dw_out[i * W + j] = dw_at(x, NULL, dy, B, T, D, w, W, bias, pd[i], j, 1);
+        dbias_out[i] = dbias_at(x, NULL, dy, B, T, D, w, W, bias, pd[i], 1);
     }
 }
 
@@ -244,18 +248,58 @@ void oracle_bwd_state(const float* x, const float* h0, const float* dy, int64_t 
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         int64_t b = r / T, u = r % T;
-        for (int64_t d = 0; d < D; ++d) dx_out[r * D + d] = dx_at(x, h0, dy, T, D, w, W, bias, b, u, d);
+        for (int64_t d = 0; d < D; ++d) dx_out[r * D + d] = dx_at(x, h0, dy, T, D, w, W, bias, b, u, d, 1);
     }
 #pragma omp parallel for schedule(static)
     for (int64_t d = 0; d < D; ++d) {
-        for (int j = 0; j < W; ++j) dw_out[d * W + j] = dw_at(x, h0, dy, B, T, D, w, W, bias, d, j);
-        if (dbias_out) dbias_out[d] = dbias_at(x, h0, dy, B, T, D, w, W, bias, d);
+        for (int j = 0; j < W; ++j) dw_out[d * W + j] = dw_at(x, h0, dy, B, T, D, w, W, bias, d, j, 1);
+        if (dbias_out) dbias_out[d] = dbias_at(x, h0, dy, B, T, D, w, W, bias, d, 1);
     }
     if (dh0_out)
         for (int64_t b = 0; b < B; ++b)
             for (int64_t d = 0; d < D; ++d)
                 for (int j = 0; j < W - 1; ++j)
-                    dh0_out[(b * D + d) * (W - 1) + j] = dx_at(x, h0, dy, T, D, w, W, bias, b, -(int64_t)(W - 1) + j, d);
+                    dh0_out[(b * D + d) * (W - 1) + j] = dx_at(x, h0, dy, T, D, w, W, bias, b, -(int64_t)(W - 1) + j, d, 1);
+}
+
+/* The epilogue variants of fla's parameter list: act = 0 drops the activation (y = z, so g = dy);
+ * a residual r [B, T, D] (NULL: none) is added to the output after the activation (its own
+ * gradient is dy, nothing to compute). History h0 as in oracle_fwd_state. */
+void oracle_fwd_epi(const float* x, const float* h0, const float* r, int act, int64_t B, int64_t T, int64_t D,
+                    const float* w, int W, const float* bias, real* y_out) {
+    int64_t rows = B * T;
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < rows; ++q) {
+        int64_t b = q / T, t = q % T;
+        for (int64_t d = 0; d < D; ++d) {
+            real z = z_at(x, h0, T, D, w, W, bias, b, t, d);
+            real y = act ? z * sigmoid(z) : z;
+            if (r) y = y + (real)r[q * D + d];
+            y_out[q * D + d] = y;
+        }
+    }
+}
+
+void oracle_bwd_epi(const float* x, const float* h0, const float* dy, int act, int64_t B, int64_t T, int64_t D,
+                    const float* w, int W, const float* bias, real* dx_out, real* dw_out, real* dbias_out,
+                    real* dh0_out) {
+    int64_t rows = B * T;
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < rows; ++q) {
+        int64_t b = q / T, u = q % T;
+        for (int64_t d = 0; d < D; ++d) dx_out[q * D + d] = dx_at(x, h0, dy, T, D, w, W, bias, b, u, d, act);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t d = 0; d < D; ++d) {
+        for (int j = 0; j < W; ++j) dw_out[d * W + j] = dw_at(x, h0, dy, B, T, D, w, W, bias, d, j, act);
+        if (dbias_out) dbias_out[d] = dbias_at(x, h0, dy, B, T, D, w, W, bias, d, act);
+    }
+    if (dh0_out)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t d = 0; d < D; ++d)
+                for (int j = 0; j < W - 1; ++j)
+                    dh0_out[(b * D + d) * (W - 1) + j] =
+                        dx_at(x, h0, dy, T, D, w, W, bias, b, -(int64_t)(W - 1) + j, d, act);
 }
 
 /*

@@ -737,6 +737,48 @@ def check_update_ex_validation(orc):
     assert ok
 
 
+def check_epilogue_torch(orc):
+    """float64 torch conv1d over [history; x], then no activation or SiLU, plus a residual after
+    it, with autograd: y, dx, history gradient, dw, dbias; the residual's gradient is dy."""
+    for W in (1, 2, 4):
+        for act in (False, True):
+            for with_res in (False, True):
+                x, h0, w, b, dy = _problem_h0(600 + W + 2 * act + with_res, 2, 9, 5, W)
+                rng = np.random.default_rng(610 + W)
+                r = _bf16_values(rng, x.shape) if with_res else None
+                B, T, D = x.shape
+                xe = torch.cat([torch.tensor(h0, dtype=torch.float64).permute(0, 2, 1),
+                                torch.tensor(x, dtype=torch.float64)], 1).requires_grad_(True)
+                wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+                bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+                rt = torch.tensor(r, dtype=torch.float64, requires_grad=True) if with_res else None
+                z = F.conv1d(xe.transpose(1, 2), wt[:, None, :], bt, padding=0, groups=D).transpose(1, 2)
+                yt = F.silu(z) if act else z
+                if with_res:
+                    yt = yt + rt
+                (yt * torch.tensor(dy, dtype=torch.float64)).sum().backward()
+                what = f"W={W} act={act} residual={with_res}"
+                y = orc.fwd_epi(x, w, b, h0=h0, residual=r, act=act)
+                _close(y, yt.detach().numpy(), 1e-12, 1e-14, what=f"epilogue y {what}")
+                dx, dw, db, dh0 = orc.bwd_epi(x, dy, w, b, h0=h0, act=act)
+                g = xe.grad.numpy()
+                _close(dx, g[:, W - 1:], 1e-12, 1e-13, what=f"epilogue dx {what}")
+                _close(dh0, g[:, :W - 1].transpose(0, 2, 1), 1e-12, 1e-13, what=f"epilogue dh0 {what}")
+                _close(dw, wt.grad.numpy(), 1e-12, 1e-12, what=f"epilogue dw {what}")
+                _close(db, bt.grad.numpy(), 1e-12, 1e-12, what=f"epilogue dbias {what}")
+                if with_res:
+                    assert np.array_equal(rt.grad.numpy(), dy.astype(np.float64)), "residual gradient"
+
+
+def check_epilogue_default_is_plain(orc):
+    """SiLU without a residual is the history forward and backward, bit for bit."""
+    x, h0, w, b, dy = _problem_h0(620, 2, 13, 6, 4)
+    y, _ = orc.fwd_state(x, h0, w, b)
+    assert np.array_equal(orc.fwd_epi(x, w, b, h0=h0), y)
+    for a, c in zip(orc.bwd_epi(x, dy, w, b, h0=h0), orc.bwd_state(x, h0, dy, w, b)):
+        assert np.array_equal(a, c)
+
+
 ALL_CHECKS = [
     check_rounding_matches_torch,
     check_rounding_from_double_is_direct,
@@ -770,4 +812,6 @@ ALL_CHECKS = [
     check_update_ex_decode_equals_forward,
     check_update_ex_oldest_entry_unused,
     check_update_ex_validation,
+    check_epilogue_torch,
+    check_epilogue_default_is_plain,
 ]

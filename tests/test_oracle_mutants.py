@@ -21,7 +21,7 @@ MUTANTS = [
     ("sigmoid_sign", "r_exp(-z)", "r_exp(z)"),
     ("dsilu_sign", "s * ((real)1 + z * ((real)1 - s))", "s * ((real)1 - z * ((real)1 - s))"),
     ("dsilu_dy_dropped", "return (real)dy[(b * T + t) * D + d] * s *", "return s *"),
-    ("dx_index", "g_at(x, h0, dy, T, D, w, W, bias, b, u + (W - 1) - j, d)", "g_at(x, h0, dy, T, D, w, W, bias, b, u + j, d)"),
+    ("dx_index", "g_at(x, h0, dy, T, D, w, W, bias, b, u + (W - 1) - j, d,", "g_at(x, h0, dy, T, D, w, W, bias, b, u + j, d,"),
     ("dx_tap_transposed", "acc = acc + (real)w[d * W + j] * g_at", "acc = acc + (real)w[d * W + (W - 1 - j)] * g_at"),
     ("dw_index", "* xval(x, h0, T, D, W, b, t - (W - 1) + j, d);\n    return acc;", "* xval(x, h0, T, D, W, b, t - j, d);\n    return acc;"),
     ("dbias_skips_head", "for (int64_t t = 0; t < T; ++t) acc = acc + g_at", "for (int64_t t = W - 1; t < T; ++t) acc = acc + g_at"),
@@ -39,7 +39,7 @@ MUTANTS = [
     ("history_reversed", "h0[(b * D + d) * (W - 1) + (t + W - 1)]", "h0[(b * D + d) * (W - 1) + (-1 - t)]"),
     ("history_ignored", "if (h0 && t >= -(int64_t)(W - 1))", "if (0)"),
     ("final_state_off_by_one", "xval(x, h0, T, D, W, b, T - (W - 1) + j, d)", "xval(x, h0, T, D, W, b, T - W + j, d)"),
-    ("history_grad_shifted", "b, -(int64_t)(W - 1) + j, d)", "b, -(int64_t)(W - 1) + j + 1, d)"),
+    ("history_grad_shifted", "b, -(int64_t)(W - 1) + j, d, 1)", "b, -(int64_t)(W - 1) + j + 1, d, 1)"),
     ("varlen_end_unchecked", "if (cu[0] != 0 || (int64_t)cu[n] != total) return 0;", "if (cu[0] != 0) return 0;"),
     ("varlen_history_of_next", "oracle_fwd_state(x + a * D, h0 ? h0 + i * D * L : NULL", "oracle_fwd_state(x + a * D, h0 ? h0 + ((i + 1) % n) * D * L : NULL"),
     ("varlen_rows_shifted", "oracle_fwd_state(x + a * D,", "oracle_fwd_state(x + (a > 0 ? a - 1 : 0) * D,"),
@@ -48,6 +48,9 @@ MUTANTS = [
     ("ring_read_reversed", "((c - k) % L + L) % L", "((c + k) % L + L) % L"),
     ("ex_shift_reads_oldest", "cache_seqlens ? ((c - k) % L + L) % L : L - k;", "cache_seqlens ? ((c - k) % L + L) % L : (L - k) % (W - 1);"),
     ("ex_negative_seqlen_accepted", "if (cache_seqlens[n] < 0) return 1;", "(void)n;"),
+    ("linear_keeps_silu", "real y = act ? z * sigmoid(z) : z;", "real y = z * sigmoid(z);"),
+    ("linear_grad_dsilu", "if (!act) return (real)dy[(b * T + t) * D + d];", "(void)act;"),
+    ("residual_before_activation", "real y = act ? z * sigmoid(z) : z;\n            if (r) y = y + (real)r[q * D + d];", "if (r) z = z + (real)r[q * D + d];\n            real y = act ? z * sigmoid(z) : z;"),
     ("round_half_away", "nearbyint(a / q)", "floor(a / q + 0.5)"),
     ("round_truncate", "nearbyint(a / q)", "trunc(a / q)"),
 ]
