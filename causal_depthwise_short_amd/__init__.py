@@ -26,6 +26,10 @@ __all__ = [
     "cconv_fwd_state",
     "cconv_bwd_state",
     "cconv_fwd_pool",
+    "cconv_fwd_ex",
+    "cconv_bwd_ex",
+    "FwdOpts",
+    "BwdOpts",
     "cconv_fwd_varlen",
     "cconv_bwd_varlen",
     "cconv_bwd_workspace_bytes",
@@ -93,6 +97,38 @@ _lib = None
 _roof = None
 
 
+class FwdOpts(ctypes.Structure):
+    """cconv_fwd_opts_t."""
+
+    _fields_ = [
+        ("activation", ctypes.c_int),
+        ("residual", ctypes.c_void_p),
+        ("residual_sb", ctypes.c_int64),
+        ("residual_st", ctypes.c_int64),
+        ("init_state", ctypes.c_void_p),
+        ("final_state", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("nseq", ctypes.c_int64),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+class BwdOpts(ctypes.Structure):
+    """cconv_bwd_opts_t."""
+
+    _fields_ = [
+        ("activation", ctypes.c_int),
+        ("init_state", ctypes.c_void_p),
+        ("d_init_state", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("nseq", ctypes.c_int64),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+ACTIVATIONS = {"silu": 1, "swish": 1, None: 0, "none": 0}
+
+
 def _declare(L):
     p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.cconv_fwd.argtypes = [p, i64, i64, p, i32, p, p, i64, i64, i64, i32, p]
@@ -110,6 +146,11 @@ def _declare(L):
     L.cconv_bwd_config.restype = i32
     L.cconv_fwd_state.argtypes = [p, i64, i64, p, i32, p, p, p, p, i64, i64, i64, i32, p]
     L.cconv_fwd_state.restype = i32
+    L.cconv_fwd_ex.argtypes = [p, i64, i64, p, i32, p, p, i64, i64, i64, i32, ctypes.POINTER(FwdOpts), p]
+    L.cconv_fwd_ex.restype = i32
+    L.cconv_bwd_ex.argtypes = [p, i64, i64, p, i64, i64, p, i32, p, p, p, i32, p, p, sz, i64, i64, i64, i32,
+                               ctypes.POINTER(BwdOpts), p]
+    L.cconv_bwd_ex.restype = i32
     L.cconv_fwd_pool.argtypes = [p, i64, i64, p, i32, p, p, i64, p, p, p, p, i64, i64, i64, i32, p]
     L.cconv_fwd_pool.restype = i32
     L.cconv_fwd_varlen.argtypes = [p, i64, p, i64, i64, p, i32, p, p, p, p, p, i64, i32, p]
@@ -654,3 +695,107 @@ def cconv_update_ex(x, state, state_indices, w, bias=None, *, cache_seqlens=None
         "cconv_update_ex",
     )
     return y, status
+
+
+def _rows(t, name: str, packed: bool):
+    """(batch stride, row stride) of a bf16 activation: [B, T, D], or [total, D] when packed."""
+    if packed:
+        return 0, _packed(t, name)
+    return _act(t, name)
+
+
+def cconv_fwd_ex(x, w, bias=None, *, activation="silu", residual=None, init_state=None, final_state=None,
+                 want_final_state=False, cu_seqlens=None, y=None, status=None, stream=None):
+    """The general forward: y = act(conv(x) + bias) + residual, optionally from a history, with
+    a final state, over a [B, T, D] batch or (cu_seqlens) a packed [total, D] batch. Returns
+    (y, final_state, status); status is None for fixed-length batches."""
+    packed = cu_seqlens is not None
+    sb, st = _rows(x, "x", packed)
+    if packed:
+        B, (T, D) = 1, x.shape
+        n = _offsets(cu_seqlens, w.shape[1], D, init_state, x.device)
+        state_rows = n
+    else:
+        B, T, D = x.shape
+        state_rows = B
+        _state(init_state, "init_state", B, D, w.shape[1])
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(k for k in ACTIVATIONS if k)} or None")
+    rsb = rst = 0
+    if residual is not None:
+        if tuple(residual.shape) != tuple(x.shape):
+            raise ValueError("residual must have x's shape")
+        rsb, rst = _rows(residual, "residual", packed)
+    if want_final_state and final_state is None:
+        final_state = torch.empty((state_rows, D, W - 1), dtype=torch.bfloat16, device=x.device)
+    _state(final_state, "final_state", state_rows, D, W)
+    if y is None:
+        y = torch.empty(tuple(x.shape), dtype=torch.bfloat16, device=x.device)
+    elif y.dtype != torch.bfloat16 or tuple(y.shape) != tuple(x.shape) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous bf16 tensor of x's shape")
+    if packed and status is None:
+        status = torch.empty(1, dtype=torch.int32, device=x.device)
+    o = FwdOpts(ACTIVATIONS[activation], _ptr(residual), rsb, rst, _ptr(init_state), _ptr(final_state),
+                _ptr(cu_seqlens), state_rows if packed else 0, _ptr(status) if packed else None)
+    _check(lib().cconv_fwd_ex(_ptr(x), sb, st, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(y), B, T, D, W,
+                              ctypes.byref(o), _stream(stream)), "cconv_fwd_ex")
+    return y, final_state, status
+
+
+def cconv_bwd_ex(x, dy, w, bias=None, *, activation="silu", init_state=None, d_init_state=None,
+                 want_d_init_state=False, cu_seqlens=None, dx=None, dw=None, dbias=None, want_dbias=True,
+                 dw_dtype=None, workspace=None, status=None, stream=None):
+    """The general backward (see cconv_fwd_ex; a residual's gradient is dy itself). Returns
+    (dx, dw, dbias, d_init_state, status)."""
+    packed = cu_seqlens is not None
+    sb, st = _rows(x, "x", packed)
+    dsb, dst = _rows(dy, "dy", packed)
+    if tuple(dy.shape) != tuple(x.shape):
+        raise ValueError("dy must have x's shape")
+    _dev(w, "w")
+    W = w.shape[1]
+    if packed:
+        B, (T, D) = 1, x.shape
+        state_rows = _offsets(cu_seqlens, W, D, init_state, x.device)
+    else:
+        B, T, D = x.shape
+        state_rows = B
+        _state(init_state, "init_state", B, D, W)
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(k for k in ACTIVATIONS if k)} or None")
+    dev = x.device
+    if dx is None:
+        dx = torch.empty(tuple(x.shape), dtype=torch.bfloat16, device=dev)
+    if dw is None:
+        dw = torch.empty((D, W), dtype=dw_dtype or w.dtype, device=dev)
+    if want_dbias and dbias is None:
+        dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    if want_d_init_state and d_init_state is None:
+        d_init_state = torch.empty((state_rows, D, W - 1), dtype=torch.bfloat16, device=dev)
+    _state(d_init_state, "d_init_state", state_rows, D, W)
+    need = cconv_bwd_workspace_bytes(B, T, D, W)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if packed and status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    o = BwdOpts(ACTIVATIONS[activation], _ptr(init_state), _ptr(d_init_state), _ptr(cu_seqlens),
+                state_rows if packed else 0, _ptr(status) if packed else None)
+    _check(lib().cconv_bwd_ex(_ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(dx),
+                              _ptr(dw), _wdt(dw, "dw"), _ptr(dbias), _ptr(workspace), ws_bytes, B, T, D, W,
+                              ctypes.byref(o), _stream(stream)), "cconv_bwd_ex")
+    return dx, dw, dbias, d_init_state, status

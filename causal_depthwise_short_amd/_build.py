@@ -32,7 +32,10 @@ CFLAGS = [
 ]
 
 LIBS = {
-    "libcconv.so": ["cconv_api.hip", "cconv_fwd.hip", "cconv_bwd.hip", "cconv_update.hip", "cconv_seq.hip"],
+    "libcconv.so": [
+        "cconv_api.hip", "cconv_fwd.hip", "cconv_fwd_extra.hip", "cconv_bwd.hip", "cconv_bwd_extra.hip",
+        "cconv_update.hip", "cconv_seq.hip",
+    ],
     "libcconv_roofline.so": ["roofline_copy.hip"],
 }
 

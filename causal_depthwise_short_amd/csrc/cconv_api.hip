@@ -150,6 +150,10 @@ struct Extra {
     const uint8_t* has_init = nullptr;  // kPool
     const int32_t* cu = nullptr;        // kPacked
     int32_t* status = nullptr;          // kPool, kPacked
+    // epilogue: no activation (y = z; the backward's g = dy), and the forward's residual
+    bool linear = false;
+    const void* r = nullptr;
+    int64_t r_sb = 0, r_st = 0;
 };
 
 // Checks of the states and of the pool/packed metadata against the call's other operands.
@@ -218,19 +222,24 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     if (!aligned(y, 16)) return CCONV_ERR_MISALIGNED;
     const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
-    if (ex.mode == kPacked && (c.options & ~cconv::kSolo) != cconv::kVarlenFwdOptions) return CCONV_ERR_BAD_CONFIG;
+    const int epi = (ex.linear ? cconv::kLinear : 0) | (ex.r ? cconv::kResidual : 0);
+    if (!cconv::fwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
+        return CCONV_ERR_BAD_CONFIG;
+    if (ex.r && (st = check_act(ex.r, ex.r_sb, ex.r_st, D)) != CCONV_OK) return st;
     const Span sy = span(y, extent3(B, T, D, T * D, D, 2));
     const Span sx = span(x, extent3(B, T, D, x_sb, x_st, 2));
     const Span sw = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
     const Span sb = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
-    if (overlap(sy, sx) || overlap(sy, sw) || overlap(sy, sb)) return CCONV_ERR_ALIASING;
+    const Span sr = ex.r ? span(ex.r, extent3(B, T, D, ex.r_sb, ex.r_st, 2)) : Span{0, 0};
+    if (overlap(sy, sx) || overlap(sy, sw) || overlap(sy, sb) || overlap(sy, sr)) return CCONV_ERR_ALIASING;
     // history in, final state out (W == 1 has none)
     if (W == 1) ex.h0 = ex.out = nullptr;
-    const Span ins[3] = {sx, sw, sb};
+    const Span ins[4] = {sx, sw, sb, sr};
     Span sh0;
-    if ((st = check_extra(ex, B, D, W, true, ins, 3, &sy, 1, &sh0)) != CCONV_OK) return st;
+    if ((st = check_extra(ex, B, D, W, true, ins, 4, &sy, 1, &sh0)) != CCONV_OK) return st;
     Plan p;
     if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
+    p.options |= epi;
     // a per-sequence or pool final state needs at least one token
     if (ex.out && ex.mode != kPacked && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -251,6 +260,9 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     a.status = ex.status;
     a.cu = ex.cu;
     a.nseq = ex.mode == kPacked ? ex.rows : 0;
+    a.r = static_cast<const uint16_t*>(ex.r);
+    a.r_sb = ex.r_sb;
+    a.r_st = ex.r_st;
     a.B = B;
     a.T = T;
     a.D = D;
@@ -295,9 +307,12 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     if (!aligned(dx, 16) || !aligned(dw, 16) || (dbias && !aligned(dbias, 16))) return CCONV_ERR_MISALIGNED;
     const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W);
     if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
-    if (ex.mode == kPacked && (c.options & ~cconv::kSolo) != cconv::kVarlenBwdOptions) return CCONV_ERR_BAD_CONFIG;
+    const int epi = ex.linear ? cconv::kLinear : 0;
+    if (!cconv::bwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
+        return CCONV_ERR_BAD_CONFIG;
     Plan p;
     if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
+    p.options |= epi;
     const size_t need = (B == 0 || T == 0 || D == 0) ? 0 : bwd_workspace(p, D, W);
     if (need > 0 && (!workspace || !aligned(workspace, 16))) return workspace ? CCONV_ERR_MISALIGNED : CCONV_ERR_NULL_POINTER;
 
@@ -517,6 +532,54 @@ cconv_status_t cconv_bwd_state(const void* x, int64_t x_sb, int64_t x_st, const 
     Extra ex;
     ex.h0 = init_state;
     ex.out = d_init_state;
+    return bwd_impl(kMain | kFinish, x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias,
+                    workspace, workspace_bytes, B, T, D, W, nullptr, stream, ex);
+}
+
+cconv_status_t cconv_fwd_ex(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
+                            const float* bias, void* y, int64_t B, int64_t T, int64_t D, int W,
+                            const cconv_fwd_opts_t* o, cconv_stream_t stream) {
+    Extra ex;
+    if (o) {
+        if (o->activation != CCONV_ACT_SILU && o->activation != CCONV_ACT_NONE) return CCONV_ERR_BAD_CONFIG;
+        ex.linear = (o->activation == CCONV_ACT_NONE);
+        ex.r = o->residual;
+        ex.r_sb = o->residual_sb;
+        ex.r_st = o->residual_st;
+        if (o->cu_seqlens) {
+            if (B != 1) return CCONV_ERR_BAD_SHAPE;
+            const cconv_status_t st =
+                packed_extra(o->cu_seqlens, o->nseq, T, o->init_state, o->final_state, o->status, &ex);
+            if (st != CCONV_OK) return st;
+            x_sb = 0;
+            ex.r_sb = 0;
+        } else {
+            ex.h0 = o->init_state;
+            ex.out = o->final_state;
+        }
+    }
+    return fwd_impl(x, x_sb, x_st, w, w_dtype, bias, y, B, T, D, W, nullptr, stream, ex);
+}
+
+cconv_status_t cconv_bwd_ex(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb, int64_t dy_st,
+                            const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
+                            cconv_dtype_t dw_dtype, float* dbias, void* workspace, size_t workspace_bytes, int64_t B,
+                            int64_t T, int64_t D, int W, const cconv_bwd_opts_t* o, cconv_stream_t stream) {
+    Extra ex;
+    if (o) {
+        if (o->activation != CCONV_ACT_SILU && o->activation != CCONV_ACT_NONE) return CCONV_ERR_BAD_CONFIG;
+        ex.linear = (o->activation == CCONV_ACT_NONE);
+        if (o->cu_seqlens) {
+            if (B != 1) return CCONV_ERR_BAD_SHAPE;
+            const cconv_status_t st =
+                packed_extra(o->cu_seqlens, o->nseq, T, o->init_state, o->d_init_state, o->status, &ex);
+            if (st != CCONV_OK) return st;
+            x_sb = dy_sb = 0;
+        } else {
+            ex.h0 = o->init_state;
+            ex.out = o->d_init_state;
+        }
+    }
     return bwd_impl(kMain | kFinish, x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias,
                     workspace, workspace_bytes, B, T, D, W, nullptr, stream, ex);
 }

@@ -1,328 +1,9 @@
-// cconv_bwd.hip -- backward of the depthwise causal short convolution + SiLU on gfx950.
-//
-// Same decomposition as the forward (lane = VEC channels, wave = channel strip x time
-// segment x batch row). Each row recomputes z from the x ring (the forward is never re-run),
-// forms g = dy * s * (1 + z(1-s)), s = sigmoid(z) [strip.py: `_dsilu`], accumulates the tap
-// gradients dw_k += g[t] * x[t-k] and dbias += g[t] in fp32, and keeps the W-1 previous
-// rows of g in a second ring: dx[u] = sum_k w[:, W-1-k] * g[u+k] is complete W-1 rows after u
-// [strip.py: `_bwd4` docstring]. A segment does not own dx for its first W-1 rows' lag
-// window: the previous segment finishes those from a right halo of W-1 rows whose g it
-// recomputes without accumulating dw [strip.py: `cconv_bwd_strip` halo].
-//
-// dw/dbias partials: the waves of a block (consecutive segments of one strip and batch row)
-// are summed through LDS in wave order, and the block writes one fp32 partial row
-// [W+1][D] (columns 0..W-1 dw, column W dbias). A second kernel sums the partials over
-// blocks in a fixed order and casts dw to its dtype [strip.py: host `cconv_bwd`, the
-// deterministic reduction with no atomics]. Both orders are fixed, so dw/dbias are bitwise
-// reproducible.
-#include "cconv_device.hpp"
-#include "cconv_internal.hpp"
+// cconv_bwd.hip -- the plain backward in every launch variant, the backward's dispatch, and
+// the fixed-order reduction of the dw/dbias partials. Packed batches and the variant without
+// an activation are instantiated in cconv_bwd_extra.hip.
+#include "cconv_bwd_body.hpp"
 
 namespace cconv {
-
-// One backward row t. `acc_on`: the row belongs to this segment (accumulate dw/dbias);
-// `emit`: dx of row t-(W-1) is this segment's and gets stored.
-template <int VEC, int W, bool NTS>
-__device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float (&b)[VEC],
-                                        const Row<VEC>& rx, const Row<VEC>& rdy,
-                                        float (&xr)[W > 1 ? W - 1 : 1][VEC],
-                                        float (&gr)[W > 1 ? W - 1 : 1][VEC], float (&acc)[W][VEC],
-                                        float (&db)[VEC], bool acc_on, bool emit,
-                                        uint16_t* __restrict__ dxrow, uint32_t lo, uint16_t* hist_grad = nullptr,
-                                        int64_t hb = 0, int64_t D = 0, int64_t d = 0, int hj = 0) {
-    float xt[VEC], dyt[VEC], g[VEC];
-    widen(rx, xt);
-    widen(rdy, dyt);
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-        // g = dy * s * (1 + z(1-s)) as a + a*m with a = dy*s and m = z - z*s: three VALU ops
-        const float z = conv_z<VEC, W>(tap, b, xt, xr, v);
-        const float s = sigmoid(z);
-        const float a = dyt[v] * s;
-        g[v] = __builtin_fmaf(a, __builtin_fmaf(-z, s, z), a);
-    }
-    if (acc_on) {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            acc[0][v] = __builtin_fmaf(g[v], xt[v], acc[0][v]);
-#pragma unroll
-            for (int k = 1; k < W; ++k) acc[k][v] = __builtin_fmaf(g[v], xr[k - 1][v], acc[k][v]);
-            db[v] += g[v];
-        }
-    }
-    if (emit) {
-        // dx[u], u = t-(W-1): sum over k ascending of tap[k] * g[u+k]; g[u+k] is g (k = W-1)
-        // or the ring entry gr[W-2-k] = g[t-(W-1-k)].
-        float dx[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            float s = tap[0][v] * (W == 1 ? g[v] : gr[W > 1 ? W - 2 : 0][v]);
-#pragma unroll
-            for (int k = 1; k < W; ++k) s = __builtin_fmaf(tap[k][v], k == W - 1 ? g[v] : gr[W - 2 - k][v], s);
-            dx[v] = s;
-        }
-        if (hist_grad) {  // a row before t = 0: the history's gradient, slot hj of [B, D, W-1]
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) store_state_bf16(hist_grad, hb, D, d + v, W - 1, hj, dx[v]);
-        } else {
-            store_row<VEC, NTS>(at(dxrow, lo), narrow<VEC>(dx));
-        }
-    }
-#pragma unroll
-    for (int k = W - 2; k > 0; --k)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            xr[k][v] = xr[k - 1][v];
-            gr[k][v] = gr[k - 1][v];
-        }
-    if constexpr (W > 1) {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            xr[0][v] = xt[v];
-            gr[0][v] = g[v];
-        }
-    }
-}
-
-// Where a run's dx rows go. Row u's dx is emitted when row u+W-1 is processed. Rows u >= own
-// are this wave's; with hg set (the wave holds the sequence's first row), the W-1 rows before
-// `start` give the history gradient of state row s instead.
-struct DxSink {
-    uint16_t* dxb;
-    int64_t dxs;
-    uint32_t lo;
-    int64_t own, start;
-    uint16_t* hg;
-    int64_t s, D, d;
-};
-
-// One row t of a run. GEN: the general emission rule (the first W-1 rows of a run, the tail
-// and the halo); otherwise row t-(W-1) is known to be this wave's own dx row.
-template <int VEC, int W, bool NTS, bool GEN>
-__device__ __forceinline__ void bwd_step(const float (&tap)[W][VEC], const float (&bs)[VEC], const Row<VEC>& rx,
-                                         const Row<VEC>& rdy, float (&xr)[W > 1 ? W - 1 : 1][VEC],
-                                         float (&gr)[W > 1 ? W - 1 : 1][VEC], float (&acc)[W][VEC], float (&db)[VEC],
-                                         const DxSink& k, int64_t t, bool acc_on) {
-    const int64_t u = t - (W - 1);
-    if constexpr (GEN) {
-        const bool emit = u >= k.own || (k.hg && u >= k.start - (W - 1));
-        bwd_row<VEC, W, NTS>(tap, bs, rx, rdy, xr, gr, acc, db, acc_on, emit, k.dxb + u * k.dxs, k.lo,
-                             u < k.start ? k.hg : nullptr, k.s, k.D, k.d, static_cast<int>(u - k.start + (W - 1)));
-    } else {
-        bwd_row<VEC, W, NTS>(tap, bs, rx, rdy, xr, gr, acc, db, acc_on, true, k.dxb + u * k.dxs, k.lo);
-    }
-}
-
-// Rows [t, e) of one sequence, t being the first row whose dx this wave owns in it (k.own).
-// Only the first G >= W-1 rows can emit a row before k.own, so the first group takes the
-// general rule and the steady loop none. With PF the next group's x and dy loads are in
-// flight while a group is computed (look-ahead clamped into [t, e)).
-template <int VEC, int G, int W, bool NTL, bool NTS, bool PF>
-__device__ __forceinline__ void bwd_run(const float (&tap)[W][VEC], const float (&bs)[VEC],
-                                        float (&xr)[W > 1 ? W - 1 : 1][VEC], float (&gr)[W > 1 ? W - 1 : 1][VEC],
-                                        float (&acc)[W][VEC], float (&db)[VEC], const uint16_t* __restrict__ xb,
-                                        int64_t xs, const uint16_t* __restrict__ dyb, int64_t dys, const DxSink& k,
-                                        int64_t t, const int64_t e) {
-    static_assert(G >= W - 1, "the first group must cover the rows that need the general rule");
-    const uint32_t lo = k.lo;
-    if constexpr (PF) {
-        if (t + G <= e) {
-            Row<VEC> cx[G], cdy[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) cx[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
-#pragma unroll
-            for (int g = 0; g < G; ++g) cdy[g] = load_row<VEC, NTL>(at(dyb + (t + g) * dys, lo));
-            bool head = true;
-            for (; t + G <= e; t += G) {
-                Row<VEC> nx[G], ndy[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) nx[g] = load_row<VEC, NTL>(at(xb + min(t + G + g, e - 1) * xs, lo));
-#pragma unroll
-                for (int g = 0; g < G; ++g) ndy[g] = load_row<VEC, NTL>(at(dyb + min(t + G + g, e - 1) * dys, lo));
-                if (head) {
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        bwd_step<VEC, W, NTS, true>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, k, t + g, true);
-                    head = false;
-                } else {
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        bwd_step<VEC, W, NTS, false>(tap, bs, cx[g], cdy[g], xr, gr, acc, db, k, t + g, true);
-                }
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    cx[g] = nx[g];
-                    cdy[g] = ndy[g];
-                }
-            }
-        }
-    } else {
-        bool head = true;
-        for (; t + G <= e; t += G) {
-            Row<VEC> rx[G], rdy[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
-#pragma unroll
-            for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC, NTL>(at(dyb + (t + g) * dys, lo));
-            if (head) {
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    bwd_step<VEC, W, NTS, true>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, k, t + g, true);
-                head = false;
-            } else {
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    bwd_step<VEC, W, NTS, false>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, k, t + g, true);
-            }
-        }
-    }
-    for (; t < e; ++t)
-        bwd_step<VEC, W, NTS, true>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)),
-                                    load_row<VEC, NTL>(at(dyb + t * dys, lo)), xr, gr, acc, db, k, t, true);
-}
-
-// The halo after a run ending at row e: rows e .. e+W-2 finish dx of the run's last W-1 rows.
-// Rows before the sequence end are read (the next segment's first rows: g only, no dw); rows
-// at or past it have g = 0 for this sequence.
-template <int VEC, int W, bool NTS>
-__device__ __forceinline__ void bwd_halo(const float (&tap)[W][VEC], const float (&bs)[VEC],
-                                         float (&xr)[W > 1 ? W - 1 : 1][VEC], float (&gr)[W > 1 ? W - 1 : 1][VEC],
-                                         float (&acc)[W][VEC], float (&db)[VEC], const uint16_t* __restrict__ xb,
-                                         int64_t xs, const uint16_t* __restrict__ dyb, int64_t dys, const DxSink& k,
-                                         int64_t e, int64_t end) {
-#pragma unroll
-    for (int h = 0; h < W - 1; ++h) {
-        const int64_t th = e + h;
-        Row<VEC> hx = zero_row<VEC>(), hdy = zero_row<VEC>();
-        if (th < end) {
-            hx = load_row<VEC>(at(xb + th * xs, k.lo));
-            hdy = load_row<VEC>(at(dyb + th * dys, k.lo));
-        }
-        bwd_step<VEC, W, NTS, true>(tap, bs, hx, hdy, xr, gr, acc, db, k, th, false);
-    }
-}
-
-template <int VEC, int G, int W, int F, bool VL>
-__device__ __forceinline__ void bwd_body(const BwdArgs& a) {
-    constexpr int R = W > 1 ? W - 1 : 1;
-    constexpr bool NTL = (F & kNtLoad) != 0, NTS = (F & kNtStore) != 0, PF = (F & kPrefetch) != 0;
-    extern __shared__ float red[];  // [waves][VEC][64], one column at a time
-    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T);
-    const int64_t t0 = wt.t0, t1 = wt.t1;
-    const int wave = wave_id();
-    const int lane = threadIdx.x % kWave;
-    const bool active = wt.d < a.D;
-    const bool valid = !(a.status && *a.status != 0);  // the offset check passed (or there is none)
-    const uint32_t lo = static_cast<uint32_t>(wt.d) * 2u;  // byte offset of the lane's channels
-
-    float acc[W][VEC], db[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-        db[v] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < W; ++k) acc[k][v] = 0.0f;
-    }
-
-    if (active && valid && t0 < a.T) {
-        // wave-uniform row bases plus the lane's 32-bit channel offset
-        const uint16_t* __restrict__ xb = a.x + wt.b * a.x_sb;
-        const uint16_t* __restrict__ dyb = a.dy + wt.b * a.dy_sb;
-        const int64_t xs = a.x_st, dys = a.dy_st;
-
-        float tap[W][VEC];
-        load_taps<VEC, W>(a.w, a.w_f32, wt.d, tap);
-        float bs[VEC];
-        load_bias<VEC>(a.bias, wt.d, bs);
-
-        // the sequence holding row t0: its rows [start, end) and its state row
-        int64_t s = wt.b, start = 0, end = a.T;
-        if constexpr (VL) {
-            s = seq_of(a.cu, a.nseq, t0);
-            start = a.cu[s];
-            end = a.cu[s + 1];
-        }
-        // ring prologue as in the forward; the g ring starts at zero (rows before t0 are not
-        // this wave's, and history rows have no g)
-        float xr[R][VEC], gr[R][VEC];
-        ring_at<VEC, W>(xr, t0, start, xb, xs, lo, a.h0, s, a.D, wt.d);
-#pragma unroll
-        for (int k = 0; k < R; ++k)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) gr[k][v] = 0.0f;
-        DxSink k{a.dx + wt.b * a.T * a.D, a.D, lo, t0, start, (t0 == start) ? a.dh0 : nullptr, s, a.D, wt.d};
-
-        int64_t t = t0;
-        for (;;) {
-            const int64_t e = VL ? min(t1, end) : t1;
-            bwd_run<VEC, G, W, NTL, NTS, PF>(tap, bs, xr, gr, acc, db, xb, xs, dyb, dys, k, t, e);
-            bwd_halo<VEC, W, NTS>(tap, bs, xr, gr, acc, db, xb, xs, dyb, dys, k, e, end);
-            if constexpr (!VL) {
-                break;
-            } else {
-                if (e >= t1) break;
-                // the next non-empty sequence starts at row e: this wave holds its first row
-                do {
-                    ++s;
-                } while (a.cu[s + 1] <= e);
-                start = e;
-                end = a.cu[s + 1];
-                ring_at<VEC, W>(xr, e, start, xb, xs, lo, a.h0, s, a.D, wt.d);
-#pragma unroll
-                for (int kk = 0; kk < R; ++kk)
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) gr[kk][v] = 0.0f;
-                k.own = e;
-                k.start = e;
-                k.hg = a.dh0;
-                k.s = s;
-                t = e;
-            }
-        }
-    }
-
-    // The waves that share a strip (same ws_i, consecutive segments) are summed through LDS in
-    // segment order, one column at a time; the first of them stores the block's partial.
-    const int64_t p = wt.b * a.seg_groups + wt.sg;
-    float* __restrict__ out = a.partial + p * (W + 1) * a.D;
-#pragma unroll
-    for (int j = 0; j <= W; ++j) {
-        // column j < W is dw[:, j], the gradient of tap k = W-1-j; column W is dbias
-#pragma unroll
-        for (int v = 0; v < VEC; ++v)
-            red[(wave * VEC + v) * kWave + lane] = (j < W) ? acc[W - 1 - j][v] : db[v];
-        __syncthreads();
-        if (wt.wt_i == 0 && active && valid) {
-            float s[VEC];
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                s[v] = red[(wt.ws_i * VEC + v) * kWave + lane];
-                for (int i = 1; i < wt.wt; ++i) s[v] += red[((i * a.ws + wt.ws_i) * VEC + v) * kWave + lane];
-            }
-            float* o = at(out + j * a.D, lo * 2u);  // fp32 partials: twice the bf16 byte offset
-            if constexpr (VEC == 8) {
-                reinterpret_cast<float4*>(o)[0] = make_float4(s[0], s[1], s[2], s[3]);
-                reinterpret_cast<float4*>(o)[1] = make_float4(s[4], s[5], s[6], s[7]);
-            } else {
-                reinterpret_cast<float4*>(o)[0] = make_float4(s[0], s[1], s[2], s[3]);
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// The kernels: a general one (blocks of up to 8 waves, at most 256 VGPRs per wave so two
-// waves fit a SIMD), and a "solo" one for one-wave blocks run one wave per SIMD, which may use
-// the whole register file (256 VGPRs + 256 AGPRs): deeper row groups then fit without scratch
-// spills (the compiler parks values in AGPRs).
-template <int VEC, int G, int W, int F, bool VL>
-__global__ __launch_bounds__(512) void cconv_bwd_kernel(const BwdArgs a) {
-    bwd_body<VEC, G, W, F, VL>(a);
-}
-
-template <int VEC, int G, int W, int F, bool VL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void cconv_bwd_kernel_solo(const BwdArgs a) {
-    bwd_body<VEC, G, W, F, VL>(a);
-}
 
 // dw[d, j] = sum_p partial[p, j, d] (j < W), dbias[d] = sum_p partial[p, W, d]. A block
 // handles 64 consecutive (j, d) entries; its 4 waves each sum a contiguous quarter of the
@@ -370,17 +51,10 @@ __global__ __launch_bounds__(256) void cconv_dw_reduce_kernel(const ReduceArgs a
 namespace {
 
 template <int VEC, int G, int W>
-hipError_t launch_bwd_f(int F, bool vl, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_f(int F, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
 #define CCONV_BWD_CASE(f, vl)                                                                              \
     case f: hipLaunchKernelGGL((cconv_bwd_kernel<VEC, G, W, f, vl>), grid, block, lds, s, a); break;        \
     case f + kSolo: hipLaunchKernelGGL((cconv_bwd_kernel_solo<VEC, G, W, f, vl>), grid, block, lds, s, a); break;
-    if (vl) {  // packed batches: the streaming options only
-        switch (F) {
-            CCONV_BWD_CASE(kVarlenBwdOptions, true)
-            default: return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
-    }
     switch (F) {
         CCONV_BWD_CASE(0, false)
         CCONV_BWD_CASE(1, false)
@@ -398,12 +72,11 @@ hipError_t launch_bwd_f(int F, bool vl, dim3 grid, dim3 block, size_t lds, const
 
 template <int VEC, int G>
 hipError_t launch_bwd_w(int W, int F, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
-    const bool vl = a.cu != nullptr;
     switch (W) {
-        case 1: return launch_bwd_f<VEC, G, 1>(F, vl, grid, block, lds, a, s);
-        case 2: return launch_bwd_f<VEC, G, 2>(F, vl, grid, block, lds, a, s);
-        case 3: return launch_bwd_f<VEC, G, 3>(F, vl, grid, block, lds, a, s);
-        case 4: return launch_bwd_f<VEC, G, 4>(F, vl, grid, block, lds, a, s);
+        case 1: return launch_bwd_f<VEC, G, 1>(F, grid, block, lds, a, s);
+        case 2: return launch_bwd_f<VEC, G, 2>(F, grid, block, lds, a, s);
+        case 3: return launch_bwd_f<VEC, G, 3>(F, grid, block, lds, a, s);
+        case 4: return launch_bwd_f<VEC, G, 4>(F, grid, block, lds, a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -415,6 +88,7 @@ bool bwd_variant_exists(int vec, int group) {
 }
 
 hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t s) {
+    if (a.cu || (p.options & kLinear)) return launch_bwd_extra(p, W, a, s);
     const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
     const size_t lds = static_cast<size_t>(p.waves) * p.vec * kWave * sizeof(float);
     const int F = p.options;

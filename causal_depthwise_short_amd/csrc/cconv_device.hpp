@@ -92,6 +92,10 @@ constexpr int kSolo = 8;      // one-wave blocks, one wave per SIMD, whole regis
 // Packed batches are compiled for the streaming options only (with or without kSolo).
 constexpr int kVarlenFwdOptions = kNtLoad | kNtStore;
 constexpr int kVarlenBwdOptions = kNtLoad | kNtStore | kPrefetch;
+// Epilogue variants (compile-time, default launch only): no activation (y = z, g = dy), and a
+// residual added to the forward's output after the activation.
+constexpr int kLinear = 16;
+constexpr int kResidual = 32;
 
 // The wave's index in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }

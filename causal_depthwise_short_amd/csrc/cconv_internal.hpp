@@ -49,6 +49,9 @@ struct FwdArgs {
     // row, so hT must not share h0's memory). *status holds the offset check's verdict.
     const int32_t* cu;
     int64_t nseq;
+    // residual added after the activation (kResidual): bf16 rows like x's, strides r_sb, r_st
+    const uint16_t* r;
+    int64_t r_sb, r_st;
     int64_t B, T, D;
     int64_t seg_rows, strip_groups, seg_groups;
     int ws;
@@ -106,6 +109,13 @@ struct UpdateArgs {
 // Launchers: enqueue on `stream`, return hipGetLastError() after the launch.
 hipError_t launch_fwd(const Plan& p, int W, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t stream);
+// Packed batches and epilogue variants (their own translation units).
+hipError_t launch_fwd_extra(const Plan& p, int W, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_extra(const Plan& p, int W, const BwdArgs& a, hipStream_t stream);
+// Whether a kernel is compiled for this launch: (vec, group), options (kernel option bits,
+// kSolo and the epilogue bits included), packed or not.
+bool fwd_launch_exists(int vec, int group, int options, bool packed);
+bool bwd_launch_exists(int vec, int group, int options, bool packed);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_update(int W, int L, const UpdateArgs& a, int block_threads, int64_t grid_x,
                          int64_t grid_y, size_t lds_bytes, hipStream_t stream);

@@ -193,6 +193,56 @@ cconv_status_t cconv_bwd_varlen(const void* x, int64_t x_st, const void* dy, int
                                 int64_t D, int W, cconv_stream_t stream);
 
 /*
+ * The general forward and backward [fla's causal_conv1d parameter list, kernel-fun wheel,
+ * _common/compat.py FLA_KWARGS: activation, residual, initial_state, output_final_state,
+ * cu_seqlens]: one entry point each combining the epilogue variants with a history and with
+ * packed batches. opts == NULL is SiLU and nothing else (cconv_fwd / cconv_bwd).
+ *   activation   CCONV_ACT_SILU (y = silu(z)) or CCONV_ACT_NONE (y = z; the backward's g = dy).
+ *                Anything else: CCONV_ERR_BAD_CONFIG.
+ *   residual     bf16 rows like x (batch stride residual_sb, row stride residual_st elements,
+ *                multiples of 8, residual_st >= D; 16-byte aligned) added to y after the
+ *                activation, or NULL. Its gradient is dy itself: the backward has nothing to do.
+ *   init_state, final_state, d_init_state
+ *                as cconv_fwd_state / cconv_bwd_state ([B, D, W-1]), or per packed sequence
+ *                ([nseq, D, W-1]) with cu_seqlens.
+ *   cu_seqlens, nseq, status
+ *                a packed batch as cconv_fwd_varlen / cconv_bwd_varlen: then B must be 1 and
+ *                T is the packed row count; x_sb, dy_sb and residual_sb are ignored.
+ * The variants without an activation or with a residual run the default launch (no
+ * configuration entry point).
+ */
+typedef enum { CCONV_ACT_NONE = 0, CCONV_ACT_SILU = 1 } cconv_activation_t;
+
+typedef struct {
+    int activation;
+    const void* residual;
+    int64_t residual_sb, residual_st;
+    const void* init_state;
+    void* final_state;
+    const int32_t* cu_seqlens;
+    int64_t nseq;
+    int32_t* status;
+} cconv_fwd_opts_t;
+
+typedef struct {
+    int activation;
+    const void* init_state;
+    void* d_init_state;
+    const int32_t* cu_seqlens;
+    int64_t nseq;
+    int32_t* status;
+} cconv_bwd_opts_t;
+
+cconv_status_t cconv_fwd_ex(const void* x, int64_t x_sb, int64_t x_st, const void* w, cconv_dtype_t w_dtype,
+                            const float* bias, void* y, int64_t B, int64_t T, int64_t D, int W,
+                            const cconv_fwd_opts_t* opts, cconv_stream_t stream);
+
+cconv_status_t cconv_bwd_ex(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb, int64_t dy_st,
+                            const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx, void* dw,
+                            cconv_dtype_t dw_dtype, float* dbias, void* workspace, size_t workspace_bytes, int64_t B,
+                            int64_t T, int64_t D, int W, const cconv_bwd_opts_t* opts, cconv_stream_t stream);
+
+/*
  * The backward's two stages, for callers that want the fp32 partials themselves (a
  * data-parallel caller can sum them across ranks before the final cast) or that time the
  * stages apart. cconv_bwd_main writes dx and fills the workspace with fp32 dw/dbias partial

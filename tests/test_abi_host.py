@@ -432,3 +432,86 @@ def test_update_ex_host_errors(kw, code):
 def test_update_ex_width_one_shift_needs_no_state():
     # W = 1, L = 0, shift: no state at all; nothing to launch for N = 0
     assert upd_ex(W=1, L=0, cs=None, state=None, N=0, status=None) == OK
+
+
+def test_option_structs_match_the_header(tmp_path):
+    """The binding's ctypes structures have the C layout of cconv_fwd_opts_t / cconv_bwd_opts_t."""
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"cconv.h\"\n"
+        "#define O(T, f) printf(\"%zu \", offsetof(T, f))\n"
+        "int main(void) {\n"
+        "  printf(\"%zu %zu \", sizeof(cconv_fwd_opts_t), sizeof(cconv_bwd_opts_t));\n"
+        "  O(cconv_fwd_opts_t, activation); O(cconv_fwd_opts_t, residual); O(cconv_fwd_opts_t, residual_sb);\n"
+        "  O(cconv_fwd_opts_t, residual_st); O(cconv_fwd_opts_t, init_state); O(cconv_fwd_opts_t, final_state);\n"
+        "  O(cconv_fwd_opts_t, cu_seqlens); O(cconv_fwd_opts_t, nseq); O(cconv_fwd_opts_t, status);\n"
+        "  O(cconv_bwd_opts_t, activation); O(cconv_bwd_opts_t, init_state); O(cconv_bwd_opts_t, d_init_state);\n"
+        "  O(cconv_bwd_opts_t, cu_seqlens); O(cconv_bwd_opts_t, nseq); O(cconv_bwd_opts_t, status);\n"
+        "  return 0;\n}\n"
+    )
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", str(ROOT / "include"), "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", str(src),
+                    "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(cc.FwdOpts), ctypes.sizeof(cc.BwdOpts)]
+    want += [getattr(cc.FwdOpts, f).offset for f, _ in cc.FwdOpts._fields_]
+    want += [getattr(cc.BwdOpts, f).offset for f, _ in cc.BwdOpts._fields_]
+    assert got == want
+
+
+RES = 0x70_0000_0000
+
+
+def fwd_ex(x=X, y=Y, B=2, T=64, D=512, W=4, act=1, res=RES, r_st=None, r_sb=None, h0=H0, hT=HT, cu=None, nseq=0,
+           status=None):
+    r_st = D if r_st is None else r_st
+    r_sb = T * r_st if r_sb is None else r_sb
+    o = cc.FwdOpts(act, res, r_sb, r_st, h0, hT, cu, nseq, status)
+    return cc.lib().cconv_fwd_ex(x, T * D, D, WT, BF16, BIAS, y, B, T, D, W, ctypes.byref(o), None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(act=2), CONFIG),
+        (dict(act=-1), CONFIG),
+        (dict(cu=CU, nseq=2), SHAPE),  # packed batches have B = 1
+        (dict(cu=CU, nseq=2, B=1, status=None), NULLP),
+        (dict(res=RES + 2), MISAL),
+        (dict(r_st=500), STRIDE),
+        (dict(r_st=516), STRIDE),
+        (dict(y=RES + 32), ALIAS),
+        (dict(hT=RES), ALIAS),
+        (dict(res=Y), ALIAS),
+        (dict(W=5), SHAPE),
+    ],
+)
+def test_fwd_ex_host_errors(kw, code):
+    assert fwd_ex(**kw) == code
+
+
+def bwd_ex(act=1, dx=DX, h0=H0, dh=DH, cu=None, nseq=0, status=None, B=2, T=64, D=512, W=4, ws_bytes=1 << 40):
+    o = cc.BwdOpts(act, h0, dh, cu, nseq, status)
+    return cc.lib().cconv_bwd_ex(X, T * D, D, DY, T * D, D, WT, BF16, BIAS, dx, DW, BF16, DB, WSP, ws_bytes, B, T, D, W,
+                                 ctypes.byref(o), None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(act=3), CONFIG),
+        (dict(cu=CU, nseq=2), SHAPE),
+        (dict(cu=CU, nseq=2, B=1), NULLP),
+        (dict(dh=H0), ALIAS),
+        (dict(dx=H0 + 16), ALIAS),
+        (dict(ws_bytes=16), WS),
+        (dict(act=0, ws_bytes=16), WS),  # the variant without an activation exists for the default launch
+    ],
+)
+def test_bwd_ex_host_errors(kw, code):
+    assert bwd_ex(**kw) == code
