@@ -35,7 +35,12 @@ sys.path.insert(0, str(ROOT))
 METRIC = "effective HBM GB/s (fwd, bwd) B8/T8192/D4096/W4 bf16; % of flat-copy roofline"
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = ROOT / "profiles" / "bwd_main_B8_T8192_D4096_W4_traffic.txt"
-KERNEL_SOURCES = ["causal_depthwise_short_amd/csrc/cconv_bwd.hip", "causal_depthwise_short_amd/csrc/cconv_device.hpp"]
+KERNEL_SOURCES = [
+    "causal_depthwise_short_amd/csrc/cconv_bwd.hip",
+    "causal_depthwise_short_amd/csrc/cconv_bwd_body.hpp",
+    "causal_depthwise_short_amd/csrc/cconv_device.hpp",
+    "causal_depthwise_short_amd/csrc/cconv_internal.hpp",
+]
 
 
 def log(*a):

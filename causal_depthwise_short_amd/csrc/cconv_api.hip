@@ -21,6 +21,7 @@ constexpr int64_t kMaxChannels = int64_t(1) << 30;    // D: lane channel offsets
 constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices (LDS bit set)
 constexpr int64_t kMaxSequences = int64_t(1) << 24;     // packed sequences per call
 constexpr int64_t kTargetWaves = 1024;  // one wave per SIMD (256 CUs x 4 SIMDs)
+constexpr int64_t kNarrowTargetWaves = 8192;  // the narrow path: several waves per SIMD
 // forward: non-temporal loads and stores, solo kernel; backward: the same plus prefetch
 constexpr int kFwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
 constexpr int kBwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kPrefetch | cconv::kSolo;
@@ -75,16 +76,19 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) {
     (void)W;
     cconv_config_t c;
-    c.vec = bwd ? 8 : 4;
-    c.rows_per_group = bwd ? 8 : 16;
-    c.waves_per_block = 1;
+    const bool narrow = (D % 8 != 0);
+    c.vec = narrow ? 1 : (bwd ? 8 : 4);
+    c.rows_per_group = (bwd && !narrow) ? 8 : 16;
+    c.waves_per_block = narrow ? 4 : 1;
     c.strips_per_block = 1;
-    c.options = bwd ? kBwdOptions : kFwdOptions;
+    // the narrow path: one channel per lane moves 8x fewer bytes per wave, so it runs several
+    // waves per SIMD (the general kernel) instead of one solo wave
+    c.options = narrow ? (bwd ? cconv::kVarlenBwdOptions : cconv::kVarlenFwdOptions) : (bwd ? kBwdOptions : kFwdOptions);
     // segment length: a multiple of the row group (and of 8), at least kMinSeg rows, at most
     // T rounded up
     const int64_t align = std::max<int64_t>(8, c.rows_per_group);
     const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
-    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / kTargetWaves;
+    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / (narrow ? kNarrowTargetWaves : kTargetWaves);
     ts = std::max(kMinSeg, ts - ts % align);
     const int64_t tcap = ((std::max<int64_t>(T, 1) + align - 1) / align) * align;
     c.seg_rows = std::min(ts, tcap);
@@ -116,16 +120,26 @@ cconv_status_t check_train_common(const void* w, cconv_dtype_t w_dtype, const fl
                                   int64_t T, int64_t D, int W) {
     if (B < 0 || T < 0 || D < 0 || B > kMaxDim || T > kMaxDim || D > kMaxDim) return CCONV_ERR_BAD_SHAPE;
     if (W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
-    if (D % 8 != 0 || D > kMaxChannels) return CCONV_ERR_BAD_SHAPE;
+    if (D > kMaxChannels) return CCONV_ERR_BAD_SHAPE;
     if (!dtype_ok(w_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
-    if (!aligned(w, 16) || (bias && !aligned(bias, 16))) return CCONV_ERR_MISALIGNED;
     return CCONV_OK;
 }
 
-cconv_status_t check_act(const void* p, int64_t sb, int64_t st, int64_t D) {
+// Alignment of the taps and bias: 16 bytes on the vector path; the element size on the
+// element-granular one (narrow: one channel per lane, for D not a multiple of 8).
+cconv_status_t check_params(const void* w, cconv_dtype_t w_dtype, const float* bias, bool narrow) {
+    const uintptr_t wa = narrow ? static_cast<uintptr_t>(esize(w_dtype)) : 16, ba = narrow ? 4 : 16;
+    if (!aligned(w, wa) || (bias && !aligned(bias, ba))) return CCONV_ERR_MISALIGNED;
+    return CCONV_OK;
+}
+
+// A bf16 [B, T, D] operand with strides (sb, st, 1). Vector path: strides multiples of 8 and
+// 16-byte alignment (whole 16- or 8-byte rows per lane). Narrow path: any strides, 2-byte
+// alignment.
+cconv_status_t check_act(const void* p, int64_t sb, int64_t st, int64_t D, bool narrow = false) {
     if (sb < 0 || st < D || sb > kMaxDim || st > kMaxDim) return CCONV_ERR_BAD_STRIDE;
-    if (sb % 8 != 0 || st % 8 != 0) return CCONV_ERR_BAD_STRIDE;
-    if (!aligned(p, 16)) return CCONV_ERR_MISALIGNED;
+    if (!narrow && (sb % 8 != 0 || st % 8 != 0)) return CCONV_ERR_BAD_STRIDE;
+    if (!aligned(p, narrow ? 2 : 16)) return CCONV_ERR_MISALIGNED;
     return CCONV_OK;
 }
 
@@ -159,10 +173,10 @@ struct Extra {
 // Checks of the states and of the pool/packed metadata against the call's other operands.
 // `ins` and `outs` are the call's own tensors; returns CCONV_OK or the error.
 cconv_status_t check_extra(const Extra& ex, int64_t B, int64_t D, int W, bool fwd, const Span* ins, int n_in,
-                           const Span* outs, int n_out, Span* sh0_out) {
+                           const Span* outs, int n_out, Span* sh0_out, uintptr_t state_align) {
     const void* h0 = ex.h0;
     const void* out = ex.out;
-    if (!aligned(h0, 16) || !aligned(out, 16)) return CCONV_ERR_MISALIGNED;
+    if (!aligned(h0, state_align) || !aligned(out, state_align)) return CCONV_ERR_MISALIGNED;
     const int64_t rows = ex.mode == kPerSeq ? B : ex.rows;
     const __int128 state_bytes = static_cast<__int128>(rows) * D * (W - 1) * 2;
     const Span sh0 = span(h0, state_bytes), so = span(out, state_bytes);
@@ -218,14 +232,17 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     if ((!x && !act_empty) || (!w && D > 0) || (!y && !act_empty)) return CCONV_ERR_NULL_POINTER;
     cconv_status_t st = check_train_common(w, w_dtype, bias, B, T, D, W);
     if (st != CCONV_OK) return st;
-    if ((st = check_act(x, x_sb, x_st, D)) != CCONV_OK) return st;
-    if (!aligned(y, 16)) return CCONV_ERR_MISALIGNED;
     const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
+    const bool narrow = (c.vec == 1);
+    if (!narrow && D % 8 != 0) return CCONV_ERR_BAD_CONFIG;  // a vector plan needs whole 8-channel groups
+    if ((st = check_params(w, w_dtype, bias, narrow)) != CCONV_OK) return st;
+    if ((st = check_act(x, x_sb, x_st, D, narrow)) != CCONV_OK) return st;
+    if (!aligned(y, narrow ? 2 : 16)) return CCONV_ERR_MISALIGNED;
     const int epi = (ex.linear ? cconv::kLinear : 0) | (ex.r ? cconv::kResidual : 0);
     if (!cconv::fwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
         return CCONV_ERR_BAD_CONFIG;
-    if (ex.r && (st = check_act(ex.r, ex.r_sb, ex.r_st, D)) != CCONV_OK) return st;
+    if (ex.r && (st = check_act(ex.r, ex.r_sb, ex.r_st, D, narrow)) != CCONV_OK) return st;
     const Span sy = span(y, extent3(B, T, D, T * D, D, 2));
     const Span sx = span(x, extent3(B, T, D, x_sb, x_st, 2));
     const Span sw = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
@@ -236,7 +253,7 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     if (W == 1) ex.h0 = ex.out = nullptr;
     const Span ins[4] = {sx, sw, sb, sr};
     Span sh0;
-    if ((st = check_extra(ex, B, D, W, true, ins, 4, &sy, 1, &sh0)) != CCONV_OK) return st;
+    if ((st = check_extra(ex, B, D, W, true, ins, 4, &sy, 1, &sh0, narrow ? 2 : 16)) != CCONV_OK) return st;
     Plan p;
     if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
     p.options |= epi;
@@ -302,11 +319,16 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     cconv_status_t st = check_train_common(w, w_dtype, bias, B, T, D, W);
     if (st != CCONV_OK) return st;
     if (!dtype_ok(dw_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
-    if ((st = check_act(x, x_sb, x_st, D)) != CCONV_OK) return st;
-    if ((st = check_act(dy, dy_sb, dy_st, D)) != CCONV_OK) return st;
-    if (!aligned(dx, 16) || !aligned(dw, 16) || (dbias && !aligned(dbias, 16))) return CCONV_ERR_MISALIGNED;
     const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W);
     if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
+    const bool narrow = (c.vec == 1);
+    if (!narrow && D % 8 != 0) return CCONV_ERR_BAD_CONFIG;  // a vector plan needs whole 8-channel groups
+    if ((st = check_params(w, w_dtype, bias, narrow)) != CCONV_OK) return st;
+    if ((st = check_act(x, x_sb, x_st, D, narrow)) != CCONV_OK) return st;
+    if ((st = check_act(dy, dy_sb, dy_st, D, narrow)) != CCONV_OK) return st;
+    if (!aligned(dx, narrow ? 2 : 16) || !aligned(dw, narrow ? static_cast<uintptr_t>(esize(dw_dtype)) : 16) ||
+        (dbias && !aligned(dbias, narrow ? 4 : 16)))
+        return CCONV_ERR_MISALIGNED;
     const int epi = ex.linear ? cconv::kLinear : 0;
     if (!cconv::bwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
         return CCONV_ERR_BAD_CONFIG;
@@ -334,7 +356,7 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
             if (overlap(outs[i], outs[j])) return CCONV_ERR_ALIASING;
     }
     Span sh0;
-    if ((st = check_extra(ex, B, D, W, false, ins, 4, outs, 4, &sh0)) != CCONV_OK) return st;
+    if ((st = check_extra(ex, B, D, W, false, ins, 4, outs, 4, &sh0, narrow ? 2 : 16)) != CCONV_OK) return st;
     if (workspace_bytes < need) return CCONV_ERR_WORKSPACE;
     // a per-sequence history gradient needs at least one token
     if (ex.out && ex.mode != kPacked && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;
@@ -430,14 +452,19 @@ cconv_status_t update_impl(const void* x, int64_t x_ld, void* state, int64_t S, 
     if (cache_seqlens && L < 1) return CCONV_ERR_BAD_SHAPE;  // a circular state needs entries
     if (((!x || !y) && N > 0 && D > 0) || (!w && D > 0) || (!state && S > 0 && D > 0 && L > 0))
         return CCONV_ERR_NULL_POINTER;
-    if (N < 0 || S < 0 || D < 0 || N > kMaxDecodeRows || S > kMaxDim || D > kMaxDim) return CCONV_ERR_BAD_SHAPE;
-    if (W < 1 || W > 4 || D % 8 != 0) return CCONV_ERR_BAD_SHAPE;
+    if (N < 0 || S < 0 || D < 0 || N > kMaxDecodeRows || S > kMaxDim || D > kMaxChannels) return CCONV_ERR_BAD_SHAPE;
+    if (W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
     if (state_indices && S > kMaxIndexedSlots) return CCONV_ERR_BAD_SHAPE;
     if (!state_indices && N > S) return CCONV_ERR_BAD_SHAPE;
     if (!dtype_ok(w_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
-    if (x_ld < D || x_ld > kMaxDim || x_ld % 8 != 0) return CCONV_ERR_BAD_STRIDE;
-    if (!aligned(x, 16) || !aligned(state, 16) || !aligned(w, 16) || !aligned(y, 16) ||
-        (bias && !aligned(bias, 16)) || (state_indices && !aligned(state_indices, 4)) ||
+    // Rows: D a multiple of 8 with a row stride that is one too takes the 8-channel path; any
+    // other D takes the one-channel path, with compact rows (x_ld == D) or a stride that is a
+    // multiple of 8 [the decode PR's row-stride contract].
+    const bool narrow = (D % 8 != 0);
+    if (x_ld < D || x_ld > kMaxDim || (x_ld % 8 != 0 && !(narrow && x_ld == D))) return CCONV_ERR_BAD_STRIDE;
+    const uintptr_t va = narrow ? 2 : 16;
+    if (!aligned(x, va) || !aligned(state, va) || !aligned(w, narrow ? static_cast<uintptr_t>(esize(w_dtype)) : 16) ||
+        !aligned(y, va) || (bias && !aligned(bias, narrow ? 4 : 16)) || (state_indices && !aligned(state_indices, 4)) ||
         (cache_seqlens && !aligned(cache_seqlens, 4)) || (status && !aligned(status, 4)))
         return CCONV_ERR_MISALIGNED;
     const Span in_x = span(x, N == 0 || D == 0 ? 0 : (static_cast<__int128>(N - 1) * x_ld + D) * 2);
@@ -461,7 +488,7 @@ cconv_status_t update_impl(const void* x, int64_t x_ld, void* state, int64_t S, 
         if (status) return cconv::launch_status(status, CCONV_OK, s) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
         return CCONV_OK;
     }
-    const int64_t dv = D / 8;  // 8-channel vectors per row
+    const int64_t dv = narrow ? D : D / 8;  // channel groups per row (one thread each)
     const int threads = static_cast<int>(std::min<int64_t>(256, ((dv + 63) / 64) * 64));
     const int64_t grid_x = (dv + threads - 1) / threads;
     const int64_t rpb = std::max<int64_t>(1, (N * grid_x + kUpdateTargetBlocks - 1) / kUpdateTargetBlocks);
@@ -483,8 +510,8 @@ cconv_status_t update_impl(const void* x, int64_t x_ld, void* state, int64_t S, 
     a.D = D;
     a.rows_per_block = rpb;
     a.status = status;
-    return cconv::launch_update(W, L, a, threads, grid_x, grid_y, lds, s) == hipSuccess ? CCONV_OK
-                                                                                        : CCONV_ERR_LAUNCH;
+    return cconv::launch_update(W, L, narrow, a, threads, grid_x, grid_y, lds, s) == hipSuccess ? CCONV_OK
+                                                                                                : CCONV_ERR_LAUNCH;
 }
 
 }  // namespace

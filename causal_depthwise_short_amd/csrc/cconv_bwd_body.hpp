@@ -256,10 +256,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         // this wave's, and history rows have no g)
         float xr[R][VEC], gr[R][VEC];
         ring_at<VEC, W>(xr, t0, start, xb, xs, lo, a.h0, s, a.D, wt.d);
-#pragma unroll
-        for (int k = 0; k < R; ++k)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) gr[k][v] = 0.0f;
+        for (auto& row : gr)
+            for (float& g : row) g = 0.0f;
         DxSink k{a.dx + wt.b * a.T * a.D, a.D, lo, t0, start, (t0 == start) ? a.dh0 : nullptr, s, a.D, wt.d};
 
         int64_t t = t0;
@@ -278,10 +276,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
                 start = e;
                 end = a.cu[s + 1];
                 ring_at<VEC, W>(xr, e, start, xb, xs, lo, a.h0, s, a.D, wt.d);
-#pragma unroll
-                for (int kk = 0; kk < R; ++kk)
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) gr[kk][v] = 0.0f;
+                for (auto& row : gr)
+                    for (float& g : row) g = 0.0f;
                 k.own = e;
                 k.start = e;
                 k.hg = a.dh0;
@@ -310,7 +306,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
                 for (int i = 1; i < wt.wt; ++i) s[v] += red[((i * a.ws + wt.ws_i) * VEC + v) * kWave + lane];
             }
             float* o = at(out + j * a.D, lo * 2u);  // fp32 partials: twice the bf16 byte offset
-            if constexpr (VEC == 8) {
+            if constexpr (VEC == 1) {
+                o[0] = s[0];
+            } else if constexpr (VEC == 8) {
                 reinterpret_cast<float4*>(o)[0] = make_float4(s[0], s[1], s[2], s[3]);
                 reinterpret_cast<float4*>(o)[1] = make_float4(s[4], s[5], s[6], s[7]);
             } else {

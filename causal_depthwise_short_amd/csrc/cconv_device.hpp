@@ -2,7 +2,8 @@
 //
 // Data movement is in whole rows of a lane's VEC contiguous channels: one 16-byte (VEC = 8)
 // or 8-byte (VEC = 4) global load or store per row, so a wave64 moves 1 KB (or 512 B) of a
-// bf16 row per instruction, fully coalesced. bf16 values stay packed two to a dword until
+// bf16 row per instruction, fully coalesced. VEC = 1 (2 bytes per lane) serves any D and any
+// row alignment. bf16 values stay packed two to a dword until
 // they are used; widening is a shift or a mask, narrowing is gfx950's packed
 // round-to-nearest-even convert (v_cvt_pk_bf16_f32).
 #pragma once
@@ -19,10 +20,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-// VEC bf16 values of one row, packed two per dword (element 2i in the low half of u[i]).
+// VEC bf16 values of one row, packed two per dword (element 2i in the low half of u[i]); with
+// VEC = 1 (the element-granular path for any D) the one value is the low half of u[0].
 template <int VEC>
 struct Row {
-    uint32_t u[VEC / 2];
+    uint32_t u[VEC >= 2 ? VEC / 2 : 1];
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -31,9 +33,15 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // NT selects non-temporal loads/stores (streamed data that is not re-read soon).
 template <int VEC, bool NT = false>
 __device__ __forceinline__ Row<VEC> load_row(const uint16_t* __restrict__ p) {
-    static_assert(VEC == 4 || VEC == 8, "VEC is 4 or 8");
+    static_assert(VEC == 1 || VEC == 4 || VEC == 8, "VEC is 1, 4 or 8");
     Row<VEC> r;
-    if constexpr (VEC == 8) {
+    if constexpr (VEC == 1) {
+        if constexpr (NT) {
+            r.u[0] = __builtin_nontemporal_load(p);
+        } else {
+            r.u[0] = *p;
+        }
+    } else if constexpr (VEC == 8) {
         u32x4 v;
         if constexpr (NT) {
             v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -61,13 +69,20 @@ template <int VEC>
 __device__ __forceinline__ Row<VEC> zero_row() {
     Row<VEC> r;
 #pragma unroll
-    for (int i = 0; i < VEC / 2; ++i) r.u[i] = 0u;
+    for (int i = 0; i < (VEC >= 2 ? VEC / 2 : 1); ++i) r.u[i] = 0u;
     return r;
 }
 
 template <int VEC, bool NT = false>
 __device__ __forceinline__ void store_row(uint16_t* __restrict__ p, const Row<VEC>& r) {
-    if constexpr (VEC == 8) {
+    if constexpr (VEC == 1) {
+        const uint16_t v = static_cast<uint16_t>(r.u[0]);
+        if constexpr (NT) {
+            __builtin_nontemporal_store(v, p);
+        } else {
+            *p = v;
+        }
+    } else if constexpr (VEC == 8) {
         const u32x4 v = {r.u[0], r.u[1], r.u[2], r.u[3]};
         if constexpr (NT) {
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
@@ -115,6 +130,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 
 template <int VEC>
 __device__ __forceinline__ void widen(const Row<VEC>& r, float (&f)[VEC]) {
+    if constexpr (VEC == 1) f[0] = bf16_lo(r.u[0]);
 #pragma unroll
     for (int i = 0; i < VEC / 2; ++i) {
         f[2 * i] = bf16_lo(r.u[i]);
@@ -132,6 +148,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int VEC>
 __device__ __forceinline__ Row<VEC> narrow(const float (&f)[VEC]) {
     Row<VEC> r;
+    if constexpr (VEC == 1) r.u[0] = pack_bf16x2(f[0], 0.0f) & 0xffffu;
 #pragma unroll
     for (int i = 0; i < VEC / 2; ++i) r.u[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
     return r;

@@ -117,7 +117,7 @@ hipError_t launch_bwd_extra(const Plan& p, int W, const BwdArgs& a, hipStream_t 
 bool fwd_launch_exists(int vec, int group, int options, bool packed);
 bool bwd_launch_exists(int vec, int group, int options, bool packed);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
-hipError_t launch_update(int W, int L, const UpdateArgs& a, int block_threads, int64_t grid_x,
+hipError_t launch_update(int W, int L, bool narrow, const UpdateArgs& a, int block_threads, int64_t grid_x,
                          int64_t grid_y, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_status(int32_t* status, int32_t value, hipStream_t stream);
 hipError_t launch_slots(const int32_t* idx, int64_t N, int64_t S, int32_t* status, hipStream_t stream);

@@ -23,20 +23,19 @@ namespace cconv {
 // The tokens 1 .. W-1 steps back, from the L state entries a thread loaded (h[v*L + e] is
 // entry e of channel d+v), in the forward's ring order: ring[k-1] = x[t-k]. Shift mode
 // (ROT < 0): entry L-k. Circular mode with rotation ROT = c mod L: entry (ROT - k) mod L.
-template <int W, int L, int ROT>
-__device__ __forceinline__ void ring_from_state(const uint16_t (&h)[8 * (L > 0 ? L : 1)],
-                                                float (&ring)[W > 1 ? W - 1 : 1][8]) {
-#pragma unroll
+template <int VEC, int W, int L, int ROT>
+__device__ __forceinline__ void ring_from_state(const uint16_t (&h)[VEC * (L > 0 ? L : 1)],
+                                                float (&ring)[W > 1 ? W - 1 : 1][VEC]) {
     for (int k = 1; k < W; ++k) {
         const int e = ROT < 0 ? L - k : ((ROT - k) % L + L) % L;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) ring[k - 1][v] = __uint_as_float(static_cast<uint32_t>(h[v * L + e]) << 16);
+        for (int v = 0; v < VEC; ++v) ring[k - 1][v] = __uint_as_float(static_cast<uint32_t>(h[v * L + e]) << 16);
     }
 }
 
-template <int W, int L, bool CIRC>
+// VEC = 8: a thread owns 8 channels (16-byte x rows, 16*L-byte state runs); VEC = 1: one channel
+// (any D, any row stride).
+template <int W, int L, bool CIRC, int VEC>
 __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
-    constexpr int VEC = 8;
     constexpr int R = W > 1 ? W - 1 : 1;
     extern __shared__ uint32_t seen[];
 
@@ -75,7 +74,9 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
         // 16-bit position v*L + e
         uint16_t h[VEC * (L > 0 ? L : 1)];
         uint16_t* __restrict__ sp = a.state + (s * a.D + d) * L;
-        if constexpr (L > 0) {
+        if constexpr (L > 0 && VEC == 1) {
+            for (int e = 0; e < L; ++e) h[e] = sp[e];
+        } else if constexpr (L > 0) {
 #pragma unroll
             for (int q = 0; q < L; ++q) {
                 const uint4 v4 = reinterpret_cast<const uint4*>(sp)[q];
@@ -91,13 +92,13 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
         int rot = 0;  // circular: the entry that takes the token (block-uniform: one row at a time)
         if constexpr (W > 1) {
             if constexpr (!CIRC) {
-                ring_from_state<W, L, -1>(h, ring);
+                ring_from_state<VEC, W, L, -1>(h, ring);
             } else {
                 rot = static_cast<int>(static_cast<int64_t>(a.cs[n]) % L);
-                if (rot == 0) ring_from_state<W, L, 0>(h, ring);
-                if constexpr (L > 1) if (rot == 1) ring_from_state<W, L, (L > 1 ? 1 : 0)>(h, ring);
-                if constexpr (L > 2) if (rot == 2) ring_from_state<W, L, (L > 2 ? 2 : 0)>(h, ring);
-                if constexpr (L > 3) if (rot == 3) ring_from_state<W, L, (L > 3 ? 3 : 0)>(h, ring);
+                if (rot == 0) ring_from_state<VEC, W, L, 0>(h, ring);
+                if constexpr (L > 1) if (rot == 1) ring_from_state<VEC, W, L, (L > 1 ? 1 : 0)>(h, ring);
+                if constexpr (L > 2) if (rot == 2) ring_from_state<VEC, W, L, (L > 2 ? 2 : 0)>(h, ring);
+                if constexpr (L > 3) if (rot == 3) ring_from_state<VEC, W, L, (L > 3 ? 3 : 0)>(h, ring);
             }
         } else if constexpr (CIRC) {
             rot = static_cast<int>(static_cast<int64_t>(a.cs[n]) % L);
@@ -116,6 +117,9 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
                     const uint32_t xw = rx.u[v / 2];
                     sp[v * L + rot] = static_cast<uint16_t>((v & 1) ? (xw >> 16) : (xw & 0xffffu));
                 }
+            } else if constexpr (VEC == 1) {  // shift, one channel
+                for (int j = 0; j + 1 < L; ++j) sp[j] = h[j + 1];
+                sp[L - 1] = static_cast<uint16_t>(rx.u[0] & 0xffffu);
             } else {  // shift: drop the oldest entry, append the token
                 uint16_t nh[VEC * L];
 #pragma unroll
@@ -154,25 +158,29 @@ __global__ void cconv_status_kernel(int32_t* status, int32_t value) {
 namespace {
 
 template <int W, int L, bool CIRC>
-void launch_update_k(dim3 grid, dim3 block, size_t lds, const UpdateArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((cconv_update_kernel<W, L, CIRC>), grid, block, lds, s, a);
+void launch_update_k(bool narrow, dim3 grid, dim3 block, size_t lds, const UpdateArgs& a, hipStream_t s) {
+    if (narrow)
+        hipLaunchKernelGGL((cconv_update_kernel<W, L, CIRC, 1>), grid, block, lds, s, a);
+    else
+        hipLaunchKernelGGL((cconv_update_kernel<W, L, CIRC, 8>), grid, block, lds, s, a);
 }
 
 template <int W>
-hipError_t launch_update_w(int L, bool circ, dim3 grid, dim3 block, size_t lds, const UpdateArgs& a, hipStream_t s) {
+hipError_t launch_update_w(int L, bool circ, bool narrow, dim3 grid, dim3 block, size_t lds, const UpdateArgs& a,
+                           hipStream_t s) {
     if (L == W - 1) {
         if (!circ) {
-            launch_update_k<W, W - 1, false>(grid, block, lds, a, s);
+            launch_update_k<W, W - 1, false>(narrow, grid, block, lds, a, s);
         } else if constexpr (W > 1) {
-            launch_update_k<W, W - 1, true>(grid, block, lds, a, s);
+            launch_update_k<W, W - 1, true>(narrow, grid, block, lds, a, s);
         } else {
             return hipErrorInvalidValue;  // a circular state needs at least one entry
         }
     } else if (L == W) {
         if (circ)
-            launch_update_k<W, W, true>(grid, block, lds, a, s);
+            launch_update_k<W, W, true>(narrow, grid, block, lds, a, s);
         else
-            launch_update_k<W, W, false>(grid, block, lds, a, s);
+            launch_update_k<W, W, false>(narrow, grid, block, lds, a, s);
     } else {
         return hipErrorInvalidValue;
     }
@@ -181,15 +189,15 @@ hipError_t launch_update_w(int L, bool circ, dim3 grid, dim3 block, size_t lds, 
 
 }  // namespace
 
-hipError_t launch_update(int W, int L, const UpdateArgs& a, int block_threads, int64_t grid_x, int64_t grid_y,
-                         size_t lds, hipStream_t s) {
+hipError_t launch_update(int W, int L, bool narrow, const UpdateArgs& a, int block_threads, int64_t grid_x,
+                         int64_t grid_y, size_t lds, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(grid_x), static_cast<uint32_t>(grid_y)), block(block_threads);
     const bool circ = a.cs != nullptr;
     switch (W) {
-        case 1: return launch_update_w<1>(L, circ, grid, block, lds, a, s);
-        case 2: return launch_update_w<2>(L, circ, grid, block, lds, a, s);
-        case 3: return launch_update_w<3>(L, circ, grid, block, lds, a, s);
-        case 4: return launch_update_w<4>(L, circ, grid, block, lds, a, s);
+        case 1: return launch_update_w<1>(L, circ, narrow, grid, block, lds, a, s);
+        case 2: return launch_update_w<2>(L, circ, narrow, grid, block, lds, a, s);
+        case 3: return launch_update_w<3>(L, circ, narrow, grid, block, lds, a, s);
+        case 4: return launch_update_w<4>(L, circ, narrow, grid, block, lds, a, s);
         default: return hipErrorInvalidValue;
     }
 }

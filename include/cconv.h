@@ -27,9 +27,17 @@
  *    captured into a HIP graph from the first call.
  *  - bf16 tensors are passed as raw 16-bit patterns; fp32 as IEEE binary32. Outputs in
  *    bf16 are rounded to nearest-even [strip.py: `_st`].
- *  - Alignment: every tensor pointer must be 16-byte aligned, except state_indices and
- *    status (4 bytes) [PR #797 review thread: alignment contract]. D must be a multiple of 8
- *    and every row stride a multiple of 8 elements, so that each lane moves 16-byte vectors.
+ *  - Alignment and D. When D is a multiple of 8 (the vector path: each lane moves whole 16- or
+ *    8-byte groups of channels), every tensor pointer must be 16-byte aligned, except
+ *    state_indices, cache_seqlens, cu_seqlens and status (4 bytes) [PR #797 review thread:
+ *    alignment contract], and every row and batch stride a multiple of 8 elements. Any other
+ *    D (the element-granular path [strip.py's masked loads handle any D]: one channel per
+ *    lane) needs only element alignment (2 bytes for bf16, 4 for fp32) and strides >= D; the
+ *    decode update then takes compact rows (x_ld == D) or a row stride that is a multiple of
+ *    8 [the decode PR's row-stride contract]. The element-granular path runs the streaming
+ *    launch only (its own default configuration: 1 channel per lane, 16-row groups, 4-wave
+ *    blocks); with D % 8 != 0 a configuration with vec != 1 is CCONV_ERR_BAD_CONFIG. The
+ *    alignments stated below are those of the vector path.
  *  - Errors fail closed. A problem visible on the host returns its code before anything is
  *    enqueued, leaving every output untouched: NULL required pointer, negative size, W
  *    outside [1, 4] (the pages' kernels are written for at most 4 taps, strip.py module

@@ -60,7 +60,9 @@ def fwd(x=X, x_sb=None, x_st=None, w=WT, w_dt=BF16, bias=BIAS, y=Y, B=2, T=64, D
         (dict(T=-5), SHAPE),
         (dict(W=0), SHAPE),
         (dict(W=5), SHAPE),
-        (dict(D=500), SHAPE),
+        (dict(D=500, y=Y + 1), MISAL),  # any D is accepted: element alignment on that path
+        (dict(D=500, x=X + 1), MISAL),
+        (dict(D=500, x_st=499), STRIDE),
         (dict(x_st=504, D=512), STRIDE),
         (dict(x_st=516), STRIDE),
         (dict(x_sb=-8), STRIDE),
@@ -102,7 +104,7 @@ def bwd(x=X, dy=DY, w=WT, w_dt=BF16, bias=BIAS, dx=DX, dw=DW, dw_dt=BF16, db=DB,
         (dict(dw=None), NULLP),
         (dict(ws=None), NULLP),
         (dict(W=7), SHAPE),
-        (dict(D=12), SHAPE),
+        (dict(D=12, dx=DX + 1), MISAL),
         (dict(dy_st=100), STRIDE),
         (dict(dw_dt=3), DTYPE),
         (dict(w_dt=2), DTYPE),
@@ -165,7 +167,8 @@ def upd(x=X, x_ld=None, state=ST, S=512, idx=IDX, w=WT, w_dt=BF16, bias=BIAS, y=
         (dict(state=None), NULLP),
         (dict(y=None), NULLP),
         (dict(W=5), SHAPE),
-        (dict(D=4100), SHAPE),
+        (dict(D=4100, x_ld=4101), STRIDE),  # neither compact rows nor a stride that is a multiple of 8
+        (dict(D=4100, x=X + 1), MISAL),
         (dict(N=-1), SHAPE),
         (dict(N=(1 << 24) + 1), SHAPE),
         (dict(S=(1 << 19) + 1), SHAPE),
@@ -209,7 +212,7 @@ def test_default_configs_are_valid(which):
     """Every default plan over a grid of shapes is one the library accepts."""
     for B in (1, 3, 8):
         for T in (1, 2, 7, 8, 15, 16, 17, 100, 1000, 8192, 100003):
-            for D in (8, 520, 4096):
+            for D in (8, 520, 4096, 1, 7, 1003):
                 for W in (1, 4):
                     c = cc.cconv_default_config(which, B, T, D, W)
                     assert c.seg_rows % c.rows_per_group == 0 and c.seg_rows >= 8, (which, B, T, D, W, c)
@@ -349,7 +352,7 @@ def fwd_varlen(x=X, x_st=512, cu=CU, nseq=4, total=1000, h0=H0, hT=HT, status=PS
         (dict(nseq=(1 << 24) + 1), SHAPE),
         (dict(total=1 << 31), SHAPE),
         (dict(total=-1), SHAPE),
-        (dict(D=100), SHAPE),
+        (dict(D=100, y=Y + 1), MISAL),
         (dict(x_st=500), STRIDE),
         (dict(cu=CU + 2), MISAL),
         (dict(status=PST + 1), MISAL),
@@ -515,3 +518,19 @@ def bwd_ex(act=1, dx=DX, h0=H0, dh=DH, cu=None, nseq=0, status=None, B=2, T=64, 
 )
 def test_bwd_ex_host_errors(kw, code):
     assert bwd_ex(**kw) == code
+
+
+def test_odd_channel_counts_need_the_narrow_launch():
+    """With D not a multiple of 8 only the one-channel-per-lane plan is accepted."""
+    L = cc.lib()
+    D, T = 500, 64
+    vec4 = cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
+    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, Y, 2, T, D, 4, ctypes.byref(vec4), None) == CONFIG
+    narrow = cc.cconv_default_config("fwd", 2, T, D, 4)
+    assert narrow.vec == 1 and narrow.rows_per_group == 16 and narrow.options == 3
+    # accepted: with y aliasing x it gets as far as the aliasing check
+    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(narrow), None) == ALIAS
+    solo = cc.Config(vec=1, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
+    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(solo), None) == CONFIG
+    nb = cc.cconv_default_config("bwd", 2, T, D, 4)
+    assert nb.vec == 1 and nb.options == 7 and nb.waves_per_block == 4

@@ -1,0 +1,182 @@
+"""GPU parity of the element-granular path (D not a multiple of 8: one channel per lane) for
+every entry point, against the oracle, through the C ABI. Tolerances in parity.py; states bit
+for bit.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import causal_depthwise_short_amd as cc
+import oracle
+import synth_inputs as si
+from parity import TOL_BWD, TOL_FWD, assert_close, bits, canaries_intact, guarded
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _g(t):
+    return None if t is None else t.to(DEV)
+
+
+def _check_train(x, dy, w, b, h0, what, *, config_f=None, config_b=None):
+    y, hT, _ = cc.cconv_fwd_ex(_g(x), _g(w), _g(b), init_state=_g(h0), want_final_state=True)
+    dx, dw, db, dh0, _ = cc.cconv_bwd_ex(_g(x), _g(dy), _g(w), _g(b), init_state=_g(h0), want_d_init_state=True)
+    torch.cuda.synchronize()
+    yr, hTr = oracle.fwd_state(x, h0, w, b)
+    dxr, dwr, dbr, dh0r = oracle.bwd_state(x, h0, dy, w, b)
+    assert_close(y.cpu(), yr, TOL_FWD, f"{what} y")
+    assert_close(dx.cpu(), dxr, TOL_BWD, f"{what} dx")
+    assert_close(dw.cpu(), dwr, TOL_BWD, f"{what} dw")
+    assert_close(db.cpu(), dbr, TOL_BWD, f"{what} dbias")
+    if w.shape[1] > 1:
+        assert np.array_equal(hT.cpu().float().numpy(), hTr), f"{what}: final state"
+        assert_close(dh0.cpu(), dh0r, TOL_BWD, f"{what} d_init_state")
+
+
+@pytest.mark.parametrize("D", [1, 7, 100, 1003])
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
+def test_narrow_train_parity(D, W):
+    inp = si.train_inputs(2, 300, D, W, bias=True, seed=800 + D + W)
+    h0 = si.history_input(2, D, W, seed=801 + D)
+    _check_train(inp["x"], inp["dy"], inp["w"], inp["bias"], h0, f"D{D} W{W}")
+
+
+def test_narrow_plain_entry_points_and_fp32_taps():
+    inp = si.train_inputs(3, 1000, 333, 4, bias=True, seed=810, w_dtype=torch.float32)
+    x, w, b, dy = (_g(inp[k]) for k in ("x", "w", "bias", "dy"))
+    y = cc.cconv_fwd(x, w, b)
+    dx, dw, db = cc.cconv_bwd(x, dy, w, b)
+    torch.cuda.synchronize()
+    _, yr = oracle.fwd(inp["x"], inp["w"], inp["bias"])
+    dxr, dwr, dbr = oracle.bwd(inp["x"], inp["dy"], inp["w"], inp["bias"])
+    assert dw.dtype == torch.float32
+    assert_close(y.cpu(), yr, TOL_FWD, "D333 y")
+    assert_close(dx.cpu(), dxr, TOL_BWD, "D333 dx")
+    assert_close(dw.cpu(), dwr, TOL_BWD, "D333 dw")
+    assert_close(db.cpu(), dbr, TOL_BWD, "D333 dbias")
+
+
+def test_narrow_decode_pr_width():
+    """D = 4100 (not a multiple of 8), 2 x 2048 rows: the whole path against the oracle."""
+    inp = si.train_inputs(2, 2048, 4100, 4, bias=True, seed=820)
+    _check_train(inp["x"], inp["dy"], inp["w"], inp["bias"], None, "D4100")
+
+
+def test_narrow_unaligned_strides_and_guards():
+    """x and dy as column slices at odd offsets of wider tensors (any stride, 2-byte alignment);
+    nothing written outside y and dx."""
+    B, T, D, W = 2, 257, 131, 4
+    big = si.train_inputs(B, T, D + 9, W, bias=True, seed=830)
+    x = big["x"][:, :, 3:3 + D]
+    dy = big["dy"][:, :, 5:5 + D]
+    w, b = big["w"][:D].contiguous(), big["bias"][:D].contiguous()
+    xd, dyd = _g(big["x"])[:, :, 3:3 + D], _g(big["dy"])[:, :, 5:5 + D]
+    y, ybuf, ylo, yhi = guarded((B, T, D), torch.bfloat16, DEV)
+    dx, xbuf, xlo, xhi = guarded((B, T, D), torch.bfloat16, DEV)
+    cc.cconv_fwd(xd, _g(w), _g(b), y=y)
+    cc.cconv_bwd(xd, dyd, _g(w), _g(b), dx=dx)
+    torch.cuda.synchronize()
+    assert canaries_intact(ybuf, ylo, yhi) and canaries_intact(xbuf, xlo, xhi)
+    _, yr = oracle.fwd(x.contiguous(), w, b)
+    dxr, _, _ = oracle.bwd(x.contiguous(), dy.contiguous(), w, b)
+    assert_close(y.cpu(), yr, TOL_FWD, "strided y")
+    assert_close(dx.cpu(), dxr, TOL_BWD, "strided dx")
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_narrow_launch_invariance(i):
+    cfgs = [
+        dict(vec=1, rows_per_group=16, waves_per_block=1, options=3, seg_rows=16),
+        dict(vec=1, rows_per_group=16, waves_per_block=8, options=3, seg_rows=32),
+        dict(vec=1, rows_per_group=16, waves_per_block=2, strips_per_block=2, options=3, seg_rows=48),
+        dict(vec=1, rows_per_group=16, waves_per_block=4, options=3, seg_rows=4096),
+    ]
+    inp = si.train_inputs(2, 700, 199, 4, bias=True, seed=840)
+    x, w, b, dy = (_g(inp[k]) for k in ("x", "w", "bias", "dy"))
+    ref_y = cc.cconv_fwd(x, w, b)
+    ref_dx, ref_dw, _ = cc.cconv_bwd(x, dy, w, b, dw_dtype=torch.float32)
+    cf = cc.Config(**cfgs[i])
+    cb = cc.Config(**dict(cfgs[i], options=7))
+    y = cc.cconv_fwd(x, w, b, config=cf)
+    dx, dw, _ = cc.cconv_bwd(x, dy, w, b, config=cb, dw_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(y), bits(ref_y)) and torch.equal(bits(dx), bits(ref_dx))
+    # fp32 partial sums grouped per launch: rounding-order differences only (~1e-5 here)
+    assert_close(dw.cpu(), ref_dw.cpu(), 1e-4, "narrow dw across launches")
+
+
+def test_narrow_packed_and_epilogue():
+    lens = [100, 0, 1, 3, 250]
+    D, W = 77, 4
+    total = sum(lens)
+    inp = si.train_inputs(1, total, D, W, bias=True, seed=850)
+    x, dy, w, b = inp["x"][0], inp["dy"][0], inp["w"], inp["bias"]
+    h0 = si.history_input(len(lens), D, W, seed=851)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    y, hT, st = cc.cconv_fwd_varlen(_g(x), _g(cu), _g(w), _g(b), _g(h0), want_final_state=True)
+    dx, dw, db, dh0, st2 = cc.cconv_bwd_varlen(_g(x), _g(dy), _g(cu), _g(w), _g(b), _g(h0), want_d_init_state=True)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(st2.item()) == 0
+    ok, yr, hTr = oracle.fwd_varlen(x, cu.numpy(), w, b, h0)
+    _, dxr, dwr, dbr, dh0r = oracle.bwd_varlen(x, dy, cu.numpy(), w, b, h0)
+    assert_close(y.cpu(), yr, TOL_FWD, "packed y")
+    assert np.array_equal(hT.cpu().float().numpy(), hTr)
+    assert_close(dx.cpu(), dxr, TOL_BWD, "packed dx")
+    assert_close(dw.cpu(), dwr, TOL_BWD, "packed dw")
+    assert_close(dh0.cpu(), dh0r, TOL_BWD, "packed dh0")
+    # epilogue, fixed length
+    e = si.train_inputs(2, 150, D, W, bias=True, seed=852)
+    r = si.train_inputs(2, 150, D, W, bias=False, seed=853)["x"]
+    ye, _, _ = cc.cconv_fwd_ex(_g(e["x"]), _g(e["w"]), _g(e["bias"]), activation=None, residual=_g(r))
+    dxe, _, _, _, _ = cc.cconv_bwd_ex(_g(e["x"]), _g(e["dy"]), _g(e["w"]), _g(e["bias"]), activation=None)
+    torch.cuda.synchronize()
+    assert_close(ye.cpu(), oracle.fwd_epi(e["x"], e["w"], e["bias"], residual=r, act=False), TOL_FWD, "epilogue y")
+    assert_close(dxe.cpu(), oracle.bwd_epi(e["x"], e["dy"], e["w"], e["bias"], act=False)[0], TOL_BWD, "epilogue dx")
+
+
+@pytest.mark.parametrize("ld_pad", [0, 3], ids=["compact", "padded"])
+@pytest.mark.parametrize("D", [5, 4100])
+def test_narrow_decode(D, ld_pad):
+    """Decode with any D: compact rows, or rows padded to a stride that is a multiple of 8."""
+    N, S, W = 40, 64, 4
+    inp = si.decode_inputs(N, S, D, W, bias=True, seed=860 + D)
+    ld = D if ld_pad == 0 else ((D + 7) // 8) * 8 + 8
+    xw = torch.zeros(N, ld, dtype=torch.bfloat16)
+    xw[:, :D] = inp["x"]
+    st = inp["state"].to(DEV)
+    y, status = cc.cconv_update(_g(xw)[:, :D], st, _g(inp["state_indices"]), _g(inp["w"]), _g(inp["bias"]))
+    torch.cuda.synchronize()
+    ok, yr, sr = oracle.update(inp["x"], inp["state"], inp["state_indices"], inp["w"], inp["bias"])
+    assert ok and int(status.item()) == 0
+    assert torch.equal(bits(st.cpu()), bits(torch.from_numpy(sr).to(torch.bfloat16)))
+    assert_close(y.cpu(), yr, TOL_FWD, f"decode D{D} ld{ld}")
+    # circular variant, L = W
+    state4 = torch.randn(S, D, W, generator=torch.Generator().manual_seed(861)).to(torch.bfloat16)
+    cs = torch.randint(0, 50, (N,), generator=torch.Generator().manual_seed(862), dtype=torch.int32)
+    st4 = state4.to(DEV)
+    y4, status = cc.cconv_update_ex(_g(xw)[:, :D], st4, _g(inp["state_indices"]), _g(inp["w"]), _g(inp["bias"]),
+                                    cache_seqlens=_g(cs))
+    torch.cuda.synchronize()
+    ok, yr4, sr4 = oracle.update_ex(inp["x"], state4, inp["state_indices"].numpy(), cs.numpy(), inp["w"], inp["bias"])
+    assert ok and int(status.item()) == 0
+    assert torch.equal(bits(st4.cpu()), bits(torch.from_numpy(sr4).to(torch.bfloat16)))
+    assert_close(y4.cpu(), yr4, TOL_FWD, f"circular decode D{D}")
+
+
+def test_narrow_pool():
+    B, T, D, W, S = 3, 90, 45, 4, 7
+    inp = si.train_inputs(B, T, D, W, bias=True, seed=870)
+    state = torch.randn(S, D, W - 1, generator=torch.Generator().manual_seed(871)).to(torch.bfloat16)
+    idx = torch.tensor([5, -1, 2], dtype=torch.int32)
+    has = torch.tensor([1, 0, 0], dtype=torch.uint8)
+    st = state.to(DEV)
+    y, status = cc.cconv_fwd_pool(_g(inp["x"]), _g(inp["w"]), _g(inp["bias"]), st, _g(idx), _g(has))
+    torch.cuda.synchronize()
+    ok, yr, sr = oracle.fwd_pool(inp["x"], state, idx.numpy(), has.numpy(), inp["w"], inp["bias"])
+    assert ok and int(status.item()) == 0
+    assert np.array_equal(st.cpu().float().numpy(), sr)
+    assert_close(y.cpu(), yr, TOL_FWD, "pool y")
