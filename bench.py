@@ -203,7 +203,7 @@ def main():
             res = []
             for u, th, nt in copy_cfgs:
                 t = time_fn(lambda: copy(kind, u, th, nt), reps=10 if not args.profile else 3, warm=2)
-                res.append(((kind + 1) * nbytes / t / 1e9, f"u={u} threads={th} nt={nt}"))
+                res.append(((kind + 1) * nbytes / t / 1e9, f"u={u} threads={th} nt={nt}", (u, th, nt)))
             best[kind] = max(res)
         return best
 
@@ -224,12 +224,15 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
 
-    def med(i, j):
-        v = sorted(events[k][i].elapsed_time(events[k][j]) * 1e-3 for k in range(K))
-        return v[len(v) // 2]
+    def quant(v):
+        v = sorted(v)
+        return v[len(v) // 10], v[len(v) // 2], v[min(len(v) - 1, (9 * len(v)) // 10)]
 
-    t_fwd, t_main, t_fin, t_upd = med(0, 1), med(1, 2), med(2, 3), med(3, 4)
-    t_bwd = med(1, 3)
+    def med(i, j):
+        return quant([events[k][i].elapsed_time(events[k][j]) * 1e-3 for k in range(K)])
+
+    q_fwd, q_main, q_fin, q_upd, q_bwd = med(0, 1), med(1, 2), med(2, 3), med(3, 4), med(1, 3)
+    t_fwd, t_main, t_fin, t_upd, t_bwd = q_fwd[1], q_main[1], q_fin[1], q_upd[1], q_bwd[1]
 
     log("flat copy roofline (after)")
     cp_b = copy_roofline()
@@ -248,10 +251,12 @@ def main():
                           "launch_bwd": cc.cconv_default_config("bwd", B, T, D, W).as_dict()}))
         return
 
-    def phase(nb, t, copy_gbps):
+    def phase(nb, q, copy_gbps):
+        t = q[1]
         gbps = nb / t / 1e9
         return {
             "us": round(t * 1e6, 2),
+            "us_p10_p90": [round(q[0] * 1e6, 2), round(q[2] * 1e6, 2)],
             "bytes": nb,
             "GBps": round(gbps, 1),
             "pct_flat_copy": round(100 * gbps / copy_gbps, 1) if copy_gbps else None,
@@ -259,12 +264,53 @@ def main():
         }
 
     breakdown = {
-        "fwd": phase(bytes_fwd, t_fwd, copy1[0]),
-        "bwd": phase(bytes_bwd, t_bwd, copy2[0]),
-        "bwd_main": phase(bytes_bwd_main, t_main, copy2[0]),
+        "fwd": phase(bytes_fwd, q_fwd, copy1[0]),
+        "bwd": phase(bytes_bwd, q_bwd, copy2[0]),
+        "bwd_main": phase(bytes_bwd_main, q_main, copy2[0]),
         "bwd_finish": {"us": round(t_fin * 1e6, 2), "bytes": bytes_bwd_finish},
-        "update": dict(phase(bytes_upd, t_upd, copy1[0]), cache_resident=True),
+        "update": dict(phase(bytes_upd, q_upd, copy1[0]), cache_resident=True),
     }
+
+    # ---- AB/BA interleaving with the flat copy: kernels and copies alternate in order, so
+    # the percentages also hold under the same clocks and memory state (outside `value`) ----
+    def interleaved(pairs=21):
+        mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        kt, ct = [], []
+        for i in range(pairs):
+            for part in ((0, 1) if i % 2 == 0 else (1, 0)):
+                ev = [mk(), mk(), mk()]
+                if part == 0:
+                    ev[0].record()
+                    cc.cconv_fwd(x, w, b, y=y)
+                    ev[1].record()
+                    cc.cconv_bwd_main(x, dy, w, b, dxo, ws)
+                    ev[2].record()
+                    cc.cconv_bwd_finish(ws, dwo, dbo, B, T, D, W)
+                    kt.append(ev)
+                else:
+                    ev[0].record()
+                    copy(1, *copy1[2])
+                    ev[1].record()
+                    copy(2, *copy2[2])
+                    ev[2].record()
+                    ct.append(ev)
+        torch.cuda.synchronize()
+        f = quant([e[0].elapsed_time(e[1]) * 1e-3 for e in kt])[1]
+        m = quant([e[1].elapsed_time(e[2]) * 1e-3 for e in kt])[1]
+        c1 = 2 * nbytes / quant([e[0].elapsed_time(e[1]) * 1e-3 for e in ct])[1] / 1e9
+        c2 = 3 * nbytes / quant([e[1].elapsed_time(e[2]) * 1e-3 for e in ct])[1] / 1e9
+        return {
+            "pairs": pairs,
+            "fwd_us": round(f * 1e6, 2),
+            "bwd_main_us": round(m * 1e6, 2),
+            "copy_1r1w_GBps": round(c1, 1),
+            "copy_2r1w_GBps": round(c2, 1),
+            "pct_flat_copy": {"fwd": round(100 * bytes_fwd / f / 1e9 / c1, 1),
+                              "bwd_main": round(100 * bytes_bwd_main / m / 1e9 / c2, 1)},
+        }
+
+    log("AB/BA interleaved kernels and flat copies")
+    inter = interleaved()
 
     # ---- CPU baseline: the oracle, timed on a bounded sample of the same workload ---------
     cpu = None
@@ -287,6 +333,14 @@ def main():
         rows = int(max(1, min(B, args.cpu_seconds // max(t_one, 1e-3))))
         log(f"cpu baseline: oracle on {rows} of {B} batch rows ({threads} threads)")
         t_cpu, yr, dxr, dwr, dbr = oracle_rows(rows)
+        # one-thread figure on a smaller sample: the first rows of batch row 0
+        rows1 = 2048
+        oracle.set_threads(1, "f32")
+        t1a = time.perf_counter()
+        oracle.fwd(xf[:1, :rows1], host["w"], host["bias"], precision="f32")
+        oracle.bwd(xf[:1, :rows1], dyf[:1, :rows1], host["w"], host["bias"], precision="f32")
+        t_cpu1 = time.perf_counter() - t1a
+        oracle.set_threads(threads, "f32")
         tu = time.perf_counter()
         ok, ydr, sr = oracle.update(dhost["x"], dhost["state"], dhost["state_indices"], dhost["w"], dhost["bias"],
                                     precision="f32")
@@ -302,6 +356,8 @@ def main():
                 f"+ one decode update N={dshape.N} S={dshape.S}; {t_cpu + t_cpu_upd:.1f} s"
             ),
             "host": platform.processor() or platform.machine(),
+            "value_1thread": round((rows1 * D * 10 + 2 * (w.numel() * w.element_size() + D * 4)) / t_cpu1 / 1e9, 4),
+            "sample_1thread": f"fwd+bwd on rows 0..{rows1 - 1} of batch row 0, one thread; {t_cpu1:.1f} s",
         }
 
         # parity gate: the GPU outputs of the timed configuration against the oracle
@@ -365,6 +421,7 @@ def main():
             "2r1w_GBps": round(copy2[0], 1), "2r1w_kernel": copy2[1],
             "bytes_per_operand": nbytes,
         },
+        "interleaved": inter,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),

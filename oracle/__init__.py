@@ -70,6 +70,7 @@ def _load(path: Path, prec: str):
     lib.oracle_update.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [f, f, i64]
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_real_bytes.restype = ctypes.c_int
     assert lib.oracle_real_bytes() == (8 if prec == "f64" else 4)
     return lib
@@ -128,6 +129,10 @@ class Oracle:
     def threads(self, precision: str = "f32") -> int:
         """OpenMP threads the oracle runs on (OMP_NUM_THREADS, else all host cores)."""
         return self.lib(precision).oracle_threads()
+
+    def set_threads(self, n: int, precision: str = "f32") -> None:
+        """Thread count for later calls of this build (results do not depend on it)."""
+        self.lib(precision).oracle_set_threads(int(n))
 
     def fwd(self, x, w, bias=None, *, precision: str = "f64"):
         """z and y = silu(z) for x [B, T, D], w [D, W], bias [D] or None. Unrounded."""
@@ -387,6 +392,7 @@ update = _default.update
 fwd_pool = _default.fwd_pool
 update_ex = _default.update_ex
 fwd_epi = _default.fwd_epi
+set_threads = _default.set_threads
 bwd_epi = _default.bwd_epi
 fwd_varlen = _default.fwd_varlen
 bwd_varlen = _default.bwd_varlen

@@ -152,6 +152,16 @@ int oracle_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (the CPU baseline's one-thread figure); results do not
+ * depend on it. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Forward: z (optional) and y = z * sigma(z) for every element. */
 void oracle_fwd(const float* x, int64_t B, int64_t T, int64_t D, const float* w, int W,
                 const float* bias, real* z_out, real* y_out) {
