@@ -22,9 +22,9 @@ constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices 
 constexpr int64_t kMaxSequences = int64_t(1) << 24;     // packed sequences per call
 constexpr int64_t kTargetWaves = 1024;  // one wave per SIMD (256 CUs x 4 SIMDs)
 constexpr int64_t kNarrowTargetWaves = 8192;  // the narrow path: several waves per SIMD
-// forward: non-temporal loads and stores, solo kernel; backward: the same plus prefetch
+// forward and backward: non-temporal loads and stores, solo kernel (no software prefetch)
 constexpr int kFwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
-constexpr int kBwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kPrefetch | cconv::kSolo;
+constexpr int kBwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
 constexpr int64_t kMinSeg = 64;         // shorter segments re-read too large a share of rows
 constexpr int64_t kUpdateTargetBlocks = 1024;
 

@@ -104,9 +104,12 @@ constexpr int kNtLoad = 1;    // non-temporal loads of x (and dy)
 constexpr int kNtStore = 2;   // non-temporal stores of y (dx)
 constexpr int kPrefetch = 4;  // next group's loads issued before the current group's math
 constexpr int kSolo = 8;      // one-wave blocks, one wave per SIMD, whole register file (launch-time)
-// Packed batches are compiled for the streaming options only (with or without kSolo).
+// Packed batches (and the epilogue and element-granular variants) are compiled for the
+// streaming options only, with or without kSolo: non-temporal loads and stores, no software
+// prefetch (the backward is issue-bound, and the prefetch's extra live rows cost more
+// register moves than the latency they hide).
 constexpr int kVarlenFwdOptions = kNtLoad | kNtStore;
-constexpr int kVarlenBwdOptions = kNtLoad | kNtStore | kPrefetch;
+constexpr int kVarlenBwdOptions = kNtLoad | kNtStore;
 // Epilogue variants (compile-time, default launch only): no activation (y = z, g = dy), and a
 // residual added to the forward's output after the activation.
 constexpr int kLinear = 16;

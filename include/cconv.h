@@ -186,7 +186,8 @@ cconv_status_t cconv_fwd_pool(const void* x, int64_t x_sb, int64_t x_st, const v
  *                 D, W), or cconv_bwd_workspace_bytes_config(1, total, D, W, config).
  * Limits: total <= 2^31 - 1, nseq <= 2^24. dw and dbias sum over all sequences. The _config
  * variants take a launch configuration as for one batch row of total rows; only the streaming
- * options (options & ~8 == 3 forward, 7 backward) are compiled for packed batches, others
+ * options (options & ~8 == 3: non-temporal loads and stores, no prefetch) are compiled for
+ * packed batches, others
  * give CCONV_ERR_BAD_CONFIG.
  */
 cconv_status_t cconv_fwd_varlen(const void* x, int64_t x_st, const int32_t* cu_seqlens, int64_t nseq, int64_t total,

@@ -397,8 +397,8 @@ def bwd_varlen(x=X, dy=DY, cu=CU, nseq=4, total=1000, h0=H0, dx=DX, dw=DW, db=DB
         (dict(ws=CU), ALIAS),
         (dict(dh=DH + 2), MISAL),
         (dict(ws_bytes=16), WS),
-        (dict(cfg=cc.Config(vec=8, rows_per_group=8, waves_per_block=1, options=11, seg_rows=64)), CONFIG),
-        (dict(cfg=cc.Config(vec=8, rows_per_group=8, waves_per_block=1, options=15, seg_rows=64), ws_bytes=16), WS),
+        (dict(cfg=cc.Config(vec=8, rows_per_group=8, waves_per_block=1, options=15, seg_rows=64)), CONFIG),
+        (dict(cfg=cc.Config(vec=8, rows_per_group=8, waves_per_block=1, options=11, seg_rows=64), ws_bytes=16), WS),
     ],
 )
 def test_bwd_varlen_host_errors(kw, code):
@@ -533,4 +533,4 @@ def test_odd_channel_counts_need_the_narrow_launch():
     solo = cc.Config(vec=1, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
     assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(solo), None) == CONFIG
     nb = cc.cconv_default_config("bwd", 2, T, D, 4)
-    assert nb.vec == 1 and nb.options == 7 and nb.waves_per_block == 4
+    assert nb.vec == 1 and nb.options == 3 and nb.waves_per_block == 4

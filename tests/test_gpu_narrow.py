@@ -100,7 +100,7 @@ def test_narrow_launch_invariance(i):
     ref_y = cc.cconv_fwd(x, w, b)
     ref_dx, ref_dw, _ = cc.cconv_bwd(x, dy, w, b, dw_dtype=torch.float32)
     cf = cc.Config(**cfgs[i])
-    cb = cc.Config(**dict(cfgs[i], options=7))
+    cb = cc.Config(**dict(cfgs[i], options=3))
     y = cc.cconv_fwd(x, w, b, config=cf)
     dx, dw, _ = cc.cconv_bwd(x, dy, w, b, config=cb, dw_dtype=torch.float32)
     torch.cuda.synchronize()

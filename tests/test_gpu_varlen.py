@@ -133,10 +133,10 @@ CONFIGS_F = [
     dict(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=4096),
 ]
 CONFIGS_B = [
-    dict(vec=4, rows_per_group=16, waves_per_block=1, options=15, seg_rows=64),
-    dict(vec=8, rows_per_group=4, waves_per_block=4, options=7, seg_rows=8),
-    dict(vec=4, rows_per_group=8, waves_per_block=8, strips_per_block=2, options=7, seg_rows=24),
-    dict(vec=8, rows_per_group=8, waves_per_block=1, options=15, seg_rows=4096),
+    dict(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64),
+    dict(vec=8, rows_per_group=4, waves_per_block=4, options=3, seg_rows=8),
+    dict(vec=4, rows_per_group=8, waves_per_block=8, strips_per_block=2, options=3, seg_rows=24),
+    dict(vec=8, rows_per_group=8, waves_per_block=1, options=11, seg_rows=4096),
 ]
 
 
