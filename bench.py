@@ -15,7 +15,8 @@ same read:write mix measured in the same run. The CPU oracle is timed beside it 
 sample of the same workload ("cpu_baseline"); that leg also serves as the parity gate.
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
-(--gpus N with N > 1 is refused: this build measures one GPU.)
+(--gpus N with N > 1 is refused: the library runs on one GPU; how the path would shard is a
+design note, not code.)
 """
 
 from __future__ import annotations
@@ -90,7 +91,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(
             f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-            "this build has no multi-GPU path to time.",
+            "the library has no multi-GPU path to time.",
             file=sys.stderr,
         )
         sys.exit(2)

@@ -72,7 +72,8 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 // whole register file (the "solo" kernels), which is what lets deep row groups stay in flight
 // without scratch spills. Segments never drop below kMinSeg rows (the W-1 rows each segment
 // re-reads stay a small share). Forward: 4 channels per lane, 16-row groups. Backward: 8
-// channels per lane, 8-row groups of x and dy with the next group prefetched.
+// channels per lane, 8-row groups of x and dy. D not a multiple of 8: one channel per lane,
+// 16-row groups, 4-wave blocks and about kNarrowTargetWaves waves.
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) {
     (void)W;
     cconv_config_t c;
@@ -83,12 +84,16 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) 
     c.strips_per_block = 1;
     // the narrow path: one channel per lane moves 8x fewer bytes per wave, so it runs several
     // waves per SIMD (the general kernel) instead of one solo wave
-    c.options = narrow ? (bwd ? cconv::kVarlenBwdOptions : cconv::kVarlenFwdOptions) : (bwd ? kBwdOptions : kFwdOptions);
+    if (narrow)
+        c.options = bwd ? cconv::kVarlenBwdOptions : cconv::kVarlenFwdOptions;
+    else
+        c.options = bwd ? kBwdOptions : kFwdOptions;
     // segment length: a multiple of the row group (and of 8), at least kMinSeg rows, at most
     // T rounded up
     const int64_t align = std::max<int64_t>(8, c.rows_per_group);
     const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
-    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / (narrow ? kNarrowTargetWaves : kTargetWaves);
+    const int64_t target = narrow ? kNarrowTargetWaves : kTargetWaves;
+    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / target;
     ts = std::max(kMinSeg, ts - ts % align);
     const int64_t tcap = ((std::max<int64_t>(T, 1) + align - 1) / align) * align;
     c.seg_rows = std::min(ts, tcap);
@@ -114,10 +119,8 @@ bool make_plan(const cconv_config_t& c, int64_t B, int64_t T, int64_t D, Plan* p
     return true;
 }
 
-// Checks shared by the forward and backward: shape, dtype, strides, alignment of x-like
-// inputs and of the taps/bias.
-cconv_status_t check_train_common(const void* w, cconv_dtype_t w_dtype, const float* bias, int64_t B,
-                                  int64_t T, int64_t D, int W) {
+// Checks shared by the forward and backward before a plan exists: sizes, width, tap dtype.
+cconv_status_t check_train_common(cconv_dtype_t w_dtype, int64_t B, int64_t T, int64_t D, int W) {
     if (B < 0 || T < 0 || D < 0 || B > kMaxDim || T > kMaxDim || D > kMaxDim) return CCONV_ERR_BAD_SHAPE;
     if (W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
     if (D > kMaxChannels) return CCONV_ERR_BAD_SHAPE;
@@ -230,7 +233,7 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     // a pointer may be NULL only when its tensor is empty
     const bool act_empty = (B == 0 || T == 0 || D == 0);
     if ((!x && !act_empty) || (!w && D > 0) || (!y && !act_empty)) return CCONV_ERR_NULL_POINTER;
-    cconv_status_t st = check_train_common(w, w_dtype, bias, B, T, D, W);
+    cconv_status_t st = check_train_common(w_dtype, B, T, D, W);
     if (st != CCONV_OK) return st;
     const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
@@ -316,7 +319,7 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
         dbias = nullptr;
         dw_dtype = CCONV_BF16;
     }
-    cconv_status_t st = check_train_common(w, w_dtype, bias, B, T, D, W);
+    cconv_status_t st = check_train_common(w_dtype, B, T, D, W);
     if (st != CCONV_OK) return st;
     if (!dtype_ok(dw_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
     const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W);

@@ -18,7 +18,7 @@ struct Plan {
     int waves;
     int ws;  // strips per block
     int64_t seg_rows;
-    int options;  // kNtLoad | kNtStore | kPrefetch
+    int options;  // kNtLoad | kNtStore | kPrefetch | kSolo, plus the epilogue bits kLinear | kResidual
     // derived
     int64_t strips;        // ceil(D / (64*vec))
     int64_t strip_groups;  // ceil(strips / ws)

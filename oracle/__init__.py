@@ -131,7 +131,7 @@ class Oracle:
         return self.lib(precision).oracle_threads()
 
     def set_threads(self, n: int, precision: str = "f32") -> None:
-        """Thread count for later calls of this build (results do not depend on it)."""
+        """Thread count for later calls of the library of this precision (results do not depend on it)."""
         self.lib(precision).oracle_set_threads(int(n))
 
     def fwd(self, x, w, bias=None, *, precision: str = "f64"):
