@@ -232,3 +232,34 @@ def test_varlen_graph_replay():
         for got, want, nm in ((y, ref[0], "y"), (hT, ref[1], "hT"), (dx, ref[2], "dx"), (dw, ref[3], "dw"),
                               (db, ref[4], "dbias"), (dh, ref[5], "dh0")):
             assert torch.equal(bits(got), bits(want)), f"replay {r}: {nm}"
+
+
+def test_varlen_beyond_2_31_elements():
+    """A packed batch of 600,000 rows x 4096 channels (2.5e9 elements, 4.9 GB per tensor) in three
+    sequences: y and dx bit for bit as the fixed-length path on the same sequences (zero
+    histories), the final states the last rows of each sequence."""
+    D, W = 4096, 4
+    lens = [300_000, 1, 299_999]
+    total = sum(lens)
+    assert total * D > 2**31
+    g = si.train_inputs_device(1, total, D, W, bias=True, seed=270)
+    x, dy = g["x"][0], g["dy"][0]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    y, hT, st = cc.cconv_fwd_varlen(x, cu, g["w"], g["bias"], want_final_state=True)
+    dx, _, _, _, st2 = cc.cconv_bwd_varlen(x, dy, cu, g["w"], g["bias"])
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(st2.item()) == 0
+    a = 0
+    for i, L in enumerate(lens):
+        xs, dys = x[a:a + L][None], dy[a:a + L][None]
+        yb = cc.cconv_fwd(xs, g["w"], g["bias"])
+        dxb, _, _ = cc.cconv_bwd(xs, dys, g["w"], g["bias"])
+        torch.cuda.synchronize()
+        assert torch.equal(y[a:a + L].view(torch.int16), yb[0].view(torch.int16)), i
+        assert torch.equal(dx[a:a + L].view(torch.int16), dxb[0].view(torch.int16)), i
+        tail = torch.zeros(W - 1, D, dtype=torch.bfloat16, device=DEV)
+        k = min(L, W - 1)
+        tail[W - 1 - k:] = x[a + L - k:a + L]
+        assert torch.equal(hT[i].view(torch.int16), tail.transpose(0, 1).contiguous().view(torch.int16)), i
+        del yb, dxb
+        a += L
