@@ -34,10 +34,50 @@ __device__ __forceinline__ void ring_from_state(const uint16_t (&h)[VEC * (L > 0
 
 // VEC = 8: a thread owns 8 channels (16-byte x rows, 16*L-byte state runs); VEC = 1: one channel
 // (any D, any row stride).
+// The thread's channels of one row: x (VEC values) and the state entries of slot s (VEC x L
+// values, entry e of channel d+v at 16-bit position v*L + e).
+template <int L, int VEC>
+__device__ __forceinline__ void gather_row(const UpdateArgs& a, int64_t n, int64_t s, int64_t d, Row<VEC>& rx,
+                                           uint16_t (&h)[VEC * (L > 0 ? L : 1)]) {
+    rx = load_row<VEC>(a.x + n * a.x_ld + d);
+    const uint16_t* __restrict__ sp = a.state + (s * a.D + d) * L;
+    if constexpr (L > 0 && VEC == 1) {
+        for (int e = 0; e < L; ++e) h[e] = sp[e];
+    } else if constexpr (L > 0) {
+#pragma unroll
+        for (int q = 0; q < L; ++q) {
+            const uint4 v4 = reinterpret_cast<const uint4*>(sp)[q];
+            const uint32_t u[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                h[q * 8 + 2 * i] = static_cast<uint16_t>(u[i] & 0xffffu);
+                h[q * 8 + 2 * i + 1] = static_cast<uint16_t>(u[i] >> 16);
+            }
+        }
+    }
+}
+
+// VEC = 8: a thread owns 8 channels (16-byte x rows, 16*L-byte state runs); VEC = 1: one channel
+// (any D, any row stride).
 template <int W, int L, bool CIRC, int VEC>
 __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
     constexpr int R = W > 1 ? W - 1 : 1;
     extern __shared__ uint32_t seen[];
+
+    const int64_t d = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * VEC;
+    const bool lane = d < a.D;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * a.rows_per_block;
+    const int64_t n1 = min(n0 + a.rows_per_block, a.N);
+
+    // The block's first row is gathered before the slot check, so its loads overlap the check;
+    // a slot outside [0, S) is not read, and nothing is stored before the verdict.
+    Row<VEC> rx0 = zero_row<VEC>();
+    uint16_t h0[VEC * (L > 0 ? L : 1)];
+    int64_t s0 = -1;
+    if (lane && n0 < n1) {
+        s0 = a.idx ? static_cast<int64_t>(a.idx[n0]) : n0;
+        if (s0 >= 0 && s0 < a.S) gather_row<L, VEC>(a, n0, s0, d, rx0, h0);
+    }
 
     bool bad = a.idx ? block_slots_bad(a.idx, a.N, a.S, seen) : false;
     if (CIRC) {  // every cache_seqlens entry must be >= 0
@@ -48,46 +88,32 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
     }
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && a.status)
         a.status[0] = bad ? CCONV_ERR_INDEX : CCONV_OK;
-    if (bad) return;
-
-    const int64_t d = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * VEC;
-    if (d >= a.D) return;
+    if (bad || !lane) return;
 
     float tap[W][VEC];
     load_taps<VEC, W>(a.w, a.w_f32, d, tap);
     float bs[VEC];
     load_bias<VEC>(a.bias, d, bs);
 
-    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * a.rows_per_block;
-    const int64_t n1 = min(n0 + a.rows_per_block, a.N);
     for (int64_t n = n0; n < n1; ++n) {
-        const int64_t s = a.idx ? static_cast<int64_t>(a.idx[n]) : n;
+        const bool first = (n == n0);
+        const int64_t s = first ? s0 : (a.idx ? static_cast<int64_t>(a.idx[n]) : n);
         uint16_t* __restrict__ yp = a.y + n * a.D + d;
         if (s < 0) {  // padding row: no state access, output 0
             store_row<VEC>(yp, zero_row<VEC>());
             continue;
         }
-        const Row<VEC> rx = load_row<VEC>(a.x + n * a.x_ld + d);
+        Row<VEC> rx = rx0;
+        uint16_t h[VEC * (L > 0 ? L : 1)];
+        if (first) {
+#pragma unroll
+            for (int i = 0; i < VEC * (L > 0 ? L : 1); ++i) h[i] = h0[i];
+        } else {
+            gather_row<L, VEC>(a, n, s, d, rx, h);
+        }
         float xt[VEC];
         widen(rx, xt);
-        // the thread's 8 channels x L entries: 16*L contiguous bytes, entry e of channel d+v at
-        // 16-bit position v*L + e
-        uint16_t h[VEC * (L > 0 ? L : 1)];
         uint16_t* __restrict__ sp = a.state + (s * a.D + d) * L;
-        if constexpr (L > 0 && VEC == 1) {
-            for (int e = 0; e < L; ++e) h[e] = sp[e];
-        } else if constexpr (L > 0) {
-#pragma unroll
-            for (int q = 0; q < L; ++q) {
-                const uint4 v4 = reinterpret_cast<const uint4*>(sp)[q];
-                const uint32_t u[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    h[q * 8 + 2 * i] = static_cast<uint16_t>(u[i] & 0xffffu);
-                    h[q * 8 + 2 * i + 1] = static_cast<uint16_t>(u[i] >> 16);
-                }
-            }
-        }
         float ring[R][VEC];
         int rot = 0;  // circular: the entry that takes the token (block-uniform: one row at a time)
         if constexpr (W > 1) {
