@@ -71,15 +71,16 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 // waves beat more, shorter ones for both kernels, and a wave alone on its SIMD may use the
 // whole register file (the "solo" kernels), which is what lets deep row groups stay in flight
 // without scratch spills. Segments never drop below kMinSeg rows (the W-1 rows each segment
-// re-reads stay a small share). Forward: 4 channels per lane, 16-row groups. Backward: 8
-// channels per lane, 8-row groups of x and dy. D not a multiple of 8: one channel per lane,
-// 16-row groups, 4-wave blocks and about kNarrowTargetWaves waves.
+// re-reads stay a small share). Forward and backward: 4 channels per lane, 16-row groups (the
+// backward loads 16 rows of x and 16 of dy per group: 16 KiB in flight per wave). D not a
+// multiple of 8: one channel per lane, 16-row groups, 4-wave blocks and about
+// kNarrowTargetWaves waves.
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) {
     (void)W;
     cconv_config_t c;
     const bool narrow = (D % 8 != 0);
-    c.vec = narrow ? 1 : (bwd ? 8 : 4);
-    c.rows_per_group = (bwd && !narrow) ? 8 : 16;
+    c.vec = narrow ? 1 : 4;
+    c.rows_per_group = 16;
     c.waves_per_block = narrow ? 4 : 1;
     c.strips_per_block = 1;
     // the narrow path: one channel per lane moves 8x fewer bytes per wave, so it runs several

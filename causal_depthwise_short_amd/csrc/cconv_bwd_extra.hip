@@ -1,6 +1,6 @@
 // cconv_bwd_extra.hip -- the backward's packed-batch kernels (every (vec, group) pair,
-// streaming options), its variant without an activation (g = dy; the default launch only: 8
-// channels per lane, 8-row groups, one-wave solo blocks), and the element-granular path (one
+// streaming options), its variant without an activation (g = dy; the default launch only: 4
+// channels per lane, 16-row groups, one-wave solo blocks), and the element-granular path (one
 // channel per lane, for D not a multiple of 8), fixed-length and packed.
 #include "cconv_bwd_body.hpp"
 
@@ -40,10 +40,10 @@ template <bool VL>
 hipError_t launch_lin(int W, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
     constexpr int F = kVarlenBwdOptions | kLinear;
     switch (W) {
-        case 1: return launch_k<8, 8, 1, F, VL, true>(grid, block, lds, a, s);
-        case 2: return launch_k<8, 8, 2, F, VL, true>(grid, block, lds, a, s);
-        case 3: return launch_k<8, 8, 3, F, VL, true>(grid, block, lds, a, s);
-        case 4: return launch_k<8, 8, 4, F, VL, true>(grid, block, lds, a, s);
+        case 1: return launch_k<4, 16, 1, F, VL, true>(grid, block, lds, a, s);
+        case 2: return launch_k<4, 16, 2, F, VL, true>(grid, block, lds, a, s);
+        case 3: return launch_k<4, 16, 3, F, VL, true>(grid, block, lds, a, s);
+        case 4: return launch_k<4, 16, 4, F, VL, true>(grid, block, lds, a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -74,7 +74,7 @@ bool bwd_launch_exists(int vec, int group, int options, bool packed) {
     const int base = options & ~(kSolo | kLinear);
     if (vec == 1) return !(options & kSolo) && base == kVarlenBwdOptions;
     if (!(options & kLinear)) return packed ? base == kVarlenBwdOptions : true;
-    return vec == 8 && group == 8 && (options & kSolo) && base == kVarlenBwdOptions;
+    return vec == 4 && group == 16 && (options & kSolo) && base == kVarlenBwdOptions;
 }
 
 hipError_t launch_bwd_extra(const Plan& p, int W, const BwdArgs& a, hipStream_t s) {
