@@ -14,6 +14,12 @@ against MI355X's 8 TB/s HBM peak ("roofline"), and every phase against a flat co
 same read:write mix measured in the same run. The CPU oracle is timed beside it on a bounded
 sample of the same workload ("cpu_baseline"); that leg also serves as the parity gate.
 
+After the headline (outside the printed value), every widened row of the path is timed alone
+at its own workload ("variants": a history in and the final state or its gradient out, prefill
+into a decode pool, a packed batch of mixed lengths, no activation and a residual, a D that is
+not a multiple of 8, and the decode state of W entries, shifted or circular), each checked
+against the oracle on a sample and the oracle timed on that sample.
+
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
 (--gpus N with N > 1 is refused: the library runs on one GPU; how the path would shard is a
 design note, not code.)
@@ -83,6 +89,308 @@ def read_traffic():
         return float(vals["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo, dwo, dbo, ws, quant, copy1, copy2,
+                 peak, rounds=7, reps=5):
+    """Times each widened row of the path alone at its own workload and keeps, for the parity
+    check in the oracle leg, host copies of the GPU outputs of a sample (batch row 0, the first
+    packed sequences, or the whole decode call) together with the inputs the oracle needs.
+    Algorithmic bytes as for the headline phases, plus each row's own state traffic.
+
+    All inputs are set up first; then a sustained warm-up; then `rounds` round-robin passes
+    over the variants, `reps` back-to-back calls each (event-timed), so that no variant is
+    timed right after an idle gap; the parity samples are copied out only after all timing."""
+    B, T, D, W = s.B, s.T, s.D, s.W
+    R = W - 1
+    n = B * T * D
+    wb = w.numel() * w.element_size()
+    fwd_b = 4 * n + wb + D * 4
+    bwd_b = 6 * n + wb + 2 * D * 4 + dwo.numel() * dwo.element_size()
+    hist_b = B * D * R * 2
+    st = torch.empty(1, dtype=torch.int32, device=dev)
+    S = {"_host": {
+        "x1": host["x"][:1], "dy1": host["dy"][:1], "w": host["w"], "b": host["bias"],
+        "xp": host["x"].view(B * T, D), "dyp": host["dy"].view(B * T, D),
+        "xd": dhost["x"], "idxd": dhost["state_indices"], "wd": dhost["w"], "bd": dhost["bias"],
+    }}
+    todo = []  # (name, what, workload, bytes, fn, copy GB/s, extra, capture)
+
+    def sync_ok():
+        torch.cuda.synchronize()
+        return int(st.item()) == 0
+
+    shape = f"[{B},{T},{D}] W={W}"
+    # state handoff: a history before t = 0 in, the final state (forward) or the history's
+    # gradient (backward) out, [B, D, W-1] each
+    h0 = si.history_input(B, D, W, seed=s.seed)
+    h0d = h0.to(dev)
+    hT, dh0 = torch.empty_like(h0d), torch.empty_like(h0d)
+
+    def cap_fwd_state():
+        torch.cuda.synchronize()
+        S["fwd_state"] = {"h0": h0[:1], "y": y[0].cpu(), "hT": hT[0].cpu()}
+
+    def cap_bwd_state():
+        torch.cuda.synchronize()
+        S["bwd_state"] = {"h0": h0[:1], "dx": dxo[0].cpu(), "dh0": dh0[0].cpu()}
+
+    todo.append(("fwd_state", "forward from a history, final state out", shape, fwd_b + 2 * hist_b,
+                 lambda: cc.cconv_fwd_state(x, w, b, h0d, final_state=hT, y=y), copy1, {}, cap_fwd_state))
+    todo.append(("bwd_state", "backward with a history, its gradient out", shape, bwd_b + 2 * hist_b,
+                 lambda: cc.cconv_bwd_state(x, dy, w, b, h0d, dx=dxo, dw=dwo, dbias=dbo, d_init_state=dh0,
+                                            workspace=ws), copy2, {}, cap_bwd_state))
+
+    # prefill into a decode pool of 64 slots: rows 0, 1, 3, 4, 6, 7 continue from their slot,
+    # rows 2 and 5 start fresh; every row's final state goes back to its slot
+    Sp = 64
+    g = torch.Generator().manual_seed(s.seed + 2000)
+    pool = si.history_input(Sp, D, W, seed=s.seed + 7)
+    idx = torch.randperm(Sp, generator=g)[:B].to(torch.int32)
+    has = (torch.arange(B) % 3 != 2).to(torch.uint8)
+    poold, idxd, hasd = pool.to(dev), idx.to(dev), has.to(dev)
+    fn_pool = lambda: cc.cconv_fwd_pool(x, w, b, poold, idxd, hasd, y=y, status=st)  # noqa: E731
+
+    def cap_pool():
+        poold.copy_(pool.to(dev))
+        fn_pool()
+        ok = sync_ok()
+        S["fwd_pool"] = {"pool": pool, "idx": idx[:1], "has": has[:1], "y": y[0].cpu(),
+                         "slot": poold[int(idx[0])].cpu(), "status_ok": ok}
+
+    todo.append(("fwd_pool", "prefill into a decode pool (slot indices, has_initial_state)",
+                 f"{shape}, pool [{Sp},{D},{R}]", fwd_b + int(has.sum()) * D * R * 2 + hist_b + B * 5, fn_pool, copy1,
+                 {}, cap_pool))
+
+    # packed batch: the same B*T rows as one [total, D] batch of a log-uniform length mix,
+    # each sequence with its own history, final state and history gradient
+    lens = si.packed_lengths(B * T, seed=s.seed + 3)
+    nseq = len(lens)
+    cu = torch.zeros(nseq + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    cud = cu.to(dev)
+    h0v = si.history_input(nseq, D, W, seed=s.seed + 11)
+    h0vd = h0v.to(dev)
+    hTv, dh0v = torch.empty_like(h0vd), torch.empty_like(h0vd)
+    xp, dyp, yp, dxp = (t.view(B * T, D) for t in (x, dy, y, dxo))
+    wsv = torch.empty(cc.cconv_bwd_workspace_bytes(1, B * T, D, W) // 4 + 1, dtype=torch.float32, device=dev)
+    vb = 2 * nseq * D * R * 2 + (nseq + 1) * 4
+    work = f"[{B * T},{D}] W={W}, {nseq} sequences of 1..{max(lens)} rows"
+    fnf = lambda: cc.cconv_fwd_varlen(xp, cud, w, b, h0vd, final_state=hTv, want_final_state=True,  # noqa: E731
+                                      y=yp, status=st)
+    fnb = lambda: cc.cconv_bwd_varlen(xp, dyp, cud, w, b, h0vd, dx=dxp, dw=dwo, dbias=dbo,  # noqa: E731
+                                      d_init_state=dh0v, want_d_init_state=True, workspace=wsv, status=st)
+
+    def cap_varlen():
+        k = max(1, int((cu[1:] <= 12288).sum()))
+        rows = int(cu[k])
+        fnf()
+        okf = sync_ok()
+        fnb()
+        okb = sync_ok()
+        S["varlen"] = {"rows": rows, "cu": cu[: k + 1], "h0": h0v[:k], "y": yp[:rows].cpu(), "hT": hTv[:k].cpu(),
+                       "dx": dxp[:rows].cpu(), "dh0": dh0v[:k].cpu(), "status_ok": okf and okb}
+
+    todo.append(("fwd_varlen", "packed batch forward (histories in, final states out)", work, fwd_b + vb, fnf,
+                 copy1, {}, None))
+    todo.append(("bwd_varlen", "packed batch backward (histories in, their gradients out)", work, bwd_b + vb, fnb,
+                 copy2, {}, cap_varlen))
+
+    # epilogues: no activation with a residual added (forward), no activation (backward)
+    def cap_lin_f():
+        torch.cuda.synchronize()
+        S["fwd_linear_residual"] = {"y": y[0].cpu()}
+
+    def cap_lin_b():
+        torch.cuda.synchronize()
+        S["bwd_linear"] = {"dx": dxo[0].cpu()}
+
+    todo.append(("fwd_linear_residual", "forward without activation, residual added (dy as the residual)", shape,
+                 6 * n + wb + D * 4, lambda: cc.cconv_fwd_ex(x, w, b, activation=None, residual=dy, y=y), copy2, {},
+                 cap_lin_f))
+    todo.append(("bwd_linear", "backward without activation", shape, bwd_b,
+                 lambda: cc.cconv_bwd_ex(x, dy, w, b, activation=None, dx=dxo, dw=dwo, dbias=dbo, workspace=ws),
+                 copy2, {}, cap_lin_b))
+
+    # any D: D = 4100 takes the element-granular path (one channel per lane)
+    Dn = 4100
+    nin = si.train_inputs_device(B, T, Dn, W, bias=True, seed=s.seed + 5, device=dev)
+    xn, wn, bn, dyn = nin["x"], nin["w"], nin["bias"], nin["dy"]
+    yn, dxn = torch.empty_like(xn), torch.empty_like(xn)
+    dwn, dbn = torch.empty_like(wn), torch.empty(Dn, dtype=torch.float32, device=dev)
+    wsn = torch.empty(cc.cconv_bwd_workspace_bytes(B, T, Dn, W) // 4 + 1, dtype=torch.float32, device=dev)
+    nn_ = B * T * Dn
+    wnb = wn.numel() * wn.element_size()
+    work = f"[{B},{T},{Dn}] W={W}"
+
+    def cap_any():
+        torch.cuda.synchronize()
+        S["any_d"] = {"x": xn[:1].cpu(), "dy": dyn[:1].cpu(), "w": wn.cpu(), "b": bn.cpu(), "y": yn[0].cpu(),
+                      "dx": dxn[0].cpu()}
+
+    todo.append(("fwd_any_d", "forward, D not a multiple of 8 (one channel per lane)", work, 4 * nn_ + wnb + Dn * 4,
+                 lambda: cc.cconv_fwd(xn, wn, bn, y=yn), copy1, {}, None))
+    todo.append(("bwd_any_d", "backward, D not a multiple of 8 (one channel per lane)", work,
+                 6 * nn_ + 2 * wnb + 2 * Dn * 4,
+                 lambda: cc.cconv_bwd(xn, dyn, wn, bn, dx=dxn, dw=dwn, dbias=dbn, workspace=wsn), copy2, {}, cap_any))
+
+    # decode variants at the decode workload: a state of L = W entries, rewritten (shift) or
+    # addressed as a circular buffer by cache_seqlens (one entry written per channel)
+    Nd, Sd, Dd = dshape.N, dshape.S, dshape.D
+    g = torch.Generator().manual_seed(dshape.seed + 9)
+    st4 = torch.randn(Sd, Dd, W, generator=g).to(torch.bfloat16)
+    cs = torch.randint(0, 1 << 20, (Nd,), generator=g, dtype=torch.int32)
+    xdd, idd = dhost["x"].to(dev), dhost["state_indices"].to(dev)
+    wdd, bdd = dhost["w"].to(dev), dhost["bias"].to(dev)
+    st4d, csd = st4.to(dev), cs.to(dev)
+    yd4 = torch.empty(Nd, Dd, dtype=torch.bfloat16, device=dev)
+    fixed = 4 * Nd * Dd + dhost["w"].numel() * dhost["w"].element_size() + Dd * 4 + Nd * 4
+    work = f"x [{Nd},{Dd}], state [{Sd},{Dd},{W}], W={W}"
+    for name, what, nb, kw in (
+        ("update_shift_l4", "decode, state of L = W entries, shifted", fixed + 2 * Nd * Dd * (R + W), {}),
+        ("update_circular_l4", "decode, circular state (cache_seqlens)", fixed + 2 * Nd * Dd * (R + 1) + Nd * 4,
+         {"cache_seqlens": csd}),
+    ):
+        fn = lambda kw=kw: cc.cconv_update_ex(xdd, st4d, idd, wdd, bdd, y=yd4, status=st, **kw)  # noqa: E731
+
+        def cap(name=name, fn=fn, kw=kw):
+            st4d.copy_(st4.to(dev))
+            fn()
+            ok = sync_ok()
+            S[name] = {"state": st4, "cs": cs if kw else None, "y": yd4.cpu(), "new_state": st4d.cpu(),
+                       "status_ok": ok}
+
+        todo.append((name, what, work, nb, fn, copy1, {"cache_resident": True}, cap))
+
+    # sustained warm-up (every variant, then the plain path for ~30 ms), then the rounds
+    for item in todo:
+        item[4]()
+    torch.cuda.synchronize()
+    for _ in range(60):
+        cc.cconv_fwd(x, w, b, y=y)
+    times = {item[0]: [] for item in todo}
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for _ in range(rounds):
+        evs = []
+        for item in todo:
+            for _ in range(reps):
+                e0, e1 = mk(), mk()
+                e0.record()
+                item[4]()
+                e1.record()
+                evs.append((item[0], e0, e1))
+        torch.cuda.synchronize()
+        for name, e0, e1 in evs:
+            times[name].append(e0.elapsed_time(e1) * 1e-3)
+    V = {}
+    for name, what, workload, nb, _, copy_gbps, extra, _ in todo:
+        q = quant(times[name])
+        gbps = nb / q[1] / 1e9
+        V[name] = {
+            "what": what, "workload": workload, "us": round(q[1] * 1e6, 2),
+            "us_p10_p90": [round(q[0] * 1e6, 2), round(q[2] * 1e6, 2)], "bytes": nb, "GBps": round(gbps, 1),
+            "pct_flat_copy": round(100 * gbps / copy_gbps, 1), "pct_hbm_peak": round(100 * gbps / peak, 1),
+            "parity": None, **extra,
+        }
+    # parity samples, after all timing: each variant runs again first (the variants share the
+    # output buffers)
+    for item in todo:
+        if item[7] is not None:
+            item[4]()
+            item[7]()
+    del nin, xn, dyn, yn, dxn, wsn
+    return V, S
+
+
+def oracle_variants(oracle, np, torch, S, err):
+    """The oracle on each variant's sample: its throughput (algorithmic bytes of the sample over
+    the oracle's time) and the parity of the GPU outputs against it (max |gpu - oracle| /
+    max(1, |oracle|); 5e-3 for forward outputs, 8e-3 for gradients; states bit for bit)."""
+    import time as _t
+
+    H = S["_host"]
+    cpu, gate = {}, {}
+    bits = lambda t: t.contiguous().view(torch.int16)  # noqa: E731
+
+    def same(g, r):
+        return bool(torch.equal(bits(g), bits(torch.from_numpy(np.asarray(r, np.float32)).to(torch.bfloat16))))
+
+    def put(name, t, nbytes, sample, checks):
+        cpu[name] = {"GBps": round(nbytes / t / 1e9, 4), "s": round(t, 2), "sample": sample}
+        gate[name] = dict(checks, **{"pass": all(v is True or (isinstance(v, float) and v <= lim)
+                                                 for (v, lim) in checks.values())})
+
+    x1, dy1, w, b = H["x1"], H["dy1"], H["w"], H["b"]
+    T, D, W = x1.shape[1], x1.shape[2], w.shape[1]
+    one = f"batch row 0 ({T} x {D})"
+    t0 = _t.perf_counter()
+    yr, hTr = oracle.fwd_state(x1, S["fwd_state"]["h0"], w, b, precision="f32")
+    t = _t.perf_counter() - t0
+    v = S["fwd_state"]
+    put("fwd_state", t, 4 * T * D, one, {"y": (err(v["y"].float(), yr[0]), 5e-3),
+                                           "final_state_bit_exact": (same(v["hT"], hTr[0]), None)})
+    t0 = _t.perf_counter()
+    dxr, _, _, dh0r = oracle.bwd_state(x1, S["bwd_state"]["h0"], dy1, w, b, precision="f32")
+    t = _t.perf_counter() - t0
+    v = S["bwd_state"]
+    put("bwd_state", t, 6 * T * D, one, {"dx": (err(v["dx"].float(), dxr[0]), 8e-3),
+                                           "d_init_state": (err(v["dh0"].float(), dh0r[0]), 8e-3)})
+    v = S["fwd_pool"]
+    t0 = _t.perf_counter()
+    ok, yr, sr = oracle.fwd_pool(x1, v["pool"], v["idx"].numpy(), v["has"].numpy(), w, b, precision="f32")
+    t = _t.perf_counter() - t0
+    put("fwd_pool", t, 4 * T * D, one, {"y": (err(v["y"].float(), yr[0]), 5e-3),
+                                          "slot_bit_exact": (bool(ok and v["status_ok"]) and same(v["slot"], sr[int(v["idx"][0])]), None)})
+    v = S["varlen"]
+    rows = v["rows"]
+    xs, dys = H["xp"][:rows], H["dyp"][:rows]
+    t0 = _t.perf_counter()
+    okf, yr, hTr = oracle.fwd_varlen(xs, v["cu"].numpy(), w, b, v["h0"], precision="f32")
+    t1 = _t.perf_counter()
+    okb, dxr, _, _, dh0r = oracle.bwd_varlen(xs, dys, v["cu"].numpy(), w, b, v["h0"], precision="f32")
+    t2 = _t.perf_counter()
+    samp = f"the first {len(v['cu']) - 1} sequences ({rows} rows)"
+    put("fwd_varlen", t1 - t0, 4 * rows * D, samp,
+        {"y": (err(v["y"].float(), yr), 5e-3),
+         "final_state_bit_exact": (bool(okf and v["status_ok"]) and same(v["hT"], hTr), None)})
+    put("bwd_varlen", t2 - t1, 6 * rows * D, samp,
+        {"dx": (err(v["dx"].float(), dxr) if okb else 1.0, 8e-3),
+         "d_init_state": (err(v["dh0"].float(), dh0r) if okb else 1.0, 8e-3)})
+    t0 = _t.perf_counter()
+    yr = oracle.fwd_epi(x1, w, b, residual=dy1, act=False, precision="f32")
+    t = _t.perf_counter() - t0
+    put("fwd_linear_residual", t, 6 * T * D, one, {"y": (err(S["fwd_linear_residual"]["y"].float(), yr[0]), 5e-3)})
+    t0 = _t.perf_counter()
+    dxr = oracle.bwd_epi(x1, dy1, w, b, act=False, precision="f32")[0]
+    t = _t.perf_counter() - t0
+    put("bwd_linear", t, 6 * T * D, one, {"dx": (err(S["bwd_linear"]["dx"].float(), dxr[0]), 8e-3)})
+    v = S["any_d"]
+    Dn = v["x"].shape[2]
+    t0 = _t.perf_counter()
+    _, yr = oracle.fwd(v["x"], v["w"], v["b"], precision="f32")
+    t1 = _t.perf_counter()
+    dxr, _, _ = oracle.bwd(v["x"], v["dy"], v["w"], v["b"], precision="f32")
+    t2 = _t.perf_counter()
+    oned = f"batch row 0 ({T} x {Dn})"
+    put("fwd_any_d", t1 - t0, 4 * T * Dn, oned, {"y": (err(v["y"].float(), yr[0]), 5e-3)})
+    put("bwd_any_d", t2 - t1, 6 * T * Dn, oned, {"dx": (err(v["dx"].float(), dxr[0]), 8e-3)})
+    for name in ("update_shift_l4", "update_circular_l4"):
+        v = S[name]
+        N, Dd = v["y"].shape
+        Wd = v["state"].shape[2]
+        t0 = _t.perf_counter()
+        ok, yr, sr = oracle.update_ex(H["xd"], v["state"], H["idxd"].numpy(), None if v["cs"] is None else v["cs"].numpy(),
+                                      H["wd"], H["bd"], precision="f32")
+        t = _t.perf_counter() - t0
+        nb = 2 * N * Dd * (1 + (Wd - 1) + (Wd if v["cs"] is None else 1) + 1)
+        put(name, t, nb, f"the whole call (N={N})",
+            {"y": (err(v["y"].float(), yr) if ok else 1.0, 5e-3),
+             "state_bit_exact": (bool(ok and v["status_ok"]) and same(v["new_state"], sr), None)})
+    for g in gate.values():
+        for k_, val in list(g.items()):
+            if isinstance(val, tuple):
+                g[k_] = val[0]
+    return cpu, gate
 
 
 def main():
@@ -181,6 +489,10 @@ def main():
                                    cur().cuda_stream)
         assert rc == 0
 
+    def quant(v):
+        v = sorted(v)
+        return v[len(v) // 10], v[len(v) // 2], v[min(len(v) - 1, (9 * len(v)) // 10)]
+
     def time_fn(fn, reps=20, warm=3):
         for _ in range(warm):
             fn()
@@ -224,10 +536,6 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
-
-    def quant(v):
-        v = sorted(v)
-        return v[len(v) // 10], v[len(v) // 2], v[min(len(v) - 1, (9 * len(v)) // 10)]
 
     def med(i, j):
         return quant([events[k][i].elapsed_time(events[k][j]) * 1e-3 for k in range(K)])
@@ -313,6 +621,11 @@ def main():
     log("AB/BA interleaved kernels and flat copies")
     inter = interleaved()
 
+    # ---- the widened rows, each timed alone at its own workload (outside `value`) ---------
+    log("variants: state handoff, pool prefill, packed batch, epilogues, any D, decode variants")
+    variants, vsample = run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo, dwo, dbo, ws,
+                                     quant, copy1[0], copy2[0], HBM_PEAK_GBPS)
+
     # ---- CPU baseline: the oracle, timed on a bounded sample of the same workload ---------
     cpu = None
     gate = None
@@ -384,6 +697,14 @@ def main():
             "decode_state_bit_exact": state_exact,
             "metric": "max |gpu-oracle|/max(1,|oracle|); bounds 5e-3 (y), 8e-3 (dx, dw, dbias)",
         }
+        log("cpu baseline: the variants' samples")
+        vcpu, vgate = oracle_variants(oracle, np, torch, vsample, err)
+        cpu["variants"] = vcpu
+        gate["variants"] = vgate
+        for k, v in vgate.items():
+            variants[k]["parity"] = v["pass"]
+        passed = passed and all(v["pass"] for v in vgate.values())
+        gate["pass"] = passed
         if not passed:
             print(json.dumps({"parity_gate": gate}), file=sys.stderr)
             raise SystemExit("parity gate failed: no throughput is reported")
@@ -423,6 +744,7 @@ def main():
             "bytes_per_operand": nbytes,
         },
         "interleaved": inter,
+        "variants": variants,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),

@@ -216,9 +216,20 @@ __device__ __forceinline__ void bwd_run(const float (&tap)[W][VEC], const float 
             }
         }
     }
-    for (; t < e; ++t)
-        bwd_step<VEC, W, F, true>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)),
-                                    load_row<VEC, NTL>(at(dyb + t * dys, lo)), xr, gr, acc, db, k, t, true);
+    if (t < e) {
+        // the run's last rows, fewer than G (a run cut by a sequence start, or a segment that
+        // is not a whole number of groups): all loaded at once, with the row indices clamped
+        // into the run, instead of one dependent load per row
+        Row<VEC> rx[G], rdy[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NTL>(at(xb + min(t + g, e - 1) * xs, lo));
+#pragma unroll
+        for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC, NTL>(at(dyb + min(t + g, e - 1) * dys, lo));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            if (t + g < e) bwd_step<VEC, W, F, true>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, k, t + g, true);
+    }
 }
 
 // The halo after a run ending at row e: rows e .. e+W-2 finish dx of the run's last W-1 rows.
@@ -230,15 +241,24 @@ __device__ __forceinline__ void bwd_halo(const float (&tap)[W][VEC], const float
                                          float (&acc)[W][VEC], float (&db)[VEC], const uint16_t* __restrict__ xb,
                                          int64_t xs, const uint16_t* __restrict__ dyb, int64_t dys, const DxSink& k,
                                          int64_t e, int64_t end) {
+    if constexpr (W > 1) {
+        // all W-1 rows' loads first (indices clamped to the sequence's last row; rows at or
+        // past its end are then replaced by zeros), so the halo costs one memory latency
+        Row<VEC> hx[W - 1], hdy[W - 1];
 #pragma unroll
-    for (int h = 0; h < W - 1; ++h) {
-        const int64_t th = e + h;
-        Row<VEC> hx = zero_row<VEC>(), hdy = zero_row<VEC>();
-        if (th < end) {
-            hx = load_row<VEC>(at(xb + th * xs, k.lo));
-            hdy = load_row<VEC>(at(dyb + th * dys, k.lo));
+        for (int h = 0; h < W - 1; ++h) {
+            const int64_t th = min(e + h, end - 1);
+            hx[h] = load_row<VEC>(at(xb + th * xs, k.lo));
+            hdy[h] = load_row<VEC>(at(dyb + th * dys, k.lo));
         }
-        bwd_step<VEC, W, F, true>(tap, bs, hx, hdy, xr, gr, acc, db, k, th, false);
+#pragma unroll
+        for (int h = 0; h < W - 1; ++h) {
+            if (e + h >= end) {
+                hx[h] = zero_row<VEC>();
+                hdy[h] = zero_row<VEC>();
+            }
+            bwd_step<VEC, W, F, true>(tap, bs, hx[h], hdy[h], xr, gr, acc, db, k, e + h, false);
+        }
     }
 }
 

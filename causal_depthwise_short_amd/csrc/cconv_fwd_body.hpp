@@ -98,9 +98,19 @@ __device__ __forceinline__ void fwd_run(const float (&tap)[W][VEC], const float 
                 store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), fwd_row<VEC, W, LIN, RES>(tap, bs, raw[g], res[g], ring));
         }
     }
-    for (; t < e; ++t)
-        store_row<VEC, NTS>(at(yb + t * ys, lo),
-                            fwd_row<VEC, W, LIN, RES>(tap, bs, load_row<VEC, NTL>(at(xb + t * xs, lo)), ldr(t), ring));
+    if (t < e) {
+        // the run's last rows, fewer than G: all loaded at once (row indices clamped into the
+        // run) instead of one dependent load per row
+        Row<VEC> raw[G], res[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) raw[g] = load_row<VEC, NTL>(at(xb + min(t + g, e - 1) * xs, lo));
+#pragma unroll
+        for (int g = 0; g < G; ++g) res[g] = ldr(min(t + g, e - 1));
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            if (t + g < e)
+                store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), fwd_row<VEC, W, LIN, RES>(tap, bs, raw[g], res[g], ring));
+    }
 }
 
 // One wave: a strip of 64*VEC channels over the rows [t0, t1) of its segment. A batch row is

@@ -145,3 +145,19 @@ def train_inputs_device(
     b = torch.randn(D, generator=g, device=device, dtype=torch.float32) * math.sqrt(0.1) if bias else None
     dy = torch.randn(B, T, D, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
     return {"x": x, "w": w, "bias": b, "dy": dy}
+
+
+def packed_lengths(total: int, *, seed: int, max_len: int = 16384) -> list:
+    """Sequence lengths for a packed batch of ``total`` rows: log-uniform on [1, max_len]
+    (many short sequences, a few long ones), drawn until the rows are used up, the last one
+    cut to fit. The pages' packed batches give no length distribution; this mix covers
+    single-token sequences and ones longer than a wave's segment."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    lens, used = [], 0
+    while used < total:
+        u = float(torch.rand(1, generator=g))
+        n = max(1, min(max_len, int(round(math.exp(u * math.log(max_len))))))
+        n = min(n, total - used)
+        lens.append(n)
+        used += n
+    return lens
