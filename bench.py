@@ -212,27 +212,31 @@ def run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo
                  lambda: cc.cconv_bwd_ex(x, dy, w, b, activation=None, dx=dxo, dw=dwo, dbias=dbo, workspace=ws),
                  copy2, {}, cap_lin_b))
 
-    # any D: D = 4100 takes the element-granular path (one channel per lane)
-    Dn = 4100
-    nin = si.train_inputs_device(B, T, Dn, W, bias=True, seed=s.seed + 5, device=dev)
-    xn, wn, bn, dyn = nin["x"], nin["w"], nin["bias"], nin["dy"]
-    yn, dxn = torch.empty_like(xn), torch.empty_like(xn)
-    dwn, dbn = torch.empty_like(wn), torch.empty(Dn, dtype=torch.float32, device=dev)
-    wsn = torch.empty(cc.cconv_bwd_workspace_bytes(B, T, Dn, W) // 4 + 1, dtype=torch.float32, device=dev)
-    nn_ = B * T * Dn
-    wnb = wn.numel() * wn.element_size()
-    work = f"[{B},{T},{Dn}] W={W}"
+    # D other than the headline's: 4100 takes the element-granular path (one channel per lane),
+    # 4104 the vector path with 17 channel strips whose rows do not start on cache lines
+    big = []
+    for Dn, tag, what in ((4100, "any_d", "D not a multiple of 8 (one channel per lane)"),
+                          (4104, "d4104", "D = 4104 (vector path, rows not on 128-byte lines)")):
+        nin = si.train_inputs_device(B, T, Dn, W, bias=True, seed=s.seed + 5, device=dev)
+        xn, wn, bn, dyn = nin["x"], nin["w"], nin["bias"], nin["dy"]
+        yn, dxn = torch.empty_like(xn), torch.empty_like(xn)
+        dwn, dbn = torch.empty_like(wn), torch.empty(Dn, dtype=torch.float32, device=dev)
+        wsn = torch.empty(cc.cconv_bwd_workspace_bytes(B, T, Dn, W) // 4 + 1, dtype=torch.float32, device=dev)
+        big.append((nin, yn, dxn, wsn))
+        nn_ = B * T * Dn
+        wnb = wn.numel() * wn.element_size()
+        work = f"[{B},{T},{Dn}] W={W}"
 
-    def cap_any():
-        torch.cuda.synchronize()
-        S["any_d"] = {"x": xn[:1].cpu(), "dy": dyn[:1].cpu(), "w": wn.cpu(), "b": bn.cpu(), "y": yn[0].cpu(),
+        def cap(tag=tag, xn=xn, dyn=dyn, wn=wn, bn=bn, yn=yn, dxn=dxn):
+            torch.cuda.synchronize()
+            S[tag] = {"x": xn[:1].cpu(), "dy": dyn[:1].cpu(), "w": wn.cpu(), "b": bn.cpu(), "y": yn[0].cpu(),
                       "dx": dxn[0].cpu()}
 
-    todo.append(("fwd_any_d", "forward, D not a multiple of 8 (one channel per lane)", work, 4 * nn_ + wnb + Dn * 4,
-                 lambda: cc.cconv_fwd(xn, wn, bn, y=yn), copy1, {}, None))
-    todo.append(("bwd_any_d", "backward, D not a multiple of 8 (one channel per lane)", work,
-                 6 * nn_ + 2 * wnb + 2 * Dn * 4,
-                 lambda: cc.cconv_bwd(xn, dyn, wn, bn, dx=dxn, dw=dwn, dbias=dbn, workspace=wsn), copy2, {}, cap_any))
+        todo.append((f"fwd_{tag}", f"forward, {what}", work, 4 * nn_ + wnb + Dn * 4,
+                     lambda xn=xn, wn=wn, bn=bn, yn=yn: cc.cconv_fwd(xn, wn, bn, y=yn), copy1, {}, None))
+        todo.append((f"bwd_{tag}", f"backward, {what}", work, 6 * nn_ + 2 * wnb + 2 * Dn * 4,
+                     lambda xn=xn, dyn=dyn, wn=wn, bn=bn, dxn=dxn, dwn=dwn, dbn=dbn, wsn=wsn:
+                     cc.cconv_bwd(xn, dyn, wn, bn, dx=dxn, dw=dwn, dbias=dbn, workspace=wsn), copy2, {}, cap))
 
     # decode variants at the decode workload: a state of L = W entries, rewritten (shift) or
     # addressed as a circular buffer by cache_seqlens (one entry written per channel)
@@ -298,7 +302,7 @@ def run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo
         if item[7] is not None:
             item[4]()
             item[7]()
-    del nin, xn, dyn, yn, dxn, wsn
+    del big
     return V, S
 
 
@@ -364,16 +368,17 @@ def oracle_variants(oracle, np, torch, S, err):
     dxr = oracle.bwd_epi(x1, dy1, w, b, act=False, precision="f32")[0]
     t = _t.perf_counter() - t0
     put("bwd_linear", t, 6 * T * D, one, {"dx": (err(S["bwd_linear"]["dx"].float(), dxr[0]), 8e-3)})
-    v = S["any_d"]
-    Dn = v["x"].shape[2]
-    t0 = _t.perf_counter()
-    _, yr = oracle.fwd(v["x"], v["w"], v["b"], precision="f32")
-    t1 = _t.perf_counter()
-    dxr, _, _ = oracle.bwd(v["x"], v["dy"], v["w"], v["b"], precision="f32")
-    t2 = _t.perf_counter()
-    oned = f"batch row 0 ({T} x {Dn})"
-    put("fwd_any_d", t1 - t0, 4 * T * Dn, oned, {"y": (err(v["y"].float(), yr[0]), 5e-3)})
-    put("bwd_any_d", t2 - t1, 6 * T * Dn, oned, {"dx": (err(v["dx"].float(), dxr[0]), 8e-3)})
+    for tag in ("any_d", "d4104"):
+        v = S[tag]
+        Dn = v["x"].shape[2]
+        t0 = _t.perf_counter()
+        _, yr = oracle.fwd(v["x"], v["w"], v["b"], precision="f32")
+        t1 = _t.perf_counter()
+        dxr, _, _ = oracle.bwd(v["x"], v["dy"], v["w"], v["b"], precision="f32")
+        t2 = _t.perf_counter()
+        oned = f"batch row 0 ({T} x {Dn})"
+        put(f"fwd_{tag}", t1 - t0, 4 * T * Dn, oned, {"y": (err(v["y"].float(), yr[0]), 5e-3)})
+        put(f"bwd_{tag}", t2 - t1, 6 * T * Dn, oned, {"dx": (err(v["dx"].float(), dxr[0]), 8e-3)})
     for name in ("update_shift_l4", "update_circular_l4"):
         v = S[name]
         N, Dd = v["y"].shape

@@ -20,8 +20,8 @@ constexpr int64_t kMaxDecodeRows = int64_t(1) << 24;  // N
 constexpr int64_t kMaxChannels = int64_t(1) << 30;    // D: lane channel offsets are 32-bit
 constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices (LDS bit set)
 constexpr int64_t kMaxSequences = int64_t(1) << 24;     // packed sequences per call
-constexpr int64_t kTargetWaves = 1024;  // one wave per SIMD (256 CUs x 4 SIMDs)
-constexpr int64_t kNarrowTargetWaves = 8192;  // the narrow path: several waves per SIMD
+constexpr int64_t kTargetWaves = 1024;  // wave slots of the solo kernels: one per SIMD (256 CUs x 4 SIMDs)
+constexpr int64_t kNarrowTargetWaves = 4096;  // wave slots of the narrow path: four waves per SIMD
 // forward and backward: non-temporal loads and stores, solo kernel (no software prefetch)
 constexpr int kFwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
 constexpr int kBwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
@@ -65,38 +65,51 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
     return true;
 }
 
-// The static launch table (from sweeps on MI355X at 8x8192x4096, W=4). Each wave owns one
-// (channel strip, time segment, batch row) and streams its rows; segments are sized so the
-// grid holds about kTargetWaves waves, one per SIMD of the 256 CUs: fewer, longer-running
-// waves beat more, shorter ones for both kernels, and a wave alone on its SIMD may use the
+// The static launch table (from sweeps on MI355X at 8x8192x4096, W=4, and at D = 4100, 4104
+// and 4160). Each wave owns one (channel strip, time segment, batch row) and streams its rows:
+// fewer, longer-running waves beat more, shorter ones, and a wave alone on its SIMD may use the
 // whole register file (the "solo" kernels), which is what lets deep row groups stay in flight
-// without scratch spills. Segments never drop below kMinSeg rows (the W-1 rows each segment
-// re-reads stay a small share). Forward and backward: 4 channels per lane, 16-row groups (the
-// backward loads 16 rows of x and 16 of dy per group: 16 KiB in flight per wave). D not a
-// multiple of 8: one channel per lane, 16-row groups, 4-wave blocks and about
-// kNarrowTargetWaves waves.
-cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W) {
+// without scratch spills.
+//   * Shape: 4 channels per lane and 16-row groups (the backward loads 16 rows of x and 16 of
+//     dy per group: 16 KiB in flight per wave). D not a multiple of 8: one channel per lane,
+//     16-row groups, the general kernel.
+//   * Segments: each batch row is cut into as many segments as the wave slots allow (1024
+//     solo waves, one per SIMD; kNarrowTargetWaves for the narrow path) and no more. A grid
+//     slightly larger than the slots (17 strips x 8 segments x 8 rows = 1088 waves at D = 4160)
+//     leaves the extra waves sharing a SIMD with another, and the kernel waits for them: about
+//     twice the time. Segments never drop below kMinSeg rows (the W-1 rows each segment
+//     re-reads stay a small share).
+//   * Cache hints: non-temporal loads and stores when the output rows start on 128-byte cache
+//     lines (2D a multiple of 128); otherwise plain ones, so that the L2 merges the lines two
+//     neighbouring strips share (at D = 4104: 241 vs 264 us forward, 325 vs 389 us backward).
+//     The narrow path's rows never start on a line. Packed batches and the epilogue variants
+//     keep the streaming hints (their kernels are compiled for those only).
+cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, bool streaming_only = false) {
     (void)W;
     cconv_config_t c;
     const bool narrow = (D % 8 != 0);
     c.vec = narrow ? 1 : 4;
     c.rows_per_group = 16;
-    c.waves_per_block = narrow ? 4 : 1;
+    c.waves_per_block = 1;
     c.strips_per_block = 1;
-    // the narrow path: one channel per lane moves 8x fewer bytes per wave, so it runs several
-    // waves per SIMD (the general kernel) instead of one solo wave
+    const bool line_rows = (2 * D) % 128 == 0;
     if (narrow)
-        c.options = bwd ? cconv::kVarlenBwdOptions : cconv::kVarlenFwdOptions;
-    else
+        c.options = cconv::kNarrowOptions;
+    else if (line_rows || streaming_only)
         c.options = bwd ? kBwdOptions : kFwdOptions;
+    else
+        c.options = cconv::kSolo;
     // segment length: a multiple of the row group (and of 8), at least kMinSeg rows, at most
     // T rounded up
     const int64_t align = std::max<int64_t>(8, c.rows_per_group);
     const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
-    const int64_t target = narrow ? kNarrowTargetWaves : kTargetWaves;
-    int64_t ts = (std::max<int64_t>(B, 1) * std::max<int64_t>(T, 1) * strips) / target;
-    ts = std::max(kMinSeg, ts - ts % align);
-    const int64_t tcap = ((std::max<int64_t>(T, 1) + align - 1) / align) * align;
+    const int64_t slots = narrow ? kNarrowTargetWaves : kTargetWaves;
+    const int64_t units = std::max<int64_t>(B, 1) * strips;  // (batch row, strip) pairs
+    const int64_t per_row = std::max<int64_t>(1, slots / units);
+    const int64_t t = std::max<int64_t>(T, 1);
+    int64_t ts = (t + per_row - 1) / per_row;
+    ts = std::max(kMinSeg, ((ts + align - 1) / align) * align);
+    const int64_t tcap = ((t + align - 1) / align) * align;
     c.seg_rows = std::min(ts, tcap);
     return c;
 }
@@ -236,14 +249,15 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     if ((!x && !act_empty) || (!w && D > 0) || (!y && !act_empty)) return CCONV_ERR_NULL_POINTER;
     cconv_status_t st = check_train_common(w_dtype, B, T, D, W);
     if (st != CCONV_OK) return st;
-    const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W);
+    const int epi = (ex.linear ? cconv::kLinear : 0) | (ex.r ? cconv::kResidual : 0);
+    // packed batches and the epilogue variants are compiled for the streaming hints only
+    const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W, ex.mode == kPacked || epi != 0);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
     const bool narrow = (c.vec == 1);
     if (!narrow && D % 8 != 0) return CCONV_ERR_BAD_CONFIG;  // a vector plan needs whole 8-channel groups
     if ((st = check_params(w, w_dtype, bias, narrow)) != CCONV_OK) return st;
     if ((st = check_act(x, x_sb, x_st, D, narrow)) != CCONV_OK) return st;
     if (!aligned(y, narrow ? 2 : 16)) return CCONV_ERR_MISALIGNED;
-    const int epi = (ex.linear ? cconv::kLinear : 0) | (ex.r ? cconv::kResidual : 0);
     if (!cconv::fwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
         return CCONV_ERR_BAD_CONFIG;
     if (ex.r && (st = check_act(ex.r, ex.r_sb, ex.r_st, D, narrow)) != CCONV_OK) return st;
@@ -323,7 +337,10 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     cconv_status_t st = check_train_common(w_dtype, B, T, D, W);
     if (st != CCONV_OK) return st;
     if (!dtype_ok(dw_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
-    const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W);
+    const int epi = ex.linear ? cconv::kLinear : 0;
+    // packed batches and the variant without an activation are compiled for the streaming
+    // hints only
+    const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0);
     if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
     const bool narrow = (c.vec == 1);
     if (!narrow && D % 8 != 0) return CCONV_ERR_BAD_CONFIG;  // a vector plan needs whole 8-channel groups
@@ -333,7 +350,6 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     if (!aligned(dx, narrow ? 2 : 16) || !aligned(dw, narrow ? static_cast<uintptr_t>(esize(dw_dtype)) : 16) ||
         (dbias && !aligned(dbias, narrow ? 4 : 16)))
         return CCONV_ERR_MISALIGNED;
-    const int epi = ex.linear ? cconv::kLinear : 0;
     if (!cconv::bwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
         return CCONV_ERR_BAD_CONFIG;
     Plan p;

@@ -48,10 +48,11 @@ hipError_t launch_lin(int W, dim3 grid, dim3 block, size_t lds, const BwdArgs& a
     }
 }
 
-// element-granular D: one channel per lane, 16-row groups, the general kernel
+// element-granular D: one channel per lane, 16-row groups, the general kernel, plain loads and
+// stores
 template <bool VL>
 hipError_t launch_narrow(int W, bool lin, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
-    constexpr int F = kVarlenBwdOptions;
+    constexpr int F = kNarrowOptions;
     switch (W) {
 #define CCONV_NARROW(w)                                                                            \
     case w:                                                                                        \
@@ -72,7 +73,7 @@ bool bwd_launch_exists(int vec, int group, int options, bool packed) {
     if (!bwd_variant_exists(vec, group) || options < 0) return false;
     if (options & ~(kSolo | kLinear | kNtLoad | kNtStore | kPrefetch)) return false;
     const int base = options & ~(kSolo | kLinear);
-    if (vec == 1) return !(options & kSolo) && base == kVarlenBwdOptions;
+    if (vec == 1) return !(options & kSolo) && base == kNarrowOptions;
     if (!(options & kLinear)) return packed ? base == kVarlenBwdOptions : true;
     return vec == 4 && group == 16 && (options & kSolo) && base == kVarlenBwdOptions;
 }

@@ -110,6 +110,10 @@ constexpr int kSolo = 8;      // one-wave blocks, one wave per SIMD, whole regis
 // register moves than the latency they hide).
 constexpr int kVarlenFwdOptions = kNtLoad | kNtStore;
 constexpr int kVarlenBwdOptions = kNtLoad | kNtStore;
+// The element-granular path (D not a multiple of 8) is compiled with plain loads and stores:
+// its rows never start on a 128-byte cache line, and non-temporal hints then keep the L2 from
+// merging the lines two neighbouring strips share.
+constexpr int kNarrowOptions = 0;
 // Epilogue variants (compile-time, default launch only): no activation (y = z, g = dy), and a
 // residual added to the forward's output after the activation.
 constexpr int kLinear = 16;

@@ -58,11 +58,11 @@ hipError_t launch_epi(int W, int epi, dim3 grid, dim3 block, const FwdArgs& a, h
     }
 }
 
-// element-granular D: one channel per lane, 16-row groups, the general kernel, streaming
-// options, every epilogue, fixed-length or packed
+// element-granular D: one channel per lane, 16-row groups, the general kernel, plain loads and
+// stores, every epilogue, fixed-length or packed
 template <int W, bool VL>
 hipError_t launch_narrow_w(int epi, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
-    constexpr int B0 = kVarlenFwdOptions;
+    constexpr int B0 = kNarrowOptions;
     switch (epi) {
         case 0: return launch_k<1, 16, W, B0, VL, false>(grid, block, a, s);
         case kLinear: return launch_k<1, 16, W, B0 | kLinear, VL, false>(grid, block, a, s);
@@ -90,7 +90,7 @@ bool fwd_launch_exists(int vec, int group, int options, bool packed) {
     const int epi = options & (kLinear | kResidual);
     const int base = options & ~(kSolo | kLinear | kResidual);
     if (options & ~(kSolo | kLinear | kResidual | kNtLoad | kNtStore | kPrefetch)) return false;
-    if (vec == 1) return !(options & kSolo) && base == kVarlenFwdOptions;
+    if (vec == 1) return !(options & kSolo) && base == kNarrowOptions;
     if (epi == 0) return packed ? base == kVarlenFwdOptions : true;
     return vec == 4 && group == 16 && (options & kSolo) && base == kVarlenFwdOptions;
 }

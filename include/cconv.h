@@ -34,10 +34,10 @@
  *    D (the element-granular path [strip.py's masked loads handle any D]: one channel per
  *    lane) needs only element alignment (2 bytes for bf16, 4 for fp32) and strides >= D; the
  *    decode update then takes compact rows (x_ld == D) or a row stride that is a multiple of
- *    8 [the decode PR's row-stride contract]. The element-granular path runs the streaming
- *    launch only (its own default configuration: 1 channel per lane, 16-row groups, 4-wave
- *    blocks); with D % 8 != 0 a configuration with vec != 1 is CCONV_ERR_BAD_CONFIG. The
- *    alignments stated below are those of the vector path.
+ *    8 [the decode PR's row-stride contract]. The element-granular path runs with plain
+ *    loads and stores only (options 0; its default configuration: 1 channel per lane, 16-row
+ *    groups, one-wave blocks); with D % 8 != 0 a configuration with vec != 1 is
+ *    CCONV_ERR_BAD_CONFIG. The alignments stated below are those of the vector path.
  *  - Errors fail closed. A problem visible on the host returns its code before anything is
  *    enqueued, leaving every output untouched: NULL required pointer, negative size, W
  *    outside [1, 4] (the pages' kernels are written for at most 4 taps, strip.py module
@@ -320,7 +320,8 @@ const char* cconv_version(void);
  * entry points above pick one from a static table; these take it explicitly. y and dx do
  * not depend on the configuration (bitwise); dw and dbias depend on it only through the
  * order of their fixed-order sum.
- *   vec              channels per lane: 4 or 8 (8 or 16 bytes per row per lane)
+ *   vec              channels per lane: 4 or 8 (8 or 16 bytes per row per lane); 1 (2 bytes)
+ *                    on the element-granular path, where it is the only choice
  *   rows_per_group   rows whose loads are issued together: 4 or 8 (and 16 with vec 4)
  *   waves_per_block  1, 2, 4 or 8 waves per block
  *   strips_per_block a divisor of waves_per_block: the block's waves cover this many
@@ -343,7 +344,14 @@ typedef struct {
     int64_t seg_rows;
 } cconv_config_t;
 
-/* The configuration cconv_fwd (which = 0) or cconv_bwd (which = 1) uses for this shape. */
+/*
+ * The configuration cconv_fwd (which = 0) or cconv_bwd (which = 1) uses for this shape: 4
+ * channels per lane (1 when D % 8 != 0), 16-row groups, one-wave blocks, each batch row cut
+ * into as many segments as the wave slots hold (1024 waves, one per SIMD; 4096 on the
+ * element-granular path); non-temporal hints (options 11) when 2D is a multiple of 128, plain
+ * loads and stores (options 8; 0 on the element-granular path) otherwise. Packed batches and
+ * the epilogue variants use the same plan with the streaming hints.
+ */
 cconv_status_t cconv_default_config(int which, int64_t B, int64_t T, int64_t D, int W,
                                     cconv_config_t* out);
 

@@ -208,6 +208,30 @@ def test_bwd_stages_host_errors():
 
 
 @pytest.mark.parametrize("which", ["fwd", "bwd"])
+def test_default_plan_fits_the_wave_slots(which):
+    """Default plans cut each batch row into as many segments as the wave slots allow (1024
+    one-wave-per-SIMD waves; 4096 on the one-channel-per-lane path) and no more, and take
+    streaming cache hints only when output rows start on 128-byte lines."""
+    for B, T, D in [(8, 8192, 4096), (8, 8192, 4160), (8, 8192, 4104), (16, 8192, 2048), (3, 1000, 2000),
+                    (8, 8192, 4100), (1, 65536, 4096), (2, 100003, 520), (64, 4096, 4096)]:
+        c = cc.cconv_default_config(which, B, T, D, 4)
+        narrow = D % 8 != 0
+        slots = 4096 if narrow else 1024
+        strips = -(-D // (64 * c.vec))
+        waves = B * strips * -(-T // c.seg_rows)
+        if B * strips <= slots:
+            assert waves <= slots, (B, T, D, c, waves)
+        if c.seg_rows > 64:  # not held up by the minimum segment: one more segment would not fit
+            assert B * strips * (-(-T // c.seg_rows) + 1) > slots or -(-T // c.seg_rows) * c.seg_rows - T < c.seg_rows
+        if narrow:
+            assert c.vec == 1 and c.options == 0
+        else:
+            assert c.vec == 4 and c.options == (11 if (2 * D) % 128 == 0 else 8), (D, c.options)
+    assert cc.cconv_default_config(which, 8, 8192, 4096, 4).seg_rows == 1024
+    assert cc.cconv_default_config(which, 8, 8192, 4160, 4).seg_rows == 1184
+
+
+@pytest.mark.parametrize("which", ["fwd", "bwd"])
 def test_default_configs_are_valid(which):
     """Every default plan over a grid of shapes is one the library accepts."""
     for B in (1, 3, 8):
@@ -527,10 +551,10 @@ def test_odd_channel_counts_need_the_narrow_launch():
     vec4 = cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
     assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, Y, 2, T, D, 4, ctypes.byref(vec4), None) == CONFIG
     narrow = cc.cconv_default_config("fwd", 2, T, D, 4)
-    assert narrow.vec == 1 and narrow.rows_per_group == 16 and narrow.options == 3
+    assert narrow.vec == 1 and narrow.rows_per_group == 16 and narrow.options == 0
     # accepted: with y aliasing x it gets as far as the aliasing check
     assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(narrow), None) == ALIAS
     solo = cc.Config(vec=1, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
     assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(solo), None) == CONFIG
     nb = cc.cconv_default_config("bwd", 2, T, D, 4)
-    assert nb.vec == 1 and nb.options == 3 and nb.waves_per_block == 4
+    assert nb.vec == 1 and nb.options == 0 and nb.waves_per_block == 1

@@ -90,17 +90,17 @@ def test_narrow_unaligned_strides_and_guards():
 @pytest.mark.parametrize("i", range(4))
 def test_narrow_launch_invariance(i):
     cfgs = [
-        dict(vec=1, rows_per_group=16, waves_per_block=1, options=3, seg_rows=16),
-        dict(vec=1, rows_per_group=16, waves_per_block=8, options=3, seg_rows=32),
-        dict(vec=1, rows_per_group=16, waves_per_block=2, strips_per_block=2, options=3, seg_rows=48),
-        dict(vec=1, rows_per_group=16, waves_per_block=4, options=3, seg_rows=4096),
+        dict(vec=1, rows_per_group=16, waves_per_block=1, options=0, seg_rows=16),
+        dict(vec=1, rows_per_group=16, waves_per_block=8, options=0, seg_rows=32),
+        dict(vec=1, rows_per_group=16, waves_per_block=2, strips_per_block=2, options=0, seg_rows=48),
+        dict(vec=1, rows_per_group=16, waves_per_block=4, options=0, seg_rows=4096),
     ]
     inp = si.train_inputs(2, 700, 199, 4, bias=True, seed=840)
     x, w, b, dy = (_g(inp[k]) for k in ("x", "w", "bias", "dy"))
     ref_y = cc.cconv_fwd(x, w, b)
     ref_dx, ref_dw, _ = cc.cconv_bwd(x, dy, w, b, dw_dtype=torch.float32)
     cf = cc.Config(**cfgs[i])
-    cb = cc.Config(**dict(cfgs[i], options=3))
+    cb = cc.Config(**dict(cfgs[i], options=0))
     y = cc.cconv_fwd(x, w, b, config=cf)
     dx, dw, _ = cc.cconv_bwd(x, dy, w, b, config=cb, dw_dtype=torch.float32)
     torch.cuda.synchronize()
