@@ -251,16 +251,24 @@ __device__ __forceinline__ void ring_at(float (&ring)[W > 1 ? W - 1 : 1][VEC], i
 }
 
 // The sequence of a packed batch that holds row t: the largest s < n with cu[s] <= t, so empty
-// sequences are passed over (the offsets were checked first: cu[0] = 0 <= t < cu[n]).
-// Wave-uniform: a binary search on scalar loads.
+// sequences are passed over (the offsets were checked first: cu[0] = 0 <= t < cu[n]). Called
+// by the active lanes of a wave, all with the same t. They probe P = (active lanes) positions
+// at once, strictly inside the range [lo, hi) so that it splits into P + 1 parts; a ballot
+// counts the probes at or before t (a prefix of them, cu being nondecreasing), and the range
+// shrinks to one part. One round of loads for up to 64 sequences, 4 for 2^24; every round
+// shrinks the range, even with a single active lane.
 __device__ __forceinline__ int64_t seq_of(const int32_t* cu, int64_t n, int64_t t) {
-    int64_t lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (cu[mid] <= t)
-            lo = mid;
-        else
-            hi = mid - 1;
+    const uint64_t act = __ballot(1);
+    const int64_t P = __popcll(act);
+    const int64_t rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(act >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(act), 0u));
+    int64_t lo = 0, hi = n;
+    while (hi - lo > 1) {
+        const int64_t step = (hi - lo + P) / (P + 1);
+        const int64_t p = lo + (rank + 1) * step;
+        const int64_t k = __popcll(__ballot(p < hi && cu[p] <= t));
+        hi = min(hi, lo + (k + 1) * step);
+        lo += k * step;
     }
     return lo;
 }

@@ -160,6 +160,17 @@ def test_varlen_many_tiny_sequences():
     _check(x, dy, w, b, h0, cu, _run(x, dy, w, b, h0, cu), "tiny sequences")
 
 
+@pytest.mark.parametrize("D", [65, 264], ids=["narrow_1_lane", "vector_2_lanes"])
+def test_varlen_sequence_search_with_few_active_lanes(D):
+    """The last channel strip has one active lane (D = 65, one channel per lane) or two (D = 264,
+    four channels per lane): the waves of that strip find their first sequence with one or two
+    probes per round, over many rounds (300 sequences, empty ones among them)."""
+    rng = np.random.default_rng(260 + D)
+    lens = rng.integers(0, 40, 300).tolist()
+    x, dy, w, b, h0, cu = _case(lens, D, 4, seed=261 + D)
+    _check(x, dy, w, b, h0, cu, _run(x, dy, w, b, h0, cu), f"D{D} few active lanes")
+
+
 def test_varlen_empty_batches():
     D, W = 512, 4
     w = torch.randn(D, W).to(torch.bfloat16).to(DEV)
