@@ -32,6 +32,29 @@ __device__ __forceinline__ void ring_from_state(const uint16_t (&h)[VEC * (L > 0
     }
 }
 
+// Circular mode, VEC = 8: the thread's whole state run (8 channels x L entries, 16*L bytes)
+// stored as L 16-byte vectors, entry ROT of each channel replaced by the token and the other
+// entries rewritten with the values just read (the memory changes only at entry ROT).
+template <int L, int ROT>
+__device__ __forceinline__ void store_run_circ(uint16_t* __restrict__ sp, const uint16_t (&h)[8 * L], const Row<8>& rx) {
+    uint16_t nh[8 * L];
+#pragma unroll
+    for (int i = 0; i < 8 * L; ++i) nh[i] = h[i];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const uint32_t xw = rx.u[v / 2];
+        nh[v * L + ROT] = static_cast<uint16_t>((v & 1) ? (xw >> 16) : (xw & 0xffffu));
+    }
+#pragma unroll
+    for (int q = 0; q < L; ++q) {
+        uint32_t u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = static_cast<uint32_t>(nh[q * 8 + 2 * i]) | (static_cast<uint32_t>(nh[q * 8 + 2 * i + 1]) << 16);
+        reinterpret_cast<uint4*>(sp)[q] = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+}
+
 // VEC = 8: a thread owns 8 channels (16-byte x rows, 16*L-byte state runs); VEC = 1: one channel
 // (any D, any row stride).
 // The thread's channels of one row: x (VEC values) and the state entries of slot s (VEC x L
@@ -74,15 +97,22 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
     Row<VEC> rx0 = zero_row<VEC>();
     uint16_t h0[VEC * (L > 0 ? L : 1)];
     int64_t s0 = -1;
+    int64_t cs0 = 0;  // circular: the first row's cache_seqlens entry, loaded with its slot
     if (lane && n0 < n1) {
         s0 = a.idx ? static_cast<int64_t>(a.idx[n0]) : n0;
+        if constexpr (CIRC) cs0 = a.cs[n0];
         if (s0 >= 0 && s0 < a.S) gather_row<L, VEC>(a, n0, s0, d, rx0, h0);
     }
 
+    // circular: every cache_seqlens entry must be >= 0. The thread's first entry is loaded
+    // before the slot check and compared after it, so that its load overlaps the check; the
+    // two verdicts meet in one block-wide OR.
+    int32_t c0 = 0;
+    if (CIRC && static_cast<int64_t>(threadIdx.x) < a.N) c0 = a.cs[threadIdx.x];
     bool bad = a.idx ? block_slots_bad(a.idx, a.N, a.S, seen) : false;
-    if (CIRC) {  // every cache_seqlens entry must be >= 0
-        bool neg = false;
-        for (int64_t i = threadIdx.x; i < a.N; i += blockDim.x)
+    if (CIRC) {
+        bool neg = c0 < 0;
+        for (int64_t i = static_cast<int64_t>(threadIdx.x) + blockDim.x; i < a.N; i += blockDim.x)
             if (a.cs[i] < 0) neg = true;
         bad = __syncthreads_or(neg || bad);
     }
@@ -98,6 +128,7 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
     for (int64_t n = n0; n < n1; ++n) {
         const bool first = (n == n0);
         const int64_t s = first ? s0 : (a.idx ? static_cast<int64_t>(a.idx[n]) : n);
+        const int64_t cn = CIRC ? (first ? cs0 : static_cast<int64_t>(a.cs[n])) : 0;  // before the gather
         uint16_t* __restrict__ yp = a.y + n * a.D + d;
         if (s < 0) {  // padding row: no state access, output 0
             store_row<VEC>(yp, zero_row<VEC>());
@@ -120,14 +151,14 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
             if constexpr (!CIRC) {
                 ring_from_state<VEC, W, L, -1>(h, ring);
             } else {
-                rot = static_cast<int>(static_cast<int64_t>(a.cs[n]) % L);
+                rot = static_cast<int>(cn % L);
                 if (rot == 0) ring_from_state<VEC, W, L, 0>(h, ring);
                 if constexpr (L > 1) if (rot == 1) ring_from_state<VEC, W, L, (L > 1 ? 1 : 0)>(h, ring);
                 if constexpr (L > 2) if (rot == 2) ring_from_state<VEC, W, L, (L > 2 ? 2 : 0)>(h, ring);
                 if constexpr (L > 3) if (rot == 3) ring_from_state<VEC, W, L, (L > 3 ? 3 : 0)>(h, ring);
             }
         } else if constexpr (CIRC) {
-            rot = static_cast<int>(static_cast<int64_t>(a.cs[n]) % L);
+            rot = static_cast<int>(cn % L);
         }
         float y[VEC];
 #pragma unroll
@@ -137,12 +168,13 @@ __global__ __launch_bounds__(256) void cconv_update_kernel(const UpdateArgs a) {
         }
         store_row<VEC>(yp, narrow<VEC>(y));
         if constexpr (L > 0) {
-            if constexpr (CIRC) {  // write only the token's entry (bit copies of x)
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    const uint32_t xw = rx.u[v / 2];
-                    sp[v * L + rot] = static_cast<uint16_t>((v & 1) ? (xw >> 16) : (xw & 0xffffu));
-                }
+            if constexpr (CIRC && VEC == 8) {  // the token's entry changes; whole runs are stored
+                if (rot == 0) store_run_circ<L, 0>(sp, h, rx);
+                if constexpr (L > 1) if (rot == 1) store_run_circ<L, (L > 1 ? 1 : 0)>(sp, h, rx);
+                if constexpr (L > 2) if (rot == 2) store_run_circ<L, (L > 2 ? 2 : 0)>(sp, h, rx);
+                if constexpr (L > 3) if (rot == 3) store_run_circ<L, (L > 3 ? 3 : 0)>(sp, h, rx);
+            } else if constexpr (CIRC) {  // one channel: write only the token's entry
+                sp[rot] = static_cast<uint16_t>(rx.u[0] & 0xffffu);
             } else if constexpr (VEC == 1) {  // shift, one channel
                 for (int j = 0; j + 1 < L; ++j) sp[j] = h[j + 1];
                 sp[L - 1] = static_cast<uint16_t>(rx.u[0] & 0xffffu);

@@ -298,9 +298,12 @@ cconv_status_t cconv_update(const void* x, int64_t x_ld, void* state, int64_t S,
  *   cache_seqlens  int32 [N] on the device, or NULL. NULL: shift mode (drop the oldest entry,
  *                  append the token: L entries rewritten). Given: circular mode, nothing
  *                  moves: for row n with c = cache_seqlens[n] >= 0 the token k steps back is
- *                  entry (c - k) mod L and the new token is written to entry c mod L only (2
- *                  bytes per channel). The caller advances cache_seqlens. A state written by a
- *                  prefill (oldest first) is a circular state with c = 0 (mod L). Needs L >= 1.
+ *                  entry (c - k) mod L and the new token goes to entry c mod L; no other
+ *                  entry changes value (on the vector path the kernel stores each slot's whole
+ *                  16*L-byte run, the other entries with the values it just read: 16-byte
+ *                  stores beat 2-byte ones at decode sizes). The caller advances
+ *                  cache_seqlens. A state written by a prefill (oldest first) is a circular
+ *                  state with c = 0 (mod L). Needs L >= 1.
  * Everything else as cconv_update; a negative cache_seqlens entry fails the call like an
  * invalid index (CCONV_ERR_INDEX in *status, nothing written).
  */
