@@ -231,11 +231,10 @@ cconv_status_t launch_checks(const Extra& ex, int64_t B, int64_t T, int64_t D, i
     if (ex.mode == kPool && cconv::launch_slots(ex.sidx, B, ex.rows, ex.status, s) != hipSuccess)
         return CCONV_ERR_LAUNCH;
     if (ex.mode == kPacked) {
-        if (cconv::launch_offsets(ex.cu, ex.rows, T, ex.status, s) != hipSuccess) return CCONV_ERR_LAUNCH;
         const uint16_t* h0 = static_cast<const uint16_t*>(ex.h0);
         uint16_t* o = static_cast<uint16_t*>(ex.out);
-        if (cconv::launch_empty_seqs(ex.cu, ex.rows, h0, fwd ? o : nullptr, fwd ? nullptr : o, D, W - 1, ex.status,
-                                     s) != hipSuccess)
+        if (cconv::launch_offsets(ex.cu, ex.rows, T, ex.status, h0, fwd ? o : nullptr, fwd ? nullptr : o, D, W - 1,
+                                  s) != hipSuccess)
             return CCONV_ERR_LAUNCH;
     }
     return CCONV_OK;

@@ -121,11 +121,11 @@ hipError_t launch_update(int W, int L, bool narrow, const UpdateArgs& a, int blo
                          int64_t grid_y, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_status(int32_t* status, int32_t value, hipStream_t stream);
 hipError_t launch_slots(const int32_t* idx, int64_t N, int64_t S, int32_t* status, hipStream_t stream);
-// Packed batches: the offset check (one block writes *status), and the states of empty
-// sequences (final state = history or zeros, history gradient = 0), which no wave holds.
-hipError_t launch_offsets(const int32_t* cu, int64_t nseq, int64_t total, int32_t* status, hipStream_t stream);
-hipError_t launch_empty_seqs(const int32_t* cu, int64_t nseq, const uint16_t* h0, uint16_t* hT, uint16_t* dh0,
-                             int64_t D, int L, const int32_t* status, hipStream_t stream);
+// Packed batches: the offset check (one block writes *status), then, when it passes, the
+// states of empty sequences (final state hT = history or zeros, history gradient dh0 = 0;
+// either may be null), which no streaming wave holds.
+hipError_t launch_offsets(const int32_t* cu, int64_t nseq, int64_t total, int32_t* status, const uint16_t* h0,
+                          uint16_t* hT, uint16_t* dh0, int64_t D, int L, hipStream_t stream);
 
 // Which (vec, group) pairs are compiled.
 bool fwd_variant_exists(int vec, int group);
