@@ -104,8 +104,10 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
     const int64_t align = std::max<int64_t>(8, c.rows_per_group);
     const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
     const int64_t slots = narrow ? kNarrowTargetWaves : kTargetWaves;
-    const int64_t units = std::max<int64_t>(B, 1) * strips;  // (batch row, strip) pairs
-    const int64_t per_row = std::max<int64_t>(1, slots / units);
+    // (batch row, strip) pairs; the product is formed only when both factors are within the
+    // slot count (no overflow at the largest sizes the API accepts)
+    const int64_t b1 = std::max<int64_t>(B, 1);
+    const int64_t per_row = (b1 > slots || strips > slots) ? 1 : std::max<int64_t>(1, slots / (b1 * strips));
     const int64_t t = std::max<int64_t>(T, 1);
     int64_t ts = (t + per_row - 1) / per_row;
     ts = std::max(kMinSeg, ((ts + align - 1) / align) * align);
