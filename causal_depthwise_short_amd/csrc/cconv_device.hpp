@@ -228,24 +228,60 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t pid, int64_t n) {
 // The W-1 inputs before row t of a sequence whose first row is `start`, newest first:
 // ring[k] = X[t-1-k] for VEC consecutive channels d... Rows at or after `start` are read from
 // x; earlier ones come from the sequence's history, state row `hrow` of h0 ([rows, D, W-1],
-// slot row - start + W - 1, oldest first), or are zero without a history or before it.
+// slot row - start + W - 1, oldest first), or are zero without a history (h0 null).
+//
+// Every load is issued first (the x rows with their indices clamped into the sequence, and the
+// lane's whole history run when the sequence started fewer than W-1 rows back), and only then
+// are the entries picked: one memory round trip. How many of the W-1 rows lie inside the
+// sequence (m = t - start, capped at W-1) is wave-uniform, so a uniform switch picks a
+// compile-time entry map (no dynamic register indexing).
+template <int VEC, int R, int M>
+__device__ __forceinline__ void ring_pick(float (&ring)[R][VEC], const Row<VEC> (&rx)[R],
+                                          const uint16_t (&hv)[VEC * R]) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        if (k < M) {
+            widen(rx[k], ring[k]);
+        } else {
+            const int slot = R - 1 - (k - M);  // row t-1-k = start - (k - M) - 1
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) ring[k][v] = __uint_as_float(static_cast<uint32_t>(hv[v * R + slot]) << 16);
+        }
+    }
+}
+
 template <int VEC, int W>
 __device__ __forceinline__ void ring_at(float (&ring)[W > 1 ? W - 1 : 1][VEC], int64_t t, int64_t start,
                                         const uint16_t* __restrict__ xb, int64_t xs, uint32_t lo,
                                         const uint16_t* h0, int64_t hrow, int64_t D, int64_t d) {
-    constexpr int R = W > 1 ? W - 1 : 1;
+    if constexpr (W == 1) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const int64_t row = t - 1 - k;
-        if (W > 1 && row >= start) {
-            widen(load_row<VEC>(at(xb + row * xs, lo)), ring[k]);
+        for (int v = 0; v < VEC; ++v) ring[0][v] = 0.0f;
+    } else {
+        constexpr int R = W - 1;
+        Row<VEC> rx[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) rx[k] = load_row<VEC>(at(xb + max(t - 1 - k, start) * xs, lo));
+        const int64_t m = t - start;
+        uint16_t hv[VEC * R];
+        if (h0 && m < R) {
+            const uint16_t* __restrict__ hp = h0 + (hrow * D + d) * R;
+#pragma unroll
+            for (int i = 0; i < VEC * R; ++i) hv[i] = hp[i];
         } else {
-            const int64_t slot = row - start + R;
 #pragma unroll
-            for (int v = 0; v < VEC; ++v)
-                ring[k][v] = (W > 1 && h0 && slot >= 0)
-                                 ? __uint_as_float(static_cast<uint32_t>(h0[(hrow * D + d + v) * R + slot]) << 16)
-                                 : 0.0f;
+            for (int i = 0; i < VEC * R; ++i) hv[i] = 0;
+        }
+        if (m >= R) {
+            ring_pick<VEC, R, R>(ring, rx, hv);
+        } else if (m == 0) {
+            ring_pick<VEC, R, 0>(ring, rx, hv);
+        } else if constexpr (R > 1) {
+            if (m == 1) {
+                ring_pick<VEC, R, (R > 1 ? 1 : 0)>(ring, rx, hv);
+            } else if constexpr (R > 2) {
+                ring_pick<VEC, R, (R > 2 ? 2 : 0)>(ring, rx, hv);
+            }
         }
     }
 }
