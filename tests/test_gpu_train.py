@@ -121,6 +121,20 @@ def test_channel_tails(D):
     check_against_oracle(inp, run_train(inp), f"D={D}")
 
 
+@pytest.mark.parametrize("D", [4104, 4160], ids=["rows_off_lines", "rows_on_lines"])
+def test_seventeen_strip_plans(D):
+    """D = 4104 and 4160 give 17 channel strips, so the default plan cuts the batch rows into
+    segments that fit the wave slots; at 4104 the rows do not start on 128-byte lines and the
+    plan takes plain loads and stores, at 4160 they do and it keeps the non-temporal ones.
+    Both against the oracle, every output."""
+    B, T = 4, 700
+    cf = cc.cconv_default_config("fwd", B, T, D, 4)
+    cb = cc.cconv_default_config("bwd", B, T, D, 4)
+    assert cf.vec == 4 and cf.options == (8 if D == 4104 else 11) and cb.options == cf.options
+    inp = si.train_inputs(B, T, D, 4, bias=True, seed=130 + D)
+    check_against_oracle(inp, run_train(inp), f"D{D}")
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 4])
 @pytest.mark.parametrize("bias", [True, False])
 @pytest.mark.parametrize("w_dtype", [torch.bfloat16, torch.float32], ids=["wbf16", "wf32"])
