@@ -239,6 +239,60 @@ def run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo
                      lambda xn=xn, dyn=dyn, wn=wn, bn=bn, dxn=dxn, dwn=dwn, dbn=dbn, wsn=wsn:
                      cc.cconv_bwd(xn, dyn, wn, bn, dx=dxn, dw=dwn, dbias=dbn, workspace=wsn), copy2, {}, cap))
 
+    # a fused q|k|v projection of a KDA layer: q and k at 1024 channels, v at twice that, so
+    # [B, T, 4096] in all; one call over the 4096 channels (the three taps and biases
+    # concatenated) against three calls on its channel slices (row stride 4096)
+    parts = (1024, 1024, 2048)
+    Dq = sum(parts)
+    qin = si.train_inputs_device(B, T, Dq, W, bias=True, seed=s.seed + 6, device=dev)
+    xq, wq, bq, dyq = qin["x"], qin["w"], qin["bias"], qin["dy"]
+    yq, dxq = torch.empty_like(xq), torch.empty_like(xq)
+    dwq, dbq = torch.empty_like(wq), torch.empty(Dq, dtype=torch.float32, device=dev)
+    wsq = torch.empty(cc.cconv_bwd_workspace_bytes(B, T, Dq, W) // 4 + 1, dtype=torch.float32, device=dev)
+    edges = [0, parts[0], parts[0] + parts[1], Dq]
+    sl = [slice(edges[j], edges[j + 1]) for j in range(3)]
+    x3 = [xq[:, :, q] for q in sl]
+    dy3 = [dyq[:, :, q] for q in sl]
+    w3 = [wq[q].contiguous() for q in sl]
+    b3 = [bq[q].contiguous() for q in sl]
+    y3 = [torch.empty(B, T, p_, dtype=torch.bfloat16, device=dev) for p_ in parts]
+    dx3 = [torch.empty(B, T, p_, dtype=torch.bfloat16, device=dev) for p_ in parts]
+    dw3 = [torch.empty_like(t) for t in w3]
+    db3 = [torch.empty(p_, dtype=torch.float32, device=dev) for p_ in parts]
+    ws3 = [torch.empty(cc.cconv_bwd_workspace_bytes(B, T, p_, W) // 4 + 1, dtype=torch.float32, device=dev)
+           for p_ in parts]
+    nq = B * T * Dq
+    wqb = wq.numel() * wq.element_size()
+    work = f"[{B},{T},{parts[0]}+{parts[1]}+{parts[2]}] W={W}"
+
+    def fwd3():
+        for j in range(3):
+            cc.cconv_fwd(x3[j], w3[j], b3[j], y=y3[j])
+
+    def bwd3():
+        for j in range(3):
+            cc.cconv_bwd(x3[j], dy3[j], w3[j], b3[j], dx=dx3[j], dw=dw3[j], dbias=db3[j], workspace=ws3[j])
+
+    def cap_qkv():
+        cc.cconv_fwd(xq, wq, bq, y=yq)
+        cc.cconv_bwd(xq, dyq, wq, bq, dx=dxq, dw=dwq, dbias=dbq, workspace=wsq)
+        fwd3()
+        bwd3()
+        torch.cuda.synchronize()
+        S["qkv"] = {"x": xq[:1].cpu(), "dy": dyq[:1].cpu(), "w": wq.cpu(), "b": bq.cpu(), "y": yq[0].cpu(),
+                    "dx": dxq[0].cpu(), "y3": torch.cat([t[0] for t in y3], dim=1).cpu(),
+                    "dx3": torch.cat([t[0] for t in dx3], dim=1).cpu()}
+
+    todo.append(("fwd_qkv_one", "forward, fused q|k|v in one call", work, 4 * nq + wqb + Dq * 4,
+                 lambda: cc.cconv_fwd(xq, wq, bq, y=yq), copy1, {}, None))
+    todo.append(("fwd_qkv_three", "forward, fused q|k|v as three strided calls", work, 4 * nq + wqb + Dq * 4,
+                 fwd3, copy1, {}, None))
+    todo.append(("bwd_qkv_one", "backward, fused q|k|v in one call", work, 6 * nq + 2 * wqb + 2 * Dq * 4,
+                 lambda: cc.cconv_bwd(xq, dyq, wq, bq, dx=dxq, dw=dwq, dbias=dbq, workspace=wsq), copy2, {}, None))
+    todo.append(("bwd_qkv_three", "backward, fused q|k|v as three strided calls", work,
+                 6 * nq + 2 * wqb + 2 * Dq * 4, bwd3, copy2, {}, cap_qkv))
+    big.append((qin, yq, dxq, wsq, y3, dx3, ws3))
+
     # decode variants at the decode workload: a state of L = W entries, rewritten (shift) or
     # addressed as a circular buffer by cache_seqlens (one entry written per channel)
     Nd, Sd, Dd = dshape.N, dshape.S, dshape.D
@@ -416,6 +470,21 @@ def oracle_variants(oracle, np, torch, S, err):
         put(name, t, nb, f"the whole call (N={N})",
             {"y": (err(v["y"].float(), yr) if ok else 1.0, 5e-3),
              "state_bit_exact": (bool(ok and v["status_ok"]) and same(v["new_state"], sr), None)})
+    v = S["qkv"]
+    Dq3 = v["x"].shape[2]
+    t0 = _t.perf_counter()
+    _, yr = oracle.fwd(v["x"], v["w"], v["b"], precision="f32")
+    t1 = _t.perf_counter()
+    dxr, _, _ = oracle.bwd(v["x"], v["dy"], v["w"], v["b"], precision="f32")
+    t2 = _t.perf_counter()
+    oneq = f"batch row 0 ({T} x {Dq3})"
+    put("fwd_qkv_one", t1 - t0, 4 * T * Dq3, oneq, {"y": (err(v["y"].float(), yr[0]), 5e-3)})
+    put("bwd_qkv_one", t2 - t1, 6 * T * Dq3, oneq, {"dx": (err(v["dx"].float(), dxr[0]), 8e-3)})
+    # the three strided calls must give the one call's y and dx bit for bit
+    put("fwd_qkv_three", t1 - t0, 4 * T * Dq3, oneq,
+        {"y": (err(v["y3"].float(), yr[0]), 5e-3), "same_bits_as_one_call": (bool(torch.equal(bits(v["y3"]), bits(v["y"]))), None)})
+    put("bwd_qkv_three", t2 - t1, 6 * T * Dq3, oneq,
+        {"dx": (err(v["dx3"].float(), dxr[0]), 8e-3), "same_bits_as_one_call": (bool(torch.equal(bits(v["dx3"]), bits(v["dx"]))), None)})
     v = S["update_hbm"]
     N, Dd = v["y"].shape
     t0 = _t.perf_counter()

@@ -84,6 +84,11 @@ typedef enum {
  *   bias  fp32 [D], or NULL for none.
  *   y     bf16 [B, T, D] contiguous (written; must not overlap x, w or bias).
  *   B, T >= 0; 0 <= D <= 2^30; 1 <= W <= 4.
+ * Channels are independent, so the q, k and v convolutions of a fused projection
+ * [B, T, Dq + Dk + Dv] are one call over all its channels with the three taps and biases
+ * concatenated; y (and, in cconv_bwd, dx) is bit for bit that of three calls on the channel
+ * slices with row stride Dq + Dk + Dv [kernel-fun wheel, cconv/__init__.py docstring: a KDA
+ * layer convolves q, k and v separately, v twice as wide].
  */
 cconv_status_t cconv_fwd(const void* x, int64_t x_sb, int64_t x_st, const void* w,
                          cconv_dtype_t w_dtype, const float* bias, void* y, int64_t B,

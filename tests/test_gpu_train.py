@@ -135,6 +135,34 @@ def test_seventeen_strip_plans(D):
     check_against_oracle(inp, run_train(inp), f"D{D}")
 
 
+@pytest.mark.parametrize("split", [(512, 512, 512), (256, 256, 512)])
+def test_fused_qkv_one_launch_equals_three(split):
+    """A fused q|k|v projection [B, T, Dq + Dk + Dv] convolved in one call (the three taps and
+    biases concatenated) equals three calls on its channel slices (row stride Dq + Dk + Dv, no
+    copy): y and dx bit for bit (the same arithmetic per channel and row), dw and dbias to the
+    tolerance (their fixed-order sums are grouped by a different plan). Splits: equal thirds,
+    and a KDA layer's (v twice as wide as q and k) [kernel-fun wheel, cconv/__init__.py
+    docstring]."""
+    B, T, W = 2, 600, 4
+    Dt = sum(split)
+    inp = si.train_inputs(B, T, Dt, W, bias=True, seed=150)
+    g = _gpu(inp)
+    y, (dx, dw, db) = cc.cconv_fwd(g["x"], g["w"], g["bias"]), cc.cconv_bwd(g["x"], g["dy"], g["w"], g["bias"])
+    parts, lo = [], 0
+    for Dj in split:
+        sl = slice(lo, lo + Dj)
+        lo += Dj
+        xs, dys = g["x"][:, :, sl], g["dy"][:, :, sl]
+        wj, bj = g["w"][sl].contiguous(), g["bias"][sl].contiguous()
+        parts.append((cc.cconv_fwd(xs, wj, bj),) + tuple(cc.cconv_bwd(xs, dys, wj, bj)))
+    torch.cuda.synchronize()
+    assert torch.equal(bits(y), bits(torch.cat([p[0] for p in parts], dim=2)))
+    assert torch.equal(bits(dx), bits(torch.cat([p[1] for p in parts], dim=2)))
+    assert_close(dw.cpu().float(), torch.cat([p[2] for p in parts]).cpu().float(), TOL_BWD, "fused dw")
+    assert_close(db.cpu(), torch.cat([p[3] for p in parts]).cpu(), TOL_BWD, "fused dbias")
+    check_against_oracle(inp, (y.cpu(), dx.cpu(), dw.cpu(), db.cpu()), "fused q|k|v")
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 4])
 @pytest.mark.parametrize("bias", [True, False])
 @pytest.mark.parametrize("w_dtype", [torch.bfloat16, torch.float32], ids=["wbf16", "wf32"])
