@@ -558,13 +558,21 @@ def main():
     )
     bytes_step = bytes_fwd + bytes_bwd + bytes_upd
 
+    # launches of the backward main kernel at this shape, counted so that a kernel trace of this
+    # run can be cut at the first variant (variants launch the same kernel at other shapes)
+    n_main = [0]
+
+    def bwd_main():
+        n_main[0] += 1
+        cc.cconv_bwd_main(x, dy, w, b, dxo, ws)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
         cc.cconv_fwd(x, w, b, y=y)
         if ev is not None:
             ev[1].record()
-        cc.cconv_bwd_main(x, dy, w, b, dxo, ws)
+        bwd_main()
         if ev is not None:
             ev[2].record()
         cc.cconv_bwd_finish(ws, dwo, dbo, B, T, D, W)
@@ -699,7 +707,7 @@ def main():
                     ev[0].record()
                     cc.cconv_fwd(x, w, b, y=y)
                     ev[1].record()
-                    cc.cconv_bwd_main(x, dy, w, b, dxo, ws)
+                    bwd_main()
                     ev[2].record()
                     cc.cconv_bwd_finish(ws, dwo, dbo, B, T, D, W)
                     kt.append(ev)
@@ -730,6 +738,7 @@ def main():
 
     # ---- the widened rows, each timed alone at its own workload (outside `value`) ---------
     log("variants: state handoff, pool prefill, packed batch, epilogues, any D, decode variants")
+    main_launches = n_main[0]
     variants, vsample = run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo, dwo, dbo, ws,
                                      quant, copy1[0], copy2[0], HBM_PEAK_GBPS)
 
@@ -862,6 +871,9 @@ def main():
             "kernel": "cconv_bwd_kernel (backward main: dx and dw/dbias partials)",
             "bytes_per_launch": bytes_bwd_main,
             "us_per_launch": round(t_main * 1e6, 2),
+            # the first this many launches of the kernel in a trace of this run are at this
+            # shape (the variants that follow launch it at others)
+            "launches_at_shape": main_launches,
         },
         "cpu_baseline": cpu,
         "parity_gate": gate,
