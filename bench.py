@@ -216,17 +216,18 @@ def run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo
     # D other than the headline's: 4100 takes the element-granular path (one channel per lane),
     # 4104 the vector path with 17 channel strips whose rows do not start on cache lines
     big = []
-    for Dn, tag, what in ((4100, "any_d", "D not a multiple of 8 (one channel per lane)"),
-                          (4104, "d4104", "D = 4104 (vector path, rows not on 128-byte lines)")):
-        nin = si.train_inputs_device(B, T, Dn, W, bias=True, seed=s.seed + 5, device=dev)
+    for Bn, Dn, tag, what in ((B, 4100, "any_d", "D not a multiple of 8 (one channel per lane)"),
+                              (B, 4104, "d4104", "D = 4104 (vector path, rows not on 128-byte lines)"),
+                              (2 * B, D // 2, "b16_d2048", "the pages' production call shape (B = 16, D = 2048)")):
+        nin = si.train_inputs_device(Bn, T, Dn, W, bias=True, seed=s.seed + 5, device=dev)
         xn, wn, bn, dyn = nin["x"], nin["w"], nin["bias"], nin["dy"]
         yn, dxn = torch.empty_like(xn), torch.empty_like(xn)
         dwn, dbn = torch.empty_like(wn), torch.empty(Dn, dtype=torch.float32, device=dev)
-        wsn = torch.empty(cc.cconv_bwd_workspace_bytes(B, T, Dn, W) // 4 + 1, dtype=torch.float32, device=dev)
+        wsn = torch.empty(cc.cconv_bwd_workspace_bytes(Bn, T, Dn, W) // 4 + 1, dtype=torch.float32, device=dev)
         big.append((nin, yn, dxn, wsn))
-        nn_ = B * T * Dn
+        nn_ = Bn * T * Dn
         wnb = wn.numel() * wn.element_size()
-        work = f"[{B},{T},{Dn}] W={W}"
+        work = f"[{Bn},{T},{Dn}] W={W}"
 
         def cap(tag=tag, xn=xn, dyn=dyn, wn=wn, bn=bn, yn=yn, dxn=dxn):
             torch.cuda.synchronize()
@@ -447,7 +448,7 @@ def oracle_variants(oracle, np, torch, S, err):
     dxr = oracle.bwd_epi(x1, dy1, w, b, act=False, precision="f32")[0]
     t = _t.perf_counter() - t0
     put("bwd_linear", t, 6 * T * D, one, {"dx": (err(S["bwd_linear"]["dx"].float(), dxr[0]), 8e-3)})
-    for tag in ("any_d", "d4104"):
+    for tag in ("any_d", "d4104", "b16_d2048"):
         v = S[tag]
         Dn = v["x"].shape[2]
         t0 = _t.perf_counter()
@@ -742,6 +743,23 @@ def main():
     variants, vsample = run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo, dwo, dbo, ws,
                                      quant, copy1[0], copy2[0], HBM_PEAK_GBPS)
 
+    # ---- host enqueue cost of one eager decode update through the Python binding: wall time
+    # per call over back-to-back calls (each runs ~6 us on the GPU, so the host sets the pace)
+    def host_enqueue(fn, n=400):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            ts.append((time.perf_counter() - t0) / n)
+            torch.cuda.synchronize()
+        return sorted(ts)[len(ts) // 2]
+
+    enqueue_us = round(1e6 * host_enqueue(
+        lambda: cc.cconv_update(dx_in, state, sidx, dw_, db_, y=yd, status=status)), 2)
+
     # ---- CPU baseline: the oracle, timed on a bounded sample of the same workload ---------
     cpu = None
     gate = None
@@ -860,6 +878,7 @@ def main():
             "bytes_per_operand": nbytes,
         },
         "interleaved": inter,
+        "update_host_enqueue_us": enqueue_us,
         "variants": variants,
         "roofline": {
             "bound": "hbm",

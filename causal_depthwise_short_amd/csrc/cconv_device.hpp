@@ -122,9 +122,12 @@ constexpr int kResidual = 32;
 // The wave's index in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 
-// A row element at a wave-uniform base plus a lane's byte offset. Keeping the offset a 32-bit
-// byte count lets the compiler use the scalar-base addressing form (global_load v, v_off,
-// s[base]), so a new row costs scalar arithmetic only.
+// A row element at a wave-uniform base plus a lane's byte offset (a 32-bit byte count). In the
+// row loops the compiler keeps each lane's 64-bit row address in vector registers and steps it
+// by the row stride: one 64-bit vector add per load or store. Addressing the rows through
+// buffer resources instead (scalar row offsets, no vector address arithmetic) removed those
+// adds, 3% of the backward's vector instructions, and measured no faster: the loops wait on
+// memory, not on issue.
 template <typename P>
 __device__ __forceinline__ P* at(P* base, uint32_t off_bytes) {
     using C = typename std::conditional<std::is_const<P>::value, const char, char>::type;

@@ -125,8 +125,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     if (wt.d >= a.D) return;  // lanes past the last channel (D is a multiple of VEC)
     if (a.status && *a.status != 0) return;  // the slot or offset check failed: write nothing
 
-    // Row bases are wave-uniform (scalar registers); a lane adds its 32-bit channel offset,
-    // so a row load is one global_load with a scalar base and no per-row VALU address math.
+    // Row bases are wave-uniform; a lane adds its 32-bit byte offset to reach its channels.
     const uint32_t lo = static_cast<uint32_t>(wt.d) * 2u;  // byte offset of the lane's channels
     const uint16_t* __restrict__ xb = a.x + wt.b * a.x_sb;
     uint16_t* __restrict__ yb = a.y + wt.b * a.T * a.D;
