@@ -89,7 +89,11 @@ class Config(ctypes.Structure):
 class CconvError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {STATUS.get(status, status)} ({cconv_status_string(status)})")
+        msg = f"{where}: {STATUS.get(status, status)}"
+        # the library's own text only when it is loaded (it may be what failed to load)
+        if _lib is not None:
+            msg += f" ({cconv_status_string(status)})"
+        super().__init__(msg)
 
 
 _lock = threading.Lock()

@@ -36,6 +36,20 @@ def test_exports_every_declared_symbol():
         assert not missing, f"{path.name} lacks {missing}"
 
 
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """With no built library and no way to build one, every entry point raises: there is no
+    fallback path that computes anything without the HIP library."""
+    import causal_depthwise_short_amd._build as build
+
+    monkeypatch.setattr(cc, "_lib", None)
+    monkeypatch.setattr(cc, "LIB_PATH", tmp_path / "libcconv.so")
+    monkeypatch.setattr(build, "build", lambda *a, **k: None)
+    with pytest.raises(cc.CconvError):
+        cc.lib()
+    with pytest.raises(cc.CconvError):
+        cc.cconv_default_config("fwd", 1, 16, 64, 4)
+
+
 def test_version_and_status_strings():
     assert "gfx950" in cc.cconv_version()
     for code in range(11):
