@@ -237,12 +237,46 @@ def _stream(stream) -> Optional[int]:
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else t.data_ptr()
+    if t is None:
+        return None
+    _dev(t, "every tensor handed to the library")
+    return t.data_ptr()
 
 
 def _dev(t: torch.Tensor, name: str):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    # the library launches on the current device: an operand elsewhere would be read through a
+    # foreign address
+    if t.get_device() != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device cuda:{torch.cuda.current_device()}")
+
+
+def _out(t: Optional[torch.Tensor], name: str, shape, dtypes):
+    """A caller-provided output or buffer: the library learns only its address, so its device,
+    dtype, shape and layout are checked here (an undersized tensor would be written past)."""
+    if t is None:
+        return
+    _dev(t, name)
+    if t.dtype not in dtypes or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        kinds = "/".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} must be a contiguous {kinds} tensor of shape {list(shape)}")
+
+
+def _ws(t: Optional[torch.Tensor]) -> int:
+    """Bytes of a caller-provided workspace (contiguous, on the current device)."""
+    if t is None:
+        return 0
+    _dev(t, "workspace")
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return t.numel() * t.element_size()
+
+
+_BF = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_WT = (torch.bfloat16, torch.float32)
 
 
 def _wdt(t: torch.Tensor, name: str) -> int:
@@ -341,10 +375,13 @@ def cconv_bwd(
         dw = torch.empty((D, W), dtype=dw_dtype or w.dtype, device=dev)
     if want_dbias and dbias is None:
         dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    _out(dx, "dx", x.shape, _BF)
+    _out(dw, "dw", (D, W), _WT)
+    _out(dbias, "dbias", (D,), _F32)
     need = cconv_bwd_workspace_bytes(B, T, D, W, config)
     if workspace is None and need > 0:
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws(workspace)
     L = lib()
     args = (
         _ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(dx), _ptr(dw),
@@ -438,6 +475,7 @@ def cconv_fwd_pool(x, w, bias, state, state_indices, has_initial_state=None, *, 
         raise ValueError("y must be a contiguous bf16 [B, T, D] tensor")
     if status is None:
         status = torch.empty(1, dtype=torch.int32, device=x.device)
+    _out(status, "status", (1,), _I32)
     _check(
         lib().cconv_fwd_pool(
             _ptr(x), sb, st, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(state), S, _ptr(state_indices),
@@ -477,13 +515,16 @@ def cconv_bwd_state(x, dy, w, bias=None, init_state=None, *, dx=None, dw=None, d
         dw = torch.empty((D, W), dtype=dw_dtype or w.dtype, device=dev)
     if want_dbias and dbias is None:
         dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    _out(dx, "dx", x.shape, _BF)
+    _out(dw, "dw", (D, W), _WT)
+    _out(dbias, "dbias", (D,), _F32)
     if want_d_init_state and d_init_state is None:
         d_init_state = torch.empty((B, D, W - 1), dtype=torch.bfloat16, device=dev)
     _state(d_init_state, "d_init_state", B, D, W)
     need = cconv_bwd_workspace_bytes(B, T, D, W)
     if workspace is None and need > 0:
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws(workspace)
     _check(
         lib().cconv_bwd_state(
             _ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(init_state), _ptr(dx),
@@ -536,6 +577,7 @@ def cconv_fwd_varlen(x, cu_seqlens, w, bias=None, init_state=None, *, final_stat
         raise ValueError("y must be a contiguous bf16 [total, D] tensor")
     if status is None:
         status = torch.empty(1, dtype=torch.int32, device=x.device)
+    _out(status, "status", (1,), _I32)
     args = (_ptr(x), xst, _ptr(cu_seqlens), n, total, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(init_state),
             _ptr(final_state), _ptr(status), _ptr(y), D, W)
     L = lib()
@@ -571,15 +613,19 @@ def cconv_bwd_varlen(x, dy, cu_seqlens, w, bias=None, init_state=None, *, dx=Non
         dw = torch.empty((D, W), dtype=dw_dtype or w.dtype, device=dev)
     if want_dbias and dbias is None:
         dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    _out(dx, "dx", x.shape, _BF)
+    _out(dw, "dw", (D, W), _WT)
+    _out(dbias, "dbias", (D,), _F32)
     if want_d_init_state and d_init_state is None:
         d_init_state = torch.empty((n, D, W - 1), dtype=torch.bfloat16, device=dev)
     _state(d_init_state, "d_init_state", n, D, W)
     need = cconv_bwd_workspace_bytes(1, total, D, W, config)
     if workspace is None and need > 0:
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws(workspace)
     if status is None:
         status = torch.empty(1, dtype=torch.int32, device=dev)
+    _out(status, "status", (1,), _I32)
     args = (_ptr(x), xst, _ptr(dy), dyst, _ptr(cu_seqlens), n, total, _ptr(w), _wdt(w, "w"), _ptr(bias),
             _ptr(init_state), _ptr(dx), _ptr(dw), _wdt(dw, "dw"), _ptr(dbias), _ptr(d_init_state), _ptr(workspace),
             ws_bytes, _ptr(status), D, W)
@@ -596,8 +642,15 @@ def cconv_bwd_main(x, dy, w, bias, dx, workspace, *, stream=None):
     sb, st = _act(x, "x")
     dsb, dst = _act(dy, "dy")
     B, T, D = x.shape
+    if tuple(dy.shape) != (B, T, D):
+        raise ValueError("dy must have x's shape")
+    _dev(w, "w")
     W = w.shape[1]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    _out(bias, "bias", (D,), _F32)
+    _out(dx, "dx", (B, T, D), _BF)
+    ws_bytes = _ws(workspace)
     _check(
         lib().cconv_bwd_main(
             _ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(dx), _ptr(workspace),
@@ -610,7 +663,9 @@ def cconv_bwd_main(x, dy, w, bias, dx, workspace, *, stream=None):
 
 def cconv_bwd_finish(workspace, dw, dbias, B: int, T: int, D: int, W: int, *, stream=None):
     """Second backward stage: dw (in dw's dtype) and dbias from the partials."""
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _out(dw, "dw", (D, W), _WT)
+    _out(dbias, "dbias", (D,), _F32)
+    ws_bytes = _ws(workspace)
     _check(
         lib().cconv_bwd_finish(
             _ptr(workspace), ws_bytes, _ptr(dw), _wdt(dw, "dw"), _ptr(dbias), B, T, D, W, _stream(stream)
@@ -649,8 +704,10 @@ def cconv_update(x, state, state_indices, w, bias=None, *, y=None, status=None, 
             raise ValueError("bias must be a contiguous fp32 [D] tensor")
     if y is None:
         y = torch.empty((N, D), dtype=torch.bfloat16, device=x.device)
+    _out(y, "y", (N, D), _BF)
     if status is None:
         status = torch.empty((1,), dtype=torch.int32, device=x.device)
+    _out(status, "status", (1,), _I32)
     _check(
         lib().cconv_update(
             _ptr(x), x.stride(0) if N > 0 else D, _ptr(state), S, _ptr(state_indices), _ptr(w), _wdt(w, "w"),
@@ -689,8 +746,10 @@ def cconv_update_ex(x, state, state_indices, w, bias=None, *, cache_seqlens=None
             raise ValueError("bias must be a contiguous fp32 [D] tensor")
     if y is None:
         y = torch.empty((N, D), dtype=torch.bfloat16, device=x.device)
+    _out(y, "y", (N, D), _BF)
     if status is None:
         status = torch.empty((1,), dtype=torch.int32, device=x.device)
+    _out(status, "status", (1,), _I32)
     _check(
         lib().cconv_update_ex(
             _ptr(x), x.stride(0) if N > 0 else D, _ptr(state), S, L, _ptr(state_indices), _ptr(cache_seqlens),
@@ -747,6 +806,7 @@ def cconv_fwd_ex(x, w, bias=None, *, activation="silu", residual=None, init_stat
         raise ValueError("y must be a contiguous bf16 tensor of x's shape")
     if packed and status is None:
         status = torch.empty(1, dtype=torch.int32, device=x.device)
+    _out(status, "status", (1,), _I32)
     o = FwdOpts(ACTIVATIONS[activation], _ptr(residual), rsb, rst, _ptr(init_state), _ptr(final_state),
                 _ptr(cu_seqlens), state_rows if packed else 0, _ptr(status) if packed else None)
     _check(lib().cconv_fwd_ex(_ptr(x), sb, st, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(y), B, T, D, W,
@@ -788,15 +848,19 @@ def cconv_bwd_ex(x, dy, w, bias=None, *, activation="silu", init_state=None, d_i
         dw = torch.empty((D, W), dtype=dw_dtype or w.dtype, device=dev)
     if want_dbias and dbias is None:
         dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    _out(dx, "dx", x.shape, _BF)
+    _out(dw, "dw", (D, W), _WT)
+    _out(dbias, "dbias", (D,), _F32)
     if want_d_init_state and d_init_state is None:
         d_init_state = torch.empty((state_rows, D, W - 1), dtype=torch.bfloat16, device=dev)
     _state(d_init_state, "d_init_state", state_rows, D, W)
     need = cconv_bwd_workspace_bytes(B, T, D, W)
     if workspace is None and need > 0:
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws(workspace)
     if packed and status is None:
         status = torch.empty(1, dtype=torch.int32, device=dev)
+    _out(status, "status", (1,), _I32)
     o = BwdOpts(ACTIVATIONS[activation], _ptr(init_state), _ptr(d_init_state), _ptr(cu_seqlens),
                 state_rows if packed else 0, _ptr(status) if packed else None)
     _check(lib().cconv_bwd_ex(_ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(dx),

@@ -50,6 +50,21 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         cc.cconv_default_config("fwd", 1, 16, 64, 4)
 
 
+def test_host_tensors_are_refused_before_any_call():
+    """The binding hands the library bare addresses, so it refuses tensors that are not on the
+    GPU (inputs and caller-provided outputs alike) before calling it."""
+    import torch
+
+    x = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    w = torch.zeros(64, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        cc.cconv_fwd(x, w)
+    with pytest.raises(ValueError, match="GPU"):
+        cc.cconv_bwd(x, x, w)
+    with pytest.raises(ValueError, match="GPU"):
+        cc.cconv_update(x[0], torch.zeros(4, 64, 3, dtype=torch.bfloat16), None, w)
+
+
 def test_version_and_status_strings():
     assert "gfx950" in cc.cconv_version()
     for code in range(11):
