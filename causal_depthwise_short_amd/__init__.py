@@ -243,13 +243,18 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+# the current device, read without torch.cuda.current_device()'s per-call initialisation check
+# (a GPU tensor exists by the time it is asked, so the runtime is initialised)
+_current_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+
+
 def _dev(t: torch.Tensor, name: str):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
     # the library launches on the current device: an operand elsewhere would be read through a
     # foreign address
-    if t.get_device() != torch.cuda.current_device():
-        raise ValueError(f"{name} is on {t.device}, not on the current device cuda:{torch.cuda.current_device()}")
+    if t.get_device() != _current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device cuda:{_current_device()}")
 
 
 def _out(t: Optional[torch.Tensor], name: str, shape, dtypes):
