@@ -199,6 +199,9 @@ def _ensure_built(path: Path):
 def lib() -> ctypes.CDLL:
     """The loaded libcconv.so (built in-tree on first use if absent)."""
     global _lib
+    L = _lib
+    if L is not None:  # loaded: no lock on the per-call path
+        return L
     with _lock:
         if _lib is None:
             _ensure_built(LIB_PATH)
@@ -230,6 +233,8 @@ def cconv_version() -> str:
 
 def _stream(stream) -> Optional[int]:
     if stream is None:
+        if _raw_stream is not None:  # the current stream's handle without building a Stream object
+            return _raw_stream(_current_device())
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
@@ -246,6 +251,7 @@ def _ptr(t: Optional[torch.Tensor]):
 # the current device, read without torch.cuda.current_device()'s per-call initialisation check
 # (a GPU tensor exists by the time it is asked, so the runtime is initialised)
 _current_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _dev(t: torch.Tensor, name: str):

@@ -174,6 +174,39 @@ def test_widths_bias_dtypes(W, bias, w_dtype):
         check_against_oracle(inp, outs, f"W={W} bias={bias} w={w_dtype} dw={dw_dtype}")
 
 
+def test_binding_rejects_mismatched_outputs():
+    """The library sees only addresses: an output of the wrong shape, dtype or layout, or one in
+    host memory, is refused by the binding before any launch, and nothing is written."""
+    B, T, D, W = 2, 64, 256, 4
+    g = _gpu(si.train_inputs(B, T, D, W, bias=True, seed=160))
+    x, dy, w, b = g["x"], g["dy"], g["w"], g["bias"]
+    small = torch.zeros((B, T - 1, D), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        cc.cconv_fwd(x, w, b, y=small)
+    with pytest.raises(ValueError):
+        cc.cconv_bwd(x, dy, w, b, dx=small)
+    with pytest.raises(ValueError):
+        cc.cconv_bwd(x, dy, w, b, dw=torch.zeros((D, W + 1), dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        cc.cconv_bwd(x, dy, w, b, dbias=torch.zeros((D,), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        cc.cconv_bwd(x, dy, w, b, dx=torch.zeros((B, T, D), dtype=torch.bfloat16))  # host memory
+    with pytest.raises(ValueError):
+        cc.cconv_bwd(x, dy, w, b, dx=torch.zeros((B, T, 2 * D), dtype=torch.bfloat16, device=DEV)[:, :, :D])
+    torch.cuda.synchronize()
+    assert not small.any()
+
+
+def test_binding_launches_on_the_current_stream():
+    """Without a stream argument the binding launches on torch's current stream (read through
+    its raw handle), also inside a side-stream context."""
+    assert cc._stream(None) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert cc._stream(None) == s.cuda_stream == torch.cuda.current_stream().cuda_stream
+    assert cc._stream(s) == s.cuda_stream
+
+
 def test_empty_problems():
     for B, T in [(0, 16), (3, 0)]:
         inp = si.train_inputs(B, T, 64, 4, bias=True, seed=1)
