@@ -60,6 +60,9 @@ MEDIUM = TrainShape("B8_T1024_D4096_W4_nobias", 8, 1024, 4096, 4, False, 1)
 HEADLINE = TrainShape("B8_T8192_D4096_W4_bias", 8, 8192, 4096, 4, True, 2)
 RAGGED = TrainShape("B3_T1000_D2000_W2_bias", 3, 1000, 2000, 2, True, 3)
 DECODE = DecodeShape("decode_N256_S512_D4096_W4_bias", 256, 512, 4096, 4, True, 4)
+# the production call the kernel-fun wheel's cconv/__init__.py docstring measures (the
+# headline's element count): a parity case, not a bench line
+PRODUCTION = TrainShape("B16_T8192_D2048_W4_bias", 16, 8192, 2048, 4, True, 5)
 
 TRAIN_SHAPES = (TINY, MEDIUM, HEADLINE, RAGGED)
 

@@ -52,9 +52,9 @@ def test_parity_full(shape):
     check_against_oracle(inp, run_train(inp), shape.name)
 
 
-@pytest.fixture(scope="module")
-def headline():
-    s = si.HEADLINE
+@pytest.fixture(scope="module", params=[si.HEADLINE, si.PRODUCTION], ids=lambda s: s.name)
+def headline(request):
+    s = request.param
     inp = si.train_inputs_for(s)
     outs = run_train(inp)
     xf = inp["x"].float().numpy()
@@ -88,16 +88,16 @@ def test_headline_sampled_parity(headline):
     cfg_f = cc.cconv_default_config("fwd", s.B, s.T, s.D, s.W)
     pb, pt, pd = _sample_points(s, cfg_f, rng)
     yr = oracle.fwd_points(xf, inp["w"], inp["bias"], pb, pt, pd)
-    e1 = assert_close(y[pb, pt, pd], yr, TOL_FWD, "headline y (sampled)")
+    e1 = assert_close(y[pb, pt, pd], yr, TOL_FWD, f"{s.name} y (sampled)")
     cfg_b = cc.cconv_default_config("bwd", s.B, s.T, s.D, s.W)
     pb, pt, pd = _sample_points(s, cfg_b, rng)
     dxr = oracle.dx_points(xf, dyf, inp["w"], inp["bias"], pb, pt, pd)
-    e2 = assert_close(dx[pb, pt, pd], dxr, TOL_BWD, "headline dx (sampled)")
+    e2 = assert_close(dx[pb, pt, pd], dxr, TOL_BWD, f"{s.name} dx (sampled)")
     ch = np.unique(np.concatenate([rng.integers(0, s.D, 40), [0, 1, 511, 512, s.D - 1]]))
     dwr, dbr = oracle.dw_channels(xf, dyf, inp["w"], inp["bias"], ch)
-    e3 = assert_close(dw[ch], dwr, TOL_BWD, "headline dw (sampled channels)")
-    e4 = assert_close(db[ch], dbr, TOL_BWD, "headline dbias (sampled channels)")
-    print(f"headline sampled: err y {e1:.2e} dx {e2:.2e} dw {e3:.2e} dbias {e4:.2e} ({pb.size} points, {ch.size} channels)")
+    e3 = assert_close(dw[ch], dwr, TOL_BWD, f"{s.name} dw (sampled channels)")
+    e4 = assert_close(db[ch], dbr, TOL_BWD, f"{s.name} dbias (sampled channels)")
+    print(f"{s.name} sampled: err y {e1:.2e} dx {e2:.2e} dw {e3:.2e} dbias {e4:.2e} ({pb.size} points, {ch.size} channels)")
 
 
 def test_headline_outputs_finite_and_deterministic(headline):
