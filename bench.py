@@ -8,10 +8,11 @@ One step is one pass of the whole path over one batch of synthetic input:
 The printed value is the algorithmic bytes of every timed step (what the method must move:
 x + y + taps + bias forward; x + dy + dx + taps + dw + bias + dbias backward; x + state read
 and write + y + taps + bias + indices decode) divided by the wall time of the timed region,
-inputs already resident in HBM. HIP events on the launch stream give each kernel's duration
-inside the same timed region; the backward's main kernel is the dominant one and is reported
-against MI355X's 8 TB/s HBM peak ("roofline"), and every phase against a flat copy with the
-same read:write mix measured in the same run. The CPU oracle is timed beside it on a bounded
+inputs already resident in HBM. HIP events on the launch stream around the backward's main
+kernel, the dominant one, give its duration inside the timed region (the only events there);
+it is reported against MI355X's 8 TB/s HBM peak ("roofline"). A second pass of as many steps,
+with events around every phase, gives the per-phase breakdown, each phase set against a flat
+copy with the same read:write mix measured in the same run. The CPU oracle is timed beside it on a bounded
 sample of the same workload ("cpu_baseline"); that leg also serves as the parity gate.
 
 After the headline (outside the printed value), every widened row of the path is timed alone
@@ -568,19 +569,22 @@ def main():
         cc.cconv_bwd_main(x, dy, w, b, dxo, ws)
 
     def step(ev=None):
-        if ev is not None:
+        """One step. ev: None, two events (around the backward main kernel only: the timed
+        region's instrumentation) or five (every phase: the breakdown pass)."""
+        full = ev is not None and len(ev) == 5
+        if full:
             ev[0].record()
         cc.cconv_fwd(x, w, b, y=y)
         if ev is not None:
-            ev[1].record()
+            ev[1 if full else 0].record()
         bwd_main()
         if ev is not None:
-            ev[2].record()
+            ev[2 if full else 1].record()
         cc.cconv_bwd_finish(ws, dwo, dbo, B, T, D, W)
-        if ev is not None:
+        if full:
             ev[3].record()
         cc.cconv_update(dx_in, state, sidx, dw_, db_, y=yd, status=status)
-        if ev is not None:
+        if full:
             ev[4].record()
 
     # ---- outputs for the parity gate (before any timing) --------------------------------
@@ -644,19 +648,29 @@ def main():
     log(f"timing {K} steps after {Wm} warm-up steps")
     for _ in range(Wm):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    # the timed region carries only the two events the roofline needs (around the backward main
+    # kernel); the per-phase breakdown comes from a second pass of K steps with five events each
+    main_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(events[i])
+        step(main_ev[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    q_main = quant([e[0].elapsed_time(e[1]) * 1e-3 for e in main_ev])
+
+    log(f"per-phase breakdown: {K} more steps with events around every phase")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
 
     def med(i, j):
         return quant([events[k][i].elapsed_time(events[k][j]) * 1e-3 for k in range(K)])
 
-    q_fwd, q_main, q_fin, q_upd, q_bwd = med(0, 1), med(1, 2), med(2, 3), med(3, 4), med(1, 3)
+    q_fwd, q_fin, q_upd, q_bwd = med(0, 1), med(2, 3), med(3, 4), med(1, 3)
     t_fwd, t_main, t_fin, t_upd, t_bwd = q_fwd[1], q_main[1], q_fin[1], q_upd[1], q_bwd[1]
 
     log("flat copy roofline (after)")
