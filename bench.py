@@ -18,7 +18,9 @@ sample of the same workload ("cpu_baseline"); that leg also serves as the parity
 After the headline (outside the printed value), every widened row of the path is timed alone
 at its own workload ("variants": a history in and the final state or its gradient out, prefill
 into a decode pool, a packed batch of mixed lengths, no activation and a residual, a D that is
-not a multiple of 8, and the decode state of W entries, shifted or circular), each checked
+not a multiple of 8, D = 6144 contiguous and in rows of 8192, the pages' production call, a
+fused q|k|v projection in one call and in three, and the decode state of W entries, shifted or
+circular), each checked
 against the oracle on a sample and the oracle timed on that sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
@@ -240,6 +242,48 @@ def run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo
         todo.append((f"bwd_{tag}", f"backward, {what}", work, 6 * nn_ + 2 * wnb + 2 * Dn * 4,
                      lambda xn=xn, dyn=dyn, wn=wn, bn=bn, dxn=dxn, dwn=dwn, dbn=dbn, wsn=wsn:
                      cc.cconv_bwd(xn, dyn, wn, bn, dx=dxn, dw=dwn, dbias=dbn, workspace=wsn), copy2, {}, cap))
+
+    # a width that is not a power of two (6144, v of a 24-head KDA layer), once contiguous and
+    # once with every row of x, dy, y and dx at a power-of-two pitch (8192) through the general
+    # entry points' strides
+    Dp, Pp = 6144, 8192
+    pin = si.train_inputs_device(B, T, Dp, W, bias=True, seed=s.seed + 7, device=dev)
+    xc, dyc, wp, bp = pin["x"], pin["dy"], pin["w"], pin["bias"]
+
+    def pitched(t=None):
+        v = torch.empty(B, T, Pp, dtype=torch.bfloat16, device=dev)[:, :, :Dp]
+        if t is not None:
+            v.copy_(t)
+        return v
+
+    xpd, dypd, ypd, dxpd = pitched(xc), pitched(dyc), pitched(), pitched()
+    yc, dxc = torch.empty_like(xc), torch.empty_like(xc)
+    dwp, dbp = torch.empty_like(wp), torch.empty(Dp, dtype=torch.float32, device=dev)
+    wsp = torch.empty(cc.cconv_bwd_workspace_bytes(B, T, Dp, W) // 4 + 1, dtype=torch.float32, device=dev)
+    npd = B * T * Dp
+    wpb = wp.numel() * wp.element_size()
+    fb_p, bb_p = 4 * npd + wpb + Dp * 4, 6 * npd + 2 * wpb + 2 * Dp * 4
+
+    def cap_pitch():
+        cc.cconv_fwd(xc, wp, bp, y=yc)
+        cc.cconv_fwd_ex(xpd, wp, bp, y=ypd)
+        cc.cconv_bwd(xc, dyc, wp, bp, dx=dxc, dw=dwp, dbias=dbp, workspace=wsp)
+        cc.cconv_bwd_ex(xpd, dypd, wp, bp, dx=dxpd, workspace=wsp)
+        torch.cuda.synchronize()
+        S["pitch"] = {"x": xc[:1].cpu(), "dy": dyc[:1].cpu(), "w": wp.cpu(), "b": bp.cpu(), "y": yc[0].cpu(),
+                      "dx": dxc[0].cpu(), "y_p": ypd[0].contiguous().cpu(), "dx_p": dxpd[0].contiguous().cpu()}
+
+    work_c, work_p = f"[{B},{T},{Dp}] W={W}", f"[{B},{T},{Dp}] W={W}, rows at pitch {Pp}"
+    todo.append(("fwd_d6144", "forward, D = 6144 contiguous", work_c, fb_p,
+                 lambda: cc.cconv_fwd(xc, wp, bp, y=yc), copy1, {}, None))
+    todo.append(("fwd_d6144_pitch8192", "forward, D = 6144 in rows of 8192", work_p, fb_p,
+                 lambda: cc.cconv_fwd_ex(xpd, wp, bp, y=ypd), copy1, {}, None))
+    todo.append(("bwd_d6144", "backward, D = 6144 contiguous", work_c, bb_p,
+                 lambda: cc.cconv_bwd(xc, dyc, wp, bp, dx=dxc, dw=dwp, dbias=dbp, workspace=wsp), copy2, {}, None))
+    todo.append(("bwd_d6144_pitch8192", "backward, D = 6144 in rows of 8192", work_p, bb_p,
+                 lambda: cc.cconv_bwd_ex(xpd, dypd, wp, bp, dx=dxpd, dw=dwp, dbias=dbp, workspace=wsp), copy2, {},
+                 cap_pitch))
+    big.append((pin, xpd, dypd, ypd, dxpd, yc, dxc, wsp))
 
     # a fused q|k|v projection of a KDA layer: q and k at 1024 channels, v at twice that, so
     # [B, T, 4096] in all; one call over the 4096 channels (the three taps and biases
@@ -472,6 +516,20 @@ def oracle_variants(oracle, np, torch, S, err):
         put(name, t, nb, f"the whole call (N={N})",
             {"y": (err(v["y"].float(), yr) if ok else 1.0, 5e-3),
              "state_bit_exact": (bool(ok and v["status_ok"]) and same(v["new_state"], sr), None)})
+    v = S["pitch"]
+    Dp = v["x"].shape[2]
+    t0 = _t.perf_counter()
+    _, yr = oracle.fwd(v["x"], v["w"], v["b"], precision="f32")
+    t1 = _t.perf_counter()
+    dxr, _, _ = oracle.bwd(v["x"], v["dy"], v["w"], v["b"], precision="f32")
+    t2 = _t.perf_counter()
+    onep = f"batch row 0 ({T} x {Dp})"
+    put("fwd_d6144", t1 - t0, 4 * T * Dp, onep, {"y": (err(v["y"].float(), yr[0]), 5e-3)})
+    put("bwd_d6144", t2 - t1, 6 * T * Dp, onep, {"dx": (err(v["dx"].float(), dxr[0]), 8e-3)})
+    put("fwd_d6144_pitch8192", t1 - t0, 4 * T * Dp, onep,
+        {"y": (err(v["y_p"].float(), yr[0]), 5e-3), "same_bits_as_contiguous": (bool(torch.equal(bits(v["y_p"]), bits(v["y"]))), None)})
+    put("bwd_d6144_pitch8192", t2 - t1, 6 * T * Dp, onep,
+        {"dx": (err(v["dx_p"].float(), dxr[0]), 8e-3), "same_bits_as_contiguous": (bool(torch.equal(bits(v["dx_p"]), bits(v["dx"]))), None)})
     v = S["qkv"]
     Dq3 = v["x"].shape[2]
     t0 = _t.perf_counter()

@@ -114,6 +114,8 @@ class FwdOpts(ctypes.Structure):
         ("cu_seqlens", ctypes.c_void_p),
         ("nseq", ctypes.c_int64),
         ("status", ctypes.c_void_p),
+        ("y_sb", ctypes.c_int64),
+        ("y_st", ctypes.c_int64),
     ]
 
 
@@ -127,6 +129,8 @@ class BwdOpts(ctypes.Structure):
         ("cu_seqlens", ctypes.c_void_p),
         ("nseq", ctypes.c_int64),
         ("status", ctypes.c_void_p),
+        ("dx_sb", ctypes.c_int64),
+        ("dx_st", ctypes.c_int64),
     ]
 
 
@@ -771,6 +775,17 @@ def cconv_update_ex(x, state, state_indices, w, bias=None, *, cache_seqlens=None
     return y, status
 
 
+def _out_rows(t, name: str, like: torch.Tensor, packed: bool):
+    """(batch stride, row stride) of a caller-provided output of the general entry points: x's
+    shape, bf16, unit channel stride; (0, 0) when contiguous (the library's default layout)."""
+    _dev(t, name)
+    if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(like.shape) or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be bf16 of x's shape with unit channel stride")
+    if t.is_contiguous():
+        return 0, 0
+    return (0, t.stride(0)) if packed else (t.stride(0), t.stride(1))
+
+
 def _rows(t, name: str, packed: bool):
     """(batch stride, row stride) of a bf16 activation: [B, T, D], or [total, D] when packed."""
     if packed:
@@ -813,13 +828,12 @@ def cconv_fwd_ex(x, w, bias=None, *, activation="silu", residual=None, init_stat
     _state(final_state, "final_state", state_rows, D, W)
     if y is None:
         y = torch.empty(tuple(x.shape), dtype=torch.bfloat16, device=x.device)
-    elif y.dtype != torch.bfloat16 or tuple(y.shape) != tuple(x.shape) or not y.is_contiguous():
-        raise ValueError("y must be a contiguous bf16 tensor of x's shape")
+    ysb, yst = _out_rows(y, "y", x, packed)
     if packed and status is None:
         status = torch.empty(1, dtype=torch.int32, device=x.device)
     _out(status, "status", (1,), _I32)
     o = FwdOpts(ACTIVATIONS[activation], _ptr(residual), rsb, rst, _ptr(init_state), _ptr(final_state),
-                _ptr(cu_seqlens), state_rows if packed else 0, _ptr(status) if packed else None)
+                _ptr(cu_seqlens), state_rows if packed else 0, _ptr(status) if packed else None, ysb, yst)
     _check(lib().cconv_fwd_ex(_ptr(x), sb, st, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(y), B, T, D, W,
                               ctypes.byref(o), _stream(stream)), "cconv_fwd_ex")
     return y, final_state, status
@@ -859,7 +873,7 @@ def cconv_bwd_ex(x, dy, w, bias=None, *, activation="silu", init_state=None, d_i
         dw = torch.empty((D, W), dtype=dw_dtype or w.dtype, device=dev)
     if want_dbias and dbias is None:
         dbias = torch.empty((D,), dtype=torch.float32, device=dev)
-    _out(dx, "dx", x.shape, _BF)
+    dxsb, dxst = _out_rows(dx, "dx", x, packed)
     _out(dw, "dw", (D, W), _WT)
     _out(dbias, "dbias", (D,), _F32)
     if want_d_init_state and d_init_state is None:
@@ -873,7 +887,7 @@ def cconv_bwd_ex(x, dy, w, bias=None, *, activation="silu", init_state=None, d_i
         status = torch.empty(1, dtype=torch.int32, device=dev)
     _out(status, "status", (1,), _I32)
     o = BwdOpts(ACTIVATIONS[activation], _ptr(init_state), _ptr(d_init_state), _ptr(cu_seqlens),
-                state_rows if packed else 0, _ptr(status) if packed else None)
+                state_rows if packed else 0, _ptr(status) if packed else None, dxsb, dxst)
     _check(lib().cconv_bwd_ex(_ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(dx),
                               _ptr(dw), _wdt(dw, "dw"), _ptr(dbias), _ptr(workspace), ws_bytes, B, T, D, W,
                               ctypes.byref(o), _stream(stream)), "cconv_bwd_ex")

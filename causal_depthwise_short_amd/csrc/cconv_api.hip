@@ -162,6 +162,16 @@ cconv_status_t check_act(const void* p, int64_t sb, int64_t st, int64_t D, bool 
     return CCONV_OK;
 }
 
+// An output [B, T, D] with strides (sb, st, 1) given by the caller: the operand rules of
+// check_act, and rows that do not overlap (st >= D and, for B > 1, each batch row's rows end
+// before the next batch row starts).
+cconv_status_t check_out(const void* p, int64_t sb, int64_t st, int64_t B, int64_t T, int64_t D, bool narrow) {
+    const cconv_status_t s = check_act(p, sb, st, D, narrow);
+    if (s != CCONV_OK) return s;
+    if (B > 1 && T > 0 && static_cast<__int128>(sb) < static_cast<__int128>(T - 1) * st + D) return CCONV_ERR_BAD_STRIDE;
+    return CCONV_OK;
+}
+
 size_t bwd_workspace(const Plan& p, int64_t D, int W) {
     return static_cast<size_t>(p.partials) * static_cast<size_t>(W + 1) * static_cast<size_t>(D) * sizeof(float);
 }
@@ -187,6 +197,8 @@ struct Extra {
     bool linear = false;
     const void* r = nullptr;
     int64_t r_sb = 0, r_st = 0;
+    // the output's (y's, dx's) batch and row strides; o_st == 0: contiguous [B, T, D]
+    int64_t o_sb = 0, o_st = 0;
 };
 
 // Checks of the states and of the pool/packed metadata against the call's other operands.
@@ -258,11 +270,18 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     if (!narrow && D % 8 != 0) return CCONV_ERR_BAD_CONFIG;  // a vector plan needs whole 8-channel groups
     if ((st = check_params(w, w_dtype, bias, narrow)) != CCONV_OK) return st;
     if ((st = check_act(x, x_sb, x_st, D, narrow)) != CCONV_OK) return st;
-    if (!aligned(y, narrow ? 2 : 16)) return CCONV_ERR_MISALIGNED;
+    int64_t y_sb = T * D, y_st = D;  // contiguous unless the general entry point gives strides
+    if (ex.o_st != 0) {
+        y_st = ex.o_st;
+        y_sb = ex.mode == kPacked ? 0 : ex.o_sb;
+        if ((st = check_out(y, y_sb, y_st, B, T, D, narrow)) != CCONV_OK) return st;
+    } else if (!aligned(y, narrow ? 2 : 16)) {
+        return CCONV_ERR_MISALIGNED;
+    }
     if (!cconv::fwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
         return CCONV_ERR_BAD_CONFIG;
     if (ex.r && (st = check_act(ex.r, ex.r_sb, ex.r_st, D, narrow)) != CCONV_OK) return st;
-    const Span sy = span(y, extent3(B, T, D, T * D, D, 2));
+    const Span sy = span(y, extent3(B, T, D, y_sb, y_st, 2));
     const Span sx = span(x, extent3(B, T, D, x_sb, x_st, 2));
     const Span sw = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
     const Span sb = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
@@ -289,6 +308,8 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     a.w_f32 = (w_dtype == CCONV_F32);
     a.bias = bias;
     a.y = static_cast<uint16_t*>(y);
+    a.y_sb = y_sb;
+    a.y_st = y_st;
     a.h0 = static_cast<const uint16_t*>(ex.h0);
     a.hT = static_cast<uint16_t*>(ex.out);
     a.sidx = ex.sidx;
@@ -348,8 +369,15 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     if ((st = check_params(w, w_dtype, bias, narrow)) != CCONV_OK) return st;
     if ((st = check_act(x, x_sb, x_st, D, narrow)) != CCONV_OK) return st;
     if ((st = check_act(dy, dy_sb, dy_st, D, narrow)) != CCONV_OK) return st;
-    if (!aligned(dx, narrow ? 2 : 16) || !aligned(dw, narrow ? static_cast<uintptr_t>(esize(dw_dtype)) : 16) ||
-        (dbias && !aligned(dbias, narrow ? 4 : 16)))
+    int64_t dx_sb = T * D, dx_st = D;  // contiguous unless the general entry point gives strides
+    if (ex.o_st != 0 && main) {
+        dx_st = ex.o_st;
+        dx_sb = ex.mode == kPacked ? 0 : ex.o_sb;
+        if ((st = check_out(dx, dx_sb, dx_st, B, T, D, narrow)) != CCONV_OK) return st;
+    } else if (!aligned(dx, narrow ? 2 : 16)) {
+        return CCONV_ERR_MISALIGNED;
+    }
+    if (!aligned(dw, narrow ? static_cast<uintptr_t>(esize(dw_dtype)) : 16) || (dbias && !aligned(dbias, narrow ? 4 : 16)))
         return CCONV_ERR_MISALIGNED;
     if (!cconv::bwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
         return CCONV_ERR_BAD_CONFIG;
@@ -363,7 +391,7 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     const Span in_dy = span(dy, extent3(B, T, D, dy_sb, dy_st, 2));
     const Span in_w = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
     const Span in_b = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
-    const Span o_dx = span(dx, extent3(B, T, D, T * D, D, 2));
+    const Span o_dx = span(dx, extent3(B, T, D, dx_sb, dx_st, 2));
     const Span o_dw = span(dw, static_cast<__int128>(D) * W * esize(dw_dtype));
     const Span o_db = dbias ? span(dbias, static_cast<__int128>(D) * 4) : Span{0, 0};
     const Span o_ws = span(workspace, need);
@@ -398,6 +426,8 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
         a.w_f32 = (w_dtype == CCONV_F32);
         a.bias = bias;
         a.dx = static_cast<uint16_t*>(dx);
+        a.dx_sb = dx_sb;
+        a.dx_st = dx_st;
         a.partial = static_cast<float*>(workspace);
         a.h0 = static_cast<const uint16_t*>(ex.h0);
         a.dh0 = static_cast<uint16_t*>(ex.out);
@@ -594,6 +624,8 @@ cconv_status_t cconv_fwd_ex(const void* x, int64_t x_sb, int64_t x_st, const voi
         ex.r = o->residual;
         ex.r_sb = o->residual_sb;
         ex.r_st = o->residual_st;
+        ex.o_sb = o->y_sb;
+        ex.o_st = o->y_st;
         if (o->cu_seqlens) {
             if (B != 1) return CCONV_ERR_BAD_SHAPE;
             const cconv_status_t st =
@@ -617,6 +649,8 @@ cconv_status_t cconv_bwd_ex(const void* x, int64_t x_sb, int64_t x_st, const voi
     if (o) {
         if (o->activation != CCONV_ACT_SILU && o->activation != CCONV_ACT_NONE) return CCONV_ERR_BAD_CONFIG;
         ex.linear = (o->activation == CCONV_ACT_NONE);
+        ex.o_sb = o->dx_sb;
+        ex.o_st = o->dx_st;
         if (o->cu_seqlens) {
             if (B != 1) return CCONV_ERR_BAD_SHAPE;
             const cconv_status_t st =

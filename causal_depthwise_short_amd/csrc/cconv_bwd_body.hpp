@@ -306,7 +306,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         ring_at<VEC, W>(xr, t0, start, xb, xs, lo, a.h0, s, a.D, wt.d);
         for (auto& row : gr)
             for (float& g : row) g = 0.0f;
-        DxSink k{a.dx + wt.b * a.T * a.D, a.D, lo, t0, start, (t0 == start) ? a.dh0 : nullptr, s, a.D, wt.d};
+        DxSink k{a.dx + wt.b * a.dx_sb, a.dx_st, lo, t0, start, (t0 == start) ? a.dh0 : nullptr, s, a.D, wt.d};
 
         int64_t t = t0;
         for (;;) {

@@ -128,9 +128,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     // Row bases are wave-uniform; a lane adds its 32-bit byte offset to reach its channels.
     const uint32_t lo = static_cast<uint32_t>(wt.d) * 2u;  // byte offset of the lane's channels
     const uint16_t* __restrict__ xb = a.x + wt.b * a.x_sb;
-    uint16_t* __restrict__ yb = a.y + wt.b * a.T * a.D;
+    uint16_t* __restrict__ yb = a.y + wt.b * a.y_sb;
     const uint16_t* __restrict__ rb = a.r ? a.r + wt.b * a.r_sb : nullptr;
-    const int64_t xs = a.x_st, ys = a.D, rs = a.r_st;
+    const int64_t xs = a.x_st, ys = a.y_st, rs = a.r_st;
 
     float tap[W][VEC];
     load_taps<VEC, W>(a.w, a.w_f32, wt.d, tap);

@@ -52,6 +52,8 @@ struct FwdArgs {
     // residual added after the activation (kResidual): bf16 rows like x's, strides r_sb, r_st
     const uint16_t* r;
     int64_t r_sb, r_st;
+    // y's batch and row strides in elements (y_st >= D; y_sb ignored for packed batches)
+    int64_t y_sb, y_st;
     int64_t B, T, D;
     int64_t seg_rows, strip_groups, seg_groups;
     int ws;
@@ -66,6 +68,7 @@ struct BwdArgs {
     int w_f32;
     const float* bias;
     uint16_t* dx;
+    int64_t dx_sb, dx_st;  // dx's batch and row strides in elements (dx_st >= D)
     float* partial;      // [partials, W+1, D]
     const uint16_t* h0;  // [B, D, W-1] history before t = 0, or null (zeros)
     uint16_t* dh0;       // [B, D, W-1] gradient of the history out, or null

@@ -506,8 +506,10 @@ def test_option_structs_match_the_header(tmp_path):
         "  O(cconv_fwd_opts_t, activation); O(cconv_fwd_opts_t, residual); O(cconv_fwd_opts_t, residual_sb);\n"
         "  O(cconv_fwd_opts_t, residual_st); O(cconv_fwd_opts_t, init_state); O(cconv_fwd_opts_t, final_state);\n"
         "  O(cconv_fwd_opts_t, cu_seqlens); O(cconv_fwd_opts_t, nseq); O(cconv_fwd_opts_t, status);\n"
+        "  O(cconv_fwd_opts_t, y_sb); O(cconv_fwd_opts_t, y_st);\n"
         "  O(cconv_bwd_opts_t, activation); O(cconv_bwd_opts_t, init_state); O(cconv_bwd_opts_t, d_init_state);\n"
         "  O(cconv_bwd_opts_t, cu_seqlens); O(cconv_bwd_opts_t, nseq); O(cconv_bwd_opts_t, status);\n"
+        "  O(cconv_bwd_opts_t, dx_sb); O(cconv_bwd_opts_t, dx_st);\n"
         "  return 0;\n}\n"
     )
     exe = tmp_path / "layout"
@@ -524,10 +526,10 @@ RES = 0x70_0000_0000
 
 
 def fwd_ex(x=X, y=Y, B=2, T=64, D=512, W=4, act=1, res=RES, r_st=None, r_sb=None, h0=H0, hT=HT, cu=None, nseq=0,
-           status=None):
+           status=None, y_sb=0, y_st=0):
     r_st = D if r_st is None else r_st
     r_sb = T * r_st if r_sb is None else r_sb
-    o = cc.FwdOpts(act, res, r_sb, r_st, h0, hT, cu, nseq, status)
+    o = cc.FwdOpts(act, res, r_sb, r_st, h0, hT, cu, nseq, status, y_sb, y_st)
     return cc.lib().cconv_fwd_ex(x, T * D, D, WT, BF16, BIAS, y, B, T, D, W, ctypes.byref(o), None)
 
 
@@ -545,14 +547,21 @@ def fwd_ex(x=X, y=Y, B=2, T=64, D=512, W=4, act=1, res=RES, r_st=None, r_sb=None
         (dict(hT=RES), ALIAS),
         (dict(res=Y), ALIAS),
         (dict(W=5), SHAPE),
+        (dict(y_st=500, y_sb=64 * 512), STRIDE),  # row stride below D
+        (dict(y_st=516, y_sb=64 * 516), STRIDE),  # not a multiple of 8 on the vector path
+        (dict(y_st=1024, y_sb=1024 * 63), STRIDE),  # batch rows would overlap
+        (dict(y_st=1024, y_sb=1024 * 64 + 4), STRIDE),
+        (dict(y=Y + 8, y_st=1024, y_sb=1024 * 64), MISAL),
+        (dict(y_st=1024, y_sb=1024 * 64, res=RES + 2), MISAL),  # valid strides: the next check speaks
     ],
 )
 def test_fwd_ex_host_errors(kw, code):
     assert fwd_ex(**kw) == code
 
 
-def bwd_ex(act=1, dx=DX, h0=H0, dh=DH, cu=None, nseq=0, status=None, B=2, T=64, D=512, W=4, ws_bytes=1 << 40):
-    o = cc.BwdOpts(act, h0, dh, cu, nseq, status)
+def bwd_ex(act=1, dx=DX, h0=H0, dh=DH, cu=None, nseq=0, status=None, B=2, T=64, D=512, W=4, ws_bytes=1 << 40,
+           dx_sb=0, dx_st=0):
+    o = cc.BwdOpts(act, h0, dh, cu, nseq, status, dx_sb, dx_st)
     return cc.lib().cconv_bwd_ex(X, T * D, D, DY, T * D, D, WT, BF16, BIAS, dx, DW, BF16, DB, WSP, ws_bytes, B, T, D, W,
                                  ctypes.byref(o), None)
 
@@ -567,6 +576,10 @@ def bwd_ex(act=1, dx=DX, h0=H0, dh=DH, cu=None, nseq=0, status=None, B=2, T=64, 
         (dict(dx=H0 + 16), ALIAS),
         (dict(ws_bytes=16), WS),
         (dict(act=0, ws_bytes=16), WS),  # the variant without an activation exists for the default launch
+        (dict(dx_st=504, dx_sb=64 * 504), STRIDE),
+        (dict(dx_st=1020, dx_sb=64 * 1020), STRIDE),
+        (dict(dx_st=1024, dx_sb=1024 * 63), STRIDE),
+        (dict(dx_st=1024, dx_sb=1024 * 64, ws_bytes=16), WS),  # valid strides: the next check speaks
     ],
 )
 def test_bwd_ex_host_errors(kw, code):

@@ -132,3 +132,55 @@ def test_residual_guard_bands():
     torch.cuda.synchronize()
     assert canaries_intact(buf, lo, hi)
     assert_close(y.cpu(), oracle.fwd_epi(x, w, b, residual=r, act=False), TOL_FWD, "guarded y")
+
+
+@pytest.mark.parametrize("act", ["silu", None], ids=["silu", "linear"])
+@pytest.mark.parametrize("D,pitch,extra_rows", [(96, 128, 0), (1032, 2048, 5), (100, 131, 3)],
+                         ids=["vector", "vector_padded_batch", "element_granular"])
+def test_strided_outputs_equal_contiguous(D, pitch, extra_rows, act):
+    """y and dx written into wider rows (row pitch `pitch`, batch stride (T + extra_rows) * pitch)
+    equal the contiguous outputs bit for bit, dw and dbias too, and the padding around the D
+    channels of each row is never written."""
+    B, T, W = 2, 300, 4
+    x, dy, w, b, h0, _ = _case(B, T, D, W, seed=730 + D, history=True, residual=False)
+    gx, gdy, gw, gb, gh0 = _g(x), _g(dy), _g(w), _g(b), _g(h0)
+    y0, hT0, _ = cc.cconv_fwd_ex(gx, gw, gb, activation=act, init_state=gh0, want_final_state=True)
+    dx0, dw0, db0, dh0, _ = cc.cconv_bwd_ex(gx, gdy, gw, gb, activation=act, init_state=gh0, want_d_init_state=True)
+    canary = -12345
+    ybuf = torch.full((B, T + extra_rows, pitch), canary, dtype=torch.int16, device=DEV)
+    dxbuf = torch.full((B, T + extra_rows, pitch), canary, dtype=torch.int16, device=DEV)
+    y = ybuf.view(torch.bfloat16)[:, :T, :D]
+    dx = dxbuf.view(torch.bfloat16)[:, :T, :D]
+    assert not y.is_contiguous() and y.stride() == ((T + extra_rows) * pitch, pitch, 1)
+    _, hT, _ = cc.cconv_fwd_ex(gx, gw, gb, activation=act, init_state=gh0, want_final_state=True, y=y)
+    _, dw, db, dh, _ = cc.cconv_bwd_ex(gx, gdy, gw, gb, activation=act, init_state=gh0, want_d_init_state=True, dx=dx)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(y), bits(y0)) and torch.equal(bits(hT), bits(hT0))
+    assert torch.equal(bits(dx), bits(dx0)) and torch.equal(bits(dh), bits(dh0))
+    assert torch.equal(bits(dw), bits(dw0)) and torch.equal(db, db0)
+    for buf in (ybuf, dxbuf):
+        assert bool((buf[:, :, D:] == canary).all()) and bool((buf[:, T:, :] == canary).all()), "padding written"
+
+
+def test_strided_outputs_packed():
+    """A packed batch's y and dx written into wider rows equal the contiguous outputs."""
+    D, pitch, W = 264, 512, 4
+    lens = [5, 0, 300, 1, 77]
+    total = sum(lens)
+    inp = si.train_inputs(1, total, D, W, bias=True, seed=740)
+    x, dy = inp["x"][0].to(DEV), inp["dy"][0].to(DEV)
+    w, b = _g(inp["w"]), _g(inp["bias"])
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    y0, _, st0 = cc.cconv_fwd_ex(x, w, b, cu_seqlens=cu)
+    dx0, dw0, db0, _, _ = cc.cconv_bwd_ex(x, dy, w, b, cu_seqlens=cu)
+    canary = -4321
+    ybuf = torch.full((total, pitch), canary, dtype=torch.int16, device=DEV)
+    dxbuf = torch.full((total, pitch), canary, dtype=torch.int16, device=DEV)
+    y, dx = ybuf.view(torch.bfloat16)[:, :D], dxbuf.view(torch.bfloat16)[:, :D]
+    _, _, st = cc.cconv_fwd_ex(x, w, b, cu_seqlens=cu, y=y)
+    _, dw, db, _, st2 = cc.cconv_bwd_ex(x, dy, w, b, cu_seqlens=cu, dx=dx)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(st2.item()) == 0 and int(st0.item()) == 0
+    assert torch.equal(bits(y), bits(y0)) and torch.equal(bits(dx), bits(dx0))
+    assert torch.equal(bits(dw), bits(dw0)) and torch.equal(db, db0)
+    assert bool((ybuf[:, D:] == canary).all()) and bool((dxbuf[:, D:] == canary).all()), "padding written"
