@@ -797,7 +797,9 @@ def cconv_fwd_ex(x, w, bias=None, *, activation="silu", residual=None, init_stat
                  want_final_state=False, cu_seqlens=None, y=None, status=None, stream=None):
     """The general forward: y = act(conv(x) + bias) + residual, optionally from a history, with
     a final state, over a [B, T, D] batch or (cu_seqlens) a packed [total, D] batch. Returns
-    (y, final_state, status); status is None for fixed-length batches."""
+    (y, final_state, status); status is None for fixed-length batches. A caller-provided y may
+    be a view with wider rows (unit channel stride; e.g. D = 6144 channels of rows of 8192):
+    its strides are passed to the library."""
     packed = cu_seqlens is not None
     sb, st = _rows(x, "x", packed)
     if packed:
@@ -843,7 +845,8 @@ def cconv_bwd_ex(x, dy, w, bias=None, *, activation="silu", init_state=None, d_i
                  want_d_init_state=False, cu_seqlens=None, dx=None, dw=None, dbias=None, want_dbias=True,
                  dw_dtype=None, workspace=None, status=None, stream=None):
     """The general backward (see cconv_fwd_ex; a residual's gradient is dy itself). Returns
-    (dx, dw, dbias, d_init_state, status)."""
+    (dx, dw, dbias, d_init_state, status). A caller-provided dx may be a view with wider rows,
+    as cconv_fwd_ex's y."""
     packed = cu_seqlens is not None
     sb, st = _rows(x, "x", packed)
     dsb, dst = _rows(dy, "dy", packed)
