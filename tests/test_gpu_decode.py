@@ -157,3 +157,31 @@ def test_decode_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(bits(y), bits(y_e)) and torch.equal(bits(g["state"]), bits(st_e)), f"replay {rep}"
         assert int(status.item()) == CCONV_OK
+
+
+def test_fused_qkv_decode_one_launch_equals_three():
+    """One decode update over a fused q|k|v projection row ([N, Dq + Dk + Dv], one state of
+    Dq + Dk + Dv channels, the three taps and biases concatenated) equals three updates on the
+    channel slices (x row stride Dq + Dk + Dv, three states): y and the new states bit for
+    bit, with the same slots for all three."""
+    split, W = (256, 256, 512), 4
+    Dt = sum(split)
+    inp = si.decode_inputs(64, 96, Dt, W, bias=True, seed=91)
+    g = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    st_all = g["state"].clone()
+    y_all, s_all = cc.cconv_update(g["x"], st_all, g["state_indices"], g["w"], g["bias"])
+    ys, states, lo = [], [], 0
+    for Dj in split:
+        sl = slice(lo, lo + Dj)
+        lo += Dj
+        st = g["state"][:, sl, :].contiguous()
+        yj, sj = cc.cconv_update(g["x"][:, sl], st, g["state_indices"], g["w"][sl].contiguous(), g["bias"][sl].contiguous())
+        torch.cuda.synchronize()
+        assert int(sj.item()) == CCONV_OK
+        ys.append(yj)
+        states.append(st)
+    torch.cuda.synchronize()
+    assert int(s_all.item()) == CCONV_OK
+    assert torch.equal(bits(y_all), bits(torch.cat(ys, dim=1)))
+    assert torch.equal(bits(st_all), bits(torch.cat(states, dim=1)))
+    check_update(inp, y_all.cpu(), st_all.cpu(), int(s_all.item()), inp["state_indices"].numpy(), "fused q|k|v decode")
