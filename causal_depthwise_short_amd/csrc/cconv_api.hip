@@ -79,12 +79,15 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 //     leaves the extra waves sharing a SIMD with another, and the kernel waits for them: about
 //     twice the time. Segments never drop below kMinSeg rows (the W-1 rows each segment
 //     re-reads stay a small share).
-//   * Cache hints: non-temporal loads and stores when the output rows start on 128-byte cache
-//     lines (2D a multiple of 128); otherwise plain ones, so that the L2 merges the lines two
-//     neighbouring strips share (at D = 4104: 241 vs 264 us forward, 325 vs 389 us backward).
-//     The narrow path's rows never start on a line. Packed batches and the epilogue variants
+//   * Cache hints: non-temporal loads and stores when every streamed row starts on a 128-byte
+//     cache line (for contiguous operands, 2D a multiple of 128); otherwise plain ones, so
+//     that the L2 merges the lines two neighbouring strips share (at D = 4104: 241 vs 264 us
+//     forward, 325 vs 389 us backward). The narrow path always runs plain ones. Packed batches and the epilogue variants
 //     keep the streaming hints (their kernels are compiled for those only).
-cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, bool streaming_only = false) {
+//   `line_rows` (-1: from D alone, as for contiguous operands on 128-byte aligned bases) says
+//   whether every streamed row of the call starts on a 128-byte line.
+cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, bool streaming_only = false,
+                              int line_rows_in = -1) {
     (void)W;
     cconv_config_t c;
     const bool narrow = (D % 8 != 0);
@@ -92,7 +95,7 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
     c.rows_per_group = 16;
     c.waves_per_block = 1;
     c.strips_per_block = 1;
-    const bool line_rows = (2 * D) % 128 == 0;
+    const bool line_rows = line_rows_in < 0 ? (2 * D) % 128 == 0 : line_rows_in != 0;
     if (narrow)
         c.options = cconv::kNarrowOptions;
     else if (line_rows || streaming_only)
@@ -133,6 +136,11 @@ bool make_plan(const cconv_config_t& c, int64_t B, int64_t T, int64_t D, Plan* p
     p->blocks = static_cast<int64_t>(blocks);
     p->partials = B * p->seg_groups;
     return true;
+}
+
+// Whether every row of a [B, T, D] operand with strides (sb, st, 1) starts on a 128-byte line.
+bool on_lines(const void* p, int64_t sb, int64_t st) {
+    return aligned(p, 128) && (2 * st) % 128 == 0 && (2 * sb) % 128 == 0;
 }
 
 // Checks shared by the forward and backward before a plan exists: sizes, width, tap dtype.
@@ -264,7 +272,11 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     if (st != CCONV_OK) return st;
     const int epi = (ex.linear ? cconv::kLinear : 0) | (ex.r ? cconv::kResidual : 0);
     // packed batches and the epilogue variants are compiled for the streaming hints only
-    const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W, ex.mode == kPacked || epi != 0);
+    // the default plan's cache hints follow where the call's rows actually start
+    const bool lines = on_lines(x, x_sb, x_st) &&
+                       (ex.o_st ? on_lines(y, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_lines(y, T * D, D)) &&
+                       (!ex.r || on_lines(ex.r, ex.r_sb, ex.r_st));
+    const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W, ex.mode == kPacked || epi != 0, lines);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
     const bool narrow = (c.vec == 1);
     if (!narrow && D % 8 != 0) return CCONV_ERR_BAD_CONFIG;  // a vector plan needs whole 8-channel groups
@@ -362,7 +374,11 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     const int epi = ex.linear ? cconv::kLinear : 0;
     // packed batches and the variant without an activation are compiled for the streaming
     // hints only
-    const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0);
+    // the default plan's cache hints follow where the call's rows actually start (the plan's
+    // segments, and so the partials a finishing stage reads, do not depend on them)
+    const bool lines = on_lines(x, x_sb, x_st) && on_lines(dy, dy_sb, dy_st) &&
+                       (ex.o_st && main ? on_lines(dx, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_lines(dx, T * D, D));
+    const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0, lines);
     if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
     const bool narrow = (c.vec == 1);
     if (!narrow && D % 8 != 0) return CCONV_ERR_BAD_CONFIG;  // a vector plan needs whole 8-channel groups
