@@ -82,10 +82,11 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 //   * Cache hints: non-temporal loads and stores when every streamed row starts on a 128-byte
 //     cache line (for contiguous operands, 2D a multiple of 128); otherwise plain ones, so
 //     that the L2 merges the lines two neighbouring strips share (at D = 4104: 241 vs 264 us
-//     forward, 325 vs 389 us backward). The narrow path always runs plain ones. Packed batches and the epilogue variants
-//     keep the streaming hints (their kernels are compiled for those only).
-//   `line_rows` (-1: from D alone, as for contiguous operands on 128-byte aligned bases) says
-//   whether every streamed row of the call starts on a 128-byte line.
+//     forward, 325 vs 389 us backward). The narrow path always runs plain ones. Packed
+//     batches and the epilogue variants keep the streaming hints (their kernels are compiled
+//     for those only).
+//   `line_rows_in` (-1: from D alone, as for contiguous operands on 128-byte aligned bases)
+//   says whether every streamed row of the call starts on a 128-byte line.
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, bool streaming_only = false,
                               int line_rows_in = -1) {
     (void)W;
