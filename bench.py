@@ -216,10 +216,12 @@ def run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo
                  lambda: cc.cconv_bwd_ex(x, dy, w, b, activation=None, dx=dxo, dw=dwo, dbias=dbo, workspace=ws),
                  copy2, {}, cap_lin_b))
 
-    # D other than the headline's: 4100 takes the element-granular path (one channel per lane),
-    # 4104 the vector path with 17 channel strips whose rows do not start on cache lines
+    # D other than the headline's: 4098 takes the element-granular path (one channel per lane),
+    # 4100 = 4 (mod 8) 4-channel lanes on 8-byte aligned rows, 4104 the vector path with 17
+    # channel strips whose rows do not start on cache lines
     big = []
-    for Bn, Dn, tag, what in ((B, 4100, "any_d", "D not a multiple of 8 (one channel per lane)"),
+    for Bn, Dn, tag, what in ((B, 4098, "any_d", "D not a multiple of 4 (one channel per lane)"),
+                              (B, 4100, "d4100", "D = 4100 (4 channels per lane, 8-byte aligned rows)"),
                               (B, 4104, "d4104", "D = 4104 (vector path, rows not on 128-byte lines)"),
                               (2 * B, D // 2, "b16_d2048", "the pages' production call shape (B = 16, D = 2048)")):
         nin = si.train_inputs_device(Bn, T, Dn, W, bias=True, seed=s.seed + 5, device=dev)
@@ -493,7 +495,7 @@ def oracle_variants(oracle, np, torch, S, err):
     dxr = oracle.bwd_epi(x1, dy1, w, b, act=False, precision="f32")[0]
     t = _t.perf_counter() - t0
     put("bwd_linear", t, 6 * T * D, one, {"dx": (err(S["bwd_linear"]["dx"].float(), dxr[0]), 8e-3)})
-    for tag in ("any_d", "d4104", "b16_d2048"):
+    for tag in ("any_d", "d4100", "d4104", "b16_d2048"):
         v = S[tag]
         Dn = v["x"].shape[2]
         t0 = _t.perf_counter()

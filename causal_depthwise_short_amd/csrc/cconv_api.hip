@@ -71,8 +71,9 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 // whole register file (the "solo" kernels), which is what lets deep row groups stay in flight
 // without scratch spills.
 //   * Shape: 4 channels per lane and 16-row groups (the backward loads 16 rows of x and 16 of
-//     dy per group: 16 KiB in flight per wave). D not a multiple of 8: one channel per lane,
-//     16-row groups, the general kernel.
+//     dy per group: 16 KiB in flight per wave), also for D = 4 (mod 8), whose rows are
+//     8-byte aligned (at D = 4100 this halves the one-channel plan's time). D not a multiple
+//     of 4: one channel per lane, 16-row groups, the general kernel.
 //   * Segments: each batch row is cut into as many segments as the wave slots allow (1024
 //     solo waves, one per SIMD; kNarrowTargetWaves for the narrow path) and no more. A grid
 //     slightly larger than the slots (17 strips x 8 segments x 8 rows = 1088 waves at D = 4160)
@@ -87,11 +88,15 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 //     for those only).
 //   `line_rows_in` (-1: from D alone, as for contiguous operands on 128-byte aligned bases)
 //   says whether every streamed row of the call starts on a 128-byte line.
+//   `quads` says whether the call's activations meet the 4-channel rule (8-byte aligned,
+//   strides multiples of 4). When D = 4 (mod 8) and they do not, the plan runs one channel
+//   per lane with the 4-channel plan's segments: the dw/dbias partials (their count, so the
+//   workspace and what a finishing stage reads) stay those of the shape, whatever the layout.
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, bool streaming_only = false,
-                              int line_rows_in = -1) {
+                              int line_rows_in = -1, bool quads = true) {
     (void)W;
     cconv_config_t c;
-    const bool narrow = (D % 8 != 0);
+    const bool narrow = (D % 4 != 0);
     c.vec = narrow ? 1 : 4;
     c.rows_per_group = 16;
     c.waves_per_block = 1;
@@ -117,6 +122,10 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
     ts = std::max(kMinSeg, ((ts + align - 1) / align) * align);
     const int64_t tcap = ((t + align - 1) / align) * align;
     c.seg_rows = std::min(ts, tcap);
+    if (!narrow && D % 8 != 0 && !quads) {
+        c.vec = 1;
+        c.options = cconv::kNarrowOptions;
+    }
     return c;
 }
 
@@ -144,6 +153,9 @@ bool on_lines(const void* p, int64_t sb, int64_t st) {
     return aligned(p, 128) && (2 * st) % 128 == 0 && (2 * sb) % 128 == 0;
 }
 
+// Whether a [B, T, D] operand meets the 4-channel rule: 8-byte aligned, strides multiples of 4.
+bool on_quads(const void* p, int64_t sb, int64_t st) { return aligned(p, 8) && sb % 4 == 0 && st % 4 == 0; }
+
 // Checks shared by the forward and backward before a plan exists: sizes, width, tap dtype.
 cconv_status_t check_train_common(cconv_dtype_t w_dtype, int64_t B, int64_t T, int64_t D, int W) {
     if (B < 0 || T < 0 || D < 0 || B > kMaxDim || T > kMaxDim || D > kMaxDim) return CCONV_ERR_BAD_SHAPE;
@@ -153,29 +165,37 @@ cconv_status_t check_train_common(cconv_dtype_t w_dtype, int64_t B, int64_t T, i
     return CCONV_OK;
 }
 
-// Alignment of the taps and bias: 16 bytes on the vector path; the element size on the
-// element-granular one (narrow: one channel per lane, for D not a multiple of 8).
-cconv_status_t check_params(const void* w, cconv_dtype_t w_dtype, const float* bias, bool narrow) {
-    const uintptr_t wa = narrow ? static_cast<uintptr_t>(esize(w_dtype)) : 16, ba = narrow ? 4 : 16;
+// The channel granule of a plan: the operand rules follow from it. 8 for a vector plan over
+// whole 8-channel groups (16-byte aligned rows, strides multiples of 8, 16-byte aligned taps,
+// bias, dw and states); 4 for a 4-channel plan with D = 4 (mod 8) (8-byte aligned rows, strides
+// multiples of 4; the taps, bias, dw and states are read and written per element, so element
+// alignment); 1 for the element-granular plan (one channel per lane: any stride, element
+// alignment everywhere).
+int granule(const cconv_config_t& c, int64_t D) { return c.vec == 1 ? 1 : (D % 8 == 0 ? 8 : 4); }
+
+// Alignment of the taps and bias: 16 bytes for granule 8; the element size otherwise.
+cconv_status_t check_params(const void* w, cconv_dtype_t w_dtype, const float* bias, int gran) {
+    const bool wide = (gran == 8);
+    const uintptr_t wa = wide ? 16 : static_cast<uintptr_t>(esize(w_dtype)), ba = wide ? 16 : 4;
     if (!aligned(w, wa) || (bias && !aligned(bias, ba))) return CCONV_ERR_MISALIGNED;
     return CCONV_OK;
 }
 
-// A bf16 [B, T, D] operand with strides (sb, st, 1). Vector path: strides multiples of 8 and
-// 16-byte alignment (whole 16- or 8-byte rows per lane). Narrow path: any strides, 2-byte
-// alignment.
-cconv_status_t check_act(const void* p, int64_t sb, int64_t st, int64_t D, bool narrow = false) {
+// A bf16 [B, T, D] operand with strides (sb, st, 1): strides multiples of the plan's granule
+// and 2 * granule bytes of alignment (granule 8: 16 bytes; 4: 8 bytes, whole 8-byte rows per
+// lane; 1: any strides, 2-byte alignment).
+cconv_status_t check_act(const void* p, int64_t sb, int64_t st, int64_t D, int gran) {
     if (sb < 0 || st < D || sb > kMaxDim || st > kMaxDim) return CCONV_ERR_BAD_STRIDE;
-    if (!narrow && (sb % 8 != 0 || st % 8 != 0)) return CCONV_ERR_BAD_STRIDE;
-    if (!aligned(p, narrow ? 2 : 16)) return CCONV_ERR_MISALIGNED;
+    if (sb % gran != 0 || st % gran != 0) return CCONV_ERR_BAD_STRIDE;
+    if (!aligned(p, static_cast<uintptr_t>(2 * gran))) return CCONV_ERR_MISALIGNED;
     return CCONV_OK;
 }
 
 // An output [B, T, D] with strides (sb, st, 1) given by the caller: the operand rules of
 // check_act, and rows that do not overlap (st >= D and, for B > 1, each batch row's rows end
 // before the next batch row starts).
-cconv_status_t check_out(const void* p, int64_t sb, int64_t st, int64_t B, int64_t T, int64_t D, bool narrow) {
-    const cconv_status_t s = check_act(p, sb, st, D, narrow);
+cconv_status_t check_out(const void* p, int64_t sb, int64_t st, int64_t B, int64_t T, int64_t D, int gran) {
+    const cconv_status_t s = check_act(p, sb, st, D, gran);
     if (s != CCONV_OK) return s;
     if (B > 1 && T > 0 && static_cast<__int128>(sb) < static_cast<__int128>(T - 1) * st + D) return CCONV_ERR_BAD_STRIDE;
     return CCONV_OK;
@@ -277,23 +297,27 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     const bool lines = on_lines(x, x_sb, x_st) &&
                        (ex.o_st ? on_lines(y, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_lines(y, T * D, D)) &&
                        (!ex.r || on_lines(ex.r, ex.r_sb, ex.r_st));
-    const cconv_config_t c = cfg ? *cfg : default_config(false, B, T, D, W, ex.mode == kPacked || epi != 0, lines);
+    const bool quads = on_quads(x, x_sb, x_st) &&
+                       (ex.o_st ? on_quads(y, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_quads(y, T * D, D)) &&
+                       (!ex.r || on_quads(ex.r, ex.r_sb, ex.r_st));
+    const cconv_config_t c =
+        cfg ? *cfg : default_config(false, B, T, D, W, ex.mode == kPacked || epi != 0, lines, quads);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
-    const bool narrow = (c.vec == 1);
-    if (!narrow && D % 8 != 0) return CCONV_ERR_BAD_CONFIG;  // a vector plan needs whole 8-channel groups
-    if ((st = check_params(w, w_dtype, bias, narrow)) != CCONV_OK) return st;
-    if ((st = check_act(x, x_sb, x_st, D, narrow)) != CCONV_OK) return st;
+    if (D % c.vec != 0) return CCONV_ERR_BAD_CONFIG;  // a plan needs whole groups of its lane width
+    const int gran = granule(c, D);
+    if ((st = check_params(w, w_dtype, bias, gran)) != CCONV_OK) return st;
+    if ((st = check_act(x, x_sb, x_st, D, gran)) != CCONV_OK) return st;
     int64_t y_sb = T * D, y_st = D;  // contiguous unless the general entry point gives strides
     if (ex.o_st != 0) {
         y_st = ex.o_st;
         y_sb = ex.mode == kPacked ? 0 : ex.o_sb;
-        if ((st = check_out(y, y_sb, y_st, B, T, D, narrow)) != CCONV_OK) return st;
-    } else if (!aligned(y, narrow ? 2 : 16)) {
+        if ((st = check_out(y, y_sb, y_st, B, T, D, gran)) != CCONV_OK) return st;
+    } else if (!aligned(y, static_cast<uintptr_t>(2 * gran))) {
         return CCONV_ERR_MISALIGNED;
     }
     if (!cconv::fwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
         return CCONV_ERR_BAD_CONFIG;
-    if (ex.r && (st = check_act(ex.r, ex.r_sb, ex.r_st, D, narrow)) != CCONV_OK) return st;
+    if (ex.r && (st = check_act(ex.r, ex.r_sb, ex.r_st, D, gran)) != CCONV_OK) return st;
     const Span sy = span(y, extent3(B, T, D, y_sb, y_st, 2));
     const Span sx = span(x, extent3(B, T, D, x_sb, x_st, 2));
     const Span sw = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
@@ -304,7 +328,7 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     if (W == 1) ex.h0 = ex.out = nullptr;
     const Span ins[4] = {sx, sw, sb, sr};
     Span sh0;
-    if ((st = check_extra(ex, B, D, W, true, ins, 4, &sy, 1, &sh0, narrow ? 2 : 16)) != CCONV_OK) return st;
+    if ((st = check_extra(ex, B, D, W, true, ins, 4, &sy, 1, &sh0, gran == 8 ? 16 : 2)) != CCONV_OK) return st;
     Plan p;
     if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
     p.options |= epi;
@@ -379,22 +403,25 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     // segments, and so the partials a finishing stage reads, do not depend on them)
     const bool lines = on_lines(x, x_sb, x_st) && on_lines(dy, dy_sb, dy_st) &&
                        (ex.o_st && main ? on_lines(dx, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_lines(dx, T * D, D));
-    const cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0, lines);
+    const bool quads = on_quads(x, x_sb, x_st) && on_quads(dy, dy_sb, dy_st) &&
+                       (ex.o_st && main ? on_quads(dx, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_quads(dx, T * D, D));
+    const cconv_config_t c =
+        cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0, lines, quads);
     if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
-    const bool narrow = (c.vec == 1);
-    if (!narrow && D % 8 != 0) return CCONV_ERR_BAD_CONFIG;  // a vector plan needs whole 8-channel groups
-    if ((st = check_params(w, w_dtype, bias, narrow)) != CCONV_OK) return st;
-    if ((st = check_act(x, x_sb, x_st, D, narrow)) != CCONV_OK) return st;
-    if ((st = check_act(dy, dy_sb, dy_st, D, narrow)) != CCONV_OK) return st;
+    if (D % c.vec != 0) return CCONV_ERR_BAD_CONFIG;  // a plan needs whole groups of its lane width
+    const int gran = granule(c, D);
+    if ((st = check_params(w, w_dtype, bias, gran)) != CCONV_OK) return st;
+    if ((st = check_act(x, x_sb, x_st, D, gran)) != CCONV_OK) return st;
+    if ((st = check_act(dy, dy_sb, dy_st, D, gran)) != CCONV_OK) return st;
     int64_t dx_sb = T * D, dx_st = D;  // contiguous unless the general entry point gives strides
     if (ex.o_st != 0 && main) {
         dx_st = ex.o_st;
         dx_sb = ex.mode == kPacked ? 0 : ex.o_sb;
-        if ((st = check_out(dx, dx_sb, dx_st, B, T, D, narrow)) != CCONV_OK) return st;
-    } else if (!aligned(dx, narrow ? 2 : 16)) {
+        if ((st = check_out(dx, dx_sb, dx_st, B, T, D, gran)) != CCONV_OK) return st;
+    } else if (!aligned(dx, static_cast<uintptr_t>(2 * gran))) {
         return CCONV_ERR_MISALIGNED;
     }
-    if (!aligned(dw, narrow ? static_cast<uintptr_t>(esize(dw_dtype)) : 16) || (dbias && !aligned(dbias, narrow ? 4 : 16)))
+    if (!aligned(dw, gran == 8 ? 16 : static_cast<uintptr_t>(esize(dw_dtype))) || (dbias && !aligned(dbias, gran == 8 ? 16 : 4)))
         return CCONV_ERR_MISALIGNED;
     if (!cconv::bwd_launch_exists(c.vec, c.rows_per_group, c.options | epi, ex.mode == kPacked))
         return CCONV_ERR_BAD_CONFIG;
@@ -422,7 +449,7 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
             if (overlap(outs[i], outs[j])) return CCONV_ERR_ALIASING;
     }
     Span sh0;
-    if ((st = check_extra(ex, B, D, W, false, ins, 4, outs, 4, &sh0, narrow ? 2 : 16)) != CCONV_OK) return st;
+    if ((st = check_extra(ex, B, D, W, false, ins, 4, outs, 4, &sh0, gran == 8 ? 16 : 2)) != CCONV_OK) return st;
     if (workspace_bytes < need) return CCONV_ERR_WORKSPACE;
     // a per-sequence history gradient needs at least one token
     if (ex.out && ex.mode != kPacked && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;

@@ -30,14 +30,23 @@
  *  - Alignment and D. When D is a multiple of 8 (the vector path: each lane moves whole 16- or
  *    8-byte groups of channels), every tensor pointer must be 16-byte aligned, except
  *    state_indices, cache_seqlens, cu_seqlens and status (4 bytes) [PR #797 review thread:
- *    alignment contract], and every row and batch stride a multiple of 8 elements. Any other
- *    D (the element-granular path [strip.py's masked loads handle any D]: one channel per
- *    lane) needs only element alignment (2 bytes for bf16, 4 for fp32) and strides >= D; the
- *    decode update then takes compact rows (x_ld == D) or a row stride that is a multiple of
- *    8 [the decode PR's row-stride contract]. The element-granular path runs with plain
- *    loads and stores only (options 0; its default configuration: 1 channel per lane, 16-row
- *    groups, one-wave blocks); with D % 8 != 0 a configuration with vec != 1 is
- *    CCONV_ERR_BAD_CONFIG. The alignments stated below are those of the vector path.
+ *    alignment contract], and every row and batch stride a multiple of 8 elements. The
+ *    training calls (forward and backward, every variant) also run 4 channels per lane when
+ *    D = 4 (mod 8), their default then: the bf16 activations (x, dy, y, dx, residual) 8-byte
+ *    aligned with strides that are multiples of 4, the taps, bias, dw, dbias and states with
+ *    element alignment (they are read and written per element). Any other D (the
+ *    element-granular path [strip.py's masked loads handle any D]: one channel per lane)
+ *    needs only element alignment (2 bytes for bf16, 4 for fp32) and strides >= D; an
+ *    explicit configuration with vec = 1 takes that path for any D. When D = 4 (mod 8) and
+ *    the activations miss the 8-byte rule, the default plan runs one channel per lane too,
+ *    with the segments (so the dw/dbias partials and the workspace) of the 4-channel plan;
+ *    an explicit vec = 4 configuration is checked against the rule. The decode update runs 8
+ *    channels per lane when D is a multiple of 8 and one otherwise, taking compact rows
+ *    (x_ld == D) or a row stride that is a multiple of 8 [the decode PR's row-stride
+ *    contract]. The element-granular path runs with plain loads and stores only (options 0;
+ *    its default configuration: 1 channel per lane, 16-row groups, one-wave blocks); a
+ *    configuration whose vec does not divide D is CCONV_ERR_BAD_CONFIG. The alignments
+ *    stated below are those of the vector path with D a multiple of 8.
  *  - Errors fail closed. A problem visible on the host returns its code before anything is
  *    enqueued, leaving every output untouched: NULL required pointer, negative size, W
  *    outside [1, 4] (the pages' kernels are written for at most 4 taps, strip.py module
@@ -369,7 +378,7 @@ typedef struct {
 
 /*
  * The configuration cconv_fwd (which = 0) or cconv_bwd (which = 1) uses for this shape: 4
- * channels per lane (1 when D % 8 != 0), 16-row groups, one-wave blocks, each batch row cut
+ * channels per lane (1 when D % 4 != 0), 16-row groups, one-wave blocks, each batch row cut
  * into as many segments as the wave slots hold (1024 waves, one per SIMD; 4096 on the
  * element-granular path); non-temporal hints (options 11) when 2D is a multiple of 128, plain
  * loads and stores (options 8; 0 on the element-granular path) otherwise. Packed batches and

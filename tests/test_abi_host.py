@@ -244,7 +244,7 @@ def test_default_plan_fits_the_wave_slots(which):
     for B, T, D in [(8, 8192, 4096), (8, 8192, 4160), (8, 8192, 4104), (16, 8192, 2048), (3, 1000, 2000),
                     (8, 8192, 4100), (1, 65536, 4096), (2, 100003, 520), (64, 4096, 4096)]:
         c = cc.cconv_default_config(which, B, T, D, 4)
-        narrow = D % 8 != 0
+        narrow = D % 4 != 0
         slots = 4096 if narrow else 1024
         strips = -(-D // (64 * c.vec))
         waves = B * strips * -(-T // c.seg_rows)
@@ -587,9 +587,9 @@ def test_bwd_ex_host_errors(kw, code):
 
 
 def test_odd_channel_counts_need_the_narrow_launch():
-    """With D not a multiple of 8 only the one-channel-per-lane plan is accepted."""
+    """With D not a multiple of 4 only the one-channel-per-lane plan is accepted."""
     L = cc.lib()
-    D, T = 500, 64
+    D, T = 502, 64
     vec4 = cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
     assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, Y, 2, T, D, 4, ctypes.byref(vec4), None) == CONFIG
     narrow = cc.cconv_default_config("fwd", 2, T, D, 4)
@@ -600,3 +600,50 @@ def test_odd_channel_counts_need_the_narrow_launch():
     assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(solo), None) == CONFIG
     nb = cc.cconv_default_config("bwd", 2, T, D, 4)
     assert nb.vec == 1 and nb.options == 0 and nb.waves_per_block == 1
+
+
+def test_four_channel_plans_for_d_4_mod_8():
+    """D = 4 (mod 8): the default plan runs 4 channels per lane, its activations need 8-byte
+    alignment and strides that are multiples of 4, its taps, bias, dw and states only element
+    alignment; 8 channels per lane is refused, and an explicit one-channel plan still takes any
+    layout. A call that passes every check stops at the aliasing check (y on x), so nothing is
+    launched."""
+    L = cc.lib()
+    D, T, B = 500, 64, 2
+    for which in ("fwd", "bwd"):
+        c = cc.cconv_default_config(which, B, T, D, 4)
+        assert c.vec == 4 and c.options == 8 and c.rows_per_group == 16
+    # accepted: 8-byte aligned activations, strides a multiple of 4, taps and bias off 16 bytes
+    assert fwd(D=D, y=X) == ALIAS
+    assert fwd(D=D, x=X + 8, y=X + 8) == ALIAS
+    assert fwd(D=D, x_st=504, y=X) == ALIAS
+    assert fwd(D=D, w=WT + 2, bias=BIAS + 4, y=X) == ALIAS
+    assert fwd(D=D, w=WT + 4, w_dt=F32, y=X) == ALIAS
+    # activations off the rule (4-byte aligned rows, strides off the 4-element granule): the
+    # default plan runs one channel per lane instead, so these are accepted too
+    assert fwd(D=D, x=X + 4, y=X + 4) == ALIAS
+    assert fwd(D=D, x_st=502, y=X) == ALIAS
+    assert fwd(D=D, x_sb=T * D + 2, y=X) == ALIAS
+    assert fwd(D=D, y=Y + 1) == MISAL
+    assert fwd(D=D, w=WT + 1) == MISAL
+    # the backward: dw and dbias per element; dx, x, dy on the 8-byte rule or the fallback
+    assert bwd(D=D, dx=X) == ALIAS
+    assert bwd(D=D, dw=DW + 2, db=DB + 4, dx=X) == ALIAS
+    assert bwd(D=D, dx=X + 4) == ALIAS
+    assert bwd(D=D, dy_st=502, dx=X) == ALIAS
+    assert bwd(D=D, dx=DX + 1) == MISAL
+    # the fallback keeps the shape's partials: the workspace is the 4-channel plan's
+    need = L.cconv_bwd_workspace_bytes(B, T, D, 4)
+    assert need > 0
+    assert bwd(D=D, dx=DX + 4, dy=DY + 4, x=X + 4, ws_bytes=need - 1) == WS
+    # D a multiple of 8 keeps the 16-byte rule
+    assert fwd(D=512, x=X + 8) == MISAL
+    assert fwd(D=512, x_st=516) == STRIDE
+    # explicit plans: 8 channels per lane needs D % 8 == 0; one channel per lane takes any layout
+    vec8 = cc.Config(vec=8, rows_per_group=16, waves_per_block=1, options=8, seg_rows=64)
+    vec4 = cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=8, seg_rows=64)
+    one = cc.Config(vec=1, rows_per_group=16, waves_per_block=1, options=0, seg_rows=64)
+    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, B, T, D, 4, ctypes.byref(vec8), None) == CONFIG
+    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, B, T, D, 4, ctypes.byref(vec4), None) == ALIAS
+    assert L.cconv_fwd_config(X + 4, T * D, D, WT, BF16, BIAS, Y, B, T, D, 4, ctypes.byref(vec4), None) == MISAL
+    assert L.cconv_fwd_config(X + 2, T * 502, 502, WT, BF16, BIAS, X + 2, B, T, D, 4, ctypes.byref(one), None) == ALIAS

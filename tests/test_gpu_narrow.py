@@ -1,6 +1,7 @@
-"""GPU parity of the element-granular path (D not a multiple of 8: one channel per lane) for
-every entry point, against the oracle, through the C ABI. Tolerances in parity.py; states bit
-for bit.
+"""GPU parity for channel counts that are not multiples of 8, for every entry point, against
+the oracle, through the C ABI: the element-granular path (one channel per lane, D not a
+multiple of 4) and, for the training calls, the 4-channel lanes that D = 4 (mod 8) takes
+(D = 100 and 4100 below). Tolerances in parity.py; states bit for bit.
 """
 
 from __future__ import annotations
@@ -109,9 +110,12 @@ def test_narrow_launch_invariance(i):
     assert_close(dw.cpu(), ref_dw.cpu(), 1e-4, "narrow dw across launches")
 
 
-def test_narrow_packed_and_epilogue():
+@pytest.mark.parametrize("D", [77, 100])
+def test_narrow_packed_and_epilogue(D):
+    """Packed batches and the epilogue variants at D = 77 (one channel per lane) and D = 100
+    (4 channels per lane)."""
     lens = [100, 0, 1, 3, 250]
-    D, W = 77, 4
+    W = 4
     total = sum(lens)
     inp = si.train_inputs(1, total, D, W, bias=True, seed=850)
     x, dy, w, b = inp["x"][0], inp["dy"][0], inp["w"], inp["bias"]
@@ -167,8 +171,11 @@ def test_narrow_decode(D, ld_pad):
     assert_close(y4.cpu(), yr4, TOL_FWD, f"circular decode D{D}")
 
 
-def test_narrow_pool():
-    B, T, D, W, S = 3, 90, 45, 4, 7
+@pytest.mark.parametrize("D", [45, 60])
+def test_narrow_pool(D):
+    """The prefill into a decode pool at D = 45 (one channel per lane) and D = 60 (4 channels
+    per lane)."""
+    B, T, W, S = 3, 90, 4, 7
     inp = si.train_inputs(B, T, D, W, bias=True, seed=870)
     state = torch.randn(S, D, W - 1, generator=torch.Generator().manual_seed(871)).to(torch.bfloat16)
     idx = torch.tensor([5, -1, 2], dtype=torch.int32)
@@ -180,3 +187,38 @@ def test_narrow_pool():
     assert ok and int(status.item()) == 0
     assert np.array_equal(st.cpu().float().numpy(), sr)
     assert_close(y.cpu(), yr, TOL_FWD, "pool y")
+
+
+@pytest.mark.parametrize("D", [4, 1028])
+@pytest.mark.parametrize("W", [1, 4])
+def test_four_channel_lanes_d_4_mod_8(D, W):
+    """D = 4 (mod 8) runs 4 channels per lane: x and dy as 8-byte aligned column slices of wider
+    tensors (row stride D + 8), y and dx into guarded buffers, a ragged last strip and segment;
+    against the oracle, and y and dx equal to the one-channel plan's bit for bit."""
+    B, T = 2, 1000
+    assert cc.cconv_default_config("fwd", B, T, D, W).vec == 4
+    assert cc.cconv_default_config("bwd", B, T, D, W).vec == 4
+    big = si.train_inputs(B, T, D + 8, W, bias=True, seed=860 + D + W)
+    x = big["x"][:, :, 4:4 + D]
+    dy = big["dy"][:, :, 4:4 + D]
+    w, b = big["w"][:D].contiguous(), big["bias"][:D].contiguous()
+    xd, dyd = _g(big["x"])[:, :, 4:4 + D], _g(big["dy"])[:, :, 4:4 + D]
+    wd, bd = _g(w), _g(b)
+    y, ybuf, ylo, yhi = guarded((B, T, D), torch.bfloat16, DEV)
+    dx, xbuf, xlo, xhi = guarded((B, T, D), torch.bfloat16, DEV)
+    cc.cconv_fwd(xd, wd, bd, y=y)
+    _, dw, db = cc.cconv_bwd(xd, dyd, wd, bd, dx=dx, dw_dtype=torch.float32)
+    one = cc.Config(vec=1, rows_per_group=16, waves_per_block=1, options=0, seg_rows=64)
+    y1 = cc.cconv_fwd(xd, wd, bd, config=one)
+    dx1, dw1, _ = cc.cconv_bwd(xd, dyd, wd, bd, config=one, dw_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert canaries_intact(ybuf, ylo, yhi) and canaries_intact(xbuf, xlo, xhi)
+    _, yr = oracle.fwd(x.contiguous(), w, b)
+    dxr, dwr, dbr = oracle.bwd(x.contiguous(), dy.contiguous(), w, b)
+    assert_close(y.cpu(), yr, TOL_FWD, f"D{D} W{W} y")
+    assert_close(dx.cpu(), dxr, TOL_BWD, f"D{D} W{W} dx")
+    assert_close(dw.cpu(), dwr, TOL_BWD, f"D{D} W{W} dw")
+    assert_close(db.cpu(), dbr, TOL_BWD, f"D{D} W{W} dbias")
+    assert torch.equal(bits(y), bits(y1)) and torch.equal(bits(dx), bits(dx1))
+    # fp32 partial sums grouped per launch: rounding-order differences only
+    assert_close(dw.cpu(), dw1.cpu(), 1e-4, f"D{D} W{W} dw across lane widths")
