@@ -379,8 +379,8 @@ typedef struct {
 /*
  * The configuration cconv_fwd (which = 0) or cconv_bwd (which = 1) uses for this shape: 4
  * channels per lane (1 when D % 4 != 0), 16-row groups, one-wave blocks, each batch row cut
- * into as many segments as the wave slots hold (1024 waves, one per SIMD; 3072 for the forward
- * and 2048 for the backward on the
+ * into as many segments as the wave slots hold (1024 waves, one per SIMD; 768 for a forward
+ * whose rows miss the 128-byte lines; 3072 for the forward and 2048 for the backward on the
  * element-granular path); non-temporal hints (options 11) when 2D is a multiple of 128, plain
  * loads and stores (options 8; 0 on the element-granular path) otherwise. Packed batches and
  * the epilogue variants use the same plan with the streaming hints.

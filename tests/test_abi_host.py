@@ -246,7 +246,9 @@ def test_default_plan_fits_the_wave_slots(which):
                     (8, 8192, 4100), (1, 65536, 4096), (2, 100003, 520), (64, 4096, 4096)]:
         c = cc.cconv_default_config(which, B, T, D, 4)
         narrow = D % 4 != 0
-        slots = ((3072 if which in ("fwd", 0) else 2048) if narrow else 1024)
+        fwd = which in ("fwd", 0)
+        off_lines = (2 * D) % 128 != 0
+        slots = (3072 if fwd else 2048) if narrow else (768 if fwd and off_lines else 1024)
         strips = -(-D // (64 * c.vec))
         waves = B * strips * -(-T // c.seg_rows)
         if B * strips <= slots:
