@@ -37,6 +37,9 @@ __all__ = [
     "cconv_bwd_finish",
     "cconv_update",
     "cconv_update_ex",
+    "cconv_update_config",
+    "UpdateConfig",
+    "cconv_default_update_config",
     "cconv_default_config",
     "cconv_status_string",
     "cconv_version",
@@ -81,6 +84,29 @@ class Config(ctypes.Structure):
 
     def __repr__(self):
         return "Config(" + ", ".join(f"{k}={v}" for k, v in self.as_dict().items()) + ")"
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class UpdateConfig(ctypes.Structure):
+    """cconv_update_config_t: vec, block_threads, rows_per_thread, options, rows_per_block."""
+
+    _fields_ = [
+        ("vec", ctypes.c_int),
+        ("block_threads", ctypes.c_int),
+        ("rows_per_thread", ctypes.c_int),
+        ("options", ctypes.c_int),
+        ("rows_per_block", ctypes.c_int64),
+    ]
+
+    def __init__(self, *args, **kw):
+        kw.setdefault("rows_per_thread", 1)
+        kw.setdefault("vec", 8)
+        super().__init__(*args, **kw)
+
+    def __repr__(self):
+        return "UpdateConfig(" + ", ".join(f"{k}={v}" for k, v in self.as_dict().items()) + ")"
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -182,6 +208,11 @@ def _declare(L):
     L.cconv_update_ex.restype = i32
     L.cconv_update.argtypes = [p, i64, p, i64, p, p, i32, p, p, i64, i64, i32, p, p]
     L.cconv_update.restype = i32
+    L.cconv_update_config.argtypes = [p, i64, p, i64, i32, p, p, p, i32, p, p, i64, i64, i32, p,
+                                      ctypes.POINTER(UpdateConfig), p]
+    L.cconv_update_config.restype = i32
+    L.cconv_default_update_config.argtypes = [i64, i64, ctypes.POINTER(UpdateConfig)]
+    L.cconv_default_update_config.restype = i32
     L.cconv_default_config.argtypes = [i32, i64, i64, i64, i32, ctypes.POINTER(Config)]
     L.cconv_default_config.restype = i32
     L.cconv_status_string.argtypes = [i32]
@@ -773,6 +804,56 @@ def cconv_update_ex(x, state, state_indices, w, bias=None, *, cache_seqlens=None
         "cconv_update_ex",
     )
     return y, status
+
+
+def cconv_update_config(x, state, state_indices, w, bias=None, *, config, cache_seqlens=None, y=None, status=None,
+                        stream=None):
+    """cconv_update_ex with an explicit launch configuration (an UpdateConfig). Returns (y, status);
+    state (bf16 [S, D, L]) is updated in place."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be bf16 [N, D] with unit channel stride")
+    N, D = x.shape
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    _dev(state, "state")
+    if state.dtype != torch.bfloat16 or state.dim() != 3 or state.shape[1] != D or not state.is_contiguous():
+        raise ValueError("state must be a contiguous bf16 [S, D, L] tensor")
+    S, L = state.shape[0], state.shape[2]
+    for t, name in ((state_indices, "state_indices"), (cache_seqlens, "cache_seqlens")):
+        if t is not None:
+            _dev(t, name)
+            if t.dtype != torch.int32 or t.shape != (N,) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 [N] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    if not isinstance(config, UpdateConfig):
+        raise TypeError("config must be an UpdateConfig")
+    if y is None:
+        y = torch.empty((N, D), dtype=torch.bfloat16, device=x.device)
+    _out(y, "y", (N, D), _BF)
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=x.device)
+    _out(status, "status", (1,), _I32)
+    _check(
+        lib().cconv_update_config(
+            _ptr(x), x.stride(0) if N > 0 else D, _ptr(state), S, L, _ptr(state_indices), _ptr(cache_seqlens),
+            _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(y), N, D, W, _ptr(status), ctypes.byref(config), _stream(stream),
+        ),
+        "cconv_update_config",
+    )
+    return y, status
+
+
+def cconv_default_update_config(N: int, D: int) -> UpdateConfig:
+    """The launch configuration cconv_update / cconv_update_ex use for N rows of D channels."""
+    c = UpdateConfig()
+    _check(lib().cconv_default_update_config(N, D, ctypes.byref(c)), "cconv_default_update_config")
+    return c
 
 
 def _out_rows(t, name: str, like: torch.Tensor, packed: bool):

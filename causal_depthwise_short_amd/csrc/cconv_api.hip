@@ -18,7 +18,8 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 40;        // any one size or stride
 constexpr int64_t kMaxDecodeRows = int64_t(1) << 24;  // N
 constexpr int64_t kMaxChannels = int64_t(1) << 30;    // D: lane channel offsets are 32-bit
-constexpr int64_t kMaxIndexedSlots = int64_t(1) << 19;  // S with state_indices (LDS bit set)
+// S with state_indices: the slot check's S-bit set and its verdict word fill at most 64 KB of LDS
+constexpr int64_t kMaxIndexedSlots = (int64_t(1) << 19) - 32;
 constexpr int64_t kMaxSequences = int64_t(1) << 24;     // packed sequences per call
 constexpr int64_t kTargetWaves = 1024;  // wave slots of the solo kernels: one per SIMD (256 CUs x 4 SIMDs)
 // wave slots of the narrow path (one channel per lane): three waves per SIMD for the forward,
@@ -36,6 +37,17 @@ constexpr int kFwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
 constexpr int kBwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
 constexpr int64_t kMinSeg = 64;         // shorter segments re-read too large a share of rows
 constexpr int64_t kUpdateTargetBlocks = 1024;
+// D of the decode update: its buffer ranges (a slot's [D, L] state run, fp32 taps [D, W]) stay
+// below 2^31 bytes
+constexpr int64_t kMaxDecodeChannels = int64_t(1) << 26;
+// Decode launch (kernel-trace sweeps of block size x rows per thread x channels per thread x
+// store hints at N = 256, D = 4096, W = 4, from HBM: 256-thread blocks, two rows per thread,
+// 8 channels per thread and non-temporal stores took 5.3 us per call, the other 33 shapes
+// 5.3-8.0 us; non-temporal loads and 4-channel threads did not help)
+constexpr int64_t kUpdateThreads = 256;
+constexpr int kUpdateOptions = cconv::kUpdNtStore;
+constexpr int64_t kUpdateRowsPerThread = 2;
+constexpr int kUpdateVec8 = 8;  // channels per thread when D % 8 == 0
 
 struct Span {
     uintptr_t lo, hi;
@@ -548,31 +560,63 @@ cconv_status_t bwd_varlen_impl(const void* x, int64_t x_st, const void* dy, int6
                     workspace_bytes, 1, total, D, W, cfg, stream, ex);
 }
 
+// The decode update's launch rule: a thread per `vec` channels (8 when D % 8 == 0, 4 when
+// D % 4 == 0, else 1); blocks of up to kUpdateThreads threads across a row's channel groups;
+// rows per block chosen so that the grid holds about kUpdateTargetBlocks blocks (each block
+// pays the O(N) slot check, so their number is kept near a constant).
+cconv_update_config_t update_config_for(int64_t N, int64_t D, int vec) {
+    cconv_update_config_t c;
+    c.vec = vec;
+    const int64_t dv = D / c.vec;
+    c.block_threads = static_cast<int>(std::min<int64_t>(kUpdateThreads, std::max<int64_t>(64, ((dv + 63) / 64) * 64)));
+    const int64_t grid_x = std::max<int64_t>(1, (dv + c.block_threads - 1) / c.block_threads);
+    c.rows_per_block = std::max<int64_t>(1, (std::max<int64_t>(N, 1) * grid_x + kUpdateTargetBlocks - 1) / kUpdateTargetBlocks);
+    c.rows_per_thread = 1;
+    c.options = 0;
+    if (c.vec > 1) {
+        c.options = kUpdateOptions;
+        c.rows_per_thread = static_cast<int>(kUpdateRowsPerThread);
+        c.rows_per_block = ((c.rows_per_block + c.rows_per_thread - 1) / c.rows_per_thread) * c.rows_per_thread;
+        c.block_threads = std::min(c.block_threads, cconv::update_max_threads(c.rows_per_thread));
+    }
+    return c;
+}
+
+cconv_update_config_t default_update_config(int64_t N, int64_t D) {
+    return update_config_for(N, D, (D % 8 == 0) ? kUpdateVec8 : (D % 4 == 0 ? 4 : 1));
+}
+
 // The decode update: state of L entries (L = W-1 or W), shift or (with cache_seqlens)
 // circular addressing.
 cconv_status_t update_impl(const void* x, int64_t x_ld, void* state, int64_t S, int L, const int32_t* state_indices,
                            const int32_t* cache_seqlens, const void* w, cconv_dtype_t w_dtype, const float* bias,
-                           void* y, int64_t N, int64_t D, int W, int32_t* status, cconv_stream_t stream) {
+                           void* y, int64_t N, int64_t D, int W, int32_t* status, const cconv_update_config_t* cfg,
+                           cconv_stream_t stream) {
     if (N < 0 || S < 0 || D < 0 || W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
     if (L != W - 1 && L != W) return CCONV_ERR_BAD_SHAPE;
     if (cache_seqlens && L < 1) return CCONV_ERR_BAD_SHAPE;  // a circular state needs entries
     if (((!x || !y) && N > 0 && D > 0) || (!w && D > 0) || (!state && S > 0 && D > 0 && L > 0))
         return CCONV_ERR_NULL_POINTER;
-    if (N < 0 || S < 0 || D < 0 || N > kMaxDecodeRows || S > kMaxDim || D > kMaxChannels) return CCONV_ERR_BAD_SHAPE;
-    if (W < 1 || W > 4) return CCONV_ERR_BAD_SHAPE;
+    // what only the device can check is reported through the status word, so a call that has
+    // such entries needs one
+    if ((state_indices || cache_seqlens) && !status && N > 0) return CCONV_ERR_NULL_POINTER;
+    if (N > kMaxDecodeRows || S > kMaxDim || D > kMaxDecodeChannels) return CCONV_ERR_BAD_SHAPE;
     if (state_indices && S > kMaxIndexedSlots) return CCONV_ERR_BAD_SHAPE;
     if (!state_indices && N > S) return CCONV_ERR_BAD_SHAPE;
     if (!dtype_ok(w_dtype)) return CCONV_ERR_UNSUPPORTED_DTYPE;
-    // Rows: D a multiple of 8 with a row stride that is one too takes the 8-channel path; any
-    // other D takes the one-channel path, with compact rows (x_ld == D) or a stride that is a
-    // multiple of 8 [the decode PR's row-stride contract].
-    const bool narrow = (D % 8 != 0);
-    if (x_ld < D || x_ld > kMaxDim || (x_ld % 8 != 0 && !(narrow && x_ld == D))) return CCONV_ERR_BAD_STRIDE;
-    const uintptr_t va = narrow ? 2 : 16;
-    if (!aligned(x, va) || !aligned(state, va) || !aligned(w, narrow ? static_cast<uintptr_t>(esize(w_dtype)) : 16) ||
-        !aligned(y, va) || (bias && !aligned(bias, narrow ? 4 : 16)) || (state_indices && !aligned(state_indices, 4)) ||
+    // Rows: D a multiple of 8 needs a row stride that is one too and 16-byte aligned operands;
+    // any other D takes compact rows (x_ld == D) or a stride that is a multiple of 8 [the
+    // decode PR's row-stride contract], with element alignment.
+    const bool wide = (D % 8 == 0);
+    if (x_ld < D || x_ld > kMaxDim || (x_ld % 8 != 0 && !(!wide && x_ld == D))) return CCONV_ERR_BAD_STRIDE;
+    const uintptr_t va = wide ? 16 : 2;
+    if (!aligned(x, va) || !aligned(state, va) || !aligned(w, wide ? 16 : static_cast<uintptr_t>(esize(w_dtype))) ||
+        !aligned(y, va) || (bias && !aligned(bias, wide ? 16 : 4)) || (state_indices && !aligned(state_indices, 4)) ||
         (cache_seqlens && !aligned(cache_seqlens, 4)) || (status && !aligned(status, 4)))
         return CCONV_ERR_MISALIGNED;
+    // 4 channels per thread: 8-byte rows and state runs, taps and bias in 8/16-byte chunks
+    const bool quad_ok = D % 4 == 0 && x_ld % 4 == 0 && aligned(x, 8) && aligned(y, 8) && aligned(state, 8) &&
+                         aligned(w, w_dtype == CCONV_F32 ? 16 : 8) && (!bias || aligned(bias, 16));
     const Span in_x = span(x, N == 0 || D == 0 ? 0 : (static_cast<__int128>(N - 1) * x_ld + D) * 2);
     const Span in_w = span(w, static_cast<__int128>(D) * W * esize(w_dtype));
     const Span in_b = bias ? span(bias, static_cast<__int128>(D) * 4) : Span{0, 0};
@@ -589,18 +633,31 @@ cconv_status_t update_impl(const void* x, int64_t x_ld, void* state, int64_t S, 
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], outs[j])) return CCONV_ERR_ALIASING;
     }
+    cconv_update_config_t c;
+    if (cfg) {
+        c = *cfg;
+        if (c.vec == 4 && D % 4 == 0 && x_ld % 4 == 0 && !quad_ok) return CCONV_ERR_MISALIGNED;
+    } else {
+        c = default_update_config(N, D);
+        if (c.vec == 4 && !quad_ok) c = update_config_for(N, D, 1);  // operands off the 4-channel rule
+    }
+    if (c.block_threads < 64 || c.block_threads > 1024 || c.block_threads % 64 != 0 || c.rows_per_block < 1 ||
+        c.rows_per_block > kMaxDecodeRows || c.options < 0 || c.options > 1 ||
+        (c.rows_per_thread != 1 && c.rows_per_thread != 2) || c.block_threads > cconv::update_max_threads(c.rows_per_thread) ||
+        (c.vec != 1 && c.vec != 4 && c.vec != 8) || D % c.vec != 0 || (c.vec == 4 && x_ld % 4 != 0) ||
+        (c.vec == 1 && (c.options != 0 || c.rows_per_thread != 1)))
+        return CCONV_ERR_BAD_CONFIG;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (N == 0 || D == 0) {
         if (status) return cconv::launch_status(status, CCONV_OK, s) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
         return CCONV_OK;
     }
-    const int64_t dv = narrow ? D : D / 8;  // channel groups per row (one thread each)
-    const int threads = static_cast<int>(std::min<int64_t>(256, ((dv + 63) / 64) * 64));
-    const int64_t grid_x = (dv + threads - 1) / threads;
-    const int64_t rpb = std::max<int64_t>(1, (N * grid_x + kUpdateTargetBlocks - 1) / kUpdateTargetBlocks);
-    const int64_t grid_y = (N + rpb - 1) / rpb;
-    if (grid_x > INT32_MAX || grid_y > 65535) return CCONV_ERR_BAD_SHAPE;
-    const size_t lds = state_indices ? static_cast<size_t>((S + 31) / 32) * 4 : 0;
+    const int64_t dv = D / c.vec;  // channel groups per row (one thread each)
+    const int64_t grid_x = (dv + c.block_threads - 1) / c.block_threads;
+    const int64_t grid_y = (N + c.rows_per_block - 1) / c.rows_per_block;
+    if (grid_x > INT32_MAX || grid_y > 65535) return CCONV_ERR_BAD_CONFIG;
+    // the slot check's bit set and verdict word (a verdict word alone for cache_seqlens only)
+    const size_t lds = state_indices ? static_cast<size_t>((S + 31) / 32 + 1) * 4 : (cache_seqlens ? 4 : 0);
     cconv::UpdateArgs a;
     a.x = static_cast<const uint16_t*>(x);
     a.x_ld = x_ld;
@@ -614,10 +671,12 @@ cconv_status_t update_impl(const void* x, int64_t x_ld, void* state, int64_t S, 
     a.y = static_cast<uint16_t*>(y);
     a.N = N;
     a.D = D;
-    a.rows_per_block = rpb;
+    a.rows_per_block = c.rows_per_block;
     a.status = status;
-    return cconv::launch_update(W, L, narrow, a, threads, grid_x, grid_y, lds, s) == hipSuccess ? CCONV_OK
-                                                                                                : CCONV_ERR_LAUNCH;
+    return cconv::launch_update(W, L, c.vec, c.options, c.rows_per_thread, a, c.block_threads, grid_x, grid_y, lds, s) ==
+                   hipSuccess
+               ? CCONV_OK
+               : CCONV_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -821,7 +880,8 @@ cconv_status_t cconv_default_config(int which, int64_t B, int64_t T, int64_t D, 
 cconv_status_t cconv_update(const void* x, int64_t x_ld, void* state, int64_t S, const int32_t* state_indices,
                             const void* w, cconv_dtype_t w_dtype, const float* bias, void* y, int64_t N, int64_t D,
                             int W, int32_t* status, cconv_stream_t stream) {
-    return update_impl(x, x_ld, state, S, W - 1, state_indices, nullptr, w, w_dtype, bias, y, N, D, W, status, stream);
+    return update_impl(x, x_ld, state, S, W - 1, state_indices, nullptr, w, w_dtype, bias, y, N, D, W, status, nullptr,
+                       stream);
 }
 
 cconv_status_t cconv_update_ex(const void* x, int64_t x_ld, void* state, int64_t S, int L,
@@ -829,7 +889,23 @@ cconv_status_t cconv_update_ex(const void* x, int64_t x_ld, void* state, int64_t
                                cconv_dtype_t w_dtype, const float* bias, void* y, int64_t N, int64_t D, int W,
                                int32_t* status, cconv_stream_t stream) {
     return update_impl(x, x_ld, state, S, L, state_indices, cache_seqlens, w, w_dtype, bias, y, N, D, W, status,
+                       nullptr, stream);
+}
+
+cconv_status_t cconv_update_config(const void* x, int64_t x_ld, void* state, int64_t S, int L,
+                                   const int32_t* state_indices, const int32_t* cache_seqlens, const void* w,
+                                   cconv_dtype_t w_dtype, const float* bias, void* y, int64_t N, int64_t D, int W,
+                                   int32_t* status, const cconv_update_config_t* cfg, cconv_stream_t stream) {
+    if (!cfg) return CCONV_ERR_NULL_POINTER;
+    return update_impl(x, x_ld, state, S, L, state_indices, cache_seqlens, w, w_dtype, bias, y, N, D, W, status, cfg,
                        stream);
+}
+
+cconv_status_t cconv_default_update_config(int64_t N, int64_t D, cconv_update_config_t* out) {
+    if (!out) return CCONV_ERR_NULL_POINTER;
+    if (N < 0 || D < 0 || N > kMaxDecodeRows || D > kMaxDecodeChannels) return CCONV_ERR_BAD_SHAPE;
+    *out = default_update_config(N, D);
+    return CCONV_OK;
 }
 
 const char* cconv_status_string(cconv_status_t status) {

@@ -118,6 +118,8 @@ constexpr int kNarrowOptions = 0;
 // residual added to the forward's output after the activation.
 constexpr int kLinear = 16;
 constexpr int kResidual = 32;
+// Option bit of the decode update: non-temporal stores of y and the state.
+constexpr int kUpdNtStore = 1;
 
 // The wave's index in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
@@ -318,16 +320,38 @@ __device__ __forceinline__ void store_state_bf16(uint16_t* st, int64_t b, int64_
     st[(b * D + d) * L + j] = static_cast<uint16_t>(pack_bf16x2(val, 0.0f) & 0xffffu);
 }
 
+// A workgroup barrier that orders LDS accesses only: the waves' global loads in flight are not
+// waited for (a plain __syncthreads() would also wait for every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // The decode slot rule, checked by one block: true (in every thread of the block) when some
-// idx[n] lies outside [-1, S) or a non-negative slot appears twice. `seen` is an LDS bit set of
-// (S + 31) / 32 words. O(N + S/32) per block, no device trap.
-__device__ __forceinline__ bool block_slots_bad(const int32_t* idx, int64_t N, int64_t S, uint32_t* seen) {
-    const int64_t words = (S + 31) / 32;
-    for (int64_t i = threadIdx.x; i < words; i += blockDim.x) seen[i] = 0u;
-    __syncthreads();
+// idx[n] lies outside [-1, S), a non-negative slot appears twice, or (cs non-null) some cs[n]
+// is negative. idx may be null (no slots to check). `seen` is an LDS bit set of (S + 31) / 32
+// words followed by one verdict word ((S + 31) / 32 + 1 words with idx, 1 without).
+// O(N + S/32) per block, no device trap; the two barriers order LDS only, so global loads
+// the block issued before the check stay in flight through it.
+//
+// `first` holds the thread's entries of row threadIdx.x (v = -1, c = 0 past N), loaded by the
+// caller before its other loads: vector loads complete in issue order, so waiting for an
+// entry issued after them would also wait for them. Rows threadIdx.x + k * blockDim.x (N
+// larger than the block) are loaded here.
+struct SlotEntry {
+    int32_t v, c;
+};
+
+__device__ __forceinline__ bool block_slots_bad(const int32_t* __restrict__ idx, const int32_t* __restrict__ cs,
+                                                int64_t N, int64_t S, uint32_t* seen, SlotEntry first) {
+    const int64_t words = idx ? (S + 31) / 32 : 0;
+    const int64_t i0 = threadIdx.x;
+    for (int64_t i = i0; i <= words; i += blockDim.x) seen[i] = 0u;
+    lds_barrier();
     bool bad = false;
-    for (int64_t i = threadIdx.x; i < N; i += blockDim.x) {
-        const int32_t v = idx[i];
+    auto take = [&](int32_t v, int32_t c) {
+        if (c < 0) bad = true;
         if (v < -1 || static_cast<int64_t>(v) >= S) {
             bad = true;
         } else if (v >= 0) {
@@ -335,8 +359,12 @@ __device__ __forceinline__ bool block_slots_bad(const int32_t* idx, int64_t N, i
             const uint32_t old = atomicOr(&seen[v >> 5], bit);
             if (old & bit) bad = true;
         }
-    }
-    return __syncthreads_or(bad);
+    };
+    take(first.v, first.c);
+    for (int64_t i = i0 + blockDim.x; i < N; i += blockDim.x) take(idx ? idx[i] : -1, cs ? cs[i] : 0);
+    if (bad) seen[words] = 1u;  // every writer stores the same value
+    lds_barrier();
+    return seen[words] != 0u;
 }
 
 // Where a wave works. The block id (XCD-remapped) selects a (strip group, segment group,

@@ -109,6 +109,11 @@ struct UpdateArgs {
     int32_t* status;
 };
 
+// Largest block of the decode update when a thread carries R rows at once: each row in flight
+// holds up to 16 registers (x and the state run), so R = 2 needs more than the 128 VGPRs a
+// lane of a 1024-thread block may use.
+constexpr int update_max_threads(int R) { return R >= 2 ? 512 : 1024; }
+
 // Launchers: enqueue on `stream`, return hipGetLastError() after the launch.
 hipError_t launch_fwd(const Plan& p, int W, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t stream);
@@ -120,8 +125,8 @@ hipError_t launch_bwd_extra(const Plan& p, int W, const BwdArgs& a, hipStream_t 
 bool fwd_launch_exists(int vec, int group, int options, bool packed);
 bool bwd_launch_exists(int vec, int group, int options, bool packed);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
-hipError_t launch_update(int W, int L, bool narrow, const UpdateArgs& a, int block_threads, int64_t grid_x,
-                         int64_t grid_y, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_update(int W, int L, int vec, int options, int rows_per_thread, const UpdateArgs& a,
+                         int block_threads, int64_t grid_x, int64_t grid_y, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_status(int32_t* status, int32_t value, hipStream_t stream);
 hipError_t launch_slots(const int32_t* idx, int64_t N, int64_t S, int32_t* status, hipStream_t stream);
 // Packed batches: the offset check (one block writes *status), then, when it passes, the

@@ -306,12 +306,15 @@ cconv_status_t cconv_bwd_finish(const void* workspace, size_t workspace_bytes, v
  *           writes no state and whose y row is 0. NULL means slot n for row n (needs N <= S).
  *   w, bias as in cconv_fwd; y bf16 [N, D] contiguous, written.
  *   z = bias + sum_{j<W-1} w[d, j] * state[s, d, j] + w[d, W-1] * x[n, d];  y = silu(z).
- *   status  device int32 or NULL: receives CCONV_OK or CCONV_ERR_INDEX.
+ *   status  device int32: receives CCONV_OK or CCONV_ERR_INDEX. Required (non-NULL) when
+ *           state_indices is given and N > 0, since only the device sees the verdict
+ *           (CCONV_ERR_NULL_POINTER otherwise); may be NULL without indices.
  * Index validation happens on the device, inside the one kernel: an index outside [-1, S),
  * or a non-negative index that appears twice, makes the whole call invalid. Then no state
  * row is written (bitwise unchanged), y is unspecified, and *status = CCONV_ERR_INDEX.
- * No device trap is raised, so the process stays usable. Limits: N <= 2^24; with indices,
- * S <= 2^19 (the duplicate check keeps an S-bit set in LDS).
+ * No device trap is raised, so the process stays usable. Limits: N <= 2^24, D <= 2^26; with
+ * indices, S <= 2^19 - 32 (the duplicate check keeps an S-bit set and a verdict word in 64 KB
+ * of LDS).
  */
 cconv_status_t cconv_update(const void* x, int64_t x_ld, void* state, int64_t S,
                             const int32_t* state_indices, const void* w, cconv_dtype_t w_dtype,
@@ -334,12 +337,50 @@ cconv_status_t cconv_update(const void* x, int64_t x_ld, void* state, int64_t S,
  *                  cache_seqlens. A state written by a prefill (oldest first) is a circular
  *                  state with c = 0 (mod L). Needs L >= 1.
  * Everything else as cconv_update; a negative cache_seqlens entry fails the call like an
- * invalid index (CCONV_ERR_INDEX in *status, nothing written).
+ * invalid index (CCONV_ERR_INDEX in *status, nothing written), so status is required when
+ * cache_seqlens is given too.
  */
 cconv_status_t cconv_update_ex(const void* x, int64_t x_ld, void* state, int64_t S, int L,
                                const int32_t* state_indices, const int32_t* cache_seqlens, const void* w,
                                cconv_dtype_t w_dtype, const float* bias, void* y, int64_t N, int64_t D, int W,
                                int32_t* status, cconv_stream_t stream);
+
+/*
+ * Launch configuration of the decode update, for sweeps and for tests of invariance to the
+ * launch shape: y and the state do not depend on it (bit for bit).
+ *   vec              channels per thread: 8 (D % 8 == 0), 4 (D % 4 == 0, row stride a
+ *                    multiple of 4, x, y and the state 8-byte aligned, w 8-byte aligned (16
+ *                    for fp32 taps), bias 16-byte aligned; CCONV_ERR_MISALIGNED otherwise)
+ *                    or 1 (any D)
+ *   block_threads    threads per block, a multiple of 64 in [64, 1024]; a thread owns vec
+ *                    channels of every row its block walks
+ *   rows_per_thread  rows a thread carries at once, their loads in flight together and the
+ *                    taps loaded once for them: 1 or 2 (1 when vec = 1); blocks of at most
+ *                    512 threads for 2 (registers)
+ *   options          bit 0: non-temporal stores of y and the state (0 when vec = 1)
+ *   rows_per_block   rows of N each block walks (>= 1; the grid's row dimension,
+ *                    ceil(N / rows_per_block), must stay <= 65535)
+ * An invalid configuration is CCONV_ERR_BAD_CONFIG.
+ */
+typedef struct {
+    int vec;
+    int block_threads;
+    int rows_per_thread;
+    int options;
+    int64_t rows_per_block;
+} cconv_update_config_t;
+
+/* The configuration cconv_update and cconv_update_ex use for N rows of D channels (with
+ * operands that meet the vec rule above; a call whose operands miss the 4-channel rule runs
+ * one channel per thread). */
+cconv_status_t cconv_default_update_config(int64_t N, int64_t D, cconv_update_config_t* out);
+
+/* cconv_update_ex with an explicit launch configuration (cfg must not be NULL). */
+cconv_status_t cconv_update_config(const void* x, int64_t x_ld, void* state, int64_t S, int L,
+                                   const int32_t* state_indices, const int32_t* cache_seqlens,
+                                   const void* w, cconv_dtype_t w_dtype, const float* bias, void* y,
+                                   int64_t N, int64_t D, int W, int32_t* status,
+                                   const cconv_update_config_t* cfg, cconv_stream_t stream);
 
 /* A short English description of a status code (static storage). */
 const char* cconv_status_string(cconv_status_t status);

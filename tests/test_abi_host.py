@@ -200,7 +200,7 @@ def upd(x=X, x_ld=None, state=ST, S=512, idx=IDX, w=WT, w_dt=BF16, bias=BIAS, y=
         (dict(D=4100, x=X + 1), MISAL),
         (dict(N=-1), SHAPE),
         (dict(N=(1 << 24) + 1), SHAPE),
-        (dict(S=(1 << 19) + 1), SHAPE),
+        (dict(S=(1 << 19) - 31), SHAPE),
         (dict(idx=None, N=600, S=512), SHAPE),
         (dict(x_ld=4000), STRIDE),
         (dict(x_ld=4100), STRIDE),
@@ -212,6 +212,8 @@ def upd(x=X, x_ld=None, state=ST, S=512, idx=IDX, w=WT, w_dt=BF16, bias=BIAS, y=
         (dict(state=WT), ALIAS),
         (dict(status=ST + 64), ALIAS),
         (dict(status=Y + 4), ALIAS),
+        (dict(status=None), NULLP),  # indices given: only the device sees their verdict
+        (dict(D=(1 << 26) + 8, x_ld=(1 << 26) + 8), SHAPE),
     ],
 )
 def test_update_host_errors(kw, code):
@@ -358,7 +360,7 @@ def fwd_pool(x=X, state=POOL, S=64, idx=PIDX, flags=PFLAG, status=PST, y=Y, B=2,
         (dict(idx=None), NULLP),
         (dict(state=None), NULLP),
         (dict(S=-1), SHAPE),
-        (dict(S=(1 << 19) + 1), SHAPE),
+        (dict(S=(1 << 19) - 31), SHAPE),
         (dict(B=(1 << 24) + 1, T=1), SHAPE),
         (dict(T=0), SHAPE),
         (dict(status=PST + 2), MISAL),
@@ -482,6 +484,7 @@ def upd_ex(x=X, state=ST, S=512, L=3, idx=IDX, cs=CSL, y=Y, N=256, D=4096, W=4, 
         (dict(status=CSL), ALIAS),
         (dict(y=CSL - 512), ALIAS),
         (dict(L=4, state=Y - 512 * 4096 * 4 * 2 + 16), ALIAS),  # an L = 4 pool reaches further than L = 3
+        (dict(idx=None, status=None), NULLP),  # cache_seqlens given: a negative entry fails on the device
     ],
 )
 def test_update_ex_host_errors(kw, code):
@@ -491,6 +494,56 @@ def test_update_ex_host_errors(kw, code):
 def test_update_ex_width_one_shift_needs_no_state():
     # W = 1, L = 0, shift: no state at all; nothing to launch for N = 0
     assert upd_ex(W=1, L=0, cs=None, state=None, N=0, status=None) == OK
+
+
+def upd_cfg(cfg, **kw):
+    a = dict(x=X, state=ST, S=512, L=3, idx=IDX, cs=None, y=Y, N=256, D=4096, W=4, status=STATUS, x_ld=None)
+    a.update(kw)
+    x_ld = a["D"] if a["x_ld"] is None else a["x_ld"]
+    return cc.lib().cconv_update_config(a["x"], x_ld, a["state"], a["S"], a["L"], a["idx"], a["cs"], WT, BF16, BIAS,
+                                        a["y"], a["N"], a["D"], a["W"], a["status"],
+                                        None if cfg is None else ctypes.byref(cfg), None)
+
+
+@pytest.mark.parametrize(
+    "cfg,kw,code",
+    [
+        (None, {}, NULLP),
+        (dict(block_threads=32, options=0, rows_per_block=1), {}, CONFIG),
+        (dict(block_threads=96, options=0, rows_per_block=1), {}, CONFIG),
+        (dict(block_threads=2048, options=0, rows_per_block=1), {}, CONFIG),
+        (dict(block_threads=256, options=2, rows_per_block=1), {}, CONFIG),
+        (dict(block_threads=256, options=0, rows_per_block=0), {}, CONFIG),
+        (dict(block_threads=256, options=0, rows_per_block=4, rows_per_thread=4), {}, CONFIG),
+        (dict(block_threads=1024, options=0, rows_per_block=4, rows_per_thread=2), {}, CONFIG),  # registers
+        (dict(vec=2, block_threads=256, options=0, rows_per_block=1), {}, CONFIG),
+        (dict(vec=8, block_threads=256, options=0, rows_per_block=1), dict(D=4100), CONFIG),  # 8 does not divide D
+        (dict(vec=4, block_threads=256, options=0, rows_per_block=1), dict(D=4098), CONFIG),
+        (dict(vec=4, block_threads=256, options=0, rows_per_block=1), dict(D=4100, x_ld=4102), STRIDE),
+        (dict(vec=4, block_threads=256, options=0, rows_per_block=1), dict(D=4100, x=X + 2), MISAL),
+        (dict(vec=1, block_threads=256, options=1, rows_per_block=1), dict(D=4100), CONFIG),  # one channel: no hints
+        (dict(vec=1, block_threads=256, options=0, rows_per_block=2, rows_per_thread=2), {}, CONFIG),
+        (dict(block_threads=64, options=0, rows_per_block=1), dict(N=65536 * 2, S=65536 * 2), CONFIG),  # grid rows
+    ],
+)
+def test_update_config_host_errors(cfg, kw, code):
+    c = None if cfg is None else cc.UpdateConfig(**cfg)
+    assert upd_cfg(c, **kw) == code
+
+
+def test_default_update_config():
+    c = cc.UpdateConfig()
+    assert cc.lib().cconv_default_update_config(256, 4096, ctypes.byref(c)) == OK
+    assert c.vec == 8 and c.rows_per_block >= 1
+    assert cc.lib().cconv_default_update_config(256, 4100, ctypes.byref(c)) == OK
+    assert c.vec == 4
+    assert cc.lib().cconv_default_update_config(256, 4098, ctypes.byref(c)) == OK
+    assert (c.vec, c.options, c.rows_per_thread) == (1, 0, 1)
+    assert cc.lib().cconv_default_update_config(1 << 20, 4096, ctypes.byref(c)) == OK
+    blocks_x = -(-(4096 // c.vec) // c.block_threads)
+    assert -(-(1 << 20) // c.rows_per_block) * blocks_x <= 1024 + blocks_x
+    assert cc.lib().cconv_default_update_config(-1, 4096, ctypes.byref(c)) == SHAPE
+    assert cc.lib().cconv_default_update_config(4, 4096, None) == NULLP
 
 
 def test_option_structs_match_the_header(tmp_path):

@@ -132,3 +132,76 @@ def test_circular_graph_replay():
         torch.cuda.synchronize()
         assert int(status.item()) == 0 and torch.equal(bits(y_out), bits(ys[r])), r
     assert torch.equal(bits(st), bits(ref))
+
+
+# (vec, block_threads, options, rows_per_block, rows_per_thread): 8, 4 and 1 channels per
+# thread, block shapes from one wave to sixteen, both cache hints, threads that carry one or
+# two rows at once, and blocks that walk several groups of rows (the next group's loads
+# issued before the current group's arithmetic), with ragged last groups
+UPDATE_CONFIGS = [(8, 64, 0, 1, 1), (8, 128, 1, 3, 1), (8, 256, 0, 7, 2), (8, 512, 1, 2, 2), (8, 1024, 0, 5, 1),
+                  (8, 256, 1, 64, 2), (4, 64, 1, 9, 2), (4, 256, 0, 1, 1), (4, 512, 1, 5, 2), (4, 1024, 1, 3, 1),
+                  (1, 64, 0, 1, 1), (1, 256, 0, 6, 1), (1, 1024, 0, 2, 1)]
+
+
+@pytest.mark.parametrize("D", [4096, 1032, 1004, 1003])
+@pytest.mark.parametrize("circular", [False, True], ids=["shift", "circular"])
+@pytest.mark.parametrize("WL", [(1, 1), (2, 1), (3, 3), (4, 3), (4, 4)], ids=lambda p: f"W{p[0]}L{p[1]}")
+def test_update_launch_config_invariance(WL, circular, D):
+    """y and the new state do not depend on the launch configuration, bit for bit; the default
+    launch matches the oracle (state bit-exact, y within tolerance)."""
+    W, L = WL
+    N, S = 37, 50
+    x, state, idx, cs, w, b = _inputs(N, S, D, W, L, seed=500 + 10 * W + L + D % 7, circular=circular)
+    y0, st0, status = _run(x, state, idx, cs, w, b)
+    ok, yr, sr = oracle.update_ex(x, state, idx.numpy(), None if cs is None else cs.numpy(), w, b)
+    assert ok and status == 0
+    assert torch.equal(bits(st0), bits(torch.from_numpy(sr).to(torch.bfloat16)))
+    assert_close(y0, yr, TOL_FWD, f"W{W} L{L} D{D} default launch")
+    ran = 0
+    for vec, bt, opt, rpb, rpt in UPDATE_CONFIGS:
+        if D % vec != 0:
+            continue
+        cfg = cc.UpdateConfig(vec=vec, block_threads=bt, options=opt if vec > 1 else 0, rows_per_block=rpb,
+                              rows_per_thread=rpt if vec > 1 else 1)
+        st = state.to(DEV)
+        y, s = cc.cconv_update_config(x.to(DEV), st, idx.to(DEV), w.to(DEV), b.to(DEV), config=cfg,
+                                      cache_seqlens=None if cs is None else cs.to(DEV))
+        torch.cuda.synchronize()
+        assert int(s.item()) == 0, cfg
+        assert torch.equal(bits(y.cpu()), bits(y0)), f"y differs under {cfg}"
+        assert torch.equal(bits(st.cpu()), bits(st0)), f"state differs under {cfg}"
+        ran += 1
+    assert ran >= 3
+
+
+@pytest.mark.parametrize("circular", [False, True], ids=["shift", "circular"])
+def test_update_many_rows_per_block(circular):
+    """N = 3000 rows: the default launch walks several rows per block (about 1024 blocks)."""
+    N, S, D, W, L = 3000, 3500, 4096, 4, 3
+    cfg = cc.cconv_default_update_config(N, D)
+    assert cfg.rows_per_block > 1
+    x, state, idx, cs, w, b = _inputs(N, S, D, W, L, seed=540, circular=circular)
+    y, st, status = _run(x, state, idx, cs, w, b)
+    ok, yr, sr = oracle.update_ex(x, state, idx.numpy(), None if cs is None else cs.numpy(), w, b)
+    assert ok and status == 0
+    assert torch.equal(bits(st), bits(torch.from_numpy(sr).to(torch.bfloat16)))
+    assert_close(y, yr, TOL_FWD, f"N{N} {'circular' if circular else 'shift'}")
+
+
+@pytest.mark.parametrize("case", ["duplicate_late", "out_of_range_late", "negative_seqlen_late"])
+def test_update_invalid_entry_past_the_first_block_of_rows(case):
+    """An invalid entry beyond the first blockDim rows (the slot check's later rounds) still
+    fails the whole call closed: nothing written, CCONV_ERR_INDEX."""
+    N, S, D, W, L = 1500, 1600, 512, 4, 3
+    x, state, idx, cs, w, b = _inputs(N, S, D, W, L, seed=550, circular=(case == "negative_seqlen_late"), pad=False)
+    idx = idx.clone()
+    if case == "duplicate_late":
+        idx[1400] = idx[3]
+    elif case == "out_of_range_late":
+        idx[1499] = S
+    else:
+        cs = cs.clone()
+        cs[1333] = -1
+    y, st, status = _run(x, state, idx, cs, w, b)
+    assert status == 8, case
+    assert torch.equal(bits(st), bits(state)), f"{case}: state modified"
