@@ -33,6 +33,8 @@ __all__ = [
     "cconv_fwd_varlen",
     "cconv_bwd_varlen",
     "cconv_bwd_workspace_bytes",
+    "cconv_bwd_noalloc",
+    "cconv_bwd_noalloc_max_workspace",
     "cconv_bwd_main",
     "cconv_bwd_finish",
     "cconv_update",
@@ -200,6 +202,10 @@ def _declare(L):
     L.cconv_bwd_state.argtypes = [p, i64, i64, p, i64, i64, p, i32, p, p, p, p, i32, p, p, p, sz, i64, i64, i64,
                                   i32, p]
     L.cconv_bwd_state.restype = i32
+    L.cconv_bwd_noalloc.argtypes = [p, i64, i64, p, i64, i64, p, i32, p, p, p, i32, p, i64, i64, i64, i32, p]
+    L.cconv_bwd_noalloc.restype = i32
+    L.cconv_bwd_noalloc_max_workspace.argtypes = []
+    L.cconv_bwd_noalloc_max_workspace.restype = sz
     L.cconv_bwd_main.argtypes = [p, i64, i64, p, i64, i64, p, i32, p, p, p, sz, i64, i64, i64, i32, p]
     L.cconv_bwd_main.restype = i32
     L.cconv_bwd_finish.argtypes = [p, sz, p, i32, p, i64, i64, i64, i32, p]
@@ -681,6 +687,41 @@ def cconv_bwd_varlen(x, dy, cu_seqlens, w, bias=None, init_state=None, *, dx=Non
     else:
         _check(L.cconv_bwd_varlen_config(*args, ctypes.byref(config), _stream(stream)), "cconv_bwd_varlen_config")
     return dx, dw, dbias, d_init_state, status
+
+
+def cconv_bwd_noalloc(x, dy, w, bias=None, *, dx, dw, dbias=None, stream=None):
+    """cconv_bwd with the library's static scratch instead of a workspace: nothing is
+    allocated, so the outputs dx (bf16, x's shape), dw ([D, W], bf16 or fp32) and dbias
+    (fp32 [D] or None) must be given. Returns (dx, dw, dbias)."""
+    sb, st = _act(x, "x")
+    dsb, dst = _act(dy, "dy")
+    B, T, D = x.shape
+    if tuple(dy.shape) != (B, T, D):
+        raise ValueError("dy must have x's shape")
+    _dev(w, "w")
+    W = w.shape[1]
+    if w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [D, W] tensor")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (D,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous fp32 [D] tensor")
+    _out(dx, "dx", x.shape, _BF)
+    _out(dw, "dw", (D, W), _WT)
+    _out(dbias, "dbias", (D,), _F32)
+    _check(
+        lib().cconv_bwd_noalloc(
+            _ptr(x), sb, st, _ptr(dy), dsb, dst, _ptr(w), _wdt(w, "w"), _ptr(bias), _ptr(dx), _ptr(dw),
+            _wdt(dw, "dw"), _ptr(dbias), B, T, D, W, _stream(stream),
+        ),
+        "cconv_bwd_noalloc",
+    )
+    return dx, dw, dbias
+
+
+def cconv_bwd_noalloc_max_workspace() -> int:
+    """Bytes of the static scratch cconv_bwd_noalloc uses (its largest workspace)."""
+    return int(lib().cconv_bwd_noalloc_max_workspace())
 
 
 def cconv_bwd_main(x, dy, w, bias, dx, workspace, *, stream=None):

@@ -5,13 +5,49 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/cconv.h"
 #include "cconv_device.hpp"
 #include "cconv_internal.hpp"
 
 using cconv::Plan;
+
+// ---- the backward without a caller workspace ----------------------------------------------
+// The dw/dbias partials of cconv_bwd_noalloc live in this file-scope device array: each GPU the
+// library runs on holds its own copy from the first call until the process ends. In host code
+// `scratch` is only a stand-in for the symbol; the array's device address on each GPU comes
+// from hipGetSymbolAddress, looked up once per device (with that device current) and kept.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (looked up on its first use on that device).
+cconv_status_t scratch_ptr(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return CCONV_ERR_LAUNCH;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CCONV_ERR_LAUNCH;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return CCONV_OK;
+}
+
+}  // namespace
+
 
 namespace {
 
@@ -251,6 +287,8 @@ struct Extra {
     int64_t r_sb = 0, r_st = 0;
     // the output's (y's, dx's) batch and row strides; o_st == 0: contiguous [B, T, D]
     int64_t o_sb = 0, o_st = 0;
+    // backward: the partials go to the library's static scratch (no caller workspace)
+    bool scratch = false;
 };
 
 // Checks of the states and of the pool/packed metadata against the call's other operands.
@@ -452,7 +490,12 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     if (!make_plan(c, B, T, D, &p)) return CCONV_ERR_BAD_SHAPE;
     p.options |= epi;
     const size_t need = (B == 0 || T == 0 || D == 0) ? 0 : bwd_workspace(p, D, W);
-    if (need > 0 && (!workspace || !aligned(workspace, 16))) return workspace ? CCONV_ERR_MISALIGNED : CCONV_ERR_NULL_POINTER;
+    if (ex.scratch) {
+        workspace = nullptr;  // resolved after every check has passed
+        workspace_bytes = kScratchBytes;
+    } else if (need > 0 && (!workspace || !aligned(workspace, 16))) {
+        return workspace ? CCONV_ERR_MISALIGNED : CCONV_ERR_NULL_POINTER;
+    }
 
     const Span in_x = span(x, extent3(B, T, D, x_sb, x_st, 2));
     const Span in_dy = span(dy, extent3(B, T, D, dy_sb, dy_st, 2));
@@ -477,6 +520,7 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     // a per-sequence history gradient needs at least one token
     if (ex.out && ex.mode != kPacked && T == 0 && B > 0 && D > 0) return CCONV_ERR_BAD_SHAPE;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (ex.scratch && need > 0 && (st = scratch_ptr(&workspace)) != CCONV_OK) return st;
     if ((st = launch_checks(ex, B, T, D, W, false, s)) != CCONV_OK) return st;
     if (D == 0) return CCONV_OK;
 
@@ -844,6 +888,18 @@ cconv_status_t cconv_bwd(const void* x, int64_t x_sb, int64_t x_st, const void* 
     return bwd_impl(kMain | kFinish, x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias,
                     workspace, workspace_bytes, B, T, D, W, nullptr, stream);
 }
+
+cconv_status_t cconv_bwd_noalloc(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
+                                 int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx,
+                                 void* dw, cconv_dtype_t dw_dtype, float* dbias, int64_t B, int64_t T, int64_t D,
+                                 int W, cconv_stream_t stream) {
+    Extra ex;
+    ex.scratch = true;
+    return bwd_impl(kMain | kFinish, x, x_sb, x_st, dy, dy_sb, dy_st, w, w_dtype, bias, dx, dw, dw_dtype, dbias,
+                    nullptr, 0, B, T, D, W, nullptr, stream, ex);
+}
+
+size_t cconv_bwd_noalloc_max_workspace(void) { return kScratchBytes; }
 
 cconv_status_t cconv_bwd_main(const void* x, int64_t x_sb, int64_t x_st, const void* dy, int64_t dy_sb,
                               int64_t dy_st, const void* w, cconv_dtype_t w_dtype, const float* bias, void* dx,

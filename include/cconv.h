@@ -132,6 +132,30 @@ cconv_status_t cconv_bwd(const void* x, int64_t x_sb, int64_t x_st, const void* 
                          int64_t T, int64_t D, int W, cconv_stream_t stream);
 
 /*
+ * cconv_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the dw/dbias partials go to a
+ * static scratch array inside the library instead of a caller workspace. Arguments,
+ * results and errors as cconv_bwd, with no workspace: dx, dw and dbias are bit for bit those
+ * of cconv_bwd. The call allocates nothing and calls no allocating routine.
+ *   Limit: cconv_bwd_workspace_bytes(B, T, D, W) <= cconv_bwd_noalloc_max_workspace()
+ *   (16 MiB; the B8 T8192 D4096 W4 backward needs 10.5 MB); larger problems return
+ *   CCONV_ERR_WORKSPACE before anything is enqueued.
+ *   Each GPU holds its own copy of the array from the first call on it until the process
+ *   ends; that first call looks up the copy's device address (a host-side runtime query,
+ *   made with the calling thread's current device). Every call on one GPU uses the same
+ *   array, so calls that overlap on one GPU (on different streams, or from several threads
+ *   without ordering) race and give wrong dw/dbias; calls ordered on one stream are safe.
+ */
+cconv_status_t cconv_bwd_noalloc(const void* x, int64_t x_sb, int64_t x_st, const void* dy,
+                                 int64_t dy_sb, int64_t dy_st, const void* w, cconv_dtype_t w_dtype,
+                                 const float* bias, void* dx, void* dw, cconv_dtype_t dw_dtype,
+                                 float* dbias, int64_t B, int64_t T, int64_t D, int W,
+                                 cconv_stream_t stream);
+
+/* Bytes of the static scratch cconv_bwd_noalloc uses: its largest workspace. */
+size_t cconv_bwd_noalloc_max_workspace(void);
+
+/*
  * Forward and backward with a history before t = 0: the prefill <-> decode state handoff
  * (fla's initial_state and output_final_state parameters, in the kernel-fun wheel's
  * _common/compat.py FLA_KWARGS table; the decode PR's description names a direct

@@ -224,6 +224,20 @@ def test_update_empty_without_status_is_ok():
     assert upd(N=0, status=None) == OK
 
 
+def test_bwd_noalloc_host_errors():
+    """The static-scratch backward checks like cconv_bwd and refuses problems whose partials do
+    not fit its array, before any device call."""
+    L = cc.lib()
+    cap = L.cconv_bwd_noalloc_max_workspace()
+    assert cap == 16 << 20
+    call = lambda B, T, D, W, **k: L.cconv_bwd_noalloc(k.get("x", X), T * D, D, DY, T * D, D, WT, BF16, BIAS,
+                                                       k.get("dx", DX), DW, BF16, DB, B, T, D, W, None)
+    assert L.cconv_bwd_workspace_bytes(1, 64, 1 << 20, 4) > cap
+    assert call(1, 64, 1 << 20, 4) == WS
+    assert call(2, 64, 512, 5) == SHAPE
+    assert call(2, 64, 512, 4, x=None) == NULLP
+
+
 def test_bwd_stages_host_errors():
     L = cc.lib()
     D, T, B, W = 512, 64, 2, 4
