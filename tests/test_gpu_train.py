@@ -1,10 +1,12 @@
 """GPU parity of the forward and backward against the CPU oracle, through the C ABI.
 
 Sizes the oracle finishes in seconds are compared element by element (every y, dx, dw,
-dbias); the 8x8192x4096 workload, in the launch configuration the benchmark times, is
-compared on sampled outputs the oracle computes one by one (random points plus the sequence
-start, segment boundaries, the sequence end and strip edges) and on sampled channels of dw
-and dbias (full sums over batch and time). Tolerances are in parity.py.
+dbias). The 8x8192x4096 workload (and the 16x8192x2048 production call), in the launch
+configuration the benchmark times, is compared in full too (every element of y and dx, every
+channel of dw and dbias: the multithreaded oracle takes seconds), and also on sampled outputs
+the oracle computes one by one (random points plus the sequence start, segment boundaries,
+the sequence end and strip edges). Tolerances and the element-wise ulp checks are in
+parity.py.
 """
 
 from __future__ import annotations
@@ -100,6 +102,26 @@ def test_headline_sampled_parity(headline):
     print(f"{s.name} sampled: err y {e1:.2e} dx {e2:.2e} dw {e3:.2e} dbias {e4:.2e} ({pb.size} points, {ch.size} channels)")
 
 
+@pytest.mark.timeout(900)
+def test_headline_full_parity(headline):
+    """Every element of the full-size workload against the float64 oracle, in the launch the
+    benchmark times: all of y and dx (the last W-1 rows of every batch row included, where the
+    halo reads past T), all channels of dw and dbias, and dw again accumulated to fp32 (the
+    tight check of the long sums)."""
+    s, inp, (y, dx, dw, db), xf, dyf = headline
+    _, yr = oracle.fwd(xf, inp["w"], inp["bias"])
+    dxr, dwr, dbr = oracle.bwd(xf, dyf, inp["w"], inp["bias"])
+    ey = max(assert_close(y[b], yr[b], TOL_FWD, f"{s.name} y[{b}]") for b in range(s.B))
+    del yr
+    edx = max(assert_close(dx[b], dxr[b], TOL_BWD, f"{s.name} dx[{b}]") for b in range(s.B))
+    del dxr
+    edw = assert_close(dw, dwr, TOL_BWD, f"{s.name} dw")
+    edb = assert_close(db, dbr, TOL_BWD, f"{s.name} dbias")
+    _, _, dw32, _ = run_train(inp, dw_dtype=torch.float32)
+    edw32 = assert_close(dw32, dwr, TOL_BWD, f"{s.name} fp32 dw")
+    print(f"{s.name} full: err y {ey:.2e} dx {edx:.2e} dw {edw:.2e} dbias {edb:.2e} fp32 dw {edw32:.2e}", flush=True)
+
+
 def test_headline_outputs_finite_and_deterministic(headline):
     s, inp, (y, dx, dw, db), _, _ = headline
     assert torch.isfinite(y.float()).all() and torch.isfinite(dx.float()).all()
@@ -158,7 +180,7 @@ def test_fused_qkv_one_launch_equals_three(split):
     torch.cuda.synchronize()
     assert torch.equal(bits(y), bits(torch.cat([p[0] for p in parts], dim=2)))
     assert torch.equal(bits(dx), bits(torch.cat([p[1] for p in parts], dim=2)))
-    assert_close(dw.cpu().float(), torch.cat([p[2] for p in parts]).cpu().float(), TOL_BWD, "fused dw")
+    assert_close(dw.cpu(), torch.cat([p[2] for p in parts]).cpu().float(), TOL_BWD, "fused dw")
     assert_close(db.cpu(), torch.cat([p[3] for p in parts]).cpu(), TOL_BWD, "fused dbias")
     check_against_oracle(inp, (y.cpu(), dx.cpu(), dw.cpu(), db.cpu()), "fused q|k|v")
 
