@@ -260,6 +260,9 @@ def roofline_lib() -> ctypes.CDLL:
             p = ctypes.c_void_p
             L.cconv_roofline_copy.argtypes = [ctypes.c_int, p, p, p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, p]
             L.cconv_roofline_copy.restype = ctypes.c_int
+            L.cconv_roofline_copy_persistent.argtypes = [ctypes.c_int, p, p, p, ctypes.c_int64, ctypes.c_int,
+                                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, p]
+            L.cconv_roofline_copy_persistent.restype = ctypes.c_int
             _roof = L
         return _roof
 

@@ -12,6 +12,12 @@
  *   unroll: 16-byte vectors per thread (1, 2, 4 or 8); threads per block: 256, 512 or 1024;
  *   nontemporal: 1 to use non-temporal loads and stores.
  * Returns 0 on success, 1 on a bad argument (nothing enqueued), 2 on a failed launch.
+ *
+ * cconv_roofline_copy_persistent(kind, a, b, dst, bytes, blocks, unroll, threads, nontemporal,
+ *                                stream)
+ *   The same copies with a fixed grid of `blocks` blocks (1 .. 65536) walking the buffer in
+ *   grid-stride chunks; each thread keeps `unroll` (2, 4 or 8) 16-byte loads in flight before
+ *   its stores. Same arguments and returns otherwise.
  */
 #ifndef CCONV_ROOFLINE_H
 #define CCONV_ROOFLINE_H
@@ -26,6 +32,9 @@ struct ihipStream_t;
 
 int cconv_roofline_copy(int kind, const void* a, const void* b, void* dst, int64_t bytes, int unroll,
                         int threads, int nontemporal, struct ihipStream_t* stream);
+
+int cconv_roofline_copy_persistent(int kind, const void* a, const void* b, void* dst, int64_t bytes, int blocks,
+                                   int unroll, int threads, int nontemporal, struct ihipStream_t* stream);
 
 #ifdef __cplusplus
 }
