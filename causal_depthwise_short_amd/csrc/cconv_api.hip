@@ -71,7 +71,9 @@ constexpr int64_t kNarrowBwdTargetWaves = 2048;
 // forward and backward: non-temporal loads and stores, solo kernel (no software prefetch)
 constexpr int kFwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
 constexpr int kBwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
-constexpr int64_t kMinSeg = 64;         // shorter segments re-read too large a share of rows
+// calls that stream at most this many bytes (the 256 MB Infinity Cache) keep non-temporal hints
+// even on rows that miss the 128-byte lines
+constexpr int64_t kSmallStreamBytes = int64_t(256) << 20;
 constexpr int64_t kUpdateTargetBlocks = 1024;
 // D of the decode update: its buffer ranges (a slot's [D, L] state run, fp32 taps [D, W]) stay
 // below 2^31 bytes
@@ -135,14 +137,19 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 //     solo waves, one per SIMD; kNarrow*TargetWaves for the narrow path) and no more. A grid
 //     slightly larger than the slots (17 strips x 8 segments x 8 rows = 1088 waves at D = 4160)
 //     leaves the extra waves sharing a SIMD with another, and the kernel waits for them: about
-//     twice the time. Segments never drop below kMinSeg rows (the W-1 rows each segment
-//     re-reads stay a small share).
+//     twice the time. Segments shrink to a single row group (16 rows) when the problem is
+//     too small to fill the slots otherwise: the W-1 rows each segment re-reads then cost
+//     less than idle SIMDs (graph-timed, from HBM: [1,256,512] forward 9.9 -> 4.3 us and
+//     backward 20.4 -> 11.0 us with 16- instead of 64-row segments; [3,1000,2000] W=2 forward
+//     12.9 -> 8.9 us and backward 22.6 -> 17.3 us with 32-row ones).
 //   * Cache hints: non-temporal loads and stores when every streamed row starts on a 128-byte
-//     cache line (for contiguous operands, 2D a multiple of 128); otherwise plain ones, so
-//     that the L2 merges the lines two neighbouring strips share (at D = 4104: 241 vs 264 us
-//     forward, 325 vs 389 us backward). The narrow path always runs plain ones. Packed
-//     batches and the epilogue variants keep the streaming hints (their kernels are compiled
-//     for those only).
+//     cache line (for contiguous operands, 2D a multiple of 128), or when the call streams at
+//     most kSmallStreamBytes; otherwise plain ones, so that the L2 merges the lines two
+//     neighbouring strips share (at D = 4104: 241 vs 264 us forward, 325 vs 389 us backward;
+//     at [3,1000,2000], whose rows miss the lines too, the non-temporal hints are the faster:
+//     8.9 vs 10.1 us forward, 17.3 vs 19.2 us backward). The narrow path always runs plain
+//     ones. Packed batches and the epilogue variants keep the streaming hints (their kernels
+//     are compiled for those only).
 //   `line_rows_in` (-1: from D alone, as for contiguous operands on 128-byte aligned bases)
 //   says whether every streamed row of the call starts on a 128-byte line.
 //   `quads` says whether the call's activations meet the 4-channel rule (8-byte aligned,
@@ -159,14 +166,15 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
     c.waves_per_block = 1;
     c.strips_per_block = 1;
     const bool line_rows = line_rows_in < 0 ? (2 * D) % 128 == 0 : line_rows_in != 0;
+    const bool small = static_cast<__int128>(B) * T * D * (bwd ? 6 : 4) <= kSmallStreamBytes;
     if (narrow)
         c.options = cconv::kNarrowOptions;
-    else if (line_rows || streaming_only)
+    else if (line_rows || streaming_only || small)
         c.options = bwd ? kBwdOptions : kFwdOptions;
     else
         c.options = cconv::kSolo;
-    // segment length: a multiple of the row group (and of 8), at least kMinSeg rows, at most
-    // T rounded up
+    // segment length: a multiple of the row group (and of 8), at least one group, at most T
+    // rounded up
     const int64_t align = std::max<int64_t>(8, c.rows_per_group);
     const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
     const int64_t slots = narrow                            ? (bwd ? kNarrowBwdTargetWaves : kNarrowFwdTargetWaves)
@@ -178,7 +186,7 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
     const int64_t per_row = (b1 > slots || strips > slots) ? 1 : std::max<int64_t>(1, slots / (b1 * strips));
     const int64_t t = std::max<int64_t>(T, 1);
     int64_t ts = (t + per_row - 1) / per_row;
-    ts = std::max(kMinSeg, ((ts + align - 1) / align) * align);
+    ts = std::max(align, ((ts + align - 1) / align) * align);
     const int64_t tcap = ((t + align - 1) / align) * align;
     c.seg_rows = std::min(ts, tcap);
     if (!narrow && D % 8 != 0 && !quads) {

@@ -256,27 +256,31 @@ def test_bwd_stages_host_errors():
 def test_default_plan_fits_the_wave_slots(which):
     """Default plans cut each batch row into as many segments as the wave slots allow (1024
     one-wave-per-SIMD waves; 3072 (forward) and 2048 (backward) on the one-channel-per-lane
-    path) and no more, and take
-    streaming cache hints only when output rows start on 128-byte lines."""
+    path) and no more, down to one 16-row group, and take streaming cache hints when output
+    rows start on 128-byte lines or the call streams at most 256 MB."""
     for B, T, D in [(8, 8192, 4096), (8, 8192, 4160), (8, 8192, 4104), (16, 8192, 2048), (3, 1000, 2000),
-                    (8, 8192, 4100), (1, 65536, 4096), (2, 100003, 520), (64, 4096, 4096)]:
+                    (8, 8192, 4100), (1, 65536, 4096), (2, 100003, 520), (64, 4096, 4096), (1, 256, 512)]:
         c = cc.cconv_default_config(which, B, T, D, 4)
         narrow = D % 4 != 0
         fwd = which in ("fwd", 0)
-        off_lines = (2 * D) % 128 != 0
+        small = B * T * D * (4 if fwd else 6) <= 256 << 20
+        off_lines = (2 * D) % 128 != 0 and not small
         slots = (3072 if fwd else 2048) if narrow else (768 if fwd and off_lines else 1024)
         strips = -(-D // (64 * c.vec))
         waves = B * strips * -(-T // c.seg_rows)
         if B * strips <= slots:
             assert waves <= slots, (B, T, D, c, waves)
-        if c.seg_rows > 64:  # not held up by the minimum segment: one more segment would not fit
+        if c.seg_rows > 16:  # not held up by the one-group minimum: one more segment would not fit
             assert B * strips * (-(-T // c.seg_rows) + 1) > slots or -(-T // c.seg_rows) * c.seg_rows - T < c.seg_rows
         if narrow:
             assert c.vec == 1 and c.options == 0
         else:
-            assert c.vec == 4 and c.options == (11 if (2 * D) % 128 == 0 else 8), (D, c.options)
+            assert c.vec == 4 and c.options == (8 if off_lines else 11), (D, c.options)
     assert cc.cconv_default_config(which, 8, 8192, 4096, 4).seg_rows == 1024
     assert cc.cconv_default_config(which, 8, 8192, 4160, 4).seg_rows == 1184
+    # the small workloads: one-group segments at B1 T256 D512, 32-row ones at B3 T1000 D2000
+    assert cc.cconv_default_config(which, 1, 256, 512, 4).seg_rows == 16
+    assert cc.cconv_default_config(which, 3, 1000, 2000, 2).seg_rows == 32
 
 
 @pytest.mark.parametrize("which", ["fwd", "bwd"])
@@ -681,8 +685,12 @@ def test_four_channel_plans_for_d_4_mod_8():
     L = cc.lib()
     D, T, B = 500, 64, 2
     for which in ("fwd", "bwd"):
+        # a small call keeps the streaming hints; a large one, whose rows miss the 128-byte
+        # lines, takes plain ones
         c = cc.cconv_default_config(which, B, T, D, 4)
-        assert c.vec == 4 and c.options == 8 and c.rows_per_group == 16
+        assert c.vec == 4 and c.options == 11 and c.rows_per_group == 16
+        c = cc.cconv_default_config(which, 8, 8192, 4100, 4)
+        assert c.vec == 4 and c.options == 8
     # accepted: 8-byte aligned activations, strides a multiple of 4, taps and bias off 16 bytes
     assert fwd(D=D, y=X) == ALIAS
     assert fwd(D=D, x=X + 8, y=X + 8) == ALIAS
