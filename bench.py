@@ -69,7 +69,10 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (and with it the parity gate)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile", action="store_true",
-                    help="profiling run: steps plus calibration copies only (no sweep, no oracle)")
+                    help="profiling run: steps, decode graph replays and calibration copies only (no sweep, no oracle)")
+    ap.add_argument("--profile-shapes", action="store_true",
+                    help="profiling run of the widths off the 8-channel path: forward and backward at [8,8192,D] for "
+                         "D = 4098, 4100, 4104 and 6144, then calibration copies")
     return ap.parse_args()
 
 
@@ -716,7 +719,37 @@ def time_configs(cc, si, torch, np, dev, copy_rates, peak, with_oracle, min_byte
     return out, cpu
 
 
-def decode_graph(cc, torch, dev, dhost, nbytes, peak, nsets=24):
+def profile_shapes(cc, si, torch, dev, steps):
+    """Forward and backward at [8, 8192, D] for the widths that leave the 8-channel path (one
+    channel per lane at 4098; 4-channel lanes on rows that miss the 128-byte lines at 4100 and
+    4104; contiguous 6144), `steps` calls each, then one 1R:1W and one 2R:1W flat copy of the
+    D = 4096 activation size for counter calibration."""
+    R = cc.roofline_lib()
+    out = {}
+    for D in (4098, 4100, 4104, 6144):
+        inp = si.train_inputs(8, 8192, D, 4, bias=True, seed=30 + D % 97)
+        x, w, b, dy = (inp[k].to(dev) for k in ("x", "w", "bias", "dy"))
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        dw, db = torch.empty_like(w), torch.empty(D, dtype=torch.float32, device=dev)
+        ws = torch.empty(cc.cconv_bwd_workspace_bytes(8, 8192, D, 4) // 4 + 1, dtype=torch.float32, device=dev)
+        for _ in range(steps):
+            cc.cconv_fwd(x, w, b, y=y)
+            cc.cconv_bwd(x, dy, w, b, dx=dx, dw=dw, dbias=db, workspace=ws)
+        torch.cuda.synchronize()
+        out[D] = {"fwd": cc.cconv_default_config("fwd", 8, 8192, D, 4).as_dict(),
+                  "bwd": cc.cconv_default_config("bwd", 8, 8192, D, 4).as_dict()}
+        del x, dy, y, dx, ws
+        torch.cuda.empty_cache()
+    nbytes = 8 * 8192 * 4096 * 2
+    a, bb, c = (torch.empty(nbytes // 2, dtype=torch.int16, device=dev) for _ in range(3))
+    st = torch.cuda.current_stream().cuda_stream
+    assert R.cconv_roofline_copy(1, a.data_ptr(), a.data_ptr(), c.data_ptr(), nbytes, 1, 256, 1, st) == 0
+    assert R.cconv_roofline_copy(2, a.data_ptr(), bb.data_ptr(), c.data_ptr(), nbytes, 1, 256, 1, st) == 0
+    torch.cuda.synchronize()
+    return {"profile_shapes": True, "steps": steps, "copy_bytes_per_operand": nbytes, "launch": out}
+
+
+def decode_graph(cc, torch, dev, dhost, nbytes, peak, nsets=24, reps=30):
     """The decode update timed as 24 back-to-back calls in one graph: each call on its own
     buffer set (x, state, y; 400 MB in all, more than the Infinity Cache holds, so each finds
     its rows in HBM), and again with every call on set 0 (cache-resident)."""
@@ -729,7 +762,7 @@ def decode_graph(cc, torch, dev, dhost, nbytes, peak, nsets=24):
     out = {"calls_per_graph": nsets, "launch": cc.cconv_default_update_config(N, D).as_dict()}
     for label, sets in (("hbm", list(range(nsets))), ("cache_resident", [0] * nsets)):
         q = graph_time(torch, [lambda i=i: cc.cconv_update(xs[i], sts[i], idx, w, b, y=ys[i], status=st) for i in sets],
-                       reps=30)
+                       reps=reps)
         gb = nbytes / q[1] / 1e9
         out[label] = {"us": round(q[1] * 1e6, 2), "us_p10_p90": [round(q[0] * 1e6, 2), round(q[2] * 1e6, 2)],
                       "GBps": round(gb, 1), "pct_hbm_peak": round(100 * gb / peak, 1)}
@@ -762,6 +795,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cur = torch.cuda.current_stream
+    if args.profile_shapes:
+        print(json.dumps(profile_shapes(cc, si, torch, dev, args.steps)))
+        return
 
     s = si.HEADLINE
     dshape = si.DECODE
@@ -949,7 +985,7 @@ def main():
         # the decode update from HBM and cache-resident (graph replays), then calibration
         # dispatches of known size for the HBM counters: one 1R:1W copy and one 2R:1W copy of
         # `nbytes` per source
-        dgraph = decode_graph(cc, torch, dev, dhost, bytes_upd, HBM_PEAK_GBPS)
+        dgraph = decode_graph(cc, torch, dev, dhost, bytes_upd, HBM_PEAK_GBPS, reps=5)
         copy(1, 1, 256, 1)
         copy(2, 1, 256, 1)
         torch.cuda.synchronize()

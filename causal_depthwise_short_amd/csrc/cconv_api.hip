@@ -62,11 +62,6 @@ constexpr int64_t kTargetWaves = 1024;  // wave slots of the solo kernels: one p
 // two for the backward (interleaved sweeps at [8,8192,D] for D = 4098, 2050, 1003 and at
 // [4,4096,4098]: 6-9% faster forwards, 4-8% faster backwards than four waves per SIMD)
 constexpr int64_t kNarrowFwdTargetWaves = 3072;
-// wave slots of a 4-channel forward whose rows miss the cache lines (plain hints): three
-// quarters of the SIMDs, so each wave streams a longer segment (interleaved sweeps at
-// [8,8192,D] for D = 4100, 4104 and 2052: 2-5% faster than 1024 waves; the backward is 19%
-// slower that way and keeps kTargetWaves)
-constexpr int64_t kOffLineFwdTargetWaves = 768;
 constexpr int64_t kNarrowBwdTargetWaves = 2048;
 // forward and backward: non-temporal loads and stores, solo kernel (no software prefetch)
 constexpr int kFwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
@@ -133,6 +128,11 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 //     dy per group: 16 KiB in flight per wave), also for D = 4 (mod 8), whose rows are
 //     8-byte aligned (at D = 4100 this halves the one-channel plan's time). D not a multiple
 //     of 4: one channel per lane, 16-row groups, the general kernel.
+//   * Strips: the D/vec lane groups are dealt to ceil(D/(64*vec)) strips of near-equal width
+//     (strip s takes groups floor(s*L/n) .. floor((s+1)*L/n) - 1). At D = 4100 and 4104 the 17
+//     strips carry 60 or 61 lane groups each instead of sixteen full strips and one holding one
+//     or two: forward 238 -> 208 us and 247 -> 210 us at [8,8192,D] (the backward, whose waves
+//     are bound by their own instruction stream, is unchanged at 323-326 us).
 //   * Segments: each batch row is cut into as many segments as the wave slots allow (1024
 //     solo waves, one per SIMD; kNarrow*TargetWaves for the narrow path) and no more. A grid
 //     slightly larger than the slots (17 strips x 8 segments x 8 rows = 1088 waves at D = 4160)
@@ -145,7 +145,7 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 //   * Cache hints: non-temporal loads and stores when every streamed row starts on a 128-byte
 //     cache line (for contiguous operands, 2D a multiple of 128), or when the call streams at
 //     most kSmallStreamBytes; otherwise plain ones, so that the L2 merges the lines two
-//     neighbouring strips share (at D = 4104: 241 vs 264 us forward, 325 vs 389 us backward;
+//     neighbouring strips share (at D = 4104: 214 vs 254 us forward, 332 vs 387 us backward;
 //     at [3,1000,2000], whose rows miss the lines too, the non-temporal hints are the faster:
 //     8.9 vs 10.1 us forward, 17.3 vs 19.2 us backward). The narrow path always runs plain
 //     ones. Packed batches and the epilogue variants keep the streaming hints (their kernels
@@ -176,10 +176,9 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
     // segment length: a multiple of the row group (and of 8), at least one group, at most T
     // rounded up
     const int64_t align = std::max<int64_t>(8, c.rows_per_group);
-    const int64_t strips = std::max<int64_t>(1, (D + 64 * c.vec - 1) / (64 * c.vec));
-    const int64_t slots = narrow                            ? (bwd ? kNarrowBwdTargetWaves : kNarrowFwdTargetWaves)
-                          : (!bwd && c.options == cconv::kSolo) ? kOffLineFwdTargetWaves
-                                                                : kTargetWaves;
+    const int64_t lane_groups = (D + c.vec - 1) / c.vec;
+    const int64_t strips = std::max<int64_t>(1, (lane_groups + cconv::kWave - 1) / cconv::kWave);
+    const int64_t slots = narrow ? (bwd ? kNarrowBwdTargetWaves : kNarrowFwdTargetWaves) : kTargetWaves;
     // (batch row, strip) pairs; the product is formed only when both factors are within the
     // slot count (no overflow at the largest sizes the API accepts)
     const int64_t b1 = std::max<int64_t>(B, 1);
@@ -203,7 +202,8 @@ bool make_plan(const cconv_config_t& c, int64_t B, int64_t T, int64_t D, Plan* p
     p->ws = c.strips_per_block;
     p->seg_rows = c.seg_rows;
     p->options = c.options;
-    p->strips = (D + 64 * c.vec - 1) / (64 * c.vec);
+    p->lane_groups = (D + c.vec - 1) / c.vec;
+    p->strips = (p->lane_groups + cconv::kWave - 1) / cconv::kWave;
     p->strip_groups = (p->strips + p->ws - 1) / p->ws;
     p->segs = (T + c.seg_rows - 1) / c.seg_rows;
     const int64_t wt = c.waves_per_block / c.strips_per_block;
@@ -433,6 +433,8 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     a.strip_groups = p.strip_groups;
     a.seg_groups = p.seg_groups;
     a.ws = p.ws;
+    a.lane_groups = p.lane_groups;
+    a.strips = p.strips;
     return cconv::launch_fwd(p, W, a, hs) == hipSuccess ? CCONV_OK : CCONV_ERR_LAUNCH;
 }
 
@@ -560,6 +562,8 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
         a.strip_groups = p.strip_groups;
         a.seg_groups = p.seg_groups;
         a.ws = p.ws;
+        a.lane_groups = p.lane_groups;
+        a.strips = p.strips;
         if (cconv::launch_bwd(p, W, a, s) != hipSuccess) return CCONV_ERR_LAUNCH;
     }
     if (!finish) return CCONV_OK;

@@ -266,11 +266,11 @@ template <int VEC, int G, int W, int F, bool VL>
 __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     constexpr int R = W > 1 ? W - 1 : 1;
     extern __shared__ float red[];  // [waves][VEC][64], one column at a time
-    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T);
+    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T, a.lane_groups, a.strips);
     const int64_t t0 = wt.t0, t1 = wt.t1;
     const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
-    const bool active = wt.d < a.D;
+    const bool active = wt.active;
     const bool valid = !(a.status && *a.status != 0);  // the offset check passed (or there is none)
     const uint32_t lo = static_cast<uint32_t>(wt.d) * 2u;  // byte offset of the lane's channels
 

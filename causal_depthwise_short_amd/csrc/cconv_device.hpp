@@ -369,15 +369,19 @@ __device__ __forceinline__ bool block_slots_bad(const int32_t* __restrict__ idx,
 
 // Where a wave works. The block id (XCD-remapped) selects a (strip group, segment group,
 // batch row); the wave's index selects its strip within the group (ws_i) and its segment
-// within the group (wt_i). All fields are wave-uniform except `d`, the lane's first channel.
+// within the group (wt_i). The strip holds lane groups floor(s*L/strips) .. floor((s+1)*L/
+// strips) - 1 of the L = lane_groups (as equal widths as integers allow, at most 64: no strip
+// is left nearly empty); `active` marks the lanes that own one. All fields are wave-uniform
+// except `d`, the lane's first channel, and `active`.
 struct WaveTile {
     int64_t b, sg, t0, t1, d;
     int ws_i, wt_i, wt;
+    bool active;
 };
 
 template <int VEC>
 __device__ __forceinline__ WaveTile wave_tile(int64_t strip_groups, int64_t seg_groups, int ws, int64_t seg_rows,
-                                              int64_t T) {
+                                              int64_t T, int64_t lane_groups, int64_t strips) {
     WaveTile w;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t sgrp = tile % strip_groups;
@@ -390,7 +394,11 @@ __device__ __forceinline__ WaveTile wave_tile(int64_t strip_groups, int64_t seg_
     w.wt_i = wave / ws;
     w.t0 = (w.sg * w.wt + w.wt_i) * seg_rows;
     w.t1 = min(w.t0 + seg_rows, T);
-    w.d = ((sgrp * ws + w.ws_i) * kWave + static_cast<int64_t>(threadIdx.x % kWave)) * VEC;
+    const int64_t strip = sgrp * ws + w.ws_i;
+    const int64_t g0 = strip * lane_groups / strips, g1 = (strip + 1) * lane_groups / strips;
+    const int64_t lane = threadIdx.x % kWave;
+    w.active = strip < strips && lane < g1 - g0;
+    w.d = (g0 + lane) * VEC;
     return w;
 }
 

@@ -119,10 +119,10 @@ __device__ __forceinline__ void fwd_run(const float (&tap)[W][VEC], const float 
 template <int VEC, int G, int W, int F, bool VL>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     constexpr int R = W > 1 ? W - 1 : 1;
-    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T);
+    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T, a.lane_groups, a.strips);
     const int64_t t0 = wt.t0, t1 = wt.t1;
     if (t0 >= a.T) return;    // a trailing wave of the last segment group
-    if (wt.d >= a.D) return;  // lanes past the last channel (D is a multiple of VEC)
+    if (!wt.active) return;   // lanes past the strip's channels
     if (a.status && *a.status != 0) return;  // the slot or offset check failed: write nothing
 
     // Row bases are wave-uniform; a lane adds its 32-bit byte offset to reach its channels.

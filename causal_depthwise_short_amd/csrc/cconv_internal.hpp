@@ -8,10 +8,12 @@
 namespace cconv {
 
 // How a forward or backward call is cut into work.
-//   A lane owns `vec` consecutive channels; a wave owns a strip of 64*vec channels and one
-//   time segment of `seg_rows` rows of one batch row. A block holds `waves` waves arranged as
-//   `ws` adjacent strips x `waves/ws` consecutive segments of one batch row. `group` rows are
-//   loaded together.
+//   A lane owns `vec` consecutive channels (a lane group); the D/vec lane groups are split into
+//   `strips` channel strips of as equal a width as integers allow (strip s holds lane groups
+//   floor(s*L/strips) .. floor((s+1)*L/strips) - 1, at most 64), and a wave owns one strip for
+//   one time segment of `seg_rows` rows of one batch row. A block holds `waves` waves arranged
+//   as `ws` adjacent strips x `waves/ws` consecutive segments of one batch row. `group` rows
+//   are loaded together.
 struct Plan {
     int vec;
     int group;
@@ -20,7 +22,8 @@ struct Plan {
     int64_t seg_rows;
     int options;  // kNtLoad | kNtStore | kPrefetch | kSolo, plus the epilogue bits kLinear | kResidual
     // derived
-    int64_t strips;        // ceil(D / (64*vec))
+    int64_t lane_groups;   // ceil(D / vec)
+    int64_t strips;        // ceil(lane_groups / 64)
     int64_t strip_groups;  // ceil(strips / ws)
     int64_t segs;          // ceil(T / seg_rows)
     int64_t seg_groups;    // ceil(segs / (waves/ws))
@@ -57,6 +60,7 @@ struct FwdArgs {
     int64_t B, T, D;
     int64_t seg_rows, strip_groups, seg_groups;
     int ws;
+    int64_t lane_groups, strips;  // the channel split (see Plan)
 };
 
 struct BwdArgs {
@@ -81,6 +85,7 @@ struct BwdArgs {
     int64_t B, T, D;
     int64_t seg_rows, strip_groups, seg_groups;
     int ws;
+    int64_t lane_groups, strips;  // the channel split (see Plan)
 };
 
 struct ReduceArgs {

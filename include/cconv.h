@@ -431,6 +431,8 @@ const char* cconv_version(void);
  *                    group's arithmetic (software prefetch); bit 3: "solo" kernels for
  *                    one-wave blocks (waves_per_block must be 1) that run one wave per SIMD
  *                    and may use the whole register file. Results do not depend on them.
+ * The lane groups (D / vec of them) are split into ceil(D / (64 * vec)) channel strips of as
+ * equal widths as integers allow.
  */
 typedef struct {
     int vec;
@@ -444,11 +446,13 @@ typedef struct {
 /*
  * The configuration cconv_fwd (which = 0) or cconv_bwd (which = 1) uses for this shape: 4
  * channels per lane (1 when D % 4 != 0), 16-row groups, one-wave blocks, each batch row cut
- * into as many segments as the wave slots hold (1024 waves, one per SIMD; 768 for a forward
- * whose rows miss the 128-byte lines; 3072 for the forward and 2048 for the backward on the
- * element-granular path); non-temporal hints (options 11) when 2D is a multiple of 128, plain
- * loads and stores (options 8; 0 on the element-granular path) otherwise. Packed batches and
- * the epilogue variants use the same plan with the streaming hints.
+ * into as many segments as the wave slots hold (1024 waves, one per SIMD; 3072 for the
+ * forward and 2048 for the backward on the element-granular path), down to one 16-row group;
+ * non-temporal hints (options 11) when 2D is a multiple of 128 or the call streams at most
+ * 256 MB, plain loads and stores (options 8; 0 on the element-granular path) otherwise.
+ * Packed batches and the epilogue variants use the same plan with the streaming hints. The
+ * segments depend on the shape alone, so the workspace cconv_bwd_workspace_bytes reports
+ * holds for every layout of the operands.
  */
 cconv_status_t cconv_default_config(int which, int64_t B, int64_t T, int64_t D, int W,
                                     cconv_config_t* out);

@@ -265,7 +265,7 @@ def test_default_plan_fits_the_wave_slots(which):
         fwd = which in ("fwd", 0)
         small = B * T * D * (4 if fwd else 6) <= 256 << 20
         off_lines = (2 * D) % 128 != 0 and not small
-        slots = (3072 if fwd else 2048) if narrow else (768 if fwd and off_lines else 1024)
+        slots = (3072 if fwd else 2048) if narrow else 1024
         strips = -(-D // (64 * c.vec))
         waves = B * strips * -(-T // c.seg_rows)
         if B * strips <= slots:
