@@ -63,6 +63,12 @@ constexpr int64_t kTargetWaves = 1024;  // wave slots of the solo kernels: one p
 // [4,4096,4098]: 6-9% faster forwards, 4-8% faster backwards than four waves per SIMD)
 constexpr int64_t kNarrowFwdTargetWaves = 3072;
 constexpr int64_t kNarrowBwdTargetWaves = 2048;
+// wave slots of the two-channel lanes (D = 2 mod 4): two waves per SIMD (interleaved sweeps of
+// 1024 to 4096 at [8,8192,4098] and [4,8192,2050]: best or within 3% of the best for both
+// passes; 4098 forward 262 us and backward 387 us against 272 and 420 us with one channel per
+// lane)
+constexpr int64_t kPairFwdTargetWaves = 2048;
+constexpr int64_t kPairBwdTargetWaves = 2048;
 // forward and backward: non-temporal loads and stores, solo kernel (no software prefetch)
 constexpr int kFwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
 constexpr int kBwdOptions = cconv::kNtLoad | cconv::kNtStore | cconv::kSolo;
@@ -152,16 +158,19 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 //     are compiled for those only).
 //   `line_rows_in` (-1: from D alone, as for contiguous operands on 128-byte aligned bases)
 //   says whether every streamed row of the call starts on a 128-byte line.
-//   `quads` says whether the call's activations meet the 4-channel rule (8-byte aligned,
-//   strides multiples of 4). When D = 4 (mod 8) and they do not, the plan runs one channel
-//   per lane with the 4-channel plan's segments: the dw/dbias partials (their count, so the
-//   workspace and what a finishing stage reads) stay those of the shape, whatever the layout.
+//   `lanes` says whether the call's activations meet the rule of the shape's lane width: for
+//   D = 4 (mod 8), 4 channels per lane (8-byte aligned, strides multiples of 4); for D = 2
+//   (mod 4), 2 channels per lane (4-byte aligned, even strides). When they do not, the plan
+//   runs one channel per lane with that lane width's segments: the dw/dbias partials (their
+//   count, so the workspace and what a finishing stage reads) stay those of the shape,
+//   whatever the layout.
 cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, bool streaming_only = false,
-                              int line_rows_in = -1, bool quads = true) {
+                              int line_rows_in = -1, bool lanes = true) {
     (void)W;
     cconv_config_t c;
     const bool narrow = (D % 4 != 0);
-    c.vec = narrow ? 1 : 4;
+    const bool pair = (D % 4 == 2);
+    c.vec = pair ? 2 : (narrow ? 1 : 4);
     c.rows_per_group = 16;
     c.waves_per_block = 1;
     c.strips_per_block = 1;
@@ -178,7 +187,9 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
     const int64_t align = std::max<int64_t>(8, c.rows_per_group);
     const int64_t lane_groups = (D + c.vec - 1) / c.vec;
     const int64_t strips = std::max<int64_t>(1, (lane_groups + cconv::kWave - 1) / cconv::kWave);
-    const int64_t slots = narrow ? (bwd ? kNarrowBwdTargetWaves : kNarrowFwdTargetWaves) : kTargetWaves;
+    const int64_t slots = pair     ? (bwd ? kPairBwdTargetWaves : kPairFwdTargetWaves)
+                          : narrow ? (bwd ? kNarrowBwdTargetWaves : kNarrowFwdTargetWaves)
+                                   : kTargetWaves;
     // (batch row, strip) pairs; the product is formed only when both factors are within the
     // slot count (no overflow at the largest sizes the API accepts)
     const int64_t b1 = std::max<int64_t>(B, 1);
@@ -188,7 +199,7 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
     ts = std::max(align, ((ts + align - 1) / align) * align);
     const int64_t tcap = ((t + align - 1) / align) * align;
     c.seg_rows = std::min(ts, tcap);
-    if (!narrow && D % 8 != 0 && !quads) {
+    if ((pair || (!narrow && D % 8 != 0)) && !lanes) {
         c.vec = 1;
         c.options = cconv::kNarrowOptions;
     }
@@ -220,8 +231,15 @@ bool on_lines(const void* p, int64_t sb, int64_t st) {
     return aligned(p, 128) && (2 * st) % 128 == 0 && (2 * sb) % 128 == 0;
 }
 
-// Whether a [B, T, D] operand meets the 4-channel rule: 8-byte aligned, strides multiples of 4.
-bool on_quads(const void* p, int64_t sb, int64_t st) { return aligned(p, 8) && sb % 4 == 0 && st % 4 == 0; }
+// Whether a [B, T, D] operand meets the rule of v channels per lane: 2v-byte aligned, strides
+// multiples of v.
+bool on_lanes(const void* p, int64_t sb, int64_t st, int v) {
+    return aligned(p, static_cast<uintptr_t>(2 * v)) && sb % v == 0 && st % v == 0;
+}
+
+// The lane width whose operand rule the default plan of D asks for (4 also for D = 0 mod 8,
+// whose plans check the 8-channel granule instead).
+int lane_width(int64_t D) { return D % 4 == 0 ? 4 : (D % 4 == 2 ? 2 : 1); }
 
 // Checks shared by the forward and backward before a plan exists: sizes, width, tap dtype.
 cconv_status_t check_train_common(cconv_dtype_t w_dtype, int64_t B, int64_t T, int64_t D, int W) {
@@ -236,9 +254,10 @@ cconv_status_t check_train_common(cconv_dtype_t w_dtype, int64_t B, int64_t T, i
 // whole 8-channel groups (16-byte aligned rows, strides multiples of 8, 16-byte aligned taps,
 // bias, dw and states); 4 for a 4-channel plan with D = 4 (mod 8) (8-byte aligned rows, strides
 // multiples of 4; the taps, bias, dw and states are read and written per element, so element
-// alignment); 1 for the element-granular plan (one channel per lane: any stride, element
+// alignment); 2 for a 2-channel plan (4-byte aligned rows, even strides, element alignment
+// elsewhere); 1 for the element-granular plan (one channel per lane: any stride, element
 // alignment everywhere).
-int granule(const cconv_config_t& c, int64_t D) { return c.vec == 1 ? 1 : (D % 8 == 0 ? 8 : 4); }
+int granule(const cconv_config_t& c, int64_t D) { return c.vec <= 2 ? c.vec : (D % 8 == 0 ? 8 : 4); }
 
 // Alignment of the taps and bias: 16 bytes for granule 8; the element size otherwise.
 cconv_status_t check_params(const void* w, cconv_dtype_t w_dtype, const float* bias, int gran) {
@@ -250,7 +269,7 @@ cconv_status_t check_params(const void* w, cconv_dtype_t w_dtype, const float* b
 
 // A bf16 [B, T, D] operand with strides (sb, st, 1): strides multiples of the plan's granule
 // and 2 * granule bytes of alignment (granule 8: 16 bytes; 4: 8 bytes, whole 8-byte rows per
-// lane; 1: any strides, 2-byte alignment).
+// lane; 2: 4 bytes; 1: any strides, 2-byte alignment).
 cconv_status_t check_act(const void* p, int64_t sb, int64_t st, int64_t D, int gran) {
     if (sb < 0 || st < D || sb > kMaxDim || st > kMaxDim) return CCONV_ERR_BAD_STRIDE;
     if (sb % gran != 0 || st % gran != 0) return CCONV_ERR_BAD_STRIDE;
@@ -366,11 +385,12 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     const bool lines = on_lines(x, x_sb, x_st) &&
                        (ex.o_st ? on_lines(y, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_lines(y, T * D, D)) &&
                        (!ex.r || on_lines(ex.r, ex.r_sb, ex.r_st));
-    const bool quads = on_quads(x, x_sb, x_st) &&
-                       (ex.o_st ? on_quads(y, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_quads(y, T * D, D)) &&
-                       (!ex.r || on_quads(ex.r, ex.r_sb, ex.r_st));
+    const int lv = lane_width(D);
+    const bool lanes = on_lanes(x, x_sb, x_st, lv) &&
+                       (ex.o_st ? on_lanes(y, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st, lv) : on_lanes(y, T * D, D, lv)) &&
+                       (!ex.r || on_lanes(ex.r, ex.r_sb, ex.r_st, lv));
     const cconv_config_t c =
-        cfg ? *cfg : default_config(false, B, T, D, W, ex.mode == kPacked || epi != 0, lines, quads);
+        cfg ? *cfg : default_config(false, B, T, D, W, ex.mode == kPacked || epi != 0, lines, lanes);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
     if (D % c.vec != 0) return CCONV_ERR_BAD_CONFIG;  // a plan needs whole groups of its lane width
     const int gran = granule(c, D);
@@ -474,10 +494,12 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     // segments, and so the partials a finishing stage reads, do not depend on them)
     const bool lines = on_lines(x, x_sb, x_st) && on_lines(dy, dy_sb, dy_st) &&
                        (ex.o_st && main ? on_lines(dx, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_lines(dx, T * D, D));
-    const bool quads = on_quads(x, x_sb, x_st) && on_quads(dy, dy_sb, dy_st) &&
-                       (ex.o_st && main ? on_quads(dx, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st) : on_quads(dx, T * D, D));
+    const int lv = lane_width(D);
+    const bool lanes = on_lanes(x, x_sb, x_st, lv) && on_lanes(dy, dy_sb, dy_st, lv) &&
+                       (ex.o_st && main ? on_lanes(dx, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st, lv)
+                                        : on_lanes(dx, T * D, D, lv));
     const cconv_config_t c =
-        cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0, lines, quads);
+        cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0, lines, lanes);
     if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
     if (D % c.vec != 0) return CCONV_ERR_BAD_CONFIG;  // a plan needs whole groups of its lane width
     const int gran = granule(c, D);

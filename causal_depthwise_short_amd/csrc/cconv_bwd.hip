@@ -85,11 +85,11 @@ hipError_t launch_bwd_w(int W, int F, dim3 grid, dim3 block, size_t lds, const B
 
 bool bwd_variant_exists(int vec, int group) {
     return (vec == 8 && (group == 4 || group == 8)) || (vec == 4 && (group == 4 || group == 8 || group == 16)) ||
-           (vec == 1 && group == 16);
+           ((vec == 1 || vec == 2) && group == 16);
 }
 
 hipError_t launch_bwd(const Plan& p, int W, const BwdArgs& a, hipStream_t s) {
-    if (a.cu || p.vec == 1 || (p.options & kLinear)) return launch_bwd_extra(p, W, a, s);
+    if (a.cu || p.vec <= 2 || (p.options & kLinear)) return launch_bwd_extra(p, W, a, s);
     const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
     const size_t lds = static_cast<size_t>(p.waves) * p.vec * kWave * sizeof(float);
     const int F = p.options;

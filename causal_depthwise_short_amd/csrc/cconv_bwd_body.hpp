@@ -356,6 +356,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             float* o = at(out + j * a.D, lo * 2u);  // fp32 partials: twice the bf16 byte offset
             if constexpr (VEC == 1) {
                 o[0] = s[0];
+            } else if constexpr (VEC == 2) {
+                reinterpret_cast<float2*>(o)[0] = make_float2(s[0], s[1]);
             } else if constexpr (VEC == 8) {
                 reinterpret_cast<float4*>(o)[0] = make_float4(s[0], s[1], s[2], s[3]);
                 reinterpret_cast<float4*>(o)[1] = make_float4(s[4], s[5], s[6], s[7]);

@@ -1,7 +1,7 @@
 // cconv_bwd_extra.hip -- the backward's packed-batch kernels (every (vec, group) pair,
 // streaming options), its variant without an activation (g = dy; the default launch only: 4
-// channels per lane, 16-row groups, one-wave solo blocks), and the element-granular path (one
-// channel per lane, for D not a multiple of 8), fixed-length and packed.
+// channels per lane, 16-row groups, one-wave solo blocks), and the element-granular paths (two
+// channels per lane for D = 2 mod 4, one for any D), fixed-length and packed.
 #include "cconv_bwd_body.hpp"
 
 namespace cconv {
@@ -48,16 +48,16 @@ hipError_t launch_lin(int W, dim3 grid, dim3 block, size_t lds, const BwdArgs& a
     }
 }
 
-// element-granular D: one channel per lane, 16-row groups, the general kernel, plain loads and
-// stores
-template <bool VL>
+// element-granular D: one or two channels per lane, 16-row groups, the general kernel, plain
+// loads and stores
+template <int VEC, bool VL>
 hipError_t launch_narrow(int W, bool lin, dim3 grid, dim3 block, size_t lds, const BwdArgs& a, hipStream_t s) {
     constexpr int F = kNarrowOptions;
     switch (W) {
 #define CCONV_NARROW(w)                                                                            \
     case w:                                                                                        \
-        return lin ? launch_k<1, 16, w, F | kLinear, VL, false>(grid, block, lds, a, s)           \
-                   : launch_k<1, 16, w, F, VL, false>(grid, block, lds, a, s);
+        return lin ? launch_k<VEC, 16, w, F | kLinear, VL, false>(grid, block, lds, a, s)         \
+                   : launch_k<VEC, 16, w, F, VL, false>(grid, block, lds, a, s);
         CCONV_NARROW(1)
         CCONV_NARROW(2)
         CCONV_NARROW(3)
@@ -73,7 +73,7 @@ bool bwd_launch_exists(int vec, int group, int options, bool packed) {
     if (!bwd_variant_exists(vec, group) || options < 0) return false;
     if (options & ~(kSolo | kLinear | kNtLoad | kNtStore | kPrefetch)) return false;
     const int base = options & ~(kSolo | kLinear);
-    if (vec == 1) return !(options & kSolo) && base == kNarrowOptions;
+    if (vec <= 2) return !(options & kSolo) && base == kNarrowOptions;
     if (!(options & kLinear)) return packed ? base == kVarlenBwdOptions : true;
     return vec == 4 && group == 16 && (options & kSolo) && base == kVarlenBwdOptions;
 }
@@ -84,9 +84,12 @@ hipError_t launch_bwd_extra(const Plan& p, int W, const BwdArgs& a, hipStream_t 
     const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
     const size_t lds = static_cast<size_t>(p.waves) * p.vec * kWave * sizeof(float);
     const bool solo = (p.options & kSolo) != 0;
-    if (p.vec == 1) {
+    if (p.vec <= 2) {
         const bool lin = (p.options & kLinear) != 0;
-        return vl ? launch_narrow<true>(W, lin, grid, block, lds, a, s) : launch_narrow<false>(W, lin, grid, block, lds, a, s);
+        if (p.vec == 2)
+            return vl ? launch_narrow<2, true>(W, lin, grid, block, lds, a, s)
+                      : launch_narrow<2, false>(W, lin, grid, block, lds, a, s);
+        return vl ? launch_narrow<1, true>(W, lin, grid, block, lds, a, s) : launch_narrow<1, false>(W, lin, grid, block, lds, a, s);
     }
     if (p.options & kLinear)
         return vl ? launch_lin<true>(W, grid, block, lds, a, s) : launch_lin<false>(W, grid, block, lds, a, s);

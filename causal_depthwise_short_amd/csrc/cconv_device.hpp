@@ -2,8 +2,9 @@
 //
 // Data movement is in whole rows of a lane's VEC contiguous channels: one 16-byte (VEC = 8)
 // or 8-byte (VEC = 4) global load or store per row, so a wave64 moves 1 KB (or 512 B) of a
-// bf16 row per instruction, fully coalesced. VEC = 1 (2 bytes per lane) serves any D and any
-// row alignment. bf16 values stay packed two to a dword until
+// bf16 row per instruction, fully coalesced. VEC = 2 (4 bytes per lane) serves rows that are
+// only 4-byte aligned (D = 2 mod 4), VEC = 1 (2 bytes per lane) any D and any row alignment.
+// bf16 values stay packed two to a dword until
 // they are used; widening is a shift or a mask, narrowing is gfx950's packed
 // round-to-nearest-even convert (v_cvt_pk_bf16_f32).
 #pragma once
@@ -33,13 +34,20 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // NT selects non-temporal loads/stores (streamed data that is not re-read soon).
 template <int VEC, bool NT = false>
 __device__ __forceinline__ Row<VEC> load_row(const uint16_t* __restrict__ p) {
-    static_assert(VEC == 1 || VEC == 4 || VEC == 8, "VEC is 1, 4 or 8");
+    static_assert(VEC == 1 || VEC == 2 || VEC == 4 || VEC == 8, "VEC is 1, 2, 4 or 8");
     Row<VEC> r;
     if constexpr (VEC == 1) {
         if constexpr (NT) {
             r.u[0] = __builtin_nontemporal_load(p);
         } else {
             r.u[0] = *p;
+        }
+    } else if constexpr (VEC == 2) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+        if constexpr (NT) {
+            r.u[0] = __builtin_nontemporal_load(q);
+        } else {
+            r.u[0] = *q;
         }
     } else if constexpr (VEC == 8) {
         u32x4 v;
@@ -82,6 +90,13 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ p, const Row<VE
         } else {
             *p = v;
         }
+    } else if constexpr (VEC == 2) {
+        uint32_t* q = reinterpret_cast<uint32_t*>(p);
+        if constexpr (NT) {
+            __builtin_nontemporal_store(r.u[0], q);
+        } else {
+            *q = r.u[0];
+        }
     } else if constexpr (VEC == 8) {
         const u32x4 v = {r.u[0], r.u[1], r.u[2], r.u[3]};
         if constexpr (NT) {
@@ -110,9 +125,9 @@ constexpr int kSolo = 8;      // one-wave blocks, one wave per SIMD, whole regis
 // register moves than the latency they hide).
 constexpr int kVarlenFwdOptions = kNtLoad | kNtStore;
 constexpr int kVarlenBwdOptions = kNtLoad | kNtStore;
-// The element-granular path (D not a multiple of 8) is compiled with plain loads and stores:
-// its rows never start on a 128-byte cache line, and non-temporal hints then keep the L2 from
-// merging the lines two neighbouring strips share.
+// The element-granular paths (one or two channels per lane: D not a multiple of 4) are
+// compiled with plain loads and stores: their rows never start on a 128-byte cache line, and
+// non-temporal hints then keep the L2 from merging the lines two neighbouring strips share.
 constexpr int kNarrowOptions = 0;
 // Epilogue variants (compile-time, default launch only): no activation (y = z, g = dy), and a
 // residual added to the forward's output after the activation.

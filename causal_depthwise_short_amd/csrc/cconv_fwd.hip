@@ -41,11 +41,11 @@ hipError_t launch_fwd_w(int W, int F, dim3 grid, dim3 block, const FwdArgs& a, h
 
 bool fwd_variant_exists(int vec, int group) {
     return (vec == 8 && (group == 4 || group == 8)) || (vec == 4 && (group == 4 || group == 8 || group == 16)) ||
-           (vec == 1 && group == 16);
+           ((vec == 1 || vec == 2) && group == 16);
 }
 
 hipError_t launch_fwd(const Plan& p, int W, const FwdArgs& a, hipStream_t s) {
-    if (a.cu || p.vec == 1 || (p.options & (kLinear | kResidual))) return launch_fwd_extra(p, W, a, s);
+    if (a.cu || p.vec <= 2 || (p.options & (kLinear | kResidual))) return launch_fwd_extra(p, W, a, s);
     const dim3 grid(static_cast<uint32_t>(p.blocks)), block(static_cast<uint32_t>(p.waves * kWave));
     const int F = p.options;
     if (p.vec == 8) {

@@ -1,7 +1,7 @@
 // cconv_fwd_extra.hip -- the forward's packed-batch kernels (every (vec, group) pair, streaming
 // options), its epilogue variants (no activation, residual; the default launch only: 4
-// channels per lane, 16-row groups, one-wave solo blocks), and the element-granular path (one
-// channel per lane, for D not a multiple of 8), fixed-length and packed.
+// channels per lane, 16-row groups, one-wave solo blocks), and the element-granular paths (two
+// channels per lane for D = 2 mod 4, one for any D), fixed-length and packed.
 #include "cconv_fwd_body.hpp"
 
 namespace cconv {
@@ -58,27 +58,27 @@ hipError_t launch_epi(int W, int epi, dim3 grid, dim3 block, const FwdArgs& a, h
     }
 }
 
-// element-granular D: one channel per lane, 16-row groups, the general kernel, plain loads and
-// stores, every epilogue, fixed-length or packed
-template <int W, bool VL>
+// element-granular D: one or two channels per lane, 16-row groups, the general kernel, plain
+// loads and stores, every epilogue, fixed-length or packed
+template <int VEC, int W, bool VL>
 hipError_t launch_narrow_w(int epi, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
     constexpr int B0 = kNarrowOptions;
     switch (epi) {
-        case 0: return launch_k<1, 16, W, B0, VL, false>(grid, block, a, s);
-        case kLinear: return launch_k<1, 16, W, B0 | kLinear, VL, false>(grid, block, a, s);
-        case kResidual: return launch_k<1, 16, W, B0 | kResidual, VL, false>(grid, block, a, s);
-        case kLinear | kResidual: return launch_k<1, 16, W, B0 | kLinear | kResidual, VL, false>(grid, block, a, s);
+        case 0: return launch_k<VEC, 16, W, B0, VL, false>(grid, block, a, s);
+        case kLinear: return launch_k<VEC, 16, W, B0 | kLinear, VL, false>(grid, block, a, s);
+        case kResidual: return launch_k<VEC, 16, W, B0 | kResidual, VL, false>(grid, block, a, s);
+        case kLinear | kResidual: return launch_k<VEC, 16, W, B0 | kLinear | kResidual, VL, false>(grid, block, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool VL>
+template <int VEC, bool VL>
 hipError_t launch_narrow(int W, int epi, dim3 grid, dim3 block, const FwdArgs& a, hipStream_t s) {
     switch (W) {
-        case 1: return launch_narrow_w<1, VL>(epi, grid, block, a, s);
-        case 2: return launch_narrow_w<2, VL>(epi, grid, block, a, s);
-        case 3: return launch_narrow_w<3, VL>(epi, grid, block, a, s);
-        case 4: return launch_narrow_w<4, VL>(epi, grid, block, a, s);
+        case 1: return launch_narrow_w<VEC, 1, VL>(epi, grid, block, a, s);
+        case 2: return launch_narrow_w<VEC, 2, VL>(epi, grid, block, a, s);
+        case 3: return launch_narrow_w<VEC, 3, VL>(epi, grid, block, a, s);
+        case 4: return launch_narrow_w<VEC, 4, VL>(epi, grid, block, a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -90,7 +90,7 @@ bool fwd_launch_exists(int vec, int group, int options, bool packed) {
     const int epi = options & (kLinear | kResidual);
     const int base = options & ~(kSolo | kLinear | kResidual);
     if (options & ~(kSolo | kLinear | kResidual | kNtLoad | kNtStore | kPrefetch)) return false;
-    if (vec == 1) return !(options & kSolo) && base == kNarrowOptions;
+    if (vec <= 2) return !(options & kSolo) && base == kNarrowOptions;
     if (epi == 0) return packed ? base == kVarlenFwdOptions : true;
     return vec == 4 && group == 16 && (options & kSolo) && base == kVarlenFwdOptions;
 }
@@ -102,7 +102,9 @@ hipError_t launch_fwd_extra(const Plan& p, int W, const FwdArgs& a, hipStream_t 
     const int epi = p.options & (kLinear | kResidual);
     const bool solo = (p.options & kSolo) != 0;
     if (p.vec == 1)
-        return vl ? launch_narrow<true>(W, epi, grid, block, a, s) : launch_narrow<false>(W, epi, grid, block, a, s);
+        return vl ? launch_narrow<1, true>(W, epi, grid, block, a, s) : launch_narrow<1, false>(W, epi, grid, block, a, s);
+    if (p.vec == 2)
+        return vl ? launch_narrow<2, true>(W, epi, grid, block, a, s) : launch_narrow<2, false>(W, epi, grid, block, a, s);
     if (epi) return vl ? launch_epi<true>(W, epi, grid, block, a, s) : launch_epi<false>(W, epi, grid, block, a, s);
     if (p.vec == 8) {
         if (p.group == 4) return launch_vl<8, 4>(W, solo, grid, block, a, s);

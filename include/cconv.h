@@ -34,17 +34,19 @@
  *    training calls (forward and backward, every variant) also run 4 channels per lane when
  *    D = 4 (mod 8), their default then: the bf16 activations (x, dy, y, dx, residual) 8-byte
  *    aligned with strides that are multiples of 4, the taps, bias, dw, dbias and states with
- *    element alignment (they are read and written per element). Any other D (the
- *    element-granular path [strip.py's masked loads handle any D]: one channel per lane)
- *    needs only element alignment (2 bytes for bf16, 4 for fp32) and strides >= D; an
- *    explicit configuration with vec = 1 takes that path for any D. When D = 4 (mod 8) and
- *    the activations miss the 8-byte rule, the default plan runs one channel per lane too,
- *    with the segments (so the dw/dbias partials and the workspace) of the 4-channel plan;
- *    an explicit vec = 4 configuration is checked against the rule. The decode update runs 8
+ *    element alignment (they are read and written per element). When D = 2 (mod 4) they run
+ *    2 channels per lane by default, the activations then 4-byte aligned with even strides.
+ *    Any other D (the element-granular path [strip.py's masked loads handle any D]: one
+ *    channel per lane) needs only element alignment (2 bytes for bf16, 4 for fp32) and
+ *    strides >= D; an explicit configuration with vec = 1 takes that path for any D. When
+ *    D = 4 (mod 8) or D = 2 (mod 4) and the activations miss the rule of that lane width,
+ *    the default plan runs one channel per lane too, with the segments (so the dw/dbias
+ *    partials and the workspace) of the wider plan; an explicit vec = 4 or vec = 2
+ *    configuration is checked against its rule. The decode update runs 8
  *    channels per lane when D is a multiple of 8 and one otherwise, taking compact rows
  *    (x_ld == D) or a row stride that is a multiple of 8 [the decode PR's row-stride
- *    contract]. The element-granular path runs with plain loads and stores only (options 0;
- *    its default configuration: 1 channel per lane, 16-row groups, one-wave blocks); a
+ *    contract]. The element-granular paths (1 or 2 channels per lane) run with plain loads
+ *    and stores only (options 0; 16-row groups, one-wave blocks by default); a
  *    configuration whose vec does not divide D is CCONV_ERR_BAD_CONFIG. The alignments
  *    stated below are those of the vector path with D a multiple of 8.
  *  - Errors fail closed. A problem visible on the host returns its code before anything is
@@ -417,8 +419,9 @@ const char* cconv_version(void);
  * entry points above pick one from a static table; these take it explicitly. y and dx do
  * not depend on the configuration (bitwise); dw and dbias depend on it only through the
  * order of their fixed-order sum.
- *   vec              channels per lane: 4 or 8 (8 or 16 bytes per row per lane); 1 (2 bytes)
- *                    on the element-granular path, where it is the only choice
+ *   vec              channels per lane: 4 or 8 (8 or 16 bytes per row per lane); 2 (4 bytes)
+ *                    or 1 (2 bytes) on the element-granular paths (16-row groups, plain
+ *                    loads and stores, the general kernel: options 0)
  *   rows_per_group   rows whose loads are issued together: 4 or 8 (and 16 with vec 4)
  *   waves_per_block  1, 2, 4 or 8 waves per block
  *   strips_per_block a divisor of waves_per_block: the block's waves cover this many
@@ -445,9 +448,10 @@ typedef struct {
 
 /*
  * The configuration cconv_fwd (which = 0) or cconv_bwd (which = 1) uses for this shape: 4
- * channels per lane (1 when D % 4 != 0), 16-row groups, one-wave blocks, each batch row cut
- * into as many segments as the wave slots hold (1024 waves, one per SIMD; 3072 for the
- * forward and 2048 for the backward on the element-granular path), down to one 16-row group;
+ * channels per lane (2 when D % 4 == 2, 1 for odd D), 16-row groups, one-wave blocks, each
+ * batch row cut into as many segments as the wave slots hold (1024 waves, one per SIMD; 2048
+ * with 2 channels per lane; 3072 for the forward and 2048 for the backward with one), down
+ * to one 16-row group;
  * non-temporal hints (options 11) when 2D is a multiple of 128 or the call streams at most
  * 256 MB, plain loads and stores (options 8; 0 on the element-granular path) otherwise.
  * Packed batches and the epilogue variants use the same plan with the streaming hints. The

@@ -1,6 +1,6 @@
 """GPU parity for channel counts that are not multiples of 8, for every entry point, against
-the oracle, through the C ABI: the element-granular path (one channel per lane, D not a
-multiple of 4) and, for the training calls, the 4-channel lanes that D = 4 (mod 8) takes
+the oracle, through the C ABI: the element-granular paths (one channel per lane for odd D, two
+for D = 2 mod 4) and, for the training calls, the 4-channel lanes that D = 4 (mod 8) takes
 (D = 100 and 4100 below). Tolerances in parity.py; states bit for bit.
 """
 
@@ -38,7 +38,7 @@ def _check_train(x, dy, w, b, h0, what, *, config_f=None, config_b=None):
         assert_close(dh0.cpu(), dh0r, TOL_BWD, f"{what} d_init_state")
 
 
-@pytest.mark.parametrize("D", [1, 7, 100, 1003])
+@pytest.mark.parametrize("D", [1, 2, 7, 100, 130, 1003])
 @pytest.mark.parametrize("W", [1, 2, 3, 4])
 def test_narrow_train_parity(D, W):
     inp = si.train_inputs(2, 300, D, W, bias=True, seed=800 + D + W)
@@ -110,10 +110,10 @@ def test_narrow_launch_invariance(i):
     assert_close(dw.cpu(), ref_dw.cpu(), 1e-4, "narrow dw across launches")
 
 
-@pytest.mark.parametrize("D", [77, 100])
+@pytest.mark.parametrize("D", [77, 78, 100])
 def test_narrow_packed_and_epilogue(D):
-    """Packed batches and the epilogue variants at D = 77 (one channel per lane) and D = 100
-    (4 channels per lane)."""
+    """Packed batches and the epilogue variants at D = 77 (one channel per lane), D = 78 (two)
+    and D = 100 (4 channels per lane)."""
     lens = [100, 0, 1, 3, 250]
     W = 4
     total = sum(lens)
@@ -171,10 +171,10 @@ def test_narrow_decode(D, ld_pad):
     assert_close(y4.cpu(), yr4, TOL_FWD, f"circular decode D{D}")
 
 
-@pytest.mark.parametrize("D", [45, 60])
+@pytest.mark.parametrize("D", [45, 46, 60])
 def test_narrow_pool(D):
-    """The prefill into a decode pool at D = 45 (one channel per lane) and D = 60 (4 channels
-    per lane)."""
+    """The prefill into a decode pool at D = 45 (one channel per lane), D = 46 (two) and D = 60
+    (4 channels per lane)."""
     B, T, W, S = 3, 90, 4, 7
     inp = si.train_inputs(B, T, D, W, bias=True, seed=870)
     state = torch.randn(S, D, W - 1, generator=torch.Generator().manual_seed(871)).to(torch.bfloat16)
@@ -222,3 +222,46 @@ def test_four_channel_lanes_d_4_mod_8(D, W):
     assert torch.equal(bits(y), bits(y1)) and torch.equal(bits(dx), bits(dx1))
     # fp32 partial sums grouped per launch: rounding-order differences only
     assert_close(dw.cpu(), dw1.cpu(), 1e-4, f"D{D} W{W} dw across lane widths")
+
+
+@pytest.mark.parametrize("D", [2, 1002, 4098])
+@pytest.mark.parametrize("W", [1, 4])
+def test_two_channel_lanes_d_2_mod_4(D, W):
+    """D = 2 (mod 4) runs 2 channels per lane: x and dy as 4-byte aligned column slices of
+    wider tensors (row stride D + 2), y and dx into guarded buffers, a ragged last strip and
+    segment; against the oracle, and y and dx equal to the one-channel plan's bit for bit."""
+    B, T = 2, 1000
+    assert cc.cconv_default_config("fwd", B, T, D, W).vec == 2
+    assert cc.cconv_default_config("bwd", B, T, D, W).vec == 2
+    big = si.train_inputs(B, T, D + 2, W, bias=True, seed=880 + D + W)
+    x = big["x"][:, :, 2:2 + D]
+    dy = big["dy"][:, :, 2:2 + D]
+    w, b = big["w"][:D].contiguous(), big["bias"][:D].contiguous()
+    xd, dyd = _g(big["x"])[:, :, 2:2 + D], _g(big["dy"])[:, :, 2:2 + D]
+    wd, bd = _g(w), _g(b)
+    y, ybuf, ylo, yhi = guarded((B, T, D), torch.bfloat16, DEV)
+    dx, xbuf, xlo, xhi = guarded((B, T, D), torch.bfloat16, DEV)
+    cc.cconv_fwd(xd, wd, bd, y=y)
+    _, dw, db = cc.cconv_bwd(xd, dyd, wd, bd, dx=dx, dw_dtype=torch.float32)
+    one = cc.Config(vec=1, rows_per_group=16, waves_per_block=1, options=0, seg_rows=64)
+    y1 = cc.cconv_fwd(xd, wd, bd, config=one)
+    dx1, dw1, _ = cc.cconv_bwd(xd, dyd, wd, bd, config=one, dw_dtype=torch.float32)
+    # off the 4-byte rule (x and dy at odd element offsets): the default plan takes one channel
+    # per lane, the same values
+    xo, dyo = _g(big["x"])[:, :, 1:1 + D], _g(big["dy"])[:, :, 1:1 + D]
+    yo = cc.cconv_fwd(xo, wd, bd)
+    dxo, _, _ = cc.cconv_bwd(xo, dyo, wd, bd)
+    torch.cuda.synchronize()
+    assert canaries_intact(ybuf, ylo, yhi) and canaries_intact(xbuf, xlo, xhi)
+    _, yr = oracle.fwd(x.contiguous(), w, b)
+    dxr, dwr, dbr = oracle.bwd(x.contiguous(), dy.contiguous(), w, b)
+    assert_close(y.cpu(), yr, TOL_FWD, f"D{D} W{W} y")
+    assert_close(dx.cpu(), dxr, TOL_BWD, f"D{D} W{W} dx")
+    assert_close(dw.cpu(), dwr, TOL_BWD, f"D{D} W{W} dw")
+    assert_close(db.cpu(), dbr, TOL_BWD, f"D{D} W{W} dbias")
+    assert torch.equal(bits(y), bits(y1)) and torch.equal(bits(dx), bits(dx1))
+    assert_close(dw.cpu(), dw1.cpu(), 1e-4, f"D{D} W{W} dw across lane widths")
+    _, yro = oracle.fwd(big["x"][:, :, 1:1 + D].contiguous(), w, b)
+    dxro, _, _ = oracle.bwd(big["x"][:, :, 1:1 + D].contiguous(), big["dy"][:, :, 1:1 + D].contiguous(), w, b)
+    assert_close(yo.cpu(), yro, TOL_FWD, f"D{D} W{W} y off the 4-byte rule")
+    assert_close(dxo.cpu(), dxro, TOL_BWD, f"D{D} W{W} dx off the 4-byte rule")
