@@ -56,6 +56,8 @@ constexpr int64_t kMaxDecodeRows = int64_t(1) << 24;  // N
 constexpr int64_t kMaxChannels = int64_t(1) << 30;    // D: lane channel offsets are 32-bit
 // S with state_indices: the slot check's S-bit set and its verdict word fill at most 64 KB of LDS
 constexpr int64_t kMaxIndexedSlots = (int64_t(1) << 19) - 32;
+// LDS of a decode block with staged state runs (the slot check's words plus the regions)
+constexpr size_t kMaxUpdateLds = size_t(64) << 10;
 constexpr int64_t kMaxSequences = int64_t(1) << 24;     // packed sequences per call
 constexpr int64_t kTargetWaves = 1024;  // wave slots of the solo kernels: one per SIMD (256 CUs x 4 SIMDs)
 // wave slots of the narrow path (one channel per lane): three waves per SIMD for the forward,
@@ -82,9 +84,13 @@ constexpr int64_t kMaxDecodeChannels = int64_t(1) << 26;
 // Decode launch (kernel-trace sweeps of block size x rows per thread x channels per thread x
 // store hints at N = 256, D = 4096, W = 4, from HBM: 256-thread blocks, two rows per thread,
 // 8 channels per thread and non-temporal stores took 5.3 us per call, the other 33 shapes
-// 5.3-8.0 us; non-temporal loads and 4-channel threads did not help)
+// 5.3-8.0 us; non-temporal loads and 4-channel threads did not help). With 8 channels per
+// thread the state runs also pass through LDS (contiguous loads and stores): 5.53 -> 5.33 us
+// a call in graph replays from HBM (the 16*L-byte lane stride had kept the texture
+// addresser's queues full). Without room in LDS (a very large S) the plan drops that bit.
 constexpr int64_t kUpdateThreads = 256;
 constexpr int kUpdateOptions = cconv::kUpdNtStore;
+constexpr int kUpdateOptions8 = cconv::kUpdNtStore | cconv::kUpdStaged;
 constexpr int64_t kUpdateRowsPerThread = 2;
 constexpr int kUpdateVec8 = 8;  // channels per thread when D % 8 == 0
 
@@ -652,7 +658,7 @@ cconv_update_config_t update_config_for(int64_t N, int64_t D, int vec) {
     c.rows_per_thread = 1;
     c.options = 0;
     if (c.vec > 1) {
-        c.options = kUpdateOptions;
+        c.options = c.vec == 8 ? kUpdateOptions8 : kUpdateOptions;
         c.rows_per_thread = static_cast<int>(kUpdateRowsPerThread);
         c.rows_per_block = ((c.rows_per_block + c.rows_per_thread - 1) / c.rows_per_thread) * c.rows_per_thread;
         c.block_threads = std::min(c.block_threads, cconv::update_max_threads(c.rows_per_thread));
@@ -720,7 +726,8 @@ cconv_status_t update_impl(const void* x, int64_t x_ld, void* state, int64_t S, 
         if (c.vec == 4 && !quad_ok) c = update_config_for(N, D, 1);  // operands off the 4-channel rule
     }
     if (c.block_threads < 64 || c.block_threads > 1024 || c.block_threads % 64 != 0 || c.rows_per_block < 1 ||
-        c.rows_per_block > kMaxDecodeRows || c.options < 0 || c.options > 1 ||
+        c.rows_per_block > kMaxDecodeRows || c.options < 0 || c.options > 5 ||
+        ((c.options & cconv::kUpdStaged) && (c.vec != 8 || (c.options & cconv::kUpdNtLoad))) ||
         (c.rows_per_thread != 1 && c.rows_per_thread != 2) || c.block_threads > cconv::update_max_threads(c.rows_per_thread) ||
         (c.vec != 1 && c.vec != 4 && c.vec != 8) || D % c.vec != 0 || (c.vec == 4 && x_ld % 4 != 0) ||
         (c.vec == 1 && (c.options != 0 || c.rows_per_thread != 1)))
@@ -734,8 +741,20 @@ cconv_status_t update_impl(const void* x, int64_t x_ld, void* state, int64_t S, 
     const int64_t grid_x = (dv + c.block_threads - 1) / c.block_threads;
     const int64_t grid_y = (N + c.rows_per_block - 1) / c.rows_per_block;
     if (grid_x > INT32_MAX || grid_y > 65535) return CCONV_ERR_BAD_CONFIG;
-    // the slot check's bit set and verdict word (a verdict word alone for cache_seqlens only)
-    const size_t lds = state_indices ? static_cast<size_t>((S + 31) / 32 + 1) * 4 : (cache_seqlens ? 4 : 0);
+    // the slot check's bit set and verdict word (a verdict word alone for cache_seqlens only),
+    // then, when staged, one region of 64 * L 16-byte chunks per wave
+    const int64_t words = state_indices ? (S + 31) / 32 + 1 : (cache_seqlens ? 1 : 0);
+    size_t lds = static_cast<size_t>(words) * 4;
+    if ((c.options & cconv::kUpdStaged) && L > 0) {
+        const size_t staged = static_cast<size_t>((words + 3) & ~int64_t(3)) * 4 +
+                              static_cast<size_t>(c.block_threads / cconv::kWave) * cconv::kWave * 16 * L;
+        if (staged <= kMaxUpdateLds)
+            lds = staged;
+        else if (cfg)
+            return CCONV_ERR_BAD_CONFIG;
+        else
+            c.options &= ~cconv::kUpdStaged;  // the default plan without the staging
+    }
     cconv::UpdateArgs a;
     a.x = static_cast<const uint16_t*>(x);
     a.x_ld = x_ld;

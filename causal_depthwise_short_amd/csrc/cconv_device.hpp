@@ -133,8 +133,15 @@ constexpr int kNarrowOptions = 0;
 // residual added to the forward's output after the activation.
 constexpr int kLinear = 16;
 constexpr int kResidual = 32;
-// Option bit of the decode update: non-temporal stores of y and the state.
+// Option bits of the decode update: non-temporal stores of y and the state; non-temporal loads
+// of x and the state.
 constexpr int kUpdNtStore = 1;
+constexpr int kUpdNtLoad = 2;
+// Option bit of the decode update (8 channels per thread): the state runs move between memory
+// and registers through the wave's LDS region, so that every load and store instruction covers
+// contiguous bytes (lane i takes 16-byte chunk q*64 + i of the wave's run) instead of 16 bytes
+// at a 16*L-byte lane stride.
+constexpr int kUpdStaged = 4;
 
 // The wave's index in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }

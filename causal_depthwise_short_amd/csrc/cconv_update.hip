@@ -225,7 +225,7 @@ __device__ __forceinline__ void dec_take_slots(const RowSlots& r, int64_t n, int
 
 // Issue the gathers of row n: the x row and the slot's state run (empty ranges for a row past
 // the block's end and for a slot outside [0, S)).
-template <int VEC, int L, bool NTL>
+template <int VEC, int L, bool NTL, bool STG = false>
 __device__ __forceinline__ void dec_gather(const UpdateArgs& a, int64_t n, int64_t d, DecIn<VEC, (L > 0 ? L : 1)>& in) {
     constexpr int LL = L > 0 ? L : 1;
     const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (in.valid ? n : 0) * a.x_ld, in.valid ? a.D * 2 : 0);
@@ -240,7 +240,14 @@ __device__ __forceinline__ void dec_gather(const UpdateArgs& a, int64_t n, int64
     if constexpr (L > 0) {
         const __amdgpu_buffer_rsrc_t rs = state_rsrc<L>(a, in.s);
         const uint32_t os = static_cast<uint32_t>(d * L * 2);
-        if constexpr (VEC >= 4) {
+        if constexpr (STG) {
+            // the wave's run, chunk q*64 + lane in this lane (stage_in puts the lane's own
+            // chunks in place once they have landed)
+            const uint32_t lane = threadIdx.x % kWave;
+            const uint32_t wb = os - lane * (VEC * L * 2);
+#pragma unroll
+            for (int q = 0; q < L; ++q) bload_chunk<VEC, NTL>(rs, wb + (q * kWave + lane) * 16, &in.h[4 * q]);
+        } else if constexpr (VEC >= 4) {
             // the run is L chunks of VEC values (chunk q: flat entries q*VEC .. q*VEC+VEC-1)
 #pragma unroll
             for (int q = 0; q < L; ++q) bload_chunk<VEC, NTL>(rs, os + VEC * 2 * q, &in.h[(VEC / 2) * q]);
@@ -252,13 +259,38 @@ __device__ __forceinline__ void dec_gather(const UpdateArgs& a, int64_t n, int64
 }
 
 // The loads of rows n .. n+R-1 (those before `end` exist): slots, then gathers.
-template <int VEC, int L, bool CIRC, bool IDX, bool NTL, int R>
+template <int VEC, int L, bool CIRC, bool IDX, bool NTL, int R, bool STG = false>
 __device__ __forceinline__ void dec_load(const UpdateArgs& a, const int32_t* __restrict__ idx,
                                          const int32_t* __restrict__ cs, int64_t n, int64_t end, int64_t d,
                                          DecIn<VEC, (L > 0 ? L : 1)> (&in)[R]) {
     dec_take_slots<CIRC, IDX, R>(dec_slots<CIRC, IDX, R>(idx, cs, n, end), n, end, in);
 #pragma unroll
-    for (int i = 0; i < R; ++i) dec_gather<VEC, L, NTL>(a, n + i, d, in[i]);
+    for (int i = 0; i < R; ++i) dec_gather<VEC, L, NTL, STG>(a, n + i, d, in[i]);
+}
+
+// The wave's LDS staging region: 64 * L 16-byte chunks. Only this wave touches it; the
+// fences order its LDS writes before the reads of other lanes of the same wave, and those
+// reads before the region's next writes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Chunk-major (chunk q*64 + lane in this lane's h[4q..4q+3]) -> lane-major (the lane's own
+// run, chunk k in h[4k..4k+3]).
+template <int L, int NH>
+__device__ __forceinline__ void stage_in(u32x4* __restrict__ stg, uint32_t (&h)[NH]) {
+    const uint32_t lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int q = 0; q < L; ++q) stg[q * kWave + lane] = u32x4{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const u32x4 v = stg[lane * L + k];
+        h[4 * k] = v.x, h[4 * k + 1] = v.y, h[4 * k + 2] = v.z, h[4 * k + 3] = v.w;
+    }
+    wave_lds_sync();
 }
 
 // The tokens 1 .. W-1 steps back, from the L state entries, in the forward's ring order:
@@ -280,7 +312,7 @@ __device__ __forceinline__ void ring_from_state(const uint32_t (&h)[NH], float (
 // by entry (shift) or the one changed entry (circular).
 template <int VEC, int L, int ROT, bool NTS, int NH>
 __device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t rs, uint32_t os, const uint32_t (&h)[NH],
-                                            const Row<VEC>& rx) {
+                                            const Row<VEC>& rx, u32x4* __restrict__ stg = nullptr) {
     if constexpr (VEC >= 4) {
         uint32_t nu[(VEC / 2) * L];
 #pragma unroll
@@ -293,6 +325,25 @@ __device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t rs, uint32_t 
                 half[j] = tok ? half_at(rx.u, v) : half_at(h, ROT < 0 ? p + 1 : p);
             }
             nu[i] = half[0] | (half[1] << 16);
+        }
+        if constexpr (VEC == 8) {
+            if (stg) {
+                // lane-major -> chunk-major through the wave's region: lane i stores chunk
+                // q*64 + i of the wave's run
+                const uint32_t lane = threadIdx.x % kWave;
+                const uint32_t wb = os - lane * (VEC * L * 2);
+#pragma unroll
+                for (int k = 0; k < L; ++k) stg[lane * L + k] = u32x4{nu[4 * k], nu[4 * k + 1], nu[4 * k + 2], nu[4 * k + 3]};
+                wave_lds_sync();
+#pragma unroll
+                for (int q = 0; q < L; ++q) {
+                    const u32x4 v = stg[q * kWave + lane];
+                    const uint32_t c[4] = {v.x, v.y, v.z, v.w};
+                    bstore_chunk<8, NTS>(rs, wb + (q * kWave + lane) * 16, c);
+                }
+                wave_lds_sync();
+                return;
+            }
         }
 #pragma unroll
         for (int q = 0; q < L; ++q) bstore_chunk<VEC, NTS>(rs, os + VEC * 2 * q, &nu[(VEC / 2) * q]);
@@ -309,7 +360,8 @@ __device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t rs, uint32_t 
 // y = 0 and, its state range being empty, no state.
 template <int W, int L, int VEC, bool NTS, int ROT>
 __device__ __forceinline__ void dec_finish(const UpdateArgs& a, const float (&tap)[W][VEC], const float (&bs)[VEC],
-                                           const DecIn<VEC, (L > 0 ? L : 1)>& in, int64_t n, int64_t d) {
+                                           const DecIn<VEC, (L > 0 ? L : 1)>& in, int64_t n, int64_t d,
+                                           u32x4* __restrict__ stg) {
     constexpr int R = W > 1 ? W - 1 : 1;
     float xt[VEC];
     widen(in.rx, xt);
@@ -335,21 +387,24 @@ __device__ __forceinline__ void dec_finish(const UpdateArgs& a, const float (&ta
     } else {
         bstore2<NTS>(rr, oy, ry.u[0]);
     }
-    if constexpr (L > 0) store_state<VEC, L, ROT, NTS>(state_rsrc<L>(a, in.s), static_cast<uint32_t>(d * L * 2), in.h, in.rx);
+    if constexpr (L > 0)
+        store_state<VEC, L, ROT, NTS>(state_rsrc<L>(a, in.s), static_cast<uint32_t>(d * L * 2), in.h, in.rx, stg);
 }
 
-template <int W, int L, bool CIRC, int VEC, bool NTS>
+template <int W, int L, bool CIRC, int VEC, bool NTS, bool STG = false>
 __device__ __forceinline__ void dec_row(const UpdateArgs& a, const float (&tap)[W][VEC], const float (&bs)[VEC],
-                                        const DecIn<VEC, (L > 0 ? L : 1)>& in, int64_t n, int64_t d) {
+                                        DecIn<VEC, (L > 0 ? L : 1)>& in, int64_t n, int64_t d, u32x4* __restrict__ stg) {
+    if constexpr (STG && L > 0) stage_in<L>(stg, in.h);
+    u32x4* const sp = STG ? stg : nullptr;
     if constexpr (!CIRC || L == 0) {
-        dec_finish<W, L, VEC, NTS, -1>(a, tap, bs, in, n, d);
+        dec_finish<W, L, VEC, NTS, -1>(a, tap, bs, in, n, d, sp);
     } else {
         // the rotation is block-uniform: a uniform switch picks a compile-time entry map
         const int rot = static_cast<int>(in.c % L);
-        if (rot == 0) dec_finish<W, L, VEC, NTS, 0>(a, tap, bs, in, n, d);
-        if constexpr (L > 1) if (rot == 1) dec_finish<W, L, VEC, NTS, (L > 1 ? 1 : 0)>(a, tap, bs, in, n, d);
-        if constexpr (L > 2) if (rot == 2) dec_finish<W, L, VEC, NTS, (L > 2 ? 2 : 0)>(a, tap, bs, in, n, d);
-        if constexpr (L > 3) if (rot == 3) dec_finish<W, L, VEC, NTS, (L > 3 ? 3 : 0)>(a, tap, bs, in, n, d);
+        if (rot == 0) dec_finish<W, L, VEC, NTS, 0>(a, tap, bs, in, n, d, sp);
+        if constexpr (L > 1) if (rot == 1) dec_finish<W, L, VEC, NTS, (L > 1 ? 1 : 0)>(a, tap, bs, in, n, d, sp);
+        if constexpr (L > 2) if (rot == 2) dec_finish<W, L, VEC, NTS, (L > 2 ? 2 : 0)>(a, tap, bs, in, n, d, sp);
+        if constexpr (L > 3) if (rot == 3) dec_finish<W, L, VEC, NTS, (L > 3 ? 3 : 0)>(a, tap, bs, in, n, d, sp);
     }
 }
 
@@ -359,9 +414,16 @@ template <int W, int L, bool CIRC, int VEC, bool IDX, bool WF32, int OPT, int R>
 __global__ __launch_bounds__(update_max_threads(R)) void cconv_update_kernel(const UpdateArgs a, const int32_t* __restrict__ idx,
                                                             const int32_t* __restrict__ cs) {
     constexpr int LL = L > 0 ? L : 1;
-    constexpr bool NTS = (OPT & kUpdNtStore) != 0, NTL = false;
+    constexpr bool NTS = (OPT & kUpdNtStore) != 0, NTL = (OPT & kUpdNtLoad) != 0;
+    constexpr bool STG = (OPT & kUpdStaged) != 0 && VEC == 8 && L > 0;
     constexpr bool CHECK = IDX || CIRC;
     extern __shared__ uint32_t seen[];
+    // the staging regions follow the slot check's words, 16-byte aligned, one per wave
+    u32x4* stg = nullptr;
+    if constexpr (STG) {
+        const int64_t words = IDX ? (a.S + 31) / 32 + 1 : (CIRC ? 1 : 0);
+        stg = reinterpret_cast<u32x4*>(seen + ((words + 3) & ~int64_t(3))) + (threadIdx.x / kWave) * (kWave * LL);
+    }
 
     const int64_t d = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * VEC;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * a.rows_per_block;
@@ -384,7 +446,7 @@ __global__ __launch_bounds__(update_max_threads(R)) void cconv_update_kernel(con
     DecIn<VEC, LL> cur[R];
     dec_take_slots<CIRC, IDX, R>(rs0, n0, n1, cur);
 #pragma unroll
-    for (int i = 0; i < R; ++i) dec_gather<VEC, L, NTL>(a, n0 + i, d, cur[i]);
+    for (int i = 0; i < R; ++i) dec_gather<VEC, L, NTL, STG>(a, n0 + i, d, cur[i]);
 
     if constexpr (CHECK) {
         const bool bad = block_slots_bad(IDX ? idx : nullptr, CIRC ? cs : nullptr, a.N, a.S, seen, first);
@@ -399,9 +461,9 @@ __global__ __launch_bounds__(update_max_threads(R)) void cconv_update_kernel(con
     unpack_params<VEC, W, WF32>(prm, tap, bs);
     for (int64_t g = n0; g < n1; g += R) {
         DecIn<VEC, LL> nxt[R];
-        if (g + R < n1) dec_load<VEC, L, CIRC, IDX, NTL, R>(a, idx, cs, g + R, n1, d, nxt);
+        if (g + R < n1) dec_load<VEC, L, CIRC, IDX, NTL, R, STG>(a, idx, cs, g + R, n1, d, nxt);
 #pragma unroll
-        for (int i = 0; i < R; ++i) dec_row<W, L, CIRC, VEC, NTS>(a, tap, bs, cur[i], g + i, d);
+        for (int i = 0; i < R; ++i) dec_row<W, L, CIRC, VEC, NTS, STG>(a, tap, bs, cur[i], g + i, d, stg);
 #pragma unroll
         for (int i = 0; i < R; ++i) cur[i] = nxt[i];
     }
@@ -441,13 +503,20 @@ void launch_opt(int options, int rows_per_thread, const UpdLaunch& l, const Upda
     if constexpr (VEC == 1) {
         launch_one<W, L, CIRC, 1, IDX, WF32, 0, 1>(l, a);
     } else {
-        const bool nts = (options & kUpdNtStore) != 0;
-        if (rows_per_thread == 1)
-            nts ? launch_one<W, L, CIRC, VEC, IDX, WF32, kUpdNtStore, 1>(l, a)
-                : launch_one<W, L, CIRC, VEC, IDX, WF32, 0, 1>(l, a);
-        else
-            nts ? launch_one<W, L, CIRC, VEC, IDX, WF32, kUpdNtStore, 2>(l, a)
-                : launch_one<W, L, CIRC, VEC, IDX, WF32, 0, 2>(l, a);
+        constexpr int S = kUpdNtStore, N = kUpdNtLoad, G = kUpdStaged;
+        const bool two = rows_per_thread != 1;
+#define CCONV_UPD_OPT(o) \
+    case o: two ? launch_one<W, L, CIRC, VEC, IDX, WF32, o, 2>(l, a) : launch_one<W, L, CIRC, VEC, IDX, WF32, o, 1>(l, a); break;
+        // staging (8 channels per thread only) with or without non-temporal stores
+        switch (options & (VEC == 8 ? (S | N | G) : (S | N))) {
+            CCONV_UPD_OPT(0)
+            CCONV_UPD_OPT(S)
+            CCONV_UPD_OPT(N)
+            CCONV_UPD_OPT(S | N)
+            CCONV_UPD_OPT(G)
+            default: CCONV_UPD_OPT(G | S)
+        }
+#undef CCONV_UPD_OPT
     }
 }
 

@@ -383,7 +383,11 @@ cconv_status_t cconv_update_ex(const void* x, int64_t x_ld, void* state, int64_t
  *   rows_per_thread  rows a thread carries at once, their loads in flight together and the
  *                    taps loaded once for them: 1 or 2 (1 when vec = 1); blocks of at most
  *                    512 threads for 2 (registers)
- *   options          bit 0: non-temporal stores of y and the state (0 when vec = 1)
+ *   options          bit 0: non-temporal stores of y and the state; bit 1: non-temporal
+ *                    loads of x and the state; bit 2 (vec = 8, not with bit 1): the state
+ *                    runs pass through LDS so that each load and store instruction covers
+ *                    contiguous bytes (the block's LDS, slot check included, must stay
+ *                    within 64 KiB); 0 when vec = 1
  *   rows_per_block   rows of N each block walks (>= 1; the grid's row dimension,
  *                    ceil(N / rows_per_block), must stay <= 65535)
  * An invalid configuration is CCONV_ERR_BAD_CONFIG.
@@ -398,7 +402,9 @@ typedef struct {
 
 /* The configuration cconv_update and cconv_update_ex use for N rows of D channels (with
  * operands that meet the vec rule above; a call whose operands miss the 4-channel rule runs
- * one channel per thread). */
+ * one channel per thread): 8 channels per thread with options 5 (non-temporal stores, state
+ * runs staged through LDS; the call drops the staging when S is too large for the LDS), 4
+ * with options 1, 1 with options 0; 256-thread blocks, 2 rows per thread. */
 cconv_status_t cconv_default_update_config(int64_t N, int64_t D, cconv_update_config_t* out);
 
 /* cconv_update_ex with an explicit launch configuration (cfg must not be NULL). */

@@ -531,7 +531,10 @@ def upd_cfg(cfg, **kw):
         (dict(block_threads=32, options=0, rows_per_block=1), {}, CONFIG),
         (dict(block_threads=96, options=0, rows_per_block=1), {}, CONFIG),
         (dict(block_threads=2048, options=0, rows_per_block=1), {}, CONFIG),
-        (dict(block_threads=256, options=2, rows_per_block=1), {}, CONFIG),
+        (dict(block_threads=256, options=6, rows_per_block=1), {}, CONFIG),  # staged with non-temporal loads
+        (dict(block_threads=256, options=8, rows_per_block=1), {}, CONFIG),
+        (dict(vec=4, block_threads=256, options=4, rows_per_block=1), dict(D=4100), CONFIG),  # staged: vec 8 only
+        (dict(block_threads=1024, options=4, rows_per_block=1), dict(S=(1 << 19) - 64, D=8), CONFIG),  # LDS over 64 KiB
         (dict(block_threads=256, options=0, rows_per_block=0), {}, CONFIG),
         (dict(block_threads=256, options=0, rows_per_block=4, rows_per_thread=4), {}, CONFIG),
         (dict(block_threads=1024, options=0, rows_per_block=4, rows_per_thread=2), {}, CONFIG),  # registers
@@ -554,8 +557,9 @@ def test_default_update_config():
     c = cc.UpdateConfig()
     assert cc.lib().cconv_default_update_config(256, 4096, ctypes.byref(c)) == OK
     assert c.vec == 8 and c.rows_per_block >= 1
+    assert c.options == 5  # non-temporal stores, state runs staged through LDS
     assert cc.lib().cconv_default_update_config(256, 4100, ctypes.byref(c)) == OK
-    assert c.vec == 4
+    assert c.vec == 4 and c.options == 1
     assert cc.lib().cconv_default_update_config(256, 4098, ctypes.byref(c)) == OK
     assert (c.vec, c.options, c.rows_per_thread) == (1, 0, 1)
     assert cc.lib().cconv_default_update_config(1 << 20, 4096, ctypes.byref(c)) == OK

@@ -139,7 +139,9 @@ def test_circular_graph_replay():
 # two rows at once, and blocks that walk several groups of rows (the next group's loads
 # issued before the current group's arithmetic), with ragged last groups
 UPDATE_CONFIGS = [(8, 64, 0, 1, 1), (8, 128, 1, 3, 1), (8, 256, 0, 7, 2), (8, 512, 1, 2, 2), (8, 1024, 0, 5, 1),
-                  (8, 256, 1, 64, 2), (4, 64, 1, 9, 2), (4, 256, 0, 1, 1), (4, 512, 1, 5, 2), (4, 1024, 1, 3, 1),
+                  (8, 256, 1, 64, 2), (8, 256, 3, 1, 2), (8, 128, 2, 4, 1), (8, 256, 5, 2, 2), (8, 64, 4, 3, 1),
+                  (8, 512, 5, 1, 2), (8, 512, 4, 2, 1), (4, 64, 1, 9, 2), (4, 256, 0, 1, 1),
+                  (4, 512, 1, 5, 2), (4, 1024, 1, 3, 1), (4, 256, 3, 2, 2), (4, 64, 2, 1, 1),
                   (1, 64, 0, 1, 1), (1, 256, 0, 6, 1), (1, 1024, 0, 2, 1)]
 
 
@@ -205,3 +207,22 @@ def test_update_invalid_entry_past_the_first_block_of_rows(case):
     y, st, status = _run(x, state, idx, cs, w, b)
     assert status == 8, case
     assert torch.equal(bits(st), bits(state)), f"{case}: state modified"
+
+
+@pytest.mark.parametrize("circular", [False, True], ids=["shift", "circular"])
+def test_update_staging_dropped_for_a_large_pool(circular):
+    """With S near the largest indexed pool the slot check's bit set leaves no LDS room for the
+    staged state runs: the default launch drops the staging and stays correct (an explicit
+    staged configuration is refused)."""
+    N, S, D, W, L = 64, (1 << 19) - 64, 8, 4, 3
+    x, state, idx, cs, w, b = _inputs(N, S, D, W, L, seed=560, circular=circular)
+    y, st, status = _run(x, state, idx, cs, w, b)
+    ok, yr, sr = oracle.update_ex(x, state, idx.numpy(), None if cs is None else cs.numpy(), w, b)
+    assert ok and status == 0
+    assert torch.equal(bits(st), bits(torch.from_numpy(sr).to(torch.bfloat16)))
+    assert_close(y, yr, TOL_FWD, f"S{S} {'circular' if circular else 'shift'}")
+    cfg = cc.cconv_default_update_config(N, D)
+    assert cfg.options & 4
+    with pytest.raises(cc.CconvError):
+        cc.cconv_update_config(x.to(DEV), state.to(DEV), idx.to(DEV), w.to(DEV), b.to(DEV), config=cfg,
+                               cache_seqlens=None if cs is None else cs.to(DEV))
