@@ -127,13 +127,24 @@ __device__ __forceinline__ void bwd_step(const float (&tap)[W][VEC], const float
 // G consecutive rows of x, then of dy, from row pointers xp and dyp (the lane's channels at
 // byte offset lo). One tensor's rows go out back to back (x rows together, then dy rows):
 // measured faster than alternating the two tensors row by row.
+//
+// With 4 or 8 channels per lane each row goes through a buffer resource at the row's base
+// (scalar arithmetic), the lane's byte offset in a vector register: the lane's address is
+// formed once, not once per row.
 template <int VEC, int G, bool NT>
 __device__ __forceinline__ void load_group(Row<VEC> (&rx)[G], Row<VEC> (&rdy)[G], const uint16_t* __restrict__ xp,
                                            int64_t xs, const uint16_t* __restrict__ dyp, int64_t dys, uint32_t lo) {
+    if constexpr (VEC == 4 || VEC == 8) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NT>(at(xp + g * xs, lo));
+        for (int g = 0; g < G; ++g) rx[g] = load_row_rs<VEC, NT>(row_rsrc(xp + g * xs), lo, 0);
 #pragma unroll
-    for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC, NT>(at(dyp + g * dys, lo));
+        for (int g = 0; g < G; ++g) rdy[g] = load_row_rs<VEC, NT>(row_rsrc(dyp + g * dys), lo, 0);
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NT>(at(xp + g * xs, lo));
+#pragma unroll
+        for (int g = 0; g < G; ++g) rdy[g] = load_row<VEC, NT>(at(dyp + g * dys, lo));
+    }
 }
 
 // Rows t .. t+G-1 of a run, already loaded.

@@ -114,6 +114,28 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ p, const Row<VE
     }
 }
 
+// A row of a lane through a buffer resource: the resource holds the row's wave-uniform base
+// (built with scalar instructions), `voff` the lane's byte offset. No per-lane 64-bit address
+// arithmetic per row. The range is the whole 32-bit offset space.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(0xffffffffu), 0x00020000);
+}
+
+template <int VEC, bool NT = false>
+__device__ __forceinline__ Row<VEC> load_row_rs(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    static_assert(VEC == 4 || VEC == 8, "buffer rows: 4 or 8 channels per lane");
+    constexpr int aux = NT ? 2 : 0;  // 2: non-temporal
+    Row<VEC> row;
+    if constexpr (VEC == 8) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), aux);
+        row.u[0] = v.x, row.u[1] = v.y, row.u[2] = v.z, row.u[3] = v.w;
+    } else {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), static_cast<int>(soff), aux);
+        row.u[0] = v.x, row.u[1] = v.y;
+    }
+    return row;
+}
+
 // Option bits of the row kernels (a template parameter).
 constexpr int kNtLoad = 1;    // non-temporal loads of x (and dy)
 constexpr int kNtStore = 2;   // non-temporal stores of y (dx)
@@ -148,10 +170,11 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 // A row element at a wave-uniform base plus a lane's byte offset (a 32-bit byte count). In the
 // row loops the compiler keeps each lane's 64-bit row address in vector registers and steps it
-// by the row stride: one 64-bit vector add per load or store. Addressing the rows through
-// buffer resources instead (scalar row offsets, no vector address arithmetic) removed those
-// adds, 3% of the backward's vector instructions, and measured no faster: the loops wait on
-// memory, not on issue.
+// by the row stride: one 64-bit vector add per load or store. The backward's group loads go
+// through buffer resources instead (load_row_rs: the row base in scalar registers), which
+// takes 32 of those adds off each 16-row group (23.3 -> 22.8 vector instructions per element)
+// at the same speed; its dx stores keep the vector form (a buffer store there had the
+// compiler move the row base through vector registers and back).
 template <typename P>
 __device__ __forceinline__ P* at(P* base, uint32_t off_bytes) {
     using C = typename std::conditional<std::is_const<P>::value, const char, char>::type;
