@@ -223,11 +223,11 @@ def run_variants(cc, si, torch, dev, host, dhost, s, dshape, x, dy, w, b, y, dxo
                  lambda: cc.cconv_bwd_ex(x, dy, w, b, activation=None, dx=dxo, dw=dwo, dbias=dbo, workspace=ws),
                  copy2, {}, cap_lin_b))
 
-    # D other than the headline's: 4098 takes the element-granular path (one channel per lane),
-    # 4100 = 4 (mod 8) 4-channel lanes on 8-byte aligned rows, 4104 the vector path with 17
-    # channel strips whose rows do not start on cache lines
+    # D other than the headline's: 4098 = 2 (mod 4) 4-channel lanes on 4-byte aligned rows (the
+    # last group overlapping the one before), 4100 = 4 (mod 8) 4-channel lanes on 8-byte aligned
+    # rows, 4104 the vector path with 17 channel strips whose rows do not start on cache lines
     big = []
-    for Bn, Dn, tag, what in ((B, 4098, "any_d", "D not a multiple of 4 (one channel per lane)"),
+    for Bn, Dn, tag, what in ((B, 4098, "any_d", "D = 4098 (4 channels per lane, 4-byte aligned rows)"),
                               (B, 4100, "d4100", "D = 4100 (4 channels per lane, 8-byte aligned rows)"),
                               (B, 4104, "d4104", "D = 4104 (vector path, rows not on 128-byte lines)"),
                               (2 * B, D // 2, "b16_d2048", "the pages' production call shape (B = 16, D = 2048)")):
@@ -720,9 +720,9 @@ def time_configs(cc, si, torch, np, dev, copy_rates, peak, with_oracle, min_byte
 
 
 def profile_shapes(cc, si, torch, dev, steps):
-    """Forward and backward at [8, 8192, D] for the widths that leave the 8-channel path (one
-    channel per lane at 4098; 4-channel lanes on rows that miss the 128-byte lines at 4100 and
-    4104; contiguous 6144), `steps` calls each, then one 1R:1W and one 2R:1W flat copy of the
+    """Forward and backward at [8, 8192, D] for the widths that leave the 8-channel path
+    (4-channel lanes on rows that miss the 128-byte lines at 4098, 4100 and 4104; contiguous
+    6144), `steps` calls each, then one 1R:1W and one 2R:1W flat copy of the
     D = 4096 activation size for counter calibration."""
     R = cc.roofline_lib()
     out = {}

@@ -65,10 +65,9 @@ constexpr int64_t kTargetWaves = 1024;  // wave slots of the solo kernels: one p
 // [4,4096,4098]: 6-9% faster forwards, 4-8% faster backwards than four waves per SIMD)
 constexpr int64_t kNarrowFwdTargetWaves = 3072;
 constexpr int64_t kNarrowBwdTargetWaves = 2048;
-// wave slots of the two-channel lanes (D = 2 mod 4): two waves per SIMD (interleaved sweeps of
-// 1024 to 4096 at [8,8192,4098] and [4,8192,2050]: best or within 3% of the best for both
-// passes; 4098 forward 262 us and backward 387 us against 272 and 420 us with one channel per
-// lane)
+// wave slots of the two-channel lanes (the default at D = 2; an explicit option at other
+// D = 2 (mod 4)): two waves per SIMD (interleaved sweeps of 1024 to 4096 at [8,8192,4098] and
+// [4,8192,2050]: best or within 3% of the best for both passes)
 constexpr int64_t kPairFwdTargetWaves = 2048;
 constexpr int64_t kPairBwdTargetWaves = 2048;
 // forward and backward: non-temporal loads and stores, solo kernel (no software prefetch)
@@ -138,8 +137,12 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 // without scratch spills.
 //   * Shape: 4 channels per lane and 16-row groups (the backward loads 16 rows of x and 16 of
 //     dy per group: 16 KiB in flight per wave), also for D = 4 (mod 8), whose rows are
-//     8-byte aligned (at D = 4100 this halves the one-channel plan's time). D not a multiple
-//     of 4: one channel per lane, 16-row groups, the general kernel.
+//     8-byte aligned (at D = 4100 this halves the one-channel plan's time), and for D = 2
+//     (mod 4), D >= 6, whose rows are 4-byte aligned (8-byte accesses need only dword
+//     alignment) and whose last lane group overlaps its neighbour by two channels (at
+//     [8,8192,4098] forward 261 -> 210 us, backward 386 -> 328 us against two channels per
+//     lane). D = 2: two channels per lane; odd D: one; both with 16-row groups and the general
+//     kernel.
 //   * Strips: the D/vec lane groups are dealt to ceil(D/(64*vec)) strips of near-equal width
 //     (strip s takes groups floor(s*L/n) .. floor((s+1)*L/n) - 1). At D = 4100 and 4104 the 17
 //     strips carry 60 or 61 lane groups each instead of sixteen full strips and one holding one
@@ -165,8 +168,8 @@ bool config_ok(const cconv_config_t& c, bool bwd) {
 //   `line_rows_in` (-1: from D alone, as for contiguous operands on 128-byte aligned bases)
 //   says whether every streamed row of the call starts on a 128-byte line.
 //   `lanes` says whether the call's activations meet the rule of the shape's lane width: for
-//   D = 4 (mod 8), 4 channels per lane (8-byte aligned, strides multiples of 4); for D = 2
-//   (mod 4), 2 channels per lane (4-byte aligned, even strides). When they do not, the plan
+//   D = 4 (mod 8), 8-byte aligned, strides multiples of 4; for D = 2 (mod 4), 4-byte aligned,
+//   even strides. When they do not, the plan
 //   runs one channel per lane with that lane width's segments: the dw/dbias partials (their
 //   count, so the workspace and what a finishing stage reads) stay those of the shape,
 //   whatever the layout.
@@ -174,15 +177,17 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
                               int line_rows_in = -1, bool lanes = true) {
     (void)W;
     cconv_config_t c;
-    const bool narrow = (D % 4 != 0);
-    const bool pair = (D % 4 == 2);
+    // odd D: one channel per lane; D = 2: two; every other even D: four (at D = 2 (mod 4) the
+    // last lane group overlaps its neighbour by two channels)
+    const bool narrow = (D % 2 != 0);
+    const bool pair = (D == 2);
     c.vec = pair ? 2 : (narrow ? 1 : 4);
     c.rows_per_group = 16;
     c.waves_per_block = 1;
     c.strips_per_block = 1;
     const bool line_rows = line_rows_in < 0 ? (2 * D) % 128 == 0 : line_rows_in != 0;
     const bool small = static_cast<__int128>(B) * T * D * (bwd ? 6 : 4) <= kSmallStreamBytes;
-    if (narrow)
+    if (narrow || pair)
         c.options = cconv::kNarrowOptions;
     else if (line_rows || streaming_only || small)
         c.options = bwd ? kBwdOptions : kFwdOptions;
@@ -205,7 +210,7 @@ cconv_config_t default_config(bool bwd, int64_t B, int64_t T, int64_t D, int W, 
     ts = std::max(align, ((ts + align - 1) / align) * align);
     const int64_t tcap = ((t + align - 1) / align) * align;
     c.seg_rows = std::min(ts, tcap);
-    if ((pair || (!narrow && D % 8 != 0)) && !lanes) {
+    if (!narrow && D % 8 != 0 && !lanes) {
         c.vec = 1;
         c.options = cconv::kNarrowOptions;
     }
@@ -243,9 +248,16 @@ bool on_lanes(const void* p, int64_t sb, int64_t st, int v) {
     return aligned(p, static_cast<uintptr_t>(2 * v)) && sb % v == 0 && st % v == 0;
 }
 
-// The lane width whose operand rule the default plan of D asks for (4 also for D = 0 mod 8,
-// whose plans check the 8-channel granule instead).
+// The operand rule (channels of alignment) the default plan of D asks for: 4 for D = 0 (mod 4)
+// (also for D = 0 mod 8, whose plans check the 8-channel granule instead), 2 for D = 2 (mod 4)
+// (four channels per lane on 4-byte aligned rows), 1 for odd D.
 int lane_width(int64_t D) { return D % 4 == 0 ? 4 : (D % 4 == 2 ? 2 : 1); }
+
+// Whether a plan's lane width fits D: whole lane groups, or four channels per lane over an
+// even D >= 6 whose last group overlaps its neighbour.
+bool width_ok(const cconv_config_t& c, int64_t D) {
+    return D % c.vec == 0 || (c.vec == 4 && D % 4 == 2 && D > 4);
+}
 
 // Checks shared by the forward and backward before a plan exists: sizes, width, tap dtype.
 cconv_status_t check_train_common(cconv_dtype_t w_dtype, int64_t B, int64_t T, int64_t D, int W) {
@@ -260,10 +272,12 @@ cconv_status_t check_train_common(cconv_dtype_t w_dtype, int64_t B, int64_t T, i
 // whole 8-channel groups (16-byte aligned rows, strides multiples of 8, 16-byte aligned taps,
 // bias, dw and states); 4 for a 4-channel plan with D = 4 (mod 8) (8-byte aligned rows, strides
 // multiples of 4; the taps, bias, dw and states are read and written per element, so element
-// alignment); 2 for a 2-channel plan (4-byte aligned rows, even strides, element alignment
-// elsewhere); 1 for the element-granular plan (one channel per lane: any stride, element
-// alignment everywhere).
-int granule(const cconv_config_t& c, int64_t D) { return c.vec <= 2 ? c.vec : (D % 8 == 0 ? 8 : 4); }
+// alignment); 2 for a 2-channel plan, and for a 4-channel plan with D = 2 (mod 4) (4-byte
+// aligned rows, even strides, element alignment elsewhere); 1 for the element-granular plan
+// (one channel per lane: any stride, element alignment everywhere).
+int granule(const cconv_config_t& c, int64_t D) {
+    return c.vec <= 2 ? c.vec : (D % 8 == 0 ? 8 : (D % 4 == 0 ? 4 : 2));
+}
 
 // Alignment of the taps and bias: 16 bytes for granule 8; the element size otherwise.
 cconv_status_t check_params(const void* w, cconv_dtype_t w_dtype, const float* bias, int gran) {
@@ -398,7 +412,7 @@ cconv_status_t fwd_impl(const void* x, int64_t x_sb, int64_t x_st, const void* w
     const cconv_config_t c =
         cfg ? *cfg : default_config(false, B, T, D, W, ex.mode == kPacked || epi != 0, lines, lanes);
     if (!config_ok(c, false)) return CCONV_ERR_BAD_CONFIG;
-    if (D % c.vec != 0) return CCONV_ERR_BAD_CONFIG;  // a plan needs whole groups of its lane width
+    if (!width_ok(c, D)) return CCONV_ERR_BAD_CONFIG;
     const int gran = granule(c, D);
     if ((st = check_params(w, w_dtype, bias, gran)) != CCONV_OK) return st;
     if ((st = check_act(x, x_sb, x_st, D, gran)) != CCONV_OK) return st;
@@ -507,7 +521,7 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     const cconv_config_t c =
         cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0, lines, lanes);
     if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
-    if (D % c.vec != 0) return CCONV_ERR_BAD_CONFIG;  // a plan needs whole groups of its lane width
+    if (!width_ok(c, D)) return CCONV_ERR_BAD_CONFIG;
     const int gran = granule(c, D);
     if ((st = check_params(w, w_dtype, bias, gran)) != CCONV_OK) return st;
     if ((st = check_act(x, x_sb, x_st, D, gran)) != CCONV_OK) return st;

@@ -277,7 +277,7 @@ template <int VEC, int G, int W, int F, bool VL>
 __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     constexpr int R = W > 1 ? W - 1 : 1;
     extern __shared__ float red[];  // [waves][VEC][64], one column at a time
-    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T, a.lane_groups, a.strips);
+    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T, a.lane_groups, a.strips, a.D);
     const int64_t t0 = wt.t0, t1 = wt.t1;
     const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
@@ -372,8 +372,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             } else if constexpr (VEC == 8) {
                 reinterpret_cast<float4*>(o)[0] = make_float4(s[0], s[1], s[2], s[3]);
                 reinterpret_cast<float4*>(o)[1] = make_float4(s[4], s[5], s[6], s[7]);
-            } else {
-                reinterpret_cast<float4*>(o)[0] = make_float4(s[0], s[1], s[2], s[3]);
+            } else {  // 4 channels: 8-byte aligned when D = 2 (mod 4)
+                const f32x4a q = {s[0], s[1], s[2], s[3]};
+                *reinterpret_cast<f32x4a*>(o) = q;
             }
         }
         __syncthreads();

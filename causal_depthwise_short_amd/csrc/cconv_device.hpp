@@ -30,6 +30,11 @@ struct Row {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+// A lane's 8-byte row chunk of 4 channels needs only 4-byte alignment: multi-dword accesses on
+// CDNA ignore the two low address bits' alignment beyond the dword, so rows of a width
+// D = 2 (mod 4) (4-byte aligned) take the same one-instruction 8-byte loads and stores.
+typedef unsigned int u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+typedef float f32x4a __attribute__((ext_vector_type(4), aligned(4)));
 
 // NT selects non-temporal loads/stores (streamed data that is not re-read soon).
 template <int VEC, bool NT = false>
@@ -61,11 +66,11 @@ __device__ __forceinline__ Row<VEC> load_row(const uint16_t* __restrict__ p) {
         r.u[2] = v.z;
         r.u[3] = v.w;
     } else {
-        u32x2 v;
+        u32x2a v;
         if constexpr (NT) {
-            v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+            v = __builtin_nontemporal_load(reinterpret_cast<const u32x2a*>(p));
         } else {
-            v = *reinterpret_cast<const u32x2*>(p);
+            v = *reinterpret_cast<const u32x2a*>(p);
         }
         r.u[0] = v.x;
         r.u[1] = v.y;
@@ -105,11 +110,11 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ p, const Row<VE
             *reinterpret_cast<u32x4*>(p) = v;
         }
     } else {
-        const u32x2 v = {r.u[0], r.u[1]};
+        const u32x2a v = {r.u[0], r.u[1]};
         if constexpr (NT) {
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2a*>(p));
         } else {
-            *reinterpret_cast<u32x2*>(p) = v;
+            *reinterpret_cast<u32x2a*>(p) = v;
         }
     }
 }
@@ -147,7 +152,7 @@ constexpr int kSolo = 8;      // one-wave blocks, one wave per SIMD, whole regis
 // register moves than the latency they hide).
 constexpr int kVarlenFwdOptions = kNtLoad | kNtStore;
 constexpr int kVarlenBwdOptions = kNtLoad | kNtStore;
-// The element-granular paths (one or two channels per lane: D not a multiple of 4) are
+// The element-granular paths (one channel per lane for odd D, two for D = 2) are
 // compiled with plain loads and stores: their rows never start on a 128-byte cache line, and
 // non-temporal hints then keep the L2 from merging the lines two neighbouring strips share.
 constexpr int kNarrowOptions = 0;
@@ -418,6 +423,12 @@ __device__ __forceinline__ bool block_slots_bad(const int32_t* __restrict__ idx,
 // strips) - 1 of the L = lane_groups (as equal widths as integers allow, at most 64: no strip
 // is left nearly empty); `active` marks the lanes that own one. All fields are wave-uniform
 // except `d`, the lane's first channel, and `active`.
+//
+// Lane group g starts at channel g*VEC, except that the last one of a width D that is not a
+// multiple of VEC (4 channels per lane at D = 2 (mod 4)) starts at D - VEC: it overlaps its
+// neighbour by VEC - D % VEC channels. Both lanes compute those channels from the same inputs
+// in the same order, so what they store there (y, dx, states, the dw/dbias partials) is the
+// same bits, and no lane reads or writes past channel D - 1.
 struct WaveTile {
     int64_t b, sg, t0, t1, d;
     int ws_i, wt_i, wt;
@@ -426,7 +437,7 @@ struct WaveTile {
 
 template <int VEC>
 __device__ __forceinline__ WaveTile wave_tile(int64_t strip_groups, int64_t seg_groups, int ws, int64_t seg_rows,
-                                              int64_t T, int64_t lane_groups, int64_t strips) {
+                                              int64_t T, int64_t lane_groups, int64_t strips, int64_t D) {
     WaveTile w;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t sgrp = tile % strip_groups;
@@ -443,7 +454,7 @@ __device__ __forceinline__ WaveTile wave_tile(int64_t strip_groups, int64_t seg_
     const int64_t g0 = strip * lane_groups / strips, g1 = (strip + 1) * lane_groups / strips;
     const int64_t lane = threadIdx.x % kWave;
     w.active = strip < strips && lane < g1 - g0;
-    w.d = (g0 + lane) * VEC;
+    w.d = min((g0 + lane) * VEC, D - VEC);
     return w;
 }
 

@@ -119,7 +119,7 @@ __device__ __forceinline__ void fwd_run(const float (&tap)[W][VEC], const float 
 template <int VEC, int G, int W, int F, bool VL>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     constexpr int R = W > 1 ? W - 1 : 1;
-    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T, a.lane_groups, a.strips);
+    const WaveTile wt = wave_tile<VEC>(a.strip_groups, a.seg_groups, a.ws, a.seg_rows, a.T, a.lane_groups, a.strips, a.D);
     const int64_t t0 = wt.t0, t1 = wt.t1;
     if (t0 >= a.T) return;    // a trailing wave of the last segment group
     if (!wt.active) return;   // lanes past the strip's channels

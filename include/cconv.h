@@ -35,19 +35,24 @@
  *    D = 4 (mod 8), their default then: the bf16 activations (x, dy, y, dx, residual) 8-byte
  *    aligned with strides that are multiples of 4, the taps, bias, dw, dbias and states with
  *    element alignment (they are read and written per element). When D = 2 (mod 4) they run
- *    2 channels per lane by default, the activations then 4-byte aligned with even strides.
+ *    4 channels per lane by default from D = 6 on (8-byte accesses need only 4-byte alignment;
+ *    the last lane group starts at channel D - 4 and overlaps the one before by two channels,
+ *    which both write with the same bits) and 2 channels per lane at D = 2, the activations
+ *    then 4-byte aligned with even strides.
  *    Any other D (the element-granular path [strip.py's masked loads handle any D]: one
  *    channel per lane) needs only element alignment (2 bytes for bf16, 4 for fp32) and
  *    strides >= D; an explicit configuration with vec = 1 takes that path for any D. When
  *    D = 4 (mod 8) or D = 2 (mod 4) and the activations miss the rule of that lane width,
  *    the default plan runs one channel per lane too, with the segments (so the dw/dbias
  *    partials and the workspace) of the wider plan; an explicit vec = 4 or vec = 2
- *    configuration is checked against its rule. The decode update runs 8
+ *    configuration is checked against its rule (vec = 4 with D = 2 (mod 4): 4-byte aligned,
+ *    even strides). The decode update runs 8
  *    channels per lane when D is a multiple of 8 and one otherwise, taking compact rows
  *    (x_ld == D) or a row stride that is a multiple of 8 [the decode PR's row-stride
  *    contract]. The element-granular paths (1 or 2 channels per lane) run with plain loads
  *    and stores only (options 0; 16-row groups, one-wave blocks by default); a
- *    configuration whose vec does not divide D is CCONV_ERR_BAD_CONFIG. The alignments
+ *    configuration whose vec does not divide D is CCONV_ERR_BAD_CONFIG, except vec = 4 with
+ *    D = 2 (mod 4) and D >= 6. The alignments
  *    stated below are those of the vector path with D a multiple of 8.
  *  - Errors fail closed. A problem visible on the host returns its code before anything is
  *    enqueued, leaving every output untouched: NULL required pointer, negative size, W
@@ -454,7 +459,7 @@ typedef struct {
 
 /*
  * The configuration cconv_fwd (which = 0) or cconv_bwd (which = 1) uses for this shape: 4
- * channels per lane (2 when D % 4 == 2, 1 for odd D), 16-row groups, one-wave blocks, each
+ * channels per lane (2 when D == 2, 1 for odd D), 16-row groups, one-wave blocks, each
  * batch row cut into as many segments as the wave slots hold (1024 waves, one per SIMD; 2048
  * with 2 channels per lane; 3072 for the forward and 2048 for the backward with one), down
  * to one 16-row group;

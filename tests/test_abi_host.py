@@ -255,30 +255,32 @@ def test_bwd_stages_host_errors():
 @pytest.mark.parametrize("which", ["fwd", "bwd"])
 def test_default_plan_fits_the_wave_slots(which):
     """Default plans cut each batch row into as many segments as the wave slots allow (1024
-    one-wave-per-SIMD waves; 2048 with two channels per lane; 3072 (forward) and 2048
-    (backward) with one) and no more, down to one 16-row group, and take streaming cache hints
-    when output rows start on 128-byte lines or the call streams at most 256 MB."""
+    one-wave-per-SIMD waves with four channels per lane, also at D = 2 (mod 4); 2048 with two
+    (D = 2); 3072 (forward) and 2048 (backward) with one (odd D)) and no more, down to one
+    16-row group, and take streaming cache hints when output rows start on 128-byte lines or the
+    call streams at most 256 MB."""
     for B, T, D in [(8, 8192, 4096), (8, 8192, 4160), (8, 8192, 4104), (16, 8192, 2048), (3, 1000, 2000),
                     (8, 8192, 4100), (1, 65536, 4096), (2, 100003, 520), (64, 4096, 4096), (1, 256, 512),
-                    (8, 8192, 4098), (8, 8192, 4097), (4, 4096, 1002), (2, 5000, 333)]:
+                    (8, 8192, 4098), (8, 8192, 4097), (4, 4096, 1002), (2, 5000, 333), (4, 100, 2), (4, 100, 6)]:
         c = cc.cconv_default_config(which, B, T, D, 4)
-        narrow = D % 4 != 0
+        narrow = D % 2 != 0 or D == 2
         fwd = which in ("fwd", 0)
         small = B * T * D * (4 if fwd else 6) <= 256 << 20
         off_lines = (2 * D) % 128 != 0 and not small
-        slots = (2048 if D % 4 == 2 else 3072 if fwd else 2048) if narrow else 1024
-        strips = -(-D // (64 * c.vec))
+        slots = (2048 if D == 2 else 3072 if fwd else 2048) if narrow else 1024
+        strips = -(-(-(-D // c.vec)) // 64)
         waves = B * strips * -(-T // c.seg_rows)
         if B * strips <= slots:
             assert waves <= slots, (B, T, D, c, waves)
         if c.seg_rows > 16:  # not held up by the one-group minimum: one more segment would not fit
             assert B * strips * (-(-T // c.seg_rows) + 1) > slots or -(-T // c.seg_rows) * c.seg_rows - T < c.seg_rows
         if narrow:
-            assert c.vec == (2 if D % 4 == 2 else 1) and c.options == 0
+            assert c.vec == (2 if D == 2 else 1) and c.options == 0
         else:
             assert c.vec == 4 and c.options == (8 if off_lines else 11), (D, c.options)
     assert cc.cconv_default_config(which, 8, 8192, 4096, 4).seg_rows == 1024
     assert cc.cconv_default_config(which, 8, 8192, 4160, 4).seg_rows == 1184
+    assert cc.cconv_default_config(which, 8, 8192, 4098, 4).seg_rows == 1184  # 17 strips, as D = 4100
     # the small workloads: one-group segments at B1 T256 D512, 32-row ones at B3 T1000 D2000
     assert cc.cconv_default_config(which, 1, 256, 512, 4).seg_rows == 16
     assert cc.cconv_default_config(which, 3, 1000, 2000, 2).seg_rows == 32
@@ -666,34 +668,35 @@ def test_bwd_ex_host_errors(kw, code):
 
 
 def test_odd_channel_counts_need_the_narrow_launch():
-    """With D not a multiple of 4 only the one- and two-channel-per-lane plans are accepted
-    (two channels only for even D), with plain hints and the general kernel."""
+    """With D odd only the one-channel-per-lane plan is accepted, with plain hints and the
+    general kernel; two or four channels per lane need an even D."""
     L = cc.lib()
-    T = 64
-    for D, v in ((502, 2), (501, 1)):
-        vec4 = cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
-        assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, Y, 2, T, D, 4, ctypes.byref(vec4), None) == CONFIG
-        narrow = cc.cconv_default_config("fwd", 2, T, D, 4)
-        assert narrow.vec == v and narrow.rows_per_group == 16 and narrow.options == 0
-        # accepted: with y aliasing x it gets as far as the aliasing check
-        assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(narrow), None) == ALIAS
-        for vv in (1, 2):
-            solo = cc.Config(vec=vv, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
-            assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(solo), None) == CONFIG
-            g8 = cc.Config(vec=vv, rows_per_group=8, waves_per_block=1, options=0, seg_rows=64)
-            assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(g8), None) == CONFIG
-        nb = cc.cconv_default_config("bwd", 2, T, D, 4)
-        assert nb.vec == v and nb.options == 0 and nb.waves_per_block == 1
+    T, D = 64, 501
+    vec4 = cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
+    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(vec4), None) == CONFIG
+    narrow = cc.cconv_default_config("fwd", 2, T, D, 4)
+    assert narrow.vec == 1 and narrow.rows_per_group == 16 and narrow.options == 0
+    # accepted: with y aliasing x it gets as far as the aliasing check
+    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(narrow), None) == ALIAS
+    for vv in (1, 2):
+        solo = cc.Config(vec=vv, rows_per_group=16, waves_per_block=1, options=11, seg_rows=64)
+        assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(solo), None) == CONFIG
+        g8 = cc.Config(vec=vv, rows_per_group=8, waves_per_block=1, options=0, seg_rows=64)
+        assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(g8), None) == CONFIG
+    nb = cc.cconv_default_config("bwd", 2, T, D, 4)
+    assert nb.vec == 1 and nb.options == 0 and nb.waves_per_block == 1
     pair = cc.Config(vec=2, rows_per_group=16, waves_per_block=1, options=0, seg_rows=64)
-    assert L.cconv_fwd_config(X, T * 501, 501, WT, BF16, BIAS, X, 2, T, 501, 4, ctypes.byref(pair), None) == CONFIG
+    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, 2, T, D, 4, ctypes.byref(pair), None) == CONFIG
 
 
-def test_two_channel_plans_for_d_2_mod_4():
-    """D = 2 (mod 4): the default plan runs 2 channels per lane, its activations need 4-byte
-    alignment and even strides, everything else element alignment; activations off that rule
-    take one channel per lane with the same segments (so the same workspace). An explicit
-    two-channel plan is checked against the rule. A call that passes every check stops at the
-    aliasing check (y on x), so nothing is launched."""
+def test_four_channel_plans_for_d_2_mod_4():
+    """D = 2 (mod 4), D >= 6: the default plan runs 4 channels per lane (the last lane group
+    overlapping its neighbour) on the solo kernels; its activations need 4-byte alignment and
+    even strides, everything else element alignment; activations off that rule take one
+    channel per lane with the same segments (so the same workspace). Explicit two- and
+    four-channel plans are checked against the same rule; eight channels per lane and four at
+    D = 2 are refused. A call that passes every check stops at the aliasing check (y on x), so
+    nothing is launched."""
     L = cc.lib()
     D, T, B = 502, 64, 2
     assert fwd(D=D, y=X) == ALIAS
@@ -710,14 +713,22 @@ def test_two_channel_plans_for_d_2_mod_4():
     need = L.cconv_bwd_workspace_bytes(B, T, D, 4)
     assert need > 0
     assert bwd(D=D, dx=DX + 2, dy=DY + 2, x=X + 2, ws_bytes=need - 1) == WS
-    pair = cc.Config(vec=2, rows_per_group=16, waves_per_block=1, options=0, seg_rows=64)
-    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, B, T, D, 4, ctypes.byref(pair), None) == ALIAS
-    assert L.cconv_fwd_config(X + 2, T * D, D, WT, BF16, BIAS, Y, B, T, D, 4, ctypes.byref(pair), None) == MISAL
-    assert L.cconv_fwd_config(X, T * 503, 503, WT, BF16, BIAS, Y, B, T, D, 4, ctypes.byref(pair), None) == STRIDE
+    for vec, opts in ((2, 0), (4, 8), (4, 11)):
+        c = cc.Config(vec=vec, rows_per_group=16, waves_per_block=1, options=opts, seg_rows=64)
+        assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, B, T, D, 4, ctypes.byref(c), None) == ALIAS
+        assert L.cconv_fwd_config(X + 4, T * D, D, WT, BF16, BIAS, X + 4, B, T, D, 4, ctypes.byref(c), None) == ALIAS
+        assert L.cconv_fwd_config(X + 2, T * D, D, WT, BF16, BIAS, Y, B, T, D, 4, ctypes.byref(c), None) == MISAL
+        assert L.cconv_fwd_config(X, T * 503, 503, WT, BF16, BIAS, Y, B, T, D, 4, ctypes.byref(c), None) == STRIDE
+    v8 = cc.Config(vec=8, rows_per_group=8, waves_per_block=1, options=11, seg_rows=64)
+    assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, B, T, D, 4, ctypes.byref(v8), None) == CONFIG
+    v4 = cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=8, seg_rows=64)
+    assert L.cconv_fwd_config(X, T * 2, 2, WT, BF16, BIAS, X, B, T, 2, 4, ctypes.byref(v4), None) == CONFIG
+    assert cc.cconv_default_config("fwd", B, T, 2, 4).vec == 2
+    assert cc.cconv_default_config("fwd", B, T, 6, 4).vec == 4
     # the default plan's partials (and the workspace) follow the shape, not the layout
-    c2 = cc.cconv_default_config("bwd", 8, 8192, 4098, 4)
-    assert (c2.vec, c2.options) == (2, 0)
-    one = cc.Config(**{**c2.as_dict(), "vec": 1})
+    c4 = cc.cconv_default_config("bwd", 8, 8192, 4098, 4)
+    assert (c4.vec, c4.options) == (4, 8)
+    one = cc.Config(**{**c4.as_dict(), "vec": 1, "options": 0})
     assert cc.cconv_bwd_workspace_bytes(8, 8192, 4098, 4, one) == cc.cconv_bwd_workspace_bytes(8, 8192, 4098, 4)
 
 

@@ -1,7 +1,8 @@
 """GPU parity for channel counts that are not multiples of 8, for every entry point, against
 the oracle, through the C ABI: the element-granular paths (one channel per lane for odd D, two
-for D = 2 mod 4) and, for the training calls, the 4-channel lanes that D = 4 (mod 8) takes
-(D = 100 and 4100 below). Tolerances in parity.py; states bit for bit.
+for D = 2) and, for the training calls, the 4-channel lanes that D = 4 (mod 8) takes (D = 100
+and 4100 below) and that D = 2 (mod 4) takes with its last lane group overlapping the one
+before (D = 6, 46, 78, 130, 1002, 4098). Tolerances in parity.py; states bit for bit.
 """
 
 from __future__ import annotations
@@ -112,8 +113,8 @@ def test_narrow_launch_invariance(i):
 
 @pytest.mark.parametrize("D", [77, 78, 100])
 def test_narrow_packed_and_epilogue(D):
-    """Packed batches and the epilogue variants at D = 77 (one channel per lane), D = 78 (two)
-    and D = 100 (4 channels per lane)."""
+    """Packed batches and the epilogue variants at D = 77 (one channel per lane), D = 78 (four,
+    the last lane group overlapping) and D = 100 (four)."""
     lens = [100, 0, 1, 3, 250]
     W = 4
     total = sum(lens)
@@ -173,8 +174,8 @@ def test_narrow_decode(D, ld_pad):
 
 @pytest.mark.parametrize("D", [45, 46, 60])
 def test_narrow_pool(D):
-    """The prefill into a decode pool at D = 45 (one channel per lane), D = 46 (two) and D = 60
-    (4 channels per lane)."""
+    """The prefill into a decode pool at D = 45 (one channel per lane), D = 46 (four, the last
+    lane group overlapping) and D = 60 (four)."""
     B, T, W, S = 3, 90, 4, 7
     inp = si.train_inputs(B, T, D, W, bias=True, seed=870)
     state = torch.randn(S, D, W - 1, generator=torch.Generator().manual_seed(871)).to(torch.bfloat16)
@@ -224,15 +225,18 @@ def test_four_channel_lanes_d_4_mod_8(D, W):
     assert_close(dw.cpu(), dw1.cpu(), 1e-4, f"D{D} W{W} dw across lane widths")
 
 
-@pytest.mark.parametrize("D", [2, 1002, 4098])
+@pytest.mark.parametrize("D", [2, 6, 10, 1002, 4098])
 @pytest.mark.parametrize("W", [1, 4])
-def test_two_channel_lanes_d_2_mod_4(D, W):
-    """D = 2 (mod 4) runs 2 channels per lane: x and dy as 4-byte aligned column slices of
-    wider tensors (row stride D + 2), y and dx into guarded buffers, a ragged last strip and
-    segment; against the oracle, and y and dx equal to the one-channel plan's bit for bit."""
+def test_lanes_d_2_mod_4(D, W):
+    """D = 2 (mod 4) runs 4 channels per lane from D = 6 on (the last lane group starts at
+    D - 4 and overlaps the one before by two channels) and 2 at D = 2: x and dy as 4-byte
+    aligned column slices of wider tensors (row stride D + 2), y and dx into guarded buffers, a
+    ragged last strip and segment; against the oracle, and y and dx equal bit for bit to the
+    two- and one-channel plans' and to four-channel plans with other hints and block shapes."""
     B, T = 2, 1000
-    assert cc.cconv_default_config("fwd", B, T, D, W).vec == 2
-    assert cc.cconv_default_config("bwd", B, T, D, W).vec == 2
+    v = 2 if D == 2 else 4
+    assert cc.cconv_default_config("fwd", B, T, D, W).vec == v
+    assert cc.cconv_default_config("bwd", B, T, D, W).vec == v
     big = si.train_inputs(B, T, D + 2, W, bias=True, seed=880 + D + W)
     x = big["x"][:, :, 2:2 + D]
     dy = big["dy"][:, :, 2:2 + D]
@@ -243,9 +247,18 @@ def test_two_channel_lanes_d_2_mod_4(D, W):
     dx, xbuf, xlo, xhi = guarded((B, T, D), torch.bfloat16, DEV)
     cc.cconv_fwd(xd, wd, bd, y=y)
     _, dw, db = cc.cconv_bwd(xd, dyd, wd, bd, dx=dx, dw_dtype=torch.float32)
-    one = cc.Config(vec=1, rows_per_group=16, waves_per_block=1, options=0, seg_rows=64)
-    y1 = cc.cconv_fwd(xd, wd, bd, config=one)
-    dx1, dw1, _ = cc.cconv_bwd(xd, dyd, wd, bd, config=one, dw_dtype=torch.float32)
+    others = [dict(vec=1, rows_per_group=16, waves_per_block=1, options=0, seg_rows=64),
+              dict(vec=2, rows_per_group=16, waves_per_block=1, options=0, seg_rows=128)]
+    if D > 4:
+        others += [dict(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=96),
+                   dict(vec=4, rows_per_group=8, waves_per_block=4, strips_per_block=2, options=3, seg_rows=48),
+                   dict(vec=4, rows_per_group=4, waves_per_block=8, options=0, seg_rows=32)]
+    outs = []
+    for cf in others:
+        c = cc.Config(**cf)
+        yo = cc.cconv_fwd(xd, wd, bd, config=c)
+        dxo, dwo, _ = cc.cconv_bwd(xd, dyd, wd, bd, config=c, dw_dtype=torch.float32)
+        outs.append((cf, yo, dxo, dwo))
     # off the 4-byte rule (x and dy at odd element offsets): the default plan takes one channel
     # per lane, the same values
     xo, dyo = _g(big["x"])[:, :, 1:1 + D], _g(big["dy"])[:, :, 1:1 + D]
@@ -259,9 +272,40 @@ def test_two_channel_lanes_d_2_mod_4(D, W):
     assert_close(dx.cpu(), dxr, TOL_BWD, f"D{D} W{W} dx")
     assert_close(dw.cpu(), dwr, TOL_BWD, f"D{D} W{W} dw")
     assert_close(db.cpu(), dbr, TOL_BWD, f"D{D} W{W} dbias")
-    assert torch.equal(bits(y), bits(y1)) and torch.equal(bits(dx), bits(dx1))
-    assert_close(dw.cpu(), dw1.cpu(), 1e-4, f"D{D} W{W} dw across lane widths")
+    for cf, y2, dx2, dw2 in outs:
+        assert torch.equal(bits(y), bits(y2)) and torch.equal(bits(dx), bits(dx2)), cf
+        # fp32 partial sums grouped per launch: rounding-order differences only
+        assert_close(dw.cpu(), dw2.cpu(), 1e-4, f"D{D} W{W} dw across launches {cf}")
     _, yro = oracle.fwd(big["x"][:, :, 1:1 + D].contiguous(), w, b)
     dxro, _, _ = oracle.bwd(big["x"][:, :, 1:1 + D].contiguous(), big["dy"][:, :, 1:1 + D].contiguous(), w, b)
     assert_close(yo.cpu(), yro, TOL_FWD, f"D{D} W{W} y off the 4-byte rule")
     assert_close(dxo.cpu(), dxro, TOL_BWD, f"D{D} W{W} dx off the 4-byte rule")
+
+
+@pytest.mark.parametrize("D", [6, 1002])
+def test_overlapping_lane_group_with_states(D):
+    """The overlapping last lane group of D = 2 (mod 4) through the state paths: a history in,
+    the final state and the history's gradient out, and the packed batches with their states,
+    at D = 6 (two lane groups, one wave) and 1002 (the overlap in the last of four strips)."""
+    W = 4
+    inp = si.train_inputs(3, 333, D, W, bias=True, seed=890 + D)
+    h0 = si.history_input(3, D, W, seed=891 + D)
+    _check_train(inp["x"], inp["dy"], inp["w"], inp["bias"], h0, f"D{D} states")
+    lens = [5, 0, 2, 300, 26]
+    total = sum(lens)
+    x, dy = inp["x"][0, :total], inp["dy"][0, :total]
+    hp = si.history_input(len(lens), D, W, seed=892 + D)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    y, hT, st = cc.cconv_fwd_varlen(_g(x), _g(cu), _g(inp["w"]), _g(inp["bias"]), _g(hp), want_final_state=True)
+    dx, dw, db, dh0, st2 = cc.cconv_bwd_varlen(_g(x), _g(dy), _g(cu), _g(inp["w"]), _g(inp["bias"]), _g(hp),
+                                               want_d_init_state=True)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(st2.item()) == 0
+    ok, yr, hTr = oracle.fwd_varlen(x, cu.numpy(), inp["w"], inp["bias"], hp)
+    _, dxr, dwr, dbr, dh0r = oracle.bwd_varlen(x, dy, cu.numpy(), inp["w"], inp["bias"], hp)
+    assert_close(y.cpu(), yr, TOL_FWD, "packed y")
+    assert np.array_equal(hT.cpu().float().numpy(), hTr)
+    assert_close(dx.cpu(), dxr, TOL_BWD, "packed dx")
+    assert_close(dw.cpu(), dwr, TOL_BWD, "packed dw")
+    assert_close(db.cpu(), dbr, TOL_BWD, "packed dbias")
+    assert_close(dh0.cpu(), dh0r, TOL_BWD, "packed dh0")

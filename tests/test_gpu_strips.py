@@ -4,8 +4,9 @@ The D/vec lane groups of a row are dealt to ceil(D / (64 vec)) strips in near-eq
 s takes groups floor(s L / n) .. floor((s+1) L / n) - 1), so that no strip holds only a handful
 of lanes. Each channel is written by exactly one wave per row: a guard band around y and dx
 stays untouched, and every output matches the oracle. Widths: 17 strips of 60-61 groups (D =
-4100 on 8-byte rows, 4104), one channel per lane (4098), 3 strips of 43-44 groups (520), 33
-strips of 62-63 groups (8200), and widths below one strip.
+4100 on 8-byte rows, 4104, and 4098 on 4-byte rows, whose last 4-channel group overlaps the one
+before), 3 strips of 43-44 groups (520), 33 strips of 62-63 groups (8200), and widths below one
+strip (12; 6 with two overlapping groups).
 """
 
 from __future__ import annotations
