@@ -30,9 +30,9 @@ struct Row {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-// A lane's 8-byte row chunk of 4 channels needs only 4-byte alignment: multi-dword accesses on
-// CDNA ignore the two low address bits' alignment beyond the dword, so rows of a width
-// D = 2 (mod 4) (4-byte aligned) take the same one-instruction 8-byte loads and stores.
+// A lane's 8-byte row chunk of 4 channels needs only 4-byte alignment: CDNA's vector memory
+// instructions ask dword alignment of an access of a dword or more, so the 4-byte aligned rows
+// of a width D = 2 (mod 4) take the same one-instruction 8-byte loads and stores.
 typedef unsigned int u32x2a __attribute__((ext_vector_type(2), aligned(4)));
 typedef float f32x4a __attribute__((ext_vector_type(4), aligned(4)));
 

@@ -61,9 +61,11 @@
  *    operand, a workspace that is too small. A failed launch returns CCONV_ERR_LAUNCH.
  *  - An empty problem (B*T*D == 0, N*D == 0) is CCONV_OK; the backward still writes its
  *    zero dw/dbias when D > 0, and the decode update still writes *status when given.
- *  - Performance: rows of x and dy whose pitch (x_st, dy_st) is a power of two stream
- *    fastest on MI355X; other pitches measure 7-15% slower at the same D. Only the D
- *    channels of a row are read, so a padded pitch costs memory, not bandwidth.
+ *  - Performance: at a fixed D the time depends on the pitch of the rows (x_st, dy_st and
+ *    the output strides of the general entry points) by up to 25% on MI355X, with no simple
+ *    rule: D = 4096 contiguous and D = 6144 in rows of 8192 stream at 94-95% of a flat copy,
+ *    D = 4096 in rows of 8192 and D = 6144 contiguous at ~78%. Only the D channels of a row
+ *    are read or written, so a padded pitch costs memory, not bandwidth.
  */
 #ifndef CCONV_H
 #define CCONV_H
