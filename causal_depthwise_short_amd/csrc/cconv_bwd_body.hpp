@@ -27,7 +27,8 @@ namespace cconv {
 
 
 // One backward row t. `acc_on`: the row belongs to this segment (accumulate dw/dbias);
-// `emit`: dx of row t-(W-1) is this segment's and gets stored.
+// `emit`: dx of row t-(W-1) is this segment's: it is stored at dxrow (or into the history's
+// gradient when hist_grad is given), or, with `defer`, handed back for the caller to store.
 template <int VEC, int W, int F>
 __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float (&b)[VEC],
                                         const Row<VEC>& rx, const Row<VEC>& rdy,
@@ -35,7 +36,8 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
                                         float (&gr)[W > 1 ? W - 1 : 1][VEC], float (&acc)[W][VEC],
                                         float (&db)[VEC], bool acc_on, bool emit,
                                         uint16_t* __restrict__ dxrow, uint32_t lo, uint16_t* hist_grad = nullptr,
-                                        int64_t hb = 0, int64_t D = 0, int64_t d = 0, int hj = 0) {
+                                        int64_t hb = 0, int64_t D = 0, int64_t d = 0, int hj = 0,
+                                        Row<VEC>* defer = nullptr) {
     constexpr bool NTS = (F & kNtStore) != 0, LIN = (F & kLinear) != 0;
     float xt[VEC], dyt[VEC], g[VEC];
     widen(rx, xt);
@@ -75,6 +77,8 @@ __device__ __forceinline__ void bwd_row(const float (&tap)[W][VEC], const float 
         if (hist_grad) {  // a row before t = 0: the history's gradient, slot hj of [B, D, W-1]
 #pragma unroll
             for (int v = 0; v < VEC; ++v) store_state_bf16(hist_grad, hb, D, d + v, W - 1, hj, dx[v]);
+        } else if (defer) {
+            *defer = narrow<VEC>(dx);
         } else {
             store_row<VEC, NTS>(at(dxrow, lo), narrow<VEC>(dx));
         }
@@ -108,19 +112,21 @@ struct DxSink {
 };
 
 // One row t of a run. GEN: the general emission rule (the first W-1 rows of a run, the tail
-// and the halo); otherwise row t-(W-1) is known to be this wave's own dx row.
+// and the halo); otherwise row t-(W-1) is known to be this wave's own dx row (its dx goes to
+// *defer when given).
 template <int VEC, int W, int F, bool GEN>
 __device__ __forceinline__ void bwd_step(const float (&tap)[W][VEC], const float (&bs)[VEC], const Row<VEC>& rx,
                                          const Row<VEC>& rdy, float (&xr)[W > 1 ? W - 1 : 1][VEC],
                                          float (&gr)[W > 1 ? W - 1 : 1][VEC], float (&acc)[W][VEC], float (&db)[VEC],
-                                         const DxSink& k, int64_t t, bool acc_on) {
+                                         const DxSink& k, int64_t t, bool acc_on, Row<VEC>* defer = nullptr) {
     const int64_t u = t - (W - 1);
     if constexpr (GEN) {
         const bool emit = u >= k.own || (k.hg && u >= k.start - (W - 1));
         bwd_row<VEC, W, F>(tap, bs, rx, rdy, xr, gr, acc, db, acc_on, emit, k.dxb + u * k.dxs, k.lo,
                              u < k.start ? k.hg : nullptr, k.s, k.D, k.d, static_cast<int>(u - k.start + (W - 1)));
     } else {
-        bwd_row<VEC, W, F>(tap, bs, rx, rdy, xr, gr, acc, db, acc_on, true, k.dxb + u * k.dxs, k.lo);
+        bwd_row<VEC, W, F>(tap, bs, rx, rdy, xr, gr, acc, db, acc_on, true, k.dxb + u * k.dxs, k.lo, nullptr, 0, 0,
+                             0, 0, defer);
     }
 }
 
@@ -147,14 +153,29 @@ __device__ __forceinline__ void load_group(Row<VEC> (&rx)[G], Row<VEC> (&rdy)[G]
     }
 }
 
-// Rows t .. t+G-1 of a run, already loaded.
+// Rows t .. t+G-1 of a run, already loaded. Outside the general rule every row's dx (row
+// t+g-(W-1)) is this wave's own, and the group's G dx rows are stored together after its math
+// (a scheduling barrier keeps the compiler from moving them back between the rows): a run of
+// G row stores measured 2.5-3.5% faster than one store per row as it is formed (268-274 vs
+// 276-278 us at [8,8192,4096], 320 vs 326 us at [8,8192,4100], interleaved; dx bit-identical).
 template <int VEC, int G, int W, int F, bool GEN>
 __device__ __forceinline__ void bwd_group(const float (&tap)[W][VEC], const float (&bs)[VEC], const Row<VEC> (&rx)[G],
                                           const Row<VEC> (&rdy)[G], float (&xr)[W > 1 ? W - 1 : 1][VEC],
                                           float (&gr)[W > 1 ? W - 1 : 1][VEC], float (&acc)[W][VEC], float (&db)[VEC],
                                           const DxSink& k, int64_t t) {
+    if constexpr (GEN) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) bwd_step<VEC, W, F, GEN>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, k, t + g, true);
+        for (int g = 0; g < G; ++g) bwd_step<VEC, W, F, GEN>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, k, t + g, true);
+    } else {
+        constexpr bool NTS = (F & kNtStore) != 0;
+        Row<VEC> out[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            bwd_step<VEC, W, F, GEN>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, k, t + g, true, &out[g]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < G; ++g) store_row<VEC, NTS>(at(k.dxb + (t + g - (W - 1)) * k.dxs, k.lo), out[g]);
+    }
 }
 
 // Rows [t, e) of one sequence, t being the first row whose dx this wave owns in it (k.own).

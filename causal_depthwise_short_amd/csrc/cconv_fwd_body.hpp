@@ -93,9 +93,13 @@ __device__ __forceinline__ void fwd_run(const float (&tap)[W][VEC], const float 
             for (int g = 0; g < G; ++g) raw[g] = load_row<VEC, NTL>(at(xb + (t + g) * xs, lo));
 #pragma unroll
             for (int g = 0; g < G; ++g) res[g] = ldr(t + g);
+            // the group's G rows of y go out together after its math (as the backward's dx)
+            Row<VEC> out[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g)
-                store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), fwd_row<VEC, W, LIN, RES>(tap, bs, raw[g], res[g], ring));
+            for (int g = 0; g < G; ++g) out[g] = fwd_row<VEC, W, LIN, RES>(tap, bs, raw[g], res[g], ring);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < G; ++g) store_row<VEC, NTS>(at(yb + (t + g) * ys, lo), out[g]);
         }
     }
     if (t < e) {
