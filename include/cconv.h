@@ -447,8 +447,9 @@ const char* cconv_version(void);
  *                    group's arithmetic (software prefetch); bit 3: "solo" kernels for
  *                    one-wave blocks (waves_per_block must be 1) that run one wave per SIMD
  *                    and may use the whole register file. Results do not depend on them.
- * The lane groups (D / vec of them) are split into ceil(D / (64 * vec)) channel strips of as
- * equal widths as integers allow.
+ * The lane groups (ceil(D / vec) of them; with vec = 4 and D = 2 (mod 4) the last one starts
+ * at channel D - 4) are split into ceil(D / (64 * vec)) channel strips of as equal widths as
+ * integers allow.
  */
 typedef struct {
     int vec;
