@@ -283,14 +283,14 @@ def test_lanes_d_2_mod_4(D, W):
 
 
 @pytest.mark.parametrize("D", [6, 1002])
-def test_overlapping_lane_group_with_states(D):
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_overlapping_lane_group_with_states(D, W):
     """The overlapping last lane group of D = 2 (mod 4) through the state paths: a history in,
     the final state and the history's gradient out, and the packed batches with their states,
     at D = 6 (two lane groups, one wave) and 1002 (the overlap in the last of four strips)."""
-    W = 4
-    inp = si.train_inputs(3, 333, D, W, bias=True, seed=890 + D)
+    inp = si.train_inputs(3, 333, D, W, bias=True, seed=890 + D + W)
     h0 = si.history_input(3, D, W, seed=891 + D)
-    _check_train(inp["x"], inp["dy"], inp["w"], inp["bias"], h0, f"D{D} states")
+    _check_train(inp["x"], inp["dy"], inp["w"], inp["bias"], h0, f"D{D} W{W} states")
     lens = [5, 0, 2, 300, 26]
     total = sum(lens)
     x, dy = inp["x"][0, :total], inp["dy"][0, :total]
