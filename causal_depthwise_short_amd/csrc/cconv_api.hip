@@ -518,8 +518,17 @@ cconv_status_t bwd_impl(int stages, const void* x, int64_t x_sb, int64_t x_st, c
     const bool lanes = on_lanes(x, x_sb, x_st, lv) && on_lanes(dy, dy_sb, dy_st, lv) &&
                        (ex.o_st && main ? on_lanes(dx, ex.mode == kPacked ? 0 : ex.o_sb, ex.o_st, lv)
                                         : on_lanes(dx, T * D, D, lv));
-    const cconv_config_t c =
-        cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0, lines, lanes);
+    cconv_config_t c = cfg ? *cfg : default_config(true, B, T, D, W, ex.mode == kPacked || epi != 0, lines, lanes);
+    // the 4- and 8-channel kernels address a row group as 32-bit scalar offsets from its first
+    // row: row strides up to kMaxGroupStride; beyond that the default plan runs one channel per
+    // lane with the same segments (so the same partials and workspace)
+    const int64_t dx_row = ex.o_st && main ? ex.o_st : D;
+    if (c.vec >= 4 && (x_st > cconv::kMaxGroupStride || dy_st > cconv::kMaxGroupStride ||
+                       dx_row > cconv::kMaxGroupStride)) {
+        if (cfg) return CCONV_ERR_BAD_STRIDE;
+        c.vec = 1;
+        c.options = cconv::kNarrowOptions;
+    }
     if (!config_ok(c, true)) return CCONV_ERR_BAD_CONFIG;
     if (!width_ok(c, D)) return CCONV_ERR_BAD_CONFIG;
     const int gran = granule(c, D);

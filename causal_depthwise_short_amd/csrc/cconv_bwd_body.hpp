@@ -134,17 +134,19 @@ __device__ __forceinline__ void bwd_step(const float (&tap)[W][VEC], const float
 // byte offset lo). One tensor's rows go out back to back (x rows together, then dy rows):
 // measured faster than alternating the two tensors row by row.
 //
-// With 4 or 8 channels per lane each row goes through a buffer resource at the row's base
-// (scalar arithmetic), the lane's byte offset in a vector register: the lane's address is
-// formed once, not once per row.
+// With 4 or 8 channels per lane the rows go through one buffer resource per tensor at the
+// group's first row: row g is the scalar byte offset g * stride * 2 (loop-invariant), the
+// lane's channel offset the vector offset, so no address arithmetic is done per row. The host
+// keeps these plans to row strides of at most kMaxGroupStride elements.
 template <int VEC, int G, bool NT>
 __device__ __forceinline__ void load_group(Row<VEC> (&rx)[G], Row<VEC> (&rdy)[G], const uint16_t* __restrict__ xp,
                                            int64_t xs, const uint16_t* __restrict__ dyp, int64_t dys, uint32_t lo) {
     if constexpr (VEC == 4 || VEC == 8) {
+        const __amdgpu_buffer_rsrc_t r1 = row_rsrc(xp), r2 = row_rsrc(dyp);
 #pragma unroll
-        for (int g = 0; g < G; ++g) rx[g] = load_row_rs<VEC, NT>(row_rsrc(xp + g * xs), lo, 0);
+        for (int g = 0; g < G; ++g) rx[g] = load_row_rs<VEC, NT>(r1, lo, static_cast<uint32_t>(g * xs * 2));
 #pragma unroll
-        for (int g = 0; g < G; ++g) rdy[g] = load_row_rs<VEC, NT>(row_rsrc(dyp + g * dys), lo, 0);
+        for (int g = 0; g < G; ++g) rdy[g] = load_row_rs<VEC, NT>(r2, lo, static_cast<uint32_t>(g * dys * 2));
     } else {
 #pragma unroll
         for (int g = 0; g < G; ++g) rx[g] = load_row<VEC, NT>(at(xp + g * xs, lo));
@@ -173,8 +175,14 @@ __device__ __forceinline__ void bwd_group(const float (&tap)[W][VEC], const floa
         for (int g = 0; g < G; ++g)
             bwd_step<VEC, W, F, GEN>(tap, bs, rx[g], rdy[g], xr, gr, acc, db, k, t + g, true, &out[g]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (VEC == 4 || VEC == 8) {  // dx rows as scalar offsets, as the loads
+            const __amdgpu_buffer_rsrc_t rd = row_rsrc(k.dxb + (t - (W - 1)) * k.dxs);
 #pragma unroll
-        for (int g = 0; g < G; ++g) store_row<VEC, NTS>(at(k.dxb + (t + g - (W - 1)) * k.dxs, k.lo), out[g]);
+            for (int g = 0; g < G; ++g) store_row_rs<VEC, NTS>(rd, k.lo, static_cast<uint32_t>(g * k.dxs * 2), out[g]);
+        } else {
+#pragma unroll
+            for (int g = 0; g < G; ++g) store_row<VEC, NTS>(at(k.dxb + (t + g - (W - 1)) * k.dxs, k.lo), out[g]);
+        }
     }
 }
 

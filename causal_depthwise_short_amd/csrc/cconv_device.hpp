@@ -141,6 +141,25 @@ __device__ __forceinline__ Row<VEC> load_row_rs(__amdgpu_buffer_rsrc_t r, uint32
     return row;
 }
 
+template <int VEC, bool NT = false>
+__device__ __forceinline__ void store_row_rs(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                             const Row<VEC>& row) {
+    static_assert(VEC == 4 || VEC == 8, "buffer rows: 4 or 8 channels per lane");
+    constexpr int aux = NT ? 2 : 0;  // 2: non-temporal
+    if constexpr (VEC == 8) {
+        const u32x4 v = {row.u[0], row.u[1], row.u[2], row.u[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voff), static_cast<int>(soff), aux);
+    } else {
+        const u32x2 v = {row.u[0], row.u[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(voff), static_cast<int>(soff), aux);
+    }
+}
+
+// The backward's 4- and 8-channel kernels address a row group from one buffer resource at its
+// first row, row g at the scalar byte offset g * stride * 2. The offsets are 32-bit: with row
+// strides of at most kMaxGroupStride elements, 15 strides plus a row's bytes stay below 2^32.
+constexpr int64_t kMaxGroupStride = int64_t(1) << 26;
+
 // Option bits of the row kernels (a template parameter).
 constexpr int kNtLoad = 1;    // non-temporal loads of x (and dy)
 constexpr int kNtStore = 2;   // non-temporal stores of y (dx)
@@ -175,11 +194,11 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 // A row element at a wave-uniform base plus a lane's byte offset (a 32-bit byte count). In the
 // row loops the compiler keeps each lane's 64-bit row address in vector registers and steps it
-// by the row stride: one 64-bit vector add per load or store. The backward's group loads go
-// through buffer resources instead (load_row_rs: the row base in scalar registers), which
-// takes 32 of those adds off each 16-row group (23.3 -> 22.8 vector instructions per element)
-// at the same speed; its dx stores keep the vector form (a buffer store there had the
-// compiler move the row base through vector registers and back).
+// by the row stride: one 64-bit vector add per load or store. The backward's row groups go
+// through buffer resources instead (load_row_rs / store_row_rs: one resource per tensor at the
+// group's first row, the rows as loop-invariant scalar offsets), which takes the 16 dx-store
+// adds and the scalar row-base arithmetic of the 32 loads off each 16-row group (1629 -> 1531
+// instructions, 1458 -> 1442 of them vector; backward 1-2% faster).
 template <typename P>
 __device__ __forceinline__ P* at(P* base, uint32_t off_bytes) {
     using C = typename std::conditional<std::is_const<P>::value, const char, char>::type;

@@ -781,3 +781,28 @@ def test_four_channel_plans_for_d_4_mod_8():
     assert L.cconv_fwd_config(X, T * D, D, WT, BF16, BIAS, X, B, T, D, 4, ctypes.byref(vec4), None) == ALIAS
     assert L.cconv_fwd_config(X + 4, T * D, D, WT, BF16, BIAS, Y, B, T, D, 4, ctypes.byref(vec4), None) == MISAL
     assert L.cconv_fwd_config(X + 2, T * 502, 502, WT, BF16, BIAS, X + 2, B, T, D, 4, ctypes.byref(one), None) == ALIAS
+
+
+def test_backward_row_strides_beyond_the_group_offsets():
+    """The 4- and 8-channel backward addresses a row group as 32-bit offsets from its first row,
+    so its row strides are at most 2^26 elements: beyond that the default plan runs one channel
+    per lane (same segments, so the same workspace) and an explicit 4-channel plan is
+    CCONV_ERR_BAD_STRIDE. The forward has no such limit. A call that passes every check stops at
+    the aliasing check (dx or y on x), so nothing is launched."""
+    L = cc.lib()
+    B, T, D, W = 1, 16, 512, 4
+    big, edge = (1 << 26) + 8, 1 << 26
+    assert bwd(B=B, T=T, D=D, x_st=big, dx=X) == ALIAS
+    assert bwd(B=B, T=T, D=D, dy_st=big, dx=X) == ALIAS
+    assert bwd(B=B, T=T, D=D, x_st=edge, dx=X) == ALIAS
+    assert fwd(B=B, T=T, D=D, x_st=big, y=X) == ALIAS
+
+    def bwd_cfg(cfg, x_st):
+        return L.cconv_bwd_config(X, T * x_st, x_st, DY, T * D, D, WT, BF16, BIAS, X, DW, BF16, DB, WSP, 1 << 40,
+                                  B, T, D, W, ctypes.byref(cfg), None)
+
+    v4 = cc.Config(vec=4, rows_per_group=16, waves_per_block=1, options=11, seg_rows=16)
+    v1 = cc.Config(vec=1, rows_per_group=16, waves_per_block=1, options=0, seg_rows=16)
+    assert bwd_cfg(v4, big) == STRIDE
+    assert bwd_cfg(v4, edge) == ALIAS
+    assert bwd_cfg(v1, big) == ALIAS

@@ -309,3 +309,28 @@ def test_overlapping_lane_group_with_states(D, W):
     assert_close(dw.cpu(), dwr, TOL_BWD, "packed dw")
     assert_close(db.cpu(), dbr, TOL_BWD, "packed dbias")
     assert_close(dh0.cpu(), dh0r, TOL_BWD, "packed dh0")
+
+
+def test_backward_beyond_the_group_offset_strides():
+    """Rows of x and dy 2^26 + 8 elements apart (134 MB): past the row strides the 4-channel
+    backward addresses as 32-bit offsets, so the default plan runs one channel per lane; the
+    result still matches the oracle, and the forward (no such limit) too."""
+    B, T, D, W = 1, 5, 512, 4
+    st = (1 << 26) + 8
+    inp = si.train_inputs(B, T, D, W, bias=True, seed=895)
+    xb = torch.zeros(T, st, dtype=torch.bfloat16, device=DEV)
+    dyb = torch.zeros(T, st, dtype=torch.bfloat16, device=DEV)
+    xb[:, :D] = inp["x"][0].to(DEV)
+    dyb[:, :D] = inp["dy"][0].to(DEV)
+    x, dy = xb[:, :D].unsqueeze(0), dyb[:, :D].unsqueeze(0)
+    assert x.stride() == (T * st, st, 1)
+    w, b = _g(inp["w"]), _g(inp["bias"])
+    y = cc.cconv_fwd(x, w, b)
+    dx, dw, db = cc.cconv_bwd(x, dy, w, b, dw_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _, yr = oracle.fwd(inp["x"], inp["w"], inp["bias"])
+    dxr, dwr, dbr = oracle.bwd(inp["x"], inp["dy"], inp["w"], inp["bias"])
+    assert_close(y.cpu(), yr, TOL_FWD, "huge-stride y")
+    assert_close(dx.cpu(), dxr, TOL_BWD, "huge-stride dx")
+    assert_close(dw.cpu(), dwr, TOL_BWD, "huge-stride dw")
+    assert_close(db.cpu(), dbr, TOL_BWD, "huge-stride dbias")
