@@ -38,7 +38,11 @@
  *    4 channels per lane by default from D = 6 on (8-byte accesses need only 4-byte alignment;
  *    the last lane group starts at channel D - 4 and overlaps the one before by two channels,
  *    which both write with the same bits) and 2 channels per lane at D = 2, the activations
- *    then 4-byte aligned with even strides.
+ *    then 4-byte aligned with even strides. The backward's 4- and 8-channel plans address a
+ *    group of rows as 32-bit offsets from its first row, so they take row strides (x_st,
+ *    dy_st and dx's) of at most 2^26 elements: beyond that the default backward plan runs one
+ *    channel per lane (the same segments and workspace) and an explicit vec >= 4
+ *    configuration returns CCONV_ERR_BAD_STRIDE.
  *    Any other D (the element-granular path [strip.py's masked loads handle any D]: one
  *    channel per lane) needs only element alignment (2 bytes for bf16, 4 for fp32) and
  *    strides >= D; an explicit configuration with vec = 1 takes that path for any D. When
